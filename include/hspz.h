@@ -1,0 +1,227 @@
+/*
+ * hspz.h -- C ABI of libhspz, the MI355X (gfx950) seed-and-extend hot path described
+ * by the hspZ documentation pages "C. Hit discovery", "D. Score gate" and
+ * "E. X-drop materialization".
+ *
+ * One engine holds one reference (its spaced-seed index and encoded bases) and one
+ * query strand (its encoded bases and seeds) in device memory.  A pass over one batch
+ * of query seeds is:
+ *
+ *   hspz_plan         counts, global prefix, MAX_HITS chunk list     (C.1 - C.3)
+ *   per chunk:
+ *     hspz_find_hits  packed anchors in raw (backward) order        (C.4 - C.5)
+ *     hspz_score_gate one survivor byte per anchor                  (D.1 - D.3)
+ *     hspz_compact    increasing survivor ids                       (D.4)
+ *     hspz_materialize exact X-drop SegmentPair + status per id     (E.1 - E.5)
+ *     hspz_compact_hsps accepted SegmentPairs in survivor order     (E.5)
+ *
+ * Conventions
+ *  - Every function returns HSPZ_OK (0) or a negative HSPZ_E_* code; no exception or
+ *    signal crosses the ABI.  On error, outputs are unspecified, every *n_out is set to
+ *    0 and hspz_last_error(engine) describes the failure.
+ *  - Pointers named d_* are device pointers on the engine's device, owned by the
+ *    caller; the library never frees them.  h_* pointers are host memory.
+ *  - stream is a hipStream_t (NULL = the default stream).  Calls that return a count
+ *    (hspz_plan, hspz_compact, hspz_compact_hsps) synchronise that stream; every other
+ *    kernel-launching call is asynchronous on it.
+ *  - An engine is not thread-safe: use one engine per host thread.
+ *  - Coordinates are 0-based.  Sequences are ASCII; A/C/G/T in either case are bases,
+ *    every other byte is N.
+ */
+#ifndef HSPZ_H
+#define HSPZ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSPZ_OK 0
+#define HSPZ_E_INVALID (-1)  /* bad parameter, malformed seed pattern, out-of-range arg */
+#define HSPZ_E_OVERFLOW (-2) /* batch total exceeds the 32-bit hit index (refused)      */
+#define HSPZ_E_CAPACITY (-3) /* caller buffer too small                                 */
+#define HSPZ_E_NOMEM (-4)    /* host or device allocation failed                        */
+#define HSPZ_E_HIP (-5)      /* a HIP runtime call failed                               */
+#define HSPZ_E_STATE (-6)    /* call out of order (e.g. find_hits before plan)          */
+
+typedef struct hspz_engine hspz_engine;
+
+/* One ungapped high-scoring segment pair ("E. X-drop materialization", E.4): the
+ * closed interval ref_start..=ref_start+len on the reference and
+ * query_start..=query_start+len on the query; len is an extent (the number of bases
+ * covered minus one).  score is the X-drop total L* + R*.  16 bytes, little-endian,
+ * this field order. */
+typedef struct {
+    uint32_t ref_start;
+    uint32_t query_start;
+    uint32_t len;
+    int32_t score;
+} hspz_segment_pair;
+
+/* One MAX_HITS chunk ("C. Hit discovery", C.3): seeds seed_lo..=seed_hi (indices into
+ * the current strand's seed list) whose anchors occupy hits hit_lo..hit_lo+n_hits-1 of
+ * the batch's global prefix.  A chunk's anchors are numbered 0..n_hits-1 locally. */
+typedef struct {
+    uint64_t seed_lo;
+    uint64_t seed_hi;
+    uint64_t hit_lo;
+    uint64_t n_hits;
+} hspz_chunk;
+
+/* Engine parameters.
+ *  seed_pattern  spaced seed, '1' = care position; must start and end with '1',
+ *                weight 1..14, span <= 64 ("C. Hit discovery", C.1 packed k-mer).
+ *  sub           substitution scores, row = reference base, column = query base, order
+ *                A,C,G,T, row-major; each |entry| <= 10000.
+ *  n_score       score of any pair involving N; |n_score| <= 10000.
+ *  xdrop         X-drop, 0 <= xdrop <= 1000000 ("D. Score gate", D.2).
+ *  hsp_threshold K >= 1; the keep threshold T is derived from it once per engine.
+ *  max_hits      MAX_HITS chunk cap, 0 = unlimited ("C. Hit discovery", C.3).
+ *  expand_mode   0 = density rule (>= 16 hits per seed -> group per seed), 1 = always
+ *                thread per seed, 2 = always group per seed ("C. Hit discovery", C.4).
+ *  chunk_walk    0 = locate boundaries through block sums, copying one prefix block per
+ *                boundary; 1 = copy the whole prefix and walk it.  Same chunks.
+ *  device        HIP device ordinal the engine lives on.
+ */
+typedef struct {
+    const char *seed_pattern;
+    int32_t sub[16];
+    int32_t n_score;
+    int32_t xdrop;
+    int32_t hsp_threshold;
+    int32_t expand_mode;
+    uint64_t max_hits;
+    int32_t chunk_walk;
+    int32_t device;
+} hspz_params;
+
+/* Create an engine on params->device and compute the keep threshold T once: the least
+ * int32 t with (float)t >= (float)K ("D. Score gate", D.2 invariant), so that the
+ * gate's integer compare total >= T keeps exactly what the single-precision comparison
+ * keeps.  *out receives the engine (caller frees it with hspz_engine_destroy).
+ * Errors: HSPZ_E_INVALID (parameters), HSPZ_E_NOMEM, HSPZ_E_HIP. */
+int hspz_engine_create(const hspz_params *params, hspz_engine **out);
+
+/* Free the engine and every device buffer it owns.  NULL is accepted. */
+int hspz_engine_destroy(hspz_engine *engine);
+
+/* The keep threshold T computed at creation. */
+int32_t hspz_keep_threshold(const hspz_engine *engine);
+
+/* Last error message of this engine ("" if none); owned by the engine, valid until
+ * the next call on it.  A NULL engine returns the message of the last failed create. */
+const char *hspz_last_error(const hspz_engine *engine);
+
+/* Encode the reference and build its spaced-seed index on the host ("C. Hit
+ * discovery", C.1: a cumulative bucket-end table, one entry per packed k-mer, and the
+ * concatenated buckets of reference end coordinates, ascending within a bucket), then
+ * copy both and the encoded bases to the device.  h_ascii (len bytes, host) is not
+ * retained.  len < 2^32 - 64.  Replaces any previous reference and invalidates a plan.
+ * Synchronises stream.  Errors: HSPZ_E_INVALID, HSPZ_E_NOMEM, HSPZ_E_HIP. */
+int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                          void *stream);
+
+/* Encode one query strand and list its seeds: every window whose care positions are
+ * all A/C/G/T, in ascending window position, each with its packed k-mer and its
+ * query end coordinate (window start + span).  strand 0 = the sequence as given,
+ * 1 = its reverse complement, in the reverse complement's own coordinates.  Replaces
+ * the previous query and invalidates a plan.  Synchronises stream.  Errors as above. */
+int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                      int32_t strand, void *stream);
+
+/* Number of seeds of the current query strand. */
+uint64_t hspz_num_seeds(const hspz_engine *engine);
+
+/* Seed-index range [*seed_lo, *seed_hi) of the seeds whose window starts in
+ * [pos_lo, pos_hi) -- a contiguous query batch.  Errors: HSPZ_E_STATE (no query). */
+int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
+                    uint64_t *seed_lo, uint64_t *seed_hi);
+
+/* Plan one batch, seeds [seed_lo, seed_hi) ("C. Hit discovery", C.1-C.3): count each
+ * seed's hits, scan blocks of counts on the device, exclusive-scan the block sums on
+ * the host in 64 bits, add the offsets back to form the global inclusive prefix, and
+ * cut MAX_HITS chunks with the lower-bound walk (a seed is never split).  A batch whose
+ * total exceeds 2^32 - 1 is refused with HSPZ_E_OVERFLOW before anything else is done.
+ * *total_hits and *n_chunks receive the totals (0 chunks when the total is 0).
+ * Synchronises stream.  Errors: HSPZ_E_STATE (no reference/query), HSPZ_E_INVALID,
+ * HSPZ_E_OVERFLOW, HSPZ_E_NOMEM, HSPZ_E_HIP. */
+int hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
+              uint64_t *total_hits, uint32_t *n_chunks);
+
+/* Chunk i of the current plan.  Errors: HSPZ_E_STATE (no plan), HSPZ_E_INVALID. */
+int hspz_get_chunk(const hspz_engine *engine, uint32_t i, hspz_chunk *out);
+
+/* Expand chunk i into packed anchors ("C. Hit discovery", C.4-C.5): occurrence j of
+ * seed s is written to d_anchors[P[s] - 1 - hit_lo - j] as
+ * (reference end) | (query end) << 32, so each bucket lands backwards from the seed's
+ * inclusive prefix.  d_anchors holds cap u64 entries (device); cap must be at least the
+ * chunk's n_hits.  The choice between thread-per-seed and group-per-seed expansion
+ * changes memory traffic only, never the bytes.  Errors: HSPZ_E_STATE, HSPZ_E_INVALID,
+ * HSPZ_E_CAPACITY, HSPZ_E_HIP. */
+int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors, uint64_t cap,
+                   void *stream);
+
+/* Score-only X-drop gate over n packed anchors ("D. Score gate", D.1-D.3).  For each
+ * anchor (r, q) the right walk scores (r+i, q+i) and the left walk (r-1-i, q-1-i); each
+ * stops at the first base whose running score is more than xdrop below its best so far,
+ * or at a sequence end, and contributes that best (0 for an empty walk).  d_flags[i]
+ * becomes 1 if the two bests sum to at least T, else 0; all n bytes are written.
+ * d_anchors must hold coordinates within the uploaded sequences.  n < 2^32.
+ * Errors: HSPZ_E_STATE, HSPZ_E_INVALID, HSPZ_E_HIP. */
+int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                    uint8_t *d_flags, void *stream);
+
+/* Stable compaction of n flag bytes ("D. Score gate", D.4): d_ids receives, in
+ * increasing order, the index of every non-zero byte.  *n_out receives their number;
+ * if it exceeds cap (the capacity of d_ids, u32 entries) the call fails with
+ * HSPZ_E_CAPACITY and *n_out = 0.  n < 2^32.  Synchronises stream. */
+int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n, uint32_t *d_ids,
+                 uint64_t cap, uint64_t *n_out, void *stream);
+
+/* Exact materialization of n_surv survivors ("E. X-drop materialization", E.1-E.5).
+ * For each i the anchor d_anchors[d_ids[i]] is extended to both sides by the same
+ * X-drop rule as the gate, keeping the earliest base that attains each side's best.
+ * With left extent m and right extent k the record is
+ * {r - m, q - m, m + k - 1, L* + R*}.  d_status[i] = 1 if the record is accepted
+ * (score >= T), else 0; d_hsp[i] is written in either case and is meaningful only when
+ * accepted.  Errors: HSPZ_E_STATE, HSPZ_E_HIP. */
+int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors, const uint32_t *d_ids,
+                     uint64_t n_surv, hspz_segment_pair *d_hsp, uint8_t *d_status,
+                     void *stream);
+
+/* Stable compaction of the accepted records ("E. X-drop materialization", E.5): the
+ * d_hsp[i] with d_status[i] != 0, in order, into d_out (cap records).  *n_out receives
+ * their number; HSPZ_E_CAPACITY if it exceeds cap.  Synchronises stream. */
+int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
+                      const uint8_t *d_status, uint64_t n, hspz_segment_pair *d_out,
+                      uint64_t cap, uint64_t *n_out, void *stream);
+
+/* ---- inspection (tests and tools) -------------------------------------------------- */
+
+/* Copy seeds [lo, hi) of the current strand to the host: packed k-mers and query end
+ * coordinates (either pointer may be NULL).  Synchronous. */
+int hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi, uint32_t *h_kmer,
+                   uint32_t *h_q_end);
+
+/* Copy the planned batch's per-seed hit counts and global inclusive prefix (u32 each,
+ * one per seed of the batch) to the host (either pointer may be NULL).  Synchronous. */
+int hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts, uint32_t *h_prefix);
+
+/* Run the prefix and chunk steps ("C. Hit discovery", C.2-C.3) on n injected per-seed
+ * counts (host array) instead of index lookups, leaving a plan whose chunks and prefix
+ * can be read back but not expanded.  Synchronises stream.  Errors as hspz_plan. */
+int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64_t n,
+                           void *stream, uint64_t *total_hits, uint32_t *n_chunks);
+
+/* Exact algorithmic work of the score gate over n anchors: the number of bases their
+ * right and left X-drop walks score (each walk up to and including its first dropping
+ * base, never past a sequence end), summed into *total_steps.  Allocates a small
+ * temporary device buffer; synchronises stream.  Not part of a pass. */
+int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                          uint64_t *total_steps, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSPZ_H */

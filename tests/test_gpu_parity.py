@@ -1,0 +1,290 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small seeded inputs span several scan blocks, gate tiles and compaction blocks with
+ragged tails; every byte of seeds, counts, prefix, chunks, anchors, flags, ids, status
+and accepted records is compared.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (assert_pass_equal, engine, gpu_full_pass, oracle_pass, params_of,
+                      require_gpu)
+from workloads import HOXD70, SEED_PATTERN, build, random_pair
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def test_worked_example_through_the_abi():
+    # one-base seed: buckets A:0 C:3 G:1 T:5 give the page's counts 0 3 1 0 5
+    g = json.load(open(os.path.join(GOLD, "hit_discovery_worked_example.json")))
+    p = params_of("1")
+    eng = engine(p)
+    r = gpu_full_pass(eng, b"CCCGTTTTT", b"ACGAT")
+    cnt, pre = r["plan_arrays"]
+    assert cnt.tolist() == g["counts"] and pre.tolist() == g["inclusive_prefix"]
+    a = r["chunks"][0]["anchors"]
+    q_end_of = {1: 2, 2: 3, 4: 5}  # seed s covers query base s, exclusive end s + 1
+    for s, slots in g["slots_by_seed_in_occurrence_order"].items():
+        qe = q_end_of[int(s)]
+        assert [int(a[x] >> 32) for x in slots] == [qe] * len(slots)
+        # occurrences ascend in reference end along j, so slots descend
+        refs = [int(a[x] & 0xFFFFFFFF) for x in slots]
+        assert refs == sorted(refs)
+    o, _, _ = oracle_pass(b"CCCGTTTTT", b"ACGAT", p)
+    assert_pass_equal(r, o)
+
+
+@pytest.mark.parametrize("walk", [0, 1])
+def test_chunk_cuts_from_injected_counts(walk):
+    gold = json.load(open(os.path.join(GOLD, "chunk_cuts_worked_example.json")))
+    for case in gold["cases"]:
+        eng = engine(params_of(SEED_PATTERN), chunk_walk=walk, max_hits=case["max_hits"])
+        tot, nch = eng.debug_plan_counts(np.asarray([0, 3, 1, 0, 5], np.uint32))
+        got = [[c["seed_lo"], c["seed_hi"], c["hit_lo"], c["n_hits"]]
+               for c in (eng.get_chunk(i) for i in range(nch))]
+        assert tot == 9 and got == case["chunks"]
+        cnt, pre = eng.get_plan_arrays(5)
+        assert pre.tolist() == [0, 3, 4, 4, 9]
+
+
+@pytest.mark.parametrize("walk", [0, 1])
+@pytest.mark.parametrize("seed", range(3))
+def test_chunk_walk_on_many_blocks(walk, seed):
+    rng = np.random.default_rng(seed)
+    counts = rng.choice([0, 0, 1, 2, 5, 40, 300], size=50_000).astype(np.uint32)
+    P, _ = oracle.prefix(counts)
+    for mx in (1, 3, 16, 1000, 77_777, int(P[-1]) - 1, 0):
+        eng = engine(params_of(SEED_PATTERN), chunk_walk=walk, max_hits=mx)
+        tot, nch = eng.debug_plan_counts(counts)
+        got = [eng.get_chunk(i) for i in range(nch)]
+        want = oracle.chunks(P, mx)
+        assert tot == int(P[-1])
+        assert [(c["seed_lo"], c["seed_hi"], c["hit_lo"], c["n_hits"]) for c in got] == \
+            [(c["seed_lo"], c["seed_hi"], c["hit_lo"], c["n_hits"]) for c in want]
+        _, pre = eng.get_plan_arrays(counts.size)
+        assert np.array_equal(pre.astype(np.uint64), P)
+
+
+CASES = [
+    # (seed, n_ref, n_qry, pattern, max_hits, n_frac, plant, identity, gc)
+    (0, 30_000, 30_000, "1101011", 0, 0.0, 20, 0.92, 0.5),
+    (1, 25_000, 31_000, "1101011", 5_000, 0.03, 15, 0.85, 0.41),
+    (2, 40_000, 20_000, SEED_PATTERN, 0, 0.02, 30, 0.9, 0.41),
+    (3, 12_345, 23_456, "11011", 2_000, 0.05, 10, 0.95, 0.5),
+    (4, 8_000, 8_000, "111", 7, 0.0, 5, 0.8, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
+@pytest.mark.parametrize("expand_mode", [0, 1, 2])
+def test_random_pass_parity(case, expand_mode):
+    seed, nr, nq, pat, mx, nf, plant, ident, gc = case
+    ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
+                           identity=ident, gc=gc, alphabet_noise=True)
+    p = params_of(pat, max_hits=mx)
+    o, _, _ = oracle_pass(ref, qry, p)
+    r = gpu_full_pass(engine(p, expand_mode=expand_mode), ref, qry)
+    assert_pass_equal(r, o)
+
+
+@pytest.mark.parametrize("strand", ["+", "-"])
+def test_reverse_strand_parity(strand):
+    ref, qry = random_pair(7, 20_000, 20_000, plant=20, plant_len=(100, 800), identity=0.9)
+    from workloads import reverse_complement_ascii
+    qry = np.concatenate([qry[:10_000], reverse_complement_ascii(ref[5_000:15_000])])
+    p = params_of("1101011", max_hits=30_000)
+    o, _, _ = oracle_pass(ref, qry, p, strand=strand)
+    assert o["total"] > 0 and sum(c["ids"].size for c in o["chunks"]) > 0
+    assert_pass_equal(gpu_full_pass(engine(p), ref, qry, strand=strand), o)
+
+
+def test_query_batches_parity():
+    ref, qry = random_pair(8, 20_000, 30_000, plant=25, plant_len=(100, 500), identity=0.9,
+                           n_frac=0.02)
+    p = params_of("1101011", max_hits=4_000)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    from ungapped_drop_hsp_amd.pipeline import batches
+    bs = batches(eng, 7_000, qry.size)
+    assert len(bs) == 5
+    for lo, hi in bs:
+        o, _, _ = oracle_pass(ref, qry, p, seed_range=(lo, hi))
+        assert_pass_equal(gpu_full_pass(eng, ref, qry, seed_range=(lo, hi)), o)
+
+
+@pytest.mark.parametrize("xdrop,n_score", [(910, -100), (400, -100), (150, 30), (60, -20),
+                                           (0, -100)])
+def test_block_sizes_and_scores(xdrop, n_score):
+    # small X forces 4-, 2- and 1-base gate blocks; a positive N score is allowed too
+    sub = np.asarray(HOXD70, np.int32).copy()
+    sub[0, 1], sub[1, 0] = 40, -90  # asymmetric: ref row, query column
+    ref, qry = random_pair(9, 15_000, 15_000, plant=30, plant_len=(50, 400), identity=0.9,
+                           n_frac=0.03)
+    p = params_of("11011", sub=sub, xdrop=xdrop, K=400, n_score=n_score)
+    o, _, _ = oracle_pass(ref, qry, p)
+    assert_pass_equal(gpu_full_pass(engine(p), ref, qry), o)
+
+
+def test_identical_sequences_long_walks():
+    ref, _ = random_pair(10, 30_000, 1, gc=0.41)
+    p = params_of(SEED_PATTERN, max_hits=100_000)
+    o, _, _ = oracle_pass(ref, ref, p)
+    r = gpu_full_pass(engine(p), ref, ref)
+    assert_pass_equal(r, o)
+    # the main diagonal's records span the whole sequence
+    acc = np.concatenate([c["accepted"] for c in r["chunks"]])
+    full = acc[(acc["ref_start"] == 0) & (acc["len"] == ref.size - 1)]
+    assert full.size > 0
+
+
+@pytest.mark.parametrize("qry", [b"", b"ACGT", b"N" * 5000, b"ACGTACGTAC" * 3])
+def test_degenerate_queries(qry):
+    ref, _ = random_pair(11, 5_000, 1)
+    p = params_of("1101011")
+    o, _, _ = oracle_pass(ref, np.frombuffer(qry, np.uint8), p)
+    r = gpu_full_pass(engine(p), ref, np.frombuffer(qry, np.uint8))
+    assert_pass_equal(r, o)
+
+
+def test_empty_reference():
+    p = params_of("11011")
+    eng = engine(p)
+    eng.upload_reference(b"")
+    eng.upload_query(b"ACGTACGTACGT")
+    assert eng.plan(0, eng.num_seeds()) == (0, 0)
+
+
+def test_overflow_is_refused():
+    # 70,000 x A against itself: 69,982 seeds x 69,982 hits > 2^32 - 1
+    p = params_of(SEED_PATTERN)
+    eng = engine(p)
+    eng.upload_reference(b"A" * 70_000)
+    eng.upload_query(b"A" * 70_000)
+    import ungapped_drop_hsp_amd as h
+    with pytest.raises(h.HspzError) as ei:
+        eng.plan(0, eng.num_seeds())
+    assert ei.value.name == "HSPZ_E_OVERFLOW"
+    with pytest.raises(h.HspzError) as ei:
+        eng.find_hits(0, 0, cap=0)
+    assert ei.value.name == "HSPZ_E_STATE"
+    # a smaller batch of the same query fits
+    tot, nch = eng.plan(0, 1000)
+    assert tot == 1000 * 69_982 and nch == 1
+
+
+def test_errors_and_capacity():
+    import torch
+    import ungapped_drop_hsp_amd as h
+    ref, qry = random_pair(12, 5_000, 5_000, plant=5, identity=0.95)
+    p = params_of("11011")
+    eng = engine(p)
+    with pytest.raises(h.HspzError) as ei:
+        eng.plan(0, 0)
+    assert ei.value.name == "HSPZ_E_STATE"
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    with pytest.raises(h.HspzError) as ei:
+        eng.plan(0, eng.num_seeds() + 1)
+    assert ei.value.name == "HSPZ_E_INVALID"
+    tot, nch = eng.plan(0, eng.num_seeds())
+    small = torch.empty(tot - 1, dtype=torch.int64, device="cuda")
+    with pytest.raises(h.HspzError) as ei:
+        eng.find_hits(0, small)
+    assert ei.value.name == "HSPZ_E_CAPACITY"
+    a = torch.empty(tot, dtype=torch.int64, device="cuda")
+    eng.find_hits(0, a)
+    f = torch.empty(tot, dtype=torch.uint8, device="cuda")
+    eng.score_gate(a, tot, f)
+    n_keep = int((f != 0).sum())
+    assert n_keep > 1
+    ids = torch.empty(n_keep - 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(h.HspzError) as ei:
+        eng.compact(f, tot, ids)
+    assert ei.value.name == "HSPZ_E_CAPACITY"
+    with pytest.raises(h.HspzError):
+        eng.get_chunk(nch)
+
+
+def test_poisoned_outputs_are_overwritten():
+    import torch
+    ref, qry = random_pair(13, 20_000, 20_000, plant=20, plant_len=(80, 500), identity=0.9)
+    p = params_of("1101011")
+    o, _, _ = oracle_pass(ref, qry, p)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    tot, _ = eng.plan(0, eng.num_seeds())
+    a = torch.full((tot + 7,), -0x5454545454545455, dtype=torch.int64, device="cuda")
+    f = torch.full((tot + 7,), 0xAB, dtype=torch.uint8, device="cuda")
+    eng.find_hits(0, a)
+    eng.score_gate(a, tot, f)
+    ah = a.cpu().numpy().view(np.uint64)
+    assert np.array_equal(ah[:tot], o["chunks"][0]["anchors"])
+    fh = f.cpu().numpy()
+    assert np.array_equal(fh[:tot], o["chunks"][0]["flags"])
+    assert (fh[tot:] == 0xAB).all()  # nothing past n is touched
+    ids = torch.full((tot,), -1, dtype=torch.int32, device="cuda")
+    ns = eng.compact(f, tot, ids)
+    hsp = torch.full((ns + 3, 4), 0x2B2B2B2B, dtype=torch.int32, device="cuda")
+    st = torch.full((ns + 3,), 0xAB, dtype=torch.uint8, device="cuda")
+    eng.materialize(a, ids, ns, hsp, st)
+    sh = st.cpu().numpy()
+    assert set(np.unique(sh[:ns]).tolist()) <= {0, 1} and (sh[ns:] == 0xAB).all()
+    assert np.array_equal(sh[:ns], o["chunks"][0]["status"])
+
+
+def test_unaligned_buffers_and_out_of_range_anchors():
+    import torch
+    ref, qry = random_pair(14, 10_000, 10_000, plant=10, plant_len=(100, 400), identity=0.92)
+    p = params_of("11011")
+    o, R, qc = oracle_pass(ref, qry, p)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    want = o["chunks"][0]
+    n = want["anchors"].size
+    extra = np.asarray([(ref.size + 5) | (3 << 32), 7 | ((qry.size + 1) << 32),
+                        ref.size | (qry.size << 32), 0], np.uint64)
+    anchors = np.concatenate([want["anchors"], extra])
+    a = torch.from_numpy(anchors.view(np.int64)).cuda()
+    base = torch.zeros(anchors.size + 9, dtype=torch.uint8, device="cuda")
+    f = base[1:1 + anchors.size]  # 1-byte offset: unaligned flag buffer
+    eng.score_gate(a, anchors.size, f)
+    fo = oracle.gate(anchors, R.codes, qc, p["sub"], p["n_score"], p["xdrop"],
+                     oracle.keep_threshold(p["hsp_threshold"]))
+    assert np.array_equal(f.cpu().numpy(), fo)
+    ids = torch.empty(anchors.size, dtype=torch.int32, device="cuda")
+    ns = eng.compact(f, anchors.size, ids)
+    assert np.array_equal(ids[:ns].cpu().numpy().view(np.uint32), oracle.compact(fo))
+    # materialize out-of-range anchors directly: empty walks on both sides
+    bad_ids = torch.arange(n, n + 4, dtype=torch.int32, device="cuda")
+    hsp = torch.empty((4, 4), dtype=torch.int32, device="cuda")
+    st = torch.empty(4, dtype=torch.uint8, device="cuda")
+    eng.materialize(a, bad_ids, 4, hsp, st)
+    oh, ost = oracle.materialize(anchors, np.arange(n, n + 4, dtype=np.uint32), R.codes, qc,
+                                 p["sub"], p["n_score"], p["xdrop"],
+                                 oracle.keep_threshold(p["hsp_threshold"]))
+    assert np.array_equal(st.cpu().numpy(), ost)
+    gh = hsp.cpu().numpy().view(oracle.HSP_DTYPE).reshape(-1)
+    assert np.array_equal(gh[:3], oh[:3])
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_config_full_parity(cfg):
+    w = build(cfg)
+    p = w.params()
+    o, _, _ = oracle_pass(w.ref, w.query, p)
+    r = gpu_full_pass(engine(p), w.ref, w.query)
+    assert_pass_equal(r, o)
+    print(f"config {cfg}: anchors {r['total']} survivors {r['n_surv']} accepted {r['n_acc']}")

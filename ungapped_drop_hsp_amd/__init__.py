@@ -1,0 +1,268 @@
+"""Python binding of libhspz, the MI355X seed-and-extend hot path.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI declared
+in ``include/hspz.h``.  PyTorch supplies device memory (tensors) and streams.  Importing
+this package raises if ``libhspz.so`` has not been built -- there is no fallback.
+
+Names follow the C ABI without the ``hspz_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhspz.so")
+
+HSPZ_OK = 0
+ERRORS = {-1: "HSPZ_E_INVALID", -2: "HSPZ_E_OVERFLOW", -3: "HSPZ_E_CAPACITY",
+          -4: "HSPZ_E_NOMEM", -5: "HSPZ_E_HIP", -6: "HSPZ_E_STATE"}
+
+SEGMENT_PAIR = np.dtype([("ref_start", "<u4"), ("query_start", "<u4"), ("len", "<u4"),
+                         ("score", "<i4")])
+
+# Every symbol include/hspz.h declares.
+ABI_SYMBOLS = (
+    "hspz_engine_create", "hspz_engine_destroy", "hspz_keep_threshold", "hspz_last_error",
+    "hspz_upload_reference", "hspz_upload_query", "hspz_num_seeds", "hspz_seed_range",
+    "hspz_plan", "hspz_get_chunk", "hspz_find_hits", "hspz_score_gate", "hspz_compact",
+    "hspz_materialize", "hspz_compact_hsps", "hspz_get_seeds", "hspz_get_plan_arrays",
+    "hspz_debug_plan_counts", "hspz_debug_walk_steps",
+)
+
+
+class HspzError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("seed_pattern", ctypes.c_char_p), ("sub", ctypes.c_int32 * 16),
+                ("n_score", ctypes.c_int32), ("xdrop", ctypes.c_int32),
+                ("hsp_threshold", ctypes.c_int32), ("expand_mode", ctypes.c_int32),
+                ("max_hits", ctypes.c_uint64), ("chunk_walk", ctypes.c_int32),
+                ("device", ctypes.c_int32)]
+
+
+class Chunk(ctypes.Structure):
+    _fields_ = [("seed_lo", ctypes.c_uint64), ("seed_hi", ctypes.c_uint64),
+                ("hit_lo", ctypes.c_uint64), ("n_hits", ctypes.c_uint64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python ungapped_drop_hsp_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, U64, I32, U32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_uint32
+    PU64, PU32 = ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint32)
+    sig = {
+        "hspz_engine_create": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.POINTER(P)]),
+        "hspz_engine_destroy": (ctypes.c_int, [P]),
+        "hspz_keep_threshold": (I32, [P]),
+        "hspz_last_error": (ctypes.c_char_p, [P]),
+        "hspz_upload_reference": (ctypes.c_int, [P, P, U64, P]),
+        "hspz_upload_query": (ctypes.c_int, [P, P, U64, I32, P]),
+        "hspz_num_seeds": (U64, [P]),
+        "hspz_seed_range": (ctypes.c_int, [P, U64, U64, PU64, PU64]),
+        "hspz_plan": (ctypes.c_int, [P, U64, U64, P, PU64, PU32]),
+        "hspz_get_chunk": (ctypes.c_int, [P, U32, ctypes.POINTER(Chunk)]),
+        "hspz_find_hits": (ctypes.c_int, [P, U32, P, U64, P]),
+        "hspz_score_gate": (ctypes.c_int, [P, P, U64, P, P]),
+        "hspz_compact": (ctypes.c_int, [P, P, U64, P, U64, PU64, P]),
+        "hspz_materialize": (ctypes.c_int, [P, P, P, U64, P, P, P]),
+        "hspz_compact_hsps": (ctypes.c_int, [P, P, P, U64, P, U64, PU64, P]),
+        "hspz_get_seeds": (ctypes.c_int, [P, U64, U64, P, P]),
+        "hspz_get_plan_arrays": (ctypes.c_int, [P, P, P]),
+        "hspz_debug_plan_counts": (ctypes.c_int, [P, P, U64, P, PU64, PU32]),
+        "hspz_debug_walk_steps": (ctypes.c_int, [P, P, U64, PU64, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    """Device pointer of a torch tensor, or a raw integer address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not x.is_cuda:
+            raise ValueError("expected a device tensor")
+        if not x.is_contiguous():
+            raise ValueError("expected a contiguous tensor")
+        return x.data_ptr()
+    raise TypeError(f"cannot take a device pointer of {type(x)}")
+
+
+def _nbytes(x) -> Optional[int]:
+    if hasattr(x, "data_ptr"):
+        return x.numel() * x.element_size()
+    return None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _host_bytes(seq) -> np.ndarray:
+    if isinstance(seq, (bytes, bytearray)):
+        return np.frombuffer(bytes(seq), dtype=np.uint8)
+    a = np.ascontiguousarray(seq)
+    if a.dtype != np.uint8:
+        raise TypeError("sequence must be bytes or a uint8 array")
+    return a
+
+
+class Engine:
+    """One engine: a reference index and one query strand on one device."""
+
+    def __init__(self, seed_pattern: str, sub, n_score: int, xdrop: int, hsp_threshold: int,
+                 max_hits: int = 0, expand_mode: int = 0, chunk_walk: int = 0,
+                 device: int = 0):
+        self._pat = seed_pattern.encode()
+        m = np.asarray(sub, dtype=np.int32).reshape(-1)
+        if m.size != 16:
+            raise ValueError("sub must hold 16 entries (4x4, ref row, query column)")
+        p = Params(self._pat, (ctypes.c_int32 * 16)(*m.tolist()), n_score, xdrop,
+                   hsp_threshold, expand_mode, max_hits, chunk_walk, device)
+        h = ctypes.c_void_p()
+        rc = _lib.hspz_engine_create(ctypes.byref(p), ctypes.byref(h))
+        if rc != HSPZ_OK:
+            raise HspzError(rc, _lib.hspz_last_error(None).decode())
+        self._h = h
+        self.device = device
+
+    # -- plumbing
+    def _check(self, rc: int):
+        if rc != HSPZ_OK:
+            raise HspzError(rc, _lib.hspz_last_error(self._h).decode())
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.hspz_engine_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # -- ABI
+    @property
+    def keep_threshold(self) -> int:
+        return int(_lib.hspz_keep_threshold(self._h))
+
+    def last_error(self) -> str:
+        return _lib.hspz_last_error(self._h).decode()
+
+    def upload_reference(self, seq, stream=None):
+        a = _host_bytes(seq)
+        self._check(_lib.hspz_upload_reference(self._h, a.ctypes.data, a.size, _stream(stream)))
+
+    def upload_query(self, seq, strand: int = 0, stream=None):
+        a = _host_bytes(seq)
+        self._check(_lib.hspz_upload_query(self._h, a.ctypes.data, a.size, strand,
+                                           _stream(stream)))
+
+    def num_seeds(self) -> int:
+        return int(_lib.hspz_num_seeds(self._h))
+
+    def seed_range(self, pos_lo: int, pos_hi: int) -> Tuple[int, int]:
+        lo, hi = ctypes.c_uint64(), ctypes.c_uint64()
+        self._check(_lib.hspz_seed_range(self._h, pos_lo, pos_hi, ctypes.byref(lo),
+                                         ctypes.byref(hi)))
+        return lo.value, hi.value
+
+    def plan(self, seed_lo: int, seed_hi: int, stream=None) -> Tuple[int, int]:
+        tot, nch = ctypes.c_uint64(), ctypes.c_uint32()
+        self._check(_lib.hspz_plan(self._h, seed_lo, seed_hi, _stream(stream),
+                                   ctypes.byref(tot), ctypes.byref(nch)))
+        return tot.value, nch.value
+
+    def get_chunk(self, i: int) -> Dict[str, int]:
+        c = Chunk()
+        self._check(_lib.hspz_get_chunk(self._h, i, ctypes.byref(c)))
+        return dict(seed_lo=c.seed_lo, seed_hi=c.seed_hi, hit_lo=c.hit_lo, n_hits=c.n_hits)
+
+    def find_hits(self, chunk: int, anchors, cap: Optional[int] = None, stream=None):
+        if cap is None:
+            cap = _nbytes(anchors) // 8
+        self._check(_lib.hspz_find_hits(self._h, chunk, _ptr(anchors), cap, _stream(stream)))
+
+    def score_gate(self, anchors, n: int, flags, stream=None):
+        self._check(_lib.hspz_score_gate(self._h, _ptr(anchors), n, _ptr(flags),
+                                         _stream(stream)))
+
+    def compact(self, flags, n: int, ids, cap: Optional[int] = None, stream=None) -> int:
+        if cap is None:
+            cap = _nbytes(ids) // 4 if ids is not None else 0
+        out = ctypes.c_uint64()
+        self._check(_lib.hspz_compact(self._h, _ptr(flags), n, _ptr(ids), cap, ctypes.byref(out),
+                                      _stream(stream)))
+        return out.value
+
+    def materialize(self, anchors, ids, n_surv: int, hsp, status, stream=None):
+        self._check(_lib.hspz_materialize(self._h, _ptr(anchors), _ptr(ids), n_surv, _ptr(hsp),
+                                          _ptr(status), _stream(stream)))
+
+    def compact_hsps(self, hsp, status, n: int, out, cap: Optional[int] = None,
+                     stream=None) -> int:
+        if cap is None:
+            cap = _nbytes(out) // 16 if out is not None else 0
+        res = ctypes.c_uint64()
+        self._check(_lib.hspz_compact_hsps(self._h, _ptr(hsp), _ptr(status), n, _ptr(out), cap,
+                                           ctypes.byref(res), _stream(stream)))
+        return res.value
+
+    def get_seeds(self, lo: int, hi: int) -> Tuple[np.ndarray, np.ndarray]:
+        k = np.empty(max(hi - lo, 0), np.uint32)
+        q = np.empty(max(hi - lo, 0), np.uint32)
+        self._check(_lib.hspz_get_seeds(self._h, lo, hi, k.ctypes.data, q.ctypes.data))
+        return k, q
+
+    def get_plan_arrays(self, n: int) -> Tuple[np.ndarray, np.ndarray]:
+        c = np.empty(max(n, 1), np.uint32)
+        p = np.empty(max(n, 1), np.uint32)
+        self._check(_lib.hspz_get_plan_arrays(self._h, c.ctypes.data, p.ctypes.data))
+        return c[:n], p[:n]
+
+    def debug_plan_counts(self, counts, stream=None) -> Tuple[int, int]:
+        c = np.ascontiguousarray(counts, dtype=np.uint32)
+        tot, nch = ctypes.c_uint64(), ctypes.c_uint32()
+        self._check(_lib.hspz_debug_plan_counts(self._h, c.ctypes.data, c.size, _stream(stream),
+                                                ctypes.byref(tot), ctypes.byref(nch)))
+        return tot.value, nch.value
+
+    def debug_walk_steps(self, anchors, n: int, stream=None) -> int:
+        tot = ctypes.c_uint64()
+        self._check(_lib.hspz_debug_walk_steps(self._h, _ptr(anchors), n, ctypes.byref(tot),
+                                               _stream(stream)))
+        return tot.value

@@ -1,0 +1,711 @@
+// Host side of libhspz: parameter validation, the keep threshold, reference index and
+// query seed construction, the plan (prefix and MAX_HITS chunk walk) and the C ABI.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "hspz_internal.h"
+
+#define HSPZ_API extern "C" __attribute__((visibility("default")))
+
+namespace hspz {
+
+namespace {
+
+thread_local std::string g_create_error;
+
+int fail(Engine *e, int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (e) e->err = buf;
+    else g_create_error = buf;
+    return code;
+}
+
+#define HIP_TRY(e, call)                                                              \
+    do {                                                                              \
+        hipError_t _st = (call);                                                      \
+        if (_st != hipSuccess)                                                        \
+            return fail((e), HSPZ_E_HIP, "%s failed: %s", #call, hipGetErrorString(_st)); \
+    } while (0)
+
+template <class T>
+void dfree(T *&p) {
+    if (p) (void)hipFree(p);
+    p = nullptr;
+}
+
+template <class T>
+int dalloc(Engine *e, T *&p, uint64_t count) {
+    dfree(p);
+    const size_t bytes = (size_t)std::max<uint64_t>(count, 1) * sizeof(T);
+    hipError_t st = hipMalloc(reinterpret_cast<void **>(&p), bytes);
+    if (st != hipSuccess) {
+        p = nullptr;
+        return fail(e, HSPZ_E_NOMEM, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(st));
+    }
+    return HSPZ_OK;
+}
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// A,C,G,T in either case -> 0..3, anything else -> N.
+inline uint8_t code_of(uint8_t c) {
+    switch (c) {
+    case 'A': case 'a': return 0;
+    case 'C': case 'c': return 1;
+    case 'G': case 'g': return 2;
+    case 'T': case 't': return 3;
+    default: return kCodeN;
+    }
+}
+
+// Least int32 t with (float)t >= (float)K: the integer form of the single-precision keep
+// comparison.  Searched from K downward and upward; float rounding moves it by at most
+// one ulp of K, so the loops are short.
+int32_t keep_threshold(int32_t K) {
+    const float fk = (float)K;
+    int64_t t = K;
+    while (t > INT32_MIN && (float)(int32_t)(t - 1) >= fk) t--;
+    while ((float)(int32_t)t < fk) t++;
+    return (int32_t)t;
+}
+
+// Packed keys of every window of `codes` (0xFFFFFFFF where a care position is N or the
+// window does not fit).
+void window_keys(const std::vector<uint8_t> &codes, const std::vector<int32_t> &care, int span,
+                 std::vector<uint32_t> &keys) {
+    const uint64_t n = codes.size();
+    const uint64_t nw = n >= (uint64_t)span ? n - span + 1 : 0;
+    keys.assign(nw, 0xFFFFFFFFu);
+    const int w = (int)care.size();
+    for (uint64_t p = 0; p < nw; p++) {
+        uint32_t k = 0;
+        int i = 0;
+        for (; i < w; i++) {
+            const uint8_t c = codes[p + care[i]];
+            if (c > 3) break;
+            k = (k << 2) | c;
+        }
+        if (i == w) keys[p] = k;
+    }
+}
+
+int upload_padded(Engine *e, uint8_t *&dst, const std::vector<uint8_t> &codes, int shift,
+                  hipStream_t s) {
+    const uint64_t n = codes.size();
+    std::vector<uint8_t> buf(n + 2 * kPad, (uint8_t)(kCodeEdge << shift));
+    for (uint64_t i = 0; i < n; i++) buf[kPad + i] = (uint8_t)(codes[i] << shift);
+    int rc = dalloc(e, dst, buf.size());
+    if (rc) return rc;
+    HIP_TRY(e, hipMemcpyAsync(dst, buf.data(), buf.size(), hipMemcpyHostToDevice, s));
+    HIP_TRY(e, hipStreamSynchronize(s));
+    return HSPZ_OK;
+}
+
+// Shared by hspz_plan and hspz_debug_plan_counts once counts and block-local prefixes
+// are on the device: 64-bit host scan of the block sums, refusal, add-back, chunk walk.
+int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint32_t *n_chunks) {
+    const uint64_t nblk = (n + kScanBlock - 1) / kScanBlock;
+    std::vector<uint64_t> blk(nblk);
+    if (nblk) {
+        HIP_TRY(e, hipMemcpyAsync(blk.data(), e->d_blksum, nblk * sizeof(uint64_t),
+                                  hipMemcpyDeviceToHost, s));
+        HIP_TRY(e, hipStreamSynchronize(s));
+    }
+    // exclusive block offsets; inclusive block prefix for the boundary search
+    std::vector<uint64_t> incl(nblk);
+    std::vector<uint32_t> off(nblk);
+    uint64_t acc = 0;
+    for (uint64_t b = 0; b < nblk; b++) {
+        off[b] = (uint32_t)acc;
+        acc += blk[b];
+        incl[b] = acc;
+        if (acc > 0xFFFFFFFFull) {
+            e->has_plan = false;
+            return fail(e, HSPZ_E_OVERFLOW,
+                        "batch total exceeds the 32-bit hit index (%llu hits or more); refused",
+                        (unsigned long long)acc);
+        }
+    }
+    const uint64_t total = acc;
+    if (nblk) {
+        HIP_TRY(e, hipMemcpyAsync(e->d_blkoff, off.data(), nblk * sizeof(uint32_t),
+                                  hipMemcpyHostToDevice, s));
+        HIP_TRY(e, launch_add_offsets(e->d_prefix, n, e->d_blkoff, s));
+    }
+
+    // Lower-bound walk ("C. Hit discovery", C.3).
+    e->chunks.clear();
+    const uint64_t MAX = e->params.max_hits;
+    std::vector<uint32_t> full;  // whole prefix (chunk_walk = 1)
+    if (e->params.chunk_walk == 1 && total > 0 && MAX != 0 && total > MAX) {
+        full.resize(n);
+        HIP_TRY(e, hipMemcpyAsync(full.data(), e->d_prefix, n * sizeof(uint32_t),
+                                  hipMemcpyDeviceToHost, s));
+    }
+    HIP_TRY(e, hipStreamSynchronize(s));
+    std::vector<uint32_t> blkvals(kScanBlock);
+    uint64_t s0 = 0, H = 0;
+    while (total > 0 && s0 < n) {
+        hspz_chunk c{};
+        c.seed_lo = e->batch_lo + s0;
+        c.hit_lo = H;
+        if (MAX == 0 || total - H <= MAX) {
+            c.seed_hi = e->batch_lo + n - 1;
+            c.n_hits = total - H;
+            e->chunks.push_back(c);
+            break;
+        }
+        const uint64_t target = H + MAX;  // first prefix >= target ends the chunk
+        uint64_t eidx;
+        if (!full.empty()) {
+            eidx = (uint64_t)(std::lower_bound(full.begin() + s0, full.end(), target) -
+                              full.begin());
+        } else {
+            const uint64_t b =
+                (uint64_t)(std::lower_bound(incl.begin(), incl.end(), target) - incl.begin());
+            const uint64_t lo = b * kScanBlock, cnt = std::min<uint64_t>(kScanBlock, n - lo);
+            HIP_TRY(e, hipMemcpy(blkvals.data(), e->d_prefix + lo, cnt * sizeof(uint32_t),
+                                 hipMemcpyDeviceToHost));
+            eidx = lo + (uint64_t)(std::lower_bound(blkvals.begin(), blkvals.begin() + cnt,
+                                                    target) - blkvals.begin());
+        }
+        if (eidx >= n || eidx < s0)
+            return fail(e, HSPZ_E_HIP, "chunk walk lost its boundary (internal error)");
+        const uint64_t Pe = !full.empty() ? full[eidx] : blkvals[eidx % kScanBlock];
+        c.seed_hi = e->batch_lo + eidx;
+        c.n_hits = Pe - H;
+        e->chunks.push_back(c);
+        H = Pe;
+        s0 = eidx + 1;
+    }
+    e->total = total;
+    e->has_plan = true;
+    *total_hits = total;
+    *n_chunks = (uint32_t)e->chunks.size();
+    return HSPZ_OK;
+}
+
+int ensure_batch(Engine *e, uint64_t n) {
+    if (n <= e->cap_batch && e->d_count) return HSPZ_OK;
+    const uint64_t cap = std::max<uint64_t>(n, 1);
+    const uint64_t nblk = (cap + kScanBlock - 1) / kScanBlock;
+    int rc;
+    if ((rc = dalloc(e, e->d_count, cap))) return rc;
+    if ((rc = dalloc(e, e->d_prefix, cap))) return rc;
+    if ((rc = dalloc(e, e->d_blksum, nblk))) return rc;
+    if ((rc = dalloc(e, e->d_blkoff, nblk))) return rc;
+    e->cap_batch = cap;
+    return HSPZ_OK;
+}
+
+int ensure_compact(Engine *e, uint64_t n) {
+    const uint64_t nblk = (n + kCompactBlock - 1) / kCompactBlock + 1;
+    if (nblk <= e->cap_cblk && e->d_cblk) return HSPZ_OK;
+    int rc = dalloc(e, e->d_cblk, nblk);
+    if (rc) return rc;
+    e->cap_cblk = nblk;
+    return HSPZ_OK;
+}
+
+int set_device(Engine *e) {
+    HIP_TRY(e, hipSetDevice(e->device));
+    return HSPZ_OK;
+}
+
+}  // namespace
+
+Engine::~Engine() {
+    (void)hipSetDevice(device);
+    dfree(d_end);
+    dfree(d_pos);
+    dfree(d_ref);
+    dfree(d_qry);
+    dfree(d_kmer);
+    dfree(d_qend);
+    dfree(d_count);
+    dfree(d_prefix);
+    dfree(d_blksum);
+    dfree(d_blkoff);
+    dfree(d_cblk);
+    dfree(d_ctotal);
+    if (h_pinned) (void)hipHostFree(h_pinned);
+}
+
+void Engine::free_plan() {
+    has_plan = false;
+    plan_expandable = false;
+    chunks.clear();
+    total = 0;
+}
+
+}  // namespace hspz
+
+using namespace hspz;
+
+HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
+    if (!out) return fail(nullptr, HSPZ_E_INVALID, "out is NULL");
+    *out = nullptr;
+    if (!p || !p->seed_pattern) return fail(nullptr, HSPZ_E_INVALID, "params or pattern NULL");
+    const size_t L = strlen(p->seed_pattern);
+    std::vector<int32_t> care;
+    for (size_t i = 0; i < L; i++) {
+        if (p->seed_pattern[i] == '1') care.push_back((int32_t)i);
+        else if (p->seed_pattern[i] != '0')
+            return fail(nullptr, HSPZ_E_INVALID, "seed pattern may hold only '0' and '1'");
+    }
+    if (L == 0 || L > 64 || care.empty() || care.size() > 14 || p->seed_pattern[0] != '1' ||
+        p->seed_pattern[L - 1] != '1')
+        return fail(nullptr, HSPZ_E_INVALID,
+                    "seed pattern must start and end with '1', weight 1..14, span <= 64");
+    for (int i = 0; i < 16; i++)
+        if (p->sub[i] > 10000 || p->sub[i] < -10000)
+            return fail(nullptr, HSPZ_E_INVALID, "|sub| must be <= 10000");
+    if (p->n_score > 10000 || p->n_score < -10000)
+        return fail(nullptr, HSPZ_E_INVALID, "|n_score| must be <= 10000");
+    if (p->xdrop < 0 || p->xdrop > 1000000)
+        return fail(nullptr, HSPZ_E_INVALID, "xdrop must be in 0..1000000");
+    if (p->hsp_threshold < 1) return fail(nullptr, HSPZ_E_INVALID, "hsp_threshold must be >= 1");
+    if (p->expand_mode < 0 || p->expand_mode > 2)
+        return fail(nullptr, HSPZ_E_INVALID, "expand_mode must be 0, 1 or 2");
+    if (p->chunk_walk < 0 || p->chunk_walk > 1)
+        return fail(nullptr, HSPZ_E_INVALID, "chunk_walk must be 0 or 1");
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev)
+        return fail(nullptr, HSPZ_E_INVALID, "device %d not available (%d devices)", p->device,
+                    ndev);
+
+    Engine *e = new (std::nothrow) Engine();
+    if (!e) return fail(nullptr, HSPZ_E_NOMEM, "engine allocation failed");
+    e->params = *p;
+    e->pattern = p->seed_pattern;
+    e->params.seed_pattern = e->pattern.c_str();
+    e->care = care;
+    e->span = (int)L;
+    e->weight = (int)care.size();
+    e->device = p->device;
+    e->T = keep_threshold(p->hsp_threshold);
+
+    // Score table indexed by ref*8 + query (codes 0..3, N = 4, edge = 5).
+    int32_t smax = std::max<int32_t>(p->n_score, 0);
+    for (int r = 0; r < 8; r++) {
+        for (int q = 0; q < 8; q++) {
+            int32_t v;
+            if (r == kCodeEdge || q == kCodeEdge || r > kCodeEdge || q > kCodeEdge)
+                v = -(p->xdrop + 1);
+            else if (r == kCodeN || q == kCodeN) v = p->n_score;
+            else v = p->sub[r * 4 + q];
+            e->sp.tab[(r << kRefShift) | q] = v;
+        }
+    }
+    for (int i = 0; i < 16; i++) smax = std::max(smax, p->sub[i]);
+    // Largest block B with (B - 1) * max score <= xdrop (see the gate kernel).
+    e->block_bases = 1;
+    for (int b : {8, 4, 2}) {
+        if ((int64_t)(b - 1) * smax <= p->xdrop) {
+            e->block_bases = b;
+            break;
+        }
+    }
+    e->sp.xdrop = p->xdrop;
+    e->sp.T = e->T;
+    int rc = set_device(e);
+    if (rc) {
+        g_create_error = e->err;
+        delete e;
+        return rc;
+    }
+    if (hipHostMalloc(reinterpret_cast<void **>(&e->h_pinned), 64 * sizeof(uint32_t)) !=
+            hipSuccess ||
+        dalloc(e, e->d_ctotal, 16) != HSPZ_OK) {
+        g_create_error = "pinned/device staging allocation failed";
+        delete e;
+        return HSPZ_E_NOMEM;
+    }
+    *out = reinterpret_cast<hspz_engine *>(e);
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_engine_destroy(hspz_engine *engine) {
+    delete reinterpret_cast<Engine *>(engine);
+    return HSPZ_OK;
+}
+
+HSPZ_API int32_t hspz_keep_threshold(const hspz_engine *engine) {
+    return engine ? reinterpret_cast<const Engine *>(engine)->T : 0;
+}
+
+HSPZ_API const char *hspz_last_error(const hspz_engine *engine) {
+    if (!engine) return g_create_error.c_str();
+    return reinterpret_cast<const Engine *>(engine)->err.c_str();
+}
+
+HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                                   void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!h_ascii && len) return fail(e, HSPZ_E_INVALID, "reference pointer is NULL");
+    if (len >= 0xFFFFFFFFull - kPad) return fail(e, HSPZ_E_INVALID, "reference too long");
+    int rc = set_device(e);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    e->free_plan();
+    e->has_ref = false;
+
+    std::vector<uint8_t> codes(len);
+    for (uint64_t i = 0; i < len; i++) codes[i] = code_of(h_ascii[i]);
+    std::vector<uint32_t> keys;
+    window_keys(codes, e->care, e->span, keys);
+    // Counting sort by key; positions ascend within a bucket because windows are visited
+    // in ascending position.
+    const uint64_t nb = 1ull << (2 * e->weight);
+    std::vector<uint32_t> end(nb + 1, 0);
+    for (uint32_t k : keys)
+        if (k != 0xFFFFFFFFu) end[k + 1]++;
+    for (uint64_t k = 0; k < nb; k++) end[k + 1] += end[k];
+    const uint64_t nwin = end[nb];
+    std::vector<uint32_t> pos(std::max<uint64_t>(nwin, 1));
+    {
+        std::vector<uint32_t> cur(end.begin(), end.end() - 1);
+        for (uint64_t p = 0; p < keys.size(); p++)
+            if (keys[p] != 0xFFFFFFFFu) pos[cur[keys[p]]++] = (uint32_t)(p + e->span);
+    }
+    if ((rc = dalloc(e, e->d_end, nb + 1))) return rc;
+    if ((rc = dalloc(e, e->d_pos, std::max<uint64_t>(nwin, 1)))) return rc;
+    HIP_TRY(e, hipMemcpyAsync(e->d_end, end.data(), (nb + 1) * sizeof(uint32_t),
+                              hipMemcpyHostToDevice, s));
+    HIP_TRY(e, hipMemcpyAsync(e->d_pos, pos.data(), std::max<uint64_t>(nwin, 1) * sizeof(uint32_t),
+                              hipMemcpyHostToDevice, s));
+    if ((rc = upload_padded(e, e->d_ref, codes, kRefShift, s))) return rc;
+    e->n_ref = len;
+    e->sp.n_ref = (uint32_t)len;
+    e->has_ref = true;
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                               int32_t strand, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!h_ascii && len) return fail(e, HSPZ_E_INVALID, "query pointer is NULL");
+    if (strand != 0 && strand != 1) return fail(e, HSPZ_E_INVALID, "strand must be 0 or 1");
+    if (len >= 0xFFFFFFFFull - kPad) return fail(e, HSPZ_E_INVALID, "query too long");
+    int rc = set_device(e);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    e->free_plan();
+    e->has_qry = false;
+
+    std::vector<uint8_t> codes(len);
+    for (uint64_t i = 0; i < len; i++) {
+        if (strand == 0) {
+            codes[i] = code_of(h_ascii[i]);
+        } else {
+            const uint8_t c = code_of(h_ascii[len - 1 - i]);
+            codes[i] = c < 4 ? (uint8_t)(3 - c) : kCodeN;
+        }
+    }
+    std::vector<uint32_t> keys;
+    window_keys(codes, e->care, e->span, keys);
+    std::vector<uint32_t> kmer, qend;
+    e->h_seed_start.clear();
+    for (uint64_t p = 0; p < keys.size(); p++) {
+        if (keys[p] == 0xFFFFFFFFu) continue;
+        kmer.push_back(keys[p]);
+        qend.push_back((uint32_t)(p + e->span));
+        e->h_seed_start.push_back((uint32_t)p);
+    }
+    const uint64_t ns = kmer.size();
+    if ((rc = dalloc(e, e->d_kmer, ns))) return rc;
+    if ((rc = dalloc(e, e->d_qend, ns))) return rc;
+    if (ns) {
+        HIP_TRY(e, hipMemcpyAsync(e->d_kmer, kmer.data(), ns * sizeof(uint32_t),
+                                  hipMemcpyHostToDevice, s));
+        HIP_TRY(e, hipMemcpyAsync(e->d_qend, qend.data(), ns * sizeof(uint32_t),
+                                  hipMemcpyHostToDevice, s));
+    }
+    if ((rc = upload_padded(e, e->d_qry, codes, 0, s))) return rc;
+    e->n_qry = len;
+    e->sp.n_qry = (uint32_t)len;
+    e->n_seeds = ns;
+    e->strand = strand;
+    e->has_qry = true;
+    return HSPZ_OK;
+}
+
+HSPZ_API uint64_t hspz_num_seeds(const hspz_engine *engine) {
+    const Engine *e = reinterpret_cast<const Engine *>(engine);
+    return (e && e->has_qry) ? e->n_seeds : 0;
+}
+
+HSPZ_API int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
+                             uint64_t *seed_lo, uint64_t *seed_hi) {
+    const Engine *ce = reinterpret_cast<const Engine *>(engine);
+    Engine *e = const_cast<Engine *>(ce);
+    if (!e) return HSPZ_E_INVALID;
+    if (!seed_lo || !seed_hi) return fail(e, HSPZ_E_INVALID, "NULL output");
+    if (!e->has_qry) return fail(e, HSPZ_E_STATE, "no query uploaded");
+    const auto &v = e->h_seed_start;
+    auto lb = [&](uint64_t x) {
+        if (x > 0xFFFFFFFFull) return (uint64_t)v.size();
+        return (uint64_t)(std::lower_bound(v.begin(), v.end(), (uint32_t)x) - v.begin());
+    };
+    *seed_lo = lb(pos_lo);
+    *seed_hi = std::max(*seed_lo, lb(pos_hi));
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
+                       uint64_t *total_hits, uint32_t *n_chunks) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!total_hits || !n_chunks) return fail(e, HSPZ_E_INVALID, "NULL output");
+    *total_hits = 0;
+    *n_chunks = 0;
+    if (!e->has_ref || !e->has_qry)
+        return fail(e, HSPZ_E_STATE, "plan needs an uploaded reference and query");
+    if (seed_lo > seed_hi || seed_hi > e->n_seeds)
+        return fail(e, HSPZ_E_INVALID, "seed range [%llu, %llu) outside 0..%llu",
+                    (unsigned long long)seed_lo, (unsigned long long)seed_hi,
+                    (unsigned long long)e->n_seeds);
+    int rc = set_device(e);
+    if (rc) return rc;
+    e->free_plan();
+    hipStream_t s = as_stream(stream);
+    const uint64_t n = seed_hi - seed_lo;
+    if ((rc = ensure_batch(e, n))) return rc;
+    e->batch_lo = seed_lo;
+    e->batch_n = n;
+    HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_count,
+                                 e->d_prefix, e->d_blksum, s));
+    rc = finish_plan(e, n, s, total_hits, n_chunks);
+    if (rc) {
+        *total_hits = 0;
+        *n_chunks = 0;
+        return rc;
+    }
+    e->plan_expandable = true;
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64_t n,
+                                    void *stream, uint64_t *total_hits, uint32_t *n_chunks) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!total_hits || !n_chunks || (!h_counts && n))
+        return fail(e, HSPZ_E_INVALID, "NULL argument");
+    *total_hits = 0;
+    *n_chunks = 0;
+    int rc = set_device(e);
+    if (rc) return rc;
+    e->free_plan();
+    hipStream_t s = as_stream(stream);
+    if ((rc = ensure_batch(e, n))) return rc;
+    e->batch_lo = 0;
+    e->batch_n = n;
+    if (n) {
+        // counts are staged through the prefix buffer, then scanned into place
+        HIP_TRY(e, hipMemcpyAsync(e->d_count, h_counts, n * sizeof(uint32_t),
+                                  hipMemcpyHostToDevice, s));
+        HIP_TRY(e, launch_count_scan(nullptr, e->d_count, n, nullptr, e->d_count, e->d_prefix,
+                                     e->d_blksum, s));
+    }
+    rc = finish_plan(e, n, s, total_hits, n_chunks);
+    if (rc) {
+        *total_hits = 0;
+        *n_chunks = 0;
+    }
+    return rc;
+}
+
+HSPZ_API int hspz_get_chunk(const hspz_engine *engine, uint32_t i, hspz_chunk *out) {
+    Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
+    if (!e) return HSPZ_E_INVALID;
+    if (!out) return fail(e, HSPZ_E_INVALID, "NULL output");
+    if (!e->has_plan) return fail(e, HSPZ_E_STATE, "no plan");
+    if (i >= e->chunks.size()) return fail(e, HSPZ_E_INVALID, "chunk %u out of range", i);
+    *out = e->chunks[i];
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts,
+                                  uint32_t *h_prefix) {
+    Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_plan) return fail(e, HSPZ_E_STATE, "no plan");
+    int rc = set_device(e);
+    if (rc) return rc;
+    if (e->batch_n) {
+        if (h_counts)
+            HIP_TRY(e, hipMemcpy(h_counts, e->d_count, e->batch_n * sizeof(uint32_t),
+                                 hipMemcpyDeviceToHost));
+        if (h_prefix)
+            HIP_TRY(e, hipMemcpy(h_prefix, e->d_prefix, e->batch_n * sizeof(uint32_t),
+                                 hipMemcpyDeviceToHost));
+    }
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi,
+                            uint32_t *h_kmer, uint32_t *h_q_end) {
+    Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_qry) return fail(e, HSPZ_E_STATE, "no query uploaded");
+    if (lo > hi || hi > e->n_seeds) return fail(e, HSPZ_E_INVALID, "seed range out of bounds");
+    int rc = set_device(e);
+    if (rc) return rc;
+    if (hi > lo) {
+        if (h_kmer)
+            HIP_TRY(e, hipMemcpy(h_kmer, e->d_kmer + lo, (hi - lo) * sizeof(uint32_t),
+                                 hipMemcpyDeviceToHost));
+        if (h_q_end)
+            HIP_TRY(e, hipMemcpy(h_q_end, e->d_qend + lo, (hi - lo) * sizeof(uint32_t),
+                                 hipMemcpyDeviceToHost));
+    }
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
+                            uint64_t cap, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_plan || !e->plan_expandable)
+        return fail(e, HSPZ_E_STATE, "find_hits needs a plan from hspz_plan");
+    if (chunk >= e->chunks.size()) return fail(e, HSPZ_E_INVALID, "chunk %u out of range", chunk);
+    const hspz_chunk &c = e->chunks[chunk];
+    if (cap < c.n_hits)
+        return fail(e, HSPZ_E_CAPACITY, "anchor buffer holds %llu, chunk needs %llu",
+                    (unsigned long long)cap, (unsigned long long)c.n_hits);
+    if (!d_anchors && c.n_hits) return fail(e, HSPZ_E_INVALID, "anchor buffer is NULL");
+    int rc = set_device(e);
+    if (rc) return rc;
+    const uint64_t ns = c.seed_hi - c.seed_lo + 1;
+    bool dense;
+    if (e->params.expand_mode == 1) dense = false;
+    else if (e->params.expand_mode == 2) dense = true;
+    else dense = c.n_hits >= 16 * ns;  // "C. Hit discovery", C.4 density rule
+    const uint64_t local = c.seed_lo - e->batch_lo;
+    HIP_TRY(e, launch_expand(dense, e->d_kmer + c.seed_lo, e->d_qend + c.seed_lo,
+                             e->d_prefix + local, ns, e->d_end, e->d_pos, (uint32_t)c.hit_lo,
+                             d_anchors, as_stream(stream)));
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                             uint8_t *d_flags, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_ref || !e->has_qry)
+        return fail(e, HSPZ_E_STATE, "score_gate needs an uploaded reference and query");
+    if (n >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n must be < 2^32");
+    if (n && (!d_anchors || !d_flags)) return fail(e, HSPZ_E_INVALID, "NULL buffer");
+    int rc = set_device(e);
+    if (rc) return rc;
+    HIP_TRY(e, launch_gate(e->block_bases, d_anchors, (uint32_t)n, d_flags, e->d_ref + kPad,
+                           e->d_qry + kPad, e->sp, as_stream(stream)));
+    return HSPZ_OK;
+}
+
+static int compact_common(Engine *e, const uint8_t *d_flags, uint64_t n, uint32_t *ids,
+                          const hspz_segment_pair *rin, hspz_segment_pair *rout, uint64_t cap,
+                          uint64_t *n_out, hipStream_t s) {
+    if (n >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n must be < 2^32");
+    if (n && !d_flags) return fail(e, HSPZ_E_INVALID, "NULL flags");
+    int rc = set_device(e);
+    if (rc) return rc;
+    if ((rc = ensure_compact(e, n))) return rc;
+    const uint32_t c32 = (uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull);
+    HIP_TRY(e, launch_compact(d_flags, (uint32_t)n, e->d_cblk, e->d_ctotal, ids, rin, rout, c32, s));
+    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_ctotal, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(e, hipStreamSynchronize(s));
+    const uint64_t total = e->h_pinned[0];
+    if (total > cap)
+        return fail(e, HSPZ_E_CAPACITY, "%llu selected, capacity %llu",
+                    (unsigned long long)total, (unsigned long long)cap);
+    *n_out = total;
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n,
+                          uint32_t *d_ids, uint64_t cap, uint64_t *n_out, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!n_out) return fail(e, HSPZ_E_INVALID, "NULL n_out");
+    *n_out = 0;
+    if (!d_ids && cap) return fail(e, HSPZ_E_INVALID, "NULL ids with nonzero capacity");
+    int rc = compact_common(e, d_flags, n, d_ids, nullptr, nullptr, d_ids ? cap : 0, n_out,
+                            as_stream(stream));
+    if (rc) *n_out = 0;
+    return rc;
+}
+
+HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
+                              const uint32_t *d_ids, uint64_t n_surv, hspz_segment_pair *d_hsp,
+                              uint8_t *d_status, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_ref || !e->has_qry)
+        return fail(e, HSPZ_E_STATE, "materialize needs an uploaded reference and query");
+    if (n_surv >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n_surv must be < 2^32");
+    if (n_surv && (!d_anchors || !d_ids || !d_hsp || !d_status))
+        return fail(e, HSPZ_E_INVALID, "NULL buffer");
+    int rc = set_device(e);
+    if (rc) return rc;
+    HIP_TRY(e, launch_materialize(d_anchors, d_ids, (uint32_t)n_surv, d_hsp, d_status,
+                                  e->d_ref + kPad, e->d_qry + kPad, e->sp, as_stream(stream)));
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
+                               const uint8_t *d_status, uint64_t n, hspz_segment_pair *d_out,
+                               uint64_t cap, uint64_t *n_out, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!n_out) return fail(e, HSPZ_E_INVALID, "NULL n_out");
+    *n_out = 0;
+    if (n && !d_hsp) return fail(e, HSPZ_E_INVALID, "NULL records");
+    if (!d_out && cap) return fail(e, HSPZ_E_INVALID, "NULL output with nonzero capacity");
+    int rc = compact_common(e, d_status, n, nullptr, d_hsp, d_out, d_out ? cap : 0, n_out,
+                            as_stream(stream));
+    if (rc) *n_out = 0;
+    return rc;
+}
+
+HSPZ_API int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                                   uint64_t *total_steps, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!total_steps) return fail(e, HSPZ_E_INVALID, "NULL output");
+    *total_steps = 0;
+    if (!e->has_ref || !e->has_qry)
+        return fail(e, HSPZ_E_STATE, "walk statistics need an uploaded reference and query");
+    if (n >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n must be < 2^32");
+    if (n && !d_anchors) return fail(e, HSPZ_E_INVALID, "NULL anchors");
+    if (n == 0) return HSPZ_OK;
+    int rc = set_device(e);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    const uint32_t nb = walk_steps_blocks((uint32_t)n);
+    uint64_t *d_part = nullptr;
+    if ((rc = dalloc(e, d_part, nb))) return rc;
+    std::vector<uint64_t> part(nb);
+    hipError_t st = launch_walk_steps(d_anchors, (uint32_t)n, e->d_ref + kPad, e->d_qry + kPad,
+                                      e->sp, d_part, s);
+    if (st == hipSuccess)
+        st = hipMemcpyAsync(part.data(), d_part, nb * sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+    if (st == hipSuccess) st = hipStreamSynchronize(s);
+    dfree(d_part);
+    if (st != hipSuccess)
+        return fail(e, HSPZ_E_HIP, "walk statistics failed: %s", hipGetErrorString(st));
+    uint64_t t = 0;
+    for (uint64_t v : part) t += v;
+    *total_steps = t;
+    return HSPZ_OK;
+}

@@ -1,0 +1,119 @@
+// Internal declarations of libhspz: device data layout, engine state and the kernel
+// launchers.  Nothing here is part of the C ABI (include/hspz.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "hspz.h"
+
+namespace hspz {
+
+// ---- device layout -----------------------------------------------------------------
+// Sequences live on the device one byte per base, padded on both sides with kPad
+// "edge" bytes.  A reference byte holds code*8 and a query byte holds code, so OR-ing a
+// reference byte with a query byte gives the pair index ref*8 + query (0..45) into the
+// score table.  Codes: A,C,G,T = 0..3, N = 4, edge (outside the sequence) = 5.
+constexpr int kPad = 256;
+constexpr uint8_t kCodeN = 4;
+constexpr uint8_t kCodeEdge = 5;
+constexpr int kRefShift = 3;
+constexpr int kTabSize = 64;
+
+// Seeds per block of the device prefix scan.
+constexpr int kScanBlock = 1024;
+// Flag bytes per block of the compaction kernels.
+constexpr int kCompactBlock = 8192;
+
+// Score table and gate constants, passed by value to the X-drop kernels.  tab[ref*8 +
+// query] is the substitution score; any pair with N scores n_score; any pair with an
+// edge byte scores -(xdrop + 1), which ends a walk exactly where the sequence ends.
+struct ScoreParams {
+    int32_t tab[kTabSize];
+    int32_t xdrop;
+    int32_t T;
+    uint32_t n_ref;
+    uint32_t n_qry;
+};
+
+// ---- launchers (kernels in k_*.hip) --------------------------------------------------
+hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, uint64_t n,
+                             const uint32_t *end_tbl, uint32_t *count, uint32_t *prefix,
+                             uint64_t *blksum, hipStream_t s);
+hipError_t launch_add_offsets(uint32_t *prefix, uint64_t n, const uint32_t *blkoff,
+                              hipStream_t s);
+hipError_t launch_expand(bool dense, const uint32_t *kmer, const uint32_t *q_end,
+                         const uint32_t *prefix, uint64_t n_seeds, const uint32_t *end_tbl,
+                         const uint32_t *pos, uint32_t hit_lo, uint64_t *anchors,
+                         hipStream_t s);
+hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uint8_t *flags,
+                       const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
+                       hipStream_t s);
+hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint32_t n_surv,
+                              hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
+                              const uint8_t *qry, const ScoreParams &sp, hipStream_t s);
+// Stable compaction: count non-zero bytes per block, scan block counts on the device
+// (total -> *d_total), then emit either the indices (ids != nullptr) or the selected
+// 16-byte records (rec_in/rec_out).
+hipError_t launch_compact(const uint8_t *flags, uint32_t n, uint32_t *blk, uint32_t *d_total,
+                          uint32_t *ids, const hspz_segment_pair *rec_in,
+                          hspz_segment_pair *rec_out, uint32_t cap, hipStream_t s);
+
+hipError_t launch_walk_steps(const uint64_t *anchors, uint32_t n, const uint8_t *ref,
+                             const uint8_t *qry, const ScoreParams &sp, uint64_t *partial,
+                             hipStream_t s);
+uint32_t walk_steps_blocks(uint32_t n);
+
+// ---- engine ----------------------------------------------------------------------------
+struct Engine {
+    hspz_params params{};
+    std::string pattern;
+    std::vector<int32_t> care;
+    int span = 0, weight = 0;
+    int device = 0;
+    int32_t T = 0;
+    int block_bases = 8;
+    ScoreParams sp{};
+    std::string err;
+
+    // reference
+    bool has_ref = false;
+    uint64_t n_ref = 0;
+    uint32_t *d_end = nullptr;   // 4^w + 1 cumulative bucket ends, leading 0
+    uint32_t *d_pos = nullptr;   // reference end coordinate of every valid window
+    uint8_t *d_ref = nullptr;    // padded encoded reference (kPad edge bytes each side)
+
+    // query strand
+    bool has_qry = false;
+    uint64_t n_qry = 0;
+    int strand = 0;
+    uint8_t *d_qry = nullptr;
+    uint32_t *d_kmer = nullptr;
+    uint32_t *d_qend = nullptr;
+    uint64_t n_seeds = 0;
+    std::vector<uint32_t> h_seed_start;  // window start of every seed (ascending)
+
+    // plan of one batch
+    bool has_plan = false;
+    bool plan_expandable = false;
+    uint64_t batch_lo = 0, batch_n = 0, total = 0;
+    uint32_t *d_count = nullptr, *d_prefix = nullptr;
+    uint64_t *d_blksum = nullptr;
+    uint32_t *d_blkoff = nullptr;
+    uint64_t cap_batch = 0;
+    std::vector<hspz_chunk> chunks;
+
+    // compaction scratch
+    uint32_t *d_cblk = nullptr;
+    uint32_t *d_ctotal = nullptr;
+    uint64_t cap_cblk = 0;
+    uint32_t *h_pinned = nullptr;  // small pinned staging buffer (64 u32)
+
+    ~Engine();
+    void free_plan();
+};
+
+}  // namespace hspz

@@ -92,17 +92,16 @@ def _n_runs(rng: np.random.Generator, seq: np.ndarray, frac: float, lo: int, hi:
         return 0
     target = int(frac * seq.size)
     covered = np.zeros(seq.size, dtype=bool)
-    runs = 0
-    while int(covered.sum()) < target:
-        need = target - int(covered.sum())
-        batch = max(1, need // ((lo + hi) // 2) + 1)
+    runs, have = 0, 0
+    while have < target:
+        # draw about half of what is missing at a time, so the overshoot stays small
+        batch = max(1, (target - have) // (lo + hi) + 1)
         lens = rng.integers(lo, hi + 1, size=batch)
         starts = rng.integers(0, max(1, seq.size - hi), size=batch)
         for s, l in zip(starts, lens):
             covered[s:s + l] = True
-            runs += 1
-            if int(covered[: seq.size].sum()) >= target:
-                break
+        runs += batch
+        have = int(covered.sum())
     seq[covered] = ord("N")
     return runs
 
@@ -210,8 +209,8 @@ def _c2(rng):
 # (~0.02 % survivors), so lengths are log-uniform and identities skewed low.  The
 # numbers below were chosen by measuring the funnel (the design doc records the result).
 C3_MIX = dict(
-    n_homologs=20_000, len_lo=50, len_hi=10_000, len_shape=3.0,
-    id_lo=0.65, id_hi=0.95, id_shape=6.0,
+    n_homologs=20_000, len_lo=50, len_hi=10_000, len_shape=8.0,
+    id_lo=0.65, id_hi=0.95, id_shape=30.0,
     repeat_frac=0.15, families=2_000, fam_len=(300, 3000), frag_len=(30, 60),
     repeat_identity=0.80, n_frac=0.03,
 )
