@@ -1,0 +1,196 @@
+"""Benchmark of the seed-and-extend hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--cpu-seconds S]
+
+A step is one whole pass over the query's seeds on the forward strand: plan (hit counts,
+global prefix, MAX_HITS chunk cut), then for every chunk the backward expansion, the
+score gate, survivor compaction, exact materialization and accepted-record compaction,
+with the accepted records copied to the host.  The reference index, the query seeds and
+the encoded sequences are resident in HBM before the timed region starts.
+
+Prints one JSON line: raw anchors/s through the whole pass (``value``), HSPs/s, per-stage
+times from HIP events on the launch stream, the score gate's roofline figures and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "raw anchors/s through gate+materialize at 1 GPU; gate HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+CUS, LANES, CLOCK_GHZ = 256, 64, 2.4
+# One base step of an X-drop walk needs at least four 32-bit vector operations: the
+# substitution score lookup, the running-score add, the best/drawdown update and the
+# drop compare.  The ALU peak in base steps per second follows from the lane count.
+OPS_PER_BASE_STEP = 4
+ALU_PEAK_GSTEPS = CUS * LANES * CLOCK_GHZ / OPS_PER_BASE_STEP   # G base steps/s
+GATE_BYTES_PER_ANCHOR = 9       # 8-byte packed anchor read + 1-byte flag write
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload index (3 = 50 Mb x 50 Mb, the one the metric is quoted on)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU oracle sample budget in seconds (0 skips the CPU leg)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same pass.
+
+    Setup that the GPU side also does outside its timed region (encoding, the reference
+    index, the query's seed list) is untimed.  Then contiguous blocks of 20,000 query
+    seeds, spread evenly over the query in a fixed shuffled order, go through the
+    oracle's whole pass (counts, prefix, chunks, anchors, gate, compaction,
+    materialization) until the budget is spent.
+    """
+    import oracle
+    p = w.params()
+    R = oracle.Reference(w.ref, p["seed_pattern"])
+    qc = oracle.strand_codes(w.query, "+")
+    seeds = oracle.query_seeds(qc, p["seed_pattern"])
+    n = seeds[0].size
+    blk = 20_000
+    order = np.random.default_rng(0).permutation(max(n // blk, 1))
+    anchors = surv = acc = seeds_done = 0
+    t0 = time.perf_counter()
+    for b in order:
+        lo, hi = int(b) * blk, min(n, int(b) * blk + blk)
+        o = oracle.run_pass(R, qc, p, seed_range=(lo, hi), seeds=seeds)
+        anchors += o["total"]
+        seeds_done += hi - lo
+        for ch in o["chunks"]:
+            surv += ch["ids"].size
+            acc += ch["accepted"].size
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=anchors / el, unit="anchors/s", cores=1, kind="oracle",
+                sample=f"{seeds_done} of {n} query seeds in blocks of {blk} spread over the "
+                       f"query: {anchors} raw anchors, {surv} survivors, {acc} accepted, "
+                       f"{el:.1f} s single-threaded",
+                seconds=el)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the path needs no exchange between GPUs, so "
+              "no multi-GPU figure is produced (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(1)
+    import ungapped_drop_hsp_amd as h
+    from ungapped_drop_hsp_amd.pipeline import PassBuffers, StageTimer, run_pass
+    from workloads import build
+
+    t = time.perf_counter()
+    w = build(args.config)
+    gen_s = time.perf_counter() - t
+    p = w.params()
+    print(f"[bench] workload {w.name} generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    eng = h.Engine(seed_pattern=p["seed_pattern"], sub=p["sub"], n_score=p["n_score"],
+                   xdrop=p["xdrop"], hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"])
+    t = time.perf_counter()
+    eng.upload_reference(w.ref)
+    eng.upload_query(w.query, strand=0)
+    torch.cuda.synchronize()
+    upload_s = time.perf_counter() - t
+    ns = eng.num_seeds()
+    print(f"[bench] index + seeds uploaded in {upload_s:.1f} s ({ns} seeds)", file=sys.stderr,
+          flush=True)
+
+    bufs = PassBuffers(0)
+    for _ in range(args.warmup):
+        r = run_pass(eng, 0, ns, bufs)
+    torch.cuda.synchronize()
+    if args.warmup == 0:
+        r = None
+
+    timer = StageTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        r = run_pass(eng, 0, ns, bufs, timer=timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] {args.steps} timed steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    ms = timer.elapsed_ms()
+    ms_per_step = 1000.0 * wall / args.steps
+    anchors = r["total"]
+    value = anchors / (ms_per_step / 1000.0)
+    stage_ms = {k: sum(v) / args.steps for k, v in ms.items()}
+
+    # Gate roofline: compulsory bytes and exact base steps of the launches timed above.
+    gate_ms = ms["score_gate"]
+    gate_units = timer.units["score_gate"]
+    gate_launches = len(gate_ms)
+    gate_ms_avg = sum(gate_ms) / gate_launches
+    units_avg = sum(gate_units) / gate_launches
+    gate_gbs = GATE_BYTES_PER_ANCHOR * units_avg / (gate_ms_avg * 1e6)
+    steps_total = 0
+    for c in range(r["n_chunks"]):
+        ch = eng.get_chunk(c)
+        eng.find_hits(c, bufs.anchors)
+        steps_total += eng.debug_walk_steps(bufs.anchors, ch["n_hits"])
+    steps_per_anchor = steps_total / max(anchors, 1)
+    gate_gsteps = steps_per_anchor * units_avg / (gate_ms_avg * 1e6)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    out = dict(
+        metric=METRIC, value=value, unit="anchors/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="int32", data="synthetic",
+        config=dict(workload=w.name, ref_bp=int(w.ref.size), query_bp=int(w.query.size),
+                    strands="+", seed_pattern=p["seed_pattern"], xdrop=p["xdrop"],
+                    hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"], seeds=ns,
+                    raw_anchors=anchors, chunks=r["n_chunks"], survivors=r["n_surv"],
+                    accepted=r["n_acc"]),
+        hsps_per_s=r["n_acc"] / (ms_per_step / 1000.0),
+        stage_ms=stage_ms,
+        roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
+                      unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS, traffic=None,
+                      kernel="k_gate", launches_per_step=gate_launches,
+                      avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
+                      base_steps_per_anchor=steps_per_anchor),
+        gate_hbm=dict(achieved=gate_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=gate_gbs / HBM_PEAK_GBS, bytes_per_anchor=GATE_BYTES_PER_ANCHOR),
+        gate_anchors_per_s=units_avg / (gate_ms_avg / 1000.0),
+        setup_s=dict(generate=gen_s, upload=upload_s),
+    )
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -83,6 +83,10 @@ typedef struct {
  *  chunk_walk    0 = locate boundaries through block sums, copying one prefix block per
  *                boundary; 1 = copy the whole prefix and walk it.  Same chunks.
  *  device        HIP device ordinal the engine lives on.
+ *  gate_mode     0 = windowed score gate when it is exact for these parameters (eight-base
+ *                blocks, 16-bit pair scores), else the exact per-base walk; 1 = always the
+ *                per-base walk; 2 = always windowed (HSPZ_E_INVALID if not exact).  Every
+ *                mode writes the same flags ("D. Score gate", D.2).
  */
 typedef struct {
     const char *seed_pattern;
@@ -94,6 +98,7 @@ typedef struct {
     uint64_t max_hits;
     int32_t chunk_walk;
     int32_t device;
+    int32_t gate_mode;
 } hspz_params;
 
 /* Create an engine on params->device and compute the keep threshold T once: the least
@@ -220,6 +225,11 @@ int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64
  * temporary device buffer; synchronises stream.  Not part of a pass. */
 int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
                           uint64_t *total_steps, void *stream);
+
+/* How many anchors of the last hspz_score_gate call walked past the windowed gate's
+ * 128-base window and were decided by the exact per-base walk instead.  Synchronises
+ * stream.  Errors: HSPZ_E_STATE if that call did not take the window path. */
+int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_deferred, void *stream);
 
 #ifdef __cplusplus
 }

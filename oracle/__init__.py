@@ -277,15 +277,17 @@ def strand_codes(query_ascii, strand: str) -> np.ndarray:
 
 
 def run_pass(ref: Reference, qcodes: np.ndarray, params: Dict, *, seed_range=None,
-             stages=("anchors", "gate", "materialize")) -> Dict:
+             stages=("anchors", "gate", "materialize"), seeds=None) -> Dict:
     """All oracle steps for one strand and one batch of query seeds.
 
     ``seed_range`` = (lo, hi) half-open indices into the strand's seed list (all seeds by
-    default).  Returns the seeds, counts, prefix, chunks and, per chunk, anchors, flags,
-    survivor ids, records, status and accepted records.
+    default).  ``seeds`` = the (kmer, q_end, pos) triple that ``query_seeds`` returns for
+    ``qcodes``, when the caller already has it.  Returns the seeds, counts, prefix,
+    chunks and, per chunk, anchors, flags, survivor ids, records, status and accepted
+    records.
     """
     pat = params["seed_pattern"]
-    kmer, q_end, pos = query_seeds(qcodes, pat)
+    kmer, q_end, pos = seeds if seeds is not None else query_seeds(qcodes, pat)
     if seed_range is not None:
         lo, hi = seed_range
         kmer, q_end, pos = kmer[lo:hi], q_end[lo:hi], pos[lo:hi]

@@ -86,15 +86,77 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
-@pytest.mark.parametrize("expand_mode", [0, 1, 2])
-def test_random_pass_parity(case, expand_mode):
+@pytest.mark.parametrize("expand_mode,gate_mode", [(0, 0), (1, 1), (2, 2)],
+                         ids=["auto", "sparse-exact", "dense-window"])
+def test_random_pass_parity(case, expand_mode, gate_mode):
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
     ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
                            identity=ident, gc=gc, alphabet_noise=True)
     p = params_of(pat, max_hits=mx)
     o, _, _ = oracle_pass(ref, qry, p)
-    r = gpu_full_pass(engine(p, expand_mode=expand_mode), ref, qry)
+    r = gpu_full_pass(engine(p, expand_mode=expand_mode, gate_mode=gate_mode), ref, qry)
     assert_pass_equal(r, o)
+
+
+def _edge_anchors(rng, nr, nq, k):
+    """Anchors at and next to both ends of both sequences, plus random interior ones."""
+    r = list(rng.integers(0, nr + 1, size=k)) + [0, 1, 7, 8, 71, 72, 73, nr - 1, nr, nr - 48,
+                                                    nr - 47, nr - 8, 0, nr, 5, nr - 5]
+    q = list(rng.integers(0, nq + 1, size=k)) + [0, 1, 9, 8, 72, 71, 80, nq, nq - 1, nq - 47,
+                                                    nq - 48, nq - 9, nq, 0, nq - 5, 5]
+    return np.asarray([(a & 0xFFFFFFFF) | (b << 32) for a, b in zip(r, q)], np.uint64)
+
+
+@pytest.mark.parametrize("gate_mode", [1, 2])
+@pytest.mark.parametrize("seed", range(3))
+def test_gate_on_arbitrary_anchors(gate_mode, seed):
+    # anchors need not come from seeds: walks from every offset near both sequence ends,
+    # through N runs, and on planted homologs (long walks past the window)
+    import torch
+    rng = np.random.default_rng(100 + seed)
+    ref, qry = random_pair(200 + seed, 3_000 + 500 * seed, 2_500 + 700 * seed, n_frac=0.05,
+                           plant=12, plant_len=(100, 900), identity=0.93)
+    p = params_of("11011", K=300 + 200 * seed)
+    eng = engine(p, gate_mode=gate_mode)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    a = _edge_anchors(rng, ref.size, qry.size, 30_000)
+    # plus the diagonals of the planted homologs, where walks are long
+    o, R, qc = oracle_pass(ref, qry, p)
+    a = np.concatenate([a] + [c["anchors"] for c in o["chunks"]])
+    T = oracle.keep_threshold(p["hsp_threshold"])
+    want = oracle.gate(a, R.codes, qc, p["sub"], p["n_score"], p["xdrop"], T)
+    assert 0 < int(want.sum()) < a.size
+    at = torch.from_numpy(a.view(np.int64)).cuda()
+    f = torch.full((a.size,), 0xAB, dtype=torch.uint8, device="cuda")
+    eng.score_gate(at, a.size, f)
+    got = f.cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} flags differ, first anchors {a[bad[:5]]}"
+    if gate_mode == 2:
+        nd = eng.debug_gate_deferred()
+        assert 0 < nd < a.size
+
+
+def test_window_gate_defers_long_walks():
+    # a sequence against itself: every anchor on the main diagonal walks to both ends
+    ref, _ = random_pair(15, 20_000, 1, gc=0.41)
+    p = params_of("1101011", K=10**6)
+    eng = engine(p, gate_mode=2)
+    eng.upload_reference(ref)
+    eng.upload_query(ref)
+    import torch
+    diag = np.arange(0, ref.size + 1, 97, dtype=np.uint64)
+    a = diag | (diag << np.uint64(32))
+    at = torch.from_numpy(a.view(np.int64)).cuda()
+    f = torch.empty(a.size, dtype=torch.uint8, device="cuda")
+    eng.score_gate(at, a.size, f)
+    codes = oracle.encode(ref)
+    want = oracle.gate(a, codes, codes, p["sub"], p["n_score"], p["xdrop"],
+                       oracle.keep_threshold(p["hsp_threshold"]))
+    assert np.array_equal(f.cpu().numpy(), want)
+    # all but the anchors within a window of either end are deferred
+    assert eng.debug_gate_deferred() >= a.size - 4
 
 
 @pytest.mark.parametrize("strand", ["+", "-"])
@@ -148,7 +210,8 @@ def test_identical_sequences_long_walks():
     assert full.size > 0
 
 
-@pytest.mark.parametrize("qry", [b"", b"ACGT", b"N" * 5000, b"ACGTACGTAC" * 3])
+@pytest.mark.parametrize("qry", [b"", b"ACGT", b"N" * 5000, b"ACGTACGTAC" * 3],
+                         ids=["empty", "short", "all-N", "repeat"])
 def test_degenerate_queries(qry):
     ref, _ = random_pair(11, 5_000, 1)
     p = params_of("1101011")

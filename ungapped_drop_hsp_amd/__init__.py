@@ -30,7 +30,7 @@ ABI_SYMBOLS = (
     "hspz_upload_reference", "hspz_upload_query", "hspz_num_seeds", "hspz_seed_range",
     "hspz_plan", "hspz_get_chunk", "hspz_find_hits", "hspz_score_gate", "hspz_compact",
     "hspz_materialize", "hspz_compact_hsps", "hspz_get_seeds", "hspz_get_plan_arrays",
-    "hspz_debug_plan_counts", "hspz_debug_walk_steps",
+    "hspz_debug_plan_counts", "hspz_debug_walk_steps", "hspz_debug_gate_deferred",
 )
 
 
@@ -46,7 +46,7 @@ class Params(ctypes.Structure):
                 ("n_score", ctypes.c_int32), ("xdrop", ctypes.c_int32),
                 ("hsp_threshold", ctypes.c_int32), ("expand_mode", ctypes.c_int32),
                 ("max_hits", ctypes.c_uint64), ("chunk_walk", ctypes.c_int32),
-                ("device", ctypes.c_int32)]
+                ("device", ctypes.c_int32), ("gate_mode", ctypes.c_int32)]
 
 
 class Chunk(ctypes.Structure):
@@ -80,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "hspz_get_plan_arrays": (ctypes.c_int, [P, P, P]),
         "hspz_debug_plan_counts": (ctypes.c_int, [P, P, U64, P, PU64, PU32]),
         "hspz_debug_walk_steps": (ctypes.c_int, [P, P, U64, PU64, P]),
+        "hspz_debug_gate_deferred": (ctypes.c_int, [P, PU64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -139,13 +140,13 @@ class Engine:
 
     def __init__(self, seed_pattern: str, sub, n_score: int, xdrop: int, hsp_threshold: int,
                  max_hits: int = 0, expand_mode: int = 0, chunk_walk: int = 0,
-                 device: int = 0):
+                 device: int = 0, gate_mode: int = 0):
         self._pat = seed_pattern.encode()
         m = np.asarray(sub, dtype=np.int32).reshape(-1)
         if m.size != 16:
             raise ValueError("sub must hold 16 entries (4x4, ref row, query column)")
         p = Params(self._pat, (ctypes.c_int32 * 16)(*m.tolist()), n_score, xdrop,
-                   hsp_threshold, expand_mode, max_hits, chunk_walk, device)
+                   hsp_threshold, expand_mode, max_hits, chunk_walk, device, gate_mode)
         h = ctypes.c_void_p()
         rc = _lib.hspz_engine_create(ctypes.byref(p), ctypes.byref(h))
         if rc != HSPZ_OK:
@@ -265,4 +266,9 @@ class Engine:
         tot = ctypes.c_uint64()
         self._check(_lib.hspz_debug_walk_steps(self._h, _ptr(anchors), n, ctypes.byref(tot),
                                                _stream(stream)))
+        return tot.value
+
+    def debug_gate_deferred(self, stream=None) -> int:
+        tot = ctypes.c_uint64()
+        self._check(_lib.hspz_debug_gate_deferred(self._h, ctypes.byref(tot), _stream(stream)))
         return tot.value

@@ -109,6 +109,25 @@ int upload_padded(Engine *e, uint8_t *&dst, const std::vector<uint8_t> &codes, i
     return HSPZ_OK;
 }
 
+// 4-bit copy for the windowed gate: kPad4 edge codes, the sequence, kPad4 edge codes,
+// rounded up to whole 16-byte groups.
+int upload_nibbles(Engine *e, uint32_t *&dst, const std::vector<uint8_t> &codes, hipStream_t s) {
+    const uint64_t n = codes.size();
+    const uint64_t nib = n + 2 * (uint64_t)kPad4;
+    const uint64_t words = (nib + 31) / 32 * 4;
+    std::vector<uint32_t> buf(words, 0);
+    for (uint64_t m = 0; m < words * 8; m++) {
+        const uint32_t c = (m >= (uint64_t)kPad4 && m < (uint64_t)kPad4 + n) ? codes[m - kPad4]
+                                                                            : kCodeEdge;
+        buf[m >> 3] |= c << (4 * (m & 7));
+    }
+    int rc = dalloc(e, dst, words);
+    if (rc) return rc;
+    HIP_TRY(e, hipMemcpyAsync(dst, buf.data(), words * sizeof(uint32_t), hipMemcpyHostToDevice, s));
+    HIP_TRY(e, hipStreamSynchronize(s));
+    return HSPZ_OK;
+}
+
 // Shared by hspz_plan and hspz_debug_plan_counts once counts and block-local prefixes
 // are on the device: 64-bit host scan of the block sums, refusal, add-back, chunk walk.
 int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint32_t *n_chunks) {
@@ -228,6 +247,10 @@ Engine::~Engine() {
     dfree(d_pos);
     dfree(d_ref);
     dfree(d_qry);
+    dfree(d_ref4);
+    dfree(d_qry4);
+    dfree(d_defer);
+    dfree(d_defer_cnt);
     dfree(d_kmer);
     dfree(d_qend);
     dfree(d_count);
@@ -277,6 +300,8 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "expand_mode must be 0, 1 or 2");
     if (p->chunk_walk < 0 || p->chunk_walk > 1)
         return fail(nullptr, HSPZ_E_INVALID, "chunk_walk must be 0 or 1");
+    if (p->gate_mode < 0 || p->gate_mode > 2)
+        return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1 or 2");
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev)
         return fail(nullptr, HSPZ_E_INVALID, "device %d not available (%d devices)", p->device,
@@ -316,6 +341,21 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     }
     e->sp.xdrop = p->xdrop;
     e->sp.T = e->T;
+    // Windowed gate: exact when eight-base blocks are (B = 8 above) and every pair score,
+    // the edge score included, fits 16 bits.
+    e->window_ok = e->block_bases == 8 && p->xdrop + 1 <= 32767;
+    for (int r = 0; r < 6; r++) {
+        for (int q = 0; q < 16; q++) {
+            const int32_t v = q < 6 ? e->sp.tab[(r << kRefShift) | q] : -(p->xdrop + 1);
+            if (v < -32768 || v > 32767) e->window_ok = false;
+            e->wp.tab[r * 16 + q] = (int16_t)v;
+        }
+    }
+    e->wp.xdrop = p->xdrop;
+    e->wp.T = e->T;
+    if (p->gate_mode == 2 && !e->window_ok)
+        return fail(nullptr, HSPZ_E_INVALID,
+                    "gate_mode 2 needs 7 * max score <= xdrop and 16-bit pair scores");
     int rc = set_device(e);
     if (rc) {
         g_create_error = e->err;
@@ -324,7 +364,7 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     }
     if (hipHostMalloc(reinterpret_cast<void **>(&e->h_pinned), 64 * sizeof(uint32_t)) !=
             hipSuccess ||
-        dalloc(e, e->d_ctotal, 16) != HSPZ_OK) {
+        dalloc(e, e->d_ctotal, 16) != HSPZ_OK || dalloc(e, e->d_defer_cnt, 16) != HSPZ_OK) {
         g_create_error = "pinned/device staging allocation failed";
         delete e;
         return HSPZ_E_NOMEM;
@@ -384,8 +424,10 @@ HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, 
     HIP_TRY(e, hipMemcpyAsync(e->d_pos, pos.data(), std::max<uint64_t>(nwin, 1) * sizeof(uint32_t),
                               hipMemcpyHostToDevice, s));
     if ((rc = upload_padded(e, e->d_ref, codes, kRefShift, s))) return rc;
+    if ((rc = upload_nibbles(e, e->d_ref4, codes, s))) return rc;
     e->n_ref = len;
     e->sp.n_ref = (uint32_t)len;
+    e->wp.n_ref = (uint32_t)len;
     e->has_ref = true;
     return HSPZ_OK;
 }
@@ -432,8 +474,10 @@ HSPZ_API int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint
                                   hipMemcpyHostToDevice, s));
     }
     if ((rc = upload_padded(e, e->d_qry, codes, 0, s))) return rc;
+    if ((rc = upload_nibbles(e, e->d_qry4, codes, s))) return rc;
     e->n_qry = len;
     e->sp.n_qry = (uint32_t)len;
+    e->wp.n_qry = (uint32_t)len;
     e->n_seeds = ns;
     e->strand = strand;
     e->has_qry = true;
@@ -608,8 +652,28 @@ HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uin
     if (n && (!d_anchors || !d_flags)) return fail(e, HSPZ_E_INVALID, "NULL buffer");
     int rc = set_device(e);
     if (rc) return rc;
-    HIP_TRY(e, launch_gate(e->block_bases, d_anchors, (uint32_t)n, d_flags, e->d_ref + kPad,
-                           e->d_qry + kPad, e->sp, as_stream(stream)));
+    hipStream_t s = as_stream(stream);
+    e->gate_deferred_valid = false;
+    const bool window = e->window_ok && e->params.gate_mode != 1;
+    if (!window) {
+        HIP_TRY(e, launch_gate(e->block_bases, d_anchors, (uint32_t)n, d_flags, e->d_ref + kPad,
+                               e->d_qry + kPad, e->sp, s));
+        return HSPZ_OK;
+    }
+    if (n > e->cap_defer || !e->d_defer) {
+        // the deferred list can hold every anchor; grow with headroom
+        const uint64_t cap = std::max<uint64_t>(n + n / 4, 1u << 16);
+        if ((rc = dalloc(e, e->d_defer, cap))) {
+            e->cap_defer = 0;
+            return rc;
+        }
+        e->cap_defer = cap;
+    }
+    HIP_TRY(e, launch_gate_window(d_anchors, (uint32_t)n, d_flags, e->d_ref4, e->d_qry4, e->wp,
+                                  e->d_defer, e->d_defer_cnt, s));
+    HIP_TRY(e, launch_gate_list(e->block_bases, d_anchors, e->d_defer, e->d_defer_cnt,
+                                (uint32_t)n, d_flags, e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
+    e->gate_deferred_valid = true;
     return HSPZ_OK;
 }
 
@@ -707,5 +771,22 @@ HSPZ_API int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchor
     uint64_t t = 0;
     for (uint64_t v : part) t += v;
     *total_steps = t;
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_deferred, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!n_deferred) return fail(e, HSPZ_E_INVALID, "NULL output");
+    *n_deferred = 0;
+    if (!e->gate_deferred_valid)
+        return fail(e, HSPZ_E_STATE, "the last score_gate call did not take the window path");
+    int rc = set_device(e);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_defer_cnt, sizeof(uint32_t), hipMemcpyDeviceToHost,
+                              s));
+    HIP_TRY(e, hipStreamSynchronize(s));
+    *n_deferred = e->h_pinned[0];
     return HSPZ_OK;
 }

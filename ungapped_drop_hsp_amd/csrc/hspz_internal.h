@@ -23,6 +23,12 @@ constexpr uint8_t kCodeEdge = 5;
 constexpr int kRefShift = 3;
 constexpr int kTabSize = 64;
 
+// 4-bit copy of each sequence for the windowed score gate: eight bases per dword, the
+// base at padded nibble index m in dword m / 8, bits 4 * (m % 8).  Base b sits at padded
+// nibble b + kPad4; kPad4 edge nibbles precede and follow the sequence.  Codes are the
+// unshifted ones above on both sequences (A,C,G,T = 0..3, N = 4, edge = 5).
+constexpr int kPad4 = 256;
+
 // Seeds per block of the device prefix scan.
 constexpr int kScanBlock = 1024;
 // Flag bytes per block of the compaction kernels.
@@ -33,6 +39,18 @@ constexpr int kCompactBlock = 8192;
 // edge byte scores -(xdrop + 1), which ends a walk exactly where the sequence ends.
 struct ScoreParams {
     int32_t tab[kTabSize];
+    int32_t xdrop;
+    int32_t T;
+    uint32_t n_ref;
+    uint32_t n_qry;
+};
+
+// Constants of the windowed gate.  tab[r * 16 + q] is the 16-bit pair score for codes
+// r, q in 0..5 (edge pairs score -(xdrop + 1)); the window path is used only when every
+// entry fits 16 bits and blocks of eight bases are exact (7 * max score <= xdrop).
+constexpr int kWinTab = 96;
+struct WindowParams {
+    int16_t tab[kWinTab];
     int32_t xdrop;
     int32_t T;
     uint32_t n_ref;
@@ -52,6 +70,16 @@ hipError_t launch_expand(bool dense, const uint32_t *kmer, const uint32_t *q_end
 hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uint8_t *flags,
                        const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
                        hipStream_t s);
+// Windowed gate: decides every anchor whose walks end inside a 128-base window around it
+// and appends the index of every other anchor to defer[] (count in *defer_cnt, which the
+// launcher clears first).  launch_gate_list then decides the deferred ones exactly.
+hipError_t launch_gate_window(const uint64_t *anchors, uint32_t n, uint8_t *flags,
+                              const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
+                              uint32_t *defer, uint32_t *defer_cnt, hipStream_t s);
+hipError_t launch_gate_list(int block_bases, const uint64_t *anchors, const uint32_t *list,
+                            const uint32_t *count, uint32_t max_count, uint8_t *flags,
+                            const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
+                            hipStream_t s);
 hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint32_t n_surv,
                               hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
                               const uint8_t *qry, const ScoreParams &sp, hipStream_t s);
@@ -77,6 +105,8 @@ struct Engine {
     int32_t T = 0;
     int block_bases = 8;
     ScoreParams sp{};
+    WindowParams wp{};
+    bool window_ok = false;  // the windowed gate is exact for these parameters
     std::string err;
 
     // reference
@@ -85,12 +115,14 @@ struct Engine {
     uint32_t *d_end = nullptr;   // 4^w + 1 cumulative bucket ends, leading 0
     uint32_t *d_pos = nullptr;   // reference end coordinate of every valid window
     uint8_t *d_ref = nullptr;    // padded encoded reference (kPad edge bytes each side)
+    uint32_t *d_ref4 = nullptr;  // 4-bit packed reference (kPad4 edge nibbles each side)
 
     // query strand
     bool has_qry = false;
     uint64_t n_qry = 0;
     int strand = 0;
     uint8_t *d_qry = nullptr;
+    uint32_t *d_qry4 = nullptr;
     uint32_t *d_kmer = nullptr;
     uint32_t *d_qend = nullptr;
     uint64_t n_seeds = 0;
@@ -105,6 +137,12 @@ struct Engine {
     uint32_t *d_blkoff = nullptr;
     uint64_t cap_batch = 0;
     std::vector<hspz_chunk> chunks;
+
+    // gate scratch: deferred anchor indices and their count
+    uint32_t *d_defer = nullptr;
+    uint64_t cap_defer = 0;
+    uint32_t *d_defer_cnt = nullptr;
+    bool gate_deferred_valid = false;
 
     // compaction scratch
     uint32_t *d_cblk = nullptr;

@@ -1,22 +1,32 @@
 // Score-only X-drop gate ("D. Score gate", D.1-D.3).
 //
-// Mapping (designed for wave64, not the pages' warp-per-anchor tiles): every lane walks
-// one anchor at a time, base by base, and a wave refills finished lanes from its own
-// tile of kTile consecutive anchors (ranks from a ballot).  A random anchor scores only
-// ~60 bases in total, so spreading one anchor over a whole wave would idle most lanes;
-// one anchor per lane keeps every lane on useful bases.
+// Every kernel here keeps, per walk and per block of B bases, only the drawdown
+// d = best - score (d' = max(d - sigma, 0)), its running maximum and the score.  A drop
+// inside a block shows as max(d) > xdrop at the block's end.  B satisfies
+// (B - 1) * max(sigma) <= xdrop, so after a drop the score cannot climb back above the
+// best inside the same block: best = score + d at the block's end is exactly the
+// maximum before the first drop, with no per-base branch.  Bases outside a sequence are
+// edge codes scoring -(xdrop + 1), which forces that drop where the sequence ends.
 //
-// Per lane and per block of B bases the walk keeps, for the running score s and best
-// score b, only the drawdown d = b - s (d' = max(d - sigma, 0)), its block maximum and
-// s.  A drop inside the block shows as max(d) > xdrop at the block end.  B is chosen by
-// the host so that (B - 1) * max(sigma) <= xdrop: after a drop the score cannot climb
-// back above the best inside the same block, so b = s + d at the block end is exactly
-// the maximum before the first drop, with no per-base branch.  Walks past a sequence
-// end read edge bytes whose score -(xdrop + 1) forces that drop.
+// Two paths decide the same flag:
 //
-// Phase 1 walks every anchor of the tile to the right and parks R* in LDS; phase 2
-// walks left and decides the flag, stopping early once R* + (best so far) reaches T
-// (the flag cannot change after that).  Flags are staged in LDS and written per tile.
+//  window (k_gate_window): one lane per anchor, 64 anchors of consecutive raw ids per
+//    wave step.  Each lane loads a 128-base window of both sequences around its anchor
+//    once (4-bit codes, four 16-byte loads per sequence, kept in registers): 72 bases
+//    before the anchor and 48 from it.  The right walk then scores up to six blocks of
+//    eight bases and the left walk up to nine, all lanes in step, so every block's
+//    window word has a compile-time register index.  Pair scores come from a 16-bit LDS
+//    table indexed by (ref code << 4) | query code, formed for four bases at once with
+//    byte-wise bit selects.  A lane stops as soon as its flag is known: at the first
+//    drop, or once R* (right) or R* + best so far (left) reaches T.  Walks still running
+//    at the window's end are appended to a deferred list.
+//
+//  exact (k_gate, k_gate_list): one lane per anchor walking base blocks straight from
+//    the byte-per-base sequences, refilling finished lanes from the wave's tile of
+//    anchors (ranks from a ballot).  Used for the deferred anchors, and for every anchor
+//    when the window path's preconditions do not hold.
+#include <algorithm>
+
 #include "hspz_internal.h"
 #include "wave.h"
 
@@ -27,7 +37,9 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPerLane = 8;
-constexpr int kTile = 64 * kPerLane;  // anchors per wave
+constexpr int kTile = 64 * kPerLane;  // anchors per wave tile (exact path)
+
+// ------------------------------------------------------------------ exact path
 
 // Eight consecutive bytes starting at p, any alignment: three aligned dwords and two
 // byte funnels.  Reads [p - 3, p + 12).
@@ -62,15 +74,18 @@ __device__ __forceinline__ void block_step(const int32_t *tab, const uint8_t *rp
     }
 }
 
+// Walk every anchor of a tile (an[0..cnt), LDS or global) in direction D.  D > 0 parks
+// R* in rstar[]; D < 0 decides the flag into fl8[].
 template <int D, int B>
-__device__ __forceinline__ void walk_phase(const uint64_t *__restrict__ an, int cnt,
-                                           const int32_t *tab, const uint8_t *ref,
-                                           const uint8_t *qry, const ScoreParams &sp,
-                                           int32_t *rstar, uint8_t *fl8) {
+__device__ __forceinline__ void walk_phase(const uint64_t *an, int cnt, const int32_t *tab,
+                                           const uint8_t *__restrict__ ref,
+                                           const uint8_t *__restrict__ qry,
+                                           const ScoreParams &sp, int32_t *rstar,
+                                           uint8_t *fl8) {
     const int lane = lane_id();
     int next = 64;
     int cur = lane < cnt ? lane : -1;
-    const uint8_t *rp = ref, *qp = qry;
+    const uint8_t *rp = ref, *qp = qry;  // next base to score (right) or one past it (left)
     int32_t d = 0, dmax = 0, s = 0, other = 0;
 
     auto start = [&](int i) {
@@ -98,9 +113,9 @@ __device__ __forceinline__ void walk_phase(const uint64_t *__restrict__ an, int 
             qp += D * B;
             const int32_t best = s + d;
             const bool keep = (int64_t)other + best >= (int64_t)sp.T;
-            done = dmax > sp.xdrop || (D < 0 && keep);
+            done = dmax > sp.xdrop || keep;
             if (done) {
-                if (D > 0) rstar[cur] = best;
+                if (D > 0) rstar[cur] = keep ? sp.T : best;  // R* >= T already decides
                 else fl8[cur] = keep ? 1 : 0;
             }
         }
@@ -149,6 +164,181 @@ __global__ __launch_bounds__(kThreads) void k_gate(const uint64_t *__restrict__ 
     }
 }
 
+// The exact path over a list of anchor indices (*count of them, read on the device):
+// each wave gathers a tile of listed anchors into LDS, walks them, and writes their
+// flags back to the listed slots.  Waves stride over the list's tiles.
+template <int B>
+__global__ __launch_bounds__(kThreads) void k_gate_list(const uint64_t *__restrict__ anchors,
+                                                        const uint32_t *__restrict__ list,
+                                                        const uint32_t *__restrict__ count,
+                                                        uint8_t *__restrict__ flags,
+                                                        const uint8_t *__restrict__ ref,
+                                                        const uint8_t *__restrict__ qry,
+                                                        ScoreParams sp) {
+    __shared__ int32_t tab[kTabSize];
+    __shared__ int32_t rstar[kWaves][kTile];
+    __shared__ uint32_t flg[kWaves][kTile / 4];
+    __shared__ uint64_t an[kWaves][kTile];
+    if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
+    __syncthreads();
+
+    const int w = threadIdx.x >> 6;
+    const int lane = lane_id();
+    const uint64_t total = *count;
+    const uint64_t stride = (uint64_t)gridDim.x * kWaves * kTile;
+    uint8_t *fl8 = reinterpret_cast<uint8_t *>(flg[w]);
+    for (uint64_t tile0 = ((uint64_t)blockIdx.x * kWaves + w) * kTile; tile0 < total;
+         tile0 += stride) {
+        const int cnt = (int)min<uint64_t>((uint64_t)kTile, total - tile0);
+        for (int i = lane; i < cnt; i += 64) an[w][i] = anchors[list[tile0 + i]];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        walk_phase<+1, B>(an[w], cnt, tab, ref, qry, sp, rstar[w], fl8);
+        walk_phase<-1, B>(an[w], cnt, tab, ref, qry, sp, rstar[w], fl8);
+        for (int i = lane; i < cnt; i += 64) flags[list[tile0 + i]] = fl8[i];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// ------------------------------------------------------------------ window path
+
+constexpr int kWinDw = 16;       // window dwords per sequence: 128 bases
+constexpr int kLead = 72;        // window bases before the anchor
+constexpr int kRightBlocks = 6;  // 48 bases from the anchor
+constexpr int kLeftBlocks = 9;   // 72 bases before it
+constexpr int kSteps = 8;        // 64-anchor steps per wave
+static_assert(kLead == 8 * kLeftBlocks, "left blocks fill the lead");
+static_assert(kLead + 8 * kRightBlocks + 8 <= 8 * kWinDw, "right blocks fit the window");
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// 16 dwords from base + nib / 8 (nib a multiple of 8): 128 consecutive 4-bit codes.
+__device__ __forceinline__ void load_window(const uint32_t *__restrict__ base, uint32_t nib,
+                                            uint32_t (&W)[kWinDw]) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(base + (nib >> 3));
+#pragma unroll
+    for (int j = 0; j < kWinDw / 4; j++) {
+        const u32x4 v = p[j];
+        W[4 * j + 0] = v.x;
+        W[4 * j + 1] = v.y;
+        W[4 * j + 2] = v.z;
+        W[4 * j + 3] = v.w;
+    }
+}
+
+// Eight bases: R and Q hold codes of bases 0..7 in nibbles 0..7.  Even bases' table
+// indices (r << 4 | q) land in the bytes of ie, odd bases' in the bytes of io.
+template <bool Right>
+__device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t Q, int32_t &d,
+                                       int32_t &dmax, int32_t &s) {
+    const uint32_t hi = 0xF0F0F0F0u;
+    const uint32_t ie = ((R << 4) & hi) | (Q & ~hi);
+    const uint32_t io = (R & hi) | ((Q >> 4) & ~hi);
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        const int i = Right ? t : 7 - t;
+        const uint32_t w = (i & 1) ? io : ie;
+        const int32_t sg = tab[(w >> (8 * (i >> 1))) & 0xFFu];
+        const int32_t x = d - sg;
+        dmax = max(dmax, x);
+        d = max(x, 0);
+        s += sg;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_gate_window(
+    const uint64_t *__restrict__ anchors, uint32_t n, uint8_t *__restrict__ flags,
+    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
+    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    __shared__ int16_t tab[kWinTab];
+    if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    __syncthreads();
+
+    const int lane = lane_id();
+    const uint64_t first = ((uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * (64 * kSteps);
+    for (int step = 0; step < kSteps; step++) {
+        const uint64_t i0 = first + (uint64_t)step * 64;
+        if (i0 >= n) break;  // uniform
+        const uint64_t i = i0 + lane;
+        const bool valid = i < n;
+        uint32_t r = 0, q = 0;
+        if (valid) {
+            const uint64_t a = anchors[i];
+            r = (uint32_t)a;
+            q = (uint32_t)(a >> 32);
+        }
+        // An anchor outside the sequences scores 0 on both sides: flag 0.
+        const bool inrange = valid && r <= wp.n_ref && q <= wp.n_qry;
+        const uint32_t wr = (inrange ? r : 0u) + (uint32_t)(kPad4 - kLead);
+        const uint32_t wq = (inrange ? q : 0u) + (uint32_t)(kPad4 - kLead);
+        uint32_t WR[kWinDw], WQ[kWinDw];
+        load_window(ref4, wr & ~7u, WR);
+        load_window(qry4, wq & ~7u, WQ);
+        const uint32_t shr = (wr & 7u) * 4u, shq = (wq & 7u) * 4u;
+
+        bool keep = false;
+        int32_t rstar = 0;
+        // right: bases r + 8k .. r + 8k + 7 are window dword 9 + k onward
+        bool act = inrange;
+        int32_t d = 0, dmax = 0, s = 0;
+#pragma unroll
+        for (int k = 0; k < kRightBlocks; k++) {
+            if (__ballot(act) == 0) break;
+            if (act) {
+                const uint32_t R = __builtin_amdgcn_alignbit(WR[10 + k], WR[9 + k], shr);
+                const uint32_t Q = __builtin_amdgcn_alignbit(WQ[10 + k], WQ[9 + k], shq);
+                block8<true>(tab, R, Q, d, dmax, s);
+                const int32_t best = s + d;
+                if (dmax > wp.xdrop) {
+                    act = false;
+                    rstar = best;
+                } else if (best >= wp.T) {
+                    act = false;
+                    keep = true;
+                }
+            }
+        }
+        bool undecided = act;
+        // left: bases r - 8k - 8 .. r - 8k - 1 are window dword 8 - k onward
+        act = inrange && !keep && !undecided;
+        d = 0;
+        dmax = 0;
+        s = 0;
+#pragma unroll
+        for (int k = 0; k < kLeftBlocks; k++) {
+            if (__ballot(act) == 0) break;
+            if (act) {
+                const uint32_t R = __builtin_amdgcn_alignbit(WR[9 - k], WR[8 - k], shr);
+                const uint32_t Q = __builtin_amdgcn_alignbit(WQ[9 - k], WQ[8 - k], shq);
+                block8<false>(tab, R, Q, d, dmax, s);
+                const int32_t tot = rstar + s + d;
+                if (dmax > wp.xdrop) {
+                    act = false;
+                    keep = tot >= wp.T;
+                } else if (tot >= wp.T) {
+                    act = false;
+                    keep = true;
+                }
+            }
+        }
+        undecided = undecided || act;
+
+        if (valid && !undecided) flags[i] = keep ? 1 : 0;
+        const bool dfr = valid && undecided;
+        const uint64_t m = __ballot(dfr);
+        if (m) {
+            const int leader = __builtin_ctzll(m);
+            uint32_t base = 0;
+            if (lane == leader) base = atomicAdd(defer_cnt, (uint32_t)__popcll(m));
+            base = __shfl(base, leader, 64);
+            if (dfr) defer[base + lane_rank(m)] = (uint32_t)i;
+        }
+    }
+}
+
+__global__ void k_zero_u32(uint32_t *p) { *p = 0; }
+
 }  // namespace
 
 hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uint8_t *flags,
@@ -176,6 +366,47 @@ hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uin
                            ref, qry, sp, aligned8);
         break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_list(int block_bases, const uint64_t *anchors, const uint32_t *list,
+                            const uint32_t *count, uint32_t max_count, uint8_t *flags,
+                            const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
+                            hipStream_t s) {
+    if (max_count == 0) return hipSuccess;
+    const uint32_t per_block = kWaves * kTile;
+    const uint32_t blocks =
+        (uint32_t)std::min<uint64_t>(((uint64_t)max_count + per_block - 1) / per_block, 2048);
+    switch (block_bases) {
+    case 8:
+        hipLaunchKernelGGL(k_gate_list<8>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
+                           count, flags, ref, qry, sp);
+        break;
+    case 4:
+        hipLaunchKernelGGL(k_gate_list<4>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
+                           count, flags, ref, qry, sp);
+        break;
+    case 2:
+        hipLaunchKernelGGL(k_gate_list<2>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
+                           count, flags, ref, qry, sp);
+        break;
+    default:
+        hipLaunchKernelGGL(k_gate_list<1>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
+                           count, flags, ref, qry, sp);
+        break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_window(const uint64_t *anchors, uint32_t n, uint8_t *flags,
+                              const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
+                              uint32_t *defer, uint32_t *defer_cnt, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, defer_cnt);
+    if (n == 0) return hipGetLastError();
+    const uint64_t per_block = (uint64_t)kWaves * 64 * kSteps;
+    const uint32_t blocks = (uint32_t)(((uint64_t)n + per_block - 1) / per_block);
+    hipLaunchKernelGGL(k_gate_window, dim3(blocks), dim3(kThreads), 0, s, anchors, n, flags,
+                       ref4, qry4, wp, defer, defer_cnt);
     return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@ find_hits (C.4-C.5), score_gate (D.1-D.3), compact (D.4), materialize and compac
 """
 from __future__ import annotations
 
+from collections import defaultdict
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -41,6 +42,40 @@ class PassBuffers:
             self.cap_s = cap
 
 
+class StageTimer:
+    """HIP events around each ABI call, recorded on the stream the call launches on.
+
+    ``spans[name]`` collects (start, end) event pairs; ``elapsed_ms()`` sums them per
+    stage after a synchronisation.  ``units[name]`` holds what each launch processed
+    (anchors for the gate), so per-launch averages can be formed.
+    """
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.spans = defaultdict(list)
+        self.units = defaultdict(list)
+
+    def start(self, stream=None):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        return ev
+
+    def stop(self, name: str, ev0, units: int = 0, stream=None):
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev1.record(stream)
+        self.spans[name].append((ev0, ev1))
+        self.units[name].append(int(units))
+
+    def elapsed_ms(self) -> Dict[str, List[float]]:
+        self.torch.cuda.synchronize()
+        return {k: [a.elapsed_time(b) for a, b in v] for k, v in self.spans.items()}
+
+    def reset(self):
+        self.spans.clear()
+        self.units.clear()
+
+
 def _host_records(t, n: int) -> np.ndarray:
     if n == 0:
         return np.zeros(0, SEGMENT_PAIR)
@@ -48,24 +83,46 @@ def _host_records(t, n: int) -> np.ndarray:
 
 
 def run_pass(eng: Engine, seed_lo: int, seed_hi: int, bufs: PassBuffers, *,
-             collect: bool = False, stream=None) -> Dict:
+             collect: bool = False, stream=None, timer: Optional[StageTimer] = None) -> Dict:
     """Plan seeds [seed_lo, seed_hi) and run every chunk to accepted records.
 
     The accepted records of every chunk are copied to the host (the pass's output).  With
     ``collect`` the anchors, flags, ids, records and status of each chunk are copied too.
+    With ``timer`` every call is bracketed by events on the launch stream.
     """
+    tm = timer
+
+    def t0():
+        return tm.start(stream) if tm else None
+
+    def t1(name, ev, units=0):
+        if tm:
+            tm.stop(name, ev, units, stream)
+
+    ev = t0()
     total, nch = eng.plan(seed_lo, seed_hi, stream=stream)
+    t1("plan", ev, seed_hi - seed_lo)
     out: Dict = dict(total=total, n_chunks=nch, chunks=[], n_surv=0, n_acc=0)
     for c in range(nch):
         ch = eng.get_chunk(c)
         n = ch["n_hits"]
         bufs.ensure(n)
+        ev = t0()
         eng.find_hits(c, bufs.anchors, stream=stream)
+        t1("find_hits", ev, n)
+        ev = t0()
         eng.score_gate(bufs.anchors, n, bufs.flags, stream=stream)
+        t1("score_gate", ev, n)
+        ev = t0()
         ns = eng.compact(bufs.flags, n, bufs.ids, cap=n, stream=stream)
+        t1("compact", ev, n)
         bufs.ensure(n, ns)
+        ev = t0()
         eng.materialize(bufs.anchors, bufs.ids, ns, bufs.hsp, bufs.status, stream=stream)
+        t1("materialize", ev, ns)
+        ev = t0()
         na = eng.compact_hsps(bufs.hsp, bufs.status, ns, bufs.out, stream=stream)
+        t1("compact_hsps", ev, ns)
         rec: Dict = dict(chunk=ch, n_anchors=n, n_surv=ns, n_acc=na,
                          accepted=_host_records(bufs.out, na))
         if collect:
