@@ -19,7 +19,8 @@
 //    table indexed by (ref code << 4) | query code, formed for four bases at once with
 //    byte-wise bit selects.  A lane stops as soon as its flag is known: at the first
 //    drop, or once R* (right) or R* + best so far (left) reaches T.  Walks still running
-//    at the window's end are appended to a deferred list.
+//    at the window's end are appended to a deferred list: each wave collects them in
+//    LDS and the workgroup reserves its share of the global list with one atomic.
 //
 //  exact (k_gate, k_gate_list): one lane per anchor walking base blocks straight from
 //    the byte-per-base sequences, refilling finished lanes from the wave's tile of
@@ -207,7 +208,8 @@ constexpr int kWinDw = 16;       // window dwords per sequence: 128 bases
 constexpr int kLead = 72;        // window bases before the anchor
 constexpr int kRightBlocks = 6;  // 48 bases from the anchor
 constexpr int kLeftBlocks = 9;   // 72 bases before it
-constexpr int kSteps = 8;        // 64-anchor steps per wave
+constexpr int kSteps = 32;       // 64-anchor steps per wave
+constexpr int kSeg = 256;        // LDS slots per wave for deferred anchor indices
 static_assert(kLead == 8 * kLeftBlocks, "left blocks fill the lead");
 static_assert(kLead + 8 * kRightBlocks + 8 <= 8 * kWinDw, "right blocks fit the window");
 
@@ -252,11 +254,16 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
     __shared__ int16_t tab[kWinTab];
+    __shared__ uint32_t seg[kWaves][kSeg];   // deferred indices per wave
+    __shared__ uint32_t seg_n[kWaves];
+    __shared__ uint32_t blk_base;
     if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
     __syncthreads();
 
     const int lane = lane_id();
-    const uint64_t first = ((uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * (64 * kSteps);
+    const int w = threadIdx.x >> 6;
+    uint32_t nseg = 0;  // wave-uniform fill of seg[w]
+    const uint64_t first = ((uint64_t)blockIdx.x * kWaves + w) * (64 * kSteps);
     for (int step = 0; step < kSteps; step++) {
         const uint64_t i0 = first + (uint64_t)step * 64;
         if (i0 >= n) break;  // uniform
@@ -328,13 +335,32 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
         const bool dfr = valid && undecided;
         const uint64_t m = __ballot(dfr);
         if (m) {
-            const int leader = __builtin_ctzll(m);
-            uint32_t base = 0;
-            if (lane == leader) base = atomicAdd(defer_cnt, (uint32_t)__popcll(m));
-            base = __shfl(base, leader, 64);
-            if (dfr) defer[base + lane_rank(m)] = (uint32_t)i;
+            const uint32_t c = (uint32_t)__popcll(m);
+            if (nseg + c > (uint32_t)kSeg) {
+                // full: move this wave's collection to the global list now
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                uint32_t base = 0;
+                if (lane == 0) base = atomicAdd(defer_cnt, nseg);
+                base = __shfl(base, 0, 64);
+                for (uint32_t j = lane; j < nseg; j += 64) defer[base + j] = seg[w][j];
+                nseg = 0;
+            }
+            if (dfr) seg[w][nseg + lane_rank(m)] = (uint32_t)i;
+            nseg += c;
         }
     }
+    if (lane == 0) seg_n[w] = nseg;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t tot = 0;
+        for (int v = 0; v < kWaves; v++) tot += seg_n[v];
+        blk_base = tot ? atomicAdd(defer_cnt, tot) : 0u;
+    }
+    __syncthreads();
+    uint32_t base = blk_base;
+    for (int v = 0; v < w; v++) base += seg_n[v];
+    for (uint32_t j = lane; j < nseg; j += 64) defer[base + j] = seg[w][j];
 }
 
 __global__ void k_zero_u32(uint32_t *p) { *p = 0; }
