@@ -218,6 +218,7 @@ int ensure_batch(Engine *e, uint64_t n) {
     const uint64_t nblk = (cap + kScanBlock - 1) / kScanBlock;
     int rc;
     if ((rc = dalloc(e, e->d_count, cap))) return rc;
+    if ((rc = dalloc(e, e->d_first, cap))) return rc;
     if ((rc = dalloc(e, e->d_prefix, cap))) return rc;
     if ((rc = dalloc(e, e->d_blksum, nblk))) return rc;
     if ((rc = dalloc(e, e->d_blkoff, nblk))) return rc;
@@ -254,6 +255,7 @@ Engine::~Engine() {
     dfree(d_kmer);
     dfree(d_qend);
     dfree(d_count);
+    dfree(d_first);
     dfree(d_prefix);
     dfree(d_blksum);
     dfree(d_blkoff);
@@ -528,7 +530,7 @@ HSPZ_API int hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, 
     e->batch_lo = seed_lo;
     e->batch_n = n;
     HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_count,
-                                 e->d_prefix, e->d_blksum, s));
+                                 e->d_first, e->d_prefix, e->d_blksum, s));
     rc = finish_plan(e, n, s, total_hits, n_chunks);
     if (rc) {
         *total_hits = 0;
@@ -558,8 +560,8 @@ HSPZ_API int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_count
         // counts are staged through the prefix buffer, then scanned into place
         HIP_TRY(e, hipMemcpyAsync(e->d_count, h_counts, n * sizeof(uint32_t),
                                   hipMemcpyHostToDevice, s));
-        HIP_TRY(e, launch_count_scan(nullptr, e->d_count, n, nullptr, e->d_count, e->d_prefix,
-                                     e->d_blksum, s));
+        HIP_TRY(e, launch_count_scan(nullptr, e->d_count, n, nullptr, e->d_count, nullptr,
+                                     e->d_prefix, e->d_blksum, s));
     }
     rc = finish_plan(e, n, s, total_hits, n_chunks);
     if (rc) {
@@ -636,9 +638,9 @@ HSPZ_API int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anc
     else if (e->params.expand_mode == 2) dense = true;
     else dense = c.n_hits >= 16 * ns;  // "C. Hit discovery", C.4 density rule
     const uint64_t local = c.seed_lo - e->batch_lo;
-    HIP_TRY(e, launch_expand(dense, e->d_kmer + c.seed_lo, e->d_qend + c.seed_lo,
-                             e->d_prefix + local, ns, e->d_end, e->d_pos, (uint32_t)c.hit_lo,
-                             d_anchors, as_stream(stream)));
+    HIP_TRY(e, launch_expand(dense, e->d_count + local, e->d_first + local,
+                             e->d_qend + c.seed_lo, e->d_prefix + local, ns, e->d_pos,
+                             (uint32_t)c.hit_lo, d_anchors, as_stream(stream)));
     return HSPZ_OK;
 }
 

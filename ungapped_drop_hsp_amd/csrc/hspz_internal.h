@@ -58,13 +58,16 @@ struct WindowParams {
 };
 
 // ---- launchers (kernels in k_*.hip) --------------------------------------------------
+// Per seed: hit count, bucket start (first, when kmer is given) and block-local
+// inclusive prefix; one 64-bit sum per kScanBlock seeds into blksum.
 hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, uint64_t n,
-                             const uint32_t *end_tbl, uint32_t *count, uint32_t *prefix,
-                             uint64_t *blksum, hipStream_t s);
+                             const uint32_t *end_tbl, uint32_t *count, uint32_t *first,
+                             uint32_t *prefix, uint64_t *blksum, hipStream_t s);
 hipError_t launch_add_offsets(uint32_t *prefix, uint64_t n, const uint32_t *blkoff,
                               hipStream_t s);
-hipError_t launch_expand(bool dense, const uint32_t *kmer, const uint32_t *q_end,
-                         const uint32_t *prefix, uint64_t n_seeds, const uint32_t *end_tbl,
+// Expand the seeds of one chunk (count, first, prefix and q_end of its seeds).
+hipError_t launch_expand(bool dense, const uint32_t *count, const uint32_t *first,
+                         const uint32_t *q_end, const uint32_t *prefix, uint64_t n_seeds,
                          const uint32_t *pos, uint32_t hit_lo, uint64_t *anchors,
                          hipStream_t s);
 hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uint8_t *flags,
@@ -133,6 +136,7 @@ struct Engine {
     bool plan_expandable = false;
     uint64_t batch_lo = 0, batch_n = 0, total = 0;
     uint32_t *d_count = nullptr, *d_prefix = nullptr;
+    uint32_t *d_first = nullptr;  // bucket start of every seed of the batch
     uint64_t *d_blksum = nullptr;
     uint32_t *d_blkoff = nullptr;
     uint64_t cap_batch = 0;
