@@ -1,11 +1,12 @@
 // Exact X-drop materialization ("E. X-drop materialization", E.1-E.5).
 //
 // One wave per survivor.  Each step scores a 64-base tile: lane i holds base
-// base + i, an inclusive wave scan gives the running score, a prefix maximum (seeded
-// with the best so far) gives the running best, and a ballot of lanes whose drawdown
-// exceeds xdrop marks the first drop.  The tile's best is taken over the lanes before
-// the first drop, and its extent is the lowest such lane attaining it, so an equal later
-// maximum never moves the endpoint.  Lane 0 stores the 16-byte record and the status.
+// base + i, an inclusive wave scan (DPP) gives the running score, a prefix maximum
+// (seeded with the best so far) gives the running best, and a ballot of lanes whose
+// drawdown exceeds xdrop marks the first drop.  The running best in the lane before the
+// first drop is the tile's best; its extent is the lowest lane attaining it, so an equal
+// later maximum never moves the endpoint.  Lane 0 stores the 16-byte record and the
+// status.
 #include <climits>
 
 #include "hspz_internal.h"
@@ -29,17 +30,20 @@ __device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp
         const int64_t off = D > 0 ? (int64_t)base + l : -(int64_t)base - 1 - l;
         const int32_t sg = tab[rp[off] | qp[off]];
         const int32_t s = wave_incl_sum(sg) + carry;
+        // running best including every base up to this lane (and the tiles before)
         const int32_t run_best = max(wave_incl_max(s), best);
         const uint64_t dm = __ballot(run_best - s > xdrop);
-        const int f = dm ? __builtin_ctzll(dm) : 64;
-        const int32_t tb = wave_max(l < f ? s : INT_MIN);
-        if (tb > best) {
-            const uint64_t at = __ballot(l < f && s == tb);
-            ext = base + (uint32_t)__builtin_ctzll(at) + 1u;
-            best = tb;
+        const int f = dm ? (int)__builtin_ctzll(dm) : 64;  // first dropping lane
+        if (f > 0) {
+            const int32_t tb = lane_value(run_best, f - 1);  // best before the drop
+            if (tb > best) {
+                const uint64_t at = __ballot(l < f && s == tb);
+                ext = base + (uint32_t)__builtin_ctzll(at) + 1u;
+                best = tb;
+            }
         }
         if (dm) break;
-        carry = __shfl(s, 63, 64);
+        carry = lane_value(s, 63);
         base += 64;
     }
     best_out = best;
