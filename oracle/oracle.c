@@ -132,11 +132,12 @@ int64_t orc_ref_index(const uint8_t *codes, int64_t n, const char *pattern,
     return m;
 }
 
-static int64_t orc_lower_bound_key(const uint32_t *keys, int64_t n, uint32_t k) {
+/* First index in the sorted key list whose key is >= k (upper = 0) or > k (upper = 1). */
+static int64_t orc_bound_key(const uint32_t *keys, int64_t n, uint32_t k, int upper) {
     int64_t lo = 0, hi = n;
     while (lo < hi) {
         int64_t mid = lo + (hi - lo) / 2;
-        if (keys[mid] < k) lo = mid + 1; else hi = mid;
+        if (keys[mid] < k || (upper && keys[mid] == k)) lo = mid + 1; else hi = mid;
     }
     return lo;
 }
@@ -149,9 +150,8 @@ void orc_counts_indexed(const uint32_t *keys, const uint32_t *ends, int64_t n_wi
                         int64_t *first) {
     (void)ends;
     for (int64_t s = 0; s < n_seeds; s++) {
-        int64_t lo = orc_lower_bound_key(keys, n_win, kmer[s]);
-        int64_t hi = lo;
-        while (hi < n_win && keys[hi] == kmer[s]) hi++;
+        int64_t lo = orc_bound_key(keys, n_win, kmer[s], 0);
+        int64_t hi = orc_bound_key(keys, n_win, kmer[s], 1);
         count[s] = (uint32_t)(hi - lo);
         if (first) first[s] = lo;
     }

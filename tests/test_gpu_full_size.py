@@ -1,0 +1,148 @@
+"""Parity at the workloads' full sizes (c2 5 Mb, c3 50 Mb, c4 200 Mb both strands).
+
+The HIP path runs exactly as bench.py runs it (whole query batches, the workload's
+MAX_HITS, default modes).  The oracle cannot redo every anchor's walks at these sizes,
+so each batch is checked like this:
+  - every seed count, the whole global prefix and the whole chunk list, element by element;
+  - for sampled chunks, every anchor byte;
+  - flags on a random sample of anchors plus every anchor the GPU kept;
+  - survivor ids against the flag bytes;
+  - records and status of sampled survivors, recomputed one by one by the oracle;
+  - the accepted records as the stable selection of the records.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import engine, require_gpu
+from workloads import build
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _check_batch(eng, bufs, R, qc, seeds, p, lo, hi, chunk_pick, rng, full_plan=True,
+                 n_flag=60_000, n_mat=3_000, n_count=400_000):
+    kmer, q_end, _ = seeds
+    tot, nch = eng.plan(lo, hi)
+    gc, gp = eng.get_plan_arrays(hi - lo)
+    if full_plan:
+        count, first = oracle.counts_indexed(R.keys, R.ends, kmer[lo:hi])
+        assert np.array_equal(gc, count), "hit counts differ"
+    else:
+        # counts of a random sample of seeds, one by one; the prefix from the counts
+        samp = rng.choice(hi - lo, size=min(hi - lo, n_count), replace=False)
+        sc, _ = oracle.counts_indexed(R.keys, R.ends, kmer[lo:hi][samp])
+        assert np.array_equal(gc[samp], sc), "sampled hit counts differ"
+        count = gc
+    P, ok = oracle.prefix(count)
+    assert ok and tot == int(P[-1])
+    assert np.array_equal(gp.astype(np.uint64), P), "global prefix differs"
+    och = oracle.chunks(P, p["max_hits"])
+    gch = [eng.get_chunk(i) for i in range(nch)]
+    assert [(c["seed_lo"] - lo, c["seed_hi"] - lo, c["hit_lo"], c["n_hits"]) for c in gch] == \
+        [(c["seed_lo"], c["seed_hi"], c["hit_lo"], c["n_hits"]) for c in och], "chunks differ"
+    T = oracle.keep_threshold(p["hsp_threshold"])
+    stats = dict(total=tot, chunks=nch, checked=0, surv=0)
+    for ci in chunk_pick(nch):
+        c = och[ci]
+        n = c["n_hits"]
+        bufs.ensure(n)
+        eng.find_hits(ci, bufs.anchors)
+        # the oracle's own counts and bucket starts for this chunk's seeds
+        a0, a1 = c["seed_lo"], c["seed_hi"] + 1
+        cc, cf = oracle.counts_indexed(R.keys, R.ends, kmer[lo + a0:lo + a1])
+        assert np.array_equal(cc, gc[a0:a1]), f"hit counts of chunk {ci} differ"
+        cnt_l = np.zeros(hi - lo, np.uint32)
+        fst_l = np.zeros(hi - lo, np.int64)
+        cnt_l[a0:a1] = cc
+        fst_l[a0:a1] = cf
+        oa = oracle.anchors(P, cnt_l, fst_l, R.ends, q_end[lo:hi], c)
+        ga = bufs.anchors[:n].cpu().numpy().view(np.uint64)
+        assert np.array_equal(ga, oa), f"anchors of chunk {ci} differ"
+        eng.score_gate(bufs.anchors, n, bufs.flags)
+        gf = bufs.flags[:n].cpu().numpy()
+        ns = eng.compact(bufs.flags, n, bufs.ids, cap=n)
+        ids = bufs.ids[:ns].cpu().numpy().view(np.uint32)
+        assert np.array_equal(ids, np.flatnonzero(gf).astype(np.uint32)), "ids != kept flags"
+        samp = np.union1d(rng.choice(n, size=min(n, n_flag), replace=False),
+                          rng.choice(ids, size=min(ids.size, n_flag // 4), replace=False)
+                          if ids.size else np.zeros(0, np.int64)).astype(np.int64)
+        of = oracle.gate(oa[samp], R.codes, qc, p["sub"], p["n_score"], p["xdrop"], T)
+        bad = np.flatnonzero(of != gf[samp])
+        assert bad.size == 0, f"chunk {ci}: {bad.size} of {samp.size} sampled flags differ"
+        bufs.ensure(n, ns)
+        eng.materialize(bufs.anchors, bufs.ids, ns, bufs.hsp, bufs.status)
+        na = eng.compact_hsps(bufs.hsp, bufs.status, ns, bufs.out)
+        if ns:
+            gh = bufs.hsp[:ns].cpu().numpy().view(oracle.HSP_DTYPE).reshape(-1)
+            gs = bufs.status[:ns].cpu().numpy()
+            go = bufs.out[:na].cpu().numpy().view(oracle.HSP_DTYPE).reshape(-1)
+            assert np.array_equal(go, gh[gs == 1]), "accepted records are not the selection"
+            pick = np.sort(rng.choice(ns, size=min(ns, n_mat), replace=False))
+            oh, ost = oracle.materialize(oa, ids[pick], R.codes, qc, p["sub"], p["n_score"],
+                                         p["xdrop"], T)
+            assert np.array_equal(gs[pick], ost), "status differs"
+            acc = ost == 1
+            assert np.array_equal(gh[pick][acc], oh[acc]), "records differ"
+        stats["checked"] += 1
+        stats["surv"] += ns
+    return stats
+
+
+def _run_config(cfg, chunk_pick, batch_pick=None, full_plan=True):
+    from ungapped_drop_hsp_amd.pipeline import PassBuffers, batches
+    w = build(cfg)
+    p = w.params()
+    R = oracle.Reference(w.ref, p["seed_pattern"])
+    eng = engine(p)
+    eng.upload_reference(w.ref)
+    bufs = PassBuffers()
+    rng = np.random.default_rng(cfg)
+    out = []
+    for strand in w.strands:
+        qc = oracle.strand_codes(w.query, strand)
+        seeds = oracle.query_seeds(qc, p["seed_pattern"])
+        eng.upload_query(w.query, strand=1 if strand == "-" else 0)
+        assert eng.num_seeds() == seeds[0].size
+        bs = batches(eng, w.batch_len, w.query.size)
+        # batch ranges agree with the oracle's seed positions
+        if w.batch_len:
+            edges = np.searchsorted(seeds[2], np.arange(0, w.query.size + w.batch_len,
+                                                        w.batch_len))
+            want = [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+            assert bs == want
+        for bi, (lo, hi) in enumerate(bs):
+            if batch_pick is not None and bi not in batch_pick(strand, len(bs)):
+                continue
+            st = _check_batch(eng, bufs, R, qc, seeds, p, lo, hi, chunk_pick, rng,
+                              full_plan=full_plan)
+            print(f"{w.name} strand {strand} batch {bi}: {st}", flush=True)
+            out.append(st)
+    return out
+
+
+@pytest.mark.timeout(600)
+def test_c2_dense_tandem_full_size():
+    # 5 Mb x 5 Mb, MAX_HITS 2^20: ~58 chunks; dense buckets in the tandem region
+    st = _run_config(2, lambda n: sorted({0, n // 2, n - 1}))
+    assert st[0]["chunks"] > 40 and st[0]["surv"] > 0
+
+
+@pytest.mark.timeout(600)
+def test_c3_50mb_full_size():
+    st = _run_config(3, lambda n: list(range(n)))
+    assert st[0]["chunks"] == 2 and 1.2e8 < st[0]["total"] < 2.6e8
+
+
+@pytest.mark.timeout(900)
+def test_c4_200mb_both_strands_batches():
+    # 200 Mb x 200 Mb, both strands, 50 Mb query batches, MAX_HITS 2^26
+    st = _run_config(4, lambda n: sorted({0, n - 1}),
+                     batch_pick=lambda strand, n: {0} if strand == "+" else {n - 1},
+                     full_plan=False)
+    assert len(st) == 2 and all(s["chunks"] > 1 for s in st)
