@@ -150,14 +150,16 @@ def main():
     gate_ms_avg = sum(gate_ms) / gate_launches
     units_avg = sum(gate_units) / gate_launches
     gate_gbs = GATE_BYTES_PER_ANCHOR * units_avg / (gate_ms_avg * 1e6)
-    steps_total = deferred = 0
+    steps_total = 0
+    deferred = [0, 0]
     for c in range(r["n_chunks"]):
         ch = eng.get_chunk(c)
         eng.find_hits(c, bufs.anchors)
         steps_total += eng.debug_walk_steps(bufs.anchors, ch["n_hits"])
         eng.score_gate(bufs.anchors, ch["n_hits"], bufs.flags)
         try:
-            deferred += eng.debug_gate_deferred()
+            d2, dx = eng.debug_gate_deferred()
+            deferred = [deferred[0] + d2, deferred[1] + dx]
         except h.HspzError:
             deferred = None
     steps_per_anchor = steps_total / max(anchors, 1)
@@ -183,14 +185,15 @@ def main():
         stage_ms=stage_ms,
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS, traffic=None,
-                      kernel="score_gate (k_gate_window + k_gate_list)",
+                      kernel="score_gate (two k_gate_window stages + k_gate_list)",
                       launches_per_step=gate_launches // args.steps,
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
                       base_steps_per_anchor=steps_per_anchor),
         gate_hbm=dict(achieved=gate_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=gate_gbs / HBM_PEAK_GBS, bytes_per_anchor=GATE_BYTES_PER_ANCHOR),
         gate_anchors_per_s=units_avg / (gate_ms_avg / 1000.0),
-        gate_deferred_fraction=None if deferred is None else deferred / max(anchors, 1),
+        gate_stage2_fraction=None if deferred is None else deferred[0] / max(anchors, 1),
+        gate_exact_fraction=None if deferred is None else deferred[1] / max(anchors, 1),
         setup_s=dict(generate=gen_s, upload=upload_s),
     )
     if args.cpu_seconds > 0:

@@ -50,7 +50,7 @@ def test_create_rejects_bad_parameters_without_gpu():
     from workloads import HOXD70
     for kw in (dict(seed_pattern="0111"), dict(seed_pattern="1" * 15),
                dict(seed_pattern="11x1"), dict(hsp_threshold=0), dict(xdrop=-1),
-               dict(expand_mode=3), dict(chunk_walk=2)):
+               dict(expand_mode=3), dict(chunk_walk=2), dict(gate_mode=4)):
         args = dict(seed_pattern="1110100110010101111", sub=HOXD70, n_score=-100, xdrop=910,
                     hsp_threshold=3000)
         args.update(kw)

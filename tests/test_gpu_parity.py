@@ -86,8 +86,8 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
-@pytest.mark.parametrize("expand_mode,gate_mode", [(0, 0), (1, 1), (2, 2)],
-                         ids=["auto", "sparse-exact", "dense-window"])
+@pytest.mark.parametrize("expand_mode,gate_mode", [(0, 0), (1, 1), (2, 2), (0, 3)],
+                         ids=["auto", "sparse-exact", "dense-window", "auto-window2"])
 def test_random_pass_parity(case, expand_mode, gate_mode):
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
     ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
@@ -107,7 +107,7 @@ def _edge_anchors(rng, nr, nq, k):
     return np.asarray([(a & 0xFFFFFFFF) | (b << 32) for a, b in zip(r, q)], np.uint64)
 
 
-@pytest.mark.parametrize("gate_mode", [1, 2])
+@pytest.mark.parametrize("gate_mode", [1, 2, 3])
 @pytest.mark.parametrize("seed", range(3))
 def test_gate_on_arbitrary_anchors(gate_mode, seed):
     # anchors need not come from seeds: walks from every offset near both sequence ends,
@@ -133,16 +133,20 @@ def test_gate_on_arbitrary_anchors(gate_mode, seed):
     got = f.cpu().numpy()
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, f"{bad.size} flags differ, first anchors {a[bad[:5]]}"
-    if gate_mode == 2:
-        nd = eng.debug_gate_deferred()
-        assert 0 < nd < a.size
+    if gate_mode == 3:
+        n2, nx = eng.debug_gate_deferred()
+        assert 0 < n2 < a.size and 0 < nx <= n2
+    elif gate_mode == 2:
+        n2, nx = eng.debug_gate_deferred()
+        assert n2 == 0 and 0 < nx < a.size
 
 
-def test_window_gate_defers_long_walks():
+@pytest.mark.parametrize("gate_mode", [2, 3])
+def test_window_gate_defers_long_walks(gate_mode):
     # a sequence against itself: every anchor on the main diagonal walks to both ends
     ref, _ = random_pair(15, 20_000, 1, gc=0.41)
     p = params_of("1101011", K=10**6)
-    eng = engine(p, gate_mode=2)
+    eng = engine(p, gate_mode=gate_mode)
     eng.upload_reference(ref)
     eng.upload_query(ref)
     import torch
@@ -155,8 +159,9 @@ def test_window_gate_defers_long_walks():
     want = oracle.gate(a, codes, codes, p["sub"], p["n_score"], p["xdrop"],
                        oracle.keep_threshold(p["hsp_threshold"]))
     assert np.array_equal(f.cpu().numpy(), want)
-    # all but the anchors within a window of either end are deferred
-    assert eng.debug_gate_deferred() >= a.size - 4
+    # every anchor walks past both windows (none sits within a window of both ends)
+    n2, nx = eng.debug_gate_deferred()
+    assert n2 == (a.size if gate_mode == 3 else 0) and nx == a.size
 
 
 @pytest.mark.parametrize("strand", ["+", "-"])

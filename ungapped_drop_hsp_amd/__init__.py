@@ -80,7 +80,7 @@ def _load() -> ctypes.CDLL:
         "hspz_get_plan_arrays": (ctypes.c_int, [P, P, P]),
         "hspz_debug_plan_counts": (ctypes.c_int, [P, P, U64, P, PU64, PU32]),
         "hspz_debug_walk_steps": (ctypes.c_int, [P, P, U64, PU64, P]),
-        "hspz_debug_gate_deferred": (ctypes.c_int, [P, PU64, P]),
+        "hspz_debug_gate_deferred": (ctypes.c_int, [P, PU64, PU64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -268,7 +268,9 @@ class Engine:
                                                _stream(stream)))
         return tot.value
 
-    def debug_gate_deferred(self, stream=None) -> int:
-        tot = ctypes.c_uint64()
-        self._check(_lib.hspz_debug_gate_deferred(self._h, ctypes.byref(tot), _stream(stream)))
-        return tot.value
+    def debug_gate_deferred(self, stream=None) -> Tuple[int, int]:
+        """(anchors sent to the second window stage, anchors decided by the exact walk)."""
+        a, b = ctypes.c_uint64(), ctypes.c_uint64()
+        self._check(_lib.hspz_debug_gate_deferred(self._h, ctypes.byref(a), ctypes.byref(b),
+                                                  _stream(stream)))
+        return a.value, b.value

@@ -302,8 +302,8 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "expand_mode must be 0, 1 or 2");
     if (p->chunk_walk < 0 || p->chunk_walk > 1)
         return fail(nullptr, HSPZ_E_INVALID, "chunk_walk must be 0 or 1");
-    if (p->gate_mode < 0 || p->gate_mode > 2)
-        return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1 or 2");
+    if (p->gate_mode < 0 || p->gate_mode > 3)
+        return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2 or 3");
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev)
         return fail(nullptr, HSPZ_E_INVALID, "device %d not available (%d devices)", p->device,
@@ -355,9 +355,9 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     }
     e->wp.xdrop = p->xdrop;
     e->wp.T = e->T;
-    if (p->gate_mode == 2 && !e->window_ok)
+    if (p->gate_mode >= 2 && !e->window_ok)
         return fail(nullptr, HSPZ_E_INVALID,
-                    "gate_mode 2 needs 7 * max score <= xdrop and 16-bit pair scores");
+                    "gate_modes 2 and 3 need 7 * max score <= xdrop and 16-bit pair scores");
     int rc = set_device(e);
     if (rc) {
         g_create_error = e->err;
@@ -665,15 +665,16 @@ HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uin
     if (n > e->cap_defer || !e->d_defer) {
         // the deferred list can hold every anchor; grow with headroom
         const uint64_t cap = std::max<uint64_t>(n + n / 4, 1u << 16);
-        if ((rc = dalloc(e, e->d_defer, cap))) {
+        if ((rc = dalloc(e, e->d_defer, 2 * cap))) {
             e->cap_defer = 0;
             return rc;
         }
         e->cap_defer = cap;
     }
-    HIP_TRY(e, launch_gate_window(d_anchors, (uint32_t)n, d_flags, e->d_ref4, e->d_qry4, e->wp,
-                                  e->d_defer, e->d_defer_cnt, s));
-    HIP_TRY(e, launch_gate_list(e->block_bases, d_anchors, e->d_defer, e->d_defer_cnt,
+    uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
+    HIP_TRY(e, launch_gate_window(e->params.gate_mode == 3, d_anchors, (uint32_t)n, d_flags,
+                                  e->d_ref4, e->d_qry4, e->wp, list1, list2, e->d_defer_cnt, s));
+    HIP_TRY(e, launch_gate_list(e->block_bases, d_anchors, list2, e->d_defer_cnt + 1,
                                 (uint32_t)n, d_flags, e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
     return HSPZ_OK;
@@ -776,19 +777,22 @@ HSPZ_API int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchor
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_deferred, void *stream) {
+HSPZ_API int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2,
+                                      uint64_t *n_exact, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
-    if (!n_deferred) return fail(e, HSPZ_E_INVALID, "NULL output");
-    *n_deferred = 0;
+    if (!n_stage2 || !n_exact) return fail(e, HSPZ_E_INVALID, "NULL output");
+    *n_stage2 = 0;
+    *n_exact = 0;
     if (!e->gate_deferred_valid)
         return fail(e, HSPZ_E_STATE, "the last score_gate call did not take the window path");
     int rc = set_device(e);
     if (rc) return rc;
     hipStream_t s = as_stream(stream);
-    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_defer_cnt, sizeof(uint32_t), hipMemcpyDeviceToHost,
-                              s));
+    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_defer_cnt, 2 * sizeof(uint32_t),
+                              hipMemcpyDeviceToHost, s));
     HIP_TRY(e, hipStreamSynchronize(s));
-    *n_deferred = e->h_pinned[0];
+    *n_stage2 = e->h_pinned[0];
+    *n_exact = e->h_pinned[1];
     return HSPZ_OK;
 }

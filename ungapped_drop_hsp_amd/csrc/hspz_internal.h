@@ -73,12 +73,15 @@ hipError_t launch_expand(bool dense, const uint32_t *count, const uint32_t *firs
 hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uint8_t *flags,
                        const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
                        hipStream_t s);
-// Windowed gate: decides every anchor whose walks end inside a 128-base window around it
-// and appends the index of every other anchor to defer[] (count in *defer_cnt, which the
-// launcher clears first).  launch_gate_list then decides the deferred ones exactly.
-hipError_t launch_gate_window(const uint64_t *anchors, uint32_t n, uint8_t *flags,
-                              const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
-                              uint32_t *defer, uint32_t *defer_cnt, hipStream_t s);
+// Windowed gate.  One stage decides every anchor whose walks end within 48 bases to its
+// right and 72 to its left and lists the others in list2 (count cnt[1]).  With
+// two_stage, a first stage of 32 and 56 bases lists its leftovers in list1 (cnt[0]) and
+// a second stage of 64 and 96 bases decides those, listing the rest in list2.  The
+// launcher clears both counts first; launch_gate_list then decides list2 exactly.
+hipError_t launch_gate_window(bool two_stage, const uint64_t *anchors, uint32_t n,
+                              uint8_t *flags, const uint32_t *ref4, const uint32_t *qry4,
+                              const WindowParams &wp, uint32_t *list1, uint32_t *list2,
+                              uint32_t *cnt, hipStream_t s);
 hipError_t launch_gate_list(int block_bases, const uint64_t *anchors, const uint32_t *list,
                             const uint32_t *count, uint32_t max_count, uint8_t *flags,
                             const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
@@ -142,8 +145,8 @@ struct Engine {
     uint64_t cap_batch = 0;
     std::vector<hspz_chunk> chunks;
 
-    // gate scratch: deferred anchor indices and their count
-    uint32_t *d_defer = nullptr;
+    // gate scratch: anchor indices left by each window stage, and their two counts
+    uint32_t *d_defer = nullptr;  // 2 * cap_defer entries: stage-1 list, then stage-2 list
     uint64_t cap_defer = 0;
     uint32_t *d_defer_cnt = nullptr;
     bool gate_deferred_valid = false;

@@ -11,11 +11,11 @@
 // Two paths decide the same flag:
 //
 //  window (k_gate_window): one lane per anchor, 64 anchors of consecutive raw ids per
-//    wave step.  Each lane loads a 128-base window of both sequences around its anchor
-//    once (4-bit codes, four 16-byte loads per sequence, kept in registers): 72 bases
-//    before the anchor and 48 from it.  The right walk then scores up to six blocks of
-//    eight bases and the left walk up to nine, all lanes in step, so every block's
-//    window word has a compile-time register index.  Pair scores come from a 16-bit LDS
+//    wave step.  Each lane loads a window of both sequences around its anchor once
+//    (4-bit codes, 16-byte loads, kept in registers): by default 72 bases before the
+//    anchor and 48 from it.  The right walk then scores up to six blocks of eight bases
+//    and the left walk up to nine, all lanes in step, so every block's window word has a
+//    compile-time register index.  Pair scores come from a 16-bit LDS
 //    table indexed by (ref code << 4) | query code, formed for four bases at once with
 //    byte-wise bit selects.  A lane stops as soon as its flag is known: at the first
 //    drop, or once R* (right) or R* + best so far (left) reaches T.  Walks still running
@@ -204,28 +204,32 @@ __global__ __launch_bounds__(kThreads) void k_gate_list(const uint64_t *__restri
 
 // ------------------------------------------------------------------ window path
 
-constexpr int kWinDw = 16;       // window dwords per sequence: 128 bases
-constexpr int kLead = 72;        // window bases before the anchor
-constexpr int kRightBlocks = 6;  // 48 bases from the anchor
-constexpr int kLeftBlocks = 9;   // 72 bases before it
-constexpr int kSteps = 32;       // 64-anchor steps per wave
-constexpr int kSeg = 256;        // LDS slots per wave for deferred anchor indices
-static_assert(kLead == 8 * kLeftBlocks, "left blocks fill the lead");
-static_assert(kLead + 8 * kRightBlocks + 8 <= 8 * kWinDw, "right blocks fit the window");
+constexpr int kSteps = 32;  // 64-anchor steps per wave (first window stage)
+// Window sizes, in blocks of eight bases (right of the anchor, left of it).  One stage of
+// (6, 9) decides about 98.4% of random anchors on the 50 Mb workload.  The two-stage
+// form starts narrower, (4, 7), deciding about 86%, and hands the rest to a second
+// stage of (8, 12) that decides all but about 0.15%; it does fewer block steps but
+// fetches more, and the two measure within a few percent of each other.
+constexpr int kOneRight = 6, kOneLeft = 9;
+constexpr int kStage1Right = 4, kStage1Left = 7;
+constexpr int kStage2Right = 8, kStage2Left = 12;
+constexpr int kSeg = 512;   // LDS slots per wave for deferred anchor indices
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// 16 dwords from base + nib / 8 (nib a multiple of 8): 128 consecutive 4-bit codes.
+// W dwords from base + nib / 8 (nib a multiple of 8): 8 * W consecutive 4-bit codes.
+template <int W>
 __device__ __forceinline__ void load_window(const uint32_t *__restrict__ base, uint32_t nib,
-                                            uint32_t (&W)[kWinDw]) {
+                                            uint32_t (&Wd)[W]) {
+    static_assert(W % 4 == 0, "whole 16-byte loads");
     const u32x4 *p = reinterpret_cast<const u32x4 *>(base + (nib >> 3));
 #pragma unroll
-    for (int j = 0; j < kWinDw / 4; j++) {
+    for (int j = 0; j < W / 4; j++) {
         const u32x4 v = p[j];
-        W[4 * j + 0] = v.x;
-        W[4 * j + 1] = v.y;
-        W[4 * j + 2] = v.z;
-        W[4 * j + 3] = v.w;
+        Wd[4 * j + 0] = v.x;
+        Wd[4 * j + 1] = v.y;
+        Wd[4 * j + 2] = v.z;
+        Wd[4 * j + 3] = v.w;
     }
 }
 
@@ -235,8 +239,10 @@ template <bool Right>
 __device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t Q, int32_t &d,
                                        int32_t &dmax, int32_t &s) {
     const uint32_t hi = 0xF0F0F0F0u;
-    const uint32_t ie = ((R << 4) & hi) | (Q & ~hi);
-    const uint32_t io = (R & hi) | ((Q >> 4) & ~hi);
+    uint32_t ie = ((R << 4) & hi) | (Q & ~hi);
+    uint32_t io = (R & hi) | ((Q >> 4) & ~hi);
+    // keep ie and io whole: each table address is then one byte-select shift of them
+    asm volatile("" : "+v"(ie), "+v"(io));
 #pragma unroll
     for (int t = 0; t < 8; t++) {
         const int i = Right ? t : 7 - t;
@@ -249,53 +255,44 @@ __device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t 
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_gate_window(
-    const uint64_t *__restrict__ anchors, uint32_t n, uint8_t *__restrict__ flags,
-    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
-    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
-    __shared__ int16_t tab[kWinTab];
-    __shared__ uint32_t seg[kWaves][kSeg];   // deferred indices per wave
-    __shared__ uint32_t seg_n[kWaves];
-    __shared__ uint32_t blk_base;
-    if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
-    __syncthreads();
+// The windows of one anchor per lane: 8 * LB bases before the anchor and 8 * RB from it
+// (plus one dword for the funnel shift), 4-bit codes of both sequences.  load() only
+// issues the reads, so a wave can fetch the next step's windows while it scores this
+// step's.  decide() is called by all lanes of the wave together and returns the flag
+// (0 or 1), or 2 when a walk is still running at the window's end.
+template <int RB, int LB>
+struct Win {
+    static constexpr int W = (LB + RB + 1 + 3) / 4 * 4;
+    static_assert(8 * LB + 8 <= kPad4, "left window stays inside the edge padding");
+    uint32_t R[W], Q[W];
+    uint32_t shr, shq;
+    bool inrange;
 
-    const int lane = lane_id();
-    const int w = threadIdx.x >> 6;
-    uint32_t nseg = 0;  // wave-uniform fill of seg[w]
-    const uint64_t first = ((uint64_t)blockIdx.x * kWaves + w) * (64 * kSteps);
-    for (int step = 0; step < kSteps; step++) {
-        const uint64_t i0 = first + (uint64_t)step * 64;
-        if (i0 >= n) break;  // uniform
-        const uint64_t i = i0 + lane;
-        const bool valid = i < n;
-        uint32_t r = 0, q = 0;
-        if (valid) {
-            const uint64_t a = anchors[i];
-            r = (uint32_t)a;
-            q = (uint32_t)(a >> 32);
-        }
-        // An anchor outside the sequences scores 0 on both sides: flag 0.
-        const bool inrange = valid && r <= wp.n_ref && q <= wp.n_qry;
-        const uint32_t wr = (inrange ? r : 0u) + (uint32_t)(kPad4 - kLead);
-        const uint32_t wq = (inrange ? q : 0u) + (uint32_t)(kPad4 - kLead);
-        uint32_t WR[kWinDw], WQ[kWinDw];
-        load_window(ref4, wr & ~7u, WR);
-        load_window(qry4, wq & ~7u, WQ);
-        const uint32_t shr = (wr & 7u) * 4u, shq = (wq & 7u) * 4u;
+    __device__ __forceinline__ void load(bool in, uint32_t r, uint32_t q,
+                                         const uint32_t *__restrict__ ref4,
+                                         const uint32_t *__restrict__ qry4) {
+        inrange = in;
+        const uint32_t wr = (in ? r : 0u) + (uint32_t)(kPad4 - 8 * LB);
+        const uint32_t wq = (in ? q : 0u) + (uint32_t)(kPad4 - 8 * LB);
+        load_window<W>(ref4, wr & ~7u, R);
+        load_window<W>(qry4, wq & ~7u, Q);
+        shr = (wr & 7u) * 4u;
+        shq = (wq & 7u) * 4u;
+    }
 
+    __device__ __forceinline__ int decide(const int16_t *tab, const WindowParams &wp) const {
         bool keep = false;
         int32_t rstar = 0;
-        // right: bases r + 8k .. r + 8k + 7 are window dword 9 + k onward
+        // right: bases r + 8k .. r + 8k + 7 are window dword LB + k onward
         bool act = inrange;
         int32_t d = 0, dmax = 0, s = 0;
 #pragma unroll
-        for (int k = 0; k < kRightBlocks; k++) {
+        for (int k = 0; k < RB; k++) {
             if (__ballot(act) == 0) break;
             if (act) {
-                const uint32_t R = __builtin_amdgcn_alignbit(WR[10 + k], WR[9 + k], shr);
-                const uint32_t Q = __builtin_amdgcn_alignbit(WQ[10 + k], WQ[9 + k], shq);
-                block8<true>(tab, R, Q, d, dmax, s);
+                const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB + k + 1], R[LB + k], shr);
+                const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB + k + 1], Q[LB + k], shq);
+                block8<true>(tab, Rb, Qb, d, dmax, s);
                 const int32_t best = s + d;
                 if (dmax > wp.xdrop) {
                     act = false;
@@ -307,18 +304,18 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
             }
         }
         bool undecided = act;
-        // left: bases r - 8k - 8 .. r - 8k - 1 are window dword 8 - k onward
+        // left: bases r - 8k - 8 .. r - 8k - 1 are window dword LB - 1 - k onward
         act = inrange && !keep && !undecided;
         d = 0;
         dmax = 0;
         s = 0;
 #pragma unroll
-        for (int k = 0; k < kLeftBlocks; k++) {
+        for (int k = 0; k < LB; k++) {
             if (__ballot(act) == 0) break;
             if (act) {
-                const uint32_t R = __builtin_amdgcn_alignbit(WR[9 - k], WR[8 - k], shr);
-                const uint32_t Q = __builtin_amdgcn_alignbit(WQ[9 - k], WQ[8 - k], shq);
-                block8<false>(tab, R, Q, d, dmax, s);
+                const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB - k], R[LB - 1 - k], shr);
+                const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB - k], Q[LB - 1 - k], shq);
+                block8<false>(tab, Rb, Qb, d, dmax, s);
                 const int32_t tot = rstar + s + d;
                 if (dmax > wp.xdrop) {
                     act = false;
@@ -330,40 +327,141 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
             }
         }
         undecided = undecided || act;
-
-        if (valid && !undecided) flags[i] = keep ? 1 : 0;
-        const bool dfr = valid && undecided;
-        const uint64_t m = __ballot(dfr);
-        if (m) {
-            const uint32_t c = (uint32_t)__popcll(m);
-            if (nseg + c > (uint32_t)kSeg) {
-                // full: move this wave's collection to the global list now
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                uint32_t base = 0;
-                if (lane == 0) base = atomicAdd(defer_cnt, nseg);
-                base = __shfl(base, 0, 64);
-                for (uint32_t j = lane; j < nseg; j += 64) defer[base + j] = seg[w][j];
-                nseg = 0;
-            }
-            if (dfr) seg[w][nseg + lane_rank(m)] = (uint32_t)i;
-            nseg += c;
-        }
+        return undecided ? 2 : (keep ? 1 : 0);
     }
+};
+
+// An anchor outside the sequences scores 0 on both sides: flag 0 without a walk.
+__device__ __forceinline__ bool in_range(bool valid, uint64_t a, const WindowParams &wp) {
+    return valid && (uint32_t)a <= wp.n_ref && (uint32_t)(a >> 32) <= wp.n_qry;
+}
+
+// Deferred indices are gathered per wave in LDS and reserved in the global list once per
+// workgroup (a full wave segment is flushed on its own).
+struct DeferSeg {
+    uint32_t (*seg)[kSeg];
+    uint32_t *seg_n;
+    uint32_t *blk_base;
+};
+
+__device__ __forceinline__ void defer_push(uint32_t *seg, uint32_t &nseg, bool dfr, uint32_t i,
+                                           uint32_t *__restrict__ defer,
+                                           uint32_t *__restrict__ defer_cnt) {
+    const int lane = lane_id();
+    const uint64_t m = __ballot(dfr);
+    if (!m) return;
+    const uint32_t c = (uint32_t)__popcll(m);
+    if (nseg + c > (uint32_t)kSeg) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(defer_cnt, nseg);
+        base = __shfl(base, 0, 64);
+        for (uint32_t j = lane; j < nseg; j += 64) defer[base + j] = seg[j];
+        nseg = 0;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (dfr) seg[nseg + lane_rank(m)] = i;
+    nseg += c;
+}
+
+// All waves of the block call this once at the end.
+__device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_t *seg_n,
+                                                  uint32_t *blk_base, uint32_t nseg,
+                                                  uint32_t *__restrict__ defer,
+                                                  uint32_t *__restrict__ defer_cnt) {
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
     if (lane == 0) seg_n[w] = nseg;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t tot = 0;
         for (int v = 0; v < kWaves; v++) tot += seg_n[v];
-        blk_base = tot ? atomicAdd(defer_cnt, tot) : 0u;
+        *blk_base = tot ? atomicAdd(defer_cnt, tot) : 0u;
     }
     __syncthreads();
-    uint32_t base = blk_base;
+    uint32_t base = *blk_base;
     for (int v = 0; v < w; v++) base += seg_n[v];
     for (uint32_t j = lane; j < nseg; j += 64) defer[base + j] = seg[w][j];
 }
 
-__global__ void k_zero_u32(uint32_t *p) { *p = 0; }
+// First stage: every anchor, consecutive 64-anchor steps per wave.
+template <int RB, int LB>
+__global__ __launch_bounds__(kThreads) void k_gate_window(
+    const uint64_t *__restrict__ anchors, uint32_t n, uint8_t *__restrict__ flags,
+    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
+    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    __shared__ int16_t tab[kWinTab];
+    __shared__ uint32_t seg[kWaves][kSeg];
+    __shared__ uint32_t seg_n[kWaves];
+    __shared__ uint32_t blk_base;
+    if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    __syncthreads();
+
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t nseg = 0;
+    const uint64_t first = ((uint64_t)blockIdx.x * kWaves + w) * (64 * kSteps);
+    for (int step = 0; step < kSteps; step++) {
+        const uint64_t i0 = first + (uint64_t)step * 64;
+        if (i0 >= n) break;  // uniform
+        const uint64_t i = i0 + lane;
+        const bool valid = i < n;
+        const uint64_t a = valid ? anchors[i] : 0ull;
+        Win<RB, LB> win;
+        win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4);
+        const int res = win.decide(tab, wp);
+        if (valid && res != 2) flags[i] = (uint8_t)res;
+        defer_push(seg[w], nseg, valid && res == 2, (uint32_t)i, defer, defer_cnt);
+    }
+    defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
+}
+
+// Later stage: the anchors listed by the previous stage (*count of them), wider windows.
+template <int RB, int LB>
+__global__ __launch_bounds__(kThreads) void k_gate_window_list(
+    const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ list,
+    const uint32_t *__restrict__ count, uint8_t *__restrict__ flags,
+    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
+    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    __shared__ int16_t tab[kWinTab];
+    __shared__ uint32_t seg[kWaves][kSeg];
+    __shared__ uint32_t seg_n[kWaves];
+    __shared__ uint32_t blk_base;
+    if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    __syncthreads();
+
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t nseg = 0;
+    const uint32_t total = *count;
+    const uint64_t stride = (uint64_t)gridDim.x * kWaves * 64;
+    for (uint64_t t0 = ((uint64_t)blockIdx.x * kWaves + w) * 64; t0 < total; t0 += stride) {
+        const uint64_t t = t0 + lane;
+        const bool valid = t < total;
+        uint32_t i = 0, r = 0, q = 0;
+        if (valid) {
+            i = list[t];
+            const uint64_t a = anchors[i];
+            r = (uint32_t)a;
+            q = (uint32_t)(a >> 32);
+        }
+        Win<RB, LB> win;
+        win.load(valid && r <= wp.n_ref && q <= wp.n_qry, r, q, ref4, qry4);
+        const int res = win.decide(tab, wp);
+        if (valid && res != 2) flags[i] = (uint8_t)res;
+        defer_push(seg[w], nseg, valid && res == 2, i, defer, defer_cnt);
+    }
+    defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
+}
+
+__global__ void k_zero_u32x2(uint32_t *p) {
+    p[0] = 0;
+    p[1] = 0;
+}
+
+
 
 }  // namespace
 
@@ -424,15 +522,27 @@ hipError_t launch_gate_list(int block_bases, const uint64_t *anchors, const uint
     return hipGetLastError();
 }
 
-hipError_t launch_gate_window(const uint64_t *anchors, uint32_t n, uint8_t *flags,
-                              const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
-                              uint32_t *defer, uint32_t *defer_cnt, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, defer_cnt);
+hipError_t launch_gate_window(bool two_stage, const uint64_t *anchors, uint32_t n,
+                              uint8_t *flags, const uint32_t *ref4, const uint32_t *qry4,
+                              const WindowParams &wp, uint32_t *list1, uint32_t *list2,
+                              uint32_t *cnt, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
     if (n == 0) return hipGetLastError();
     const uint64_t per_block = (uint64_t)kWaves * 64 * kSteps;
     const uint32_t blocks = (uint32_t)(((uint64_t)n + per_block - 1) / per_block);
-    hipLaunchKernelGGL(k_gate_window, dim3(blocks), dim3(kThreads), 0, s, anchors, n, flags,
-                       ref4, qry4, wp, defer, defer_cnt);
+    if (!two_stage) {  // its leftovers go straight to the exact walk
+        hipLaunchKernelGGL((k_gate_window<kOneRight, kOneLeft>), dim3(blocks), dim3(kThreads), 0,
+                           s, anchors, n, flags, ref4, qry4, wp, list2, cnt + 1);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_gate_window<kStage1Right, kStage1Left>), dim3(blocks), dim3(kThreads), 0,
+                       s, anchors, n, flags, ref4, qry4, wp, list1, cnt);
+    // the second stage strides over whatever the first left, up to all n anchors
+    const uint32_t blocks2 =
+        (uint32_t)std::min<uint64_t>(((uint64_t)n + kWaves * 64 - 1) / (kWaves * 64), 4096);
+    hipLaunchKernelGGL((k_gate_window_list<kStage2Right, kStage2Left>), dim3(blocks2),
+                       dim3(kThreads), 0, s, anchors, list1, cnt, flags, ref4, qry4, wp, list2,
+                       cnt + 1);
     return hipGetLastError();
 }
 
