@@ -85,9 +85,9 @@ typedef struct {
  *  device        HIP device ordinal the engine lives on.
  *  gate_mode     0 = windowed score gate when it is exact for these parameters (eight-base
  *                blocks, 16-bit pair scores), else the exact per-base walk; 1 = always the
- *                per-base walk; 2 = always windowed, one stage; 3 = always windowed, two
- *                stages (2 and 3 fail with HSPZ_E_INVALID if not exact).  Every mode
- *                writes the same flags ("D. Score gate", D.2).
+ *                per-base walk; 2 = always windowed; 3 = always windowed with a narrower
+ *                first window (2 and 3 fail with HSPZ_E_INVALID if not exact).  Every
+ *                mode writes the same flags ("D. Score gate", D.2).
  */
 typedef struct {
     const char *seed_pattern;
@@ -228,10 +228,10 @@ int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64
                           uint64_t *total_steps, void *stream);
 
 /* How the last hspz_score_gate call split its anchors when it took the window path:
- * *n_stage2 walked past the first of two windows (32 bases right of the anchor, 56 left;
- * gate_mode 3 only, else 0) and went to the second (64 and 96); *n_exact walked past the
- * last window (48 and 72 with one stage) and were decided by the exact per-base walk.
- * Synchronises stream.  Errors: HSPZ_E_STATE if that call did not take the window path. */
+ * *n_stage2 walked past the first window (48 bases right of the anchor and 72 left, or
+ * 32 and 56 with gate_mode 3) and went to the second (64 and 96); *n_exact walked past
+ * that too and were decided by the exact per-base walk.  Synchronises stream.
+ * Errors: HSPZ_E_STATE if that call did not take the window path. */
 int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2, uint64_t *n_exact,
                              void *stream);
 

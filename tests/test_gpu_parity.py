@@ -133,12 +133,9 @@ def test_gate_on_arbitrary_anchors(gate_mode, seed):
     got = f.cpu().numpy()
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, f"{bad.size} flags differ, first anchors {a[bad[:5]]}"
-    if gate_mode == 3:
+    if gate_mode >= 2:
         n2, nx = eng.debug_gate_deferred()
         assert 0 < n2 < a.size and 0 < nx <= n2
-    elif gate_mode == 2:
-        n2, nx = eng.debug_gate_deferred()
-        assert n2 == 0 and 0 < nx < a.size
 
 
 @pytest.mark.parametrize("gate_mode", [2, 3])
@@ -161,7 +158,7 @@ def test_window_gate_defers_long_walks(gate_mode):
     assert np.array_equal(f.cpu().numpy(), want)
     # every anchor walks past both windows (none sits within a window of both ends)
     n2, nx = eng.debug_gate_deferred()
-    assert n2 == (a.size if gate_mode == 3 else 0) and nx == a.size
+    assert n2 == a.size and nx == a.size
 
 
 @pytest.mark.parametrize("strand", ["+", "-"])

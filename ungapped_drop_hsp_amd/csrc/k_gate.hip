@@ -205,13 +205,13 @@ __global__ __launch_bounds__(kThreads) void k_gate_list(const uint64_t *__restri
 // ------------------------------------------------------------------ window path
 
 constexpr int kSteps = 32;  // 64-anchor steps per wave (first window stage)
-// Window sizes, in blocks of eight bases (right of the anchor, left of it).  One stage of
-// (6, 9) decides about 98.4% of random anchors on the 50 Mb workload.  The two-stage
-// form starts narrower, (4, 7), deciding about 86%, and hands the rest to a second
-// stage of (8, 12) that decides all but about 0.15%; it does fewer block steps but
-// fetches more, and the two measure within a few percent of each other.
-constexpr int kOneRight = 6, kOneLeft = 9;
-constexpr int kStage1Right = 4, kStage1Left = 7;
+// Window sizes, in blocks of eight bases (right of the anchor, left of it).  The first
+// stage sees every anchor: (6, 9) decides about 98.4% of random anchors on the 50 Mb
+// workload; the narrower (4, 7) about 86%, with fewer block steps but more leftovers.
+// A second stage of (8, 12) takes the first stage's leftovers and passes on about 0.15%
+// of all anchors to the exact walk.
+constexpr int kWideRight = 6, kWideLeft = 9;
+constexpr int kNarrowRight = 4, kNarrowLeft = 7;
 constexpr int kStage2Right = 8, kStage2Left = 12;
 constexpr int kSeg = 512;   // LDS slots per wave for deferred anchor indices
 
@@ -522,24 +522,23 @@ hipError_t launch_gate_list(int block_bases, const uint64_t *anchors, const uint
     return hipGetLastError();
 }
 
-hipError_t launch_gate_window(bool two_stage, const uint64_t *anchors, uint32_t n,
-                              uint8_t *flags, const uint32_t *ref4, const uint32_t *qry4,
-                              const WindowParams &wp, uint32_t *list1, uint32_t *list2,
-                              uint32_t *cnt, hipStream_t s) {
+hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
+                              const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
+                              uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
     hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
     if (n == 0) return hipGetLastError();
     const uint64_t per_block = (uint64_t)kWaves * 64 * kSteps;
     const uint32_t blocks = (uint32_t)(((uint64_t)n + per_block - 1) / per_block);
-    if (!two_stage) {  // its leftovers go straight to the exact walk
-        hipLaunchKernelGGL((k_gate_window<kOneRight, kOneLeft>), dim3(blocks), dim3(kThreads), 0,
-                           s, anchors, n, flags, ref4, qry4, wp, list2, cnt + 1);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((k_gate_window<kStage1Right, kStage1Left>), dim3(blocks), dim3(kThreads), 0,
-                       s, anchors, n, flags, ref4, qry4, wp, list1, cnt);
+    if (narrow)
+        hipLaunchKernelGGL((k_gate_window<kNarrowRight, kNarrowLeft>), dim3(blocks),
+                           dim3(kThreads), 0, s, anchors, n, flags, ref4, qry4, wp, list1, cnt);
+    else
+        hipLaunchKernelGGL((k_gate_window<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads),
+                           0, s, anchors, n, flags, ref4, qry4, wp, list1, cnt);
     // the second stage strides over whatever the first left, up to all n anchors
+    const uint32_t cap2 = narrow ? n : n / 8 + 1;
     const uint32_t blocks2 =
-        (uint32_t)std::min<uint64_t>(((uint64_t)n + kWaves * 64 - 1) / (kWaves * 64), 4096);
+        (uint32_t)std::min<uint64_t>(((uint64_t)cap2 + kWaves * 64 - 1) / (kWaves * 64), 4096);
     hipLaunchKernelGGL((k_gate_window_list<kStage2Right, kStage2Left>), dim3(blocks2),
                        dim3(kThreads), 0, s, anchors, list1, cnt, flags, ref4, qry4, wp, list2,
                        cnt + 1);
