@@ -51,6 +51,26 @@ def parse():
     return ap.parse_args()
 
 
+def gate_traffic(workload: str):
+    """Measured fabric bytes per score-gate call from the committed counter summary.
+
+    The summary was taken with rocprofv3 FETCH_SIZE / WRITE_SIZE runs and calibrated
+    against a plain device copy.  It applies only to the source it was measured on and to
+    the same workload; otherwise None.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "score_gate_traffic_c3_50Mb.json")
+    src = os.path.join(ROOT, "ungapped_drop_hsp_amd", "csrc", "k_gate.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("k_gate_hip_sha256") != sha or not rec["workload"].startswith(workload):
+        return None
+    return rec["hbm_bytes_per_call"]
+
+
 def cpu_baseline(w, budget_s: float):
     """The CPU oracle, as it stands, on a bounded sample of the same pass.
 
@@ -184,7 +204,8 @@ def main():
         hsps_per_s=r["n_acc"] / (ms_per_step / 1000.0),
         stage_ms=stage_ms,
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
-                      unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS, traffic=None,
+                      unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
+                      traffic=gate_traffic(w.name),
                       kernel="score_gate (two k_gate_window stages + k_gate_list)",
                       launches_per_step=gate_launches // args.steps,
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
