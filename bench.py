@@ -2,11 +2,13 @@
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--cpu-seconds S]
 
-A step is one whole pass over the query's seeds on the forward strand: plan (hit counts,
-global prefix, MAX_HITS chunk cut), then for every chunk the backward expansion, the
-score gate, survivor compaction, exact materialization and accepted-record compaction,
-with the accepted records copied to the host.  The reference index, the query seeds and
-the encoded sequences are resident in HBM before the timed region starts.
+A step is one whole pass over the workload's query seeds, for every strand and query
+batch it names: plan (hit counts, global prefix, MAX_HITS chunk cut), then for every
+chunk the backward expansion, the score gate, survivor compaction, exact materialization
+and accepted-record compaction, with the accepted records copied to the host.  The
+reference index, the query seeds and the encoded sequences are resident in HBM before the
+timed region starts (the engine holds one strand at a time, so each strand is uploaded
+before its own timed passes and the step time sums the strands).
 
 Prints one JSON line: raw anchors/s through the whole pass (``value``), HSPs/s, per-stage
 times from HIP events on the launch stream, the score gate's roofline figures and the
@@ -121,7 +123,7 @@ def main():
         print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
         sys.exit(1)
     import ungapped_drop_hsp_amd as h
-    from ungapped_drop_hsp_amd.pipeline import PassBuffers, StageTimer, run_pass
+    from ungapped_drop_hsp_amd.pipeline import PassBuffers, StageTimer, batches, run_pass
     from workloads import build
 
     t = time.perf_counter()
@@ -134,32 +136,46 @@ def main():
                    xdrop=p["xdrop"], hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"])
     t = time.perf_counter()
     eng.upload_reference(w.ref)
-    eng.upload_query(w.query, strand=0)
     torch.cuda.synchronize()
     upload_s = time.perf_counter() - t
-    ns = eng.num_seeds()
-    print(f"[bench] index + seeds uploaded in {upload_s:.1f} s ({ns} seeds)", file=sys.stderr,
-          flush=True)
+    print(f"[bench] reference index uploaded in {upload_s:.1f} s", file=sys.stderr, flush=True)
 
+    # A step covers every strand and every query batch of the workload.  The engine holds
+    # one query strand at a time, so each strand's seeds are uploaded before its own
+    # warmup and timed passes; the step time is the sum over strands.
     bufs = PassBuffers(0)
-    for _ in range(args.warmup):
-        r = run_pass(eng, 0, ns, bufs)
-    torch.cuda.synchronize()
-    if args.warmup == 0:
-        r = None
-
     timer = StageTimer()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        r = run_pass(eng, 0, ns, bufs, timer=timer)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = 0.0
+    anchors = surv = acc = chunks = seeds = 0
+    chunk_list = []  # (strand, lo, hi) batches of the last step, for the walk statistics
+    for strand in w.strands:
+        t = time.perf_counter()
+        eng.upload_query(w.query, strand=1 if strand == "-" else 0)
+        torch.cuda.synchronize()
+        upload_s += time.perf_counter() - t
+        bs = batches(eng, w.batch_len, w.query.size)
+        seeds += eng.num_seeds()
+        print(f"[bench] strand {strand}: {eng.num_seeds()} seeds in {len(bs)} batch(es)",
+              file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            for lo, hi in bs:
+                run_pass(eng, lo, hi, bufs)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            res = [run_pass(eng, lo, hi, bufs, timer=timer) for lo, hi in bs]
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        anchors += sum(r["total"] for r in res)
+        surv += sum(r["n_surv"] for r in res)
+        acc += sum(r["n_acc"] for r in res)
+        chunks += sum(r["n_chunks"] for r in res)
+        # the walk statistics below run on the current strand's last batches
+        chunk_list = [(strand, lo, hi) for lo, hi in bs]
     print(f"[bench] {args.steps} timed steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
     ms = timer.elapsed_ms()
     ms_per_step = 1000.0 * wall / args.steps
-    anchors = r["total"]
     value = anchors / (ms_per_step / 1000.0)
     stage_ms = {k: sum(v) / args.steps for k, v in ms.items()}
 
@@ -170,19 +186,24 @@ def main():
     gate_ms_avg = sum(gate_ms) / gate_launches
     units_avg = sum(gate_units) / gate_launches
     gate_gbs = GATE_BYTES_PER_ANCHOR * units_avg / (gate_ms_avg * 1e6)
-    steps_total = 0
+    # base steps per anchor and the gate's stage split, over the last strand's batches
+    steps_total = walked = 0
     deferred = [0, 0]
-    for c in range(r["n_chunks"]):
-        ch = eng.get_chunk(c)
-        eng.find_hits(c, bufs.anchors)
-        steps_total += eng.debug_walk_steps(bufs.anchors, ch["n_hits"])
-        eng.score_gate(bufs.anchors, ch["n_hits"], bufs.flags)
-        try:
-            d2, dx = eng.debug_gate_deferred()
-            deferred = [deferred[0] + d2, deferred[1] + dx]
-        except h.HspzError:
-            deferred = None
-    steps_per_anchor = steps_total / max(anchors, 1)
+    for _, lo, hi in chunk_list:
+        _, nch = eng.plan(lo, hi)
+        for c in range(nch):
+            ch = eng.get_chunk(c)
+            bufs.ensure(ch["n_hits"])
+            eng.find_hits(c, bufs.anchors)
+            steps_total += eng.debug_walk_steps(bufs.anchors, ch["n_hits"])
+            walked += ch["n_hits"]
+            eng.score_gate(bufs.anchors, ch["n_hits"], bufs.flags)
+            try:
+                d2, dx = eng.debug_gate_deferred()
+                deferred = [deferred[0] + d2, deferred[1] + dx]
+            except h.HspzError:
+                deferred = None
+    steps_per_anchor = steps_total / max(walked, 1)
     gate_gsteps = steps_per_anchor * units_avg / (gate_ms_avg * 1e6)
 
     if args.copy_probe_mib:
@@ -197,11 +218,11 @@ def main():
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="int32", data="synthetic",
         config=dict(workload=w.name, ref_bp=int(w.ref.size), query_bp=int(w.query.size),
-                    strands="+", seed_pattern=p["seed_pattern"], xdrop=p["xdrop"],
-                    hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"], seeds=ns,
-                    raw_anchors=anchors, chunks=r["n_chunks"], survivors=r["n_surv"],
-                    accepted=r["n_acc"]),
-        hsps_per_s=r["n_acc"] / (ms_per_step / 1000.0),
+                    strands=w.strands, batch_bp=w.batch_len or int(w.query.size),
+                    seed_pattern=p["seed_pattern"], xdrop=p["xdrop"],
+                    hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"], seeds=seeds,
+                    raw_anchors=anchors, chunks=chunks, survivors=surv, accepted=acc),
+        hsps_per_s=acc / (ms_per_step / 1000.0),
         stage_ms=stage_ms,
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
@@ -213,8 +234,8 @@ def main():
         gate_hbm=dict(achieved=gate_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=gate_gbs / HBM_PEAK_GBS, bytes_per_anchor=GATE_BYTES_PER_ANCHOR),
         gate_anchors_per_s=units_avg / (gate_ms_avg / 1000.0),
-        gate_stage2_fraction=None if deferred is None else deferred[0] / max(anchors, 1),
-        gate_exact_fraction=None if deferred is None else deferred[1] / max(anchors, 1),
+        gate_stage2_fraction=None if deferred is None else deferred[0] / max(walked, 1),
+        gate_exact_fraction=None if deferred is None else deferred[1] / max(walked, 1),
         setup_s=dict(generate=gen_s, upload=upload_s),
     )
     if args.cpu_seconds > 0:
