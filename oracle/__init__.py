@@ -64,8 +64,9 @@ def _load():
         "orc_gate": (None, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _P]),
         "orc_gate_totals": (None, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _P, _P]),
         "orc_compact": (_I64, [_P, _I64, _P]),
+        "orc_entropy_bits": (ctypes.c_double, [_P, _I64, _I64, _I64]),
         "orc_materialize": (None, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32,
-                                   _P, _P]),
+                                   _I32, _I32, _P, _P]),
         "orc_compact_hsps": (_I64, [_P, _P, _I64, _P]),
     }
     for name, (res, args) in sig.items():
@@ -239,7 +240,12 @@ def compact(flags) -> np.ndarray:
     return ids[:m].copy()
 
 
-def materialize(anchors_, ids, rcodes, qcodes, sub, n_score, X, T):
+def entropy_bits(rcodes, ref_start: int, length: int) -> float:
+    rc = _c(rcodes, np.uint8)
+    return float(_load().orc_entropy_bits(_ptr(rc), rc.size, ref_start, length))
+
+
+def materialize(anchors_, ids, rcodes, qcodes, sub, n_score, X, T, K=None, entropy_mode=0):
     a = _c(anchors_, np.uint64)
     ids = _c(ids, np.uint32)
     rc = _c(rcodes, np.uint8)
@@ -247,8 +253,8 @@ def materialize(anchors_, ids, rcodes, qcodes, sub, n_score, X, T):
     hsp = np.zeros(max(ids.size, 1), HSP_DTYPE)
     status = np.zeros(max(ids.size, 1), np.uint8)
     _load().orc_materialize(_ptr(a), _ptr(ids), ids.size, _ptr(rc), rc.size, _ptr(qc),
-                            qc.size, _ptr(_sub(sub)), n_score, X, T, _ptr(hsp),
-                            _ptr(status))
+                            qc.size, _ptr(_sub(sub)), n_score, X, T, T if K is None else K,
+                            entropy_mode, _ptr(hsp), _ptr(status))
     return hsp[: ids.size], status[: ids.size]
 
 
@@ -311,7 +317,9 @@ def run_pass(ref: Reference, qcodes: np.ndarray, params: Dict, *, seed_range=Non
                 ids = compact(f)
                 rec["ids"] = ids
                 if "materialize" in stages:
-                    h, st = materialize(a, ids, ref.codes, qcodes, sub, ns, X, T)
+                    h, st = materialize(a, ids, ref.codes, qcodes, sub, ns, X, T,
+                                        K=params["hsp_threshold"],
+                                        entropy_mode=params.get("entropy_mode", 0))
                     rec["hsp"], rec["status"] = h, st
                     rec["accepted"] = compact_hsps(h, st)
         out["chunks"].append(rec)

@@ -6,6 +6,7 @@
  */
 #include "oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -358,16 +359,43 @@ int64_t orc_compact(const uint8_t *flags, int64_t n, uint32_t *ids) {
     return m;
 }
 
+static double orc_xlog2x(int64_t c) {
+    return c > 0 ? (double)c * log2((double)c) : 0.0;
+}
+
+/* reading of the "entropy-adjusted decision" ("E. X-drop materialization", E.5), which
+ * the pages name without defining: the Shannon entropy, in bits, of the A/C/G/T counts
+ * n_b of the reference interval rs..=rs+len (N excluded), n = the sum of the counts:
+ * H = (n log2 n - (nA log2 nA + nC log2 nC + nG log2 nG + nT log2 nT)) / n, summed in
+ * that order in double precision.  Returns -1 when the interval holds no A/C/G/T. */
+double orc_entropy_bits(const uint8_t *rc, int64_t nr, int64_t rs, int64_t len) {
+    int64_t cnt[4] = {0, 0, 0, 0};
+    for (int64_t t = 0; t <= len; t++) {
+        int64_t p = rs + t;
+        if (p >= 0 && p < nr && rc[p] < 4) cnt[rc[p]]++;
+    }
+    int64_t n = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    if (n == 0) return -1.0;
+    double s = orc_xlog2x(cnt[0]);
+    s = s + orc_xlog2x(cnt[1]);
+    s = s + orc_xlog2x(cnt[2]);
+    s = s + orc_xlog2x(cnt[3]);
+    return (orc_xlog2x(n) - s) / (double)n;
+}
+
 /* "E. X-drop materialization", E.1-E.5: each survivor's anchor is extended exactly to
  * both sides; the left extent m shifts both starts, the record's len is the inclusive
  * extent m + k - 1 so the interval is start..=start+len, the score is L* + R*.
- * reading: with the entropy-adjusted rule left undefined, a record is accepted iff its
- * score reaches T (status 1), else rejected (status 0).  The record is written either
- * way; only accepted slots are part of the output. */
+ * The decision (reading): entropy_mode 0 accepts iff the score reaches T; entropy_mode 1
+ * also requires score * H >= 2 K with H the interval's entropy in bits (orc_entropy_bits;
+ * an interval without A/C/G/T is rejected), i.e. the score scaled by H / 2 -- the
+ * fraction of the 2-bit maximum -- must still reach K.  Status 1 = accepted, 0 =
+ * rejected.  The record is written either way; only accepted slots are output. */
 void orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_surv,
                      const uint8_t *rc, int64_t nr, const uint8_t *qc, int64_t nq,
                      const int32_t *sub, int32_t n_score, int32_t xdrop, int32_t T,
-                     orc_segment_pair *hsp, uint8_t *status) {
+                     int32_t K, int32_t entropy_mode, orc_segment_pair *hsp,
+                     uint8_t *status) {
     for (int64_t i = 0; i < n_surv; i++) {
         uint64_t a = anchors[ids[i]];
         int64_t r = (int64_t)(a & 0xFFFFFFFFull);
@@ -379,7 +407,12 @@ void orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_sur
         hsp[i].query_start = (uint32_t)(q - m);
         hsp[i].len = (uint32_t)(m + k - 1);
         hsp[i].score = (int32_t)(L + R);
-        status[i] = (L + R >= (int64_t)T) ? 1 : 0;
+        int ok = L + R >= (int64_t)T;
+        if (ok && entropy_mode == 1) {
+            double H = orc_entropy_bits(rc, nr, r - m, m + k - 1);
+            ok = H >= 0.0 && (double)(L + R) * H >= 2.0 * (double)K;
+        }
+        status[i] = ok ? 1 : 0;
     }
 }
 

@@ -363,3 +363,73 @@ def test_random_background_anchors_do_not_survive():
     n = sum(ch["anchors"].size for ch in out["chunks"])
     s = sum(ch["ids"].size for ch in out["chunks"])
     assert n > 100 and s == 0
+
+
+# ------------------------------------------------------------------ entropy-adjusted accept
+
+def _shannon_bits(codes):
+    """Entropy in bits of the A/C/G/T composition, from -sum p log2 p (N dropped)."""
+    c = np.bincount(codes[codes < 4], minlength=4).astype(np.float64)
+    n = c.sum()
+    p = c[c > 0] / n
+    return float(-(p * np.log2(p)).sum())
+
+
+def test_entropy_closed_forms():
+    enc = oracle.encode
+    assert oracle.entropy_bits(enc(b"AAAAAAAAAA"), 0, 9) == 0.0          # one letter: 0 bits
+    assert oracle.entropy_bits(enc(b"ACGT" * 16), 0, 63) == 2.0          # uniform, n = 64: 2 bits
+    assert oracle.entropy_bits(enc(b"AC" * 32), 0, 63) == 1.0            # two letters: 1 bit
+    assert oracle.entropy_bits(enc(b"NNNNN"), 0, 4) == -1.0              # nothing to count
+    # N inside the interval is excluded; the interval is closed (len + 1 bases)
+    assert oracle.entropy_bits(enc(b"ANCNGNT"), 0, 6) == 2.0
+    assert oracle.entropy_bits(enc(b"ACGTA"), 0, 3) == 2.0
+    assert oracle.entropy_bits(enc(b"ACGTA"), 1, 3) == 2.0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_entropy_matches_shannon_definition(seed):
+    rng = np.random.default_rng(seed)
+    ref, _ = random_pair(seed, 3000, 1, n_frac=0.05, gc=0.2 + 0.15 * seed)
+    rc = oracle.encode(ref)
+    for _ in range(200):
+        s = int(rng.integers(0, rc.size - 1))
+        l = int(rng.integers(0, min(400, rc.size - s - 1)))
+        want = _shannon_bits(rc[s:s + l + 1])
+        got = oracle.entropy_bits(rc, s, l)
+        if (rc[s:s + l + 1] < 4).any():
+            assert abs(got - want) < 1e-12
+        else:
+            assert got == -1.0
+
+
+def test_entropy_mode_decision():
+    # records from planted homologs; mode 1 keeps a record iff score * H >= 2K as well
+    ref, qry = random_pair(21, 20_000, 20_000, plant=40, plant_len=(60, 500), identity=0.95,
+                           gc=0.5)
+    # low-complexity planted copies too, so that the entropy test rejects some records
+    ref[1000:1120] = np.frombuffer(b"AT" * 60, np.uint8)
+    qry[5000:5120] = np.frombuffer(b"AT" * 60, np.uint8)
+    ref[3000:3090] = np.frombuffer(b"A" * 90, np.uint8)
+    qry[8000:8090] = np.frombuffer(b"A" * 90, np.uint8)
+    K = 600
+    p = dict(seed_pattern="1101011", sub=SUB, n_score=NS, xdrop=X, hsp_threshold=K,
+             max_hits=0)
+    R = oracle.Reference(ref, p["seed_pattern"])
+    qc = oracle.encode(qry)
+    o0 = oracle.run_pass(R, qc, p)
+    o1 = oracle.run_pass(R, qc, dict(p, entropy_mode=1))
+    T = oracle.keep_threshold(K)
+    n_rej = 0
+    for c0, c1 in zip(o0["chunks"], o1["chunks"]):
+        assert np.array_equal(c0["hsp"], c1["hsp"])  # the records do not depend on the mode
+        for h, s0, s1 in zip(c0["hsp"], c0["status"], c1["status"]):
+            H = _shannon_bits(R.codes[h["ref_start"]:h["ref_start"] + h["len"] + 1])
+            margin = float(h["score"]) * H - 2.0 * K
+            if abs(margin) < 1e-6 * K:
+                continue
+            assert s0 == (h["score"] >= T)
+            assert s1 == (s0 and margin > 0)
+            n_rej += int(s0 and not s1)
+        assert set(map(bytes, c1["accepted"])) <= set(map(bytes, c0["accepted"]))
+    assert n_rej > 0
