@@ -88,6 +88,13 @@ typedef struct {
  *                per-base walk; 2 = always windowed; 3 = always windowed with a narrower
  *                first window (2 and 3 fail with HSPZ_E_INVALID if not exact).  Every
  *                mode writes the same flags ("D. Score gate", D.2).
+ *  entropy_mode  the accept decision of hspz_materialize ("E. X-drop materialization",
+ *                E.5, which names an entropy-adjusted decision without a formula):
+ *                0 = accept iff score >= T; 1 = also require score * H >= 2 * K, where H
+ *                is the Shannon entropy in bits of the A/C/G/T composition of the
+ *                record's reference interval (N excluded), computed in double precision
+ *                as (n log2 n - sum_b n_b log2 n_b) / n; no A/C/G/T in the interval
+ *                rejects.
  */
 typedef struct {
     const char *seed_pattern;
@@ -100,6 +107,7 @@ typedef struct {
     int32_t chunk_walk;
     int32_t device;
     int32_t gate_mode;
+    int32_t entropy_mode;
 } hspz_params;
 
 /* Create an engine on params->device and compute the keep threshold T once: the least
@@ -190,8 +198,8 @@ int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n, uint32
  * X-drop rule as the gate, keeping the earliest base that attains each side's best.
  * With left extent m and right extent k the record is
  * {r - m, q - m, m + k - 1, L* + R*}.  d_status[i] = 1 if the record is accepted
- * (score >= T), else 0; d_hsp[i] is written in either case and is meaningful only when
- * accepted.  Errors: HSPZ_E_STATE, HSPZ_E_HIP. */
+ * (score >= T, and with entropy_mode 1 also score * H >= 2K, see hspz_params), else 0;
+ * d_hsp[i] is written in either case and is meaningful only when accepted.  Errors: HSPZ_E_STATE, HSPZ_E_HIP. */
 int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors, const uint32_t *d_ids,
                      uint64_t n_surv, hspz_segment_pair *d_hsp, uint8_t *d_status,
                      void *stream);

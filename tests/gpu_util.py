@@ -18,13 +18,14 @@ def engine(params, expand_mode=0, chunk_walk=0, max_hits=None, gate_mode=0):
                     n_score=params["n_score"], xdrop=params["xdrop"],
                     hsp_threshold=params["hsp_threshold"],
                     max_hits=params["max_hits"] if max_hits is None else max_hits,
-                    expand_mode=expand_mode, chunk_walk=chunk_walk, gate_mode=gate_mode)
+                    expand_mode=expand_mode, chunk_walk=chunk_walk, gate_mode=gate_mode,
+                    entropy_mode=params.get("entropy_mode", 0))
 
 
-def params_of(pattern, max_hits=0, sub=None, xdrop=910, K=3000, n_score=-100):
+def params_of(pattern, max_hits=0, sub=None, xdrop=910, K=3000, n_score=-100, entropy_mode=0):
     from workloads import HOXD70
     return dict(seed_pattern=pattern, sub=HOXD70 if sub is None else sub, n_score=n_score,
-                xdrop=xdrop, hsp_threshold=K, max_hits=max_hits)
+                xdrop=xdrop, hsp_threshold=K, max_hits=max_hits, entropy_mode=entropy_mode)
 
 
 def gpu_full_pass(eng, ref, qry, strand="+", seed_range=None, bufs=None):

@@ -353,3 +353,30 @@ def test_config_full_parity(cfg):
     r = gpu_full_pass(engine(p), w.ref, w.query)
     assert_pass_equal(r, o)
     print(f"config {cfg}: anchors {r['total']} survivors {r['n_surv']} accepted {r['n_acc']}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_entropy_mode_parity(seed):
+    # planted homologs plus low-complexity copies, which the entropy-adjusted decision
+    # rejects although their scores pass T
+    ref, qry = random_pair(30 + seed, 20_000, 20_000, plant=40, plant_len=(60, 500),
+                           identity=0.95, n_frac=0.01)
+    ref[1000:1120] = np.frombuffer(b"AT" * 60, np.uint8)
+    qry[5000:5120] = np.frombuffer(b"AT" * 60, np.uint8)
+    ref[3000:3090] = np.frombuffer(b"A" * 90, np.uint8)
+    qry[8000:8090] = np.frombuffer(b"A" * 90, np.uint8)
+    ref[9000:9200] = np.frombuffer(b"AAGAAG" * 33 + b"AA", np.uint8)
+    qry[12000:12200] = np.frombuffer(b"AAGAAG" * 33 + b"AA", np.uint8)
+    p = params_of("1101011", K=600, entropy_mode=1)
+    o, _, _ = oracle_pass(ref, qry, p)
+    n_surv = sum(c["ids"].size for c in o["chunks"])
+    n_acc = sum(c["accepted"].size for c in o["chunks"])
+    assert 0 < n_acc < n_surv
+    assert_pass_equal(gpu_full_pass(engine(p), ref, qry), o)
+
+
+def test_entropy_mode_config1():
+    w = build(1)
+    p = dict(w.params(), entropy_mode=1)
+    o, _, _ = oracle_pass(w.ref, w.query, p)
+    assert_pass_equal(gpu_full_pass(engine(p), w.ref, w.query), o)

@@ -302,6 +302,8 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "expand_mode must be 0, 1 or 2");
     if (p->chunk_walk < 0 || p->chunk_walk > 1)
         return fail(nullptr, HSPZ_E_INVALID, "chunk_walk must be 0 or 1");
+    if (p->entropy_mode < 0 || p->entropy_mode > 1)
+        return fail(nullptr, HSPZ_E_INVALID, "entropy_mode must be 0 or 1");
     if (p->gate_mode < 0 || p->gate_mode > 3)
         return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2 or 3");
     int ndev = 0;
@@ -343,6 +345,8 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     }
     e->sp.xdrop = p->xdrop;
     e->sp.T = e->T;
+    e->sp.K = p->hsp_threshold;
+    e->sp.entropy_mode = p->entropy_mode;
     // Windowed gate: exact when eight-base blocks are (B = 8 above) and every pair score,
     // the edge score included, fits 16 bits.
     e->window_ok = e->block_bases == 8 && p->xdrop + 1 <= 32767;

@@ -43,6 +43,8 @@ struct ScoreParams {
     int32_t T;
     uint32_t n_ref;
     uint32_t n_qry;
+    int32_t K;             // hsp_threshold, for the entropy-adjusted decision
+    int32_t entropy_mode;  // 0 = accept iff score >= T; 1 = also score * H >= 2K
 };
 
 // Constants of the windowed gate.  tab[r * 16 + q] is the 16-bit pair score for codes

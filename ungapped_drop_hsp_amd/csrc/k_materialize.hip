@@ -5,8 +5,9 @@
 // (seeded with the best so far) gives the running best, and a ballot of lanes whose
 // drawdown exceeds xdrop marks the first drop.  The running best in the lane before the
 // first drop is the tile's best; its extent is the lowest lane attaining it, so an equal
-// later maximum never moves the endpoint.  Lane 0 stores the 16-byte record and the
-// status.
+// later maximum never moves the endpoint.  With the entropy-adjusted decision on, the
+// wave then counts the record's reference bases (entropy_accept).  Lane 0 stores the
+// 16-byte record and the status.
 #include <climits>
 
 #include "hspz_internal.h"
@@ -50,6 +51,37 @@ __device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp
     ext_out = ext;
 }
 
+__device__ __forceinline__ double xlog2x(uint32_t c) {
+#pragma clang fp contract(off)
+    return c > 0 ? (double)c * log2((double)c) : 0.0;
+}
+
+// Entropy-adjusted decision (the pages name it without a formula; this is the engine's
+// reading): with n_b the A/C/G/T counts of the reference interval rs..=rs+len (N
+// excluded) and n their sum, H = (n log2 n - sum_b n_b log2 n_b) / n bits, summed A, C,
+// G, T in that order in double precision without contraction; accept iff n > 0 and
+// score * H >= 2K.  The whole wave counts the interval, 64 bases per step.
+__device__ __forceinline__ bool entropy_accept(const uint8_t *__restrict__ ref, uint32_t rs,
+                                               uint32_t len, int64_t score, int32_t K) {
+#pragma clang fp contract(off)
+    const int l = lane_id();
+    uint32_t cnt[4] = {0, 0, 0, 0};
+    for (uint64_t base = 0; base <= len; base += 64) {
+        const uint64_t t = base + l;
+        const uint32_t code = t <= len ? (uint32_t)(ref[rs + t] >> kRefShift) : 7u;
+#pragma unroll
+        for (int c = 0; c < 4; c++) cnt[c] += (uint32_t)__popcll(__ballot(code == (uint32_t)c));
+    }
+    const uint32_t n = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    if (n == 0) return false;
+    double s = xlog2x(cnt[0]);
+    s = s + xlog2x(cnt[1]);
+    s = s + xlog2x(cnt[2]);
+    s = s + xlog2x(cnt[3]);
+    const double H = (xlog2x(n) - s) / (double)n;
+    return (double)score * H >= 2.0 * (double)K;
+}
+
 __global__ __launch_bounds__(kThreads) void k_materialize(
     const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ ids, uint32_t n_surv,
     hspz_segment_pair *__restrict__ hsp, uint8_t *__restrict__ status,
@@ -66,15 +98,17 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
     uint32_t k, m;
     exact_walk<+1>(tab, ref + (bad ? sp.n_ref : r), qry + (bad ? sp.n_qry : q), sp.xdrop, R, k);
     exact_walk<-1>(tab, ref + (bad ? 0u : r), qry + (bad ? 0u : q), sp.xdrop, L, m);
+    const int64_t total = (int64_t)L + (int64_t)R;
+    bool ok = total >= (int64_t)sp.T;  // wave-uniform
+    if (ok && sp.entropy_mode == 1) ok = entropy_accept(ref, r - m, m + k - 1u, total, sp.K);
     if (lane_id() == 0) {
-        const int64_t total = (int64_t)L + (int64_t)R;
         hspz_segment_pair rec;
         rec.ref_start = r - m;
         rec.query_start = q - m;
         rec.len = m + k - 1u;
         rec.score = (int32_t)total;
         hsp[i] = rec;
-        status[i] = total >= (int64_t)sp.T ? 1 : 0;
+        status[i] = ok ? 1 : 0;
     }
 }
 
