@@ -127,20 +127,24 @@ int32_t hspz_keep_threshold(const hspz_engine *engine);
  * the next call on it.  A NULL engine returns the message of the last failed create. */
 const char *hspz_last_error(const hspz_engine *engine);
 
-/* Encode the reference and build its spaced-seed index on the host ("C. Hit
- * discovery", C.1: a cumulative bucket-end table, one entry per packed k-mer, and the
- * concatenated buckets of reference end coordinates, ascending within a bucket), then
- * copy both and the encoded bases to the device.  h_ascii (len bytes, host) is not
- * retained.  len < 2^32 - 64.  Replaces any previous reference and invalidates a plan.
- * Synchronises stream.  Errors: HSPZ_E_INVALID, HSPZ_E_NOMEM, HSPZ_E_HIP. */
+/* Copy the reference to the device, encode it there and build its spaced-seed index
+ * there ("C. Hit discovery", C.1: a cumulative bucket-end table, one entry per packed
+ * k-mer plus a leading 0, and the concatenated buckets of reference end coordinates,
+ * ascending within a bucket; the buckets come from a stable radix sort of (k-mer, end)
+ * pairs listed in position order).  h_ascii (len bytes, host) is not retained; bytes
+ * other than A/C/G/T (either case) encode as N.  len < 2^32 - 257.  Temporary device
+ * memory during the call: about len + 26 bytes per reference window plus 8 * 4^weight
+ * bytes.  Replaces any previous reference and invalidates a plan.  Synchronises stream.
+ * Errors: HSPZ_E_INVALID, HSPZ_E_NOMEM, HSPZ_E_HIP. */
 int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
                           void *stream);
 
-/* Encode one query strand and list its seeds: every window whose care positions are
- * all A/C/G/T, in ascending window position, each with its packed k-mer and its
- * query end coordinate (window start + span).  strand 0 = the sequence as given,
- * 1 = its reverse complement, in the reverse complement's own coordinates.  Replaces
- * the previous query and invalidates a plan.  Synchronises stream.  Errors as above. */
+/* Encode one query strand on the device and list its seeds there: every window whose
+ * care positions are all A/C/G/T, in ascending window position, each with its packed
+ * k-mer and its query end coordinate (window start + span).  strand 0 = the sequence
+ * as given, 1 = its reverse complement, in the reverse complement's own coordinates.
+ * Replaces the previous query and invalidates a plan.  Synchronises stream.  Errors as
+ * above. */
 int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
                       int32_t strand, void *stream);
 
@@ -217,6 +221,15 @@ int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
  * coordinates (either pointer may be NULL).  Synchronous. */
 int hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi, uint32_t *h_kmer,
                    uint32_t *h_q_end);
+
+/* The reference index built by hspz_upload_reference ("C. Hit discovery", C.1):
+ * *n_buckets = 4^weight, *n_pos = the number of indexed reference windows; h_end, if
+ * not NULL, receives the n_buckets + 1 cumulative bucket ends (u32, leading 0) and
+ * h_pos, if not NULL, the n_pos reference end coordinates grouped by k-mer.  Call with
+ * NULL arrays first to learn the sizes.  Synchronous.  Errors: HSPZ_E_STATE without a
+ * reference, HSPZ_E_INVALID for a NULL size pointer. */
+int hspz_get_index(const hspz_engine *engine, uint32_t *h_end, uint32_t *h_pos,
+                   uint64_t *n_buckets, uint64_t *n_pos);
 
 /* Copy the planned batch's per-seed hit counts and global inclusive prefix (u32 each,
  * one per seed of the batch) to the host (either pointer may be NULL).  Synchronous. */

@@ -3,6 +3,7 @@
 The HIP path runs exactly as bench.py runs it (whole query batches, the workload's
 MAX_HITS, default modes).  The oracle cannot redo every anchor's walks at these sizes,
 so each batch is checked like this:
+  - the whole reference index and every seed (k-mer and query end), element by element;
   - every seed count, the whole global prefix and the whole chunk list, element by element;
   - for sampled chunks, every anchor byte;
   - flags on a random sample of anchors plus every anchor the GPU kept;
@@ -101,6 +102,12 @@ def _run_config(cfg, chunk_pick, batch_pick=None, full_plan=True):
     R = oracle.Reference(w.ref, p["seed_pattern"])
     eng = engine(p)
     eng.upload_reference(w.ref)
+    # the whole device index against the oracle's sorted (key, end) list
+    end, pos = eng.get_index()
+    assert np.array_equal(pos, R.ends), "bucket contents differ"
+    assert np.array_equal(end.astype(np.int64),
+                          np.searchsorted(R.keys, np.arange(end.size, dtype=np.uint64)))
+    del end, pos
     bufs = PassBuffers()
     rng = np.random.default_rng(cfg)
     out = []
@@ -109,6 +116,9 @@ def _run_config(cfg, chunk_pick, batch_pick=None, full_plan=True):
         seeds = oracle.query_seeds(qc, p["seed_pattern"])
         eng.upload_query(w.query, strand=1 if strand == "-" else 0)
         assert eng.num_seeds() == seeds[0].size
+        gk, gq = eng.get_seeds(0, seeds[0].size)
+        assert np.array_equal(gk, seeds[0]) and np.array_equal(gq, seeds[1]), "seeds differ"
+        del gk, gq
         bs = batches(eng, w.batch_len, w.query.size)
         # batch ranges agree with the oracle's seed positions
         if w.batch_len:

@@ -30,7 +30,8 @@ ABI_SYMBOLS = (
     "hspz_upload_reference", "hspz_upload_query", "hspz_num_seeds", "hspz_seed_range",
     "hspz_plan", "hspz_get_chunk", "hspz_find_hits", "hspz_score_gate", "hspz_compact",
     "hspz_materialize", "hspz_compact_hsps", "hspz_get_seeds", "hspz_get_plan_arrays",
-    "hspz_debug_plan_counts", "hspz_debug_walk_steps", "hspz_debug_gate_deferred",
+    "hspz_get_index", "hspz_debug_plan_counts", "hspz_debug_walk_steps",
+    "hspz_debug_gate_deferred",
 )
 
 
@@ -79,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "hspz_compact_hsps": (ctypes.c_int, [P, P, P, U64, P, U64, PU64, P]),
         "hspz_get_seeds": (ctypes.c_int, [P, U64, U64, P, P]),
         "hspz_get_plan_arrays": (ctypes.c_int, [P, P, P]),
+        "hspz_get_index": (ctypes.c_int, [P, P, P, PU64, PU64]),
         "hspz_debug_plan_counts": (ctypes.c_int, [P, P, U64, P, PU64, PU32]),
         "hspz_debug_walk_steps": (ctypes.c_int, [P, P, U64, PU64, P]),
         "hspz_debug_gate_deferred": (ctypes.c_int, [P, PU64, PU64, P]),
@@ -250,6 +252,17 @@ class Engine:
         q = np.empty(max(hi - lo, 0), np.uint32)
         self._check(_lib.hspz_get_seeds(self._h, lo, hi, k.ctypes.data, q.ctypes.data))
         return k, q
+
+    def get_index(self) -> Tuple[np.ndarray, np.ndarray]:
+        """(bucket ends with the leading 0, reference ends grouped by k-mer)."""
+        nb, npos = ctypes.c_uint64(), ctypes.c_uint64()
+        self._check(_lib.hspz_get_index(self._h, None, None, ctypes.byref(nb),
+                                        ctypes.byref(npos)))
+        end = np.empty(nb.value + 1, np.uint32)
+        pos = np.empty(max(npos.value, 1), np.uint32)
+        self._check(_lib.hspz_get_index(self._h, end.ctypes.data, pos.ctypes.data,
+                                        ctypes.byref(nb), ctypes.byref(npos)))
+        return end, pos[:npos.value]
 
     def get_plan_arrays(self, n: int) -> Tuple[np.ndarray, np.ndarray]:
         c = np.empty(max(n, 1), np.uint32)

@@ -55,17 +55,6 @@ int dalloc(Engine *e, T *&p, uint64_t count) {
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
-// A,C,G,T in either case -> 0..3, anything else -> N.
-inline uint8_t code_of(uint8_t c) {
-    switch (c) {
-    case 'A': case 'a': return 0;
-    case 'C': case 'c': return 1;
-    case 'G': case 'g': return 2;
-    case 'T': case 't': return 3;
-    default: return kCodeN;
-    }
-}
-
 // Least int32 t with (float)t >= (float)K: the integer form of the single-precision keep
 // comparison.  Searched from K downward and upward; float rounding moves it by at most
 // one ulp of K, so the loops are short.
@@ -77,54 +66,84 @@ int32_t keep_threshold(int32_t K) {
     return (int32_t)t;
 }
 
-// Packed keys of every window of `codes` (0xFFFFFFFF where a care position is N or the
-// window does not fit).
-void window_keys(const std::vector<uint8_t> &codes, const std::vector<int32_t> &care, int span,
-                 std::vector<uint32_t> &keys) {
-    const uint64_t n = codes.size();
-    const uint64_t nw = n >= (uint64_t)span ? n - span + 1 : 0;
-    keys.assign(nw, 0xFFFFFFFFu);
-    const int w = (int)care.size();
-    for (uint64_t p = 0; p < nw; p++) {
-        uint32_t k = 0;
-        int i = 0;
-        for (; i < w; i++) {
-            const uint8_t c = codes[p + care[i]];
-            if (c > 3) break;
-            k = (k << 2) | c;
-        }
-        if (i == w) keys[p] = k;
-    }
-}
+int ensure_compact(Engine *e, uint64_t n);
 
-int upload_padded(Engine *e, uint8_t *&dst, const std::vector<uint8_t> &codes, int shift,
-                  hipStream_t s) {
-    const uint64_t n = codes.size();
-    std::vector<uint8_t> buf(n + 2 * kPad, (uint8_t)(kCodeEdge << shift));
-    for (uint64_t i = 0; i < n; i++) buf[kPad + i] = (uint8_t)(codes[i] << shift);
-    int rc = dalloc(e, dst, buf.size());
-    if (rc) return rc;
-    HIP_TRY(e, hipMemcpyAsync(dst, buf.data(), buf.size(), hipMemcpyHostToDevice, s));
+// Device buffer freed when it goes out of scope (upload temporaries).
+template <class T>
+struct DevBuf {
+    T *p = nullptr;
+    DevBuf() = default;
+    DevBuf(const DevBuf &) = delete;
+    DevBuf &operator=(const DevBuf &) = delete;
+    ~DevBuf() {
+        if (p) (void)hipFree(p);
+    }
+    T *release() {
+        T *q = p;
+        p = nullptr;
+        return q;
+    }
+};
+
+// Inclusive scan of n u32 counts on the device into prefix: block scans, a 64-bit host
+// scan of the block sums, add-back.  The total must fit 32 bits.  Synchronises s.
+int device_scan(Engine *e, uint32_t *counts, uint64_t n, uint32_t *prefix, hipStream_t s) {
+    if (n == 0) return HSPZ_OK;
+    const uint64_t nblk = (n + kScanBlock - 1) / kScanBlock;
+    DevBuf<uint64_t> bs;
+    DevBuf<uint32_t> bo;
+    int rc;
+    if ((rc = dalloc(e, bs.p, nblk)) || (rc = dalloc(e, bo.p, nblk))) return rc;
+    HIP_TRY(e, launch_count_scan(nullptr, counts, n, nullptr, counts, nullptr, prefix, bs.p, s));
+    std::vector<uint64_t> h(nblk);
+    std::vector<uint32_t> off(nblk);
+    HIP_TRY(e, hipMemcpyAsync(h.data(), bs.p, nblk * sizeof(uint64_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(e, hipStreamSynchronize(s));
+    uint64_t acc = 0;
+    for (uint64_t b = 0; b < nblk; b++) {
+        off[b] = (uint32_t)acc;
+        acc += h[b];
+    }
+    if (acc > 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "scan total exceeds 32 bits");
+    HIP_TRY(e, hipMemcpyAsync(bo.p, off.data(), nblk * sizeof(uint32_t), hipMemcpyHostToDevice, s));
+    HIP_TRY(e, launch_add_offsets(prefix, n, bo.p, s));
     HIP_TRY(e, hipStreamSynchronize(s));
     return HSPZ_OK;
 }
 
-// 4-bit copy for the windowed gate: kPad4 edge codes, the sequence, kPad4 edge codes,
-// rounded up to whole 16-byte groups.
-int upload_nibbles(Engine *e, uint32_t *&dst, const std::vector<uint8_t> &codes, hipStream_t s) {
-    const uint64_t n = codes.size();
-    const uint64_t nib = n + 2 * (uint64_t)kPad4;
+// Device seeder front half, shared by both uploads: copy the ASCII sequence to the
+// device, encode the strand into the padded byte array (codes << shift) and the padded
+// 4-bit array, compute every window's key and validity, and list the valid windows'
+// start positions in ascending order (stable compaction).  *count = valid windows.
+int seed_windows(Engine *e, const uint8_t *h_ascii, uint64_t len, int strand, int shift,
+                 uint8_t *&bytes, uint32_t *&nibbles, DevBuf<uint32_t> &key,
+                 DevBuf<uint32_t> &pos, uint32_t *count, hipStream_t s) {
+    *count = 0;
+    int rc;
+    DevBuf<uint8_t> ascii, valid;
+    if ((rc = dalloc(e, ascii.p, len))) return rc;
+    if (len)
+        HIP_TRY(e, hipMemcpyAsync(ascii.p, h_ascii, len, hipMemcpyHostToDevice, s));
+    const uint64_t nib = len + 2 * (uint64_t)kPad4;
     const uint64_t words = (nib + 31) / 32 * 4;
-    std::vector<uint32_t> buf(words, 0);
-    for (uint64_t m = 0; m < words * 8; m++) {
-        const uint32_t c = (m >= (uint64_t)kPad4 && m < (uint64_t)kPad4 + n) ? codes[m - kPad4]
-                                                                            : kCodeEdge;
-        buf[m >> 3] |= c << (4 * (m & 7));
-    }
-    int rc = dalloc(e, dst, words);
-    if (rc) return rc;
-    HIP_TRY(e, hipMemcpyAsync(dst, buf.data(), words * sizeof(uint32_t), hipMemcpyHostToDevice, s));
+    if ((rc = dalloc(e, bytes, len + 2 * (uint64_t)kPad))) return rc;
+    if ((rc = dalloc(e, nibbles, words))) return rc;
+    HIP_TRY(e, launch_encode(ascii.p, len, strand, bytes, shift, nibbles, words, s));
+    const uint64_t nw = len >= (uint64_t)e->span ? len - e->span + 1 : 0;
+    if ((rc = dalloc(e, key.p, nw)) || (rc = dalloc(e, pos.p, nw)) ||
+        (rc = dalloc(e, valid.p, nw)))
+        return rc;
+    SeedShape sh{};
+    for (int i = 0; i < e->weight; i++) sh.care[i] = e->care[i];
+    sh.weight = e->weight;
+    HIP_TRY(e, launch_window_keys(bytes + kPad, shift, nw, sh, valid.p, key.p, s));
+    if ((rc = ensure_compact(e, nw))) return rc;
+    HIP_TRY(e, launch_compact(valid.p, (uint32_t)nw, e->d_cblk, e->d_ctotal, pos.p, nullptr,
+                              nullptr, (uint32_t)nw, s));
+    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_ctotal, sizeof(uint32_t), hipMemcpyDeviceToHost,
+                              s));
     HIP_TRY(e, hipStreamSynchronize(s));
+    *count = e->h_pinned[0];
     return HSPZ_OK;
 }
 
@@ -405,32 +424,51 @@ HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, 
     e->free_plan();
     e->has_ref = false;
 
-    std::vector<uint8_t> codes(len);
-    for (uint64_t i = 0; i < len; i++) codes[i] = code_of(h_ascii[i]);
-    std::vector<uint32_t> keys;
-    window_keys(codes, e->care, e->span, keys);
-    // Counting sort by key; positions ascend within a bucket because windows are visited
-    // in ascending position.
+    // Device indexer ("C. Hit discovery", C.1 index table): the valid windows' keys and
+    // reference ends in position order; bucket sizes by an atomic histogram, cumulative
+    // ends by a scan (leading 0), and the ends grouped by key with a stable radix sort, so
+    // they ascend within each bucket.
+    DevBuf<uint32_t> key, pos;
+    uint32_t nwin = 0;
+    if ((rc = seed_windows(e, h_ascii, len, 0, kRefShift, e->d_ref, e->d_ref4, key, pos, &nwin,
+                           s)))
+        return rc;
     const uint64_t nb = 1ull << (2 * e->weight);
-    std::vector<uint32_t> end(nb + 1, 0);
-    for (uint32_t k : keys)
-        if (k != 0xFFFFFFFFu) end[k + 1]++;
-    for (uint64_t k = 0; k < nb; k++) end[k + 1] += end[k];
-    const uint64_t nwin = end[nb];
-    std::vector<uint32_t> pos(std::max<uint64_t>(nwin, 1));
+    DevBuf<uint32_t> ka, va, kb, vb, cnt;
+    if ((rc = dalloc(e, ka.p, nwin)) || (rc = dalloc(e, va.p, nwin)) ||
+        (rc = dalloc(e, kb.p, nwin)) || (rc = dalloc(e, vb.p, nwin)) ||
+        (rc = dalloc(e, cnt.p, nb)) || (rc = dalloc(e, e->d_end, nb + 1)))
+        return rc;
+    HIP_TRY(e, launch_gather_pairs(pos.p, nwin, key.p, (uint32_t)e->span, ka.p, va.p, s));
+    HIP_TRY(e, hipMemsetAsync(cnt.p, 0, nb * sizeof(uint32_t), s));
+    HIP_TRY(e, launch_key_hist(ka.p, nwin, cnt.p, s));
     {
-        std::vector<uint32_t> cur(end.begin(), end.end() - 1);
-        for (uint64_t p = 0; p < keys.size(); p++)
-            if (keys[p] != 0xFFFFFFFFu) pos[cur[keys[p]]++] = (uint32_t)(p + e->span);
+        // the scan's vector stores want a 16-byte aligned output, so scan into a
+        // temporary and copy it behind the leading 0
+        DevBuf<uint32_t> ends;
+        if ((rc = dalloc(e, ends.p, nb))) return rc;
+        if ((rc = device_scan(e, cnt.p, nb, ends.p, s))) return rc;
+        HIP_TRY(e, launch_set_u32(e->d_end, 0u, s));
+        HIP_TRY(e, hipMemcpyAsync(e->d_end + 1, ends.p, nb * sizeof(uint32_t),
+                                  hipMemcpyDeviceToDevice, s));
+        HIP_TRY(e, hipStreamSynchronize(s));
     }
-    if ((rc = dalloc(e, e->d_end, nb + 1))) return rc;
-    if ((rc = dalloc(e, e->d_pos, std::max<uint64_t>(nwin, 1)))) return rc;
-    HIP_TRY(e, hipMemcpyAsync(e->d_end, end.data(), (nb + 1) * sizeof(uint32_t),
-                              hipMemcpyHostToDevice, s));
-    HIP_TRY(e, hipMemcpyAsync(e->d_pos, pos.data(), std::max<uint64_t>(nwin, 1) * sizeof(uint32_t),
-                              hipMemcpyHostToDevice, s));
-    if ((rc = upload_padded(e, e->d_ref, codes, kRefShift, s))) return rc;
-    if ((rc = upload_nibbles(e, e->d_ref4, codes, s))) return rc;
+    const uint32_t nblk = radix_blocks(nwin);
+    const uint64_t nh = 256ull * nblk;
+    DevBuf<uint32_t> hist, incl;
+    if ((rc = dalloc(e, hist.p, nh)) || (rc = dalloc(e, incl.p, nh))) return rc;
+    for (int shift = 0; shift < 2 * e->weight; shift += 8) {
+        HIP_TRY(e, launch_radix_hist(ka.p, nwin, shift, hist.p, s));
+        if ((rc = device_scan(e, hist.p, nh, incl.p, s))) return rc;
+        HIP_TRY(e, launch_radix_scatter(ka.p, va.p, nwin, shift, incl.p, hist.p, kb.p, vb.p, s));
+        std::swap(ka.p, kb.p);
+        std::swap(va.p, vb.p);
+    }
+    HIP_TRY(e, hipStreamSynchronize(s));
+    dfree(e->d_pos);
+    e->d_pos = va.release();
+    if (!e->d_pos && (rc = dalloc(e, e->d_pos, 1))) return rc;
+    e->n_index = nwin;
     e->n_ref = len;
     e->sp.n_ref = (uint32_t)len;
     e->wp.n_ref = (uint32_t)len;
@@ -451,36 +489,19 @@ HSPZ_API int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint
     e->free_plan();
     e->has_qry = false;
 
-    std::vector<uint8_t> codes(len);
-    for (uint64_t i = 0; i < len; i++) {
-        if (strand == 0) {
-            codes[i] = code_of(h_ascii[i]);
-        } else {
-            const uint8_t c = code_of(h_ascii[len - 1 - i]);
-            codes[i] = c < 4 ? (uint8_t)(3 - c) : kCodeN;
-        }
-    }
-    std::vector<uint32_t> keys;
-    window_keys(codes, e->care, e->span, keys);
-    std::vector<uint32_t> kmer, qend;
-    e->h_seed_start.clear();
-    for (uint64_t p = 0; p < keys.size(); p++) {
-        if (keys[p] == 0xFFFFFFFFu) continue;
-        kmer.push_back(keys[p]);
-        qend.push_back((uint32_t)(p + e->span));
-        e->h_seed_start.push_back((uint32_t)p);
-    }
-    const uint64_t ns = kmer.size();
-    if ((rc = dalloc(e, e->d_kmer, ns))) return rc;
-    if ((rc = dalloc(e, e->d_qend, ns))) return rc;
-    if (ns) {
-        HIP_TRY(e, hipMemcpyAsync(e->d_kmer, kmer.data(), ns * sizeof(uint32_t),
-                                  hipMemcpyHostToDevice, s));
-        HIP_TRY(e, hipMemcpyAsync(e->d_qend, qend.data(), ns * sizeof(uint32_t),
-                                  hipMemcpyHostToDevice, s));
-    }
-    if ((rc = upload_padded(e, e->d_qry, codes, 0, s))) return rc;
-    if ((rc = upload_nibbles(e, e->d_qry4, codes, s))) return rc;
+    // Device seeder: every valid window of the strand, in ascending position, with its
+    // packed k-mer and query end.
+    DevBuf<uint32_t> key, pos;
+    uint32_t ns = 0;
+    if ((rc = seed_windows(e, h_ascii, len, strand, 0, e->d_qry, e->d_qry4, key, pos, &ns, s)))
+        return rc;
+    if ((rc = dalloc(e, e->d_kmer, ns)) || (rc = dalloc(e, e->d_qend, ns))) return rc;
+    HIP_TRY(e, launch_gather_pairs(pos.p, ns, key.p, (uint32_t)e->span, e->d_kmer, e->d_qend, s));
+    e->h_seed_start.resize(ns);
+    if (ns)
+        HIP_TRY(e, hipMemcpyAsync(e->h_seed_start.data(), pos.p, (uint64_t)ns * sizeof(uint32_t),
+                                  hipMemcpyDeviceToHost, s));
+    HIP_TRY(e, hipStreamSynchronize(s));
     e->n_qry = len;
     e->sp.n_qry = (uint32_t)len;
     e->wp.n_qry = (uint32_t)len;
@@ -619,6 +640,25 @@ HSPZ_API int hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi,
             HIP_TRY(e, hipMemcpy(h_q_end, e->d_qend + lo, (hi - lo) * sizeof(uint32_t),
                                  hipMemcpyDeviceToHost));
     }
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_get_index(const hspz_engine *engine, uint32_t *h_end, uint32_t *h_pos,
+                            uint64_t *n_buckets, uint64_t *n_pos) {
+    Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
+    if (!e) return HSPZ_E_INVALID;
+    if (!n_buckets || !n_pos) return fail(e, HSPZ_E_INVALID, "NULL size output");
+    if (!e->has_ref) return fail(e, HSPZ_E_STATE, "no reference uploaded");
+    const uint64_t nb = 1ull << (2 * e->weight);
+    *n_buckets = nb;
+    *n_pos = e->n_index;
+    int rc = set_device(e);
+    if (rc) return rc;
+    if (h_end)
+        HIP_TRY(e, hipMemcpy(h_end, e->d_end, (nb + 1) * sizeof(uint32_t), hipMemcpyDeviceToHost));
+    if (h_pos && e->n_index)
+        HIP_TRY(e, hipMemcpy(h_pos, e->d_pos, e->n_index * sizeof(uint32_t),
+                             hipMemcpyDeviceToHost));
     return HSPZ_OK;
 }
 

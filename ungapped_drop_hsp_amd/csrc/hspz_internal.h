@@ -59,7 +59,30 @@ struct WindowParams {
     uint32_t n_qry;
 };
 
+// Spaced seed: care offsets within the window (first care position most significant).
+struct SeedShape {
+    int32_t care[16];
+    int32_t weight;
+};
+
 // ---- launchers (kernels in k_*.hip) --------------------------------------------------
+// Device seeder and indexer (k_seed.hip).
+hipError_t launch_encode(const uint8_t *ascii, uint64_t n, int strand, uint8_t *bytes, int shift,
+                         uint32_t *nibbles, uint64_t nibble_words, hipStream_t s);
+hipError_t launch_window_keys(const uint8_t *codes, int shift, uint64_t nw, const SeedShape &sh,
+                              uint8_t *valid, uint32_t *key, hipStream_t s);
+hipError_t launch_gather_pairs(const uint32_t *pos, uint32_t count, const uint32_t *key,
+                               uint32_t span, uint32_t *key_out, uint32_t *end_out,
+                               hipStream_t s);
+hipError_t launch_key_hist(const uint32_t *key, uint32_t n, uint32_t *cnt, hipStream_t s);
+hipError_t launch_set_u32(uint32_t *p, uint32_t v, hipStream_t s);
+uint32_t radix_blocks(uint32_t n);
+hipError_t launch_radix_hist(const uint32_t *key, uint32_t n, int shift, uint32_t *hist,
+                             hipStream_t s);
+hipError_t launch_radix_scatter(const uint32_t *key_in, const uint32_t *val_in, uint32_t n,
+                                int shift, const uint32_t *incl, const uint32_t *hist,
+                                uint32_t *key_out, uint32_t *val_out, hipStream_t s);
+
 // Per seed: hit count, bucket start (first, when kmer is given) and block-local
 // inclusive prefix; one 64-bit sum per kScanBlock seeds into blksum.
 hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, uint64_t n,
@@ -121,6 +144,7 @@ struct Engine {
     uint64_t n_ref = 0;
     uint32_t *d_end = nullptr;   // 4^w + 1 cumulative bucket ends, leading 0
     uint32_t *d_pos = nullptr;   // reference end coordinate of every valid window
+    uint64_t n_index = 0;        // entries of d_pos
     uint8_t *d_ref = nullptr;    // padded encoded reference (kPad edge bytes each side)
     uint32_t *d_ref4 = nullptr;  // 4-bit packed reference (kPad4 edge nibbles each side)
 
