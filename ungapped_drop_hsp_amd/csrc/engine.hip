@@ -116,7 +116,7 @@ int device_scan(Engine *e, uint32_t *counts, uint64_t n, uint32_t *prefix, hipSt
 // 4-bit array, compute every window's key and validity, and list the valid windows'
 // start positions in ascending order (stable compaction).  *count = valid windows.
 int seed_windows(Engine *e, const uint8_t *h_ascii, uint64_t len, int strand, int shift,
-                 uint8_t *&bytes, uint32_t *&nibbles, DevBuf<uint32_t> &key,
+                 uint8_t *&bytes, uint32_t *&nibbles, uint32_t *alt, DevBuf<uint32_t> &key,
                  DevBuf<uint32_t> &pos, uint32_t *count, hipStream_t s) {
     *count = 0;
     int rc;
@@ -124,11 +124,22 @@ int seed_windows(Engine *e, const uint8_t *h_ascii, uint64_t len, int strand, in
     if ((rc = dalloc(e, ascii.p, len))) return rc;
     if (len)
         HIP_TRY(e, hipMemcpyAsync(ascii.p, h_ascii, len, hipMemcpyHostToDevice, s));
+    // 4-bit copy, then at the next 128-byte boundary its twin: the same dwords shifted
+    // down by 64 bytes, so any window of at most 64 bytes lies inside one 128-byte line
+    // of one of the two
     const uint64_t nib = len + 2 * (uint64_t)kPad4;
     const uint64_t words = (nib + 31) / 32 * 4;
+    const uint64_t twin = (words + 31) / 32 * 32;
+    if (twin + words > 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "sequence too long");
     if ((rc = dalloc(e, bytes, len + 2 * (uint64_t)kPad))) return rc;
-    if ((rc = dalloc(e, nibbles, words))) return rc;
+    if ((rc = dalloc(e, nibbles, twin + words))) return rc;
     HIP_TRY(e, launch_encode(ascii.p, len, strand, bytes, shift, nibbles, words, s));
+    HIP_TRY(e, hipMemcpyAsync(nibbles + twin, nibbles + kTwinShift,
+                              (words - kTwinShift) * sizeof(uint32_t), hipMemcpyDeviceToDevice,
+                              s));
+    HIP_TRY(e, hipMemsetAsync(nibbles + twin + words - kTwinShift, 0x55,
+                              kTwinShift * sizeof(uint32_t), s));
+    *alt = (uint32_t)twin;
     const uint64_t nw = len >= (uint64_t)e->span ? len - e->span + 1 : 0;
     if ((rc = dalloc(e, key.p, nw)) || (rc = dalloc(e, pos.p, nw)) ||
         (rc = dalloc(e, valid.p, nw)))
@@ -430,8 +441,8 @@ HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, 
     // they ascend within each bucket.
     DevBuf<uint32_t> key, pos;
     uint32_t nwin = 0;
-    if ((rc = seed_windows(e, h_ascii, len, 0, kRefShift, e->d_ref, e->d_ref4, key, pos, &nwin,
-                           s)))
+    if ((rc = seed_windows(e, h_ascii, len, 0, kRefShift, e->d_ref, e->d_ref4, &e->wp.ref4_alt,
+                           key, pos, &nwin, s)))
         return rc;
     const uint64_t nb = 1ull << (2 * e->weight);
     DevBuf<uint32_t> ka, va, kb, vb, cnt;
@@ -493,7 +504,8 @@ HSPZ_API int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint
     // packed k-mer and query end.
     DevBuf<uint32_t> key, pos;
     uint32_t ns = 0;
-    if ((rc = seed_windows(e, h_ascii, len, strand, 0, e->d_qry, e->d_qry4, key, pos, &ns, s)))
+    if ((rc = seed_windows(e, h_ascii, len, strand, 0, e->d_qry, e->d_qry4, &e->wp.qry4_alt, key,
+                           pos, &ns, s)))
         return rc;
     if ((rc = dalloc(e, e->d_kmer, ns)) || (rc = dalloc(e, e->d_qend, ns))) return rc;
     HIP_TRY(e, launch_gather_pairs(pos.p, ns, key.p, (uint32_t)e->span, e->d_kmer, e->d_qend, s));

@@ -26,8 +26,12 @@ constexpr int kTabSize = 64;
 // 4-bit copy of each sequence for the windowed score gate: eight bases per dword, the
 // base at padded nibble index m in dword m / 8, bits 4 * (m % 8).  Base b sits at padded
 // nibble b + kPad4; kPad4 edge nibbles precede and follow the sequence.  Codes are the
-// unshifted ones above on both sequences (A,C,G,T = 0..3, N = 4, edge = 5).
+// unshifted ones above on both sequences (A,C,G,T = 0..3, N = 4, edge = 5).  Each copy
+// is followed, at the next 128-byte boundary, by its twin: twin dword j holds copy dword
+// j + kTwinShift.  A window of at most 16 dwords starting at copy dword m lies inside one
+// 128-byte line of the copy when m % 32 <= 16, and of the twin otherwise.
 constexpr int kPad4 = 256;
+constexpr int kTwinShift = 16;
 
 // Seeds per block of the device prefix scan.
 constexpr int kScanBlock = 1024;
@@ -57,6 +61,9 @@ struct WindowParams {
     int32_t T;
     uint32_t n_ref;
     uint32_t n_qry;
+    // dword offset of each 4-bit copy's line-split twin (the same codes 64 bytes earlier)
+    uint32_t ref4_alt;
+    uint32_t qry4_alt;
 };
 
 // Spaced seed: care offsets within the window (first care position most significant).
@@ -146,14 +153,15 @@ struct Engine {
     uint32_t *d_pos = nullptr;   // reference end coordinate of every valid window
     uint64_t n_index = 0;        // entries of d_pos
     uint8_t *d_ref = nullptr;    // padded encoded reference (kPad edge bytes each side)
-    uint32_t *d_ref4 = nullptr;  // 4-bit packed reference (kPad4 edge nibbles each side)
+    uint32_t *d_ref4 = nullptr;  // 4-bit packed reference (kPad4 edge nibbles each side),
+                                 // then its line-split twin at wp.ref4_alt
 
     // query strand
     bool has_qry = false;
     uint64_t n_qry = 0;
     int strand = 0;
     uint8_t *d_qry = nullptr;
-    uint32_t *d_qry4 = nullptr;
+    uint32_t *d_qry4 = nullptr;  // the same layout as d_ref4 (twin at wp.qry4_alt)
     uint32_t *d_kmer = nullptr;
     uint32_t *d_qend = nullptr;
     uint64_t n_seeds = 0;

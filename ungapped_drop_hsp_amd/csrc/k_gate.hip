@@ -217,12 +217,15 @@ constexpr int kSeg = 512;   // LDS slots per wave for deferred anchor indices
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// W dwords from base + nib / 8 (nib a multiple of 8): 8 * W consecutive 4-bit codes.
+// W dwords of a 4-bit copy from dword m on (8 * W consecutive codes), read from the copy
+// or from its twin (alt dwords further on), whichever keeps a window of up to 16 dwords
+// inside one 128-byte line.  Longer windows cross a line in either.
 template <int W>
-__device__ __forceinline__ void load_window(const uint32_t *__restrict__ base, uint32_t nib,
-                                            uint32_t (&Wd)[W]) {
+__device__ __forceinline__ void load_window(const uint32_t *__restrict__ base, uint32_t alt,
+                                            uint32_t m, uint32_t (&Wd)[W]) {
     static_assert(W % 4 == 0, "whole 16-byte loads");
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(base + (nib >> 3));
+    const uint32_t off = (m & 31u) > (uint32_t)kTwinShift ? alt + m - kTwinShift : m;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(base + off);
 #pragma unroll
     for (int j = 0; j < W / 4; j++) {
         const u32x4 v = p[j];
@@ -270,12 +273,13 @@ struct Win {
 
     __device__ __forceinline__ void load(bool in, uint32_t r, uint32_t q,
                                          const uint32_t *__restrict__ ref4,
-                                         const uint32_t *__restrict__ qry4) {
+                                         const uint32_t *__restrict__ qry4,
+                                         const WindowParams &wp) {
         inrange = in;
         const uint32_t wr = (in ? r : 0u) + (uint32_t)(kPad4 - 8 * LB);
         const uint32_t wq = (in ? q : 0u) + (uint32_t)(kPad4 - 8 * LB);
-        load_window<W>(ref4, wr & ~7u, R);
-        load_window<W>(qry4, wq & ~7u, Q);
+        load_window<W>(ref4, wp.ref4_alt, wr >> 3, R);
+        load_window<W>(qry4, wp.qry4_alt, wq >> 3, Q);
         shr = (wr & 7u) * 4u;
         shq = (wq & 7u) * 4u;
     }
@@ -410,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
         const bool valid = i < n;
         const uint64_t a = valid ? anchors[i] : 0ull;
         Win<RB, LB> win;
-        win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4);
+        win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[i] = (uint8_t)res;
         defer_push(seg[w], nseg, valid && res == 2, (uint32_t)i, defer, defer_cnt);
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
             q = (uint32_t)(a >> 32);
         }
         Win<RB, LB> win;
-        win.load(valid && r <= wp.n_ref && q <= wp.n_qry, r, q, ref4, qry4);
+        win.load(valid && r <= wp.n_ref && q <= wp.n_qry, r, q, ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[i] = (uint8_t)res;
         defer_push(seg[w], nseg, valid && res == 2, i, defer, defer_cnt);
