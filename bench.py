@@ -50,10 +50,12 @@ def parse():
                     help="CPU oracle sample budget in seconds (0 skips the CPU leg)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--gate-mode", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="score gate variant (0 auto, 1 exact walk, 2 window, 3 narrow window)")
     return ap.parse_args()
 
 
-def gate_traffic(workload: str):
+def gate_traffic(workload: str, gate_mode: int):
     """Measured fabric bytes per score-gate call from the committed counter summary.
 
     The summary was taken with rocprofv3 FETCH_SIZE / WRITE_SIZE runs and calibrated
@@ -68,7 +70,8 @@ def gate_traffic(workload: str):
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if rec.get("k_gate_hip_sha256") != sha or not rec["workload"].startswith(workload):
+    if (rec.get("k_gate_hip_sha256") != sha or not rec["workload"].startswith(workload)
+            or rec.get("gate_mode", 0) != gate_mode):
         return None
     return rec["hbm_bytes_per_call"]
 
@@ -133,7 +136,8 @@ def main():
     print(f"[bench] workload {w.name} generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     eng = h.Engine(seed_pattern=p["seed_pattern"], sub=p["sub"], n_score=p["n_score"],
-                   xdrop=p["xdrop"], hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"])
+                   xdrop=p["xdrop"], hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"],
+                   gate_mode=args.gate_mode)
     t = time.perf_counter()
     eng.upload_reference(w.ref)
     torch.cuda.synchronize()
@@ -221,12 +225,13 @@ def main():
                     strands=w.strands, batch_bp=w.batch_len or int(w.query.size),
                     seed_pattern=p["seed_pattern"], xdrop=p["xdrop"],
                     hsp_threshold=p["hsp_threshold"], max_hits=p["max_hits"], seeds=seeds,
-                    raw_anchors=anchors, chunks=chunks, survivors=surv, accepted=acc),
+                    raw_anchors=anchors, chunks=chunks, survivors=surv, accepted=acc,
+                    gate_mode=args.gate_mode),
         hsps_per_s=acc / (ms_per_step / 1000.0),
         stage_ms=stage_ms,
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
-                      traffic=gate_traffic(w.name),
+                      traffic=gate_traffic(w.name, args.gate_mode),
                       kernel="score_gate (two k_gate_window stages + k_gate_list)",
                       launches_per_step=gate_launches // args.steps,
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,

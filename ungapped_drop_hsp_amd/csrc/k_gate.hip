@@ -1,7 +1,11 @@
 // Score-only X-drop gate ("D. Score gate", D.1-D.3).
 //
 // Every kernel here keeps, per walk and per block of B bases, only the drawdown
-// d = best - score (d' = max(d - sigma, 0)), its running maximum and the score.  A drop
+// d = best - score (d' = max(d - sigma, 0)), its running maximum and the score.  The
+// drawdown is held as its complement g = INT32_MAX - d: then d' = max(d - sigma, 0) is
+// the signed saturating add g' = sat(g + sigma) (the clamp at INT32_MAX is the clamp of
+// d at 0), one instruction per base, and the running maximum of d is the running
+// minimum of g.  d never exceeds xdrop + B * (xdrop + 1), far from the lower limit.  A drop
 // inside a block shows as max(d) > xdrop at the block's end.  B satisfies
 // (B - 1) * max(sigma) <= xdrop, so after a drop the score cannot climb back above the
 // best inside the same block: best = score + d at the block's end is exactly the
@@ -53,11 +57,18 @@ __device__ __forceinline__ void load8(const uint8_t *p, uint32_t &lo, uint32_t &
     hi = __builtin_amdgcn_alignbyte(w2, w1, sh);
 }
 
+constexpr int32_t kG0 = INT32_MAX;  // g of a zero drawdown
+
+// One base: g = INT32_MAX - d becomes INT32_MAX - max(d - sg, 0).
+__device__ __forceinline__ int32_t dd_step(int32_t g, int32_t sg) {
+    return __builtin_elementwise_add_sat(g, sg);
+}
+
 // Score B bases in walk direction D starting at (rp, qp) (right: rp[0..B), left:
-// rp[-1] down to rp[-B]).
+// rp[-1] down to rp[-B]).  g and gmin are the complemented drawdown and its minimum.
 template <int D, int B>
 __device__ __forceinline__ void block_step(const int32_t *tab, const uint8_t *rp,
-                                           const uint8_t *qp, int32_t &d, int32_t &dmax,
+                                           const uint8_t *qp, int32_t &g, int32_t &gmin,
                                            int32_t &s) {
     uint32_t rl, rh, ql, qh;
     load8(D > 0 ? rp : rp - B, rl, rh);
@@ -68,9 +79,8 @@ __device__ __forceinline__ void block_step(const int32_t *tab, const uint8_t *rp
         const int bi = D > 0 ? i : B - 1 - i;
         const uint32_t idx = (bi < 4 ? (pl >> (8 * bi)) : (ph >> (8 * (bi - 4)))) & 0xFFu;
         const int32_t sg = tab[idx];
-        const int32_t t = d - sg;
-        dmax = max(dmax, t);
-        d = max(t, 0);
+        g = dd_step(g, sg);
+        gmin = min(gmin, g);
         s += sg;
     }
 }
@@ -87,7 +97,8 @@ __device__ __forceinline__ void walk_phase(const uint64_t *an, int cnt, const in
     int next = 64;
     int cur = lane < cnt ? lane : -1;
     const uint8_t *rp = ref, *qp = qry;  // next base to score (right) or one past it (left)
-    int32_t d = 0, dmax = 0, s = 0, other = 0;
+    int32_t g = kG0, gmin = kG0, s = 0, other = 0;
+    const int32_t glim = kG0 - sp.xdrop;  // a drop once gmin < glim
 
     auto start = [&](int i) {
         const uint64_t a = an[i];
@@ -98,8 +109,8 @@ __device__ __forceinline__ void walk_phase(const uint64_t *an, int cnt, const in
         }
         rp = ref + r;
         qp = qry + q;
-        d = 0;
-        dmax = 0;
+        g = kG0;
+        gmin = kG0;
         s = 0;
         other = D > 0 ? 0 : rstar[i];
     };
@@ -109,12 +120,12 @@ __device__ __forceinline__ void walk_phase(const uint64_t *an, int cnt, const in
         if (__ballot(cur >= 0) == 0) break;
         bool done = false;
         if (cur >= 0) {
-            block_step<D, B>(tab, rp, qp, d, dmax, s);
+            block_step<D, B>(tab, rp, qp, g, gmin, s);
             rp += D * B;
             qp += D * B;
-            const int32_t best = s + d;
+            const int32_t best = s + (kG0 - g);
             const bool keep = (int64_t)other + best >= (int64_t)sp.T;
-            done = dmax > sp.xdrop || keep;
+            done = gmin < glim || keep;
             if (done) {
                 if (D > 0) rstar[cur] = keep ? sp.T : best;  // R* >= T already decides
                 else fl8[cur] = keep ? 1 : 0;
@@ -239,8 +250,8 @@ __device__ __forceinline__ void load_window(const uint32_t *__restrict__ base, u
 // Eight bases: R and Q hold codes of bases 0..7 in nibbles 0..7.  Even bases' table
 // indices (r << 4 | q) land in the bytes of ie, odd bases' in the bytes of io.
 template <bool Right>
-__device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t Q, int32_t &d,
-                                       int32_t &dmax, int32_t &s) {
+__device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t Q, int32_t &g,
+                                       int32_t &gmin, int32_t &s) {
     const uint32_t hi = 0xF0F0F0F0u;
     uint32_t ie = ((R << 4) & hi) | (Q & ~hi);
     uint32_t io = (R & hi) | ((Q >> 4) & ~hi);
@@ -251,9 +262,8 @@ __device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t 
         const int i = Right ? t : 7 - t;
         const uint32_t w = (i & 1) ? io : ie;
         const int32_t sg = tab[(w >> (8 * (i >> 1))) & 0xFFu];
-        const int32_t x = d - sg;
-        dmax = max(dmax, x);
-        d = max(x, 0);
+        g = dd_step(g, sg);
+        gmin = min(gmin, g);
         s += sg;
     }
 }
@@ -287,18 +297,19 @@ struct Win {
     __device__ __forceinline__ int decide(const int16_t *tab, const WindowParams &wp) const {
         bool keep = false;
         int32_t rstar = 0;
+        const int32_t glim = kG0 - wp.xdrop;  // a drop once gmin < glim
         // right: bases r + 8k .. r + 8k + 7 are window dword LB + k onward
         bool act = inrange;
-        int32_t d = 0, dmax = 0, s = 0;
+        int32_t g = kG0, gmin = kG0, s = 0;
 #pragma unroll
         for (int k = 0; k < RB; k++) {
             if (__ballot(act) == 0) break;
             if (act) {
                 const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB + k + 1], R[LB + k], shr);
                 const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB + k + 1], Q[LB + k], shq);
-                block8<true>(tab, Rb, Qb, d, dmax, s);
-                const int32_t best = s + d;
-                if (dmax > wp.xdrop) {
+                block8<true>(tab, Rb, Qb, g, gmin, s);
+                const int32_t best = s + (kG0 - g);
+                if (gmin < glim) {
                     act = false;
                     rstar = best;
                 } else if (best >= wp.T) {
@@ -310,8 +321,8 @@ struct Win {
         bool undecided = act;
         // left: bases r - 8k - 8 .. r - 8k - 1 are window dword LB - 1 - k onward
         act = inrange && !keep && !undecided;
-        d = 0;
-        dmax = 0;
+        g = kG0;
+        gmin = kG0;
         s = 0;
 #pragma unroll
         for (int k = 0; k < LB; k++) {
@@ -319,9 +330,9 @@ struct Win {
             if (act) {
                 const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB - k], R[LB - 1 - k], shr);
                 const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB - k], Q[LB - 1 - k], shq);
-                block8<false>(tab, Rb, Qb, d, dmax, s);
-                const int32_t tot = rstar + s + d;
-                if (dmax > wp.xdrop) {
+                block8<false>(tab, Rb, Qb, g, gmin, s);
+                const int32_t tot = rstar + s + (kG0 - g);
+                if (gmin < glim) {
                     act = false;
                     keep = tot >= wp.T;
                 } else if (tot >= wp.T) {
