@@ -31,10 +31,12 @@ if ROOT not in sys.path:
 METRIC = "raw anchors/s through gate+materialize at 1 GPU; gate HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 CUS, LANES, CLOCK_GHZ = 256, 64, 2.4
-# One base step of an X-drop walk needs at least four 32-bit vector operations: the
-# substitution score lookup, the running-score add, the best/drawdown update and the
-# drop compare.  The ALU peak in base steps per second follows from the lane count.
-OPS_PER_BASE_STEP = 4
+# One base step of an X-drop walk needs at least three 32-bit vector operations on
+# CDNA4: forming the substitution-table address, the drawdown update (one saturating add
+# on the drawdown's complement) and, shared between two bases through three-input
+# min/add, the running extreme and the running score.  The ALU peak in base steps per
+# second follows from the lane count.
+OPS_PER_BASE_STEP = 3
 ALU_PEAK_GSTEPS = CUS * LANES * CLOCK_GHZ / OPS_PER_BASE_STEP   # G base steps/s
 GATE_BYTES_PER_ANCHOR = 9       # 8-byte packed anchor read + 1-byte flag write
 
@@ -53,6 +55,28 @@ def parse():
     ap.add_argument("--gate-mode", type=int, default=0, choices=[0, 1, 2, 3],
                     help="score gate variant (0 auto, 1 exact walk, 2 window, 3 narrow window)")
     return ap.parse_args()
+
+
+def gather_ceiling(torch) -> float:
+    """Random-line rate of the fabric: single 4-byte gathers from a 64 MiB table.
+
+    Every gather touches its own 128-byte line, which misses L2 (4 MB per XCD); the rate
+    is the ceiling for kernels whose traffic is one random line per work unit.
+    """
+    n = 48 << 20
+    tab = torch.zeros((1 << 24) + 1, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    idx = torch.randint(0, 1 << 24, (n,), device="cuda", generator=gen)
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    torch.index_select(tab, 0, idx, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.index_select(tab, 0, idx, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return n / (e0.elapsed_time(e1) / 10 / 1000.0)
 
 
 def gate_traffic(workload: str, gate_mode: int):
@@ -210,6 +234,10 @@ def main():
     steps_per_anchor = steps_total / max(walked, 1)
     gate_gsteps = steps_per_anchor * units_avg / (gate_ms_avg * 1e6)
 
+    traffic = gate_traffic(w.name, args.gate_mode)
+    ceiling = gather_ceiling(torch)
+    gate_lines = None if traffic is None else traffic / 128.0 / (gate_ms_avg / 1000.0)
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -231,7 +259,7 @@ def main():
         stage_ms=stage_ms,
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
-                      traffic=gate_traffic(w.name, args.gate_mode),
+                      traffic=traffic,
                       kernel="score_gate (two k_gate_window stages + k_gate_list)",
                       launches_per_step=gate_launches // args.steps,
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
@@ -239,6 +267,10 @@ def main():
         gate_hbm=dict(achieved=gate_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=gate_gbs / HBM_PEAK_GBS, bytes_per_anchor=GATE_BYTES_PER_ANCHOR),
         gate_anchors_per_s=units_avg / (gate_ms_avg / 1000.0),
+        # the gate's measured fabric traffic in 128-byte lines/s against the random-line
+        # rate of a plain gather kernel, measured in this run
+        gate_lines=dict(achieved=gate_lines, ceiling=ceiling, unit="lines/s",
+                        frac=None if gate_lines is None else gate_lines / ceiling),
         gate_stage2_fraction=None if deferred is None else deferred[0] / max(walked, 1),
         gate_exact_fraction=None if deferred is None else deferred[1] / max(walked, 1),
         setup_s=dict(generate=gen_s, upload=upload_s),
