@@ -21,16 +21,20 @@
 //    and the left walk up to nine, all lanes in step, so every block's window word has a
 //    compile-time register index.  Pair scores come from a 16-bit LDS
 //    table indexed by (ref code << 4) | query code, formed for four bases at once with
-//    byte-wise bit selects.  A lane stops as soon as its flag is known: at the first
-//    drop, or once R* (right) or R* + best so far (left) reaches T.  Walks still running
-//    at the window's end are appended to a deferred list: each wave collects them in
-//    LDS and the workgroup reserves its share of the global list with one atomic.
+//    byte-wise bit selects.  A lane stops at its walk's first drop.  Later stages also
+//    stop it once R* (right) or R* + best so far (left) reaches T; the first stage, which
+//    sees every anchor, leaves that test out of its blocks, since only survivors (a few
+//    in 10^4 random anchors) would pass it, and their long walks go on to the later
+//    stages.  Walks still running at the window's end are appended to a deferred list:
+//    each wave collects them in LDS and the workgroup reserves its share of the global
+//    list with one atomic.
 //
 //  exact (k_gate, k_gate_list): one lane per anchor walking base blocks straight from
 //    the byte-per-base sequences, refilling finished lanes from the wave's tile of
 //    anchors (ranks from a ballot).  Used for the deferred anchors, and for every anchor
 //    when the window path's preconditions do not hold.
 #include <algorithm>
+#include <type_traits>
 
 #include "hspz_internal.h"
 #include "wave.h"
@@ -268,12 +272,28 @@ __device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t 
     }
 }
 
+// Calls f(integral_constant<int, K>) for K = 0, 1, ... while f returns true, unrolled at
+// compile time, so register arrays indexed by K stay in registers.
+template <int K, int N>
+struct Unrolled {
+    template <class F>
+    __device__ __forceinline__ static void run(F &&f) {
+        if (f(std::integral_constant<int, K>())) Unrolled<K + 1, N>::run(f);
+    }
+};
+template <int N>
+struct Unrolled<N, N> {
+    template <class F>
+    __device__ __forceinline__ static void run(F &&) {}
+};
+
 // The windows of one anchor per lane: 8 * LB bases before the anchor and 8 * RB from it
 // (plus one dword for the funnel shift), 4-bit codes of both sequences.  load() only
 // issues the reads, so a wave can fetch the next step's windows while it scores this
 // step's.  decide() is called by all lanes of the wave together and returns the flag
-// (0 or 1), or 2 when a walk is still running at the window's end.
-template <int RB, int LB>
+// (0 or 1), or 2 when a walk is still running at the window's end.  With EarlyKeep a walk
+// also stops once the flag is 1 whatever follows (R*, or R* + best so far, reaches T).
+template <int RB, int LB, bool EarlyKeep>
 struct Win {
     static constexpr int W = (LB + RB + 1 + 3) / 4 * 4;
     static_assert(8 * LB + 8 <= kPad4, "left window stays inside the edge padding");
@@ -295,54 +315,57 @@ struct Win {
     }
 
     __device__ __forceinline__ int decide(const int16_t *tab, const WindowParams &wp) const {
-        bool keep = false;
-        int32_t rstar = 0;
+        // Every lane scores every block the wave runs (a lane that has finished only
+        // scores its own registers again) and its results are taken at its first drop.
+        // The lane states are wave-uniform 64-bit masks, so the loops need no divergent
+        // regions and their bookkeeping stays in scalar registers.
         const int32_t glim = kG0 - wp.xdrop;  // a drop once gmin < glim
+        const uint64_t live = __builtin_amdgcn_ballot_w64(inrange);
+        uint64_t keep = 0;
+        int32_t rstar = 0;
         // right: bases r + 8k .. r + 8k + 7 are window dword LB + k onward
-        bool act = inrange;
+        uint64_t act = live;
         int32_t g = kG0, gmin = kG0, s = 0;
-#pragma unroll
-        for (int k = 0; k < RB; k++) {
-            if (__ballot(act) == 0) break;
-            if (act) {
-                const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB + k + 1], R[LB + k], shr);
-                const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB + k + 1], Q[LB + k], shq);
-                block8<true>(tab, Rb, Qb, g, gmin, s);
-                const int32_t best = s + (kG0 - g);
-                if (gmin < glim) {
-                    act = false;
-                    rstar = best;
-                } else if (best >= wp.T) {
-                    act = false;
-                    keep = true;
-                }
+        Unrolled<0, RB>::run([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if (act == 0) return false;
+            const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB + k + 1], R[LB + k], shr);
+            const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB + k + 1], Q[LB + k], shq);
+            block8<true>(tab, Rb, Qb, g, gmin, s);
+            const int32_t best = s + (kG0 - g);
+            const uint64_t drop = __builtin_amdgcn_ballot_w64(gmin < glim) & act;
+            rstar = __builtin_amdgcn_inverse_ballot_w64(drop) ? best : rstar;
+            act &= ~drop;
+            if (EarlyKeep) {
+                const uint64_t hit = __builtin_amdgcn_ballot_w64(best >= wp.T) & act;
+                keep |= hit;
+                act &= ~hit;
             }
-        }
-        bool undecided = act;
+            return true;
+        });
+        uint64_t undecided = act;
         // left: bases r - 8k - 8 .. r - 8k - 1 are window dword LB - 1 - k onward
-        act = inrange && !keep && !undecided;
+        act = live & ~keep & ~undecided;
         g = kG0;
         gmin = kG0;
         s = 0;
-#pragma unroll
-        for (int k = 0; k < LB; k++) {
-            if (__ballot(act) == 0) break;
-            if (act) {
-                const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB - k], R[LB - 1 - k], shr);
-                const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB - k], Q[LB - 1 - k], shq);
-                block8<false>(tab, Rb, Qb, g, gmin, s);
-                const int32_t tot = rstar + s + (kG0 - g);
-                if (gmin < glim) {
-                    act = false;
-                    keep = tot >= wp.T;
-                } else if (tot >= wp.T) {
-                    act = false;
-                    keep = true;
-                }
-            }
-        }
-        undecided = undecided || act;
-        return undecided ? 2 : (keep ? 1 : 0);
+        Unrolled<0, LB>::run([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if (act == 0) return false;
+            const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB - k], R[LB - 1 - k], shr);
+            const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB - k], Q[LB - 1 - k], shq);
+            block8<false>(tab, Rb, Qb, g, gmin, s);
+            const uint64_t reach = __builtin_amdgcn_ballot_w64(rstar + s + (kG0 - g) >= wp.T);
+            const uint64_t drop = __builtin_amdgcn_ballot_w64(gmin < glim) & act;
+            const uint64_t done = EarlyKeep ? (drop | (reach & act)) : drop;
+            keep |= done & reach;
+            act &= ~done;
+            return true;
+        });
+        undecided |= act;
+        return __builtin_amdgcn_inverse_ballot_w64(undecided)
+                   ? 2
+                   : (__builtin_amdgcn_inverse_ballot_w64(keep) ? 1 : 0);
     }
 };
 
@@ -424,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
         const uint64_t i = i0 + lane;
         const bool valid = i < n;
         const uint64_t a = valid ? anchors[i] : 0ull;
-        Win<RB, LB> win;
+        Win<RB, LB, false> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[i] = (uint8_t)res;
@@ -462,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
             r = (uint32_t)a;
             q = (uint32_t)(a >> 32);
         }
-        Win<RB, LB> win;
+        Win<RB, LB, true> win;
         win.load(valid && r <= wp.n_ref && q <= wp.n_qry, r, q, ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[i] = (uint8_t)res;
