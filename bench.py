@@ -17,6 +17,7 @@ CPU oracle's throughput on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -176,6 +177,11 @@ def main():
     wall = 0.0
     anchors = surv = acc = chunks = seeds = 0
     chunk_list = []  # (strand, lo, hi) batches of the last step, for the walk statistics
+    # Python's cyclic collector stays off over the passes: a collection inside the timed
+    # loop stalls the launching thread (tens of ms on the 200 Mb workload) and shows up
+    # as idle GPU time in whichever stage it lands.
+    gc.collect()
+    gc.disable()
     for strand in w.strands:
         t = time.perf_counter()
         eng.upload_query(w.query, strand=1 if strand == "-" else 0)
@@ -200,6 +206,7 @@ def main():
         chunks += sum(r["n_chunks"] for r in res)
         # the walk statistics below run on the current strand's last batches
         chunk_list = [(strand, lo, hi) for lo, hi in bs]
+    gc.enable()
     print(f"[bench] {args.steps} timed steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
     ms = timer.elapsed_ms()

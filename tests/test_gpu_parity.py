@@ -75,6 +75,28 @@ def test_chunk_walk_on_many_blocks(walk, seed):
         assert np.array_equal(pre.astype(np.uint64), P)
 
 
+@pytest.mark.parametrize("walk", [0, 1])
+def test_chunk_walk_edges(walk):
+    # the device walk returns at most 1,024 chunks and the host walks longer lists;
+    # a cut landing on the total leaves a trailing chunk of zero hits
+    cases = [
+        (np.ones(1024, np.uint32), 1),              # exactly 1,024 chunks
+        (np.ones(1025, np.uint32), 1),              # one more: the host walks
+        (np.asarray([1, 5, 0, 0], np.uint32), 2),   # [0, 1] 6 hits, then [2, 3] 0 hits
+        (np.asarray([0, 0, 7, 0], np.uint32), 3),   # one non-empty seed among empty ones
+        (np.zeros(3000, np.uint32), 5),             # no hits: no chunks
+    ]
+    for counts, mx in cases:
+        P, _ = oracle.prefix(counts)
+        eng = engine(params_of(SEED_PATTERN), chunk_walk=walk, max_hits=mx)
+        tot, nch = eng.debug_plan_counts(counts)
+        got = [eng.get_chunk(i) for i in range(nch)]
+        want = oracle.chunks(P, mx)
+        assert tot == int(P[-1])
+        assert [(c["seed_lo"], c["seed_hi"], c["hit_lo"], c["n_hits"]) for c in got] == \
+            [(c["seed_lo"], c["seed_hi"], c["hit_lo"], c["n_hits"]) for c in want]
+
+
 CASES = [
     # (seed, n_ref, n_qry, pattern, max_hits, n_frac, plant, identity, gc)
     (0, 30_000, 30_000, "1101011", 0, 0.0, 20, 0.92, 0.5),

@@ -85,8 +85,10 @@ struct DevBuf {
     }
 };
 
-// Inclusive scan of n u32 counts on the device into prefix: block scans, a 64-bit host
-// scan of the block sums, add-back.  The total must fit 32 bits.  Synchronises s.
+// Inclusive scan of n u32 counts on the device into prefix: block scans, the block-sum
+// scan and the add-back, all on the device (the upload's counts total the indexed
+// windows, below 2^32).  Uses the plan buffer's total field; synchronises s before the
+// temporaries are freed.
 int device_scan(Engine *e, uint32_t *counts, uint64_t n, uint32_t *prefix, hipStream_t s) {
     if (n == 0) return HSPZ_OK;
     const uint64_t nblk = (n + kScanBlock - 1) / kScanBlock;
@@ -95,17 +97,7 @@ int device_scan(Engine *e, uint32_t *counts, uint64_t n, uint32_t *prefix, hipSt
     int rc;
     if ((rc = dalloc(e, bs.p, nblk)) || (rc = dalloc(e, bo.p, nblk))) return rc;
     HIP_TRY(e, launch_count_scan(nullptr, counts, n, nullptr, counts, nullptr, prefix, bs.p, s));
-    std::vector<uint64_t> h(nblk);
-    std::vector<uint32_t> off(nblk);
-    HIP_TRY(e, hipMemcpyAsync(h.data(), bs.p, nblk * sizeof(uint64_t), hipMemcpyDeviceToHost, s));
-    HIP_TRY(e, hipStreamSynchronize(s));
-    uint64_t acc = 0;
-    for (uint64_t b = 0; b < nblk; b++) {
-        off[b] = (uint32_t)acc;
-        acc += h[b];
-    }
-    if (acc > 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "scan total exceeds 32 bits");
-    HIP_TRY(e, hipMemcpyAsync(bo.p, off.data(), nblk * sizeof(uint32_t), hipMemcpyHostToDevice, s));
+    HIP_TRY(e, launch_scan_blocks(bs.p, nblk, bo.p, &e->d_plan->info, s));
     HIP_TRY(e, launch_add_offsets(prefix, n, bo.p, s));
     HIP_TRY(e, hipStreamSynchronize(s));
     return HSPZ_OK;
@@ -158,40 +150,12 @@ int seed_windows(Engine *e, const uint8_t *h_ascii, uint64_t len, int strand, in
     return HSPZ_OK;
 }
 
-// Shared by hspz_plan and hspz_debug_plan_counts once counts and block-local prefixes
-// are on the device: 64-bit host scan of the block sums, refusal, add-back, chunk walk.
-int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint32_t *n_chunks) {
-    const uint64_t nblk = (n + kScanBlock - 1) / kScanBlock;
-    std::vector<uint64_t> blk(nblk);
-    if (nblk) {
-        HIP_TRY(e, hipMemcpyAsync(blk.data(), e->d_blksum, nblk * sizeof(uint64_t),
-                                  hipMemcpyDeviceToHost, s));
-        HIP_TRY(e, hipStreamSynchronize(s));
-    }
-    // exclusive block offsets; inclusive block prefix for the boundary search
-    std::vector<uint64_t> incl(nblk);
-    std::vector<uint32_t> off(nblk);
-    uint64_t acc = 0;
-    for (uint64_t b = 0; b < nblk; b++) {
-        off[b] = (uint32_t)acc;
-        acc += blk[b];
-        incl[b] = acc;
-        if (acc > 0xFFFFFFFFull) {
-            e->has_plan = false;
-            return fail(e, HSPZ_E_OVERFLOW,
-                        "batch total exceeds the 32-bit hit index (%llu hits or more); refused",
-                        (unsigned long long)acc);
-        }
-    }
-    const uint64_t total = acc;
-    if (nblk) {
-        HIP_TRY(e, hipMemcpyAsync(e->d_blkoff, off.data(), nblk * sizeof(uint32_t),
-                                  hipMemcpyHostToDevice, s));
-        HIP_TRY(e, launch_add_offsets(e->d_prefix, n, e->d_blkoff, s));
-    }
-
-    // Lower-bound walk ("C. Hit discovery", C.3).
-    e->chunks.clear();
+// Host half of the MAX_HITS walk ("C. Hit discovery", C.3), for chunk_walk = 1 and for
+// plans with more than kChunkCap chunks.  incl holds the inclusive block sums; the
+// prefix on the device is final.  With chunk_walk = 1 the whole prefix is copied back;
+// otherwise one 1,024-entry prefix block is copied per boundary.
+int host_walk(Engine *e, uint64_t n, uint64_t total, const std::vector<uint64_t> &incl,
+              hipStream_t s) {
     const uint64_t MAX = e->params.max_hits;
     std::vector<uint32_t> full;  // whole prefix (chunk_walk = 1)
     if (e->params.chunk_walk == 1 && total > 0 && MAX != 0 && total > MAX) {
@@ -235,6 +199,69 @@ int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint
         H = Pe;
         s0 = eidx + 1;
     }
+    return HSPZ_OK;
+}
+
+// Shared by hspz_plan and hspz_debug_plan_counts once counts and block-local prefixes
+// are on the device.  chunk_walk = 0: the 64-bit block-sum scan, the add-back and the
+// chunk walk run on the device, and one copy brings back the total and the chunk list.
+// chunk_walk = 1: the host scans the block sums and walks the whole prefix.  A total
+// over 2^32 - 1 is refused either way.
+int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint32_t *n_chunks) {
+    const uint64_t nblk = (n + kScanBlock - 1) / kScanBlock;
+    e->chunks.clear();
+    std::vector<uint64_t> incl;  // inclusive block sums, for the host walk
+    uint64_t total = 0;
+    bool walked = false;
+    auto refuse = [&](uint64_t t) {
+        e->has_plan = false;
+        return fail(e, HSPZ_E_OVERFLOW,
+                    "batch total exceeds the 32-bit hit index (%llu hits or more); refused",
+                    (unsigned long long)t);
+    };
+    auto host_incl = [&]() -> int {
+        std::vector<uint64_t> blk(nblk);
+        if (nblk) {
+            HIP_TRY(e, hipMemcpyAsync(blk.data(), e->d_blksum, nblk * sizeof(uint64_t),
+                                      hipMemcpyDeviceToHost, s));
+            HIP_TRY(e, hipStreamSynchronize(s));
+        }
+        incl.resize(nblk);
+        uint64_t acc = 0;
+        for (uint64_t b = 0; b < nblk; b++) incl[b] = acc += blk[b];
+        return HSPZ_OK;
+    };
+    int rc;
+    if (e->params.chunk_walk == 0) {
+        HIP_TRY(e, launch_scan_blocks(e->d_blksum, nblk, e->d_blkoff, &e->d_plan->info, s));
+        HIP_TRY(e, launch_add_offsets(e->d_prefix, n, e->d_blkoff, s));
+        HIP_TRY(e, launch_chunk_walk(e->d_prefix, n, e->params.max_hits, e->batch_lo,
+                                     e->d_plan, s));
+        HIP_TRY(e, hipMemcpyAsync(e->h_plan, e->d_plan, sizeof(PlanBuf), hipMemcpyDeviceToHost,
+                                  s));
+        HIP_TRY(e, hipStreamSynchronize(s));
+        total = e->h_plan->info.total;
+        if (total > 0xFFFFFFFFull) return refuse(total);
+        const uint32_t nc = e->h_plan->info.n_chunks;
+        if (nc <= kChunkCap) {
+            e->chunks.assign(e->h_plan->chunks, e->h_plan->chunks + nc);
+            walked = true;
+        } else if ((rc = host_incl())) {
+            return rc;
+        }
+    } else {
+        if ((rc = host_incl())) return rc;
+        total = nblk ? incl.back() : 0;
+        if (total > 0xFFFFFFFFull) return refuse(total);
+        std::vector<uint32_t> off(nblk);  // exclusive block offsets
+        for (uint64_t b = 0; b < nblk; b++) off[b] = (uint32_t)(b ? incl[b - 1] : 0);
+        if (nblk) {
+            HIP_TRY(e, hipMemcpyAsync(e->d_blkoff, off.data(), nblk * sizeof(uint32_t),
+                                      hipMemcpyHostToDevice, s));
+            HIP_TRY(e, launch_add_offsets(e->d_prefix, n, e->d_blkoff, s));
+        }
+    }
+    if (!walked && (rc = host_walk(e, n, total, incl, s))) return rc;
     e->total = total;
     e->has_plan = true;
     *total_hits = total;
@@ -242,9 +269,11 @@ int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint
     return HSPZ_OK;
 }
 
+// Per-batch and per-chunk scratch grows by at least a quarter at a time, so batches and
+// chunks a few seeds or anchors apart do not reallocate (and synchronise) pass after pass.
 int ensure_batch(Engine *e, uint64_t n) {
     if (n <= e->cap_batch && e->d_count) return HSPZ_OK;
-    const uint64_t cap = std::max<uint64_t>(n, 1);
+    const uint64_t cap = std::max<uint64_t>({n, 1, e->cap_batch + e->cap_batch / 4});
     const uint64_t nblk = (cap + kScanBlock - 1) / kScanBlock;
     int rc;
     if ((rc = dalloc(e, e->d_count, cap))) return rc;
@@ -257,8 +286,9 @@ int ensure_batch(Engine *e, uint64_t n) {
 }
 
 int ensure_compact(Engine *e, uint64_t n) {
-    const uint64_t nblk = (n + kCompactBlock - 1) / kCompactBlock + 1;
-    if (nblk <= e->cap_cblk && e->d_cblk) return HSPZ_OK;
+    const uint64_t need = (n + kCompactBlock - 1) / kCompactBlock + 1;
+    if (need <= e->cap_cblk && e->d_cblk) return HSPZ_OK;
+    const uint64_t nblk = std::max<uint64_t>(need, e->cap_cblk + e->cap_cblk / 4);
     int rc = dalloc(e, e->d_cblk, nblk);
     if (rc) return rc;
     e->cap_cblk = nblk;
@@ -291,7 +321,9 @@ Engine::~Engine() {
     dfree(d_blkoff);
     dfree(d_cblk);
     dfree(d_ctotal);
+    dfree(d_plan);
     if (h_pinned) (void)hipHostFree(h_pinned);
+    if (h_plan) (void)hipHostFree(h_plan);
 }
 
 void Engine::free_plan() {
@@ -400,7 +432,9 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     }
     if (hipHostMalloc(reinterpret_cast<void **>(&e->h_pinned), 64 * sizeof(uint32_t)) !=
             hipSuccess ||
-        dalloc(e, e->d_ctotal, 16) != HSPZ_OK || dalloc(e, e->d_defer_cnt, 16) != HSPZ_OK) {
+        hipHostMalloc(reinterpret_cast<void **>(&e->h_plan), sizeof(PlanBuf)) != hipSuccess ||
+        dalloc(e, e->d_ctotal, 16) != HSPZ_OK || dalloc(e, e->d_defer_cnt, 16) != HSPZ_OK ||
+        dalloc(e, e->d_plan, 1) != HSPZ_OK) {
         g_create_error = "pinned/device staging allocation failed";
         delete e;
         return HSPZ_E_NOMEM;

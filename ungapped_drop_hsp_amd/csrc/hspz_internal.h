@@ -97,6 +97,28 @@ hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, ui
                              uint32_t *prefix, uint64_t *blksum, hipStream_t s);
 hipError_t launch_add_offsets(uint32_t *prefix, uint64_t n, const uint32_t *blkoff,
                               hipStream_t s);
+
+// Plan results the device writes for one copy back: the batch total (64 bits, so a
+// total over 2^32 - 1 is seen and refused) and the MAX_HITS chunk list.
+constexpr uint32_t kChunkCap = 1024;
+struct PlanInfo {
+    uint64_t total;
+    uint32_t n_chunks;  // kChunkCap + 1: the list did not fit (the host walks instead)
+    uint32_t pad;
+};
+struct PlanBuf {
+    PlanInfo info;
+    hspz_chunk chunks[kChunkCap];
+};
+// Exclusive 64-bit scan of nblk block sums in one workgroup: blkoff[b] (32 bits, the
+// offset to add to block b) and info->total.
+hipError_t launch_scan_blocks(const uint64_t *blksum, uint64_t nblk, uint32_t *blkoff,
+                              PlanInfo *info, hipStream_t s);
+// Greedy MAX_HITS walk over the final inclusive prefix P[0..n) ("C. Hit discovery", C.3)
+// by one wave; chunk seed indices are offset by batch_lo.  Reads info->total and
+// writes buf->info.n_chunks and up to kChunkCap chunks.
+hipError_t launch_chunk_walk(const uint32_t *P, uint64_t n, uint64_t max_hits,
+                             uint64_t batch_lo, PlanBuf *buf, hipStream_t s);
 // Expand the seeds of one chunk (count, first, prefix and q_end of its seeds).
 hipError_t launch_expand(bool dense, const uint32_t *count, const uint32_t *first,
                          const uint32_t *q_end, const uint32_t *prefix, uint64_t n_seeds,
@@ -189,6 +211,8 @@ struct Engine {
     uint32_t *d_ctotal = nullptr;
     uint64_t cap_cblk = 0;
     uint32_t *h_pinned = nullptr;  // small pinned staging buffer (64 u32)
+    PlanBuf *d_plan = nullptr;     // device plan results
+    PlanBuf *h_plan = nullptr;     // pinned copy
 
     ~Engine();
     void free_plan();

@@ -5,8 +5,15 @@
 // kept per seed so that the expansion reads it in seed order instead of gathering it
 // from the 4^w-entry table again.  The block scans its counts locally
 // (64-bit partial sums, so a block total can never wrap) and publishes its block sum.
-// The host scans the block sums in 64 bits (refusing a batch over 2^32 - 1) and
-// k_add_offsets adds each block's exclusive offset back, giving the inclusive prefix.
+// k_scan_blocks scans the block sums in 64 bits in one workgroup (the host refuses a
+// batch whose total is over 2^32 - 1) and k_add_offsets adds each block's exclusive
+// offset back, giving the inclusive prefix.
+//
+// k_chunk_walk: the MAX_HITS cut ("C. Hit discovery", C.3) on the device, by one wave.
+// Each boundary is the first seed whose prefix reaches H + MAX_HITS, found by a 64-way
+// search: every round the lanes read the last prefix of 64 equal segments of the range
+// and a ballot picks the first segment that reaches the target, so a boundary costs
+// about log64(n) dependent reads.
 #include "hspz_internal.h"
 #include "wave.h"
 
@@ -100,7 +107,111 @@ __global__ __launch_bounds__(kThreads) void k_add_offsets(uint32_t *__restrict__
     }
 }
 
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_blocks(const uint64_t *__restrict__ blksum,
+                                                             uint64_t nblk,
+                                                             uint32_t *__restrict__ blkoff,
+                                                             PlanInfo *__restrict__ info) {
+    __shared__ uint64_t wave_tot[kScanThreads / 64];
+    const int t = threadIdx.x;
+    const uint64_t per = (nblk + kScanThreads - 1) / kScanThreads;
+    const uint64_t lo = min((uint64_t)t * per, nblk), hi = min(lo + per, nblk);
+    // each thread's segment is read eight sums at a time, so the loads overlap
+    constexpr int kBatch = 8;
+    uint64_t sum = 0;
+    uint64_t b = lo;
+    for (; b + kBatch <= hi; b += kBatch) {
+        uint64_t v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; k++) v[k] = blksum[b + k];
+#pragma unroll
+        for (int k = 0; k < kBatch; k++) sum += v[k];
+    }
+    for (; b < hi; b++) sum += blksum[b];
+    const uint64_t incl = wave_incl_sum_u64(sum);
+    if (lane_id() == 63) wave_tot[t >> 6] = incl;
+    __syncthreads();
+    uint64_t acc = incl - sum;
+    for (int w = 0; w < (t >> 6); w++) acc += wave_tot[w];
+    b = lo;
+    for (; b + kBatch <= hi; b += kBatch) {
+        uint64_t v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; k++) v[k] = blksum[b + k];
+#pragma unroll
+        for (int k = 0; k < kBatch; k++) {
+            blkoff[b + k] = (uint32_t)acc;
+            acc += v[k];
+        }
+    }
+    for (; b < hi; b++) {
+        blkoff[b] = (uint32_t)acc;
+        acc += blksum[b];
+    }
+    if (t == kScanThreads - 1) info->total = acc;
+}
+
+__global__ __launch_bounds__(64) void k_chunk_walk(const uint32_t *__restrict__ P, uint64_t n,
+                                                   uint64_t max_hits, uint64_t batch_lo,
+                                                   PlanBuf *__restrict__ buf) {
+    const int lane = lane_id();
+    const uint64_t total = buf->info.total;
+    uint32_t c = 0;
+    if (total > 0 && total <= 0xFFFFFFFFull) {
+        uint64_t s0 = 0, H = 0;
+        while (s0 < n && c <= kChunkCap) {
+            uint64_t e;
+            if (max_hits == 0 || total - H <= max_hits) {
+                e = n - 1;
+            } else {
+                // first e >= s0 with P[e] >= target; P[n - 1] = total > target
+                const uint32_t target = (uint32_t)(H + max_hits);
+                uint64_t lo = s0, hi = n - 1;
+                while (hi - lo >= 64) {
+                    const uint64_t step = (hi - lo + 64) / 64;  // ceil(span / 64)
+                    const uint64_t idx = min(lo + (uint64_t)(lane + 1) * step - 1, hi);
+                    // lane 63 reads P[hi] >= target, so the mask is never empty
+                    const uint64_t m = __ballot(P[idx] >= target);
+                    const uint64_t f = (uint64_t)__builtin_ctzll(m);
+                    hi = min(lo + (f + 1) * step - 1, hi);
+                    lo = lo + f * step;
+                }
+                const uint64_t idx = lo + (uint64_t)lane;
+                const uint64_t m = __ballot(idx <= hi && P[min(idx, hi)] >= target);
+                e = lo + (uint64_t)__builtin_ctzll(m);
+            }
+            const uint32_t Pe = P[e];
+            if (lane == 0 && c < kChunkCap) {
+                hspz_chunk ch;
+                ch.seed_lo = batch_lo + s0;
+                ch.seed_hi = batch_lo + e;
+                ch.hit_lo = H;
+                ch.n_hits = (uint64_t)Pe - H;
+                buf->chunks[c] = ch;
+            }
+            c++;
+            H = Pe;
+            s0 = e + 1;
+        }
+    }
+    if (lane == 0) buf->info.n_chunks = c;
+}
+
 }  // namespace
+
+hipError_t launch_scan_blocks(const uint64_t *blksum, uint64_t nblk, uint32_t *blkoff,
+                              PlanInfo *info, hipStream_t s) {
+    hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(kScanThreads), 0, s, blksum, nblk, blkoff,
+                       info);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_walk(const uint32_t *P, uint64_t n, uint64_t max_hits,
+                             uint64_t batch_lo, PlanBuf *buf, hipStream_t s) {
+    hipLaunchKernelGGL(k_chunk_walk, dim3(1), dim3(64), 0, s, P, n, max_hits, batch_lo, buf);
+    return hipGetLastError();
+}
 
 hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, uint64_t n,
                              const uint32_t *end_tbl, uint32_t *count, uint32_t *first,

@@ -16,7 +16,11 @@ from . import SEGMENT_PAIR, Engine
 
 
 class PassBuffers:
-    """Caller-owned device buffers for one chunk at a time, grown on demand."""
+    """Caller-owned device buffers for one chunk at a time, grown on demand.
+
+    Growth is geometric (at least a quarter more each time), so chunks that differ by a
+    few anchors do not reallocate the buffers pass after pass.
+    """
 
     def __init__(self, device: int = 0, anchors: int = 0, survivors: int = 0):
         import torch
@@ -29,13 +33,13 @@ class PassBuffers:
     def ensure(self, n_anchors: int, n_surv: int = 0):
         t = self.torch
         if n_anchors > self.cap_a or self.cap_a == 0:
-            cap = max(int(n_anchors), 1024)
+            cap = max(int(n_anchors), 1024, self.cap_a + self.cap_a // 4)
             self.anchors = t.empty(cap, dtype=t.int64, device=self.dev)
             self.flags = t.empty(cap + 16, dtype=t.uint8, device=self.dev)
             self.ids = t.empty(cap, dtype=t.int32, device=self.dev)
             self.cap_a = cap
         if n_surv > self.cap_s or self.cap_s == 0:
-            cap = max(int(n_surv), 1024)
+            cap = max(int(n_surv), 1024, self.cap_s + self.cap_s // 4)
             self.hsp = t.empty((cap, 4), dtype=t.int32, device=self.dev)
             self.status = t.empty(cap + 16, dtype=t.uint8, device=self.dev)
             self.out = t.empty((cap, 4), dtype=t.int32, device=self.dev)
