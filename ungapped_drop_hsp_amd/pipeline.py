@@ -51,21 +51,27 @@ class StageTimer:
 
     ``spans[name]`` collects (start, end) event pairs; ``elapsed_ms()`` sums them per
     stage after a synchronisation.  ``units[name]`` holds what each launch processed
-    (anchors for the gate), so per-launch averages can be formed.
+    (anchors for the gate), so per-launch averages can be formed.  ``only`` limits the
+    events to the named stages (each event costs host time between launches).
     """
 
-    def __init__(self):
+    def __init__(self, only=None):
         import torch
         self.torch = torch
+        self.only = None if only is None else frozenset(only)  # stages to time (None: all)
         self.spans = defaultdict(list)
         self.units = defaultdict(list)
 
-    def start(self, stream=None):
+    def start(self, name: str, stream=None):
+        if self.only is not None and name not in self.only:
+            return None
         ev = self.torch.cuda.Event(enable_timing=True)
         ev.record(stream)
         return ev
 
     def stop(self, name: str, ev0, units: int = 0, stream=None):
+        if ev0 is None:
+            return
         ev1 = self.torch.cuda.Event(enable_timing=True)
         ev1.record(stream)
         self.spans[name].append((ev0, ev1))
@@ -96,14 +102,14 @@ def run_pass(eng: Engine, seed_lo: int, seed_hi: int, bufs: PassBuffers, *,
     """
     tm = timer
 
-    def t0():
-        return tm.start(stream) if tm else None
+    def t0(name):
+        return tm.start(name, stream) if tm else None
 
     def t1(name, ev, units=0):
         if tm:
             tm.stop(name, ev, units, stream)
 
-    ev = t0()
+    ev = t0("plan")
     total, nch = eng.plan(seed_lo, seed_hi, stream=stream)
     t1("plan", ev, seed_hi - seed_lo)
     out: Dict = dict(total=total, n_chunks=nch, chunks=[], n_surv=0, n_acc=0)
@@ -111,20 +117,20 @@ def run_pass(eng: Engine, seed_lo: int, seed_hi: int, bufs: PassBuffers, *,
         ch = eng.get_chunk(c)
         n = ch["n_hits"]
         bufs.ensure(n)
-        ev = t0()
+        ev = t0("find_hits")
         eng.find_hits(c, bufs.anchors, stream=stream)
         t1("find_hits", ev, n)
-        ev = t0()
+        ev = t0("score_gate")
         eng.score_gate(bufs.anchors, n, bufs.flags, stream=stream)
         t1("score_gate", ev, n)
-        ev = t0()
+        ev = t0("compact")
         ns = eng.compact(bufs.flags, n, bufs.ids, cap=n, stream=stream)
         t1("compact", ev, n)
         bufs.ensure(n, ns)
-        ev = t0()
+        ev = t0("materialize")
         eng.materialize(bufs.anchors, bufs.ids, ns, bufs.hsp, bufs.status, stream=stream)
         t1("materialize", ev, ns)
-        ev = t0()
+        ev = t0("compact_hsps")
         na = eng.compact_hsps(bufs.hsp, bufs.status, ns, bufs.out, stream=stream)
         t1("compact_hsps", ev, ns)
         rec: Dict = dict(chunk=ch, n_anchors=n, n_surv=ns, n_acc=na,
