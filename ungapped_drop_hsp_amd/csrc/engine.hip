@@ -764,8 +764,8 @@ HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uin
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
     HIP_TRY(e, launch_gate_window(e->params.gate_mode == 3, d_anchors, (uint32_t)n, d_flags,
                                   e->d_ref4, e->d_qry4, e->wp, list1, list2, e->d_defer_cnt, s));
-    HIP_TRY(e, launch_gate_list(e->block_bases, d_anchors, list2, e->d_defer_cnt + 1,
-                                (uint32_t)n, d_flags, e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
+    HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
+                                     e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
     return HSPZ_OK;
 }

@@ -130,15 +130,15 @@ hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uin
 // Windowed gate in two stages.  Stage 1 decides every anchor whose walks end within its
 // window (48 bases right of the anchor and 72 left, or 32 and 56 when narrow) and lists
 // the others in list1; stage 2 decides those with 64 and 96 bases and lists the rest in
-// list2 (counts cnt[0], cnt[1]; the launcher clears both first).  launch_gate_list then
-// decides list2 exactly.
+// list2 (counts cnt[0], cnt[1]; the launcher clears both first).  launch_gate_list_wave
+// then decides list2 exactly, one wave per listed anchor.
 hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
                               const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
                               uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s);
-hipError_t launch_gate_list(int block_bases, const uint64_t *anchors, const uint32_t *list,
-                            const uint32_t *count, uint32_t max_count, uint8_t *flags,
-                            const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
-                            hipStream_t s);
+hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
+                                 const uint32_t *count, uint32_t max_count, uint8_t *flags,
+                                 const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
+                                 hipStream_t s);
 hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint32_t n_surv,
                               hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
                               const uint8_t *qry, const ScoreParams &sp, hipStream_t s);

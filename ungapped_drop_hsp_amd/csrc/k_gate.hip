@@ -29,14 +29,18 @@
 //    each wave collects them in LDS and the workgroup reserves its share of the global
 //    list with one atomic.
 //
-//  exact (k_gate, k_gate_list): one lane per anchor walking base blocks straight from
+//  exact, all anchors (k_gate): one lane per anchor walking base blocks straight from
 //    the byte-per-base sequences, refilling finished lanes from the wave's tile of
-//    anchors (ranks from a ballot).  Used for the deferred anchors, and for every anchor
-//    when the window path's preconditions do not hold.
+//    anchors (ranks from a ballot).  Used when the window path's preconditions do not
+//    hold.
+//
+//  exact, listed anchors (k_gate_list_wave): one wave per anchor the window stages left,
+//    walking 64-base tiles with wave scans (walk.h), since those walks are long.
 #include <algorithm>
 #include <type_traits>
 
 #include "hspz_internal.h"
+#include "walk.h"
 #include "wave.h"
 
 namespace hspz {
@@ -180,40 +184,39 @@ __global__ __launch_bounds__(kThreads) void k_gate(const uint64_t *__restrict__ 
     }
 }
 
-// The exact path over a list of anchor indices (*count of them, read on the device):
-// each wave gathers a tile of listed anchors into LDS, walks them, and writes their
-// flags back to the listed slots.  Waves stride over the list's tiles.
-template <int B>
-__global__ __launch_bounds__(kThreads) void k_gate_list(const uint64_t *__restrict__ anchors,
-                                                        const uint32_t *__restrict__ list,
-                                                        const uint32_t *__restrict__ count,
-                                                        uint8_t *__restrict__ flags,
-                                                        const uint8_t *__restrict__ ref,
-                                                        const uint8_t *__restrict__ qry,
-                                                        ScoreParams sp) {
+// The exact decision for the anchors the window stages could not finish (*count of them,
+// listed by index, read on the device).  Their walks are long (homologous stretches), so
+// each gets one wave that walks 64-base tiles (exact_walk) and stops as soon as the flag
+// is known: at the drop, or once R* (right) or R* + best so far (left) reaches T.
+__global__ __launch_bounds__(kThreads) void k_gate_list_wave(const uint64_t *__restrict__ anchors,
+                                                             const uint32_t *__restrict__ list,
+                                                             const uint32_t *__restrict__ count,
+                                                             uint8_t *__restrict__ flags,
+                                                             const uint8_t *__restrict__ ref,
+                                                             const uint8_t *__restrict__ qry,
+                                                             ScoreParams sp) {
     __shared__ int32_t tab[kTabSize];
-    __shared__ int32_t rstar[kWaves][kTile];
-    __shared__ uint32_t flg[kWaves][kTile / 4];
-    __shared__ uint64_t an[kWaves][kTile];
     if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
     __syncthreads();
-
-    const int w = threadIdx.x >> 6;
-    const int lane = lane_id();
     const uint64_t total = *count;
-    const uint64_t stride = (uint64_t)gridDim.x * kWaves * kTile;
-    uint8_t *fl8 = reinterpret_cast<uint8_t *>(flg[w]);
-    for (uint64_t tile0 = ((uint64_t)blockIdx.x * kWaves + w) * kTile; tile0 < total;
-         tile0 += stride) {
-        const int cnt = (int)min<uint64_t>((uint64_t)kTile, total - tile0);
-        for (int i = lane; i < cnt; i += 64) an[w][i] = anchors[list[tile0 + i]];
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        walk_phase<+1, B>(an[w], cnt, tab, ref, qry, sp, rstar[w], fl8);
-        walk_phase<-1, B>(an[w], cnt, tab, ref, qry, sp, rstar[w], fl8);
-        for (int i = lane; i < cnt; i += 64) flags[list[tile0 + i]] = fl8[i];
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+    const uint64_t nw = (uint64_t)gridDim.x * kWaves;
+    for (uint64_t t = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); t < total; t += nw) {
+        const uint32_t i = list[t];
+        const uint64_t a = anchors[i];
+        const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
+        bool keep = false;  // an anchor outside the sequences scores 0 on both sides
+        if (r <= sp.n_ref && q <= sp.n_qry) {
+            int32_t R, L;
+            uint32_t ext;
+            exact_walk<+1, false>(tab, ref + r, qry + q, sp.xdrop, sp.T, R, ext);
+            if (R >= sp.T) {
+                keep = true;
+            } else {
+                exact_walk<-1, false>(tab, ref + r, qry + q, sp.xdrop, sp.T - R, L, ext);
+                keep = (int64_t)R + L >= (int64_t)sp.T;
+            }
+        }
+        if (lane_id() == 0) flags[i] = keep ? 1 : 0;
     }
 }
 
@@ -531,32 +534,15 @@ hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uin
     return hipGetLastError();
 }
 
-hipError_t launch_gate_list(int block_bases, const uint64_t *anchors, const uint32_t *list,
-                            const uint32_t *count, uint32_t max_count, uint8_t *flags,
-                            const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
-                            hipStream_t s) {
+hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
+                                 const uint32_t *count, uint32_t max_count, uint8_t *flags,
+                                 const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
+                                 hipStream_t s) {
     if (max_count == 0) return hipSuccess;
-    const uint32_t per_block = kWaves * kTile;
     const uint32_t blocks =
-        (uint32_t)std::min<uint64_t>(((uint64_t)max_count + per_block - 1) / per_block, 2048);
-    switch (block_bases) {
-    case 8:
-        hipLaunchKernelGGL(k_gate_list<8>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
-                           count, flags, ref, qry, sp);
-        break;
-    case 4:
-        hipLaunchKernelGGL(k_gate_list<4>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
-                           count, flags, ref, qry, sp);
-        break;
-    case 2:
-        hipLaunchKernelGGL(k_gate_list<2>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
-                           count, flags, ref, qry, sp);
-        break;
-    default:
-        hipLaunchKernelGGL(k_gate_list<1>, dim3(blocks), dim3(kThreads), 0, s, anchors, list,
-                           count, flags, ref, qry, sp);
-        break;
-    }
+        (uint32_t)std::min<uint64_t>(((uint64_t)max_count + kWaves - 1) / kWaves, 4096);
+    hipLaunchKernelGGL(k_gate_list_wave, dim3(blocks), dim3(kThreads), 0, s, anchors, list, count,
+                       flags, ref, qry, sp);
     return hipGetLastError();
 }
 

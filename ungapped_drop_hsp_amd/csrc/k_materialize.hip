@@ -1,16 +1,12 @@
 // Exact X-drop materialization ("E. X-drop materialization", E.1-E.5).
 //
-// One wave per survivor.  Each step scores a 64-base tile: lane i holds base
-// base + i, an inclusive wave scan (DPP) gives the running score, a prefix maximum
-// (seeded with the best so far) gives the running best, and a ballot of lanes whose
-// drawdown exceeds xdrop marks the first drop.  The running best in the lane before the
-// first drop is the tile's best; its extent is the lowest lane attaining it, so an equal
-// later maximum never moves the endpoint.  With the entropy-adjusted decision on, the
-// wave then counts the record's reference bases (entropy_accept).  Lane 0 stores the
-// 16-byte record and the status.
+// One wave per survivor walks both sides with exact_walk (64-base tiles, earliest
+// endpoints).  With the entropy-adjusted decision on, the wave then counts the record's
+// reference bases (entropy_accept).  Lane 0 stores the 16-byte record and the status.
 #include <climits>
 
 #include "hspz_internal.h"
+#include "walk.h"
 #include "wave.h"
 
 namespace hspz {
@@ -19,37 +15,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-
-template <int D>
-__device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp,
-                                           const uint8_t *qp, int32_t xdrop, int32_t &best_out,
-                                           uint32_t &ext_out) {
-    const int l = lane_id();
-    int32_t best = 0, carry = 0;
-    uint32_t ext = 0, base = 0;
-    for (;;) {
-        const int64_t off = D > 0 ? (int64_t)base + l : -(int64_t)base - 1 - l;
-        const int32_t sg = tab[rp[off] | qp[off]];
-        const int32_t s = wave_incl_sum(sg) + carry;
-        // running best including every base up to this lane (and the tiles before)
-        const int32_t run_best = max(wave_incl_max(s), best);
-        const uint64_t dm = __ballot(run_best - s > xdrop);
-        const int f = dm ? (int)__builtin_ctzll(dm) : 64;  // first dropping lane
-        if (f > 0) {
-            const int32_t tb = lane_value(run_best, f - 1);  // best before the drop
-            if (tb > best) {
-                const uint64_t at = __ballot(l < f && s == tb);
-                ext = base + (uint32_t)__builtin_ctzll(at) + 1u;
-                best = tb;
-            }
-        }
-        if (dm) break;
-        carry = lane_value(s, 63);
-        base += 64;
-    }
-    best_out = best;
-    ext_out = ext;
-}
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -96,8 +61,10 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
     const bool bad = r > sp.n_ref || q > sp.n_qry;  // outside the sequences: empty walks
     int32_t R, L;
     uint32_t k, m;
-    exact_walk<+1>(tab, ref + (bad ? sp.n_ref : r), qry + (bad ? sp.n_qry : q), sp.xdrop, R, k);
-    exact_walk<-1>(tab, ref + (bad ? 0u : r), qry + (bad ? 0u : q), sp.xdrop, L, m);
+    exact_walk<+1, true>(tab, ref + (bad ? sp.n_ref : r), qry + (bad ? sp.n_qry : q), sp.xdrop,
+                         INT32_MAX, R, k);
+    exact_walk<-1, true>(tab, ref + (bad ? 0u : r), qry + (bad ? 0u : q), sp.xdrop, INT32_MAX,
+                         L, m);
     const int64_t total = (int64_t)L + (int64_t)R;
     bool ok = total >= (int64_t)sp.T;  // wave-uniform
     if (ok && sp.entropy_mode == 1) ok = entropy_accept(ref, r - m, m + k - 1u, total, sp.K);
