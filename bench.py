@@ -46,8 +46,8 @@ GATE_BYTES_PER_ANCHOR = 9       # 8-byte packed anchor read + 1-byte flag write
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3,
                     help="workload index (3 = 50 Mb x 50 Mb, the one the metric is quoted on)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,

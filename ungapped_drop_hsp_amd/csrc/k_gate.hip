@@ -208,11 +208,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_list_wave(const uint64_t *__r
         if (r <= sp.n_ref && q <= sp.n_qry) {
             int32_t R, L;
             uint32_t ext;
-            exact_walk<+1, false>(tab, ref + r, qry + q, sp.xdrop, sp.T, R, ext);
+            exact_walk<+1, false, false>(tab, ref + r, qry + q, sp.xdrop, sp.T, R, ext);
             if (R >= sp.T) {
                 keep = true;
             } else {
-                exact_walk<-1, false>(tab, ref + r, qry + q, sp.xdrop, sp.T - R, L, ext);
+                exact_walk<-1, false, false>(tab, ref + r, qry + q, sp.xdrop, sp.T - R, L, ext);
                 keep = (int64_t)R + L >= (int64_t)sp.T;
             }
         }

@@ -61,10 +61,10 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
     const bool bad = r > sp.n_ref || q > sp.n_qry;  // outside the sequences: empty walks
     int32_t R, L;
     uint32_t k, m;
-    exact_walk<+1, true>(tab, ref + (bad ? sp.n_ref : r), qry + (bad ? sp.n_qry : q), sp.xdrop,
-                         INT32_MAX, R, k);
-    exact_walk<-1, true>(tab, ref + (bad ? 0u : r), qry + (bad ? 0u : q), sp.xdrop, INT32_MAX,
-                         L, m);
+    const uint8_t *rr = ref + (bad ? sp.n_ref : r), *qr = qry + (bad ? sp.n_qry : q);
+    const uint8_t *rl = ref + (bad ? 0u : r), *ql = qry + (bad ? 0u : q);
+    exact_walk<+1, true, true>(tab, rr, qr, sp.xdrop, INT32_MAX, R, k);
+    exact_walk<-1, true, true>(tab, rl, ql, sp.xdrop, INT32_MAX, L, m);
     const int64_t total = (int64_t)L + (int64_t)R;
     bool ok = total >= (int64_t)sp.T;  // wave-uniform
     if (ok && sp.entropy_mode == 1) ok = entropy_accept(ref, r - m, m + k - 1u, total, sp.K);

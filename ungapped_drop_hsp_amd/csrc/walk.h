@@ -8,7 +8,8 @@
 // lane attaining it, so an equal later maximum never moves the endpoint.  The walk also
 // ends once best >= stop (the caller's decision is then known; pass INT32_MAX to walk to
 // the drop).  Bases outside a sequence are edge codes scoring -(xdrop + 1), so a walk
-// ends within the first tile that reaches an edge; the padding holds that tile.
+// ends within the first tile that reaches an edge; the padding (kPad bytes) holds that
+// tile and the one read ahead of it.
 #pragma once
 
 #include <climits>
@@ -18,16 +19,23 @@
 
 namespace hspz {
 
-template <int D, bool Ext>
+template <int D, bool Ext, bool ReadAhead>
 __device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp,
                                            const uint8_t *qp, int32_t xdrop, int32_t stop,
                                            int32_t &best_out, uint32_t &ext_out) {
     const int l = lane_id();
     int32_t best = 0, carry = 0;
     uint32_t ext = 0, base = 0;
+    auto score = [&](uint32_t b) {
+        const int64_t off = D > 0 ? (int64_t)b + l : -(int64_t)b - 1 - l;
+        return tab[rp[off] | qp[off]];
+    };
+    int32_t sg = score(0);
     for (;;) {
-        const int64_t off = D > 0 ? (int64_t)base + l : -(int64_t)base - 1 - l;
-        const int32_t sg = tab[rp[off] | qp[off]];
+        // with ReadAhead the next tile's scores are read while this one is scored (long
+        // walks); a walk reaching an edge drops inside the tile that holds it, so this
+        // reads at most 127 bases past the first edge base, inside the padding
+        const int32_t sg_next = ReadAhead ? score(base + 64) : 0;
         const int32_t s = wave_incl_sum(sg) + carry;
         // running best including every base up to this lane (and the tiles before)
         const int32_t run_best = max(wave_incl_max(s), best);
@@ -46,6 +54,7 @@ __device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp
         if (dm || best >= stop) break;
         carry = lane_value(s, 63);
         base += 64;
+        sg = ReadAhead ? sg_next : score(base);
     }
     best_out = best;
     ext_out = ext;
