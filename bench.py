@@ -5,7 +5,8 @@
 A step is one whole pass over the workload's query seeds, for every strand and query
 batch it names: plan (hit counts, global prefix, MAX_HITS chunk cut), then for every
 chunk the backward expansion, the score gate, survivor compaction, exact materialization
-and accepted-record compaction, with the accepted records copied to the host.  The
+and accepted-record compaction, with the accepted records copied to the host.  Each batch
+is one call of the library's native driver (hspz_run_batch).  The
 reference index, the query seeds and the encoded sequences are resident in HBM before the
 timed region starts (the engine holds one strand at a time, so each strand is uploaded
 before its own timed passes and the step time sums the strands).
@@ -173,13 +174,16 @@ def main():
     # A step covers every strand and every query batch of the workload.  The engine holds
     # one query strand at a time, so each strand's seeds are uploaded before its own
     # warmup and timed passes; the step time is the sum over strands.
-    # The timed passes bracket only the score gate with HIP events (the roofline's launch
-    # time); every event costs host time between launches, so the per-stage breakdown
-    # comes from one more step per strand, instrumented throughout, after the timed ones.
+    # The timed passes run each batch through the native driver (hspz_run_batch: plan and
+    # every chunk in one call, records to pinned host memory), which brackets each
+    # score-gate call with HIP events on the launch stream for the roofline.  The
+    # per-stage breakdown comes from one more step per strand through the per-call ABI,
+    # with events around every call, after the timed ones.
     bufs = PassBuffers(0)
-    timer = StageTimer(only={"score_gate"})
     stages = StageTimer()
     wall = 0.0
+    gate_ms_sum = 0.0
+    gate_calls = gate_anchors = 0
     anchors = surv = acc = chunks = seeds = 0
     chunk_list = []  # (strand, lo, hi) batches of the last step, for the walk statistics
     # Python's cyclic collector stays off over the passes: a collection inside the timed
@@ -198,35 +202,36 @@ def main():
               file=sys.stderr, flush=True)
         for _ in range(args.warmup):
             for lo, hi in bs:
-                run_pass(eng, lo, hi, bufs)
+                eng.run_batch(lo, hi)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            res = [run_pass(eng, lo, hi, bufs, timer=timer) for lo, hi in bs]
+            res = [eng.run_batch(lo, hi, time_gate=True) for lo, hi in bs]
+            for r in res:
+                gate_ms_sum += r["gate_ms"]
+                gate_calls += r["gate_calls"]
+                gate_anchors += r["n_anchors"]
         torch.cuda.synchronize()
         wall += time.perf_counter() - t0
         for lo, hi in bs:
             run_pass(eng, lo, hi, bufs, timer=stages)
-        anchors += sum(r["total"] for r in res)
-        surv += sum(r["n_surv"] for r in res)
-        acc += sum(r["n_acc"] for r in res)
+        anchors += sum(r["n_anchors"] for r in res)
+        surv += sum(r["n_survivors"] for r in res)
+        acc += sum(r["n_accepted"] for r in res)
         chunks += sum(r["n_chunks"] for r in res)
         # the walk statistics below run on the current strand's last batches
         chunk_list = [(strand, lo, hi) for lo, hi in bs]
     gc.enable()
     print(f"[bench] {args.steps} timed steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    ms = timer.elapsed_ms()
     ms_per_step = 1000.0 * wall / args.steps
     value = anchors / (ms_per_step / 1000.0)
     stage_ms = {k: sum(v) for k, v in stages.elapsed_ms().items()}
 
     # Gate roofline: compulsory bytes and exact base steps of the launches timed above.
-    gate_ms = ms["score_gate"]
-    gate_units = timer.units["score_gate"]
-    gate_launches = len(gate_ms)
-    gate_ms_avg = sum(gate_ms) / gate_launches
-    units_avg = sum(gate_units) / gate_launches
+    gate_launches = gate_calls
+    gate_ms_avg = gate_ms_sum / gate_launches
+    units_avg = gate_anchors / gate_launches
     gate_gbs = GATE_BYTES_PER_ANCHOR * units_avg / (gate_ms_avg * 1e6)
     # base steps per anchor and the gate's stage split, over the last strand's batches
     steps_total = walked = 0

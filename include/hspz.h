@@ -157,10 +157,11 @@ int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
                     uint64_t *seed_lo, uint64_t *seed_hi);
 
 /* Plan one batch, seeds [seed_lo, seed_hi) ("C. Hit discovery", C.1-C.3): count each
- * seed's hits, scan blocks of counts on the device, exclusive-scan the block sums on
- * the host in 64 bits, add the offsets back to form the global inclusive prefix, and
- * cut MAX_HITS chunks with the lower-bound walk (a seed is never split).  A batch whose
- * total exceeds 2^32 - 1 is refused with HSPZ_E_OVERFLOW before anything else is done.
+ * seed's hits, scan blocks of counts on the device, exclusive-scan the block sums in
+ * 64 bits on the device, add the offsets back to form the global inclusive prefix, and
+ * cut MAX_HITS chunks with the lower-bound walk (a seed is never split), also on the
+ * device; one copy brings back the total and the chunk list.  A batch whose total
+ * exceeds 2^32 - 1 is refused with HSPZ_E_OVERFLOW and leaves no plan.
  * *total_hits and *n_chunks receive the totals (0 chunks when the total is 0).
  * Synchronises stream.  Errors: HSPZ_E_STATE (no reference/query), HSPZ_E_INVALID,
  * HSPZ_E_OVERFLOW, HSPZ_E_NOMEM, HSPZ_E_HIP. */
@@ -203,7 +204,8 @@ int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n, uint32
  * With left extent m and right extent k the record is
  * {r - m, q - m, m + k - 1, L* + R*}.  d_status[i] = 1 if the record is accepted
  * (score >= T, and with entropy_mode 1 also score * H >= 2K, see hspz_params), else 0;
- * d_hsp[i] is written in either case and is meaningful only when accepted.  Errors: HSPZ_E_STATE, HSPZ_E_HIP. */
+ * d_hsp[i] is written in either case and is meaningful only when accepted.
+ * Errors: HSPZ_E_STATE, HSPZ_E_HIP. */
 int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors, const uint32_t *d_ids,
                      uint64_t n_surv, hspz_segment_pair *d_hsp, uint8_t *d_status,
                      void *stream);
@@ -214,6 +216,38 @@ int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors, const uint3
 int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
                       const uint8_t *d_status, uint64_t n, hspz_segment_pair *d_out,
                       uint64_t cap, uint64_t *n_out, void *stream);
+
+/* ---- whole batch ------------------------------------------------------------------ */
+
+/* Counts of the last hspz_run_batch call. */
+typedef struct {
+    uint64_t n_anchors;    /* raw anchors (the plan's total hits)                       */
+    uint64_t n_chunks;     /* MAX_HITS chunks                                           */
+    uint64_t n_survivors;  /* anchors the gate kept                                     */
+    uint64_t n_accepted;   /* accepted records                                          */
+    uint64_t gate_calls;   /* score-gate calls timed (time_gate != 0), else 0          */
+    double gate_ms;        /* their summed durations from HIP events on the stream      */
+} hspz_batch_stats;
+
+/* The whole pass for query seeds [seed_lo, seed_hi) of the current strand, in one call:
+ * hspz_plan, then for every chunk hspz_find_hits, hspz_score_gate, hspz_compact,
+ * hspz_materialize and hspz_compact_hsps in the pages' order ("C. Hit discovery" to
+ * "E. X-drop materialization"), with the same kernels and the same bytes.  The chunk
+ * buffers are the engine's own (grown as needed); the accepted records of every chunk,
+ * in chunk order, are copied to pinned host memory the engine owns, from where
+ * hspz_get_batch_records reads them.  With time_gate != 0 each score-gate call is
+ * bracketed by HIP events on stream and *stats reports their summed duration.  The plan
+ * stays current afterwards.  Synchronises stream.  Errors: as hspz_plan, hspz_find_hits
+ * and the calls above; HSPZ_E_INVALID for a NULL stats pointer. */
+int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, int32_t time_gate,
+                   hspz_batch_stats *stats, void *stream);
+
+/* Copy the accepted records of the last hspz_run_batch (host to host): *n receives their
+ * number and up to cap records go to h_out (h_out NULL with cap 0 only reports *n).
+ * Errors: HSPZ_E_CAPACITY (cap < *n; the first cap records are still copied),
+ * HSPZ_E_INVALID (NULL n, or NULL h_out with cap > 0). */
+int hspz_get_batch_records(const hspz_engine *engine, hspz_segment_pair *h_out, uint64_t cap,
+                           uint64_t *n);
 
 /* ---- inspection (tests and tools) -------------------------------------------------- */
 

@@ -402,3 +402,65 @@ def test_entropy_mode_config1():
     p = dict(w.params(), entropy_mode=1)
     o, _, _ = oracle_pass(w.ref, w.query, p)
     assert_pass_equal(gpu_full_pass(engine(p), w.ref, w.query), o)
+
+
+def _oracle_batch(o):
+    recs = [c["accepted"] for c in o["chunks"]]
+    acc = np.concatenate(recs) if recs else np.zeros(0, oracle.HSP_DTYPE)
+    return dict(n_anchors=o["total"], n_chunks=len(o["chunks"]),
+                n_survivors=sum(int(c["ids"].size) for c in o["chunks"]),
+                n_accepted=int(acc.size)), acc
+
+
+@pytest.mark.parametrize("case", CASES[:4], ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
+def test_run_batch_matches_the_oracle(case):
+    # the native whole-batch driver against the oracle's pass: counts and every accepted
+    # record, in chunk order, over the whole strand and over sub-batches
+    seed, nr, nq, pat, mx, nf, plant, ident, gc = case
+    ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
+                           identity=ident, gc=gc, alphabet_noise=True)
+    p = params_of(pat, max_hits=mx)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    n = eng.num_seeds()
+    for lo, hi in [(0, n), (0, n // 3), (n // 3, n), (n // 2, n // 2)]:
+        o, _, _ = oracle_pass(ref, qry, p, seed_range=(lo, hi))
+        want, acc = _oracle_batch(o)
+        st = eng.run_batch(lo, hi, time_gate=True)
+        assert {k: st[k] for k in want} == want
+        assert st["gate_calls"] == st["n_chunks"]
+        assert (st["gate_ms"] > 0) == (st["n_chunks"] > 0)
+        got = eng.batch_records()
+        assert np.array_equal(got.view(np.uint8), acc.astype(oracle.HSP_DTYPE).view(np.uint8))
+
+
+def test_run_batch_reverse_strand_and_entropy():
+    ref, qry = random_pair(11, 30_000, 25_000, n_frac=0.02, plant=25, plant_len=(80, 900),
+                           identity=0.9, gc=0.41, alphabet_noise=True)
+    for mode in (0, 1):
+        p = params_of(SEED_PATTERN, max_hits=3_000, entropy_mode=mode)
+        eng = engine(p)
+        eng.upload_reference(ref)
+        eng.upload_query(qry, strand=1)
+        o, _, _ = oracle_pass(ref, qry, p, strand="-")
+        want, acc = _oracle_batch(o)
+        st = eng.run_batch(0, eng.num_seeds())
+        assert {k: st[k] for k in want} == want and st["gate_calls"] == 0
+        assert np.array_equal(eng.batch_records().view(np.uint8),
+                              acc.astype(oracle.HSP_DTYPE).view(np.uint8))
+
+
+def test_run_batch_errors():
+    p = params_of(SEED_PATTERN)
+    eng = engine(p)
+    import ungapped_drop_hsp_amd as h
+    with pytest.raises(h.HspzError):
+        eng.run_batch(0, 0)  # no reference or query yet
+    ref, qry = random_pair(3, 5_000, 5_000, plant=3, plant_len=(200, 400), identity=0.95)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    with pytest.raises(h.HspzError):
+        eng.run_batch(0, eng.num_seeds() + 1)
+    st = eng.run_batch(0, eng.num_seeds())
+    assert st["n_accepted"] == eng.batch_records().size

@@ -31,7 +31,7 @@ ABI_SYMBOLS = (
     "hspz_plan", "hspz_get_chunk", "hspz_find_hits", "hspz_score_gate", "hspz_compact",
     "hspz_materialize", "hspz_compact_hsps", "hspz_get_seeds", "hspz_get_plan_arrays",
     "hspz_get_index", "hspz_debug_plan_counts", "hspz_debug_walk_steps",
-    "hspz_debug_gate_deferred",
+    "hspz_debug_gate_deferred", "hspz_run_batch", "hspz_get_batch_records",
 )
 
 
@@ -54,6 +54,12 @@ class Params(ctypes.Structure):
 class Chunk(ctypes.Structure):
     _fields_ = [("seed_lo", ctypes.c_uint64), ("seed_hi", ctypes.c_uint64),
                 ("hit_lo", ctypes.c_uint64), ("n_hits", ctypes.c_uint64)]
+
+
+class BatchStats(ctypes.Structure):
+    _fields_ = [("n_anchors", ctypes.c_uint64), ("n_chunks", ctypes.c_uint64),
+                ("n_survivors", ctypes.c_uint64), ("n_accepted", ctypes.c_uint64),
+                ("gate_calls", ctypes.c_uint64), ("gate_ms", ctypes.c_double)]
 
 
 def _load() -> ctypes.CDLL:
@@ -81,6 +87,9 @@ def _load() -> ctypes.CDLL:
         "hspz_get_seeds": (ctypes.c_int, [P, U64, U64, P, P]),
         "hspz_get_plan_arrays": (ctypes.c_int, [P, P, P]),
         "hspz_get_index": (ctypes.c_int, [P, P, P, PU64, PU64]),
+        "hspz_run_batch": (ctypes.c_int, [P, U64, U64, ctypes.c_int32,
+                                          ctypes.POINTER(BatchStats), P]),
+        "hspz_get_batch_records": (ctypes.c_int, [P, P, U64, PU64]),
         "hspz_debug_plan_counts": (ctypes.c_int, [P, P, U64, P, PU64, PU32]),
         "hspz_debug_walk_steps": (ctypes.c_int, [P, P, U64, PU64, P]),
         "hspz_debug_gate_deferred": (ctypes.c_int, [P, PU64, PU64, P]),
@@ -252,6 +261,24 @@ class Engine:
         q = np.empty(max(hi - lo, 0), np.uint32)
         self._check(_lib.hspz_get_seeds(self._h, lo, hi, k.ctypes.data, q.ctypes.data))
         return k, q
+
+    def run_batch(self, seed_lo: int, seed_hi: int, time_gate: bool = False,
+                  stream=None) -> Dict:
+        """The whole pass over seeds [seed_lo, seed_hi) in one native call; the accepted
+        records stay in the engine's pinned staging (``batch_records``)."""
+        st = BatchStats()
+        self._check(_lib.hspz_run_batch(self._h, seed_lo, seed_hi, 1 if time_gate else 0,
+                                        ctypes.byref(st), _stream(stream)))
+        return {f: getattr(st, f) for f, _ in BatchStats._fields_}
+
+    def batch_records(self) -> np.ndarray:
+        """Accepted records of the last run_batch, in chunk order."""
+        n = ctypes.c_uint64()
+        self._check(_lib.hspz_get_batch_records(self._h, None, 0, ctypes.byref(n)))
+        out = np.empty(max(n.value, 1), SEGMENT_PAIR)
+        self._check(_lib.hspz_get_batch_records(self._h, out.ctypes.data, n.value,
+                                                ctypes.byref(n)))
+        return out[:n.value]
 
     def get_index(self) -> Tuple[np.ndarray, np.ndarray]:
         """(bucket ends with the leading 0, reference ends grouped by k-mer)."""

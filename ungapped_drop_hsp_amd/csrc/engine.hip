@@ -322,8 +322,17 @@ Engine::~Engine() {
     dfree(d_cblk);
     dfree(d_ctotal);
     dfree(d_plan);
+    dfree(rb_anchors);
+    dfree(rb_flags);
+    dfree(rb_ids);
+    dfree(rb_hsp);
+    dfree(rb_out);
+    dfree(rb_status);
+    for (hipEvent_t ev : gate_ev)
+        if (ev) (void)hipEventDestroy(ev);
     if (h_pinned) (void)hipHostFree(h_pinned);
     if (h_plan) (void)hipHostFree(h_plan);
+    if (h_rec) (void)hipHostFree(h_rec);
 }
 
 void Engine::free_plan() {
@@ -833,6 +842,121 @@ HSPZ_API int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_h
                             as_stream(stream));
     if (rc) *n_out = 0;
     return rc;
+}
+
+// Grow the whole-batch chunk buffers to n anchors and s survivors (a quarter of headroom).
+static int ensure_run_buffers(Engine *e, uint64_t n, uint64_t ns) {
+    int rc;
+    if (n > e->rb_cap_a || !e->rb_anchors) {
+        const uint64_t cap = std::max<uint64_t>({n, 1024, e->rb_cap_a + e->rb_cap_a / 4});
+        if ((rc = dalloc(e, e->rb_anchors, cap)) || (rc = dalloc(e, e->rb_flags, cap + 16)) ||
+            (rc = dalloc(e, e->rb_ids, cap))) {
+            e->rb_cap_a = 0;
+            return rc;
+        }
+        e->rb_cap_a = cap;
+    }
+    if (ns > e->rb_cap_s || !e->rb_hsp) {
+        const uint64_t cap = std::max<uint64_t>({ns, 1024, e->rb_cap_s + e->rb_cap_s / 4});
+        if ((rc = dalloc(e, e->rb_hsp, cap)) || (rc = dalloc(e, e->rb_out, cap)) ||
+            (rc = dalloc(e, e->rb_status, cap + 16))) {
+            e->rb_cap_s = 0;
+            return rc;
+        }
+        e->rb_cap_s = cap;
+    }
+    return HSPZ_OK;
+}
+
+// Room for n records in the pinned staging; the first keep records are carried over.
+static int ensure_record_staging(Engine *e, uint64_t n, uint64_t keep, hipStream_t s) {
+    if (n <= e->h_rec_cap && e->h_rec) return HSPZ_OK;
+    const uint64_t cap = std::max<uint64_t>({n, 4096, e->h_rec_cap + e->h_rec_cap / 2});
+    hspz_segment_pair *p = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void **>(&p), cap * sizeof(hspz_segment_pair)) !=
+        hipSuccess)
+        return fail(e, HSPZ_E_NOMEM, "pinned record staging of %llu records failed",
+                    (unsigned long long)cap);
+    if (e->h_rec) {
+        HIP_TRY(e, hipStreamSynchronize(s));  // copies into the old staging have landed
+        if (keep) memcpy(p, e->h_rec, keep * sizeof(hspz_segment_pair));
+        (void)hipHostFree(e->h_rec);
+    }
+    e->h_rec = p;
+    e->h_rec_cap = cap;
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi,
+                            int32_t time_gate, hspz_batch_stats *stats, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!stats) return fail(e, HSPZ_E_INVALID, "NULL stats");
+    *stats = hspz_batch_stats{};
+    e->h_rec_n = 0;
+    hipStream_t s = as_stream(stream);
+    uint64_t total = 0;
+    uint32_t nch = 0;
+    int rc = hspz_plan(engine, seed_lo, seed_hi, stream, &total, &nch);
+    if (rc) return rc;
+    stats->n_anchors = total;
+    stats->n_chunks = nch;
+    uint64_t maxn = 0;
+    for (const hspz_chunk &c : e->chunks) maxn = std::max<uint64_t>(maxn, c.n_hits);
+    if ((rc = ensure_run_buffers(e, maxn, 0))) return rc;
+    if (time_gate)
+        for (hipEvent_t &ev : e->gate_ev)
+            if (!ev) HIP_TRY(e, hipEventCreate(&ev));
+    uint64_t acc = 0;
+    for (uint32_t c = 0; c < nch; c++) {
+        const uint64_t n = e->chunks[c].n_hits;
+        if ((rc = hspz_find_hits(engine, c, e->rb_anchors, e->rb_cap_a, stream))) return rc;
+        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
+        if ((rc = hspz_score_gate(engine, e->rb_anchors, n, e->rb_flags, stream))) return rc;
+        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[1], s));
+        uint64_t ns = 0, na = 0;
+        if ((rc = hspz_compact(engine, e->rb_flags, n, e->rb_ids, e->rb_cap_a, &ns, stream)))
+            return rc;
+        if (time_gate) {  // the compaction synchronised the stream, so both events are done
+            float ms = 0.f;
+            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[0], e->gate_ev[1]));
+            stats->gate_ms += ms;
+            stats->gate_calls++;
+        }
+        if ((rc = ensure_run_buffers(e, maxn, ns))) return rc;
+        if ((rc = hspz_materialize(engine, e->rb_anchors, e->rb_ids, ns, e->rb_hsp,
+                                   e->rb_status, stream)))
+            return rc;
+        if ((rc = hspz_compact_hsps(engine, e->rb_hsp, e->rb_status, ns, e->rb_out, e->rb_cap_s,
+                                    &na, stream)))
+            return rc;
+        if (na) {
+            if ((rc = ensure_record_staging(e, acc + na, acc, s))) return rc;
+            HIP_TRY(e, hipMemcpyAsync(e->h_rec + acc, e->rb_out, na * sizeof(hspz_segment_pair),
+                                      hipMemcpyDeviceToHost, s));
+        }
+        stats->n_survivors += ns;
+        acc += na;
+    }
+    HIP_TRY(e, hipStreamSynchronize(s));
+    stats->n_accepted = acc;
+    e->h_rec_n = acc;
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_get_batch_records(const hspz_engine *engine, hspz_segment_pair *h_out,
+                                    uint64_t cap, uint64_t *n) {
+    Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
+    if (!e) return HSPZ_E_INVALID;
+    if (!n || (!h_out && cap)) return fail(e, HSPZ_E_INVALID, "NULL argument");
+    *n = e->h_rec_n;
+    if (!h_out) return HSPZ_OK;  // size query
+    const uint64_t k = std::min<uint64_t>(cap, e->h_rec_n);
+    if (k) memcpy(h_out, e->h_rec, k * sizeof(hspz_segment_pair));
+    if (cap < e->h_rec_n)
+        return fail(e, HSPZ_E_CAPACITY, "%llu records, room for %llu",
+                    (unsigned long long)e->h_rec_n, (unsigned long long)cap);
+    return HSPZ_OK;
 }
 
 HSPZ_API int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,

@@ -214,6 +214,18 @@ struct Engine {
     PlanBuf *d_plan = nullptr;     // device plan results
     PlanBuf *h_plan = nullptr;     // pinned copy
 
+    // whole-batch driver (hspz_run_batch): chunk buffers, record staging, gate events
+    uint64_t *rb_anchors = nullptr;
+    uint8_t *rb_flags = nullptr;
+    uint32_t *rb_ids = nullptr;
+    uint64_t rb_cap_a = 0;
+    hspz_segment_pair *rb_hsp = nullptr, *rb_out = nullptr;
+    uint8_t *rb_status = nullptr;
+    uint64_t rb_cap_s = 0;
+    hspz_segment_pair *h_rec = nullptr;  // pinned: accepted records of the last batch
+    uint64_t h_rec_cap = 0, h_rec_n = 0;
+    hipEvent_t gate_ev[2] = {nullptr, nullptr};
+
     ~Engine();
     void free_plan();
 };
