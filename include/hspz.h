@@ -132,7 +132,7 @@ const char *hspz_last_error(const hspz_engine *engine);
  * k-mer plus a leading 0, and the concatenated buckets of reference end coordinates,
  * ascending within a bucket; the buckets come from a stable radix sort of (k-mer, end)
  * pairs listed in position order).  h_ascii (len bytes, host) is not retained; bytes
- * other than A/C/G/T (either case) encode as N.  len < 2^32 - 257.  Temporary device
+ * other than A/C/G/T (either case) encode as N.  len < 2^32 - 513.  Temporary device
  * memory during the call: about len + 26 bytes per reference window plus 8 * 4^weight
  * bytes.  Replaces any previous reference and invalidates a plan.  Synchronises stream.
  * Errors: HSPZ_E_INVALID, HSPZ_E_NOMEM, HSPZ_E_HIP. */
@@ -275,10 +275,12 @@ int hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts, uint32_t
 int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64_t n,
                            void *stream, uint64_t *total_hits, uint32_t *n_chunks);
 
-/* Exact algorithmic work of the score gate over n anchors: the number of bases their
- * right and left X-drop walks score (each walk up to and including its first dropping
- * base, never past a sequence end), summed into *total_steps.  Allocates a small
- * temporary device buffer; synchronises stream.  Not part of a pass. */
+/* Exact algorithmic work of the score gate over n anchors, summed into *total_steps: the
+ * bases an exact decision of each flag scores.  The right walk runs up to and including
+ * its first dropping base, or until its best reaches T; the left walk, needed only when
+ * R* < T, runs up to its first dropping base or until R* + its best reaches T.  No walk
+ * scores a base past a sequence end.  Allocates a small temporary device buffer;
+ * synchronises stream.  Not part of a pass. */
 int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
                           uint64_t *total_steps, void *stream);
 

@@ -1,8 +1,10 @@
-// Diagnostics (not on the pass): the exact number of bases the right and left X-drop
-// walks of each anchor score, summed over a launch.  A walk scores bases until and
-// including the first one that drops more than xdrop below its best, and never a base
-// past a sequence end.  This is the algorithmic work of the score gate, used to price a
-// gate launch against the VALU roofline.
+// Diagnostics (not on the pass): the number of bases an exact decision of each anchor's
+// gate flag has to score, summed over a launch.  The right walk scores bases until and
+// including the first one that drops more than xdrop below its best, or until its best
+// reaches T (the flag is then 1 whatever follows); the left walk is needed only when
+// R* < T and stops the same way, at its drop or once R* + its best reaches T.  No walk
+// scores a base past a sequence end.  This is the algorithmic work of the score gate,
+// used to price a gate launch against the VALU roofline.
 #include "hspz_internal.h"
 #include "wave.h"
 
@@ -12,9 +14,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Bases scored by one walk in direction D; *best receives its best (the best so far when
+// it stops at stop).
 template <int D>
 __device__ __forceinline__ uint32_t walk_len(const int32_t *tab, const uint8_t *rp,
-                                             const uint8_t *qp, int32_t xdrop) {
+                                             const uint8_t *qp, int32_t xdrop, int32_t stop,
+                                             int32_t *best) {
     int32_t s = 0, b = 0;
     uint32_t k = 0;
     for (;;) {
@@ -23,9 +28,14 @@ __device__ __forceinline__ uint32_t walk_len(const int32_t *tab, const uint8_t *
         if (rb == (kCodeEdge << kRefShift) || qb == kCodeEdge) break;
         s += tab[rb | qb];
         k++;
-        if (s > b) b = s;
-        else if (b - s > xdrop) break;
+        if (s > b) {
+            b = s;
+            if (b >= stop) break;
+        } else if (b - s > xdrop) {
+            break;
+        }
     }
+    *best = b;
     return k;
 }
 
@@ -45,8 +55,9 @@ __global__ __launch_bounds__(kThreads) void k_walk_steps(const uint64_t *__restr
         const uint64_t a = anchors[i];
         const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
         if (r <= sp.n_ref && q <= sp.n_qry) {
-            steps = walk_len<+1>(tab, ref + r, qry + q, sp.xdrop) +
-                    walk_len<-1>(tab, ref + r, qry + q, sp.xdrop);
+            int32_t R = 0, L = 0;
+            steps = walk_len<+1>(tab, ref + r, qry + q, sp.xdrop, sp.T, &R);
+            if (R < sp.T) steps += walk_len<-1>(tab, ref + r, qry + q, sp.xdrop, sp.T - R, &L);
         }
     }
     const uint64_t tot = wave_incl_sum_u64(steps);
