@@ -132,7 +132,7 @@ const char *hspz_last_error(const hspz_engine *engine);
  * k-mer plus a leading 0, and the concatenated buckets of reference end coordinates,
  * ascending within a bucket; the buckets come from a stable radix sort of (k-mer, end)
  * pairs listed in position order).  h_ascii (len bytes, host) is not retained; bytes
- * other than A/C/G/T (either case) encode as N.  len < 2^32 - 513.  Temporary device
+ * other than A/C/G/T (either case) encode as N.  len < 2^32 - 1025.  Temporary device
  * memory during the call: about len + 26 bytes per reference window plus 8 * 4^weight
  * bytes.  Replaces any previous reference and invalidates a plan.  Synchronises stream.
  * Errors: HSPZ_E_INVALID, HSPZ_E_NOMEM, HSPZ_E_HIP. */

@@ -14,11 +14,11 @@ namespace hspz {
 
 // ---- device layout -----------------------------------------------------------------
 // Sequences live on the device one byte per base, padded on both sides with kPad
-// "edge" bytes (enough for a materializer tile of 256 bases and the one it reads ahead
+// "edge" bytes (enough for a materializer tile of 512 bases and the one it reads ahead
 // past a sequence end).  A reference byte holds code*8 and a query byte holds code, so
 // OR-ing a reference byte with a query byte gives the pair index ref*8 + query (0..45)
 // into the score table.  Codes: A,C,G,T = 0..3, N = 4, edge (outside the sequence) = 5.
-constexpr int kPad = 512;
+constexpr int kPad = 1024;
 constexpr uint8_t kCodeN = 4;
 constexpr uint8_t kCodeEdge = 5;
 constexpr int kRefShift = 3;

@@ -1,8 +1,9 @@
 // Exact X-drop materialization ("E. X-drop materialization", E.1-E.5).
 //
-// One wave per survivor walks both sides with exact_walk (64-base tiles, earliest
-// endpoints).  With the entropy-adjusted decision on, the wave then counts the record's
-// reference bases (entropy_accept).  Lane 0 stores the 16-byte record and the status.
+// One wave per survivor walks both sides with exact_walk_tiles (512-base tiles, eight
+// bases per lane, the next tile read ahead; earliest endpoints).  With the
+// entropy-adjusted decision on, the wave then counts the record's reference bases
+// (entropy_accept).  Lane 0 stores the 16-byte record and the status.
 #include <climits>
 
 #include "hspz_internal.h"
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
     uint32_t k, m;
     const uint8_t *rr = ref + (bad ? sp.n_ref : r), *qr = qry + (bad ? sp.n_qry : q);
     const uint8_t *rl = ref + (bad ? 0u : r), *ql = qry + (bad ? 0u : q);
-    exact_walk_tiles<+1, true, 4, true>(tab, rr, qr, sp.xdrop, INT32_MAX, R, k);
-    exact_walk_tiles<-1, true, 4, true>(tab, rl, ql, sp.xdrop, INT32_MAX, L, m);
+    exact_walk_tiles<+1, true, 8, true>(tab, rr, qr, sp.xdrop, INT32_MAX, R, k);
+    exact_walk_tiles<-1, true, 8, true>(tab, rl, ql, sp.xdrop, INT32_MAX, L, m);
     const int64_t total = (int64_t)L + (int64_t)R;
     bool ok = total >= (int64_t)sp.T;  // wave-uniform
     if (ok && sp.entropy_mode == 1) ok = entropy_accept(ref, r - m, m + k - 1u, total, sp.K);
