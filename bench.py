@@ -279,7 +279,7 @@ def main():
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
                       traffic=traffic,
-                      kernel="score_gate (two k_gate_window stages + k_gate_list_wave)",
+                      kernel="find_hits_gate (expansion fused into the first window stage, second stage, exact list)",
                       launches_per_step=gate_launches // args.steps,
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
                       base_steps_per_anchor=steps_per_anchor),

@@ -191,6 +191,18 @@ int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors, uin
 int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
                     uint8_t *d_flags, void *stream);
 
+/* hspz_find_hits and hspz_score_gate for chunk i in one call ("C. Hit discovery", C.5;
+ * "D. Score gate", D.1-D.3): the gate's first window stage builds each anchor from the
+ * chunk's seeds as it scores it, so the anchors are not written out and read back.
+ * d_flags receives the chunk's n_hits flags exactly as hspz_score_gate writes them;
+ * afterwards d_anchors (cap >= n_hits u64 entries) holds the anchor of every slot whose
+ * flag is 1, which is what hspz_materialize reads, and its other entries are
+ * unspecified.  When the window gate does not apply (gate_mode 1, or scores or xdrop
+ * outside its bounds) the call is hspz_find_hits followed by hspz_score_gate, and every
+ * entry is written.  Errors: as hspz_find_hits; HSPZ_E_INVALID for NULL buffers. */
+int hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors, uint64_t cap,
+                        uint8_t *d_flags, void *stream);
+
 /* Stable compaction of n flag bytes ("D. Score gate", D.4): d_ids receives, in
  * increasing order, the index of every non-zero byte.  *n_out receives their number;
  * if it exceeds cap (the capacity of d_ids, u32 entries) the call fails with
@@ -225,20 +237,21 @@ typedef struct {
     uint64_t n_chunks;     /* MAX_HITS chunks                                           */
     uint64_t n_survivors;  /* anchors the gate kept                                     */
     uint64_t n_accepted;   /* accepted records                                          */
-    uint64_t gate_calls;   /* score-gate calls timed (time_gate != 0), else 0          */
+    uint64_t gate_calls;   /* expansion-and-gate calls timed (time_gate != 0), else 0  */
     double gate_ms;        /* their summed durations from HIP events on the stream      */
 } hspz_batch_stats;
 
 /* The whole pass for query seeds [seed_lo, seed_hi) of the current strand, in one call:
- * hspz_plan, then for every chunk hspz_find_hits, hspz_score_gate, hspz_compact,
- * hspz_materialize and hspz_compact_hsps in the pages' order ("C. Hit discovery" to
- * "E. X-drop materialization"), with the same kernels and the same bytes.  The chunk
+ * hspz_plan, then for every chunk hspz_find_hits_gate, hspz_compact, hspz_materialize
+ * and hspz_compact_hsps in the pages' order ("C. Hit discovery" to
+ * "E. X-drop materialization"), with the same kernels and the same records.  The chunk
  * buffers are the engine's own (grown as needed); the accepted records of every chunk,
  * in chunk order, are copied to pinned host memory the engine owns, from where
- * hspz_get_batch_records reads them.  With time_gate != 0 each score-gate call is
- * bracketed by HIP events on stream and *stats reports their summed duration.  The plan
- * stays current afterwards.  Synchronises stream.  Errors: as hspz_plan, hspz_find_hits
- * and the calls above; HSPZ_E_INVALID for a NULL stats pointer. */
+ * hspz_get_batch_records reads them.  With time_gate != 0 each expansion-and-gate call
+ * (hspz_find_hits_gate) is bracketed by HIP events on stream and *stats reports their
+ * summed duration.  The plan stays current afterwards.  Synchronises stream.  Errors: as
+ * hspz_plan, hspz_find_hits and the calls above; HSPZ_E_INVALID for a NULL stats
+ * pointer. */
 int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, int32_t time_gate,
                    hspz_batch_stats *stats, void *stream);
 

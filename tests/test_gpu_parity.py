@@ -464,3 +464,65 @@ def test_run_batch_errors():
         eng.run_batch(0, eng.num_seeds() + 1)
     st = eng.run_batch(0, eng.num_seeds())
     assert st["n_accepted"] == eng.batch_records().size
+
+
+def _fused_vs_calls(eng, n_seeds):
+    """Every chunk through find_hits + score_gate and through find_hits_gate: identical
+    flags, and the fused call's anchors equal at every kept slot."""
+    import torch
+    tot, nch = eng.plan(0, n_seeds)
+    checked = 0
+    for c in range(nch):
+        n = eng.get_chunk(c)["n_hits"]
+        a1 = torch.empty(max(n, 1), dtype=torch.int64, device="cuda")
+        f1 = torch.empty(max(n, 1) + 16, dtype=torch.uint8, device="cuda")
+        a2 = torch.full((max(n, 1),), -1, dtype=torch.int64, device="cuda")
+        f2 = torch.full((max(n, 1) + 16,), 7, dtype=torch.uint8, device="cuda")
+        eng.find_hits(c, a1)
+        eng.score_gate(a1, n, f1)
+        eng.find_hits_gate(c, a2, f2)
+        g1 = f1[:n].cpu().numpy()
+        g2 = f2[:n].cpu().numpy()
+        assert np.array_equal(g1, g2), f"chunk {c}: flags differ"
+        keep = np.flatnonzero(g1)
+        assert np.array_equal(a1[:n].cpu().numpy()[keep], a2[:n].cpu().numpy()[keep])
+        checked += n
+    return tot, checked
+
+
+@pytest.mark.parametrize("gate_mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
+def test_find_hits_gate_matches_the_calls(case, gate_mode):
+    seed, nr, nq, pat, mx, nf, plant, ident, gc = case
+    ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
+                           identity=ident, gc=gc, alphabet_noise=True)
+    eng = engine(params_of(pat, max_hits=mx), gate_mode=gate_mode)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    tot, checked = _fused_vs_calls(eng, eng.num_seeds())
+    assert checked == tot
+
+
+def test_find_hits_gate_huge_bucket_and_sparse_seeds():
+    # one k-mer owning thousands of slots (a poly-A block on both sides), chunked so that
+    # chunks start and end inside its bucket's seeds; and a reference sharing almost no
+    # k-mers with the query, where most seeds own no slot
+    rng = np.random.default_rng(8)
+    bases = np.frombuffer(b"ACGT", np.uint8)
+    ref = np.concatenate([bases[rng.integers(0, 4, 20_000)], np.full(700, ord("A"), np.uint8),
+                          bases[rng.integers(0, 4, 20_000)]])
+    qry = np.concatenate([bases[rng.integers(0, 4, 9_000)], np.full(300, ord("A"), np.uint8),
+                          bases[rng.integers(0, 4, 9_000)]])
+    for mx in (0, 50_000, 3_000):
+        eng = engine(params_of(SEED_PATTERN, max_hits=mx))
+        eng.upload_reference(ref)
+        eng.upload_query(qry)
+        tot, checked = _fused_vs_calls(eng, eng.num_seeds())
+        assert checked == tot and tot > 100_000
+    ref2 = bases[rng.integers(0, 4, 60_000)]
+    qry2 = bases[rng.integers(0, 4, 60_000)]
+    eng = engine(params_of("11111111111", max_hits=7))
+    eng.upload_reference(ref2)
+    eng.upload_query(qry2)
+    tot, checked = _fused_vs_calls(eng, eng.num_seeds())
+    assert checked == tot

@@ -32,6 +32,7 @@ ABI_SYMBOLS = (
     "hspz_materialize", "hspz_compact_hsps", "hspz_get_seeds", "hspz_get_plan_arrays",
     "hspz_get_index", "hspz_debug_plan_counts", "hspz_debug_walk_steps",
     "hspz_debug_gate_deferred", "hspz_run_batch", "hspz_get_batch_records",
+    "hspz_find_hits_gate",
 )
 
 
@@ -90,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "hspz_run_batch": (ctypes.c_int, [P, U64, U64, ctypes.c_int32,
                                           ctypes.POINTER(BatchStats), P]),
         "hspz_get_batch_records": (ctypes.c_int, [P, P, U64, PU64]),
+        "hspz_find_hits_gate": (ctypes.c_int, [P, ctypes.c_uint32, P, U64, P, P]),
         "hspz_debug_plan_counts": (ctypes.c_int, [P, P, U64, P, PU64, PU32]),
         "hspz_debug_walk_steps": (ctypes.c_int, [P, P, U64, PU64, P]),
         "hspz_debug_gate_deferred": (ctypes.c_int, [P, PU64, PU64, P]),
@@ -230,6 +232,14 @@ class Engine:
         if cap is None:
             cap = _nbytes(anchors) // 8
         self._check(_lib.hspz_find_hits(self._h, chunk, _ptr(anchors), cap, _stream(stream)))
+
+    def find_hits_gate(self, chunk: int, anchors, flags, cap: Optional[int] = None,
+                       stream=None):
+        """find_hits + score_gate fused: all flags; anchors only where the flag is 1."""
+        if cap is None:
+            cap = _nbytes(anchors) // 8
+        self._check(_lib.hspz_find_hits_gate(self._h, chunk, _ptr(anchors), cap, _ptr(flags),
+                                             _stream(stream)))
 
     def score_gate(self, anchors, n: int, flags, stream=None):
         self._check(_lib.hspz_score_gate(self._h, _ptr(anchors), n, _ptr(flags),

@@ -322,6 +322,7 @@ Engine::~Engine() {
     dfree(d_cblk);
     dfree(d_ctotal);
     dfree(d_plan);
+    dfree(d_dir);
     dfree(rb_anchors);
     dfree(rb_flags);
     dfree(rb_ids);
@@ -743,6 +744,19 @@ HSPZ_API int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anc
     return HSPZ_OK;
 }
 
+// The window gate's deferred lists (two of them) can each hold every anchor of a call.
+static int ensure_defer(Engine *e, uint64_t n) {
+    if (n <= e->cap_defer && e->d_defer) return HSPZ_OK;
+    const uint64_t cap = std::max<uint64_t>(n + n / 4, 1u << 16);
+    int rc = dalloc(e, e->d_defer, 2 * cap);
+    if (rc) {
+        e->cap_defer = 0;
+        return rc;
+    }
+    e->cap_defer = cap;
+    return HSPZ_OK;
+}
+
 HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
                              uint8_t *d_flags, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
@@ -761,18 +775,60 @@ HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uin
                                e->d_qry + kPad, e->sp, s));
         return HSPZ_OK;
     }
-    if (n > e->cap_defer || !e->d_defer) {
-        // the deferred list can hold every anchor; grow with headroom
-        const uint64_t cap = std::max<uint64_t>(n + n / 4, 1u << 16);
-        if ((rc = dalloc(e, e->d_defer, 2 * cap))) {
-            e->cap_defer = 0;
-            return rc;
-        }
-        e->cap_defer = cap;
-    }
+    if ((rc = ensure_defer(e, n))) return rc;
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
     HIP_TRY(e, launch_gate_window(e->params.gate_mode == 3, d_anchors, (uint32_t)n, d_flags,
                                   e->d_ref4, e->d_qry4, e->wp, list1, list2, e->d_defer_cnt, s));
+    HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
+                                     e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
+    e->gate_deferred_valid = true;
+    return HSPZ_OK;
+}
+
+HSPZ_API int hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
+                                 uint64_t cap, uint8_t *d_flags, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_plan || !e->plan_expandable)
+        return fail(e, HSPZ_E_STATE, "find_hits_gate needs a plan from hspz_plan");
+    if (chunk >= e->chunks.size()) return fail(e, HSPZ_E_INVALID, "chunk %u out of range", chunk);
+    const hspz_chunk c = e->chunks[chunk];
+    if (cap < c.n_hits)
+        return fail(e, HSPZ_E_CAPACITY, "anchor buffer holds %llu, chunk needs %llu",
+                    (unsigned long long)cap, (unsigned long long)c.n_hits);
+    if (c.n_hits && (!d_anchors || !d_flags)) return fail(e, HSPZ_E_INVALID, "NULL buffer");
+    if (!(e->window_ok && e->params.gate_mode != 1)) {  // the exact gate reads every anchor
+        int rc = hspz_find_hits(engine, chunk, d_anchors, cap, stream);
+        return rc ? rc : hspz_score_gate(engine, d_anchors, c.n_hits, d_flags, stream);
+    }
+    int rc = set_device(e);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    e->gate_deferred_valid = false;
+    const uint64_t n = c.n_hits;
+    if ((rc = ensure_defer(e, n))) return rc;
+    const uint64_t n_waves = (n + gate_window_wave_slots() - 1) / gate_window_wave_slots();
+    if (n_waves > e->cap_dir || !e->d_dir) {
+        const uint64_t want = std::max<uint64_t>({n_waves, 1024, e->cap_dir + e->cap_dir / 4});
+        if ((rc = dalloc(e, e->d_dir, want))) {
+            e->cap_dir = 0;
+            return rc;
+        }
+        e->cap_dir = want;
+    }
+    const uint64_t local = c.seed_lo - e->batch_lo;
+    ChunkSeeds cs;
+    cs.prefix = e->d_prefix + local;
+    cs.first = e->d_first + local;
+    cs.q_end = e->d_qend + c.seed_lo;
+    cs.pos = e->d_pos;
+    cs.dir = e->d_dir;
+    cs.n_seeds = (uint32_t)(c.seed_hi - c.seed_lo + 1);
+    cs.hit_lo = (uint32_t)c.hit_lo;
+    uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
+    HIP_TRY(e, launch_gate_window_fused(e->params.gate_mode == 3, cs, (uint32_t)n, d_anchors,
+                                        d_flags, e->d_ref4, e->d_qry4, e->wp, list1, list2,
+                                        e->d_defer_cnt, s));
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
@@ -910,9 +966,10 @@ HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed
     uint64_t acc = 0;
     for (uint32_t c = 0; c < nch; c++) {
         const uint64_t n = e->chunks[c].n_hits;
-        if ((rc = hspz_find_hits(engine, c, e->rb_anchors, e->rb_cap_a, stream))) return rc;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
-        if ((rc = hspz_score_gate(engine, e->rb_anchors, n, e->rb_flags, stream))) return rc;
+        if ((rc = hspz_find_hits_gate(engine, c, e->rb_anchors, e->rb_cap_a, e->rb_flags,
+                                      stream)))
+            return rc;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[1], s));
         uint64_t ns = 0, na = 0;
         if ((rc = hspz_compact(engine, e->rb_flags, n, e->rb_ids, e->rb_cap_a, &ns, stream)))

@@ -136,6 +136,31 @@ hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uin
 hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
                               const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
                               uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s);
+// The seeds of one chunk, for the first gate stage fused with the expansion: their
+// inclusive prefix (batch numbering, so prefix - hit_lo runs from 0 to the chunk's hits),
+// bucket starts and query ends, the index bucket array, and the directory of the seed
+// that owns the first slot of each wave's range (filled by the launcher).
+struct ChunkSeeds {
+    const uint32_t *prefix;
+    const uint32_t *first;
+    const uint32_t *q_end;
+    const uint32_t *pos;
+    uint32_t *dir;
+    uint32_t n_seeds;
+    uint32_t hit_lo;
+};
+// Slots per wave of the first window stage (and so entries of the directory per slot).
+uint32_t gate_window_wave_slots();
+// As launch_gate_window, but the first stage builds each anchor from the chunk's seeds
+// (occurrence j of seed s at slot prefix[s] - 1 - hit_lo - j, "C. Hit discovery", C.5)
+// instead of reading it: anchors[i] is written only where the first stage does not
+// decide flag 0 (the later stages and the materializer read exactly those).
+// cs.dir holds ceil(n / gate_window_wave_slots()) entries.
+hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t n,
+                                    uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
+                                    const uint32_t *qry4, const WindowParams &wp,
+                                    uint32_t *list1, uint32_t *list2, uint32_t *cnt,
+                                    hipStream_t s);
 hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
                                  const uint32_t *count, uint32_t max_count, uint8_t *flags,
                                  const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
@@ -213,6 +238,8 @@ struct Engine {
     uint64_t cap_cblk = 0;
     uint32_t *h_pinned = nullptr;  // small pinned staging buffer (64 u32)
     PlanBuf *d_plan = nullptr;     // device plan results
+    uint32_t *d_dir = nullptr;     // fused first stage: owner seed of each wave's range
+    uint64_t cap_dir = 0;
     PlanBuf *h_plan = nullptr;     // pinned copy
 
     // whole-batch driver (hspz_run_batch): chunk buffers, record staging, gate events

@@ -459,6 +459,89 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
     defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
 }
 
+// Directory of the fused first stage: the seed that owns the first slot of each wave's
+// range, i.e. the first seed whose prefix - hit_lo exceeds that slot (a binary search).
+__global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n_waves) {
+    const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
+    if (w >= n_waves) return;
+    const uint32_t t = w * (64u * kSteps);
+    uint32_t lo = 0, hi = cs.n_seeds;
+    while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (cs.prefix[mid] - cs.hit_lo > t) hi = mid;
+        else lo = mid + 1;
+    }
+    cs.dir[w] = lo;
+}
+
+// First stage fused with the backward expansion ("C. Hit discovery", C.5): a wave walks
+// the same 64-slot steps as k_gate_window, but builds each slot's anchor from the seed
+// that owns it.  Per step the lanes load the prefixes of 64 consecutive seeds (from the
+// owner of the previous step's last slot) into LDS and binary-search them for their
+// slot; seeds with no hits make the wave load further windows until every slot has its
+// owner.  Occurrence j = prefix[s] - 1 - hit_lo - slot of seed s is the bucket entry
+// pos[first[s] + j].  The anchor is stored only when the slot is deferred or kept.
+template <int RB, int LB>
+__global__ __launch_bounds__(kThreads) void k_gate_window_fused(
+    ChunkSeeds cs, uint32_t n, uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
+    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
+    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    __shared__ int16_t tab[kWinTab];
+    __shared__ uint32_t seg[kWaves][kSeg];
+    __shared__ uint32_t seg_n[kWaves];
+    __shared__ uint32_t blk_base;
+    __shared__ uint32_t rel[kWaves][64];  // prefix - hit_lo of 64 consecutive seeds
+    if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    __syncthreads();
+
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t nseg = 0;
+    const uint64_t wave = (uint64_t)blockIdx.x * kWaves + w;
+    const uint64_t first = wave * (64 * kSteps);
+    uint32_t cb = first < n ? cs.dir[wave] : 0u;  // owner of the step's first slot
+    for (int step = 0; step < kSteps; step++) {
+        const uint64_t i0 = first + (uint64_t)step * 64;
+        if (i0 >= n) break;  // uniform
+        const uint32_t t = (uint32_t)(i0 + lane);
+        const bool valid = t < n;
+        uint32_t owner = 0, top = 0;  // top = prefix[owner] - hit_lo
+        bool found = !valid;
+        for (uint32_t base = cb;; base += 64) {  // uniform: ends once every slot has its owner
+            const uint32_t sj = base + lane;
+            rel[w][lane] = sj < cs.n_seeds ? cs.prefix[sj] - cs.hit_lo : 0xFFFFFFFFu;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (!found && t < rel[w][63]) {
+                int L = 0;  // number of the 64 seeds whose prefix - hit_lo is <= t
+#pragma unroll
+                for (int k = 32; k >= 1; k >>= 1)
+                    if (rel[w][L + k - 1] <= t) L += k;
+                owner = base + (uint32_t)L;
+                top = rel[w][L];
+                found = true;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (__ballot(!found) == 0) break;
+        }
+        const int last = (int)min<uint64_t>(63, (uint64_t)n - 1 - i0);
+        cb = (uint32_t)lane_value((int32_t)owner, last);
+        uint64_t a = 0;
+        if (valid) {
+            const uint32_t j = top - 1u - t;
+            a = (uint64_t)cs.pos[cs.first[owner] + j] | ((uint64_t)cs.q_end[owner] << 32);
+        }
+        Win<RB, LB, false> win;
+        win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
+        const int res = win.decide(tab, wp);
+        if (valid && res != 2) flags[t] = (uint8_t)res;
+        if (valid && res != 0) anchors[t] = a;
+        defer_push(seg[w], nseg, valid && res == 2, t, defer, defer_cnt);
+    }
+    defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
+}
+
 // Later stage: the anchors listed by the previous stage (*count of them), wider windows.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_list(
@@ -546,6 +629,18 @@ hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
     return hipGetLastError();
 }
 
+// The second stage strides over whatever the first left, up to all n anchors.
+static void launch_stage2(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
+                          const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
+                          uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
+    const uint32_t cap2 = narrow ? n : n / 8 + 1;
+    const uint32_t blocks2 =
+        (uint32_t)std::min<uint64_t>(((uint64_t)cap2 + kWaves * 64 - 1) / (kWaves * 64), 4096);
+    hipLaunchKernelGGL((k_gate_window_list<kStage2Right, kStage2Left>), dim3(blocks2),
+                       dim3(kThreads), 0, s, anchors, list1, cnt, flags, ref4, qry4, wp, list2,
+                       cnt + 1);
+}
+
 hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
                               const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
                               uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
@@ -559,13 +654,32 @@ hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, 
     else
         hipLaunchKernelGGL((k_gate_window<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads),
                            0, s, anchors, n, flags, ref4, qry4, wp, list1, cnt);
-    // the second stage strides over whatever the first left, up to all n anchors
-    const uint32_t cap2 = narrow ? n : n / 8 + 1;
-    const uint32_t blocks2 =
-        (uint32_t)std::min<uint64_t>(((uint64_t)cap2 + kWaves * 64 - 1) / (kWaves * 64), 4096);
-    hipLaunchKernelGGL((k_gate_window_list<kStage2Right, kStage2Left>), dim3(blocks2),
-                       dim3(kThreads), 0, s, anchors, list1, cnt, flags, ref4, qry4, wp, list2,
-                       cnt + 1);
+    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
+    return hipGetLastError();
+}
+
+uint32_t gate_window_wave_slots() { return 64u * kSteps; }
+
+hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t n,
+                                    uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
+                                    const uint32_t *qry4, const WindowParams &wp,
+                                    uint32_t *list1, uint32_t *list2, uint32_t *cnt,
+                                    hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+    if (n == 0) return hipGetLastError();
+    const uint32_t n_waves = (uint32_t)(((uint64_t)n + 64 * kSteps - 1) / (64 * kSteps));
+    hipLaunchKernelGGL(k_slot_dir, dim3((n_waves + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       s, cs, n_waves);
+    const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
+    if (narrow)
+        hipLaunchKernelGGL((k_gate_window_fused<kNarrowRight, kNarrowLeft>), dim3(blocks),
+                           dim3(kThreads), 0, s, cs, n, anchors, flags, ref4, qry4, wp, list1,
+                           cnt);
+    else
+        hipLaunchKernelGGL((k_gate_window_fused<kWideRight, kWideLeft>), dim3(blocks),
+                           dim3(kThreads), 0, s, cs, n, anchors, flags, ref4, qry4, wp, list1,
+                           cnt);
+    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
     return hipGetLastError();
 }
 
