@@ -41,7 +41,11 @@ CUS, LANES, CLOCK_GHZ = 256, 64, 2.4
 # second follows from the lane count.
 OPS_PER_BASE_STEP = 3
 ALU_PEAK_GSTEPS = CUS * LANES * CLOCK_GHZ / OPS_PER_BASE_STEP   # G base steps/s
-GATE_BYTES_PER_ANCHOR = 9       # 8-byte packed anchor read + 1-byte flag write
+# Compulsory bytes of one hspz_find_hits_gate call (expansion fused into the gate): per
+# anchor its 4-byte bucket entry read and its 1-byte flag written; per seed its 4-byte
+# inclusive prefix, bucket start and query end read.
+GATE_BYTES_PER_ANCHOR = 5
+GATE_BYTES_PER_SEED = 12
 
 
 def parse():
@@ -83,14 +87,14 @@ def gather_ceiling(torch) -> float:
 
 
 def gate_traffic(workload: str, gate_mode: int):
-    """Measured fabric bytes per score-gate call from the committed counter summary.
+    """Measured fabric bytes per hspz_find_hits_gate call from the committed counter summary.
 
     The summary was taken with rocprofv3 FETCH_SIZE / WRITE_SIZE runs and calibrated
     against a plain device copy.  It applies only to the source it was measured on and to
     the same workload; otherwise None.
     """
     import hashlib
-    path = os.path.join(ROOT, "profiles", "score_gate_traffic_c3_50Mb.json")
+    path = os.path.join(ROOT, "profiles", "find_hits_gate_traffic_c3_50Mb.json")
     src = os.path.join(ROOT, "ungapped_drop_hsp_amd", "csrc", "k_gate.hip")
     try:
         rec = json.load(open(path))
@@ -232,7 +236,9 @@ def main():
     gate_launches = gate_calls
     gate_ms_avg = gate_ms_sum / gate_launches
     units_avg = gate_anchors / gate_launches
-    gate_gbs = GATE_BYTES_PER_ANCHOR * units_avg / (gate_ms_avg * 1e6)
+    gate_bytes_avg = (GATE_BYTES_PER_ANCHOR * gate_anchors
+                      + GATE_BYTES_PER_SEED * seeds * args.steps) / gate_launches
+    gate_gbs = gate_bytes_avg / (gate_ms_avg * 1e6)
     # base steps per anchor and the gate's stage split, over the last strand's batches
     steps_total = walked = 0
     deferred = [0, 0]
@@ -284,7 +290,8 @@ def main():
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
                       base_steps_per_anchor=steps_per_anchor),
         gate_hbm=dict(achieved=gate_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=gate_gbs / HBM_PEAK_GBS, bytes_per_anchor=GATE_BYTES_PER_ANCHOR),
+                      frac=gate_gbs / HBM_PEAK_GBS, bytes_per_anchor=GATE_BYTES_PER_ANCHOR,
+                      bytes_per_seed=GATE_BYTES_PER_SEED, bytes_per_launch=gate_bytes_avg),
         gate_anchors_per_s=units_avg / (gate_ms_avg / 1000.0),
         # the gate's measured fabric traffic in 128-byte lines/s against the random-line
         # rate of a plain gather kernel, measured in this run
