@@ -9,7 +9,9 @@ so each batch is checked like this:
   - flags on a random sample of anchors plus every anchor the GPU kept;
   - survivor ids against the flag bytes;
   - records and status of sampled survivors, recomputed one by one by the oracle;
-  - the accepted records as the stable selection of the records.
+  - the accepted records as the stable selection of the records;
+  - the whole batch through hspz_run_batch (the timed path) against the per-call pass over
+    every chunk: survivor and accepted counts, and every accepted record byte.
 """
 import numpy as np
 import pytest
@@ -96,7 +98,7 @@ def _check_batch(eng, bufs, R, qc, seeds, p, lo, hi, chunk_pick, rng, full_plan=
 
 
 def _run_config(cfg, chunk_pick, batch_pick=None, full_plan=True):
-    from ungapped_drop_hsp_amd.pipeline import PassBuffers, batches
+    from ungapped_drop_hsp_amd.pipeline import PassBuffers, batches, run_pass
     w = build(cfg)
     p = w.params()
     R = oracle.Reference(w.ref, p["seed_pattern"])
@@ -131,6 +133,17 @@ def _run_config(cfg, chunk_pick, batch_pick=None, full_plan=True):
                 continue
             st = _check_batch(eng, bufs, R, qc, seeds, p, lo, hi, chunk_pick, rng,
                               full_plan=full_plan)
+            # the native whole-batch driver, as bench.py times it (expansion fused into the
+            # gate, each chunk queued one ahead of the previous one's materialization),
+            # against the per-call pass over every chunk of the batch
+            o = run_pass(eng, lo, hi, bufs)
+            want = [c["accepted"].view(np.uint8).reshape(-1) for c in o["chunks"]]
+            sb = eng.run_batch(lo, hi)
+            assert (sb["n_chunks"], sb["n_survivors"], sb["n_accepted"]) == \
+                (o["n_chunks"], o["n_surv"], o["n_acc"]), "run_batch counts differ"
+            got = eng.batch_records().view(np.uint8).reshape(-1)
+            assert np.array_equal(got, np.concatenate(want) if want else got[:0]), \
+                "run_batch records differ"
             print(f"{w.name} strand {strand} batch {bi}: {st}", flush=True)
             out.append(st)
     return out

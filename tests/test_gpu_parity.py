@@ -451,6 +451,35 @@ def test_run_batch_reverse_strand_and_entropy():
                               acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 
 
+def test_run_batch_survivors_grow_mid_batch():
+    # run_batch queues chunk c + 1's gate and survivor compaction before it reads chunk
+    # c's counts.  Here the early chunks keep nothing and the last ones keep thousands of
+    # anchors (the query ends with copies of reference stretches), so the survivor buffers
+    # grow between chunks; the chunks are of uneven size.  Run twice on one engine: the
+    # second call starts with grown buffers.
+    rng = np.random.default_rng(21)
+    acgt = np.frombuffer(b"ACGT", np.uint8)
+    ref = acgt[rng.integers(0, 4, 24_000)].copy()
+    qry = np.concatenate([acgt[rng.integers(0, 4, 18_000)], ref[2_000:7_000],
+                          acgt[rng.integers(0, 4, 3_000)], ref[15_000:16_500]])
+    # a weight-6 seed fills the first chunks with random anchors that all fail the gate
+    p = params_of("11101101", max_hits=20_000)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    o, _, _ = oracle_pass(ref, qry, p)
+    want, acc = _oracle_batch(o)
+    kept = [int(c["ids"].size) for c in o["chunks"]]
+    assert want["n_chunks"] > 5 and kept[0] == 0 and max(kept) > 2_048
+    assert len({c["chunk"]["n_hits"] for c in o["chunks"]}) > 1
+    for _ in range(2):
+        st = eng.run_batch(0, eng.num_seeds(), time_gate=True)
+        assert {k: st[k] for k in want} == want
+        assert st["gate_calls"] == st["n_chunks"]
+        assert np.array_equal(eng.batch_records().view(np.uint8),
+                              acc.astype(oracle.HSP_DTYPE).view(np.uint8))
+
+
 def test_run_batch_errors():
     p = params_of(SEED_PATTERN)
     eng = engine(p)

@@ -323,13 +323,17 @@ Engine::~Engine() {
     dfree(d_ctotal);
     dfree(d_plan);
     dfree(d_dir);
-    dfree(rb_anchors);
-    dfree(rb_flags);
-    dfree(rb_ids);
+    for (int b = 0; b < 2; b++) {
+        dfree(rb_anchors[b]);
+        dfree(rb_flags[b]);
+        dfree(rb_ids[b]);
+    }
     dfree(rb_hsp);
     dfree(rb_out);
     dfree(rb_status);
     for (hipEvent_t ev : gate_ev)
+        if (ev) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : count_ev)
         if (ev) (void)hipEventDestroy(ev);
     if (h_pinned) (void)hipHostFree(h_pinned);
     if (h_plan) (void)hipHostFree(h_plan);
@@ -757,6 +761,20 @@ static int ensure_defer(Engine *e, uint64_t n) {
     return HSPZ_OK;
 }
 
+// The fused first stage's per-wave owner directory for a chunk of n anchors.
+static int ensure_dir(Engine *e, uint64_t n) {
+    const uint64_t n_waves = (n + gate_window_wave_slots() - 1) / gate_window_wave_slots();
+    if (n_waves <= e->cap_dir && e->d_dir) return HSPZ_OK;
+    const uint64_t want = std::max<uint64_t>({n_waves, 1024, e->cap_dir + e->cap_dir / 4});
+    int rc = dalloc(e, e->d_dir, want);
+    if (rc) {
+        e->cap_dir = 0;
+        return rc;
+    }
+    e->cap_dir = want;
+    return HSPZ_OK;
+}
+
 HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
                              uint8_t *d_flags, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
@@ -807,15 +825,7 @@ HSPZ_API int hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *
     e->gate_deferred_valid = false;
     const uint64_t n = c.n_hits;
     if ((rc = ensure_defer(e, n))) return rc;
-    const uint64_t n_waves = (n + gate_window_wave_slots() - 1) / gate_window_wave_slots();
-    if (n_waves > e->cap_dir || !e->d_dir) {
-        const uint64_t want = std::max<uint64_t>({n_waves, 1024, e->cap_dir + e->cap_dir / 4});
-        if ((rc = dalloc(e, e->d_dir, want))) {
-            e->cap_dir = 0;
-            return rc;
-        }
-        e->cap_dir = want;
-    }
+    if ((rc = ensure_dir(e, n))) return rc;
     const uint64_t local = c.seed_lo - e->batch_lo;
     ChunkSeeds cs;
     cs.prefix = e->d_prefix + local;
@@ -900,16 +910,18 @@ HSPZ_API int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_h
     return rc;
 }
 
-// Grow the whole-batch chunk buffers to n anchors and s survivors (a quarter of headroom).
+// Grow both sets of whole-batch chunk buffers to n anchors, and the survivor buffers to s
+// survivors (a quarter of headroom).
 static int ensure_run_buffers(Engine *e, uint64_t n, uint64_t ns) {
     int rc;
-    if (n > e->rb_cap_a || !e->rb_anchors) {
+    if (n > e->rb_cap_a || !e->rb_anchors[0]) {
         const uint64_t cap = std::max<uint64_t>({n, 1024, e->rb_cap_a + e->rb_cap_a / 4});
-        if ((rc = dalloc(e, e->rb_anchors, cap)) || (rc = dalloc(e, e->rb_flags, cap + 16)) ||
-            (rc = dalloc(e, e->rb_ids, cap))) {
-            e->rb_cap_a = 0;
-            return rc;
-        }
+        for (int b = 0; b < 2; b++)
+            if ((rc = dalloc(e, e->rb_anchors[b], cap)) ||
+                (rc = dalloc(e, e->rb_flags[b], cap + 16)) || (rc = dalloc(e, e->rb_ids[b], cap))) {
+                e->rb_cap_a = 0;
+                return rc;
+            }
         e->rb_cap_a = cap;
     }
     if (ns > e->rb_cap_s || !e->rb_hsp) {
@@ -943,6 +955,33 @@ static int ensure_record_staging(Engine *e, uint64_t n, uint64_t keep, hipStream
     return HSPZ_OK;
 }
 
+// Queue a compaction whose count lands in pinned slot `slot` (0: survivors, 1: records),
+// with count_ev[slot] recorded behind the copy; count_wait() reads it back.
+static int count_queue(Engine *e, const uint8_t *flags, uint64_t n, uint32_t *ids,
+                       const hspz_segment_pair *rin, hspz_segment_pair *rout, uint64_t cap,
+                       int slot, hipStream_t s) {
+    if (n >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n must be < 2^32");
+    if ((n + kCompactBlock - 1) / kCompactBlock + 1 > e->cap_cblk)
+        return fail(e, HSPZ_E_INVALID, "compaction scratch not sized for %llu", (unsigned long long)n);
+    uint32_t *d_total = e->d_ctotal + 4 * (slot + 1);
+    uint32_t *h_total = e->h_pinned + 16 + 4 * slot;
+    const uint32_t c32 = (uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull);
+    HIP_TRY(e, launch_compact(flags, (uint32_t)n, e->d_cblk, d_total, ids, rin, rout, c32, s));
+    HIP_TRY(e, hipMemcpyAsync(h_total, d_total, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(e, hipEventRecord(e->count_ev[slot], s));
+    return HSPZ_OK;
+}
+
+static int count_wait(Engine *e, int slot, uint64_t cap, uint64_t *n_out) {
+    HIP_TRY(e, hipEventSynchronize(e->count_ev[slot]));
+    const uint64_t total = e->h_pinned[16 + 4 * slot];
+    if (total > cap)
+        return fail(e, HSPZ_E_CAPACITY, "%llu selected, capacity %llu", (unsigned long long)total,
+                    (unsigned long long)cap);
+    *n_out = total;
+    return HSPZ_OK;
+}
+
 HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi,
                             int32_t time_gate, hspz_batch_stats *stats, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
@@ -959,34 +998,60 @@ HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed
     stats->n_chunks = nch;
     uint64_t maxn = 0;
     for (const hspz_chunk &c : e->chunks) maxn = std::max<uint64_t>(maxn, c.n_hits);
-    if ((rc = ensure_run_buffers(e, maxn, 0))) return rc;
+    // Scratch that queued work may still be using is never regrown inside the loop: size
+    // the gate's lists and directory and the compaction blocks for the largest chunk now.
+    if ((rc = ensure_run_buffers(e, maxn, 0)) || (rc = ensure_defer(e, maxn)) ||
+        (rc = ensure_dir(e, maxn)) || (rc = ensure_compact(e, maxn)))
+        return rc;
+    for (hipEvent_t &ev : e->count_ev)
+        if (!ev) HIP_TRY(e, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
     if (time_gate)
         for (hipEvent_t &ev : e->gate_ev)
             if (!ev) HIP_TRY(e, hipEventCreate(&ev));
+
+    // One stream, queued one chunk ahead: chunk c + 1's expansion+gate and survivor
+    // compaction are queued before the host waits on chunk c's counts, so the GPU has work
+    // while the host reads them.  Chunk c uses buffer set c & 1; stream order keeps every
+    // read of a set ahead of the next write to it.
+    auto gate = [&](uint32_t c) -> int {
+        const int b = c & 1;
+        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[2 * b], s));
+        int r = hspz_find_hits_gate(engine, c, e->rb_anchors[b], e->rb_cap_a, e->rb_flags[b],
+                                    stream);
+        if (r) return r;
+        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[2 * b + 1], s));
+        return HSPZ_OK;
+    };
+    auto survivors = [&](uint32_t c) -> int {
+        const int b = c & 1;
+        return count_queue(e, e->rb_flags[b], e->chunks[c].n_hits, e->rb_ids[b], nullptr,
+                           nullptr, e->rb_cap_a, 0, s);
+    };
+    if (nch && ((rc = gate(0)) || (rc = survivors(0)))) return rc;
     uint64_t acc = 0;
     for (uint32_t c = 0; c < nch; c++) {
-        const uint64_t n = e->chunks[c].n_hits;
-        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
-        if ((rc = hspz_find_hits_gate(engine, c, e->rb_anchors, e->rb_cap_a, e->rb_flags,
-                                      stream)))
-            return rc;
-        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[1], s));
+        const int b = c & 1;
+        if (c + 1 < nch && (rc = gate(c + 1))) return rc;
         uint64_t ns = 0, na = 0;
-        if ((rc = hspz_compact(engine, e->rb_flags, n, e->rb_ids, e->rb_cap_a, &ns, stream)))
-            return rc;
-        if (time_gate) {  // the compaction synchronised the stream, so both events are done
+        if ((rc = count_wait(e, 0, e->rb_cap_a, &ns))) return rc;
+        if (time_gate) {  // the survivor count lands after the chunk's gate events
             float ms = 0.f;
-            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[0], e->gate_ev[1]));
+            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[2 * b], e->gate_ev[2 * b + 1]));
             stats->gate_ms += ms;
             stats->gate_calls++;
         }
-        if ((rc = ensure_run_buffers(e, maxn, ns))) return rc;
-        if ((rc = hspz_materialize(engine, e->rb_anchors, e->rb_ids, ns, e->rb_hsp,
+        if (ns > e->rb_cap_s) {  // the survivor buffers grow only once the stream is idle
+            HIP_TRY(e, hipStreamSynchronize(s));
+            if ((rc = ensure_run_buffers(e, maxn, ns))) return rc;
+        }
+        if ((rc = hspz_materialize(engine, e->rb_anchors[b], e->rb_ids[b], ns, e->rb_hsp,
                                    e->rb_status, stream)))
             return rc;
-        if ((rc = hspz_compact_hsps(engine, e->rb_hsp, e->rb_status, ns, e->rb_out, e->rb_cap_s,
-                                    &na, stream)))
+        if ((rc = count_queue(e, e->rb_status, ns, nullptr, e->rb_hsp, e->rb_out, e->rb_cap_s, 1,
+                              s)))
             return rc;
+        if (c + 1 < nch && (rc = survivors(c + 1))) return rc;
+        if ((rc = count_wait(e, 1, e->rb_cap_s, &na))) return rc;
         if (na) {
             if ((rc = ensure_record_staging(e, acc + na, acc, s))) return rc;
             HIP_TRY(e, hipMemcpyAsync(e->h_rec + acc, e->rb_out, na * sizeof(hspz_segment_pair),

@@ -242,17 +242,20 @@ struct Engine {
     uint64_t cap_dir = 0;
     PlanBuf *h_plan = nullptr;     // pinned copy
 
-    // whole-batch driver (hspz_run_batch): chunk buffers, record staging, gate events
-    uint64_t *rb_anchors = nullptr;
-    uint8_t *rb_flags = nullptr;
-    uint32_t *rb_ids = nullptr;
+    // whole-batch driver (hspz_run_batch): two sets of chunk buffers (chunk c uses set
+    // c & 1, so the next chunk's gate can be queued before this chunk's materialization),
+    // survivor buffers, record staging, and a pair of gate events per set
+    uint64_t *rb_anchors[2] = {nullptr, nullptr};
+    uint8_t *rb_flags[2] = {nullptr, nullptr};
+    uint32_t *rb_ids[2] = {nullptr, nullptr};
     uint64_t rb_cap_a = 0;
     hspz_segment_pair *rb_hsp = nullptr, *rb_out = nullptr;
     uint8_t *rb_status = nullptr;
     uint64_t rb_cap_s = 0;
     hspz_segment_pair *h_rec = nullptr;  // pinned: accepted records of the last batch
     uint64_t h_rec_cap = 0, h_rec_n = 0;
-    hipEvent_t gate_ev[2] = {nullptr, nullptr};
+    hipEvent_t gate_ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t count_ev[2] = {nullptr, nullptr};  // survivor and record counts landed
 
     ~Engine();
     void free_plan();
