@@ -476,11 +476,12 @@ __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n
 
 // First stage fused with the backward expansion ("C. Hit discovery", C.5): a wave walks
 // the same 64-slot steps as k_gate_window, but builds each slot's anchor from the seed
-// that owns it.  Per step the lanes load the prefixes of 64 consecutive seeds (from the
-// owner of the previous step's last slot) into LDS and binary-search them for their
-// slot; seeds with no hits make the wave load further windows until every slot has its
-// owner.  Occurrence j = prefix[s] - 1 - hit_lo - slot of seed s is the bucket entry
-// pos[first[s] + j].  The anchor is stored only when the slot is deferred or kept.
+// that owns it.  The wave keeps a window of 64 consecutive seeds in LDS (prefix - hit_lo,
+// bucket start and query end, read once, coalesced), starting at the owner of its first
+// slot; lanes binary-search it for their slot, and the window slides on by 64 seeds when
+// a slot lies past it (seeds with no hits can take several slides).  Occurrence
+// j = prefix[s] - 1 - hit_lo - slot of seed s is the bucket entry pos[first[s] + j].  The
+// anchor is stored only when the slot is deferred or kept.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     ChunkSeeds cs, uint32_t n, uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
@@ -490,7 +491,9 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     __shared__ uint32_t seg[kWaves][kSeg];
     __shared__ uint32_t seg_n[kWaves];
     __shared__ uint32_t blk_base;
-    __shared__ uint32_t rel[kWaves][64];  // prefix - hit_lo of 64 consecutive seeds
+    __shared__ uint32_t rel[kWaves][64];  // prefix - hit_lo of the window's seeds
+    __shared__ uint32_t fst[kWaves][64];  // their bucket starts
+    __shared__ uint32_t qen[kWaves][64];  // their query ends
     if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
     __syncthreads();
 
@@ -499,39 +502,45 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     uint32_t nseg = 0;
     const uint64_t wave = (uint64_t)blockIdx.x * kWaves + w;
     const uint64_t first = wave * (64 * kSteps);
-    uint32_t cb = first < n ? cs.dir[wave] : 0u;  // owner of the step's first slot
+    uint32_t wb = first < n ? cs.dir[wave] : 0u;  // window: seeds wb .. wb + 63
+    bool loaded = false;                          // uniform
     for (int step = 0; step < kSteps; step++) {
         const uint64_t i0 = first + (uint64_t)step * 64;
         if (i0 >= n) break;  // uniform
         const uint32_t t = (uint32_t)(i0 + lane);
         const bool valid = t < n;
-        uint32_t owner = 0, top = 0;  // top = prefix[owner] - hit_lo
+        uint32_t top = 0, bstart = 0, qend = 0;  // of the slot's owner
         bool found = !valid;
-        for (uint32_t base = cb;; base += 64) {  // uniform: ends once every slot has its owner
-            const uint32_t sj = base + lane;
-            rel[w][lane] = sj < cs.n_seeds ? cs.prefix[sj] - cs.hit_lo : 0xFFFFFFFFu;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
+        for (;;) {  // uniform: ends once every slot has its owner
+            if (!loaded) {
+                const uint32_t sj = wb + lane;
+                const bool in = sj < cs.n_seeds;
+                rel[w][lane] = in ? cs.prefix[sj] - cs.hit_lo : 0xFFFFFFFFu;
+                fst[w][lane] = in ? cs.first[sj] : 0u;
+                qen[w][lane] = in ? cs.q_end[sj] : 0u;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                loaded = true;
+            }
             if (!found && t < rel[w][63]) {
-                int L = 0;  // number of the 64 seeds whose prefix - hit_lo is <= t
+                int L = 0;  // number of the window's seeds whose prefix - hit_lo is <= t
 #pragma unroll
                 for (int k = 32; k >= 1; k >>= 1)
                     if (rel[w][L + k - 1] <= t) L += k;
-                owner = base + (uint32_t)L;
                 top = rel[w][L];
+                bstart = fst[w][L];
+                qend = qen[w][L];
                 found = true;
             }
+            if (__ballot(!found) == 0) break;
+            // a slot lies past the window: every lane is done reading it, slide it on
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
-            if (__ballot(!found) == 0) break;
+            wb += 64;
+            loaded = false;
         }
-        const int last = (int)min<uint64_t>(63, (uint64_t)n - 1 - i0);
-        cb = (uint32_t)lane_value((int32_t)owner, last);
         uint64_t a = 0;
-        if (valid) {
-            const uint32_t j = top - 1u - t;
-            a = (uint64_t)cs.pos[cs.first[owner] + j] | ((uint64_t)cs.q_end[owner] << 32);
-        }
+        if (valid) a = (uint64_t)cs.pos[bstart + (top - 1u - t)] | ((uint64_t)qend << 32);
         Win<RB, LB, false> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
