@@ -262,6 +262,20 @@ int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, int3
 int hspz_get_batch_records(const hspz_engine *engine, hspz_segment_pair *h_out, uint64_t cap,
                            uint64_t *n);
 
+/* Exact-duplicate removal of accepted records: the host dedup that follows acceptance in
+ * the pages' funnel ("D. Score gate", introduction; the raw order it depends on is fixed
+ * in "C. Hit discovery", C.5).  The pages give no rule.  This library's reading: two
+ * records are duplicates when all four fields are equal, and the first of them in the
+ * order of h_in is kept.  The kept records go to h_out in their input order and *n_out
+ * receives their number.  The scope is the array passed: one chunk, one batch (the
+ * records of hspz_run_batch, in chunk order) or a whole strand.  Host memory only; h_out
+ * may equal h_in (in place), otherwise the two must not overlap.  Needs no engine and no
+ * GPU.  Errors: HSPZ_E_INVALID (NULL n_out, or NULL h_in / h_out with n > 0),
+ * HSPZ_E_CAPACITY (cap < *n_out; nothing is written to h_out), HSPZ_E_NOMEM;
+ * hspz_last_error(NULL) describes the failure. */
+int hspz_dedup_records(const hspz_segment_pair *h_in, uint64_t n, hspz_segment_pair *h_out,
+                       uint64_t cap, uint64_t *n_out);
+
 /* ---- inspection (tests and tools) -------------------------------------------------- */
 
 /* Copy seeds [lo, hi) of the current strand to the host: packed k-mers and query end

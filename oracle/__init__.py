@@ -266,6 +266,22 @@ def compact_hsps(hsp, status) -> np.ndarray:
     return out[:m].copy()
 
 
+def dedup_records(hsp) -> np.ndarray:
+    """Host dedup after acceptance ("D. Score gate", introduction: accepted raw HSPs,
+    then fewer final HSPs after host dedup; the order it depends on is fixed in
+    "C. Hit discovery", C.5).  The pages give no rule; the reading taken: a record is a
+    duplicate when an earlier record of the array has the same four fields, and the
+    records that are not duplicates are kept in their order."""
+    hsp = np.ascontiguousarray(hsp, dtype=HSP_DTYPE).reshape(-1)
+    seen = set()
+    keep = []
+    for i, r in enumerate(hsp.tolist()):
+        if r not in seen:
+            seen.add(r)
+            keep.append(i)
+    return hsp[np.array(keep, dtype=np.int64)].copy()
+
+
 # ----------------------------------------------------------------------------- a pass
 
 class Reference:

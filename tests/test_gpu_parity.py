@@ -555,3 +555,47 @@ def test_find_hits_gate_huge_bucket_and_sparse_seeds():
     eng.upload_query(qry2)
     tot, checked = _fused_vs_calls(eng, eng.num_seeds())
     assert checked == tot
+
+
+def test_dedup_records_matches_the_oracle():
+    # the library's host dedup against the oracle's: random record arrays with heavy
+    # repetition, in place through the C ABI, the capacity error, and an empty array
+    import ctypes
+    import ungapped_drop_hsp_amd as h
+    rng = np.random.default_rng(8)
+    for n in (0, 1, 7, 5_000):
+        rows = rng.integers(0, 5, size=(n, 4))
+        rec = np.array([tuple(r) for r in rows], dtype=oracle.HSP_DTYPE)
+        want = oracle.dedup_records(rec)
+        got = h.dedup_records(rec.view(h.SEGMENT_PAIR))
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+        if n == 0:
+            continue
+        buf = rec.view(h.SEGMENT_PAIR).copy()
+        m = ctypes.c_uint64()
+        assert h.lib().hspz_dedup_records(buf.ctypes.data, n, buf.ctypes.data, n,
+                                          ctypes.byref(m)) == 0
+        assert np.array_equal(buf[:m.value].view(np.uint8), want.view(np.uint8))
+        if want.size > 1:
+            out = np.zeros(want.size, h.SEGMENT_PAIR)
+            rc = h.lib().hspz_dedup_records(rec.ctypes.data, n, out.ctypes.data,
+                                            want.size - 1, ctypes.byref(m))
+            assert rc == -3 and m.value == want.size and not out.view(np.uint8).any()
+
+
+def test_dedup_of_run_batch_records():
+    # the accepted records of a batch, deduplicated, against the oracle's pass and dedup
+    import ungapped_drop_hsp_amd as h
+    ref, qry = random_pair(4, 20_000, 20_000, plant=12, plant_len=(300, 900),
+                           identity=0.93)
+    p = params_of(SEED_PATTERN, max_hits=4_000)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    o, _, _ = oracle_pass(ref, qry, p)
+    _, acc = _oracle_batch(o)
+    eng.run_batch(0, eng.num_seeds())
+    got = h.dedup_records(eng.batch_records())
+    want = oracle.dedup_records(acc)
+    assert 0 < want.size < acc.size
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))

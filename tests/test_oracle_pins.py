@@ -433,3 +433,52 @@ def test_entropy_mode_decision():
             n_rej += int(s0 and not s1)
         assert set(map(bytes, c1["accepted"])) <= set(map(bytes, c0["accepted"]))
     assert n_rej > 0
+
+
+# ------------------------------------------------------------------ host dedup
+
+def _records(rows):
+    return np.array([tuple(r) for r in rows], dtype=oracle.HSP_DTYPE)
+
+
+def test_dedup_special_cases():
+    assert oracle.dedup_records(_records([])).size == 0
+    same = _records([(5, 7, 30, 3100)] * 6)
+    assert oracle.dedup_records(same).tolist() == [(5, 7, 30, 3100)]
+    distinct = _records([(i, 2 * i, 10 + i, 3000 + i) for i in range(9)])
+    assert oracle.dedup_records(distinct).tolist() == distinct.tolist()
+    # records that differ in one field only are all kept, in their order
+    one_off = _records([(1, 1, 1, 1), (2, 1, 1, 1), (1, 2, 1, 1), (1, 1, 2, 1),
+                        (1, 1, 1, 2), (1, 1, 1, 1)])
+    assert oracle.dedup_records(one_off).tolist() == one_off[:5].tolist()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_dedup_against_brute_force(seed):
+    # record i is kept iff no earlier record equals it in all four fields
+    rng = np.random.default_rng(seed)
+    n = 400
+    rows = rng.integers(0, 4, size=(n, 4))
+    rows[:, 3] += 2999  # scores near the threshold
+    rec = _records(rows)
+    keep = [i for i in range(n) if not any((rows[j] == rows[i]).all() for j in range(i))]
+    got = oracle.dedup_records(rec)
+    assert got.tolist() == rec[keep].tolist()
+    assert oracle.dedup_records(got).tolist() == got.tolist()  # idempotent
+
+
+def test_dedup_of_a_pass_removes_repeated_records_only():
+    # anchors on the diagonal of one planted homolog materialize the same interval, so a
+    # pass's accepted records repeat; dedup keeps each distinct record once, in order
+    ref, qry = random_pair(4, 20_000, 20_000, plant=12, plant_len=(300, 900),
+                           identity=0.93)
+    p = dict(seed_pattern=SEED_PATTERN, sub=HOXD70, n_score=NS, xdrop=X, hsp_threshold=K,
+             max_hits=0, entropy_mode=0)
+    R = oracle.Reference(ref, SEED_PATTERN)
+    o = oracle.run_pass(R, oracle.strand_codes(qry, "+"), p)
+    acc = np.concatenate([c["accepted"] for c in o["chunks"]])
+    d = oracle.dedup_records(acc)
+    assert 0 < d.size < acc.size
+    assert len(set(d.tolist())) == d.size and set(d.tolist()) == set(acc.tolist())
+    first = [acc.tolist().index(r) for r in d.tolist()]
+    assert first == sorted(first)

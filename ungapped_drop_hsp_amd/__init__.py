@@ -32,7 +32,7 @@ ABI_SYMBOLS = (
     "hspz_materialize", "hspz_compact_hsps", "hspz_get_seeds", "hspz_get_plan_arrays",
     "hspz_get_index", "hspz_debug_plan_counts", "hspz_debug_walk_steps",
     "hspz_debug_gate_deferred", "hspz_run_batch", "hspz_get_batch_records",
-    "hspz_find_hits_gate",
+    "hspz_find_hits_gate", "hspz_dedup_records",
 )
 
 
@@ -92,6 +92,7 @@ def _load() -> ctypes.CDLL:
                                           ctypes.POINTER(BatchStats), P]),
         "hspz_get_batch_records": (ctypes.c_int, [P, P, U64, PU64]),
         "hspz_find_hits_gate": (ctypes.c_int, [P, ctypes.c_uint32, P, U64, P, P]),
+        "hspz_dedup_records": (ctypes.c_int, [P, U64, P, U64, PU64]),
         "hspz_debug_plan_counts": (ctypes.c_int, [P, P, U64, P, PU64, PU32]),
         "hspz_debug_walk_steps": (ctypes.c_int, [P, P, U64, PU64, P]),
         "hspz_debug_gate_deferred": (ctypes.c_int, [P, PU64, PU64, P]),
@@ -147,6 +148,19 @@ def _host_bytes(seq) -> np.ndarray:
     if a.dtype != np.uint8:
         raise TypeError("sequence must be bytes or a uint8 array")
     return a
+
+
+def dedup_records(records: np.ndarray) -> np.ndarray:
+    """Exact-duplicate removal of accepted records (host): the first of equal records is
+    kept, in input order."""
+    rec = np.ascontiguousarray(records, dtype=SEGMENT_PAIR).reshape(-1)
+    out = np.empty(max(rec.size, 1), SEGMENT_PAIR)
+    n = ctypes.c_uint64()
+    rc = _lib.hspz_dedup_records(rec.ctypes.data if rec.size else None, rec.size,
+                                 out.ctypes.data, out.size, ctypes.byref(n))
+    if rc != 0:
+        raise HspzError(rc, _lib.hspz_last_error(None).decode())
+    return out[:n.value].copy()
 
 
 class Engine:

@@ -6,6 +6,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <unordered_set>
 
 #include "hspz_internal.h"
 
@@ -1078,6 +1079,61 @@ HSPZ_API int hspz_get_batch_records(const hspz_engine *engine, hspz_segment_pair
     if (cap < e->h_rec_n)
         return fail(e, HSPZ_E_CAPACITY, "%llu records, room for %llu",
                     (unsigned long long)e->h_rec_n, (unsigned long long)cap);
+    return HSPZ_OK;
+}
+
+namespace {
+
+struct RecordHash {
+    size_t operator()(const hspz_segment_pair &r) const {
+        uint64_t a = ((uint64_t)r.ref_start << 32) | r.query_start;
+        uint64_t b = ((uint64_t)r.len << 32) | (uint32_t)r.score;
+        uint64_t x = a ^ (b * 0x9E3779B97F4A7C15ull);  // splitmix64 finaliser of the mix
+        x ^= x >> 30;
+        x *= 0xBF58476D1CE4E5B9ull;
+        x ^= x >> 27;
+        x *= 0x94D049BB133111EBull;
+        return (size_t)(x ^ (x >> 31));
+    }
+};
+struct RecordEq {
+    bool operator()(const hspz_segment_pair &x, const hspz_segment_pair &y) const {
+        return x.ref_start == y.ref_start && x.query_start == y.query_start && x.len == y.len &&
+               x.score == y.score;
+    }
+};
+
+int no_engine_fail(int code, const char *msg) {
+    g_create_error = msg;
+    return code;
+}
+
+}  // namespace
+
+HSPZ_API int hspz_dedup_records(const hspz_segment_pair *h_in, uint64_t n,
+                                hspz_segment_pair *h_out, uint64_t cap, uint64_t *n_out) {
+    if (!n_out) return no_engine_fail(HSPZ_E_INVALID, "NULL n_out");
+    *n_out = 0;
+    if (n && (!h_in || !h_out)) return no_engine_fail(HSPZ_E_INVALID, "NULL records");
+    std::vector<uint8_t> first;
+    uint64_t kept = 0;
+    try {
+        first.assign(n, 0);
+        std::unordered_set<hspz_segment_pair, RecordHash, RecordEq> seen;
+        seen.reserve((size_t)n);
+        for (uint64_t i = 0; i < n; i++)
+            if (seen.insert(h_in[i]).second) {
+                first[i] = 1;
+                kept++;
+            }
+    } catch (const std::bad_alloc &) {
+        return no_engine_fail(HSPZ_E_NOMEM, "dedup: host allocation failed");
+    }
+    *n_out = kept;
+    if (kept > cap) return no_engine_fail(HSPZ_E_CAPACITY, "dedup: output capacity too small");
+    uint64_t k = 0;  // k <= i throughout, so h_out == h_in is safe
+    for (uint64_t i = 0; i < n; i++)
+        if (first[i]) h_out[k++] = h_in[i];
     return HSPZ_OK;
 }
 
