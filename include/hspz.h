@@ -86,8 +86,13 @@ typedef struct {
  *  gate_mode     0 = windowed score gate when it is exact for these parameters (eight-base
  *                blocks, 16-bit pair scores), else the exact per-base walk; 1 = always the
  *                per-base walk; 2 = always windowed; 3 = always windowed with a narrower
- *                first window (2 and 3 fail with HSPZ_E_INVALID if not exact).  Every
- *                mode writes the same flags ("D. Score gate", D.2).
+ *                first window; 4 = the reference-locality bucketed gate ("D. Score gate",
+ *                D.5): the call's anchors are sorted stably by reference slice (2^22
+ *                bases or more, at most 256 slices) with their raw indices, each XCD's
+ *                waves score the windows of about one slice at a time, and results go
+ *                back by raw index (2, 3 and 4 fail with HSPZ_E_INVALID if the window
+ *                gate is not exact).  Every mode writes the same flags ("D. Score gate",
+ *                D.2).
  *  entropy_mode  the accept decision of hspz_materialize ("E. X-drop materialization",
  *                E.5, which names an entropy-adjusted decision without a formula):
  *                0 = accept iff score >= T; 1 = also require score * H >= 2 * K, where H
@@ -95,6 +100,12 @@ typedef struct {
  *                record's reference interval (N excluded), computed in double precision
  *                as (n log2 n - sum_b n_b log2 n_b) / n; no A/C/G/T in the interval
  *                rejects.
+ *  ref_buckets   reference slices of the bucketed gate (gate_mode 4; the pages' engine
+ *                switch for reference-locality bucketing, "D. Score gate", D.5): 0 =
+ *                automatic, slices of 2^22 bases (2 MiB of 4-bit codes, inside one XCD's
+ *                L2), widened to keep at most 256; n in 1..256 = at most n slices, each
+ *                of the smallest power-of-two width that allows it.  Ignored by the
+ *                other gate modes; never changes any output.
  */
 typedef struct {
     const char *seed_pattern;
@@ -108,6 +119,7 @@ typedef struct {
     int32_t device;
     int32_t gate_mode;
     int32_t entropy_mode;
+    int32_t ref_buckets;
 } hspz_params;
 
 /* Create an engine on params->device and compute the keep threshold T once: the least
@@ -198,8 +210,9 @@ int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
  * afterwards d_anchors (cap >= n_hits u64 entries) holds the anchor of every slot whose
  * flag is 1, which is what hspz_materialize reads, and its other entries are
  * unspecified.  When the window gate does not apply (gate_mode 1, or scores or xdrop
- * outside its bounds) the call is hspz_find_hits followed by hspz_score_gate, and every
- * entry is written.  Errors: as hspz_find_hits; HSPZ_E_INVALID for NULL buffers. */
+ * outside its bounds), and with the bucketed gate (gate_mode 4, which sorts the written
+ * anchors), the call is hspz_find_hits followed by hspz_score_gate, and every entry is
+ * written.  Errors: as hspz_find_hits; HSPZ_E_INVALID for NULL buffers. */
 int hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors, uint64_t cap,
                         uint8_t *d_flags, void *stream);
 

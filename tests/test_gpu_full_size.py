@@ -169,3 +169,35 @@ def test_c4_200mb_both_strands_batches():
                      batch_pick=lambda strand, n: {0} if strand == "+" else {n - 1},
                      full_plan=False)
     assert len(st) == 2 and all(s["chunks"] > 1 for s in st)
+
+
+@pytest.mark.timeout(600)
+def test_c3_bucketed_gate_full_size():
+    # the bucketed gate (gate_mode 4, automatic slices: 12 of 2^22 bases) on every c3
+    # chunk: every flag byte equal to the default gate's, which the test above ties to the
+    # oracle; then the whole batch through run_batch, record for record
+    import torch
+    w = build(3)
+    p = w.params()
+    eng0, eng4 = engine(p), engine(p, gate_mode=4)
+    for e in (eng0, eng4):
+        e.upload_reference(w.ref)
+        e.upload_query(w.query)
+    n_seeds = eng0.num_seeds()
+    _, nch = eng0.plan(0, n_seeds)
+    assert eng4.plan(0, n_seeds)[1] == nch == 2
+    for c in range(nch):
+        n = eng0.get_chunk(c)["n_hits"]
+        a = torch.empty(n, dtype=torch.int64, device="cuda")
+        f0 = torch.empty(n, dtype=torch.uint8, device="cuda")
+        f4 = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+        eng0.find_hits(c, a)
+        eng0.score_gate(a, n, f0)
+        eng4.score_gate(a, n, f4)
+        assert torch.equal(f0, f4), f"chunk {c}: bucketed flags differ"
+        print(f"chunk {c}: {n} anchors, {int(f0.sum())} kept", flush=True)
+        del a, f0, f4
+    s0, s4 = eng0.run_batch(0, n_seeds), eng4.run_batch(0, n_seeds)
+    assert (s0["n_survivors"], s0["n_accepted"]) == (s4["n_survivors"], s4["n_accepted"])
+    assert np.array_equal(eng0.batch_records().view(np.uint8),
+                          eng4.batch_records().view(np.uint8))

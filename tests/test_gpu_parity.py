@@ -108,15 +108,19 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
-@pytest.mark.parametrize("expand_mode,gate_mode", [(0, 0), (1, 1), (2, 2), (0, 3)],
-                         ids=["auto", "sparse-exact", "dense-window", "auto-window2"])
+@pytest.mark.parametrize("expand_mode,gate_mode", [(0, 0), (1, 1), (2, 2), (0, 3), (0, 4)],
+                         ids=["auto", "sparse-exact", "dense-window", "auto-window2",
+                              "bucketed"])
 def test_random_pass_parity(case, expand_mode, gate_mode):
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
     ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
                            identity=ident, gc=gc, alphabet_noise=True)
     p = params_of(pat, max_hits=mx)
     o, _, _ = oracle_pass(ref, qry, p)
-    r = gpu_full_pass(engine(p, expand_mode=expand_mode, gate_mode=gate_mode), ref, qry)
+    # the bucketed gate over 16 reference slices (the automatic width is one slice here)
+    eng = engine(p, expand_mode=expand_mode, gate_mode=gate_mode,
+                 ref_buckets=16 if gate_mode == 4 else 0)
+    r = gpu_full_pass(eng, ref, qry)
     assert_pass_equal(r, o)
 
 
@@ -129,7 +133,7 @@ def _edge_anchors(rng, nr, nq, k):
     return np.asarray([(a & 0xFFFFFFFF) | (b << 32) for a, b in zip(r, q)], np.uint64)
 
 
-@pytest.mark.parametrize("gate_mode", [1, 2, 3])
+@pytest.mark.parametrize("gate_mode", [1, 2, 3, 4])
 @pytest.mark.parametrize("seed", range(3))
 def test_gate_on_arbitrary_anchors(gate_mode, seed):
     # anchors need not come from seeds: walks from every offset near both sequence ends,
@@ -139,7 +143,7 @@ def test_gate_on_arbitrary_anchors(gate_mode, seed):
     ref, qry = random_pair(200 + seed, 3_000 + 500 * seed, 2_500 + 700 * seed, n_frac=0.05,
                            plant=12, plant_len=(100, 900), identity=0.93)
     p = params_of("11011", K=300 + 200 * seed)
-    eng = engine(p, gate_mode=gate_mode)
+    eng = engine(p, gate_mode=gate_mode, ref_buckets=7 + 60 * seed)
     eng.upload_reference(ref)
     eng.upload_query(qry)
     a = _edge_anchors(rng, ref.size, qry.size, 30_000)
@@ -160,12 +164,12 @@ def test_gate_on_arbitrary_anchors(gate_mode, seed):
         assert 0 < n2 < a.size and 0 < nx <= n2
 
 
-@pytest.mark.parametrize("gate_mode", [2, 3])
+@pytest.mark.parametrize("gate_mode", [2, 3, 4])
 def test_window_gate_defers_long_walks(gate_mode):
     # a sequence against itself: every anchor on the main diagonal walks to both ends
     ref, _ = random_pair(15, 20_000, 1, gc=0.41)
     p = params_of("1101011", K=10**6)
-    eng = engine(p, gate_mode=gate_mode)
+    eng = engine(p, gate_mode=gate_mode, ref_buckets=32)
     eng.upload_reference(ref)
     eng.upload_query(ref)
     import torch
@@ -519,7 +523,7 @@ def _fused_vs_calls(eng, n_seeds):
     return tot, checked
 
 
-@pytest.mark.parametrize("gate_mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("gate_mode", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
 def test_find_hits_gate_matches_the_calls(case, gate_mode):
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
@@ -530,6 +534,35 @@ def test_find_hits_gate_matches_the_calls(case, gate_mode):
     eng.upload_query(qry)
     tot, checked = _fused_vs_calls(eng, eng.num_seeds())
     assert checked == tot
+
+
+@pytest.mark.parametrize("slices", [1, 2, 3, 64, 256])
+def test_bucketed_gate_slice_counts(slices):
+    # the bucketed gate ("D. Score gate", D.5) against the oracle for 1 to 256 reference
+    # slices, with anchors at both ends, past the ends (they fall in the last slice) and on
+    # planted homologs; then shrinking calls on the same engine, down to none
+    import torch
+    rng = np.random.default_rng(slices)
+    ref, qry = random_pair(40 + slices, 24_000, 9_000, n_frac=0.03, plant=20,
+                           plant_len=(100, 900), identity=0.92)
+    p = params_of("1101011", K=1_500)
+    eng = engine(p, gate_mode=4, ref_buckets=slices)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    o, R, qc = oracle_pass(ref, qry, p)
+    past = np.asarray([(ref.size + 1 + i) | (int(rng.integers(0, qry.size)) << 32)
+                       for i in range(40)], np.uint64)
+    a = np.concatenate([_edge_anchors(rng, ref.size, qry.size, 20_000), past] +
+                       [c["anchors"] for c in o["chunks"]])
+    a = a[rng.permutation(a.size)]
+    want = oracle.gate(a, R.codes, qc, p["sub"], p["n_score"], p["xdrop"],
+                       oracle.keep_threshold(p["hsp_threshold"]))
+    assert 0 < int(want.sum()) < a.size
+    at = torch.from_numpy(a.view(np.int64)).cuda()
+    for n in (a.size, a.size // 3, 1, 0):
+        f = torch.full((max(n, 1),), 0xAB, dtype=torch.uint8, device="cuda")
+        eng.score_gate(at, n, f)
+        assert np.array_equal(f[:n].cpu().numpy(), want[:n]), f"n={n}"
 
 
 def test_find_hits_gate_huge_bucket_and_sparse_seeds():

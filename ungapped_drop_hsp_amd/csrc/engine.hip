@@ -322,6 +322,13 @@ Engine::~Engine() {
     dfree(d_blkoff);
     dfree(d_cblk);
     dfree(d_ctotal);
+    dfree(d_bsa);
+    dfree(d_bsi);
+    dfree(d_bhist);
+    dfree(d_bincl);
+    dfree(d_bsum);
+    dfree(d_boff);
+    dfree(d_binfo);
     dfree(d_plan);
     dfree(d_dir);
     for (int b = 0; b < 2; b++) {
@@ -381,8 +388,10 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "chunk_walk must be 0 or 1");
     if (p->entropy_mode < 0 || p->entropy_mode > 1)
         return fail(nullptr, HSPZ_E_INVALID, "entropy_mode must be 0 or 1");
-    if (p->gate_mode < 0 || p->gate_mode > 3)
-        return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2 or 3");
+    if (p->ref_buckets < 0 || p->ref_buckets > 256)
+        return fail(nullptr, HSPZ_E_INVALID, "ref_buckets must be in 0..256");
+    if (p->gate_mode < 0 || p->gate_mode > 4)
+        return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2, 3 or 4");
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev)
         return fail(nullptr, HSPZ_E_INVALID, "device %d not available (%d devices)", p->device,
@@ -438,7 +447,7 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     e->wp.T = e->T;
     if (p->gate_mode >= 2 && !e->window_ok)
         return fail(nullptr, HSPZ_E_INVALID,
-                    "gate_modes 2 and 3 need 7 * max score <= xdrop and 16-bit pair scores");
+                    "gate_modes 2, 3 and 4 need 7 * max score <= xdrop and 16-bit pair scores");
     int rc = set_device(e);
     if (rc) {
         g_create_error = e->err;
@@ -530,6 +539,13 @@ HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, 
     if (!e->d_pos && (rc = dalloc(e, e->d_pos, 1))) return rc;
     e->n_index = nwin;
     e->n_ref = len;
+    // bucketed gate: automatic slices of 2^22 bases (2 MiB of 4-bit codes, half of one
+    // XCD's 4 MB L2), wider for references that would need more than 256 of them; or the
+    // narrowest power-of-two width giving at most ref_buckets slices
+    const uint64_t most = e->params.ref_buckets ? (uint64_t)e->params.ref_buckets : 256;
+    e->slice_shift = e->params.ref_buckets ? 0 : 22;
+    while ((len >> e->slice_shift) + 1 > most) e->slice_shift++;
+    e->n_slices = (uint32_t)(len >> e->slice_shift) + 1;
     e->sp.n_ref = (uint32_t)len;
     e->wp.n_ref = (uint32_t)len;
     e->has_ref = true;
@@ -762,6 +778,27 @@ static int ensure_defer(Engine *e, uint64_t n) {
     return HSPZ_OK;
 }
 
+// Bucketed gate scratch for n anchors.
+static int ensure_bucket(Engine *e, uint64_t n) {
+    if (!e->d_binfo) {
+        int rc = dalloc(e, e->d_binfo, 1);
+        if (rc) return rc;
+    }
+    if (n <= e->cap_bucket && e->d_bsa) return HSPZ_OK;
+    const uint64_t cap = std::max<uint64_t>({n, 4096, e->cap_bucket + e->cap_bucket / 4});
+    const uint64_t nh = 256ull * bucket_blocks((uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull));
+    const uint64_t ns = (nh + kScanBlock - 1) / kScanBlock;
+    int rc;
+    if ((rc = dalloc(e, e->d_bsa, cap)) || (rc = dalloc(e, e->d_bsi, cap)) ||
+        (rc = dalloc(e, e->d_bhist, nh)) || (rc = dalloc(e, e->d_bincl, nh)) ||
+        (rc = dalloc(e, e->d_bsum, ns)) || (rc = dalloc(e, e->d_boff, ns))) {
+        e->cap_bucket = 0;
+        return rc;
+    }
+    e->cap_bucket = cap;
+    return HSPZ_OK;
+}
+
 // The fused first stage's per-wave owner directory for a chunk of n anchors.
 static int ensure_dir(Engine *e, uint64_t n) {
     const uint64_t n_waves = (n + gate_window_wave_slots() - 1) / gate_window_wave_slots();
@@ -796,8 +833,29 @@ HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uin
     }
     if ((rc = ensure_defer(e, n))) return rc;
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
-    HIP_TRY(e, launch_gate_window(e->params.gate_mode == 3, d_anchors, (uint32_t)n, d_flags,
-                                  e->d_ref4, e->d_qry4, e->wp, list1, list2, e->d_defer_cnt, s));
+    if (e->params.gate_mode == 4) {
+        // stable sort by reference slice: slice-major histogram, its scan, the scatter
+        if ((rc = ensure_bucket(e, n))) return rc;
+        const uint32_t n32 = (uint32_t)n, nb = e->n_slices;
+        const uint64_t nh = (uint64_t)nb * bucket_blocks(n32);
+        HIP_TRY(e, launch_bucket_hist(d_anchors, n32, e->slice_shift, nb, e->d_bhist, s));
+        if (nh) {
+            HIP_TRY(e, launch_count_scan(nullptr, e->d_bhist, nh, nullptr, e->d_bhist, nullptr,
+                                         e->d_bincl, e->d_bsum, s));
+            HIP_TRY(e, launch_scan_blocks(e->d_bsum, (nh + kScanBlock - 1) / kScanBlock,
+                                          e->d_boff, e->d_binfo, s));
+            HIP_TRY(e, launch_add_offsets(e->d_bincl, nh, e->d_boff, s));
+        }
+        HIP_TRY(e, launch_bucket_scatter(d_anchors, n32, e->slice_shift, nb, e->d_bincl,
+                                         e->d_bhist, e->d_bsa, e->d_bsi, s));
+        HIP_TRY(e, launch_gate_window_bucketed(d_anchors, n32, e->d_bsa, e->d_bsi, d_flags,
+                                               e->d_ref4, e->d_qry4, e->wp, list1, list2,
+                                               e->d_defer_cnt, s));
+    } else {
+        HIP_TRY(e, launch_gate_window(e->params.gate_mode == 3, d_anchors, (uint32_t)n, d_flags,
+                                      e->d_ref4, e->d_qry4, e->wp, list1, list2, e->d_defer_cnt,
+                                      s));
+    }
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
@@ -816,7 +874,8 @@ HSPZ_API int hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *
         return fail(e, HSPZ_E_CAPACITY, "anchor buffer holds %llu, chunk needs %llu",
                     (unsigned long long)cap, (unsigned long long)c.n_hits);
     if (c.n_hits && (!d_anchors || !d_flags)) return fail(e, HSPZ_E_INVALID, "NULL buffer");
-    if (!(e->window_ok && e->params.gate_mode != 1)) {  // the exact gate reads every anchor
+    // the exact gate and the bucketed gate read every anchor from memory
+    if (!(e->window_ok && e->params.gate_mode != 1 && e->params.gate_mode != 4)) {
         int rc = hspz_find_hits(engine, chunk, d_anchors, cap, stream);
         return rc ? rc : hspz_score_gate(engine, d_anchors, c.n_hits, d_flags, stream);
     }

@@ -161,6 +161,20 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     const uint32_t *qry4, const WindowParams &wp,
                                     uint32_t *list1, uint32_t *list2, uint32_t *cnt,
                                     hipStream_t s);
+// Bucketed gate ("D. Score gate", D.5): stable sort of anchors by reference slice
+// (k_bucket.hip) and the first window stage over the sorted anchors (k_gate.hip).
+uint32_t bucket_blocks(uint32_t n);  // workgroups of the slice histogram and scatter
+hipError_t launch_bucket_hist(const uint64_t *anchors, uint32_t n, int shift, uint32_t nb,
+                              uint32_t *hist, hipStream_t s);
+hipError_t launch_bucket_scatter(const uint64_t *anchors, uint32_t n, int shift, uint32_t nb,
+                                 const uint32_t *incl, const uint32_t *hist, uint64_t *sa,
+                                 uint32_t *si, hipStream_t s);
+hipError_t launch_zero_bytes(uint8_t *p, uint64_t n, hipStream_t s);
+hipError_t launch_gate_window_bucketed(const uint64_t *anchors, uint32_t n, const uint64_t *sa,
+                                       const uint32_t *si, uint8_t *flags, const uint32_t *ref4,
+                                       const uint32_t *qry4, const WindowParams &wp,
+                                       uint32_t *list1, uint32_t *list2, uint32_t *cnt,
+                                       hipStream_t s);
 hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
                                  const uint32_t *count, uint32_t max_count, uint8_t *flags,
                                  const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
@@ -231,6 +245,19 @@ struct Engine {
     uint64_t cap_defer = 0;
     uint32_t *d_defer_cnt = nullptr;
     bool gate_deferred_valid = false;
+
+    // bucketed gate (gate_mode 4): reference slices of 2^slice_shift bases, and per-call
+    // scratch for cap_bucket anchors: sorted anchors and raw indices, the slice-major
+    // histogram and its scan
+    int slice_shift = 22;
+    uint32_t n_slices = 1;
+    uint64_t *d_bsa = nullptr;
+    uint32_t *d_bsi = nullptr;
+    uint32_t *d_bhist = nullptr, *d_bincl = nullptr;
+    uint64_t *d_bsum = nullptr;
+    uint32_t *d_boff = nullptr;
+    PlanInfo *d_binfo = nullptr;
+    uint64_t cap_bucket = 0;
 
     // compaction scratch
     uint32_t *d_cblk = nullptr;

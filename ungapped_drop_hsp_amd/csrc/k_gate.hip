@@ -254,6 +254,22 @@ __device__ __forceinline__ void load_window(const uint32_t *__restrict__ base, u
     }
 }
 
+// The same window read from the 4-bit copy alone (it may span two lines).
+template <int W>
+__device__ __forceinline__ void load_plain(const uint32_t *__restrict__ base, uint32_t m,
+                                           uint32_t (&Wd)[W]) {
+    static_assert(W % 4 == 0, "whole 16-byte loads");
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(base + m);
+#pragma unroll
+    for (int j = 0; j < W / 4; j++) {
+        const u32x4 v = p[j];
+        Wd[4 * j + 0] = v.x;
+        Wd[4 * j + 1] = v.y;
+        Wd[4 * j + 2] = v.z;
+        Wd[4 * j + 3] = v.w;
+    }
+}
+
 // Eight bases: R and Q hold codes of bases 0..7 in nibbles 0..7.  Even bases' table
 // indices (r << 4 | q) land in the bytes of ie, odd bases' in the bytes of io.
 template <bool Right>
@@ -296,7 +312,7 @@ struct Unrolled<N, N> {
 // step's.  decide() is called by all lanes of the wave together and returns the flag
 // (0 or 1), or 2 when a walk is still running at the window's end.  With EarlyKeep a walk
 // also stops once the flag is 1 whatever follows (R*, or R* + best so far, reaches T).
-template <int RB, int LB, bool EarlyKeep>
+template <int RB, int LB, bool EarlyKeep, bool RefTwin = true>
 struct Win {
     static constexpr int W = (LB + RB + 1 + 3) / 4 * 4;
     static_assert(8 * LB + 8 <= kPad4, "left window stays inside the edge padding");
@@ -311,7 +327,10 @@ struct Win {
         inrange = in;
         const uint32_t wr = (in ? r : 0u) + (uint32_t)(kPad4 - 8 * LB);
         const uint32_t wq = (in ? q : 0u) + (uint32_t)(kPad4 - 8 * LB);
-        load_window<W>(ref4, wp.ref4_alt, wr >> 3, R);
+        if (RefTwin)
+            load_window<W>(ref4, wp.ref4_alt, wr >> 3, R);
+        else
+            load_plain<W>(ref4, wr >> 3, R);
         load_window<W>(qry4, wp.qry4_alt, wq >> 3, Q);
         shr = (wr & 7u) * 4u;
         shq = (wq & 7u) * 4u;
@@ -551,6 +570,53 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
 }
 
+// First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
+// D.5).  The sorted array is cut into eight equal contiguous parts, one per XCD, and
+// workgroup b scores tile b / 8 of part b % 8: workgroups are dispatched in index order
+// and placed on the eight XCDs in turn, so each XCD walks its part of the reference from
+// start to end and holds about one slice of it (read without its twin) in its L2 at a
+// time.  The mapping only places work; every tile is scored exactly once wherever it
+// runs.  Results go back by raw index: the flag of a kept anchor is set to 1 (the caller
+// zeroed all flags), a deferred anchor's raw index joins the list for the second stage.
+template <int RB, int LB>
+__global__ __launch_bounds__(kThreads) void k_gate_window_bucketed(
+    const uint64_t *__restrict__ sa, const uint32_t *__restrict__ si, uint32_t n,
+    uint32_t part, uint8_t *__restrict__ flags, const uint32_t *__restrict__ ref4,
+    const uint32_t *__restrict__ qry4, WindowParams wp, uint32_t *__restrict__ defer,
+    uint32_t *__restrict__ defer_cnt) {
+    __shared__ int16_t tab[kWinTab];
+    __shared__ uint32_t seg[kWaves][kSeg];
+    __shared__ uint32_t seg_n[kWaves];
+    __shared__ uint32_t blk_base;
+    if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    __syncthreads();
+
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t nseg = 0;
+    const uint64_t lo = (uint64_t)(blockIdx.x & 7u) * part;
+    const uint64_t hi = std::min<uint64_t>(lo + part, n);
+    const uint64_t first = lo + ((uint64_t)(blockIdx.x >> 3) * kWaves + w) * (64 * kSteps);
+    for (int step = 0; step < kSteps; step++) {
+        const uint64_t j0 = first + (uint64_t)step * 64;
+        if (j0 >= hi) break;  // uniform
+        const uint64_t j = j0 + lane;
+        const bool valid = j < hi;
+        uint64_t a = 0;
+        uint32_t raw = 0;
+        if (valid) {
+            a = sa[j];
+            raw = si[j];
+        }
+        Win<RB, LB, false, false> win;
+        win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
+        const int res = win.decide(tab, wp);
+        if (valid && res == 1) flags[raw] = 1;
+        defer_push(seg[w], nseg, valid && res == 2, raw, defer, defer_cnt);
+    }
+    defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
+}
+
 // Later stage: the anchors listed by the previous stage (*count of them), wider windows.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_list(
@@ -689,6 +755,24 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                            dim3(kThreads), 0, s, cs, n, anchors, flags, ref4, qry4, wp, list1,
                            cnt);
     launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_window_bucketed(const uint64_t *anchors, uint32_t n, const uint64_t *sa,
+                                       const uint32_t *si, uint8_t *flags, const uint32_t *ref4,
+                                       const uint32_t *qry4, const WindowParams &wp,
+                                       uint32_t *list1, uint32_t *list2, uint32_t *cnt,
+                                       hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+    if (n == 0) return hipGetLastError();
+    hipError_t st = launch_zero_bytes(flags, n, s);
+    if (st != hipSuccess) return st;
+    const uint32_t part = (uint32_t)(((uint64_t)n + 7) / 8);
+    const uint64_t per_block = (uint64_t)kWaves * 64 * kSteps;
+    const uint32_t blocks = 8u * (uint32_t)(((uint64_t)part + per_block - 1) / per_block);
+    hipLaunchKernelGGL((k_gate_window_bucketed<kWideRight, kWideLeft>), dim3(blocks),
+                       dim3(kThreads), 0, s, sa, si, n, part, flags, ref4, qry4, wp, list1, cnt);
+    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
     return hipGetLastError();
 }
 
