@@ -87,22 +87,34 @@ def gather_ceiling(torch) -> float:
     return n / (e0.elapsed_time(e1) / 10 / 1000.0)
 
 
+# The sources the hspz_find_hits_gate call is compiled from; the committed counter summary
+# holds their combined SHA-256.
+GATE_SOURCES = ("k_gate.hip", "walk.h", "wave.h", "hspz_internal.h")
+
+
+def gate_sources_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in GATE_SOURCES:
+        with open(os.path.join(ROOT, "ungapped_drop_hsp_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def gate_traffic(workload: str, gate_mode: int):
     """Measured fabric bytes per hspz_find_hits_gate call from the committed counter summary.
 
     The summary was taken with rocprofv3 FETCH_SIZE / WRITE_SIZE runs and calibrated
-    against a plain device copy.  It applies only to the source it was measured on and to
-    the same workload; otherwise None.
+    against a plain device copy.  It applies only to the sources it was measured on and to
+    the same workload and gate mode; otherwise None.
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", "find_hits_gate_traffic_c3_50Mb.json")
-    src = os.path.join(ROOT, "ungapped_drop_hsp_amd", "csrc", "k_gate.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = gate_sources_sha()
     except OSError:
         return None
-    if (rec.get("k_gate_hip_sha256") != sha or not rec["workload"].startswith(workload)
+    if (rec.get("gate_sources_sha256") != sha or not rec["workload"].startswith(workload)
             or rec.get("gate_mode", 0) != gate_mode):
         return None
     return rec["hbm_bytes_per_call"]
