@@ -951,7 +951,8 @@ HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
     int rc = set_device(e);
     if (rc) return rc;
     HIP_TRY(e, launch_materialize(d_anchors, d_ids, (uint32_t)n_surv, d_hsp, d_status,
-                                  e->d_ref + kPad, e->d_qry + kPad, e->sp, as_stream(stream)));
+                                  e->d_ref + kPad, e->d_ref4, e->d_qry4, e->sp,
+                                  as_stream(stream)));
     return HSPZ_OK;
 }
 

@@ -14,8 +14,8 @@ namespace hspz {
 
 // ---- device layout -----------------------------------------------------------------
 // Sequences live on the device one byte per base, padded on both sides with kPad
-// "edge" bytes (enough for a materializer tile of 512 bases and the one it reads ahead
-// past a sequence end).  A reference byte holds code*8 and a query byte holds code, so
+// "edge" bytes (more than the byte-reading walks, the gate's exact ones and the walk-step
+// count, read past a sequence end: a 64-base tile and the one read ahead).  A reference byte holds code*8 and a query byte holds code, so
 // OR-ing a reference byte with a query byte gives the pair index ref*8 + query (0..45)
 // into the score table.  Codes: A,C,G,T = 0..3, N = 4, edge (outside the sequence) = 5.
 constexpr int kPad = 1024;
@@ -30,8 +30,10 @@ constexpr int kTabSize = 64;
 // unshifted ones above on both sequences (A,C,G,T = 0..3, N = 4, edge = 5).  Each copy
 // is followed, at the next 128-byte boundary, by its twin: twin dword j holds copy dword
 // j + kTwinShift.  A window of at most 16 dwords starting at copy dword m lies inside one
-// 128-byte line of the copy when m % 32 <= 16, and of the twin otherwise.
-constexpr int kPad4 = 256;
+// 128-byte line of the copy when m % 32 <= 16, and of the twin otherwise.  The padding
+// also holds the materializer's tile of 512 bases, the one it reads ahead and the dword
+// its funnel shift reads past them.
+constexpr int kPad4 = 1152;
 constexpr int kTwinShift = 16;
 
 // Seeds per block of the device prefix scan.
@@ -179,9 +181,12 @@ hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
                                  const uint32_t *count, uint32_t max_count, uint8_t *flags,
                                  const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
                                  hipStream_t s);
+// ref: the padded byte reference past its padding (base 0), for the entropy decision;
+// ref4, qry4: the 4-bit copies (base b at padded nibble kPad4 + b), for the walks.
 hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint32_t n_surv,
                               hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
-                              const uint8_t *qry, const ScoreParams &sp, hipStream_t s);
+                              const uint32_t *ref4, const uint32_t *qry4, const ScoreParams &sp,
+                              hipStream_t s);
 // Stable compaction: count non-zero bytes per block, scan block counts on the device
 // (total -> *d_total), then emit either the indices (ids != nullptr) or the selected
 // 16-byte records (rec_in/rec_out).

@@ -1,7 +1,7 @@
 // Exact X-drop materialization ("E. X-drop materialization", E.1-E.5).
 //
-// One wave per survivor walks both sides with exact_walk_tiles (512-base tiles, eight
-// bases per lane, the next tile read ahead; earliest endpoints).  With the
+// One wave per survivor walks both sides with exact_walk_tiles over the 4-bit copies
+// (512-base tiles, eight bases per lane, the next tile read ahead; earliest endpoints).  With the
 // entropy-adjusted decision on, the wave then counts the record's reference bases
 // (entropy_accept).  Lane 0 stores the 16-byte record and the status.
 #include <climits>
@@ -14,8 +14,9 @@ namespace hspz {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 1;  // one wave per workgroup: a finished walk frees its slot at once
 constexpr int kThreads = 64 * kWaves;
+constexpr int kTab4 = 96;  // pair indices r * 16 + q for codes up to 5
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -51,9 +52,14 @@ __device__ __forceinline__ bool entropy_accept(const uint8_t *__restrict__ ref, 
 __global__ __launch_bounds__(kThreads) void k_materialize(
     const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ ids, uint32_t n_surv,
     hspz_segment_pair *__restrict__ hsp, uint8_t *__restrict__ status,
-    const uint8_t *__restrict__ ref, const uint8_t *__restrict__ qry, ScoreParams sp) {
-    __shared__ int32_t tab[kTabSize];
-    if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
+    const uint8_t *__restrict__ ref, const uint32_t *__restrict__ ref4,
+    const uint32_t *__restrict__ qry4, ScoreParams sp) {
+    // pair scores indexed by r * 16 + q (codes 0..5 of the 4-bit copies)
+    __shared__ int32_t tab4[kTab4];
+    for (int i = threadIdx.x; i < kTab4; i += kThreads) {
+        const int r = i >> 4, q = i & 15;
+        tab4[i] = (r <= kCodeEdge && q <= kCodeEdge) ? sp.tab[(r << kRefShift) | q] : 0;
+    }
     __syncthreads();
     const uint32_t i = blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (i >= n_surv) return;
@@ -62,10 +68,10 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
     const bool bad = r > sp.n_ref || q > sp.n_qry;  // outside the sequences: empty walks
     int32_t R, L;
     uint32_t k, m;
-    const uint8_t *rr = ref + (bad ? sp.n_ref : r), *qr = qry + (bad ? sp.n_qry : q);
-    const uint8_t *rl = ref + (bad ? 0u : r), *ql = qry + (bad ? 0u : q);
-    exact_walk_tiles<+1, true, 8, true>(tab, rr, qr, sp.xdrop, INT32_MAX, R, k);
-    exact_walk_tiles<-1, true, 8, true>(tab, rl, ql, sp.xdrop, INT32_MAX, L, m);
+    exact_walk_tiles<+1, true, true>(tab4, ref4, qry4, kPad4 + (bad ? sp.n_ref : r),
+                                     kPad4 + (bad ? sp.n_qry : q), sp.xdrop, INT32_MAX, R, k);
+    exact_walk_tiles<-1, true, true>(tab4, ref4, qry4, kPad4 + (bad ? 0u : r),
+                                     kPad4 + (bad ? 0u : q), sp.xdrop, INT32_MAX, L, m);
     const int64_t total = (int64_t)L + (int64_t)R;
     bool ok = total >= (int64_t)sp.T;  // wave-uniform
     if (ok && sp.entropy_mode == 1) ok = entropy_accept(ref, r - m, m + k - 1u, total, sp.K);
@@ -84,11 +90,12 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
 
 hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint32_t n_surv,
                               hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
-                              const uint8_t *qry, const ScoreParams &sp, hipStream_t s) {
+                              const uint32_t *ref4, const uint32_t *qry4, const ScoreParams &sp,
+                              hipStream_t s) {
     if (n_surv == 0) return hipSuccess;
     const uint32_t blocks = (n_surv + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(k_materialize, dim3(blocks), dim3(kThreads), 0, s, anchors, ids, n_surv,
-                       hsp, status, ref, qry, sp);
+                       hsp, status, ref, ref4, qry4, sp);
     return hipGetLastError();
 }
 

@@ -60,102 +60,156 @@ __device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp
     ext_out = ext;
 }
 
-// The same walk with PER bases per lane (64 * PER-base tiles): lane l scores walk
-// positions base + PER*l .. base + PER*l + PER - 1.  Each lane forms its bases' local
-// prefix sums and prefix maxima; wave scans of the lane totals and of the lane maxima
-// (relative to the tile) give every base its running score and running best, so a base
-// drops when its running best exceeds its score by more than xdrop.  The first drop is
-// the lowest (lane, base) that drops; the best before it is the running best of the base
-// just before it, and with Ext its extent is the first base of the tile whose score equals
-// that best (a later base of the tile, past the drop, never counts).  With ReadAhead the
-// next tile's bases are read while this one is scored.  The walk reads at most
-// 64 * PER * (ReadAhead ? 2 : 1) - 1 bases past the first edge base, inside the padding.
-template <int D, bool Ext, int PER, bool ReadAhead>
-__device__ __forceinline__ void exact_walk_tiles(const int32_t *tab, const uint8_t *rp,
-                                                 const uint8_t *qp, int32_t xdrop, int32_t stop,
+// The same walk with eight bases per lane (512-base tiles), read from the 4-bit copies:
+// lane l scores walk positions base + 8l .. base + 8l + 7, one funnel-shifted dword of
+// each sequence (a right walk takes its nibbles in address order, a left walk in reverse),
+// and looks each pair up in tab4[r * 16 + q].
+//  - Each lane sums its bases' pair scores (kept in registers) and takes the maximum of
+//    its local prefix sums; wave scans of the lane sums and of the lane maxima (offset by
+//    the sums before the lane) give each lane its running score and running best at its
+//    first base.
+//  - A lane holds a drop iff its running drawdown, started from (running best - running
+//    score) at its first base, exceeds xdrop at one of its bases.  The drawdown is carried
+//    complemented, g = INT32_MAX - d, so that max(d - sigma, 0) is one saturating add.
+//  - Only in the tile of the first drop, the lowest dropping lane re-walks its bases to
+//    find the dropping base and the running best just before it (a dropping base never
+//    raises the best, since its score lies more than xdrop below it).
+//  - With Ext the extent is the first base whose running score equals the final best.
+//    Every earlier tile's scores stay below that best, so the base lies in the last tile
+//    that raised the best, before that tile's drop if it has one: the walk notes that
+//    tile, and after the walk reads it again and searches it once.
+// mr and mq are the padded nibble indices of the anchor's bases (reference end r at
+// kPad4 + r): a right walk starts there, a left walk just below.  With ReadAhead the next
+// tile's bases are read while this one is scored.  The walk reads at most
+// 64 * 8 * (ReadAhead ? 2 : 1) + 7 bases past the first edge base, inside the padding.
+template <int D, bool Ext, bool ReadAhead>
+__device__ __forceinline__ void exact_walk_tiles(const int32_t *tab4,
+                                                 const uint32_t *__restrict__ ref4,
+                                                 const uint32_t *__restrict__ qry4, uint32_t mr,
+                                                 uint32_t mq, int32_t xdrop, int32_t stop,
                                                  int32_t &best_out, uint32_t &ext_out) {
-    static_assert(PER >= 1 && 64 * PER * (ReadAhead ? 2 : 1) <= kPad,
+    constexpr int PER = 8;
+    static_assert(64 * PER * (ReadAhead ? 2 : 1) + 8 <= kPad4,
                   "a tile (and the one read ahead) must fit the edge padding");
     constexpr int32_t kLow = INT32_MIN / 2;  // below every running best (bests are >= 0)
     const int l = lane_id();
+    const int32_t glim = INT32_MAX - xdrop;  // a drop once the complemented drawdown < glim
     int32_t best = 0, carry = 0;
-    uint32_t ext = 0, base = 0;
-    auto load = [&](uint32_t b, uint32_t (&code)[PER]) {
+    uint32_t base = 0;
+    // the last tile that raised the best: its first walk position, the running score before
+    // it, and the positions of it that count (those before its drop)
+    uint32_t e_base = 0, e_lim = 0;
+    int32_t e_carry = 0;
+    // the lane's eight nibbles of one sequence: lowest padded nibble index a = m + w for a
+    // right walk, m - 1 - w - 7 for a left one (w = base + 8l); a % 8 is the same in every
+    // lane of the tile
+    auto nib8 = [&](const uint32_t *__restrict__ p, uint32_t m, uint32_t b) -> uint32_t {
+        const uint32_t a = D > 0 ? m + b + PER * l : m - b - PER * l - PER;
+        const uint32_t *w = p + (a >> 3);
+        return __builtin_amdgcn_alignbit(w[1], w[0], (a & 7u) * 4u);
+    };
+    // pair indices r * 16 + q of the lane's nibbles: nibble k's in byte k / 2 of
+    // code[k % 2] (even nibbles in code[0], odd ones in code[1])
+    auto load = [&](uint32_t b, uint32_t (&code)[2]) {
+        const uint32_t R = nib8(ref4, mr, b), Q = nib8(qry4, mq, b);
+        const uint32_t hi = 0xF0F0F0F0u;
+        code[0] = ((R << 4) & hi) | (Q & ~hi);
+        code[1] = (R & hi) | ((Q >> 4) & ~hi);
+    };
+    // the pair scores of the lane's bases in walk order
+    auto scores = [&](uint32_t (&code)[2], int32_t (&sg)[PER]) {
+        // keep the index words whole: each table address is one byte-select shift of them
+        asm volatile("" : "+v"(code[0]), "+v"(code[1]));
 #pragma unroll
         for (int j = 0; j < PER; j++) {
-            const int64_t w = (int64_t)b + PER * l + j;  // walk position
-            const int64_t off = D > 0 ? w : -w - 1;
-            code[j] = rp[off] | qp[off];
+            const int k = D > 0 ? j : PER - 1 - j;  // the nibble of walk position j
+            sg[j] = tab4[(code[k & 1] >> (8 * (k >> 1))) & 0xFFu];
         }
     };
-    uint32_t cur[PER];
+    uint32_t cur[2];
     load(0, cur);
     for (;;) {
-        uint32_t nxt[PER];
+        uint32_t nxt[2];
         if (ReadAhead) load(base + 64u * PER, nxt);
-        int32_t p[PER], m[PER];
-        int32_t acc = 0, mx = kLow;
+        int32_t sg[PER];
+        scores(cur, sg);
+        int32_t acc = 0, mx = kLow;  // local sum, and maximum of the local prefix sums
 #pragma unroll
         for (int j = 0; j < PER; j++) {
-            acc += tab[cur[j]];
-            p[j] = acc;
+            acc += sg[j];
             mx = max(mx, acc);
-            m[j] = mx;
         }
         const int32_t incl = wave_incl_sum(acc);  // tile score through this lane
-        const int32_t S = incl - acc;             // tile score before this lane
-        const int32_t lane_max = wave_incl_max(S + m[PER - 1]);
-        int32_t prev_max = __shfl_up(lane_max, 1, 64);  // best of the tile's earlier lanes
+        const int32_t C = carry + incl - acc;     // running score before this lane
+        const int32_t run_max = wave_incl_max(C + mx);
+        int32_t prev_max = __shfl_up(run_max, 1, 64);  // best of the tile's earlier lanes
         if (l == 0) prev_max = kLow;
-        const int32_t before = max(best, carry + prev_max);  // running best before this lane
-        int32_t sj[PER], rb[PER];
-        int fj = PER;  // this lane's first dropping base (PER: none)
+        const int32_t before = max(best, prev_max);  // running best before this lane
+        // the drawdown walk of this lane's bases, from before - C
+        int32_t g = INT32_MAX - (before - C), gmin = g;
 #pragma unroll
-        for (int j = PER - 1; j >= 0; j--) {
-            sj[j] = carry + S + p[j];
-            rb[j] = max(before, carry + S + m[j]);
-            if (rb[j] - sj[j] > xdrop) fj = j;
+        for (int j = 0; j < PER; j++) {
+            g = __builtin_elementwise_add_sat(g, sg[j]);
+            gmin = min(gmin, g);
         }
-        const uint64_t dl = __ballot(fj < PER);
-        int32_t tb;        // running best before the first drop, or at the tile's end
-        uint32_t limit;    // positions of the tile that count: [0, limit)
+        const uint64_t dl = __ballot(gmin < glim);
+        int32_t tb;              // running best before the first drop, or at the tile's end
+        uint32_t lim = 64u * PER;  // positions of the tile before its drop
         if (dl) {
             const int f = (int)__builtin_ctzll(dl);
-            const int ff = lane_value(fj, f);
-            // running best of the base before the drop: in lane f, or lane f - 1's last
-            int32_t rb_prev = rb[PER - 1];
+            // every lane re-walks its bases; the dropping lane's results are taken
+            int32_t sc = C, rbv = before, tbl = before;
+            int fj = PER;
 #pragma unroll
-            for (int j = 1; j < PER; j++)
-                if (fj == j) rb_prev = rb[j - 1];
-            if (ff > 0) tb = lane_value(rb_prev, f);
-            else if (f > 0) tb = lane_value(rb[PER - 1], f - 1);
-            else tb = best;
-            limit = (uint32_t)(PER * f + ff);
+            for (int j = 0; j < PER; j++) {
+                sc += sg[j];
+                rbv = max(rbv, sc);
+                const bool first = fj == PER && rbv - sc > xdrop;
+                fj = first ? j : fj;
+                tbl = first ? rbv : tbl;
+            }
+            lim = (uint32_t)(PER * f + lane_value(fj, f));
+            tb = lane_value(tbl, f);
         } else {
-            tb = max(best, carry + lane_value(lane_max, 63));
-            limit = 64u * PER;
+            tb = max(best, lane_value(run_max, 63));
         }
         if (tb > best) {
-            if (Ext) {
-                int gj = PER;  // this lane's first base reaching tb inside the limit
-#pragma unroll
-                for (int j = PER - 1; j >= 0; j--)
-                    if (sj[j] == tb && (uint32_t)(PER * l + j) < limit) gj = j;
-                const uint64_t gl = __ballot(gj < PER);
-                const int g = (int)__builtin_ctzll(gl);
-                ext = base + (uint32_t)(PER * g + lane_value(gj, g)) + 1u;
-            }
             best = tb;
+            e_base = base;
+            e_carry = carry;
+            e_lim = lim;
         }
         if (dl || best >= stop) break;
         carry += lane_value(incl, 63);
         base += 64u * PER;
         if (ReadAhead) {
-#pragma unroll
-            for (int j = 0; j < PER; j++) cur[j] = nxt[j];
+            cur[0] = nxt[0];
+            cur[1] = nxt[1];
         } else {
             load(base, cur);
         }
+    }
+    uint32_t ext = 0;
+    if (Ext && best > 0) {
+        // the first base of the noted tile, before its drop, whose running score is best
+        uint32_t code[2];
+        load(e_base, code);
+        int32_t sg[PER];
+        scores(code, sg);
+        int32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < PER; j++) acc += sg[j];
+        const int32_t C = e_carry + wave_incl_sum(acc) - acc;
+        int32_t sc = C;
+        int gj = PER;
+#pragma unroll
+        for (int j = 0; j < PER; j++) {
+            sc += sg[j];
+            gj = (gj == PER && sc == best && (uint32_t)(PER * l + j) < e_lim) ? j : gj;
+        }
+        const uint64_t hit = __ballot(gj < PER);
+        const int gl = (int)__builtin_ctzll(hit);
+        ext = e_base + (uint32_t)(PER * gl + lane_value(gj, gl)) + 1u;
     }
     best_out = best;
     ext_out = ext;
