@@ -632,3 +632,38 @@ def test_dedup_of_run_batch_records():
     want = oracle.dedup_records(acc)
     assert 0 < want.size < acc.size
     assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_materialize_every_anchor_near_the_ends(seed):
+    # the exact walks read the 4-bit copies with their edge padding: materialize every
+    # anchor (no gate) at and next to both ends of both sequences, past the ends, and on
+    # planted homologs (walks of hundreds of bases to both sides), and compare every
+    # record and status byte with the oracle
+    import torch
+    rng = np.random.default_rng(300 + seed)
+    ref, qry = random_pair(310 + seed, 2_000 + 900 * seed, 1_500 + 1_300 * seed, n_frac=0.04,
+                           plant=8, plant_len=(200, 900), identity=0.95)
+    p = params_of("11011", K=150)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    o, R, qc = oracle_pass(ref, qry, p)
+    past = np.asarray([(ref.size + 1) | (5 << 32), 9 | ((qry.size + 3) << 32)], np.uint64)
+    a = np.concatenate([_edge_anchors(rng, ref.size, qry.size, 3_000), past] +
+                       [c["anchors"][:2_000] for c in o["chunks"]])
+    ids = np.arange(a.size, dtype=np.uint32)
+    T = oracle.keep_threshold(p["hsp_threshold"])
+    oh, ost = oracle.materialize(a, ids, R.codes, qc, p["sub"], p["n_score"], p["xdrop"], T)
+    assert 0 < int(ost.sum()) < a.size
+    at = torch.from_numpy(a.view(np.int64)).cuda()
+    it = torch.from_numpy(ids.view(np.int32)).cuda()
+    hsp = torch.empty((a.size, 4), dtype=torch.int32, device="cuda")
+    st = torch.empty(a.size, dtype=torch.uint8, device="cuda")
+    eng.materialize(at, it, a.size, hsp, st)
+    gs = st.cpu().numpy()
+    gh = hsp.cpu().numpy().view(oracle.HSP_DTYPE).reshape(-1)
+    assert np.array_equal(gs, ost)
+    ok = ost == 1
+    bad = np.flatnonzero(gh[ok] != oh[ok])
+    assert bad.size == 0, f"{bad.size} records differ, first anchors {a[ok][bad[:5]]}"

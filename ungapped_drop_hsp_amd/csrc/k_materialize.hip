@@ -17,6 +17,7 @@ namespace {
 constexpr int kWaves = 1;  // one wave per workgroup: a finished walk frees its slot at once
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTab4 = 96;  // pair indices r * 16 + q for codes up to 5
+constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower on long walks)
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -68,9 +69,9 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
     const bool bad = r > sp.n_ref || q > sp.n_qry;  // outside the sequences: empty walks
     int32_t R, L;
     uint32_t k, m;
-    exact_walk_tiles<+1, true, true>(tab4, ref4, qry4, kPad4 + (bad ? sp.n_ref : r),
+    exact_walk_tiles<+1, true, kPer, true>(tab4, ref4, qry4, kPad4 + (bad ? sp.n_ref : r),
                                      kPad4 + (bad ? sp.n_qry : q), sp.xdrop, INT32_MAX, R, k);
-    exact_walk_tiles<-1, true, true>(tab4, ref4, qry4, kPad4 + (bad ? 0u : r),
+    exact_walk_tiles<-1, true, kPer, true>(tab4, ref4, qry4, kPad4 + (bad ? 0u : r),
                                      kPad4 + (bad ? 0u : q), sp.xdrop, INT32_MAX, L, m);
     const int64_t total = (int64_t)L + (int64_t)R;
     bool ok = total >= (int64_t)sp.T;  // wave-uniform

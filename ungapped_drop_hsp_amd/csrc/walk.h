@@ -60,10 +60,10 @@ __device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp
     ext_out = ext;
 }
 
-// The same walk with eight bases per lane (512-base tiles), read from the 4-bit copies:
-// lane l scores walk positions base + 8l .. base + 8l + 7, one funnel-shifted dword of
-// each sequence (a right walk takes its nibbles in address order, a left walk in reverse),
-// and looks each pair up in tab4[r * 16 + q].
+// The same walk with PER (8 or 16) bases per lane (64 * PER-base tiles), read from the
+// 4-bit copies: lane l scores walk positions base + PER*l .. base + PER*l + PER - 1, PER / 8
+// funnel-shifted dwords of each sequence (a right walk takes its nibbles in address
+// order, a left walk in reverse), and looks each pair up in tab4[r * 16 + q].
 //  - Each lane sums its bases' pair scores (kept in registers) and takes the maximum of
 //    its local prefix sums; wave scans of the lane sums and of the lane maxima (offset by
 //    the sums before the lane) give each lane its running score and running best at its
@@ -81,14 +81,15 @@ __device__ __forceinline__ void exact_walk(const int32_t *tab, const uint8_t *rp
 // mr and mq are the padded nibble indices of the anchor's bases (reference end r at
 // kPad4 + r): a right walk starts there, a left walk just below.  With ReadAhead the next
 // tile's bases are read while this one is scored.  The walk reads at most
-// 64 * 8 * (ReadAhead ? 2 : 1) + 7 bases past the first edge base, inside the padding.
-template <int D, bool Ext, bool ReadAhead>
+// 64 * PER * (ReadAhead ? 2 : 1) + 7 bases past the first edge base, inside the padding.
+template <int D, bool Ext, int PER, bool ReadAhead>
 __device__ __forceinline__ void exact_walk_tiles(const int32_t *tab4,
                                                  const uint32_t *__restrict__ ref4,
                                                  const uint32_t *__restrict__ qry4, uint32_t mr,
                                                  uint32_t mq, int32_t xdrop, int32_t stop,
                                                  int32_t &best_out, uint32_t &ext_out) {
-    constexpr int PER = 8;
+    static_assert(PER == 8 || PER == 16, "whole dwords of nibbles per lane");
+    constexpr int NW = PER / 8;  // dwords of each sequence per lane
     static_assert(64 * PER * (ReadAhead ? 2 : 1) + 8 <= kPad4,
                   "a tile (and the one read ahead) must fit the edge padding");
     constexpr int32_t kLow = INT32_MIN / 2;  // below every running best (bests are >= 0)
@@ -100,36 +101,48 @@ __device__ __forceinline__ void exact_walk_tiles(const int32_t *tab4,
     // it, and the positions of it that count (those before its drop)
     uint32_t e_base = 0, e_lim = 0;
     int32_t e_carry = 0;
-    // the lane's eight nibbles of one sequence: lowest padded nibble index a = m + w for a
-    // right walk, m - 1 - w - 7 for a left one (w = base + 8l); a % 8 is the same in every
-    // lane of the tile
-    auto nib8 = [&](const uint32_t *__restrict__ p, uint32_t m, uint32_t b) -> uint32_t {
+    // the lane's PER nibbles of one sequence, dword i holding nibbles 8i .. 8i + 7: lowest
+    // padded nibble index a = m + w for a right walk, m - 1 - w - (PER - 1) for a left one
+    // (w = base + PER*l); a % 8 is the same in every lane of the tile
+    auto nibs = [&](const uint32_t *__restrict__ p, uint32_t m, uint32_t b,
+                    uint32_t (&v)[NW]) {
         const uint32_t a = D > 0 ? m + b + PER * l : m - b - PER * l - PER;
         const uint32_t *w = p + (a >> 3);
-        return __builtin_amdgcn_alignbit(w[1], w[0], (a & 7u) * 4u);
+        uint32_t x[NW + 1];
+#pragma unroll
+        for (int i = 0; i <= NW; i++) x[i] = w[i];
+#pragma unroll
+        for (int i = 0; i < NW; i++) v[i] = __builtin_amdgcn_alignbit(x[i + 1], x[i], (a & 7u) * 4u);
     };
-    // pair indices r * 16 + q of the lane's nibbles: nibble k's in byte k / 2 of
-    // code[k % 2] (even nibbles in code[0], odd ones in code[1])
-    auto load = [&](uint32_t b, uint32_t (&code)[2]) {
-        const uint32_t R = nib8(ref4, mr, b), Q = nib8(qry4, mq, b);
+    // pair indices r * 16 + q of the lane's nibbles: nibble k's in byte (k % 8) / 2 of
+    // code[2 * (k / 8) + k % 2]
+    auto load = [&](uint32_t b, uint32_t (&code)[2 * NW]) {
+        uint32_t R[NW], Q[NW];
+        nibs(ref4, mr, b, R);
+        nibs(qry4, mq, b, Q);
         const uint32_t hi = 0xF0F0F0F0u;
-        code[0] = ((R << 4) & hi) | (Q & ~hi);
-        code[1] = (R & hi) | ((Q >> 4) & ~hi);
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            code[2 * i] = ((R[i] << 4) & hi) | (Q[i] & ~hi);
+            code[2 * i + 1] = (R[i] & hi) | ((Q[i] >> 4) & ~hi);
+        }
     };
     // the pair scores of the lane's bases in walk order
-    auto scores = [&](uint32_t (&code)[2], int32_t (&sg)[PER]) {
+    auto scores = [&](uint32_t (&code)[2 * NW], int32_t (&sg)[PER]) {
         // keep the index words whole: each table address is one byte-select shift of them
-        asm volatile("" : "+v"(code[0]), "+v"(code[1]));
+#pragma unroll
+        for (int i = 0; i < 2 * NW; i++) asm volatile("" : "+v"(code[i]));
 #pragma unroll
         for (int j = 0; j < PER; j++) {
             const int k = D > 0 ? j : PER - 1 - j;  // the nibble of walk position j
-            sg[j] = tab4[(code[k & 1] >> (8 * (k >> 1))) & 0xFFu];
+            const uint32_t word = code[2 * (k >> 3) + (k & 1)];
+            sg[j] = tab4[(word >> (8 * ((k & 7) >> 1))) & 0xFFu];
         }
     };
-    uint32_t cur[2];
+    uint32_t cur[2 * NW];
     load(0, cur);
     for (;;) {
-        uint32_t nxt[2];
+        uint32_t nxt[2 * NW];
         if (ReadAhead) load(base + 64u * PER, nxt);
         int32_t sg[PER];
         scores(cur, sg);
@@ -183,8 +196,8 @@ __device__ __forceinline__ void exact_walk_tiles(const int32_t *tab4,
         carry += lane_value(incl, 63);
         base += 64u * PER;
         if (ReadAhead) {
-            cur[0] = nxt[0];
-            cur[1] = nxt[1];
+#pragma unroll
+            for (int i = 0; i < 2 * NW; i++) cur[i] = nxt[i];
         } else {
             load(base, cur);
         }
@@ -192,7 +205,7 @@ __device__ __forceinline__ void exact_walk_tiles(const int32_t *tab4,
     uint32_t ext = 0;
     if (Ext && best > 0) {
         // the first base of the noted tile, before its drop, whose running score is best
-        uint32_t code[2];
+        uint32_t code[2 * NW];
         load(e_base, code);
         int32_t sg[PER];
         scores(code, sg);
