@@ -101,25 +101,29 @@ __device__ __forceinline__ void exact_walk_tiles(const int32_t *tab4,
     // it, and the positions of it that count (those before its drop)
     uint32_t e_base = 0, e_lim = 0;
     int32_t e_carry = 0;
-    // the lane's PER nibbles of one sequence, dword i holding nibbles 8i .. 8i + 7: lowest
-    // padded nibble index a = m + w for a right walk, m - 1 - w - (PER - 1) for a left one
-    // (w = base + PER*l); a % 8 is the same in every lane of the tile
-    auto nibs = [&](const uint32_t *__restrict__ p, uint32_t m, uint32_t b,
-                    uint32_t (&v)[NW]) {
-        const uint32_t a = D > 0 ? m + b + PER * l : m - b - PER * l - PER;
-        const uint32_t *w = p + (a >> 3);
+    // The lane's PER nibbles of one sequence in tile b, dword i holding nibbles 8i .. 8i + 7:
+    // their lowest padded nibble index is a0 + b for a right walk and a0 - b for a left one,
+    // with a0 = m + PER*l or m - PER*l - PER.  Tiles are whole dwords apart, so the funnel
+    // shift (a0 % 8 nibbles) and the lane's first dword are set once per walk.
+    const uint32_t ar = D > 0 ? mr + PER * l : mr - PER * l - PER;
+    const uint32_t aq = D > 0 ? mq + PER * l : mq - PER * l - PER;
+    const uint32_t *__restrict__ pr = ref4 + (ar >> 3);
+    const uint32_t *__restrict__ pq = qry4 + (aq >> 3);
+    const uint32_t shr = (ar & 7u) * 4u, shq = (aq & 7u) * 4u;
+    auto nibs = [&](const uint32_t *__restrict__ p0, uint32_t sh, uint32_t b, uint32_t (&v)[NW]) {
+        const uint32_t *w = D > 0 ? p0 + (b >> 3) : p0 - (b >> 3);
         uint32_t x[NW + 1];
 #pragma unroll
         for (int i = 0; i <= NW; i++) x[i] = w[i];
 #pragma unroll
-        for (int i = 0; i < NW; i++) v[i] = __builtin_amdgcn_alignbit(x[i + 1], x[i], (a & 7u) * 4u);
+        for (int i = 0; i < NW; i++) v[i] = __builtin_amdgcn_alignbit(x[i + 1], x[i], sh);
     };
     // pair indices r * 16 + q of the lane's nibbles: nibble k's in byte (k % 8) / 2 of
     // code[2 * (k / 8) + k % 2]
     auto load = [&](uint32_t b, uint32_t (&code)[2 * NW]) {
         uint32_t R[NW], Q[NW];
-        nibs(ref4, mr, b, R);
-        nibs(qry4, mq, b, Q);
+        nibs(pr, shr, b, R);
+        nibs(pq, shq, b, Q);
         const uint32_t hi = 0xF0F0F0F0u;
 #pragma unroll
         for (int i = 0; i < NW; i++) {
