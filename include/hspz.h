@@ -15,6 +15,11 @@
  *     hspz_materialize exact X-drop SegmentPair + status per id     (E.1 - E.5)
  *     hspz_compact_hsps accepted SegmentPairs in survivor order     (E.5)
  *
+ * hspz_find_hits_gate runs a chunk's expansion and gate as one call (the anchors are
+ * formed inside the gate), and hspz_run_batch runs the whole pass over a batch inside
+ * the library, leaving the accepted records in host memory (hspz_get_batch_records).
+ * hspz_dedup_records removes repeated accepted records on the host.
+ *
  * Conventions
  *  - Every function returns HSPZ_OK (0) or a negative HSPZ_E_* code; no exception or
  *    signal crosses the ABI.  On error, outputs are unspecified, every *n_out is set to
@@ -24,7 +29,10 @@
  *  - stream is a hipStream_t (NULL = the default stream).  Calls that return a count
  *    (hspz_plan, hspz_compact, hspz_compact_hsps) synchronise that stream; every other
  *    kernel-launching call is asynchronous on it.
- *  - An engine is not thread-safe: use one engine per host thread.
+ *  - An engine is not thread-safe: use one engine per host thread.  Its calls share the
+ *    engine's device scratch (the gate's deferred lists, compaction blocks, the bucketed
+ *    gate's sorted copy), so calls of one engine on different streams must not overlap:
+ *    give an engine one stream, or synchronise between streams.
  *  - Coordinates are 0-based.  Sequences are ASCII; A/C/G/T in either case are bases,
  *    every other byte is N.
  */
