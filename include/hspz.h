@@ -114,6 +114,14 @@ typedef struct {
  *                L2), widened to keep at most 256; n in 1..256 = at most n slices, each
  *                of the smallest power-of-two width that allows it.  Ignored by the
  *                other gate modes; never changes any output.
+ *  materialize_mode  how hspz_materialize walks ("E. X-drop materialization", E.1-E.3):
+ *                1 = one wave per survivor, each walk on its own; 2 = diagonal-shared
+ *                walks: survivors are sorted by diagonal, and a walk that reaches a
+ *                strictly new best at or past its neighbour's start takes the rest from
+ *                the neighbour (the walks coincide from there), so a stretch of a
+ *                diagonal shared by many survivors is walked about once; 0 = 2 for calls
+ *                of at least 65,536 survivors, else 1.  Every mode writes the same
+ *                records and status.
  */
 typedef struct {
     const char *seed_pattern;
@@ -128,6 +136,7 @@ typedef struct {
     int32_t gate_mode;
     int32_t entropy_mode;
     int32_t ref_buckets;
+    int32_t materialize_mode;
 } hspz_params;
 
 /* Create an engine on params->device and compute the keep threshold T once: the least

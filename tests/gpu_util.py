@@ -12,14 +12,16 @@ def require_gpu():
     return torch
 
 
-def engine(params, expand_mode=0, chunk_walk=0, max_hits=None, gate_mode=0, ref_buckets=0):
+def engine(params, expand_mode=0, chunk_walk=0, max_hits=None, gate_mode=0, ref_buckets=0,
+           materialize_mode=0):
     import ungapped_drop_hsp_amd as h
     return h.Engine(seed_pattern=params["seed_pattern"], sub=params["sub"],
                     n_score=params["n_score"], xdrop=params["xdrop"],
                     hsp_threshold=params["hsp_threshold"],
                     max_hits=params["max_hits"] if max_hits is None else max_hits,
                     expand_mode=expand_mode, chunk_walk=chunk_walk, gate_mode=gate_mode,
-                    entropy_mode=params.get("entropy_mode", 0), ref_buckets=ref_buckets)
+                    entropy_mode=params.get("entropy_mode", 0), ref_buckets=ref_buckets,
+                    materialize_mode=materialize_mode)
 
 
 def params_of(pattern, max_hits=0, sub=None, xdrop=910, K=3000, n_score=-100, entropy_mode=0):

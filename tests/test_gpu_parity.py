@@ -108,10 +108,11 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
-@pytest.mark.parametrize("expand_mode,gate_mode", [(0, 0), (1, 1), (2, 2), (0, 3), (0, 4)],
+@pytest.mark.parametrize("expand_mode,gate_mode,mat", [(0, 0, 0), (1, 1, 0), (2, 2, 0), (0, 3, 0),
+                                                        (0, 4, 0), (0, 0, 2)],
                          ids=["auto", "sparse-exact", "dense-window", "auto-window2",
-                              "bucketed"])
-def test_random_pass_parity(case, expand_mode, gate_mode):
+                              "bucketed", "shared-walks"])
+def test_random_pass_parity(case, expand_mode, gate_mode, mat):
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
     ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
                            identity=ident, gc=gc, alphabet_noise=True)
@@ -119,7 +120,7 @@ def test_random_pass_parity(case, expand_mode, gate_mode):
     o, _, _ = oracle_pass(ref, qry, p)
     # the bucketed gate over 16 reference slices (the automatic width is one slice here)
     eng = engine(p, expand_mode=expand_mode, gate_mode=gate_mode,
-                 ref_buckets=16 if gate_mode == 4 else 0)
+                 ref_buckets=16 if gate_mode == 4 else 0, materialize_mode=mat)
     r = gpu_full_pass(eng, ref, qry)
     assert_pass_equal(r, o)
 
@@ -226,11 +227,14 @@ def test_block_sizes_and_scores(xdrop, n_score):
     assert_pass_equal(gpu_full_pass(engine(p), ref, qry), o)
 
 
-def test_identical_sequences_long_walks():
+@pytest.mark.parametrize("mat", [1, 2], ids=["own-walks", "shared-walks"])
+def test_identical_sequences_long_walks(mat):
+    # every anchor of the main diagonal walks to both sequence ends; with shared walks
+    # each one merges into its neighbour's
     ref, _ = random_pair(10, 30_000, 1, gc=0.41)
     p = params_of(SEED_PATTERN, max_hits=100_000)
     o, _, _ = oracle_pass(ref, ref, p)
-    r = gpu_full_pass(engine(p), ref, ref)
+    r = gpu_full_pass(engine(p, materialize_mode=mat), ref, ref)
     assert_pass_equal(r, o)
     # the main diagonal's records span the whole sequence
     acc = np.concatenate([c["accepted"] for c in r["chunks"]])
@@ -371,18 +375,20 @@ def test_unaligned_buffers_and_out_of_range_anchors():
     assert np.array_equal(gh[:3], oh[:3])
 
 
+@pytest.mark.parametrize("mat", [0, 2], ids=["auto", "shared-walks"])
 @pytest.mark.parametrize("cfg", [0, 1])
-def test_config_full_parity(cfg):
+def test_config_full_parity(cfg, mat):
     w = build(cfg)
     p = w.params()
     o, _, _ = oracle_pass(w.ref, w.query, p)
-    r = gpu_full_pass(engine(p), w.ref, w.query)
+    r = gpu_full_pass(engine(p, materialize_mode=mat), w.ref, w.query)
     assert_pass_equal(r, o)
     print(f"config {cfg}: anchors {r['total']} survivors {r['n_surv']} accepted {r['n_acc']}")
 
 
+@pytest.mark.parametrize("mat", [1, 2], ids=["own-walks", "shared-walks"])
 @pytest.mark.parametrize("seed", range(3))
-def test_entropy_mode_parity(seed):
+def test_entropy_mode_parity(seed, mat):
     # planted homologs plus low-complexity copies, which the entropy-adjusted decision
     # rejects although their scores pass T
     ref, qry = random_pair(30 + seed, 20_000, 20_000, plant=40, plant_len=(60, 500),
@@ -398,7 +404,7 @@ def test_entropy_mode_parity(seed):
     n_surv = sum(c["ids"].size for c in o["chunks"])
     n_acc = sum(c["accepted"].size for c in o["chunks"])
     assert 0 < n_acc < n_surv
-    assert_pass_equal(gpu_full_pass(engine(p), ref, qry), o)
+    assert_pass_equal(gpu_full_pass(engine(p, materialize_mode=mat), ref, qry), o)
 
 
 def test_entropy_mode_config1():
@@ -634,8 +640,9 @@ def test_dedup_of_run_batch_records():
     assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
 
 
+@pytest.mark.parametrize("mat", [1, 2], ids=["own-walks", "shared-walks"])
 @pytest.mark.parametrize("seed", range(3))
-def test_materialize_every_anchor_near_the_ends(seed):
+def test_materialize_every_anchor_near_the_ends(seed, mat):
     # the exact walks read the 4-bit copies with their edge padding: materialize every
     # anchor (no gate) at and next to both ends of both sequences, past the ends, and on
     # planted homologs (walks of hundreds of bases to both sides), and compare every
@@ -645,7 +652,7 @@ def test_materialize_every_anchor_near_the_ends(seed):
     ref, qry = random_pair(310 + seed, 2_000 + 900 * seed, 1_500 + 1_300 * seed, n_frac=0.04,
                            plant=8, plant_len=(200, 900), identity=0.95)
     p = params_of("11011", K=150)
-    eng = engine(p)
+    eng = engine(p, materialize_mode=mat)
     eng.upload_reference(ref)
     eng.upload_query(qry)
     o, R, qc = oracle_pass(ref, qry, p)
@@ -667,3 +674,41 @@ def test_materialize_every_anchor_near_the_ends(seed):
     ok = ost == 1
     bad = np.flatnonzero(gh[ok] != oh[ok])
     assert bad.size == 0, f"{bad.size} records differ, first anchors {a[ok][bad[:5]]}"
+
+
+def test_shared_walks_on_tandem_repeats_and_duplicates():
+    # shared walks where they pay: a tandem array (thousands of survivors on a few
+    # diagonals, long chains of merges), plus every survivor listed twice (equal anchors
+    # never merge) and anchors in an arbitrary order; records against the oracle
+    import torch
+    rng = np.random.default_rng(77)
+    acgt = np.frombuffer(b"ACGT", np.uint8)
+    unit = acgt[rng.integers(0, 4, 97)]
+    arr = np.concatenate([unit] * 40).copy()
+    flip = rng.random(arr.size) < 0.05
+    arr[flip] = acgt[rng.integers(0, 4, int(flip.sum()))]
+    ref = np.concatenate([acgt[rng.integers(0, 4, 3_000)], arr, acgt[rng.integers(0, 4, 2_000)]])
+    qry = np.concatenate([acgt[rng.integers(0, 4, 1_000)], arr[500:], acgt[rng.integers(0, 4, 900)]])
+    p = params_of(SEED_PATTERN)
+    o, R, qc = oracle_pass(ref, qry, p)
+    a = np.concatenate([c["anchors"][c["ids"]] for c in o["chunks"]])
+    assert a.size > 2_000
+    a = np.concatenate([a, a[: a.size // 3]])
+    a = a[rng.permutation(a.size)]
+    T = oracle.keep_threshold(p["hsp_threshold"])
+    ids = np.arange(a.size, dtype=np.uint32)
+    oh, ost = oracle.materialize(a, ids, R.codes, qc, p["sub"], p["n_score"], p["xdrop"], T)
+    for mat in (1, 2):
+        eng = engine(p, materialize_mode=mat)
+        eng.upload_reference(ref)
+        eng.upload_query(qry)
+        at = torch.from_numpy(a.view(np.int64)).cuda()
+        it = torch.from_numpy(ids.view(np.int32)).cuda()
+        hsp = torch.empty((a.size, 4), dtype=torch.int32, device="cuda")
+        st = torch.empty(a.size, dtype=torch.uint8, device="cuda")
+        eng.materialize(at, it, a.size, hsp, st)
+        gs = st.cpu().numpy()
+        gh = hsp.cpu().numpy().view(oracle.HSP_DTYPE).reshape(-1)
+        assert np.array_equal(gs, ost), f"mode {mat}: status differs"
+        ok = ost == 1
+        assert np.array_equal(gh[ok], oh[ok]), f"mode {mat}: records differ"

@@ -49,7 +49,8 @@ class Params(ctypes.Structure):
                 ("hsp_threshold", ctypes.c_int32), ("expand_mode", ctypes.c_int32),
                 ("max_hits", ctypes.c_uint64), ("chunk_walk", ctypes.c_int32),
                 ("device", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
-                ("entropy_mode", ctypes.c_int32), ("ref_buckets", ctypes.c_int32)]
+                ("entropy_mode", ctypes.c_int32), ("ref_buckets", ctypes.c_int32),
+                ("materialize_mode", ctypes.c_int32)]
 
 
 class Chunk(ctypes.Structure):
@@ -169,14 +170,14 @@ class Engine:
     def __init__(self, seed_pattern: str, sub, n_score: int, xdrop: int, hsp_threshold: int,
                  max_hits: int = 0, expand_mode: int = 0, chunk_walk: int = 0,
                  device: int = 0, gate_mode: int = 0, entropy_mode: int = 0,
-                 ref_buckets: int = 0):
+                 ref_buckets: int = 0, materialize_mode: int = 0):
         self._pat = seed_pattern.encode()
         m = np.asarray(sub, dtype=np.int32).reshape(-1)
         if m.size != 16:
             raise ValueError("sub must hold 16 entries (4x4, ref row, query column)")
         p = Params(self._pat, (ctypes.c_int32 * 16)(*m.tolist()), n_score, xdrop,
                    hsp_threshold, expand_mode, max_hits, chunk_walk, device, gate_mode,
-                   entropy_mode, ref_buckets)
+                   entropy_mode, ref_buckets, materialize_mode)
         h = ctypes.c_void_p()
         rc = _lib.hspz_engine_create(ctypes.byref(p), ctypes.byref(h))
         if rc != HSPZ_OK:

@@ -322,6 +322,16 @@ Engine::~Engine() {
     dfree(d_blkoff);
     dfree(d_cblk);
     dfree(d_ctotal);
+    dfree(d_mka);
+    dfree(d_mva);
+    dfree(d_mkb);
+    dfree(d_mvb);
+    dfree(d_mhist);
+    dfree(d_mincl);
+    dfree(d_mside);
+    dfree(d_msum);
+    dfree(d_moff);
+    dfree(d_minfo);
     dfree(d_bsa);
     dfree(d_bsi);
     dfree(d_bhist);
@@ -390,6 +400,8 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "entropy_mode must be 0 or 1");
     if (p->ref_buckets < 0 || p->ref_buckets > 256)
         return fail(nullptr, HSPZ_E_INVALID, "ref_buckets must be in 0..256");
+    if (p->materialize_mode < 0 || p->materialize_mode > 2)
+        return fail(nullptr, HSPZ_E_INVALID, "materialize_mode must be 0, 1 or 2");
     if (p->gate_mode < 0 || p->gate_mode > 4)
         return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2, 3 or 4");
     int ndev = 0;
@@ -938,6 +950,113 @@ HSPZ_API int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t 
     return rc;
 }
 
+// Diagonal-shared materialization: calls of at least this many survivors take it in
+// materialize_mode 0 (below it the sort's fixed launches cost more than the walks save).
+constexpr uint64_t kMatSharedMin = 65536;
+
+// Scratch of the diagonal-shared materialization for n survivors.  The per-side arrays
+// (best, ext, term, ds, cnt, sum, pos: seven u32 each, plus the flag bytes) are carved out
+// of one allocation, each at a 16-byte aligned offset.
+static uint64_t mat_stride(uint64_t cap) { return (cap + 3) / 4 * 4; }  // u32 words per array
+static uint64_t mat_side_words(uint64_t cap) {
+    const uint64_t st = mat_stride(cap);
+    return (7 * st + st / 4 + 4 + 3) / 4 * 4;  // a multiple of 4 words: 16-byte aligned sides
+}
+
+static int ensure_mat(Engine *e, uint64_t n) {
+    if (n <= e->cap_mat && e->d_mka) return HSPZ_OK;
+    const uint64_t cap = std::max<uint64_t>({n, 4096, e->cap_mat + e->cap_mat / 4});
+    const uint64_t nh = 256ull * radix_blocks((uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull));
+    const uint64_t ns = (std::max(nh, cap) + kScanBlock - 1) / kScanBlock;
+    int rc;
+    if ((rc = dalloc(e, e->d_mka, cap)) || (rc = dalloc(e, e->d_mva, cap)) ||
+        (rc = dalloc(e, e->d_mkb, cap)) || (rc = dalloc(e, e->d_mvb, cap)) ||
+        (rc = dalloc(e, e->d_mhist, nh)) || (rc = dalloc(e, e->d_mincl, nh)) ||
+        (rc = dalloc(e, e->d_mside, 2 * mat_side_words(cap))) ||
+        (rc = dalloc(e, e->d_msum, ns)) || (rc = dalloc(e, e->d_moff, ns)) ||
+        (!e->d_minfo && (rc = dalloc(e, e->d_minfo, 1)))) {
+        e->cap_mat = 0;
+        return rc;
+    }
+    e->cap_mat = cap;
+    return HSPZ_OK;
+}
+
+static MatSide mat_side(Engine *e, int side) {
+    const uint64_t stride = mat_stride(e->cap_mat);
+    uint32_t *b = e->d_mside + (uint64_t)side * mat_side_words(e->cap_mat);
+    MatSide m;
+    m.best = reinterpret_cast<int32_t *>(b);
+    m.ext = b + stride;
+    m.term = b + 2 * stride;
+    m.ds = reinterpret_cast<int32_t *>(b + 3 * stride);
+    m.cnt = b + 4 * stride;
+    m.sum = b + 5 * stride;
+    m.pos = b + 6 * stride;
+    m.term8 = reinterpret_cast<uint8_t *>(b + 7 * stride);
+    return m;
+}
+
+// Inclusive prefix sum (modulo 2^32) of n u32 values into out (16-byte aligned), on the
+// materialization scratch.  in is written back unchanged.
+static int mat_scan(Engine *e, uint32_t *in, uint64_t n, uint32_t *out, hipStream_t s) {
+    if (n == 0) return HSPZ_OK;
+    HIP_TRY(e, launch_count_scan(nullptr, in, n, nullptr, in, nullptr, out, e->d_msum, s));
+    HIP_TRY(e, launch_scan_blocks(e->d_msum, (n + kScanBlock - 1) / kScanBlock, e->d_moff,
+                                  e->d_minfo, s));
+    HIP_TRY(e, launch_add_offsets(out, n, e->d_moff, s));
+    return HSPZ_OK;
+}
+
+static int bits_of(uint64_t v) {
+    int b = 1;
+    while (b < 64 && (v >> b)) b++;
+    return b;
+}
+
+// Stable LSD radix sort of (ka, va) by the low `bits` bits of ka; the result ends in
+// (ka, va) (the buffers are swapped as the passes go).
+static int mat_radix(Engine *e, uint32_t *&ka, uint32_t *&va, uint32_t *&kb, uint32_t *&vb,
+                     uint32_t n, int bits, hipStream_t s) {
+    const uint64_t nh = 256ull * radix_blocks(n);
+    int rc;
+    for (int shift = 0; shift < bits; shift += 8) {
+        HIP_TRY(e, launch_radix_hist(ka, n, shift, e->d_mhist, s));
+        if ((rc = mat_scan(e, e->d_mhist, nh, e->d_mincl, s))) return rc;
+        HIP_TRY(e, launch_radix_scatter(ka, va, n, shift, e->d_mincl, e->d_mhist, kb, vb, s));
+        std::swap(ka, kb);
+        std::swap(va, vb);
+    }
+    return HSPZ_OK;
+}
+
+static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32_t *d_ids,
+                              uint32_t n, hspz_segment_pair *d_hsp, uint8_t *d_status,
+                              hipStream_t s) {
+    int rc;
+    if ((rc = ensure_mat(e, n)) || (rc = ensure_compact(e, n))) return rc;
+    const uint32_t n_ref = (uint32_t)e->n_ref, n_qry = (uint32_t)e->n_qry;
+    uint32_t *ka = e->d_mka, *va = e->d_mva, *kb = e->d_mkb, *vb = e->d_mvb;
+    HIP_TRY(e, launch_mm_keys(d_anchors, d_ids, n, n_ref, n_qry, ka, va, s));
+    if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of(n_ref), s))) return rc;
+    HIP_TRY(e, launch_mm_diag(d_anchors, d_ids, va, n, n_ref, n_qry, ka, s));
+    if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of((uint64_t)n_ref + n_qry + 1), s)))
+        return rc;
+    const MatSide right = mat_side(e, 0), left = mat_side(e, 1);
+    HIP_TRY(e, launch_mm_walk(d_anchors, d_ids, ka, va, n, e->d_ref + kPad, e->d_qry + kPad,
+                              e->sp, right, left, s));
+    for (const MatSide &m : {right, left}) {
+        if ((rc = mat_scan(e, m.term, n, m.cnt, s)) ||
+            (rc = mat_scan(e, reinterpret_cast<uint32_t *>(m.ds), n, m.sum, s)))
+            return rc;
+        HIP_TRY(e, launch_compact(m.term8, n, e->d_cblk, e->d_ctotal + 12, m.pos, nullptr,
+                                  nullptr, n, s));
+    }
+    HIP_TRY(e, launch_mm_finish(d_anchors, d_ids, va, n, right, left, d_hsp, d_status,
+                                e->d_ref + kPad, e->sp, s));
+    return HSPZ_OK;
+}
+
 HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
                               const uint32_t *d_ids, uint64_t n_surv, hspz_segment_pair *d_hsp,
                               uint8_t *d_status, void *stream) {
@@ -950,6 +1069,12 @@ HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
         return fail(e, HSPZ_E_INVALID, "NULL buffer");
     int rc = set_device(e);
     if (rc) return rc;
+    // the diagonal keys r - q + n_qry must fit 32 bits for the shared walks
+    const bool fits = (uint64_t)e->n_ref + e->n_qry + 2 < 0xFFFFFFFFull;
+    const int mode = e->params.materialize_mode;
+    if (fits && n_surv && (mode == 2 || (mode == 0 && n_surv >= kMatSharedMin)))
+        return materialize_shared(e, d_anchors, d_ids, (uint32_t)n_surv, d_hsp, d_status,
+                                  as_stream(stream));
     HIP_TRY(e, launch_materialize(d_anchors, d_ids, (uint32_t)n_surv, d_hsp, d_status,
                                   e->d_ref + kPad, e->d_ref4, e->d_qry4, e->sp,
                                   as_stream(stream)));

@@ -1,5 +1,20 @@
 // Exact X-drop materialization ("E. X-drop materialization", E.1-E.5).
 //
+// Two ways to the same records:
+//  - k_materialize: one wave per survivor walks both sides on its own.
+//  - the diagonal-shared walks (k_mm_*), for calls with many survivors: survivors are
+//    sorted stably by reference end and then by diagonal, so each one's neighbours on
+//    its diagonal sit next to it.  One wave per survivor walks each side until its drop,
+//    or until it sets a strictly new best at or past its neighbour's start: from there
+//    the two walks are one (same later bases, same running best, same drop, and every
+//    base scored before lies below that best), so it stops and keeps its running score
+//    at the neighbour's start.  A side that merged takes the best of the first walk
+//    along its chain that ran to its drop, plus the summed scores of the starts in
+//    between, and that walk's extent plus the distance to it; prefix sums and the list
+//    of walks that ran to their drops give every survivor its chain end at once.  On
+//    tandem repeats, where thousands of survivors share a diagonal, this walks each
+//    stretch of the diagonal about once instead of once per survivor.
+//
 // One wave per survivor walks both sides with exact_walk_tiles over the 4-bit copies
 // (512-base tiles, eight bases per lane, the next tile read ahead; earliest endpoints).  With the
 // entropy-adjusted decision on, the wave then counts the record's reference bases
@@ -87,7 +102,184 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
     }
 }
 
+// Sort keys: the reference end (first pass) and the diagonal r - q + n_qry (second pass,
+// stable); an anchor outside the sequences gets the diagonal key n_ref + n_qry + 1 and never
+// merges.
+__global__ __launch_bounds__(256) void k_mm_keys(const uint64_t *__restrict__ anchors,
+                                                 const uint32_t *__restrict__ ids, uint32_t n,
+                                                 uint32_t n_ref, uint32_t n_qry,
+                                                 uint32_t *__restrict__ key_r,
+                                                 uint32_t *__restrict__ val) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const uint64_t a = anchors[ids[i]];
+    const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
+    key_r[i] = (r > n_ref || q > n_qry) ? 0u : r;
+    val[i] = i;
+}
+
+__device__ __forceinline__ uint32_t diag_key(uint64_t a, uint32_t n_ref, uint32_t n_qry) {
+    const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
+    return (r > n_ref || q > n_qry) ? n_ref + n_qry + 1u : r - q + n_qry;
+}
+
+__global__ __launch_bounds__(256) void k_mm_diag(const uint64_t *__restrict__ anchors,
+                                                 const uint32_t *__restrict__ ids,
+                                                 const uint32_t *__restrict__ val, uint32_t n,
+                                                 uint32_t n_ref, uint32_t n_qry,
+                                                 uint32_t *__restrict__ key_d) {
+    const uint32_t s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= n) return;
+    key_d[s] = diag_key(anchors[ids[val[s]]], n_ref, n_qry);
+}
+
+// One wave per sorted survivor: its right walk (neighbour: the next survivor on the
+// diagonal) and its left walk (neighbour: the previous one).
+__global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anchors,
+                                                const uint32_t *__restrict__ ids,
+                                                const uint32_t *__restrict__ key_d,
+                                                const uint32_t *__restrict__ val, uint32_t n,
+                                                const uint8_t *__restrict__ ref,
+                                                const uint8_t *__restrict__ qry, ScoreParams sp,
+                                                MatSide right, MatSide left) {
+    __shared__ int32_t tab[kTabSize];
+    if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
+    __syncthreads();
+    const uint32_t s = blockIdx.x;
+    if (s >= n) return;
+    const uint64_t a = anchors[ids[val[s]]];
+    const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
+    const bool bad = r > sp.n_ref || q > sp.n_qry;
+    const uint32_t key = key_d[s];
+    uint32_t wr = UINT32_MAX, wl = UINT32_MAX;  // neighbours' starts as walk indices
+    if (!bad) {
+        if (s + 1 < n && key_d[s + 1] == key) {
+            const uint32_t rn = (uint32_t)anchors[ids[val[s + 1]]];
+            if (rn > r) wr = rn - 1u - r;
+        }
+        if (s > 0 && key_d[s - 1] == key) {
+            const uint32_t rp = (uint32_t)anchors[ids[val[s - 1]]];
+            if (rp < r) wl = r - 1u - rp;
+        }
+    }
+    const uint8_t *rr = ref + (bad ? sp.n_ref : r), *qr = qry + (bad ? sp.n_qry : q);
+    const uint8_t *rl = ref + (bad ? 0u : r), *ql = qry + (bad ? 0u : q);
+    int32_t R, L, dr, dlft;
+    uint32_t k, m;
+    bool mr, ml;
+    exact_walk_merge<+1, true>(tab, rr, qr, sp.xdrop, wr, R, k, mr, dr);
+    exact_walk_merge<-1, true>(tab, rl, ql, sp.xdrop, wl, L, m, ml, dlft);
+    if (lane_id() == 0) {
+        right.best[s] = R;
+        right.ext[s] = k;
+        right.term[s] = mr ? 0u : 1u;
+        right.term8[s] = mr ? 0 : 1;
+        right.ds[s] = mr ? dr : 0;
+        left.best[s] = L;
+        left.ext[s] = m;
+        left.term[s] = ml ? 0u : 1u;
+        left.term8[s] = ml ? 0 : 1;
+        left.ds[s] = ml ? dlft : 0;
+    }
+}
+
+// One thread per sorted survivor: each side's best and extent through its chain, then the
+// record and status at the survivor's own index.  A right chain runs to the first
+// drop-ended walk t >= s (its bests add the scores at the starts s .. t - 1); a left chain
+// to the last drop-ended walk t <= s (scores at starts t + 1 .. s).
+__global__ __launch_bounds__(256) void k_mm_finish(
+    const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ ids,
+    const uint32_t *__restrict__ val, uint32_t n, MatSide right, MatSide left,
+    hspz_segment_pair *__restrict__ hsp, uint8_t *__restrict__ status, int32_t T) {
+    const uint32_t s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= n) return;
+    const uint32_t j = val[s];
+    const uint64_t a = anchors[ids[j]];
+    const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
+    int32_t R = right.best[s], L = left.best[s];
+    uint32_t k = right.ext[s], m = left.ext[s];
+    // Every chain ends at a drop-ended walk (a diagonal's last survivor has no right
+    // neighbour, its first none on the left); the index checks only keep a broken chain
+    // inside the lists.
+    const uint32_t nr = right.cnt[n - 1], nl = left.cnt[n - 1];
+    if (!right.term[s] && right.cnt[s] < nr) {
+        const uint32_t t = right.pos[right.cnt[s]];  // first drop-ended walk after s
+        const uint32_t rt = (uint32_t)anchors[ids[val[t]]];
+        // sum of the scores at the starts s .. t - 1: exclusive prefix at t minus at s
+        const uint32_t ex_t = right.sum[t] - (uint32_t)right.ds[t];
+        const uint32_t ex_s = right.sum[s] - (uint32_t)right.ds[s];
+        R = right.best[t] + (int32_t)(ex_t - ex_s);
+        k = right.ext[t] + (rt - r);
+    }
+    if (!left.term[s] && left.cnt[s] >= 1u && left.cnt[s] <= nl) {
+        const uint32_t t = left.pos[left.cnt[s] - 1u];  // last drop-ended walk before s
+        const uint32_t rt = (uint32_t)anchors[ids[val[t]]];
+        L = left.best[t] + (int32_t)(left.sum[s] - left.sum[t]);
+        m = left.ext[t] + (r - rt);
+    }
+    const int64_t total = (int64_t)L + (int64_t)R;
+    hspz_segment_pair rec;
+    rec.ref_start = r - m;
+    rec.query_start = q - m;
+    rec.len = m + k - 1u;
+    rec.score = (int32_t)total;
+    hsp[j] = rec;
+    status[j] = total >= (int64_t)T ? 1 : 0;
+}
+
+// The entropy-adjusted decision for the records that reach T: one wave per survivor.
+__global__ __launch_bounds__(64) void k_mm_entropy(const hspz_segment_pair *__restrict__ hsp,
+                                                   uint8_t *__restrict__ status, uint32_t n,
+                                                   const uint8_t *__restrict__ ref,
+                                                   ScoreParams sp) {
+    const uint32_t i = blockIdx.x;
+    if (i >= n || status[i] == 0) return;  // uniform
+    const hspz_segment_pair rec = hsp[i];
+    const bool ok = entropy_accept(ref, rec.ref_start, rec.len, rec.score, sp.K);
+    if (lane_id() == 0) status[i] = ok ? 1 : 0;
+}
+
 }  // namespace
+
+hipError_t launch_mm_keys(const uint64_t *anchors, const uint32_t *ids, uint32_t n,
+                          uint32_t n_ref, uint32_t n_qry, uint32_t *key_r, uint32_t *val,
+                          hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_mm_keys, dim3((n + 255) / 256), dim3(256), 0, s, anchors, ids, n, n_ref,
+                       n_qry, key_r, val);
+    return hipGetLastError();
+}
+
+hipError_t launch_mm_diag(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+                          uint32_t n, uint32_t n_ref, uint32_t n_qry, uint32_t *key_d,
+                          hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_mm_diag, dim3((n + 255) / 256), dim3(256), 0, s, anchors, ids, val, n,
+                       n_ref, n_qry, key_d);
+    return hipGetLastError();
+}
+
+hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const uint32_t *key_d,
+                          const uint32_t *val, uint32_t n, const uint8_t *ref,
+                          const uint8_t *qry, const ScoreParams &sp, const MatSide &right,
+                          const MatSide &left, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_mm_walk, dim3(n), dim3(64), 0, s, anchors, ids, key_d, val, n, ref, qry,
+                       sp, right, left);
+    return hipGetLastError();
+}
+
+hipError_t launch_mm_finish(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+                            uint32_t n, const MatSide &right, const MatSide &left,
+                            hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
+                            const ScoreParams &sp, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_mm_finish, dim3((n + 255) / 256), dim3(256), 0, s, anchors, ids, val, n,
+                       right, left, hsp, status, sp.T);
+    if (sp.entropy_mode == 1)
+        hipLaunchKernelGGL(k_mm_entropy, dim3(n), dim3(64), 0, s, hsp, status, n, ref, sp);
+    return hipGetLastError();
+}
 
 hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint32_t n_surv,
                               hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
