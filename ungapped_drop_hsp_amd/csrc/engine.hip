@@ -9,6 +9,7 @@
 #include <unordered_set>
 
 #include "hspz_internal.h"
+#include "mat_shared.h"
 
 #define HSPZ_API extern "C" __attribute__((visibility("default")))
 
@@ -322,16 +323,19 @@ Engine::~Engine() {
     dfree(d_blkoff);
     dfree(d_cblk);
     dfree(d_ctotal);
-    dfree(d_mka);
-    dfree(d_mva);
-    dfree(d_mkb);
-    dfree(d_mvb);
-    dfree(d_mhist);
-    dfree(d_mincl);
-    dfree(d_mside);
-    dfree(d_msum);
-    dfree(d_moff);
-    dfree(d_minfo);
+    if (mat) {
+        dfree(mat->ka);
+        dfree(mat->va);
+        dfree(mat->kb);
+        dfree(mat->vb);
+        dfree(mat->hist);
+        dfree(mat->incl);
+        dfree(mat->side);
+        dfree(mat->sum);
+        dfree(mat->off);
+        dfree(mat->info);
+        delete mat;
+    }
     dfree(d_bsa);
     dfree(d_bsi);
     dfree(d_bhist);
@@ -964,27 +968,32 @@ static uint64_t mat_side_words(uint64_t cap) {
 }
 
 static int ensure_mat(Engine *e, uint64_t n) {
-    if (n <= e->cap_mat && e->d_mka) return HSPZ_OK;
-    const uint64_t cap = std::max<uint64_t>({n, 4096, e->cap_mat + e->cap_mat / 4});
+    if (!e->mat) {
+        e->mat = new (std::nothrow) MatScratch();
+        if (!e->mat) return fail(e, HSPZ_E_NOMEM, "out of host memory");
+    }
+    MatScratch &m = *e->mat;
+    if (n <= m.cap && m.ka) return HSPZ_OK;
+    const uint64_t cap = std::max<uint64_t>({n, 4096, m.cap + m.cap / 4});
     const uint64_t nh = 256ull * radix_blocks((uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull));
     const uint64_t ns = (std::max(nh, cap) + kScanBlock - 1) / kScanBlock;
     int rc;
-    if ((rc = dalloc(e, e->d_mka, cap)) || (rc = dalloc(e, e->d_mva, cap)) ||
-        (rc = dalloc(e, e->d_mkb, cap)) || (rc = dalloc(e, e->d_mvb, cap)) ||
-        (rc = dalloc(e, e->d_mhist, nh)) || (rc = dalloc(e, e->d_mincl, nh)) ||
-        (rc = dalloc(e, e->d_mside, 2 * mat_side_words(cap))) ||
-        (rc = dalloc(e, e->d_msum, ns)) || (rc = dalloc(e, e->d_moff, ns)) ||
-        (!e->d_minfo && (rc = dalloc(e, e->d_minfo, 1)))) {
-        e->cap_mat = 0;
+    if ((rc = dalloc(e, m.ka, cap)) || (rc = dalloc(e, m.va, cap)) ||
+        (rc = dalloc(e, m.kb, cap)) || (rc = dalloc(e, m.vb, cap)) ||
+        (rc = dalloc(e, m.hist, nh)) || (rc = dalloc(e, m.incl, nh)) ||
+        (rc = dalloc(e, m.side, 2 * mat_side_words(cap))) ||
+        (rc = dalloc(e, m.sum, ns)) || (rc = dalloc(e, m.off, ns)) ||
+        (!m.info && (rc = dalloc(e, m.info, 1)))) {
+        m.cap = 0;
         return rc;
     }
-    e->cap_mat = cap;
+    m.cap = cap;
     return HSPZ_OK;
 }
 
 static MatSide mat_side(Engine *e, int side) {
-    const uint64_t stride = mat_stride(e->cap_mat);
-    uint32_t *b = e->d_mside + (uint64_t)side * mat_side_words(e->cap_mat);
+    const uint64_t stride = mat_stride(e->mat->cap);
+    uint32_t *b = e->mat->side + (uint64_t)side * mat_side_words(e->mat->cap);
     MatSide m;
     m.best = reinterpret_cast<int32_t *>(b);
     m.ext = b + stride;
@@ -1001,10 +1010,10 @@ static MatSide mat_side(Engine *e, int side) {
 // materialization scratch.  in is written back unchanged.
 static int mat_scan(Engine *e, uint32_t *in, uint64_t n, uint32_t *out, hipStream_t s) {
     if (n == 0) return HSPZ_OK;
-    HIP_TRY(e, launch_count_scan(nullptr, in, n, nullptr, in, nullptr, out, e->d_msum, s));
-    HIP_TRY(e, launch_scan_blocks(e->d_msum, (n + kScanBlock - 1) / kScanBlock, e->d_moff,
-                                  e->d_minfo, s));
-    HIP_TRY(e, launch_add_offsets(out, n, e->d_moff, s));
+    MatScratch &m = *e->mat;
+    HIP_TRY(e, launch_count_scan(nullptr, in, n, nullptr, in, nullptr, out, m.sum, s));
+    HIP_TRY(e, launch_scan_blocks(m.sum, (n + kScanBlock - 1) / kScanBlock, m.off, m.info, s));
+    HIP_TRY(e, launch_add_offsets(out, n, m.off, s));
     return HSPZ_OK;
 }
 
@@ -1021,9 +1030,9 @@ static int mat_radix(Engine *e, uint32_t *&ka, uint32_t *&va, uint32_t *&kb, uin
     const uint64_t nh = 256ull * radix_blocks(n);
     int rc;
     for (int shift = 0; shift < bits; shift += 8) {
-        HIP_TRY(e, launch_radix_hist(ka, n, shift, e->d_mhist, s));
-        if ((rc = mat_scan(e, e->d_mhist, nh, e->d_mincl, s))) return rc;
-        HIP_TRY(e, launch_radix_scatter(ka, va, n, shift, e->d_mincl, e->d_mhist, kb, vb, s));
+        HIP_TRY(e, launch_radix_hist(ka, n, shift, e->mat->hist, s));
+        if ((rc = mat_scan(e, e->mat->hist, nh, e->mat->incl, s))) return rc;
+        HIP_TRY(e, launch_radix_scatter(ka, va, n, shift, e->mat->incl, e->mat->hist, kb, vb, s));
         std::swap(ka, kb);
         std::swap(va, vb);
     }
@@ -1036,7 +1045,7 @@ static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32
     int rc;
     if ((rc = ensure_mat(e, n)) || (rc = ensure_compact(e, n))) return rc;
     const uint32_t n_ref = (uint32_t)e->n_ref, n_qry = (uint32_t)e->n_qry;
-    uint32_t *ka = e->d_mka, *va = e->d_mva, *kb = e->d_mkb, *vb = e->d_mvb;
+    uint32_t *ka = e->mat->ka, *va = e->mat->va, *kb = e->mat->kb, *vb = e->mat->vb;
     HIP_TRY(e, launch_mm_keys(d_anchors, d_ids, n, n_ref, n_qry, ka, va, s));
     if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of(n_ref), s))) return rc;
     HIP_TRY(e, launch_mm_diag(d_anchors, d_ids, va, n, n_ref, n_qry, ka, s));

@@ -187,33 +187,6 @@ hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint
                               hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
                               const uint32_t *ref4, const uint32_t *qry4, const ScoreParams &sp,
                               hipStream_t s);
-// Diagonal-shared materialization (k_materialize.hip), sequenced by the engine: sort keys,
-// a stable radix sort by reference end then by diagonal, the walks, scans of their
-// results, and the records.  Per-side walk results live in sorted order.
-struct MatSide {
-    int32_t *best;
-    uint32_t *ext;
-    uint32_t *term;   // 1: the walk ran to its drop; 0: it merged into its neighbour's
-    uint8_t *term8;   // the same as flag bytes
-    int32_t *ds;      // its running score at the neighbour's start (0 if it ran to its drop)
-    uint32_t *cnt;    // inclusive scan of term
-    uint32_t *sum;    // inclusive scan of ds, modulo 2^32
-    uint32_t *pos;    // sorted positions of the walks that ran to their drops
-};
-hipError_t launch_mm_keys(const uint64_t *anchors, const uint32_t *ids, uint32_t n,
-                          uint32_t n_ref, uint32_t n_qry, uint32_t *key_r, uint32_t *val,
-                          hipStream_t s);
-hipError_t launch_mm_diag(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
-                          uint32_t n, uint32_t n_ref, uint32_t n_qry, uint32_t *key_d,
-                          hipStream_t s);
-hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const uint32_t *key_d,
-                          const uint32_t *val, uint32_t n, const uint8_t *ref,
-                          const uint8_t *qry, const ScoreParams &sp, const MatSide &right,
-                          const MatSide &left, hipStream_t s);
-hipError_t launch_mm_finish(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
-                            uint32_t n, const MatSide &right, const MatSide &left,
-                            hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
-                            const ScoreParams &sp, hipStream_t s);
 // Stable compaction: count non-zero bytes per block, scan block counts on the device
 // (total -> *d_total), then emit either the indices (ids != nullptr) or the selected
 // 16-byte records (rec_in/rec_out).
@@ -227,6 +200,8 @@ hipError_t launch_walk_steps(const uint64_t *anchors, uint32_t n, const uint8_t 
 uint32_t walk_steps_blocks(uint32_t n);
 
 // ---- engine ----------------------------------------------------------------------------
+struct MatScratch;
+
 struct Engine {
     hspz_params params{};
     std::string pattern;
@@ -291,16 +266,8 @@ struct Engine {
     PlanInfo *d_binfo = nullptr;
     uint64_t cap_bucket = 0;
 
-    // diagonal-shared materialization scratch, for cap_mat survivors: sort keys and values
-    // (ping-pong), radix digit counts and their scan, both sides' results, and the block
-    // sums and offsets of its scans
-    uint32_t *d_mka = nullptr, *d_mva = nullptr, *d_mkb = nullptr, *d_mvb = nullptr;
-    uint32_t *d_mhist = nullptr, *d_mincl = nullptr;
-    uint32_t *d_mside = nullptr;  // both sides' arrays, carved out of one allocation
-    uint64_t *d_msum = nullptr;
-    uint32_t *d_moff = nullptr;
-    PlanInfo *d_minfo = nullptr;
-    uint64_t cap_mat = 0;
+    // diagonal-shared materialization scratch (mat_shared.h), made on first use
+    MatScratch *mat = nullptr;
 
     // compaction scratch
     uint32_t *d_cblk = nullptr;

@@ -22,7 +22,9 @@
 #include <climits>
 
 #include "hspz_internal.h"
+#include "mat_shared.h"
 #include "walk.h"
+#include "walk_merge.h"
 #include "wave.h"
 
 namespace hspz {

@@ -1,0 +1,49 @@
+// Diagonal-shared materialization ("E. X-drop materialization", E.1-E.5): the kernels in
+// k_materialize.hip, sequenced by the engine (sort keys, a stable radix sort by reference
+// end then by diagonal, the walks, scans of their results, the records), and the
+// engine's scratch for them.  Per-side walk results live in sorted order.
+#pragma once
+
+#include "hspz_internal.h"
+
+namespace hspz {
+
+// Scratch for cap survivors: sort keys and values (ping-pong), radix digit counts and
+// their scan, both sides' results (carved out of one allocation), and the block sums and
+// offsets of its scans.
+struct MatScratch {
+    uint32_t *ka = nullptr, *va = nullptr, *kb = nullptr, *vb = nullptr;
+    uint32_t *hist = nullptr, *incl = nullptr;
+    uint32_t *side = nullptr;
+    uint64_t *sum = nullptr;
+    uint32_t *off = nullptr;
+    PlanInfo *info = nullptr;
+    uint64_t cap = 0;
+};
+
+struct MatSide {
+    int32_t *best;
+    uint32_t *ext;
+    uint32_t *term;   // 1: the walk ran to its drop; 0: it merged into its neighbour's
+    uint8_t *term8;   // the same as flag bytes
+    int32_t *ds;      // its running score at the neighbour's start (0 if it ran to its drop)
+    uint32_t *cnt;    // inclusive scan of term
+    uint32_t *sum;    // inclusive scan of ds, modulo 2^32
+    uint32_t *pos;    // sorted positions of the walks that ran to their drops
+};
+hipError_t launch_mm_keys(const uint64_t *anchors, const uint32_t *ids, uint32_t n,
+                          uint32_t n_ref, uint32_t n_qry, uint32_t *key_r, uint32_t *val,
+                          hipStream_t s);
+hipError_t launch_mm_diag(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+                          uint32_t n, uint32_t n_ref, uint32_t n_qry, uint32_t *key_d,
+                          hipStream_t s);
+hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const uint32_t *key_d,
+                          const uint32_t *val, uint32_t n, const uint8_t *ref,
+                          const uint8_t *qry, const ScoreParams &sp, const MatSide &right,
+                          const MatSide &left, hipStream_t s);
+hipError_t launch_mm_finish(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+                            uint32_t n, const MatSide &right, const MatSide &left,
+                            hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
+                            const ScoreParams &sp, hipStream_t s);
+
+}  // namespace hspz
