@@ -214,17 +214,19 @@ def test_query_batches_parity():
         assert_pass_equal(gpu_full_pass(eng, ref, qry, seed_range=(lo, hi)), o)
 
 
+@pytest.mark.parametrize("mat", [0, 2], ids=["default-walks", "shared-walks"])
 @pytest.mark.parametrize("xdrop,n_score", [(910, -100), (400, -100), (150, 30), (60, -20),
                                            (0, -100)])
-def test_block_sizes_and_scores(xdrop, n_score):
-    # small X forces 4-, 2- and 1-base gate blocks; a positive N score is allowed too
+def test_block_sizes_and_scores(xdrop, n_score, mat):
+    # small X forces 4-, 2- and 1-base gate blocks (and shared walks without their
+    # eight-base lane stage); a positive N score is allowed too
     sub = np.asarray(HOXD70, np.int32).copy()
     sub[0, 1], sub[1, 0] = 40, -90  # asymmetric: ref row, query column
     ref, qry = random_pair(9, 15_000, 15_000, plant=30, plant_len=(50, 400), identity=0.9,
                            n_frac=0.03)
     p = params_of("11011", sub=sub, xdrop=xdrop, K=400, n_score=n_score)
     o, _, _ = oracle_pass(ref, qry, p)
-    assert_pass_equal(gpu_full_pass(engine(p), ref, qry), o)
+    assert_pass_equal(gpu_full_pass(engine(p, materialize_mode=mat), ref, qry), o)
 
 
 @pytest.mark.parametrize("mat", [1, 2], ids=["own-walks", "shared-walks"])

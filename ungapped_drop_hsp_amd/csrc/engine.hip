@@ -334,6 +334,8 @@ Engine::~Engine() {
         dfree(mat->sum);
         dfree(mat->off);
         dfree(mat->info);
+        dfree(mat->list);
+        dfree(mat->lcnt);
         delete mat;
     }
     dfree(d_bsa);
@@ -983,7 +985,8 @@ static int ensure_mat(Engine *e, uint64_t n) {
         (rc = dalloc(e, m.hist, nh)) || (rc = dalloc(e, m.incl, nh)) ||
         (rc = dalloc(e, m.side, 2 * mat_side_words(cap))) ||
         (rc = dalloc(e, m.sum, ns)) || (rc = dalloc(e, m.off, ns)) ||
-        (!m.info && (rc = dalloc(e, m.info, 1)))) {
+        (rc = dalloc(e, m.list, 2 * cap)) || (!m.info && (rc = dalloc(e, m.info, 1))) ||
+        (!m.lcnt && (rc = dalloc(e, m.lcnt, 2)))) {
         m.cap = 0;
         return rc;
     }
@@ -1046,14 +1049,16 @@ static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32
     if ((rc = ensure_mat(e, n)) || (rc = ensure_compact(e, n))) return rc;
     const uint32_t n_ref = (uint32_t)e->n_ref, n_qry = (uint32_t)e->n_qry;
     uint32_t *ka = e->mat->ka, *va = e->mat->va, *kb = e->mat->kb, *vb = e->mat->vb;
-    HIP_TRY(e, launch_mm_keys(d_anchors, d_ids, n, n_ref, n_qry, ka, va, s));
+    HIP_TRY(e, launch_mm_keys(d_anchors, d_ids, n, n_ref, n_qry, ka, va, e->mat->lcnt, s));
     if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of(n_ref), s))) return rc;
     HIP_TRY(e, launch_mm_diag(d_anchors, d_ids, va, n, n_ref, n_qry, ka, s));
     if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of((uint64_t)n_ref + n_qry + 1), s)))
         return rc;
     const MatSide right = mat_side(e, 0), left = mat_side(e, 1);
+    // the lane stage needs exact eight-base blocks, as the windowed gate does
     HIP_TRY(e, launch_mm_walk(d_anchors, d_ids, ka, va, n, e->d_ref + kPad, e->d_qry + kPad,
-                              e->sp, right, left, s));
+                              e->d_ref4, e->d_qry4, e->sp, right, left, e->block_bases == 8,
+                              e->mat->list, e->mat->lcnt, s));
     for (const MatSide &m : {right, left}) {
         if ((rc = mat_scan(e, m.term, n, m.cnt, s)) ||
             (rc = mat_scan(e, reinterpret_cast<uint32_t *>(m.ds), n, m.sum, s)))

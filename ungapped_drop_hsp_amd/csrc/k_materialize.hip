@@ -19,6 +19,7 @@
 // (512-base tiles, eight bases per lane, the next tile read ahead; earliest endpoints).  With the
 // entropy-adjusted decision on, the wave then counts the record's reference bases
 // (entropy_accept).  Lane 0 stores the 16-byte record and the status.
+#include <algorithm>
 #include <climits>
 
 #include "hspz_internal.h"
@@ -35,6 +36,9 @@ constexpr int kWaves = 1;  // one wave per workgroup: a finished walk frees its 
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTab4 = 96;  // pair indices r * 16 + q for codes up to 5
 constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower on long walks)
+// Window of the shared walks' lane stage, in blocks of eight bases per side: about 1% of
+// the walks on dense tandem repeats run past 96 bases.
+constexpr int kLaneBlocks = 12;
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -111,8 +115,10 @@ __global__ __launch_bounds__(256) void k_mm_keys(const uint64_t *__restrict__ an
                                                  const uint32_t *__restrict__ ids, uint32_t n,
                                                  uint32_t n_ref, uint32_t n_qry,
                                                  uint32_t *__restrict__ key_r,
-                                                 uint32_t *__restrict__ val) {
+                                                 uint32_t *__restrict__ val,
+                                                 uint32_t *__restrict__ lcnt) {
     const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i < 2) lcnt[i] = 0;  // the lane stage's deferred-walk counts
     if (i >= n) return;
     const uint64_t a = anchors[ids[i]];
     const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
@@ -135,8 +141,181 @@ __global__ __launch_bounds__(256) void k_mm_diag(const uint64_t *__restrict__ an
     key_d[s] = diag_key(anchors[ids[val[s]]], n_ref, n_qry);
 }
 
+// Sorted survivor s: its anchor and the walk indices of its neighbours' starts on its
+// diagonal (UINT32_MAX for none).  The right neighbour is the next survivor on the
+// diagonal (its right walk starts at base rn, i.e. after walk index rn - 1 - r of this
+// one); the left neighbour is the previous one (its left walk starts below base rp, walk
+// index r - 1 - rp of this one).  A neighbour at the same reference end (a duplicate
+// anchor) is none.
+struct MmAnchor {
+    uint32_t r, q, wr, wl;
+    bool bad;  // outside the sequences: both walks are empty
+};
+
+__device__ __forceinline__ MmAnchor mm_anchor(const uint64_t *__restrict__ anchors,
+                                              const uint32_t *__restrict__ ids,
+                                              const uint32_t *__restrict__ key_d,
+                                              const uint32_t *__restrict__ val, uint32_t n,
+                                              uint32_t s, const ScoreParams &sp) {
+    MmAnchor A;
+    const uint64_t a = anchors[ids[val[s]]];
+    A.r = (uint32_t)a;
+    A.q = (uint32_t)(a >> 32);
+    A.bad = A.r > sp.n_ref || A.q > sp.n_qry;
+    A.wr = UINT32_MAX;
+    A.wl = UINT32_MAX;
+    if (!A.bad) {
+        const uint32_t key = key_d[s];
+        if (s + 1 < n && key_d[s + 1] == key) {
+            const uint32_t rn = (uint32_t)anchors[ids[val[s + 1]]];
+            if (rn > A.r) A.wr = rn - 1u - A.r;
+        }
+        if (s > 0 && key_d[s - 1] == key) {
+            const uint32_t rp = (uint32_t)anchors[ids[val[s - 1]]];
+            if (rp < A.r) A.wl = A.r - 1u - rp;
+        }
+    }
+    return A;
+}
+
+__device__ __forceinline__ void mm_store(const MatSide &m, uint32_t s, int32_t best, uint32_t ext,
+                                         bool merged, int32_t ds) {
+    m.best[s] = best;
+    m.ext[s] = ext;
+    m.term[s] = merged ? 0u : 1u;
+    m.term8[s] = merged ? 0 : 1;
+    m.ds[s] = merged ? ds : 0;
+}
+
+// The merge walk of one lane, in blocks of eight bases read from the 4-bit copies, for at
+// most NB blocks.  Block k holds walk positions 8k .. 8k + 7: a right walk's nibbles
+// mr + 8k .. mr + 8k + 7 (mr the padded nibble index of the anchor's first base), a left
+// walk's mr - 8 - 8k .. mr - 1 - 8k in reverse.  Each base updates the running score,
+// the running best with its earliest extent, the largest drawdown, and at walk index wm
+// the running score (ds) and the best before that base.  Every lane runs whole blocks:
+// eight-base blocks are exact when 7 * (largest pair score) <= xdrop, since a walk that
+// has dropped cannot climb back to its best inside the same block, so a block's final
+// best and extent are those before its drop, and a block has a strict new best at or
+// past wm (a merge) only if no drop came first.  At a block's end the walk merged if its
+// best rose above the best before wm (or above the block's starting best once wm lies
+// behind), and dropped if the drawdown passed xdrop; a merge takes precedence, being
+// the earlier event.  Returns false if the walk did neither within the window; the
+// caller then walks it again in full.  Reads at most 8 * NB + 16 nibbles from mr on
+// either side, inside the edge padding.
+template <int D, int NB>
+__device__ __forceinline__ bool lane_merge_walk(const int32_t *tab4,
+                                                const uint32_t *__restrict__ ref4,
+                                                const uint32_t *__restrict__ qry4, uint32_t mr,
+                                                uint32_t mq, int32_t xdrop, uint32_t wm,
+                                                int32_t &best, uint32_t &ext, bool &merged,
+                                                int32_t &ds) {
+    static_assert(8 * NB + 16 <= kPad4, "the window must stay inside the edge padding");
+    const uint32_t ar = D > 0 ? mr : mr - 8u, aq = D > 0 ? mq : mq - 8u;
+    const uint32_t *__restrict__ pr = ref4 + (ar >> 3);
+    const uint32_t *__restrict__ pq = qry4 + (aq >> 3);
+    const uint32_t shr = (ar & 7u) * 4u, shq = (aq & 7u) * 4u;
+    // block k's nibbles are the funnel of dwords p[D * k] (low) and p[D * k + 1] (high)
+    uint32_t r0 = pr[0], r1 = pr[1], q0 = pq[0], q1 = pq[1];
+    int32_t s = 0;
+    best = 0;
+    ext = 0;
+    merged = false;
+    ds = 0;
+    for (int k = 0; k < NB; k++) {
+        const uint32_t rn = D > 0 ? pr[k + 2] : pr[-(k + 1)];  // the next block's new dword
+        const uint32_t qn = D > 0 ? pq[k + 2] : pq[-(k + 1)];
+        const uint32_t R = __builtin_amdgcn_alignbit(r1, r0, shr);
+        const uint32_t Q = __builtin_amdgcn_alignbit(q1, q0, shq);
+        const uint32_t hi = 0xF0F0F0F0u;
+        // pair indices r * 16 + q: nibble j's in byte j / 2 of c[j % 2]
+        const uint32_t c[2] = {((R << 4) & hi) | (Q & ~hi), (R & hi) | ((Q >> 4) & ~hi)};
+        const uint32_t b0 = 8u * (uint32_t)k;
+        const int32_t best0 = best;
+        int32_t bpre = best, dd = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int nib = D > 0 ? j : 7 - j;
+            const int32_t sg = tab4[(c[nib & 1] >> (8 * (nib >> 1))) & 0xFFu];
+            const uint32_t i = b0 + (uint32_t)j;
+            s += sg;
+            const bool at = i == wm;
+            bpre = at ? best : bpre;
+            ds = at ? s : ds;
+            ext = s > best ? i + 1u : ext;
+            best = max(best, s);
+            dd = max(dd, best - s);
+        }
+        const int32_t thr = wm < b0 ? best0 : (wm < b0 + 8u ? bpre : INT32_MAX);
+        if (best > thr) {
+            merged = true;
+            return true;
+        }
+        if (dd > xdrop) return true;
+        if (D > 0) {
+            r0 = r1;
+            r1 = rn;
+            q0 = q1;
+            q1 = qn;
+        } else {
+            r1 = r0;
+            r0 = rn;
+            q1 = q0;
+            q0 = qn;
+        }
+    }
+    return false;
+}
+
+// Lane stage of the diagonal-shared walks: one lane per sorted survivor walks both sides
+// with lane_merge_walk and stores what it finished; walks still running at the window's
+// end go to a list (right walks from list[0], left walks from list[n]; counts in lcnt),
+// each wave reserving its share with one atomic per side.
+template <int NB>
+__global__ __launch_bounds__(256) void k_mm_lanes(
+    const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ ids,
+    const uint32_t *__restrict__ key_d, const uint32_t *__restrict__ val, uint32_t n,
+    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, ScoreParams sp,
+    MatSide right, MatSide left, uint32_t *__restrict__ list, uint32_t *__restrict__ lcnt) {
+    __shared__ int32_t tab4[kTab4];
+    for (int i = threadIdx.x; i < kTab4; i += 256) {
+        const int r = i >> 4, q = i & 15;
+        tab4[i] = (r <= kCodeEdge && q <= kCodeEdge) ? sp.tab[(r << kRefShift) | q] : 0;
+    }
+    __syncthreads();
+    const uint32_t s = blockIdx.x * 256 + threadIdx.x;
+    const bool live = s < n;
+    MmAnchor A{};
+    if (live) A = mm_anchor(anchors, ids, key_d, val, n, s, sp);
+    bool open[2] = {false, false};
+#pragma unroll
+    for (int side = 0; side < 2; side++) {
+        if (live) {
+            int32_t best, ds;
+            uint32_t ext;
+            bool merged, done;
+            if (side == 0)
+                done = lane_merge_walk<+1, NB>(tab4, ref4, qry4, kPad4 + (A.bad ? sp.n_ref : A.r),
+                                               kPad4 + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr,
+                                               best, ext, merged, ds);
+            else
+                done = lane_merge_walk<-1, NB>(tab4, ref4, qry4, kPad4 + (A.bad ? 0u : A.r),
+                                               kPad4 + (A.bad ? 0u : A.q), sp.xdrop, A.wl, best,
+                                               ext, merged, ds);
+            if (done) mm_store(side == 0 ? right : left, s, best, ext, merged, ds);
+            open[side] = !done;
+        }
+        const uint64_t m = __ballot(open[side]);
+        if (m) {
+            uint32_t at = 0;
+            if (lane_id() == 0) at = atomicAdd(&lcnt[side], (uint32_t)__popcll(m));
+            at = __shfl(at, 0, 64);
+            if (open[side]) list[(uint64_t)side * n + at + lane_rank(m)] = s;
+        }
+    }
+}
+
 // One wave per sorted survivor: its right walk (neighbour: the next survivor on the
-// diagonal) and its left walk (neighbour: the previous one).
+// diagonal) and its left walk (neighbour: the previous one), each a one-wave merge walk.
 __global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anchors,
                                                 const uint32_t *__restrict__ ids,
                                                 const uint32_t *__restrict__ key_d,
@@ -149,39 +328,52 @@ __global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anc
     __syncthreads();
     const uint32_t s = blockIdx.x;
     if (s >= n) return;
-    const uint64_t a = anchors[ids[val[s]]];
-    const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
-    const bool bad = r > sp.n_ref || q > sp.n_qry;
-    const uint32_t key = key_d[s];
-    uint32_t wr = UINT32_MAX, wl = UINT32_MAX;  // neighbours' starts as walk indices
-    if (!bad) {
-        if (s + 1 < n && key_d[s + 1] == key) {
-            const uint32_t rn = (uint32_t)anchors[ids[val[s + 1]]];
-            if (rn > r) wr = rn - 1u - r;
-        }
-        if (s > 0 && key_d[s - 1] == key) {
-            const uint32_t rp = (uint32_t)anchors[ids[val[s - 1]]];
-            if (rp < r) wl = r - 1u - rp;
-        }
-    }
-    const uint8_t *rr = ref + (bad ? sp.n_ref : r), *qr = qry + (bad ? sp.n_qry : q);
-    const uint8_t *rl = ref + (bad ? 0u : r), *ql = qry + (bad ? 0u : q);
+    const MmAnchor A = mm_anchor(anchors, ids, key_d, val, n, s, sp);
+    const uint8_t *rr = ref + (A.bad ? sp.n_ref : A.r), *qr = qry + (A.bad ? sp.n_qry : A.q);
+    const uint8_t *rl = ref + (A.bad ? 0u : A.r), *ql = qry + (A.bad ? 0u : A.q);
     int32_t R, L, dr, dlft;
     uint32_t k, m;
     bool mr, ml;
-    exact_walk_merge<+1, true>(tab, rr, qr, sp.xdrop, wr, R, k, mr, dr);
-    exact_walk_merge<-1, true>(tab, rl, ql, sp.xdrop, wl, L, m, ml, dlft);
+    exact_walk_merge<+1, true>(tab, rr, qr, sp.xdrop, A.wr, R, k, mr, dr);
+    exact_walk_merge<-1, true>(tab, rl, ql, sp.xdrop, A.wl, L, m, ml, dlft);
     if (lane_id() == 0) {
-        right.best[s] = R;
-        right.ext[s] = k;
-        right.term[s] = mr ? 0u : 1u;
-        right.term8[s] = mr ? 0 : 1;
-        right.ds[s] = mr ? dr : 0;
-        left.best[s] = L;
-        left.ext[s] = m;
-        left.term[s] = ml ? 0u : 1u;
-        left.term8[s] = ml ? 0 : 1;
-        left.ds[s] = ml ? dlft : 0;
+        mm_store(right, s, R, k, mr, dr);
+        mm_store(left, s, L, m, ml, dlft);
+    }
+}
+
+// The walks the lane stage left open: one wave per listed walk (right walks first), a
+// fixed grid striding over the counts read on the device.
+__global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ anchors,
+                                                 const uint32_t *__restrict__ ids,
+                                                 const uint32_t *__restrict__ key_d,
+                                                 const uint32_t *__restrict__ val, uint32_t n,
+                                                 const uint8_t *__restrict__ ref,
+                                                 const uint8_t *__restrict__ qry, ScoreParams sp,
+                                                 MatSide right, MatSide left,
+                                                 const uint32_t *__restrict__ list,
+                                                 const uint32_t *__restrict__ lcnt) {
+    __shared__ int32_t tab[kTabSize];
+    if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
+    __syncthreads();
+    const uint32_t cr = lcnt[0];
+    const uint64_t total = (uint64_t)cr + lcnt[1];
+    const uint64_t nw = (uint64_t)gridDim.x * 4;
+    for (uint64_t t = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < total; t += nw) {
+        const bool rt = t < cr;
+        const uint32_t s = rt ? list[t] : list[(uint64_t)n + (t - cr)];
+        const MmAnchor A = mm_anchor(anchors, ids, key_d, val, n, s, sp);
+        int32_t best, ds;
+        uint32_t ext;
+        bool merged;
+        if (rt)
+            exact_walk_merge<+1, true>(tab, ref + (A.bad ? sp.n_ref : A.r),
+                                       qry + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr, best, ext,
+                                       merged, ds);
+        else
+            exact_walk_merge<-1, true>(tab, ref + (A.bad ? 0u : A.r), qry + (A.bad ? 0u : A.q),
+                                       sp.xdrop, A.wl, best, ext, merged, ds);
+        if (lane_id() == 0) mm_store(rt ? right : left, s, best, ext, merged, ds);
     }
 }
 
@@ -245,10 +437,10 @@ __global__ __launch_bounds__(64) void k_mm_entropy(const hspz_segment_pair *__re
 
 hipError_t launch_mm_keys(const uint64_t *anchors, const uint32_t *ids, uint32_t n,
                           uint32_t n_ref, uint32_t n_qry, uint32_t *key_r, uint32_t *val,
-                          hipStream_t s) {
+                          uint32_t *lcnt, hipStream_t s) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_mm_keys, dim3((n + 255) / 256), dim3(256), 0, s, anchors, ids, n, n_ref,
-                       n_qry, key_r, val);
+                       n_qry, key_r, val, lcnt);
     return hipGetLastError();
 }
 
@@ -263,11 +455,20 @@ hipError_t launch_mm_diag(const uint64_t *anchors, const uint32_t *ids, const ui
 
 hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const uint32_t *key_d,
                           const uint32_t *val, uint32_t n, const uint8_t *ref,
-                          const uint8_t *qry, const ScoreParams &sp, const MatSide &right,
-                          const MatSide &left, hipStream_t s) {
+                          const uint8_t *qry, const uint32_t *ref4, const uint32_t *qry4,
+                          const ScoreParams &sp, const MatSide &right, const MatSide &left,
+                          bool lanes, uint32_t *list, uint32_t *lcnt, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_mm_walk, dim3(n), dim3(64), 0, s, anchors, ids, key_d, val, n, ref, qry,
-                       sp, right, left);
+    if (!lanes) {
+        hipLaunchKernelGGL(k_mm_walk, dim3(n), dim3(64), 0, s, anchors, ids, key_d, val, n, ref,
+                           qry, sp, right, left);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_mm_lanes<kLaneBlocks>, dim3((n + 255) / 256), dim3(256), 0, s, anchors,
+                       ids, key_d, val, n, ref4, qry4, sp, right, left, list, lcnt);
+    const uint64_t grid = std::min<uint64_t>((2ull * n + 3) / 4, 2048);
+    hipLaunchKernelGGL(k_mm_list, dim3((uint32_t)grid), dim3(256), 0, s, anchors, ids, key_d, val,
+                       n, ref, qry, sp, right, left, list, lcnt);
     return hipGetLastError();
 }
 

@@ -9,8 +9,8 @@
 namespace hspz {
 
 // Scratch for cap survivors: sort keys and values (ping-pong), radix digit counts and
-// their scan, both sides' results (carved out of one allocation), and the block sums and
-// offsets of its scans.
+// their scan, both sides' results (carved out of one allocation), the block sums and
+// offsets of its scans, and the lane stage's list of open walks.
 struct MatScratch {
     uint32_t *ka = nullptr, *va = nullptr, *kb = nullptr, *vb = nullptr;
     uint32_t *hist = nullptr, *incl = nullptr;
@@ -18,6 +18,8 @@ struct MatScratch {
     uint64_t *sum = nullptr;
     uint32_t *off = nullptr;
     PlanInfo *info = nullptr;
+    uint32_t *list = nullptr;  // walks the lane stage left open (2 * cap)
+    uint32_t *lcnt = nullptr;  // their counts, right and left
     uint64_t cap = 0;
 };
 
@@ -33,14 +35,19 @@ struct MatSide {
 };
 hipError_t launch_mm_keys(const uint64_t *anchors, const uint32_t *ids, uint32_t n,
                           uint32_t n_ref, uint32_t n_qry, uint32_t *key_r, uint32_t *val,
-                          hipStream_t s);
+                          uint32_t *lcnt, hipStream_t s);
 hipError_t launch_mm_diag(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
                           uint32_t n, uint32_t n_ref, uint32_t n_qry, uint32_t *key_d,
                           hipStream_t s);
+// The walks: with lanes, a lane stage over eight-base blocks (exact only when
+// 7 * (largest pair score) <= xdrop) plus one wave per walk it left open, listed in list
+// (2 * n entries) with counts in lcnt (cleared by launch_mm_keys); else one wave per
+// survivor.
 hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const uint32_t *key_d,
                           const uint32_t *val, uint32_t n, const uint8_t *ref,
-                          const uint8_t *qry, const ScoreParams &sp, const MatSide &right,
-                          const MatSide &left, hipStream_t s);
+                          const uint8_t *qry, const uint32_t *ref4, const uint32_t *qry4,
+                          const ScoreParams &sp, const MatSide &right, const MatSide &left,
+                          bool lanes, uint32_t *list, uint32_t *lcnt, hipStream_t s);
 hipError_t launch_mm_finish(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
                             uint32_t n, const MatSide &right, const MatSide &left,
                             hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
