@@ -8,6 +8,7 @@
 #include <new>
 #include <unordered_set>
 
+#include "engine.h"
 #include "hspz_internal.h"
 #include "mat_shared.h"
 
@@ -352,13 +353,18 @@ Engine::~Engine() {
         dfree(rb_flags[b]);
         dfree(rb_ids[b]);
     }
+    if (copy_s) (void)hipStreamSynchronize(copy_s);
     dfree(rb_hsp);
-    dfree(rb_out);
+    dfree(rb_out[0]);
+    dfree(rb_out[1]);
     dfree(rb_status);
     for (hipEvent_t ev : gate_ev)
         if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : count_ev)
         if (ev) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : copied_ev)
+        if (ev) (void)hipEventDestroy(ev);
+    if (copy_s) (void)hipStreamDestroy(copy_s);
     if (h_pinned) (void)hipHostFree(h_pinned);
     if (h_plan) (void)hipHostFree(h_plan);
     if (h_rec) (void)hipHostFree(h_rec);
@@ -1126,8 +1132,8 @@ static int ensure_run_buffers(Engine *e, uint64_t n, uint64_t ns) {
     }
     if (ns > e->rb_cap_s || !e->rb_hsp) {
         const uint64_t cap = std::max<uint64_t>({ns, 1024, e->rb_cap_s + e->rb_cap_s / 4});
-        if ((rc = dalloc(e, e->rb_hsp, cap)) || (rc = dalloc(e, e->rb_out, cap)) ||
-            (rc = dalloc(e, e->rb_status, cap + 16))) {
+        if ((rc = dalloc(e, e->rb_hsp, cap)) || (rc = dalloc(e, e->rb_out[0], cap)) ||
+            (rc = dalloc(e, e->rb_out[1], cap)) || (rc = dalloc(e, e->rb_status, cap + 16))) {
             e->rb_cap_s = 0;
             return rc;
         }
@@ -1147,6 +1153,7 @@ static int ensure_record_staging(Engine *e, uint64_t n, uint64_t keep, hipStream
                     (unsigned long long)cap);
     if (e->h_rec) {
         HIP_TRY(e, hipStreamSynchronize(s));  // copies into the old staging have landed
+        if (e->copy_s) HIP_TRY(e, hipStreamSynchronize(e->copy_s));
         if (keep) memcpy(p, e->h_rec, keep * sizeof(hspz_segment_pair));
         (void)hipHostFree(e->h_rec);
     }
@@ -1205,6 +1212,17 @@ HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed
         return rc;
     for (hipEvent_t &ev : e->count_ev)
         if (!ev) HIP_TRY(e, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    for (hipEvent_t &ev : e->copied_ev)
+        if (!ev) HIP_TRY(e, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    if (!e->copy_s) HIP_TRY(e, hipStreamCreateWithFlags(&e->copy_s, hipStreamNonBlocking));
+    // every return below, error or not, first lets the record copies land
+    struct CopyDrain {
+        Engine *e;
+        ~CopyDrain() {
+            (void)hipStreamSynchronize(e->copy_s);
+            e->copy_pending[0] = e->copy_pending[1] = false;
+        }
+    } drain{e};
     if (time_gate)
         for (hipEvent_t &ev : e->gate_ev)
             if (!ev) HIP_TRY(e, hipEventCreate(&ev));
@@ -1212,7 +1230,9 @@ HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed
     // One stream, queued one chunk ahead: chunk c + 1's expansion+gate and survivor
     // compaction are queued before the host waits on chunk c's counts, so the GPU has work
     // while the host reads them.  Chunk c uses buffer set c & 1; stream order keeps every
-    // read of a set ahead of the next write to it.
+    // read of a set ahead of the next write to it.  Chunk c's accepted records go to the
+    // host on copy_s, behind its record count, while the next chunks run; the compaction
+    // of chunk c + 2 into the same record buffer waits for that copy.
     auto gate = [&](uint32_t c) -> int {
         const int b = c & 1;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[2 * b], s));
@@ -1240,27 +1260,39 @@ HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed
             stats->gate_ms += ms;
             stats->gate_calls++;
         }
-        if (ns > e->rb_cap_s) {  // the survivor buffers grow only once the stream is idle
+        if (ns > e->rb_cap_s) {  // the survivor buffers grow only once both streams are idle
             HIP_TRY(e, hipStreamSynchronize(s));
+            HIP_TRY(e, hipStreamSynchronize(e->copy_s));
+            e->copy_pending[0] = e->copy_pending[1] = false;
             if ((rc = ensure_run_buffers(e, maxn, ns))) return rc;
         }
         if ((rc = hspz_materialize(engine, e->rb_anchors[b], e->rb_ids[b], ns, e->rb_hsp,
                                    e->rb_status, stream)))
             return rc;
-        if ((rc = count_queue(e, e->rb_status, ns, nullptr, e->rb_hsp, e->rb_out, e->rb_cap_s, 1,
-                              s)))
+        if (e->copy_pending[b]) {  // chunk c - 2's records are still being read out of it
+            HIP_TRY(e, hipStreamWaitEvent(s, e->copied_ev[b], 0));
+            e->copy_pending[b] = false;
+        }
+        if ((rc = count_queue(e, e->rb_status, ns, nullptr, e->rb_hsp, e->rb_out[b],
+                              e->rb_cap_s, 1, s)))
             return rc;
         if (c + 1 < nch && (rc = survivors(c + 1))) return rc;
         if ((rc = count_wait(e, 1, e->rb_cap_s, &na))) return rc;
         if (na) {
             if ((rc = ensure_record_staging(e, acc + na, acc, s))) return rc;
-            HIP_TRY(e, hipMemcpyAsync(e->h_rec + acc, e->rb_out, na * sizeof(hspz_segment_pair),
-                                      hipMemcpyDeviceToHost, s));
+            // count_ev[1] stands behind this chunk's record compaction
+            HIP_TRY(e, hipStreamWaitEvent(e->copy_s, e->count_ev[1], 0));
+            HIP_TRY(e, hipMemcpyAsync(e->h_rec + acc, e->rb_out[b],
+                                      na * sizeof(hspz_segment_pair), hipMemcpyDeviceToHost,
+                                      e->copy_s));
+            HIP_TRY(e, hipEventRecord(e->copied_ev[b], e->copy_s));
+            e->copy_pending[b] = true;
         }
         stats->n_survivors += ns;
         acc += na;
     }
     HIP_TRY(e, hipStreamSynchronize(s));
+    HIP_TRY(e, hipStreamSynchronize(e->copy_s));
     stats->n_accepted = acc;
     e->h_rec_n = acc;
     return HSPZ_OK;
