@@ -120,8 +120,9 @@ typedef struct {
  *                strictly new best at or past its neighbour's start takes the rest from
  *                the neighbour (the walks coincide from there), so a stretch of a
  *                diagonal shared by many survivors is walked about once; 0 = 2 for calls
- *                of at least 65,536 survivors, else 1.  Every mode writes the same
- *                records and status.
+ *                of at least 65,536 survivors, else 1.  Mode 2 needs
+ *                n_ref + n_qry + 2 < 2^32 (32-bit diagonal keys) and takes mode 1
+ *                otherwise.  Every mode writes the same records and status.
  */
 typedef struct {
     const char *seed_pattern;
@@ -277,7 +278,10 @@ typedef struct {
  * "E. X-drop materialization"), with the same kernels and the same records.  The chunk
  * buffers are the engine's own (grown as needed); the accepted records of every chunk,
  * in chunk order, are copied to pinned host memory the engine owns, from where
- * hspz_get_batch_records reads them.  With time_gate != 0 each expansion-and-gate call
+ * hspz_get_batch_records reads them.  Those copies run on a second stream that the
+ * engine creates (default priority), ordered behind each chunk's records by events, so
+ * that they overlap the next chunks' kernels; the call returns once every copy has
+ * landed, also on error.  With time_gate != 0 each expansion-and-gate call
  * (hspz_find_hits_gate) is bracketed by HIP events on stream and *stats reports their
  * summed duration.  The plan stays current afterwards.  Synchronises stream.  Errors: as
  * hspz_plan, hspz_find_hits and the calls above; HSPZ_E_INVALID for a NULL stats
