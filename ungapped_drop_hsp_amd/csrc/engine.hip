@@ -1048,15 +1048,18 @@ static int mat_radix(Engine *e, uint32_t *&ka, uint32_t *&va, uint32_t *&kb, uin
     return HSPZ_OK;
 }
 
+// q_ordered: the survivors' query ends never decrease in id order (the pass's own
+// survivors: anchors lie in slot order, seeds in query order), so on each diagonal the
+// reference ends already ascend and the stable sort by diagonal alone keeps them so.
 static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32_t *d_ids,
                               uint32_t n, hspz_segment_pair *d_hsp, uint8_t *d_status,
-                              hipStream_t s) {
+                              bool q_ordered, hipStream_t s) {
     int rc;
     if ((rc = ensure_mat(e, n)) || (rc = ensure_compact(e, n))) return rc;
     const uint32_t n_ref = (uint32_t)e->n_ref, n_qry = (uint32_t)e->n_qry;
     uint32_t *ka = e->mat->ka, *va = e->mat->va, *kb = e->mat->kb, *vb = e->mat->vb;
     HIP_TRY(e, launch_mm_keys(d_anchors, d_ids, n, n_ref, n_qry, ka, va, e->mat->lcnt, s));
-    if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of(n_ref), s))) return rc;
+    if (!q_ordered && (rc = mat_radix(e, ka, va, kb, vb, n, bits_of(n_ref), s))) return rc;
     HIP_TRY(e, launch_mm_diag(d_anchors, d_ids, va, n, n_ref, n_qry, ka, s));
     if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of((uint64_t)n_ref + n_qry + 1), s)))
         return rc;
@@ -1077,11 +1080,9 @@ static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
-                              const uint32_t *d_ids, uint64_t n_surv, hspz_segment_pair *d_hsp,
-                              uint8_t *d_status, void *stream) {
-    Engine *e = reinterpret_cast<Engine *>(engine);
-    if (!e) return HSPZ_E_INVALID;
+static int materialize(Engine *e, const uint64_t *d_anchors, const uint32_t *d_ids,
+                       uint64_t n_surv, hspz_segment_pair *d_hsp, uint8_t *d_status,
+                       bool q_ordered, void *stream) {
     if (!e->has_ref || !e->has_qry)
         return fail(e, HSPZ_E_STATE, "materialize needs an uploaded reference and query");
     if (n_surv >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n_surv must be < 2^32");
@@ -1094,11 +1095,19 @@ HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
     const int mode = e->params.materialize_mode;
     if (fits && n_surv && (mode == 2 || (mode == 0 && n_surv >= kMatSharedMin)))
         return materialize_shared(e, d_anchors, d_ids, (uint32_t)n_surv, d_hsp, d_status,
-                                  as_stream(stream));
+                                  q_ordered, as_stream(stream));
     HIP_TRY(e, launch_materialize(d_anchors, d_ids, (uint32_t)n_surv, d_hsp, d_status,
                                   e->d_ref + kPad, e->d_ref4, e->d_qry4, e->sp,
                                   as_stream(stream)));
     return HSPZ_OK;
+}
+
+HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
+                              const uint32_t *d_ids, uint64_t n_surv, hspz_segment_pair *d_hsp,
+                              uint8_t *d_status, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    return materialize(e, d_anchors, d_ids, n_surv, d_hsp, d_status, false, stream);
 }
 
 HSPZ_API int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
@@ -1266,8 +1275,9 @@ HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed
             e->copy_pending[0] = e->copy_pending[1] = false;
             if ((rc = ensure_run_buffers(e, maxn, ns))) return rc;
         }
-        if ((rc = hspz_materialize(engine, e->rb_anchors[b], e->rb_ids[b], ns, e->rb_hsp,
-                                   e->rb_status, stream)))
+        // the chunk's own survivors, in slot order: query ends never decrease
+        if ((rc = materialize(e, e->rb_anchors[b], e->rb_ids[b], ns, e->rb_hsp, e->rb_status,
+                              true, stream)))
             return rc;
         if (e->copy_pending[b]) {  // chunk c - 2's records are still being read out of it
             HIP_TRY(e, hipStreamWaitEvent(s, e->copied_ev[b], 0));

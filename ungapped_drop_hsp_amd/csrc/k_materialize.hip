@@ -39,6 +39,9 @@ constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower o
 // Window of the shared walks' lane stage, in blocks of eight bases per side: about 1% of
 // the walks on dense tandem repeats run past 96 bases.
 constexpr int kLaneBlocks = 12;
+// Tiles the listed walks read ahead: the chain-end walks run thousands of bases, and one
+// tile ahead left each tile waiting on memory.
+constexpr int kListAhead = 8;
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -334,8 +337,8 @@ __global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anc
     int32_t R, L, dr, dlft;
     uint32_t k, m;
     bool mr, ml;
-    exact_walk_merge<+1, true>(tab, rr, qr, sp.xdrop, A.wr, R, k, mr, dr);
-    exact_walk_merge<-1, true>(tab, rl, ql, sp.xdrop, A.wl, L, m, ml, dlft);
+    exact_walk_merge<+1, 1>(tab, rr, qr, sp.xdrop, A.wr, R, k, mr, dr);
+    exact_walk_merge<-1, 1>(tab, rl, ql, sp.xdrop, A.wl, L, m, ml, dlft);
     if (lane_id() == 0) {
         mm_store(right, s, R, k, mr, dr);
         mm_store(left, s, L, m, ml, dlft);
@@ -367,11 +370,11 @@ __global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ an
         uint32_t ext;
         bool merged;
         if (rt)
-            exact_walk_merge<+1, true>(tab, ref + (A.bad ? sp.n_ref : A.r),
+            exact_walk_merge<+1, kListAhead>(tab, ref + (A.bad ? sp.n_ref : A.r),
                                        qry + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr, best, ext,
                                        merged, ds);
         else
-            exact_walk_merge<-1, true>(tab, ref + (A.bad ? 0u : A.r), qry + (A.bad ? 0u : A.q),
+            exact_walk_merge<-1, kListAhead>(tab, ref + (A.bad ? 0u : A.r), qry + (A.bad ? 0u : A.q),
                                        sp.xdrop, A.wl, best, ext, merged, ds);
         if (lane_id() == 0) mm_store(rt ? right : left, s, best, ext, merged, ds);
     }
