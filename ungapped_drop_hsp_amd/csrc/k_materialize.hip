@@ -39,9 +39,6 @@ constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower o
 // Window of the shared walks' lane stage, in blocks of eight bases per side: about 1% of
 // the walks on dense tandem repeats run past 96 bases.
 constexpr int kLaneBlocks = 12;
-// Tiles the listed walks read ahead: the chain-end walks run thousands of bases, and one
-// tile ahead left each tile waiting on memory.
-constexpr int kListAhead = 8;
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -346,18 +343,22 @@ __global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anc
 }
 
 // The walks the lane stage left open: one wave per listed walk (right walks first), a
-// fixed grid striding over the counts read on the device.
+// fixed grid striding over the counts read on the device.  They include the chain ends
+// that run thousands of bases, so they walk 512-base tiles from the 4-bit copies.
 __global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ anchors,
                                                  const uint32_t *__restrict__ ids,
                                                  const uint32_t *__restrict__ key_d,
                                                  const uint32_t *__restrict__ val, uint32_t n,
-                                                 const uint8_t *__restrict__ ref,
-                                                 const uint8_t *__restrict__ qry, ScoreParams sp,
-                                                 MatSide right, MatSide left,
+                                                 const uint32_t *__restrict__ ref4,
+                                                 const uint32_t *__restrict__ qry4,
+                                                 ScoreParams sp, MatSide right, MatSide left,
                                                  const uint32_t *__restrict__ list,
                                                  const uint32_t *__restrict__ lcnt) {
-    __shared__ int32_t tab[kTabSize];
-    if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
+    __shared__ int32_t tab4[kTab4];
+    for (int i = threadIdx.x; i < kTab4; i += 256) {
+        const int r = i >> 4, q = i & 15;
+        tab4[i] = (r <= kCodeEdge && q <= kCodeEdge) ? sp.tab[(r << kRefShift) | q] : 0;
+    }
     __syncthreads();
     const uint32_t cr = lcnt[0];
     const uint64_t total = (uint64_t)cr + lcnt[1];
@@ -370,12 +371,13 @@ __global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ an
         uint32_t ext;
         bool merged;
         if (rt)
-            exact_walk_merge<+1, kListAhead>(tab, ref + (A.bad ? sp.n_ref : A.r),
-                                       qry + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr, best, ext,
-                                       merged, ds);
+            exact_walk_tiles_merge<+1>(tab4, ref4, qry4, kPad4 + (A.bad ? sp.n_ref : A.r),
+                                       kPad4 + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr, best,
+                                       ext, merged, ds);
         else
-            exact_walk_merge<-1, kListAhead>(tab, ref + (A.bad ? 0u : A.r), qry + (A.bad ? 0u : A.q),
-                                       sp.xdrop, A.wl, best, ext, merged, ds);
+            exact_walk_tiles_merge<-1>(tab4, ref4, qry4, kPad4 + (A.bad ? 0u : A.r),
+                                       kPad4 + (A.bad ? 0u : A.q), sp.xdrop, A.wl, best, ext,
+                                       merged, ds);
         if (lane_id() == 0) mm_store(rt ? right : left, s, best, ext, merged, ds);
     }
 }
@@ -471,7 +473,7 @@ hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const ui
                        ids, key_d, val, n, ref4, qry4, sp, right, left, list, lcnt);
     const uint64_t grid = std::min<uint64_t>((2ull * n + 3) / 4, 2048);
     hipLaunchKernelGGL(k_mm_list, dim3((uint32_t)grid), dim3(256), 0, s, anchors, ids, key_d, val,
-                       n, ref, qry, sp, right, left, list, lcnt);
+                       n, ref4, qry4, sp, right, left, list, lcnt);
     return hipGetLastError();
 }
 
