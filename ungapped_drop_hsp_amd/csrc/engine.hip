@@ -337,6 +337,7 @@ Engine::~Engine() {
         dfree(mat->info);
         dfree(mat->list);
         dfree(mat->lcnt);
+        dfree(mat->sa);
         delete mat;
     }
     dfree(d_bsa);
@@ -991,7 +992,7 @@ static int ensure_mat(Engine *e, uint64_t n) {
         (rc = dalloc(e, m.hist, nh)) || (rc = dalloc(e, m.incl, nh)) ||
         (rc = dalloc(e, m.side, 2 * mat_side_words(cap))) ||
         (rc = dalloc(e, m.sum, ns)) || (rc = dalloc(e, m.off, ns)) ||
-        (rc = dalloc(e, m.list, 2 * cap)) || (!m.info && (rc = dalloc(e, m.info, 1))) ||
+        (rc = dalloc(e, m.list, 2 * cap)) || (rc = dalloc(e, m.sa, cap)) || (!m.info && (rc = dalloc(e, m.info, 1))) ||
         (!m.lcnt && (rc = dalloc(e, m.lcnt, 2)))) {
         m.cap = 0;
         return rc;
@@ -1064,8 +1065,10 @@ static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32
     if ((rc = mat_radix(e, ka, va, kb, vb, n, bits_of((uint64_t)n_ref + n_qry + 1), s)))
         return rc;
     const MatSide right = mat_side(e, 0), left = mat_side(e, 1);
+    uint64_t *sa = e->mat->sa;
+    HIP_TRY(e, launch_mm_gather(d_anchors, d_ids, va, n, sa, s));
     // the lane stage needs exact eight-base blocks, as the windowed gate does
-    HIP_TRY(e, launch_mm_walk(d_anchors, d_ids, ka, va, n, e->d_ref + kPad, e->d_qry + kPad,
+    HIP_TRY(e, launch_mm_walk(sa, ka, n, e->d_ref + kPad, e->d_qry + kPad,
                               e->d_ref4, e->d_qry4, e->sp, right, left, e->block_bases == 8,
                               e->mat->list, e->mat->lcnt, s));
     for (const MatSide &m : {right, left}) {
@@ -1075,7 +1078,7 @@ static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32
         HIP_TRY(e, launch_compact(m.term8, n, e->d_cblk, e->d_ctotal + 12, m.pos, nullptr,
                                   nullptr, n, s));
     }
-    HIP_TRY(e, launch_mm_finish(d_anchors, d_ids, va, n, right, left, d_hsp, d_status,
+    HIP_TRY(e, launch_mm_finish(sa, va, n, right, left, d_hsp, d_status,
                                 e->d_ref + kPad, e->sp, s));
     return HSPZ_OK;
 }

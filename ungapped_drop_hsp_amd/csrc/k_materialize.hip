@@ -141,7 +141,18 @@ __global__ __launch_bounds__(256) void k_mm_diag(const uint64_t *__restrict__ an
     key_d[s] = diag_key(anchors[ids[val[s]]], n_ref, n_qry);
 }
 
-// Sorted survivor s: its anchor and the walk indices of its neighbours' starts on its
+// The anchors in sorted order, so that the walks read themselves and their neighbours
+// with unit-stride loads instead of chains of dependent gathers.
+__global__ __launch_bounds__(256) void k_mm_gather(const uint64_t *__restrict__ anchors,
+                                                   const uint32_t *__restrict__ ids,
+                                                   const uint32_t *__restrict__ val, uint32_t n,
+                                                   uint64_t *__restrict__ sa) {
+    const uint32_t s = blockIdx.x * 256 + threadIdx.x;
+    if (s < n) sa[s] = anchors[ids[val[s]]];
+}
+
+// Sorted survivor s (sa: the anchors in sorted order): its anchor and the walk indices of
+// its neighbours' starts on its
 // diagonal (UINT32_MAX for none).  The right neighbour is the next survivor on the
 // diagonal (its right walk starts at base rn, i.e. after walk index rn - 1 - r of this
 // one); the left neighbour is the previous one (its left walk starts below base rp, walk
@@ -152,13 +163,11 @@ struct MmAnchor {
     bool bad;  // outside the sequences: both walks are empty
 };
 
-__device__ __forceinline__ MmAnchor mm_anchor(const uint64_t *__restrict__ anchors,
-                                              const uint32_t *__restrict__ ids,
-                                              const uint32_t *__restrict__ key_d,
-                                              const uint32_t *__restrict__ val, uint32_t n,
+__device__ __forceinline__ MmAnchor mm_anchor(const uint64_t *__restrict__ sa,
+                                              const uint32_t *__restrict__ key_d, uint32_t n,
                                               uint32_t s, const ScoreParams &sp) {
     MmAnchor A;
-    const uint64_t a = anchors[ids[val[s]]];
+    const uint64_t a = sa[s];
     A.r = (uint32_t)a;
     A.q = (uint32_t)(a >> 32);
     A.bad = A.r > sp.n_ref || A.q > sp.n_qry;
@@ -167,11 +176,11 @@ __device__ __forceinline__ MmAnchor mm_anchor(const uint64_t *__restrict__ ancho
     if (!A.bad) {
         const uint32_t key = key_d[s];
         if (s + 1 < n && key_d[s + 1] == key) {
-            const uint32_t rn = (uint32_t)anchors[ids[val[s + 1]]];
+            const uint32_t rn = (uint32_t)sa[s + 1];
             if (rn > A.r) A.wr = rn - 1u - A.r;
         }
         if (s > 0 && key_d[s - 1] == key) {
-            const uint32_t rp = (uint32_t)anchors[ids[val[s - 1]]];
+            const uint32_t rp = (uint32_t)sa[s - 1];
             if (rp < A.r) A.wl = A.r - 1u - rp;
         }
     }
@@ -272,8 +281,7 @@ __device__ __forceinline__ bool lane_merge_walk(const int32_t *tab4,
 // each wave reserving its share with one atomic per side.
 template <int NB>
 __global__ __launch_bounds__(256) void k_mm_lanes(
-    const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ ids,
-    const uint32_t *__restrict__ key_d, const uint32_t *__restrict__ val, uint32_t n,
+    const uint64_t *__restrict__ sa, const uint32_t *__restrict__ key_d, uint32_t n,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, ScoreParams sp,
     MatSide right, MatSide left, uint32_t *__restrict__ list, uint32_t *__restrict__ lcnt) {
     __shared__ int32_t tab4[kTab4];
@@ -285,7 +293,7 @@ __global__ __launch_bounds__(256) void k_mm_lanes(
     const uint32_t s = blockIdx.x * 256 + threadIdx.x;
     const bool live = s < n;
     MmAnchor A{};
-    if (live) A = mm_anchor(anchors, ids, key_d, val, n, s, sp);
+    if (live) A = mm_anchor(sa, key_d, n, s, sp);
     bool open[2] = {false, false};
 #pragma unroll
     for (int side = 0; side < 2; side++) {
@@ -316,10 +324,7 @@ __global__ __launch_bounds__(256) void k_mm_lanes(
 
 // One wave per sorted survivor: its right walk (neighbour: the next survivor on the
 // diagonal) and its left walk (neighbour: the previous one), each a one-wave merge walk.
-__global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anchors,
-                                                const uint32_t *__restrict__ ids,
-                                                const uint32_t *__restrict__ key_d,
-                                                const uint32_t *__restrict__ val, uint32_t n,
+__global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ sa, const uint32_t *__restrict__ key_d, uint32_t n,
                                                 const uint8_t *__restrict__ ref,
                                                 const uint8_t *__restrict__ qry, ScoreParams sp,
                                                 MatSide right, MatSide left) {
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anc
     __syncthreads();
     const uint32_t s = blockIdx.x;
     if (s >= n) return;
-    const MmAnchor A = mm_anchor(anchors, ids, key_d, val, n, s, sp);
+    const MmAnchor A = mm_anchor(sa, key_d, n, s, sp);
     const uint8_t *rr = ref + (A.bad ? sp.n_ref : A.r), *qr = qry + (A.bad ? sp.n_qry : A.q);
     const uint8_t *rl = ref + (A.bad ? 0u : A.r), *ql = qry + (A.bad ? 0u : A.q);
     int32_t R, L, dr, dlft;
@@ -345,10 +350,7 @@ __global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ anc
 // The walks the lane stage left open: one wave per listed walk (right walks first), a
 // fixed grid striding over the counts read on the device.  They include the chain ends
 // that run thousands of bases, so they walk 512-base tiles from the 4-bit copies.
-__global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ anchors,
-                                                 const uint32_t *__restrict__ ids,
-                                                 const uint32_t *__restrict__ key_d,
-                                                 const uint32_t *__restrict__ val, uint32_t n,
+__global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ sa, const uint32_t *__restrict__ key_d, uint32_t n,
                                                  const uint32_t *__restrict__ ref4,
                                                  const uint32_t *__restrict__ qry4,
                                                  ScoreParams sp, MatSide right, MatSide left,
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ an
     for (uint64_t t = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < total; t += nw) {
         const bool rt = t < cr;
         const uint32_t s = rt ? list[t] : list[(uint64_t)n + (t - cr)];
-        const MmAnchor A = mm_anchor(anchors, ids, key_d, val, n, s, sp);
+        const MmAnchor A = mm_anchor(sa, key_d, n, s, sp);
         int32_t best, ds;
         uint32_t ext;
         bool merged;
@@ -387,13 +389,12 @@ __global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ an
 // drop-ended walk t >= s (its bests add the scores at the starts s .. t - 1); a left chain
 // to the last drop-ended walk t <= s (scores at starts t + 1 .. s).
 __global__ __launch_bounds__(256) void k_mm_finish(
-    const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ ids,
-    const uint32_t *__restrict__ val, uint32_t n, MatSide right, MatSide left,
+    const uint64_t *__restrict__ sa, const uint32_t *__restrict__ val, uint32_t n, MatSide right, MatSide left,
     hspz_segment_pair *__restrict__ hsp, uint8_t *__restrict__ status, int32_t T) {
     const uint32_t s = blockIdx.x * 256 + threadIdx.x;
     if (s >= n) return;
     const uint32_t j = val[s];
-    const uint64_t a = anchors[ids[j]];
+    const uint64_t a = sa[s];
     const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
     int32_t R = right.best[s], L = left.best[s];
     uint32_t k = right.ext[s], m = left.ext[s];
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(256) void k_mm_finish(
     const uint32_t nr = right.cnt[n - 1], nl = left.cnt[n - 1];
     if (!right.term[s] && right.cnt[s] < nr) {
         const uint32_t t = right.pos[right.cnt[s]];  // first drop-ended walk after s
-        const uint32_t rt = (uint32_t)anchors[ids[val[t]]];
+        const uint32_t rt = (uint32_t)sa[t];
         // sum of the scores at the starts s .. t - 1: exclusive prefix at t minus at s
         const uint32_t ex_t = right.sum[t] - (uint32_t)right.ds[t];
         const uint32_t ex_s = right.sum[s] - (uint32_t)right.ds[s];
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(256) void k_mm_finish(
     }
     if (!left.term[s] && left.cnt[s] >= 1u && left.cnt[s] <= nl) {
         const uint32_t t = left.pos[left.cnt[s] - 1u];  // last drop-ended walk before s
-        const uint32_t rt = (uint32_t)anchors[ids[val[t]]];
+        const uint32_t rt = (uint32_t)sa[t];
         L = left.best[t] + (int32_t)(left.sum[s] - left.sum[t]);
         m = left.ext[t] + (r - rt);
     }
@@ -458,31 +459,39 @@ hipError_t launch_mm_diag(const uint64_t *anchors, const uint32_t *ids, const ui
     return hipGetLastError();
 }
 
-hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const uint32_t *key_d,
-                          const uint32_t *val, uint32_t n, const uint8_t *ref,
+hipError_t launch_mm_gather(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+                            uint32_t n, uint64_t *sa, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_mm_gather, dim3((n + 255) / 256), dim3(256), 0, s, anchors, ids, val, n,
+                       sa);
+    return hipGetLastError();
+}
+
+hipError_t launch_mm_walk(const uint64_t *sa, const uint32_t *key_d, uint32_t n,
+                          const uint8_t *ref,
                           const uint8_t *qry, const uint32_t *ref4, const uint32_t *qry4,
                           const ScoreParams &sp, const MatSide &right, const MatSide &left,
                           bool lanes, uint32_t *list, uint32_t *lcnt, hipStream_t s) {
     if (n == 0) return hipSuccess;
     if (!lanes) {
-        hipLaunchKernelGGL(k_mm_walk, dim3(n), dim3(64), 0, s, anchors, ids, key_d, val, n, ref,
-                           qry, sp, right, left);
+        hipLaunchKernelGGL(k_mm_walk, dim3(n), dim3(64), 0, s, sa, key_d, n, ref, qry, sp, right,
+                           left);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_mm_lanes<kLaneBlocks>, dim3((n + 255) / 256), dim3(256), 0, s, anchors,
-                       ids, key_d, val, n, ref4, qry4, sp, right, left, list, lcnt);
-    const uint64_t grid = std::min<uint64_t>((2ull * n + 3) / 4, 2048);
-    hipLaunchKernelGGL(k_mm_list, dim3((uint32_t)grid), dim3(256), 0, s, anchors, ids, key_d, val,
+    hipLaunchKernelGGL(k_mm_lanes<kLaneBlocks>, dim3((n + 255) / 256), dim3(256), 0, s, sa, key_d,
                        n, ref4, qry4, sp, right, left, list, lcnt);
+    const uint64_t grid = std::min<uint64_t>((2ull * n + 3) / 4, 2048);
+    hipLaunchKernelGGL(k_mm_list, dim3((uint32_t)grid), dim3(256), 0, s, sa, key_d, n, ref4, qry4,
+                       sp, right, left, list, lcnt);
     return hipGetLastError();
 }
 
-hipError_t launch_mm_finish(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+hipError_t launch_mm_finish(const uint64_t *sa, const uint32_t *val,
                             uint32_t n, const MatSide &right, const MatSide &left,
                             hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
                             const ScoreParams &sp, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_mm_finish, dim3((n + 255) / 256), dim3(256), 0, s, anchors, ids, val, n,
+    hipLaunchKernelGGL(k_mm_finish, dim3((n + 255) / 256), dim3(256), 0, s, sa, val, n,
                        right, left, hsp, status, sp.T);
     if (sp.entropy_mode == 1)
         hipLaunchKernelGGL(k_mm_entropy, dim3(n), dim3(64), 0, s, hsp, status, n, ref, sp);

@@ -20,6 +20,7 @@ struct MatScratch {
     PlanInfo *info = nullptr;
     uint32_t *list = nullptr;  // walks the lane stage left open (2 * cap)
     uint32_t *lcnt = nullptr;  // their counts, right and left
+    uint64_t *sa = nullptr;    // the anchors in sorted order
     uint64_t cap = 0;
 };
 
@@ -43,12 +44,15 @@ hipError_t launch_mm_diag(const uint64_t *anchors, const uint32_t *ids, const ui
 // 7 * (largest pair score) <= xdrop) plus one wave per walk it left open, listed in list
 // (2 * n entries) with counts in lcnt (cleared by launch_mm_keys); else one wave per
 // survivor.
-hipError_t launch_mm_walk(const uint64_t *anchors, const uint32_t *ids, const uint32_t *key_d,
-                          const uint32_t *val, uint32_t n, const uint8_t *ref,
+// sa[s] = anchors[ids[val[s]]]: the anchors in sorted order, for the walks and records.
+hipError_t launch_mm_gather(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+                            uint32_t n, uint64_t *sa, hipStream_t s);
+hipError_t launch_mm_walk(const uint64_t *sa, const uint32_t *key_d, uint32_t n,
+                          const uint8_t *ref,
                           const uint8_t *qry, const uint32_t *ref4, const uint32_t *qry4,
                           const ScoreParams &sp, const MatSide &right, const MatSide &left,
                           bool lanes, uint32_t *list, uint32_t *lcnt, hipStream_t s);
-hipError_t launch_mm_finish(const uint64_t *anchors, const uint32_t *ids, const uint32_t *val,
+hipError_t launch_mm_finish(const uint64_t *sa, const uint32_t *val,
                             uint32_t n, const MatSide &right, const MatSide &left,
                             hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
                             const ScoreParams &sp, hipStream_t s);
