@@ -39,6 +39,7 @@ constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower o
 // Window of the shared walks' lane stage, in blocks of eight bases per side: about 1% of
 // the walks on dense tandem repeats run past 96 bases.
 constexpr int kLaneBlocks = 12;
+constexpr int kLanePrefetch = 3;  // blocks each lane reads ahead
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -173,16 +174,14 @@ __device__ __forceinline__ MmAnchor mm_anchor(const uint64_t *__restrict__ sa,
     A.bad = A.r > sp.n_ref || A.q > sp.n_qry;
     A.wr = UINT32_MAX;
     A.wl = UINT32_MAX;
+    // every load at once (the neighbours' indices clamped into the array), then the tests
+    const uint32_t sn = s + 1 < n ? s + 1 : s, sp_ = s > 0 ? s - 1 : s;
+    const uint64_t an = sa[sn], ap = sa[sp_];
+    const uint32_t key = key_d[s], kn = key_d[sn], kp = key_d[sp_];
     if (!A.bad) {
-        const uint32_t key = key_d[s];
-        if (s + 1 < n && key_d[s + 1] == key) {
-            const uint32_t rn = (uint32_t)sa[s + 1];
-            if (rn > A.r) A.wr = rn - 1u - A.r;
-        }
-        if (s > 0 && key_d[s - 1] == key) {
-            const uint32_t rp = (uint32_t)sa[s - 1];
-            if (rp < A.r) A.wl = A.r - 1u - rp;
-        }
+        const uint32_t rn = (uint32_t)an, rp = (uint32_t)ap;
+        if (sn != s && kn == key && rn > A.r) A.wr = rn - 1u - A.r;
+        if (sp_ != s && kp == key && rp < A.r) A.wl = A.r - 1u - rp;
     }
     return A;
 }
@@ -209,76 +208,99 @@ __device__ __forceinline__ void mm_store(const MatSide &m, uint32_t s, int32_t b
 // best rose above the best before wm (or above the block's starting best once wm lies
 // behind), and dropped if the drawdown passed xdrop; a merge takes precedence, being
 // the earlier event.  Returns false if the walk did neither within the window; the
-// caller then walks it again in full.  Reads at most 8 * NB + 16 nibbles from mr on
-// either side, inside the edge padding.
-template <int D, int NB>
+// caller then walks it again in full.  Each sequence's dwords are read PF blocks ahead
+// of their use (a ring of PF + 2 dwords), so that a block's loads have the blocks before
+// it to land.  Reads at most 8 * (NB + PF) + 16 nibbles from mr on either side, inside
+// the edge padding.
+template <int D, int NB, int PF>
 __device__ __forceinline__ bool lane_merge_walk(const int32_t *tab4,
                                                 const uint32_t *__restrict__ ref4,
                                                 const uint32_t *__restrict__ qry4, uint32_t mr,
                                                 uint32_t mq, int32_t xdrop, uint32_t wm,
                                                 int32_t &best, uint32_t &ext, bool &merged,
                                                 int32_t &ds) {
-    static_assert(8 * NB + 16 <= kPad4, "the window must stay inside the edge padding");
+    static_assert(8 * (NB + PF) + 16 <= kPad4, "the window must stay inside the edge padding");
     const uint32_t ar = D > 0 ? mr : mr - 8u, aq = D > 0 ? mq : mq - 8u;
     const uint32_t *__restrict__ pr = ref4 + (ar >> 3);
     const uint32_t *__restrict__ pq = qry4 + (aq >> 3);
     const uint32_t shr = (ar & 7u) * 4u, shq = (aq & 7u) * 4u;
-    // block k's nibbles are the funnel of dwords p[D * k] (low) and p[D * k + 1] (high)
-    uint32_t r0 = pr[0], r1 = pr[1], q0 = pq[0], q1 = pq[1];
-    int32_t s = 0;
+    // block k's nibbles are the funnel of dwords p[k] (low) and p[k + 1] (high) for a right
+    // walk, p[-k] (low) and p[1 - k] (high) for a left one; ring slot i holds dword
+    // p[k + i] or p[1 - k - i], so block k reads slots 0 and 1
+    auto at = [](const uint32_t *__restrict__ p, int i) { return D > 0 ? p[i] : p[1 - i]; };
+    uint32_t rr[PF + 2], qq[PF + 2];
+#pragma unroll
+    for (int i = 0; i < PF + 2; i++) {
+        rr[i] = at(pr, i);
+        qq[i] = at(pq, i);
+    }
+    // The lanes run in step with no branch of their own: a lane that ends in a block keeps
+    // its results from there and goes on scoring (its reads stay inside the window), and
+    // the wave leaves once every lane has ended.  A branch per lane would make every value
+    // of the ring cross a join, and copying a register that a load still writes waits for
+    // the load; unrolled, the ring is register renaming.
+    int32_t s = 0, b_run = 0, ds_run = 0;
+    uint32_t e_run = 0;
+    bool done = false;
     best = 0;
     ext = 0;
     merged = false;
     ds = 0;
+#pragma unroll
     for (int k = 0; k < NB; k++) {
-        const uint32_t rn = D > 0 ? pr[k + 2] : pr[-(k + 1)];  // the next block's new dword
-        const uint32_t qn = D > 0 ? pq[k + 2] : pq[-(k + 1)];
-        const uint32_t R = __builtin_amdgcn_alignbit(r1, r0, shr);
-        const uint32_t Q = __builtin_amdgcn_alignbit(q1, q0, shq);
+        const uint32_t R = D > 0 ? __builtin_amdgcn_alignbit(rr[1], rr[0], shr)
+                                 : __builtin_amdgcn_alignbit(rr[0], rr[1], shr);
+        const uint32_t Q = D > 0 ? __builtin_amdgcn_alignbit(qq[1], qq[0], shq)
+                                 : __builtin_amdgcn_alignbit(qq[0], qq[1], shq);
+#pragma unroll
+        for (int i = 0; i < PF + 1; i++) {
+            rr[i] = rr[i + 1];
+            qq[i] = qq[i + 1];
+        }
+        rr[PF + 1] = at(pr, k + PF + 2);  // block k + PF + 1's new dword
+        qq[PF + 1] = at(pq, k + PF + 2);
         const uint32_t hi = 0xF0F0F0F0u;
         // pair indices r * 16 + q: nibble j's in byte j / 2 of c[j % 2]
         const uint32_t c[2] = {((R << 4) & hi) | (Q & ~hi), (R & hi) | ((Q >> 4) & ~hi)};
         const uint32_t b0 = 8u * (uint32_t)k;
-        const int32_t best0 = best;
-        int32_t bpre = best, dd = 0;
+        const int32_t best0 = b_run;
+        int32_t bpre = b_run, dd = 0;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int nib = D > 0 ? j : 7 - j;
             const int32_t sg = tab4[(c[nib & 1] >> (8 * (nib >> 1))) & 0xFFu];
             const uint32_t i = b0 + (uint32_t)j;
             s += sg;
-            const bool at = i == wm;
-            bpre = at ? best : bpre;
-            ds = at ? s : ds;
-            ext = s > best ? i + 1u : ext;
-            best = max(best, s);
-            dd = max(dd, best - s);
+            const bool at_wm = i == wm;
+            bpre = at_wm ? b_run : bpre;
+            ds_run = at_wm ? s : ds_run;
+            e_run = s > b_run ? i + 1u : e_run;
+            b_run = max(b_run, s);
+            dd = max(dd, b_run - s);
         }
         const int32_t thr = wm < b0 ? best0 : (wm < b0 + 8u ? bpre : INT32_MAX);
-        if (best > thr) {
-            merged = true;
-            return true;
-        }
-        if (dd > xdrop) return true;
-        if (D > 0) {
-            r0 = r1;
-            r1 = rn;
-            q0 = q1;
-            q1 = qn;
-        } else {
-            r1 = r0;
-            r0 = rn;
-            q1 = q0;
-            q0 = qn;
+        const bool mrg = b_run > thr;  // a merge is the earlier event
+        const bool end = !done && (mrg || dd > xdrop);
+        best = end ? b_run : best;
+        ext = end ? e_run : ext;
+        ds = end ? ds_run : ds;
+        merged = end ? mrg : merged;
+        done = done || end;
+        if (__ballot(!done) == 0) {
+            // the loads still in flight are used on this path too, so that the compiler
+            // keeps each one where it is issued rather than sinking it to its first use
+#pragma unroll
+            for (int i = 0; i < PF + 2; i++) asm volatile("" ::"v"(rr[i]), "v"(qq[i]));
+            break;
         }
     }
-    return false;
+    return done;
 }
 
 // Lane stage of the diagonal-shared walks: one lane per sorted survivor walks both sides
 // with lane_merge_walk and stores what it finished; walks still running at the window's
 // end go to a list (right walks from list[0], left walks from list[n]; counts in lcnt),
-// each wave reserving its share with one atomic per side.
+// each wave reserving its share of both with one atomic.
 template <int NB>
 __global__ __launch_bounds__(256) void k_mm_lanes(
     const uint64_t *__restrict__ sa, const uint32_t *__restrict__ key_d, uint32_t n,
@@ -302,23 +324,29 @@ __global__ __launch_bounds__(256) void k_mm_lanes(
             uint32_t ext;
             bool merged, done;
             if (side == 0)
-                done = lane_merge_walk<+1, NB>(tab4, ref4, qry4, kPad4 + (A.bad ? sp.n_ref : A.r),
+                done = lane_merge_walk<+1, NB, kLanePrefetch>(tab4, ref4, qry4, kPad4 + (A.bad ? sp.n_ref : A.r),
                                                kPad4 + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr,
                                                best, ext, merged, ds);
             else
-                done = lane_merge_walk<-1, NB>(tab4, ref4, qry4, kPad4 + (A.bad ? 0u : A.r),
+                done = lane_merge_walk<-1, NB, kLanePrefetch>(tab4, ref4, qry4, kPad4 + (A.bad ? 0u : A.r),
                                                kPad4 + (A.bad ? 0u : A.q), sp.xdrop, A.wl, best,
                                                ext, merged, ds);
             if (done) mm_store(side == 0 ? right : left, s, best, ext, merged, ds);
             open[side] = !done;
         }
-        const uint64_t m = __ballot(open[side]);
-        if (m) {
-            uint32_t at = 0;
-            if (lane_id() == 0) at = atomicAdd(&lcnt[side], (uint32_t)__popcll(m));
-            at = __shfl(at, 0, 64);
-            if (open[side]) list[(uint64_t)side * n + at + lane_rank(m)] = s;
-        }
+    }
+    // one atomic per wave reserves both sides' list entries: lcnt as one little-endian
+    // u64, the right count in its low word (a count stays below 2^32, so no carry)
+    const uint64_t mr = __ballot(open[0]), ml = __ballot(open[1]);
+    if (mr | ml) {
+        unsigned long long at = 0;
+        if (lane_id() == 0)
+            at = atomicAdd(reinterpret_cast<unsigned long long *>(lcnt),
+                           ((unsigned long long)__popcll(ml) << 32) | (unsigned long long)__popcll(mr));
+        const uint32_t at_r = __shfl((uint32_t)at, 0, 64);
+        const uint32_t at_l = __shfl((uint32_t)(at >> 32), 0, 64);
+        if (open[0]) list[at_r + lane_rank(mr)] = s;
+        if (open[1]) list[(uint64_t)n + at_l + lane_rank(ml)] = s;
     }
 }
 
