@@ -338,6 +338,7 @@ Engine::~Engine() {
         dfree(mat->list);
         dfree(mat->lcnt);
         dfree(mat->sa);
+        dfree(mat->sblk);
         delete mat;
     }
     dfree(d_bsa);
@@ -968,12 +969,11 @@ HSPZ_API int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t 
 constexpr uint64_t kMatSharedMin = 65536;
 
 // Scratch of the diagonal-shared materialization for n survivors.  The per-side arrays
-// (best, ext, term, ds, cnt, sum, pos: seven u32 each, plus the flag bytes) are carved out
+// (best, ext, term, ds, cnt, sum, pos: seven u32 each) are carved out
 // of one allocation, each at a 16-byte aligned offset.
 static uint64_t mat_stride(uint64_t cap) { return (cap + 3) / 4 * 4; }  // u32 words per array
 static uint64_t mat_side_words(uint64_t cap) {
-    const uint64_t st = mat_stride(cap);
-    return (7 * st + st / 4 + 4 + 3) / 4 * 4;  // a multiple of 4 words: 16-byte aligned sides
+    return 7 * mat_stride(cap);  // a multiple of 4 words: 16-byte aligned sides
 }
 
 static int ensure_mat(Engine *e, uint64_t n) {
@@ -992,7 +992,10 @@ static int ensure_mat(Engine *e, uint64_t n) {
         (rc = dalloc(e, m.hist, nh)) || (rc = dalloc(e, m.incl, nh)) ||
         (rc = dalloc(e, m.side, 2 * mat_side_words(cap))) ||
         (rc = dalloc(e, m.sum, ns)) || (rc = dalloc(e, m.off, ns)) ||
-        (rc = dalloc(e, m.list, 2 * cap)) || (rc = dalloc(e, m.sa, cap)) || (!m.info && (rc = dalloc(e, m.info, 1))) ||
+        (rc = dalloc(e, m.list, 2 * cap)) || (rc = dalloc(e, m.sa, cap)) ||
+        (rc = dalloc(e, m.sblk,
+                     4ull * mm_scan_blocks((uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull)))) ||
+        (!m.info && (rc = dalloc(e, m.info, 1))) ||
         (!m.lcnt && (rc = dalloc(e, m.lcnt, 2)))) {
         m.cap = 0;
         return rc;
@@ -1012,7 +1015,6 @@ static MatSide mat_side(Engine *e, int side) {
     m.cnt = b + 4 * stride;
     m.sum = b + 5 * stride;
     m.pos = b + 6 * stride;
-    m.term8 = reinterpret_cast<uint8_t *>(b + 7 * stride);
     return m;
 }
 
@@ -1056,7 +1058,7 @@ static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32
                               uint32_t n, hspz_segment_pair *d_hsp, uint8_t *d_status,
                               bool q_ordered, hipStream_t s) {
     int rc;
-    if ((rc = ensure_mat(e, n)) || (rc = ensure_compact(e, n))) return rc;
+    if ((rc = ensure_mat(e, n))) return rc;
     const uint32_t n_ref = (uint32_t)e->n_ref, n_qry = (uint32_t)e->n_qry;
     uint32_t *ka = e->mat->ka, *va = e->mat->va, *kb = e->mat->kb, *vb = e->mat->vb;
     HIP_TRY(e, launch_mm_keys(d_anchors, d_ids, n, n_ref, n_qry, ka, va, e->mat->lcnt, s));
@@ -1071,13 +1073,7 @@ static int materialize_shared(Engine *e, const uint64_t *d_anchors, const uint32
     HIP_TRY(e, launch_mm_walk(sa, ka, n, e->d_ref + kPad, e->d_qry + kPad,
                               e->d_ref4, e->d_qry4, e->sp, right, left, e->block_bases == 8,
                               e->mat->list, e->mat->lcnt, s));
-    for (const MatSide &m : {right, left}) {
-        if ((rc = mat_scan(e, m.term, n, m.cnt, s)) ||
-            (rc = mat_scan(e, reinterpret_cast<uint32_t *>(m.ds), n, m.sum, s)))
-            return rc;
-        HIP_TRY(e, launch_compact(m.term8, n, e->d_cblk, e->d_ctotal + 12, m.pos, nullptr,
-                                  nullptr, n, s));
-    }
+    HIP_TRY(e, launch_mm_scan(right, left, n, e->mat->sblk, s));
     HIP_TRY(e, launch_mm_finish(sa, va, n, right, left, d_hsp, d_status,
                                 e->d_ref + kPad, e->sp, s));
     return HSPZ_OK;

@@ -191,7 +191,6 @@ __device__ __forceinline__ void mm_store(const MatSide &m, uint32_t s, int32_t b
     m.best[s] = best;
     m.ext[s] = ext;
     m.term[s] = merged ? 0u : 1u;
-    m.term8[s] = merged ? 0 : 1;
     m.ds[s] = merged ? ds : 0;
 }
 
@@ -412,6 +411,128 @@ __global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ sa
     }
 }
 
+// The chain bookkeeping of both sides in one scan: inclusive sums (modulo 2^32) of four
+// streams, the right and left end flags (term) and scores at the neighbour's start (ds),
+// into cnt and sum; the last pass also lists each side's drop-ended walks in order
+// (pos[cnt[s] - 1] = s for a walk s that ran to its drop).  Three launches: block-local
+// scans with block totals, one workgroup scanning the totals, and the offsets.
+constexpr int kMsPer = 4;                 // survivors per thread
+constexpr int kMsBlock = 256 * kMsPer;    // survivors per block
+
+__device__ __forceinline__ uint32_t op_add_u32(uint32_t a, uint32_t b) { return a + b; }
+
+// Inclusive wave scan in wrapping unsigned arithmetic (the DPP steps of wave_incl_sum).
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+    HSPZ_DPP_SCAN(op_add_u32, 0, v);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t *ms_stream(const MatSide &r, const MatSide &l, int st,
+                                               bool out) {
+    const MatSide &m = st < 2 ? r : l;
+    if (st & 1) return out ? m.sum : reinterpret_cast<uint32_t *>(m.ds);
+    return out ? m.cnt : m.term;
+}
+
+__global__ __launch_bounds__(256) void k_mm_scan_local(MatSide right, MatSide left, uint32_t n,
+                                                       uint32_t *__restrict__ blk) {
+    __shared__ uint32_t wtot[4][4];  // [wave][stream]
+    const int t = threadIdx.x, w = t >> 6;
+    const uint64_t i0 = (uint64_t)blockIdx.x * kMsBlock + (uint64_t)t * kMsPer;
+    uint32_t v[4][kMsPer];
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        const uint32_t *in = ms_stream(right, left, st, false);
+        if (i0 + kMsPer <= n) {  // 16-byte aligned: the arrays are, and i0 % 4 == 0
+            const uint4 x = *reinterpret_cast<const uint4 *>(in + i0);
+            v[st][0] = x.x;
+            v[st][1] = x.y;
+            v[st][2] = x.z;
+            v[st][3] = x.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMsPer; j++) v[st][j] = i0 + j < n ? in[i0 + j] : 0u;
+        }
+#pragma unroll
+        for (int j = 1; j < kMsPer; j++) v[st][j] += v[st][j - 1];
+    }
+    uint32_t excl[4];
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        const uint32_t tot = v[st][kMsPer - 1];
+        const uint32_t incl = wave_scan_u32(tot);
+        excl[st] = incl - tot;
+        if (lane_id() == 63) wtot[w][st] = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            before += u < w ? wtot[u][st] : 0u;
+            all += wtot[u][st];
+        }
+        excl[st] += before;
+        uint32_t *out = ms_stream(right, left, st, true);
+        if (i0 + kMsPer <= n) {
+            *reinterpret_cast<uint4 *>(out + i0) =
+                make_uint4(v[st][0] + excl[st], v[st][1] + excl[st], v[st][2] + excl[st],
+                           v[st][3] + excl[st]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMsPer; j++)
+                if (i0 + j < n) out[i0 + j] = v[st][j] + excl[st];
+        }
+        if (t == 0) blk[4ull * blockIdx.x + st] = all;
+    }
+}
+
+// One workgroup: the exclusive scan of nb block totals per stream, in place.
+__global__ __launch_bounds__(1024) void k_mm_scan_blocks(uint32_t *__restrict__ blk, uint32_t nb) {
+    __shared__ uint32_t wtot[16][4];
+    const int t = threadIdx.x, w = t >> 6;
+    uint32_t carry[4] = {0, 0, 0, 0};
+    for (uint32_t b0 = 0; b0 < nb; b0 += 1024) {
+        const uint32_t b = b0 + (uint32_t)t;
+        uint32_t x[4], excl[4];
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            x[st] = b < nb ? blk[4ull * b + st] : 0u;
+            const uint32_t incl = wave_scan_u32(x[st]);
+            excl[st] = incl - x[st];
+            if (lane_id() == 63) wtot[w][st] = incl;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            uint32_t before = 0, all = 0;
+            for (int u = 0; u < 16; u++) {
+                before += u < w ? wtot[u][st] : 0u;
+                all += wtot[u][st];
+            }
+            if (b < nb) blk[4ull * b + st] = carry[st] + before + excl[st];
+            carry[st] += all;
+        }
+        __syncthreads();  // wtot is rewritten by the next round
+    }
+}
+
+__global__ __launch_bounds__(256) void k_mm_scan_add(MatSide right, MatSide left, uint32_t n,
+                                                     const uint32_t *__restrict__ blk) {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t b = i / kMsBlock;
+    const uint4 off = *reinterpret_cast<const uint4 *>(blk + 4ull * b);
+    const uint32_t cr = right.cnt[i] + off.x, cl = left.cnt[i] + off.z;
+    right.cnt[i] = cr;
+    right.sum[i] += off.y;
+    left.cnt[i] = cl;
+    left.sum[i] += off.w;
+    if (right.term[i]) right.pos[cr - 1u] = i;
+    if (left.term[i]) left.pos[cl - 1u] = i;
+}
+
 // One thread per sorted survivor: each side's best and extent through its chain, then the
 // record and status at the survivor's own index.  A right chain runs to the first
 // drop-ended walk t >= s (its bests add the scores at the starts s .. t - 1); a left chain
@@ -511,6 +632,18 @@ hipError_t launch_mm_walk(const uint64_t *sa, const uint32_t *key_d, uint32_t n,
     const uint64_t grid = std::min<uint64_t>((2ull * n + 3) / 4, 2048);
     hipLaunchKernelGGL(k_mm_list, dim3((uint32_t)grid), dim3(256), 0, s, sa, key_d, n, ref4, qry4,
                        sp, right, left, list, lcnt);
+    return hipGetLastError();
+}
+
+uint32_t mm_scan_blocks(uint32_t n) { return (n + kMsBlock - 1) / kMsBlock; }
+
+hipError_t launch_mm_scan(const MatSide &right, const MatSide &left, uint32_t n, uint32_t *blk,
+                          hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const uint32_t nb = mm_scan_blocks(n);
+    hipLaunchKernelGGL(k_mm_scan_local, dim3(nb), dim3(256), 0, s, right, left, n, blk);
+    hipLaunchKernelGGL(k_mm_scan_blocks, dim3(1), dim3(1024), 0, s, blk, nb);
+    hipLaunchKernelGGL(k_mm_scan_add, dim3((n + 255) / 256), dim3(256), 0, s, right, left, n, blk);
     return hipGetLastError();
 }
 

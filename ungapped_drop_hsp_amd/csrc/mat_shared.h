@@ -21,6 +21,7 @@ struct MatScratch {
     uint32_t *list = nullptr;  // walks the lane stage left open (2 * cap)
     uint32_t *lcnt = nullptr;  // their counts, right and left
     uint64_t *sa = nullptr;    // the anchors in sorted order
+    uint32_t *sblk = nullptr;  // the side scan's block totals (4 per block)
     uint64_t cap = 0;
 };
 
@@ -28,7 +29,6 @@ struct MatSide {
     int32_t *best;
     uint32_t *ext;
     uint32_t *term;   // 1: the walk ran to its drop; 0: it merged into its neighbour's
-    uint8_t *term8;   // the same as flag bytes
     int32_t *ds;      // its running score at the neighbour's start (0 if it ran to its drop)
     uint32_t *cnt;    // inclusive scan of term
     uint32_t *sum;    // inclusive scan of ds, modulo 2^32
@@ -52,6 +52,11 @@ hipError_t launch_mm_walk(const uint64_t *sa, const uint32_t *key_d, uint32_t n,
                           const uint8_t *qry, const uint32_t *ref4, const uint32_t *qry4,
                           const ScoreParams &sp, const MatSide &right, const MatSide &left,
                           bool lanes, uint32_t *list, uint32_t *lcnt, hipStream_t s);
+// Both sides' cnt, sum and pos from term and ds in one scan; blk holds
+// 4 * mm_scan_blocks(n) words.  Every array of a side must be 16-byte aligned.
+uint32_t mm_scan_blocks(uint32_t n);
+hipError_t launch_mm_scan(const MatSide &right, const MatSide &left, uint32_t n, uint32_t *blk,
+                          hipStream_t s);
 hipError_t launch_mm_finish(const uint64_t *sa, const uint32_t *val,
                             uint32_t n, const MatSide &right, const MatSide &left,
                             hspz_segment_pair *hsp, uint8_t *status, const uint8_t *ref,
