@@ -424,15 +424,17 @@ def _oracle_batch(o):
                 n_accepted=int(acc.size)), acc
 
 
+@pytest.mark.parametrize("mat", [0, 2], ids=["default-walks", "shared-walks"])
 @pytest.mark.parametrize("case", CASES[:4], ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
-def test_run_batch_matches_the_oracle(case):
+def test_run_batch_matches_the_oracle(case, mat):
     # the native whole-batch driver against the oracle's pass: counts and every accepted
-    # record, in chunk order, over the whole strand and over sub-batches
+    # record, in chunk order, over the whole strand and over sub-batches (with shared
+    # walks the driver sorts its own survivors by diagonal alone)
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
     ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
                            identity=ident, gc=gc, alphabet_noise=True)
     p = params_of(pat, max_hits=mx)
-    eng = engine(p)
+    eng = engine(p, materialize_mode=mat)
     eng.upload_reference(ref)
     eng.upload_query(qry)
     n = eng.num_seeds()
@@ -447,12 +449,13 @@ def test_run_batch_matches_the_oracle(case):
         assert np.array_equal(got.view(np.uint8), acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 
 
-def test_run_batch_reverse_strand_and_entropy():
+@pytest.mark.parametrize("mat", [0, 2], ids=["default-walks", "shared-walks"])
+def test_run_batch_reverse_strand_and_entropy(mat):
     ref, qry = random_pair(11, 30_000, 25_000, n_frac=0.02, plant=25, plant_len=(80, 900),
                            identity=0.9, gc=0.41, alphabet_noise=True)
     for mode in (0, 1):
         p = params_of(SEED_PATTERN, max_hits=3_000, entropy_mode=mode)
-        eng = engine(p)
+        eng = engine(p, materialize_mode=mat)
         eng.upload_reference(ref)
         eng.upload_query(qry, strand=1)
         o, _, _ = oracle_pass(ref, qry, p, strand="-")
@@ -463,7 +466,8 @@ def test_run_batch_reverse_strand_and_entropy():
                               acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 
 
-def test_run_batch_survivors_grow_mid_batch():
+@pytest.mark.parametrize("mat", [0, 2], ids=["default-walks", "shared-walks"])
+def test_run_batch_survivors_grow_mid_batch(mat):
     # run_batch queues chunk c + 1's gate and survivor compaction before it reads chunk
     # c's counts.  Here the early chunks keep nothing and the last ones keep thousands of
     # anchors (the query ends with copies of reference stretches), so the survivor buffers
@@ -476,7 +480,7 @@ def test_run_batch_survivors_grow_mid_batch():
                           acgt[rng.integers(0, 4, 3_000)], ref[15_000:16_500]])
     # a weight-6 seed fills the first chunks with random anchors that all fail the gate
     p = params_of("11101101", max_hits=20_000)
-    eng = engine(p)
+    eng = engine(p, materialize_mode=mat)
     eng.upload_reference(ref)
     eng.upload_query(qry)
     o, _, _ = oracle_pass(ref, qry, p)
