@@ -36,9 +36,11 @@ constexpr int kWaves = 1;  // one wave per workgroup: a finished walk frees its 
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTab4 = 96;  // pair indices r * 16 + q for codes up to 5
 constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower on long walks)
-// Window of the shared walks' lane stage, in blocks of eight bases per side: about 1% of
-// the walks on dense tandem repeats run past 96 bases.
-constexpr int kLaneBlocks = 12;
+// Window of the shared walks' lane stage, in blocks of eight bases per side: about 0.3% of
+// the walks on dense tandem repeats run past 128 bases.  Per 1.04 M-survivor chunk, lane
+// stage + listed walks measured 183 + 51, 110 + 26, 84 + 17 and 93 + 15 us at 8, 12, 16
+// and 24 blocks.
+constexpr int kLaneBlocks = 16;
 constexpr int kLanePrefetch = 3;  // blocks each lane reads ahead
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
