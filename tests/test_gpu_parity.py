@@ -682,6 +682,54 @@ def test_materialize_every_anchor_near_the_ends(seed, mat):
     assert bad.size == 0, f"{bad.size} records differ, first anchors {a[ok][bad[:5]]}"
 
 
+@pytest.mark.parametrize("identity", [1.0, 0.93], ids=["identical", "mutated"])
+def test_shared_walks_at_the_lane_window_edges(identity):
+    # survivors on the main diagonal of a sequence and a copy of it, spaced so that a walk
+    # merges into its neighbour on the last bases of the lane stage's window, on the first
+    # bases past it (the walk goes to the one-wave list), and around the 64- and 512-base
+    # tile edges; on identical sequences every walk merges exactly at its neighbour's start
+    import torch
+    rng = np.random.default_rng(91)
+    acgt = np.frombuffer(b"ACGT", np.uint8)
+    ref = acgt[rng.integers(0, 4, 24_000)].copy()
+    qry = ref.copy()
+    if identity < 1.0:  # substitutions, each to one of the three other bases
+        code = np.zeros(256, np.int64)
+        code[acgt] = np.arange(4)
+        flip = rng.random(qry.size) > identity
+        qry[flip] = acgt[(code[qry[flip]] + rng.integers(1, 4, int(flip.sum()))) % 4]
+    gaps = [1, 2, 7, 8, 9, 63, 64, 65, 127, 128, 129, 130, 136, 255, 256, 257, 511, 512, 513]
+    pos = 200 + np.cumsum(np.tile(gaps, 8))
+    pos = pos[pos < ref.size - 200]
+    # the main diagonal, plus every third position again on an unrelated diagonal
+    r = np.concatenate([pos, pos[::3] + 5_000])
+    q = np.concatenate([pos, pos[::3]])
+    keep = (r < ref.size) & (q < qry.size)
+    a = (r[keep].astype(np.uint64) | (q[keep].astype(np.uint64) << np.uint64(32)))
+    a = a[rng.permutation(a.size)]
+    p = params_of(SEED_PATTERN)
+    T = oracle.keep_threshold(p["hsp_threshold"])
+    R = oracle.Reference(ref, p["seed_pattern"])
+    qc = oracle.strand_codes(qry, "+")
+    ids = np.arange(a.size, dtype=np.uint32)
+    oh, ost = oracle.materialize(a, ids, R.codes, qc, p["sub"], p["n_score"], p["xdrop"], T)
+    assert ost.sum() > 0
+    for mat in (1, 2):
+        eng = engine(p, materialize_mode=mat)
+        eng.upload_reference(ref)
+        eng.upload_query(qry)
+        at = torch.from_numpy(a.view(np.int64)).cuda()
+        it = torch.from_numpy(ids.view(np.int32)).cuda()
+        hsp = torch.empty((a.size, 4), dtype=torch.int32, device="cuda")
+        st = torch.empty(a.size, dtype=torch.uint8, device="cuda")
+        eng.materialize(at, it, a.size, hsp, st)
+        gs = st.cpu().numpy()
+        gh = hsp.cpu().numpy().view(oracle.HSP_DTYPE).reshape(-1)
+        assert np.array_equal(gs, ost), f"mode {mat}: status differs"
+        ok = ost == 1
+        assert np.array_equal(gh[ok], oh[ok]), f"mode {mat}: records differ"
+
+
 def test_shared_walks_on_tandem_repeats_and_duplicates():
     # shared walks where they pay: a tandem array (thousands of survivors on a few
     # diagonals, long chains of merges), plus every survivor listed twice (equal anchors
