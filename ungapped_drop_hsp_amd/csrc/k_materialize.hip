@@ -1,24 +1,27 @@
 // Exact X-drop materialization ("E. X-drop materialization", E.1-E.5).
 //
 // Two ways to the same records:
-//  - k_materialize: one wave per survivor walks both sides on its own.
-//  - the diagonal-shared walks (k_mm_*), for calls with many survivors: survivors are
-//    sorted stably by reference end and then by diagonal, so each one's neighbours on
-//    its diagonal sit next to it.  One wave per survivor walks each side until its drop,
-//    or until it sets a strictly new best at or past its neighbour's start: from there
-//    the two walks are one (same later bases, same running best, same drop, and every
-//    base scored before lies below that best), so it stops and keeps its running score
-//    at the neighbour's start.  A side that merged takes the best of the first walk
-//    along its chain that ran to its drop, plus the summed scores of the starts in
-//    between, and that walk's extent plus the distance to it; prefix sums and the list
-//    of walks that ran to their drops give every survivor its chain end at once.  On
-//    tandem repeats, where thousands of survivors share a diagonal, this walks each
-//    stretch of the diagonal about once instead of once per survivor.
-//
-// One wave per survivor walks both sides with exact_walk_tiles over the 4-bit copies
-// (512-base tiles, eight bases per lane, the next tile read ahead; earliest endpoints).  With the
-// entropy-adjusted decision on, the wave then counts the record's reference bases
-// (entropy_accept).  Lane 0 stores the 16-byte record and the status.
+//  - k_materialize: one wave per survivor walks both sides on its own, with
+//    exact_walk_tiles over the 4-bit copies (512-base tiles, eight bases per lane, the
+//    next tile read ahead; earliest endpoints).  With the entropy-adjusted decision on,
+//    the wave then counts the record's reference bases (entropy_accept).  Lane 0 stores
+//    the 16-byte record and the status.
+//  - the diagonal-shared walks (k_mm_*), for calls with many survivors.  Survivors are
+//    sorted stably by diagonal (after a sort by reference end, unless the caller knows
+//    their query ends never decrease), so each one's neighbours on its diagonal sit next
+//    to it, and k_mm_gather lays their anchors out in that order.  Each side's walk stops
+//    at its drop, or at its first strictly new best at or past its neighbour's start:
+//    from there the two walks are one (same later bases, same running best, same drop,
+//    and every base scored before lies below that best), so it keeps only its running
+//    score at the neighbour's start.  k_mm_lanes walks every side one lane each, for up
+//    to 128 bases in eight-base blocks, and lists the walks still open; k_mm_list walks
+//    those one wave each in 512-base tiles.  A side that merged takes the best of the
+//    first walk along its chain that ran to its drop, plus the summed scores at the starts
+//    in between, and that walk's extent plus the distance to it: one scan over both
+//    sides (k_mm_scan_*) gives the sums and the ordered list of drop-ended walks, and
+//    k_mm_finish forms every record.  On tandem repeats, where thousands of survivors
+//    share a diagonal, this walks each stretch of a diagonal about once instead of once
+//    per survivor.
 #include <algorithm>
 #include <climits>
 
@@ -42,6 +45,9 @@ constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower o
 // and 24 blocks.
 constexpr int kLaneBlocks = 16;
 constexpr int kLanePrefetch = 3;  // blocks each lane reads ahead
+// Largest grid of the one-wave-per-survivor kernels (a launch holds fewer than 2^32
+// threads); beyond it each workgroup strides over several survivors.
+constexpr uint32_t kWaveGridMax = 1u << 22;
 
 __device__ __forceinline__ double xlog2x(uint32_t c) {
 #pragma clang fp contract(off)
@@ -86,34 +92,40 @@ __global__ __launch_bounds__(kThreads) void k_materialize(
         tab4[i] = (r <= kCodeEdge && q <= kCodeEdge) ? sp.tab[(r << kRefShift) | q] : 0;
     }
     __syncthreads();
-    const uint32_t i = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (i >= n_surv) return;
-    const uint64_t a = anchors[ids[i]];
-    const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
-    const bool bad = r > sp.n_ref || q > sp.n_qry;  // outside the sequences: empty walks
-    int32_t R, L;
-    uint32_t k, m;
-    exact_walk_tiles<+1, true, kPer, true>(tab4, ref4, qry4, kPad4 + (bad ? sp.n_ref : r),
-                                     kPad4 + (bad ? sp.n_qry : q), sp.xdrop, INT32_MAX, R, k);
-    exact_walk_tiles<-1, true, kPer, true>(tab4, ref4, qry4, kPad4 + (bad ? 0u : r),
-                                     kPad4 + (bad ? 0u : q), sp.xdrop, INT32_MAX, L, m);
-    const int64_t total = (int64_t)L + (int64_t)R;
-    bool ok = total >= (int64_t)sp.T;  // wave-uniform
-    if (ok && sp.entropy_mode == 1) ok = entropy_accept(ref, r - m, m + k - 1u, total, sp.K);
-    if (lane_id() == 0) {
-        hspz_segment_pair rec;
-        rec.ref_start = r - m;
-        rec.query_start = q - m;
-        rec.len = m + k - 1u;
-        rec.score = (int32_t)total;
-        hsp[i] = rec;
-        status[i] = ok ? 1 : 0;
+    // a wave per survivor; a grid capped at kWaveGridMax workgroups strides over the rest
+    for (uint64_t i64 = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); i64 < n_surv;
+         i64 += (uint64_t)gridDim.x * kWaves) {
+        const uint32_t i = (uint32_t)i64;
+        const uint64_t a = anchors[ids[i]];
+        const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
+        const bool bad = r > sp.n_ref || q > sp.n_qry;  // outside the sequences: empty walks
+        int32_t R, L;
+        uint32_t k, m;
+        exact_walk_tiles<+1, true, kPer, true>(tab4, ref4, qry4, kPad4 + (bad ? sp.n_ref : r),
+                                               kPad4 + (bad ? sp.n_qry : q), sp.xdrop,
+                                               INT32_MAX, R, k);
+        exact_walk_tiles<-1, true, kPer, true>(tab4, ref4, qry4, kPad4 + (bad ? 0u : r),
+                                               kPad4 + (bad ? 0u : q), sp.xdrop, INT32_MAX, L,
+                                               m);
+        const int64_t total = (int64_t)L + (int64_t)R;
+        bool ok = total >= (int64_t)sp.T;  // wave-uniform
+        if (ok && sp.entropy_mode == 1) ok = entropy_accept(ref, r - m, m + k - 1u, total, sp.K);
+        if (lane_id() == 0) {
+            hspz_segment_pair rec;
+            rec.ref_start = r - m;
+            rec.query_start = q - m;
+            rec.len = m + k - 1u;
+            rec.score = (int32_t)total;
+            hsp[i] = rec;
+            status[i] = ok ? 1 : 0;
+        }
     }
 }
 
-// Sort keys: the reference end (first pass) and the diagonal r - q + n_qry (second pass,
-// stable); an anchor outside the sequences gets the diagonal key n_ref + n_qry + 1 and never
-// merges.
+// Sort keys: the reference end (first pass; skipped when the query ends already never
+// decrease) and the diagonal r - q + n_qry (second pass, stable); an anchor outside the
+// sequences gets the diagonal key n_ref + n_qry + 1 and never merges.  Also clears the
+// lane stage's open-walk counts.
 __global__ __launch_bounds__(256) void k_mm_keys(const uint64_t *__restrict__ anchors,
                                                  const uint32_t *__restrict__ ids, uint32_t n,
                                                  uint32_t n_ref, uint32_t n_qry,
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(256) void k_mm_keys(const uint64_t *__restrict__ an
                                                  uint32_t *__restrict__ val,
                                                  uint32_t *__restrict__ lcnt) {
     const uint32_t i = blockIdx.x * 256 + threadIdx.x;
-    if (i < 2) lcnt[i] = 0;  // the lane stage's deferred-walk counts
+    if (i < 2) lcnt[i] = 0;
     if (i >= n) return;
     const uint64_t a = anchors[ids[i]];
     const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
@@ -155,12 +167,11 @@ __global__ __launch_bounds__(256) void k_mm_gather(const uint64_t *__restrict__ 
 }
 
 // Sorted survivor s (sa: the anchors in sorted order): its anchor and the walk indices of
-// its neighbours' starts on its
-// diagonal (UINT32_MAX for none).  The right neighbour is the next survivor on the
-// diagonal (its right walk starts at base rn, i.e. after walk index rn - 1 - r of this
-// one); the left neighbour is the previous one (its left walk starts below base rp, walk
-// index r - 1 - rp of this one).  A neighbour at the same reference end (a duplicate
-// anchor) is none.
+// its neighbours' starts on its diagonal (UINT32_MAX for none).  The right neighbour is
+// the next survivor on the diagonal (its right walk starts at base rn, i.e. after walk
+// index rn - 1 - r of this one); the left neighbour is the previous one (its left walk
+// starts below base rp, walk index r - 1 - rp of this one).  A neighbour at the same
+// reference end (a duplicate anchor) is none.
 struct MmAnchor {
     uint32_t r, q, wr, wl;
     bool bad;  // outside the sequences: both walks are empty
@@ -325,13 +336,13 @@ __global__ __launch_bounds__(256) void k_mm_lanes(
             uint32_t ext;
             bool merged, done;
             if (side == 0)
-                done = lane_merge_walk<+1, NB, kLanePrefetch>(tab4, ref4, qry4, kPad4 + (A.bad ? sp.n_ref : A.r),
-                                               kPad4 + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr,
-                                               best, ext, merged, ds);
+                done = lane_merge_walk<+1, NB, kLanePrefetch>(
+                    tab4, ref4, qry4, kPad4 + (A.bad ? sp.n_ref : A.r),
+                    kPad4 + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr, best, ext, merged, ds);
             else
-                done = lane_merge_walk<-1, NB, kLanePrefetch>(tab4, ref4, qry4, kPad4 + (A.bad ? 0u : A.r),
-                                               kPad4 + (A.bad ? 0u : A.q), sp.xdrop, A.wl, best,
-                                               ext, merged, ds);
+                done = lane_merge_walk<-1, NB, kLanePrefetch>(
+                    tab4, ref4, qry4, kPad4 + (A.bad ? 0u : A.r), kPad4 + (A.bad ? 0u : A.q),
+                    sp.xdrop, A.wl, best, ext, merged, ds);
             if (done) mm_store(side == 0 ? right : left, s, best, ext, merged, ds);
             open[side] = !done;
         }
@@ -343,7 +354,8 @@ __global__ __launch_bounds__(256) void k_mm_lanes(
         unsigned long long at = 0;
         if (lane_id() == 0)
             at = atomicAdd(reinterpret_cast<unsigned long long *>(lcnt),
-                           ((unsigned long long)__popcll(ml) << 32) | (unsigned long long)__popcll(mr));
+                           ((unsigned long long)__popcll(ml) << 32) |
+                               (unsigned long long)__popcll(mr));
         const uint32_t at_r = __shfl((uint32_t)at, 0, 64);
         const uint32_t at_l = __shfl((uint32_t)(at >> 32), 0, 64);
         if (open[0]) list[at_r + lane_rank(mr)] = s;
@@ -353,33 +365,36 @@ __global__ __launch_bounds__(256) void k_mm_lanes(
 
 // One wave per sorted survivor: its right walk (neighbour: the next survivor on the
 // diagonal) and its left walk (neighbour: the previous one), each a one-wave merge walk.
-__global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ sa, const uint32_t *__restrict__ key_d, uint32_t n,
+__global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ sa,
+                                                const uint32_t *__restrict__ key_d, uint32_t n,
                                                 const uint8_t *__restrict__ ref,
                                                 const uint8_t *__restrict__ qry, ScoreParams sp,
                                                 MatSide right, MatSide left) {
     __shared__ int32_t tab[kTabSize];
     if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
     __syncthreads();
-    const uint32_t s = blockIdx.x;
-    if (s >= n) return;
-    const MmAnchor A = mm_anchor(sa, key_d, n, s, sp);
-    const uint8_t *rr = ref + (A.bad ? sp.n_ref : A.r), *qr = qry + (A.bad ? sp.n_qry : A.q);
-    const uint8_t *rl = ref + (A.bad ? 0u : A.r), *ql = qry + (A.bad ? 0u : A.q);
-    int32_t R, L, dr, dlft;
-    uint32_t k, m;
-    bool mr, ml;
-    exact_walk_merge<+1, 1>(tab, rr, qr, sp.xdrop, A.wr, R, k, mr, dr);
-    exact_walk_merge<-1, 1>(tab, rl, ql, sp.xdrop, A.wl, L, m, ml, dlft);
-    if (lane_id() == 0) {
-        mm_store(right, s, R, k, mr, dr);
-        mm_store(left, s, L, m, ml, dlft);
+    for (uint64_t s64 = blockIdx.x; s64 < n; s64 += gridDim.x) {
+        const uint32_t s = (uint32_t)s64;
+        const MmAnchor A = mm_anchor(sa, key_d, n, s, sp);
+        const uint8_t *rr = ref + (A.bad ? sp.n_ref : A.r), *qr = qry + (A.bad ? sp.n_qry : A.q);
+        const uint8_t *rl = ref + (A.bad ? 0u : A.r), *ql = qry + (A.bad ? 0u : A.q);
+        int32_t R, L, dr, dlft;
+        uint32_t k, m;
+        bool mr, ml;
+        exact_walk_merge<+1, 1>(tab, rr, qr, sp.xdrop, A.wr, R, k, mr, dr);
+        exact_walk_merge<-1, 1>(tab, rl, ql, sp.xdrop, A.wl, L, m, ml, dlft);
+        if (lane_id() == 0) {
+            mm_store(right, s, R, k, mr, dr);
+            mm_store(left, s, L, m, ml, dlft);
+        }
     }
 }
 
 // The walks the lane stage left open: one wave per listed walk (right walks first), a
 // fixed grid striding over the counts read on the device.  They include the chain ends
 // that run thousands of bases, so they walk 512-base tiles from the 4-bit copies.
-__global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ sa, const uint32_t *__restrict__ key_d, uint32_t n,
+__global__ __launch_bounds__(256) void k_mm_list(const uint64_t *__restrict__ sa,
+                                                 const uint32_t *__restrict__ key_d, uint32_t n,
                                                  const uint32_t *__restrict__ ref4,
                                                  const uint32_t *__restrict__ qry4,
                                                  ScoreParams sp, MatSide right, MatSide left,
@@ -540,8 +555,9 @@ __global__ __launch_bounds__(256) void k_mm_scan_add(MatSide right, MatSide left
 // drop-ended walk t >= s (its bests add the scores at the starts s .. t - 1); a left chain
 // to the last drop-ended walk t <= s (scores at starts t + 1 .. s).
 __global__ __launch_bounds__(256) void k_mm_finish(
-    const uint64_t *__restrict__ sa, const uint32_t *__restrict__ val, uint32_t n, MatSide right, MatSide left,
-    hspz_segment_pair *__restrict__ hsp, uint8_t *__restrict__ status, int32_t T) {
+    const uint64_t *__restrict__ sa, const uint32_t *__restrict__ val, uint32_t n,
+    MatSide right, MatSide left, hspz_segment_pair *__restrict__ hsp,
+    uint8_t *__restrict__ status, int32_t T) {
     const uint32_t s = blockIdx.x * 256 + threadIdx.x;
     if (s >= n) return;
     const uint32_t j = val[s];
@@ -583,11 +599,13 @@ __global__ __launch_bounds__(64) void k_mm_entropy(const hspz_segment_pair *__re
                                                    uint8_t *__restrict__ status, uint32_t n,
                                                    const uint8_t *__restrict__ ref,
                                                    ScoreParams sp) {
-    const uint32_t i = blockIdx.x;
-    if (i >= n || status[i] == 0) return;  // uniform
-    const hspz_segment_pair rec = hsp[i];
-    const bool ok = entropy_accept(ref, rec.ref_start, rec.len, rec.score, sp.K);
-    if (lane_id() == 0) status[i] = ok ? 1 : 0;
+    for (uint64_t i64 = blockIdx.x; i64 < n; i64 += gridDim.x) {
+        const uint32_t i = (uint32_t)i64;
+        if (status[i] == 0) continue;  // uniform
+        const hspz_segment_pair rec = hsp[i];
+        const bool ok = entropy_accept(ref, rec.ref_start, rec.len, rec.score, sp.K);
+        if (lane_id() == 0) status[i] = ok ? 1 : 0;
+    }
 }
 
 }  // namespace
@@ -619,14 +637,14 @@ hipError_t launch_mm_gather(const uint64_t *anchors, const uint32_t *ids, const 
 }
 
 hipError_t launch_mm_walk(const uint64_t *sa, const uint32_t *key_d, uint32_t n,
-                          const uint8_t *ref,
-                          const uint8_t *qry, const uint32_t *ref4, const uint32_t *qry4,
+                          const uint8_t *ref, const uint8_t *qry, const uint32_t *ref4,
+                          const uint32_t *qry4,
                           const ScoreParams &sp, const MatSide &right, const MatSide &left,
                           bool lanes, uint32_t *list, uint32_t *lcnt, hipStream_t s) {
     if (n == 0) return hipSuccess;
     if (!lanes) {
-        hipLaunchKernelGGL(k_mm_walk, dim3(n), dim3(64), 0, s, sa, key_d, n, ref, qry, sp, right,
-                           left);
+        hipLaunchKernelGGL(k_mm_walk, dim3(std::min(n, kWaveGridMax)), dim3(64), 0, s, sa, key_d,
+                           n, ref, qry, sp, right, left);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_mm_lanes<kLaneBlocks>, dim3((n + 255) / 256), dim3(256), 0, s, sa, key_d,
@@ -657,7 +675,8 @@ hipError_t launch_mm_finish(const uint64_t *sa, const uint32_t *val,
     hipLaunchKernelGGL(k_mm_finish, dim3((n + 255) / 256), dim3(256), 0, s, sa, val, n,
                        right, left, hsp, status, sp.T);
     if (sp.entropy_mode == 1)
-        hipLaunchKernelGGL(k_mm_entropy, dim3(n), dim3(64), 0, s, hsp, status, n, ref, sp);
+        hipLaunchKernelGGL(k_mm_entropy, dim3(std::min(n, kWaveGridMax)), dim3(64), 0, s, hsp,
+                           status, n, ref, sp);
     return hipGetLastError();
 }
 
@@ -666,7 +685,7 @@ hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint
                               const uint32_t *ref4, const uint32_t *qry4, const ScoreParams &sp,
                               hipStream_t s) {
     if (n_surv == 0) return hipSuccess;
-    const uint32_t blocks = (n_surv + kWaves - 1) / kWaves;
+    const uint32_t blocks = std::min((n_surv + kWaves - 1) / kWaves, kWaveGridMax);
     hipLaunchKernelGGL(k_materialize, dim3(blocks), dim3(kThreads), 0, s, anchors, ids, n_surv,
                        hsp, status, ref, ref4, qry4, sp);
     return hipGetLastError();
