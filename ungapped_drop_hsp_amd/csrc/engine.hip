@@ -940,8 +940,10 @@ static int compact_common(Engine *e, const uint8_t *d_flags, uint64_t n, uint32_
     if (rc) return rc;
     if ((rc = ensure_compact(e, n))) return rc;
     const uint32_t c32 = (uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull);
-    HIP_TRY(e, launch_compact(d_flags, (uint32_t)n, e->d_cblk, e->d_ctotal, ids, rin, rout, c32, s));
-    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_ctotal, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(e, launch_compact(d_flags, (uint32_t)n, e->d_cblk, e->d_ctotal, ids, rin, rout, c32,
+                              s));
+    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_ctotal, sizeof(uint32_t), hipMemcpyDeviceToHost,
+                              s));
     HIP_TRY(e, hipStreamSynchronize(s));
     const uint64_t total = e->h_pinned[0];
     if (total > cap)
@@ -1177,7 +1179,8 @@ static int count_queue(Engine *e, const uint8_t *flags, uint64_t n, uint32_t *id
                        int slot, hipStream_t s) {
     if (n >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n must be < 2^32");
     if ((n + kCompactBlock - 1) / kCompactBlock + 1 > e->cap_cblk)
-        return fail(e, HSPZ_E_INVALID, "compaction scratch not sized for %llu", (unsigned long long)n);
+        return fail(e, HSPZ_E_INVALID, "compaction scratch not sized for %llu",
+                    (unsigned long long)n);
     uint32_t *d_total = e->d_ctotal + 4 * (slot + 1);
     uint32_t *h_total = e->h_pinned + 16 + 4 * slot;
     const uint32_t c32 = (uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull);
