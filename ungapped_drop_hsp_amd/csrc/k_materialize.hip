@@ -381,8 +381,8 @@ __global__ __launch_bounds__(64) void k_mm_walk(const uint64_t *__restrict__ sa,
         int32_t R, L, dr, dlft;
         uint32_t k, m;
         bool mr, ml;
-        exact_walk_merge<+1, 1>(tab, rr, qr, sp.xdrop, A.wr, R, k, mr, dr);
-        exact_walk_merge<-1, 1>(tab, rl, ql, sp.xdrop, A.wl, L, m, ml, dlft);
+        exact_walk_merge<+1, true>(tab, rr, qr, sp.xdrop, A.wr, R, k, mr, dr);
+        exact_walk_merge<-1, true>(tab, rl, ql, sp.xdrop, A.wl, L, m, ml, dlft);
         if (lane_id() == 0) {
             mm_store(right, s, R, k, mr, dr);
             mm_store(left, s, L, m, ml, dlft);

@@ -20,17 +20,14 @@ namespace hspz {
 // below that best).  The walk then stops with merged = true and ds = its running score at
 // index wm (0 when wm is past its start already); the caller adds ds to the neighbour's
 // best and the anchors' distance to the neighbour's extent.  Otherwise it runs to its drop
-// like exact_walk with Ext (merged = false; best and ext are its own).  The scores of
-// the next Ahead tiles are read while a tile is scored, so that a long walk does not wait
-// on memory at every tile; the walk reads at most 64 * (Ahead + 1) + 63 bases past the
-// first edge base, inside the padding.
-template <int D, int Ahead>
+// like exact_walk with Ext (merged = false; best and ext are its own).  With ReadAhead
+// the next tile's scores are read while a tile is scored; the walk reads at most 127
+// bases past the first edge base, inside the padding.
+template <int D, bool ReadAhead>
 __device__ __forceinline__ void exact_walk_merge(const int32_t *tab, const uint8_t *rp,
                                                  const uint8_t *qp, int32_t xdrop, uint32_t wm,
                                                  int32_t &best_out, uint32_t &ext_out,
                                                  bool &merged, int32_t &ds) {
-    static_assert(Ahead >= 0 && 64 * (Ahead + 1) + 64 <= kPad,
-                  "the tiles read ahead must stay inside the edge padding");
     const int l = lane_id();
     int32_t best = 0, carry = 0;
     uint32_t ext = 0, base = 0;
@@ -40,14 +37,9 @@ __device__ __forceinline__ void exact_walk_merge(const int32_t *tab, const uint8
         const int64_t off = D > 0 ? (int64_t)b + l : -(int64_t)b - 1 - l;
         return tab[rp[off] | qp[off]];
     };
-    int32_t ring[Ahead + 1];  // ring[a]: the scores of tile base + 64 a
-#pragma unroll
-    for (int a = 0; a <= Ahead; a++) ring[a] = score(64u * (uint32_t)a);
+    int32_t sg = score(0);
     for (;;) {
-        const int32_t sg = ring[0];
-#pragma unroll
-        for (int a = 0; a < Ahead; a++) ring[a] = ring[a + 1];
-        if (Ahead > 0) ring[Ahead] = score(base + 64u * (uint32_t)(Ahead + 1));
+        const int32_t sg_next = ReadAhead ? score(base + 64) : 0;
         const int32_t s = wave_incl_sum(sg) + carry;
         const int32_t run_best = max(wave_incl_max(s), best);
         int32_t prev = __shfl_up(run_best, 1, 64);  // running best before this lane's base
@@ -72,7 +64,7 @@ __device__ __forceinline__ void exact_walk_merge(const int32_t *tab, const uint8
         if (dm) break;
         carry = lane_value(s, 63);
         base += 64;
-        if (Ahead == 0) ring[0] = score(base);
+        sg = ReadAhead ? sg_next : score(base);
     }
     best_out = best;
     ext_out = ext;
