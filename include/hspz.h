@@ -31,8 +31,9 @@
  *    kernel-launching call is asynchronous on it.
  *  - An engine is not thread-safe: use one engine per host thread.  Its calls share the
  *    engine's device scratch (the gate's deferred lists, compaction blocks, the bucketed
- *    gate's sorted copy), so calls of one engine on different streams must not overlap:
- *    give an engine one stream, or synchronise between streams.
+ *    gate's sorted copy, the shared walks' sort and per-side arrays), so calls of one
+ *    engine on different streams must not overlap: give an engine one stream, or
+ *    synchronise between streams.
  *  - Coordinates are 0-based.  Sequences are ASCII; A/C/G/T in either case are bases,
  *    every other byte is N.
  */
@@ -247,8 +248,10 @@ int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n, uint32
  * With left extent m and right extent k the record is
  * {r - m, q - m, m + k - 1, L* + R*}.  d_status[i] = 1 if the record is accepted
  * (score >= T, and with entropy_mode 1 also score * H >= 2K, see hspz_params), else 0;
- * d_hsp[i] is written in either case and is meaningful only when accepted.
- * Errors: HSPZ_E_STATE, HSPZ_E_HIP. */
+ * d_hsp[i] is written in either case and is meaningful only when accepted.  The
+ * diagonal-shared walks (materialize_mode) allocate their scratch in the engine on first
+ * use and keep it.  Errors: HSPZ_E_STATE (no reference or query uploaded), HSPZ_E_INVALID
+ * (n_surv >= 2^32, NULL buffers), HSPZ_E_NOMEM (the shared walks' scratch), HSPZ_E_HIP. */
 int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors, const uint32_t *d_ids,
                      uint64_t n_surv, hspz_segment_pair *d_hsp, uint8_t *d_status,
                      void *stream);
