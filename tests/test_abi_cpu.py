@@ -50,13 +50,18 @@ def test_create_rejects_bad_parameters_without_gpu():
     from workloads import HOXD70
     for kw in (dict(seed_pattern="0111"), dict(seed_pattern="1" * 15),
                dict(seed_pattern="11x1"), dict(hsp_threshold=0), dict(xdrop=-1),
-               dict(expand_mode=3), dict(chunk_walk=2), dict(gate_mode=4)):
+               dict(expand_mode=3), dict(chunk_walk=2), dict(gate_mode=5),
+               dict(gate_mode=-1), dict(entropy_mode=2), dict(ref_buckets=257),
+               dict(ref_buckets=-1), dict(materialize_mode=3), dict(materialize_mode=-1),
+               dict(gate_mode=2, xdrop=600)):  # 7 * max score > X: no exact window gate
         args = dict(seed_pattern="1110100110010101111", sub=HOXD70, n_score=-100, xdrop=910,
                     hsp_threshold=3000)
         args.update(kw)
         with pytest.raises(h.HspzError) as ei:
             h.Engine(**args)
         assert ei.value.code == -1
+        # rejected by the parameter checks, not for want of a device
+        assert "device" not in str(ei.value), (kw, str(ei.value))
 
 
 def test_import_fails_loudly_without_library(tmp_path):

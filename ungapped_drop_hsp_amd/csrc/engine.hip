@@ -418,10 +418,6 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "materialize_mode must be 0, 1 or 2");
     if (p->gate_mode < 0 || p->gate_mode > 4)
         return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2, 3 or 4");
-    int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev)
-        return fail(nullptr, HSPZ_E_INVALID, "device %d not available (%d devices)", p->device,
-                    ndev);
 
     Engine *e = new (std::nothrow) Engine();
     if (!e) return fail(nullptr, HSPZ_E_NOMEM, "engine allocation failed");
@@ -471,9 +467,18 @@ HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     }
     e->wp.xdrop = p->xdrop;
     e->wp.T = e->T;
-    if (p->gate_mode >= 2 && !e->window_ok)
+    if (p->gate_mode >= 2 && !e->window_ok) {
+        delete e;
         return fail(nullptr, HSPZ_E_INVALID,
                     "gate_modes 2, 3 and 4 need 7 * max score <= xdrop and 16-bit pair scores");
+    }
+    // the device last, so that every parameter error is reported as such on any machine
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || p->device < 0 || p->device >= ndev) {
+        delete e;
+        return fail(nullptr, HSPZ_E_INVALID, "device %d not available (%d devices)", p->device,
+                    ndev);
+    }
     int rc = set_device(e);
     if (rc) {
         g_create_error = e->err;
