@@ -383,7 +383,7 @@ void Engine::free_plan() {
 
 using namespace hspz;
 
-HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
+static int impl_hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     if (!out) return fail(nullptr, HSPZ_E_INVALID, "out is NULL");
     *out = nullptr;
     if (!p || !p->seed_pattern) return fail(nullptr, HSPZ_E_INVALID, "params or pattern NULL");
@@ -512,8 +512,8 @@ HSPZ_API const char *hspz_last_error(const hspz_engine *engine) {
     return reinterpret_cast<const Engine *>(engine)->err.c_str();
 }
 
-HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
-                                   void *stream) {
+static int impl_hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                                      void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!h_ascii && len) return fail(e, HSPZ_E_INVALID, "reference pointer is NULL");
@@ -583,8 +583,8 @@ HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, 
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
-                               int32_t strand, void *stream) {
+static int impl_hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                                  int32_t strand, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!h_ascii && len) return fail(e, HSPZ_E_INVALID, "query pointer is NULL");
@@ -624,8 +624,8 @@ HSPZ_API uint64_t hspz_num_seeds(const hspz_engine *engine) {
     return (e && e->has_qry) ? e->n_seeds : 0;
 }
 
-HSPZ_API int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
-                             uint64_t *seed_lo, uint64_t *seed_hi) {
+static int impl_hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
+                                uint64_t *seed_lo, uint64_t *seed_hi) {
     const Engine *ce = reinterpret_cast<const Engine *>(engine);
     Engine *e = const_cast<Engine *>(ce);
     if (!e) return HSPZ_E_INVALID;
@@ -641,8 +641,8 @@ HSPZ_API int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
-                       uint64_t *total_hits, uint32_t *n_chunks) {
+static int impl_hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
+                          uint64_t *total_hits, uint32_t *n_chunks) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!total_hits || !n_chunks) return fail(e, HSPZ_E_INVALID, "NULL output");
@@ -674,8 +674,8 @@ HSPZ_API int hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, 
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64_t n,
-                                    void *stream, uint64_t *total_hits, uint32_t *n_chunks) {
+static int impl_hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64_t n,
+                                       void *stream, uint64_t *total_hits, uint32_t *n_chunks) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!total_hits || !n_chunks || (!h_counts && n))
@@ -704,7 +704,7 @@ HSPZ_API int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_count
     return rc;
 }
 
-HSPZ_API int hspz_get_chunk(const hspz_engine *engine, uint32_t i, hspz_chunk *out) {
+static int impl_hspz_get_chunk(const hspz_engine *engine, uint32_t i, hspz_chunk *out) {
     Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
     if (!e) return HSPZ_E_INVALID;
     if (!out) return fail(e, HSPZ_E_INVALID, "NULL output");
@@ -714,8 +714,8 @@ HSPZ_API int hspz_get_chunk(const hspz_engine *engine, uint32_t i, hspz_chunk *o
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts,
-                                  uint32_t *h_prefix) {
+static int impl_hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts,
+                                     uint32_t *h_prefix) {
     Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
     if (!e) return HSPZ_E_INVALID;
     if (!e->has_plan) return fail(e, HSPZ_E_STATE, "no plan");
@@ -732,8 +732,8 @@ HSPZ_API int hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts,
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi,
-                            uint32_t *h_kmer, uint32_t *h_q_end) {
+static int impl_hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi,
+                               uint32_t *h_kmer, uint32_t *h_q_end) {
     Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
     if (!e) return HSPZ_E_INVALID;
     if (!e->has_qry) return fail(e, HSPZ_E_STATE, "no query uploaded");
@@ -751,8 +751,8 @@ HSPZ_API int hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi,
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_get_index(const hspz_engine *engine, uint32_t *h_end, uint32_t *h_pos,
-                            uint64_t *n_buckets, uint64_t *n_pos) {
+static int impl_hspz_get_index(const hspz_engine *engine, uint32_t *h_end, uint32_t *h_pos,
+                               uint64_t *n_buckets, uint64_t *n_pos) {
     Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
     if (!e) return HSPZ_E_INVALID;
     if (!n_buckets || !n_pos) return fail(e, HSPZ_E_INVALID, "NULL size output");
@@ -770,8 +770,8 @@ HSPZ_API int hspz_get_index(const hspz_engine *engine, uint32_t *h_end, uint32_t
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
-                            uint64_t cap, void *stream) {
+static int impl_hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
+                               uint64_t cap, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!e->has_plan || !e->plan_expandable)
@@ -844,8 +844,8 @@ static int ensure_dir(Engine *e, uint64_t n) {
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
-                             uint8_t *d_flags, void *stream) {
+static int impl_hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                                uint8_t *d_flags, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!e->has_ref || !e->has_qry)
@@ -893,8 +893,8 @@ HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uin
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
-                                 uint64_t cap, uint8_t *d_flags, void *stream) {
+static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
+                                    uint64_t cap, uint8_t *d_flags, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!e->has_plan || !e->plan_expandable)
@@ -958,8 +958,8 @@ static int compact_common(Engine *e, const uint8_t *d_flags, uint64_t n, uint32_
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n,
-                          uint32_t *d_ids, uint64_t cap, uint64_t *n_out, void *stream) {
+static int impl_hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n,
+                             uint32_t *d_ids, uint64_t cap, uint64_t *n_out, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!n_out) return fail(e, HSPZ_E_INVALID, "NULL n_out");
@@ -1108,17 +1108,17 @@ static int materialize(Engine *e, const uint64_t *d_anchors, const uint32_t *d_i
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
-                              const uint32_t *d_ids, uint64_t n_surv, hspz_segment_pair *d_hsp,
-                              uint8_t *d_status, void *stream) {
+static int impl_hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
+                                 const uint32_t *d_ids, uint64_t n_surv, hspz_segment_pair *d_hsp,
+                                 uint8_t *d_status, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     return materialize(e, d_anchors, d_ids, n_surv, d_hsp, d_status, false, stream);
 }
 
-HSPZ_API int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
-                               const uint8_t *d_status, uint64_t n, hspz_segment_pair *d_out,
-                               uint64_t cap, uint64_t *n_out, void *stream) {
+static int impl_hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
+                                  const uint8_t *d_status, uint64_t n, hspz_segment_pair *d_out,
+                                  uint64_t cap, uint64_t *n_out, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!n_out) return fail(e, HSPZ_E_INVALID, "NULL n_out");
@@ -1205,8 +1205,8 @@ static int count_wait(Engine *e, int slot, uint64_t cap, uint64_t *n_out) {
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi,
-                            int32_t time_gate, hspz_batch_stats *stats, void *stream) {
+static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi,
+                               int32_t time_gate, hspz_batch_stats *stats, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!stats) return fail(e, HSPZ_E_INVALID, "NULL stats");
@@ -1315,8 +1315,8 @@ HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_get_batch_records(const hspz_engine *engine, hspz_segment_pair *h_out,
-                                    uint64_t cap, uint64_t *n) {
+static int impl_hspz_get_batch_records(const hspz_engine *engine, hspz_segment_pair *h_out,
+                                       uint64_t cap, uint64_t *n) {
     Engine *e = const_cast<Engine *>(reinterpret_cast<const Engine *>(engine));
     if (!e) return HSPZ_E_INVALID;
     if (!n || (!h_out && cap)) return fail(e, HSPZ_E_INVALID, "NULL argument");
@@ -1358,8 +1358,8 @@ int no_engine_fail(int code, const char *msg) {
 
 }  // namespace
 
-HSPZ_API int hspz_dedup_records(const hspz_segment_pair *h_in, uint64_t n,
-                                hspz_segment_pair *h_out, uint64_t cap, uint64_t *n_out) {
+static int impl_hspz_dedup_records(const hspz_segment_pair *h_in, uint64_t n,
+                                   hspz_segment_pair *h_out, uint64_t cap, uint64_t *n_out) {
     if (!n_out) return no_engine_fail(HSPZ_E_INVALID, "NULL n_out");
     *n_out = 0;
     if (n && (!h_in || !h_out)) return no_engine_fail(HSPZ_E_INVALID, "NULL records");
@@ -1385,8 +1385,8 @@ HSPZ_API int hspz_dedup_records(const hspz_segment_pair *h_in, uint64_t n,
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
-                                   uint64_t *total_steps, void *stream) {
+static int impl_hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                                      uint64_t *total_steps, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!total_steps) return fail(e, HSPZ_E_INVALID, "NULL output");
@@ -1417,8 +1417,8 @@ HSPZ_API int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchor
     return HSPZ_OK;
 }
 
-HSPZ_API int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2,
-                                      uint64_t *n_exact, void *stream) {
+static int impl_hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2,
+                                         uint64_t *n_exact, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!n_stage2 || !n_exact) return fail(e, HSPZ_E_INVALID, "NULL output");
@@ -1435,4 +1435,208 @@ HSPZ_API int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2,
     *n_stage2 = e->h_pinned[0];
     *n_exact = e->h_pinned[1];
     return HSPZ_OK;
+}
+
+// ---- exception barrier ----------------------------------------------------------------
+// Every int-returning entry point runs its implementation inside a handler, so that no
+// C++ exception (an allocation failure in a host-side vector or string) crosses the C ABI:
+// it becomes HSPZ_E_NOMEM with a fixed message.
+static int api_exception(Engine *e) noexcept {
+    try {
+        fail(e, HSPZ_E_NOMEM, "host allocation failed");
+    } catch (...) {
+    }
+    return HSPZ_E_NOMEM;
+}
+
+HSPZ_API int hspz_engine_create(const hspz_params *p, hspz_engine **out) {
+    try {
+        return impl_hspz_engine_create(p, out);
+    } catch (...) {
+        return api_exception(nullptr);
+    }
+}
+
+HSPZ_API int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                                   void *stream) {
+    try {
+        return impl_hspz_upload_reference(engine, h_ascii, len, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
+                               int32_t strand, void *stream) {
+    try {
+        return impl_hspz_upload_query(engine, h_ascii, len, strand, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
+                             uint64_t *seed_lo, uint64_t *seed_hi) {
+    try {
+        return impl_hspz_seed_range(engine, pos_lo, pos_hi, seed_lo, seed_hi);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
+                       uint64_t *total_hits, uint32_t *n_chunks) {
+    try {
+        return impl_hspz_plan(engine, seed_lo, seed_hi, stream, total_hits, n_chunks);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64_t n,
+                                    void *stream, uint64_t *total_hits, uint32_t *n_chunks) {
+    try {
+        return impl_hspz_debug_plan_counts(engine, h_counts, n, stream, total_hits, n_chunks);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_get_chunk(const hspz_engine *engine, uint32_t i, hspz_chunk *out) {
+    try {
+        return impl_hspz_get_chunk(engine, i, out);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts,
+                                  uint32_t *h_prefix) {
+    try {
+        return impl_hspz_get_plan_arrays(engine, h_counts, h_prefix);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_get_seeds(const hspz_engine *engine, uint64_t lo, uint64_t hi,
+                            uint32_t *h_kmer, uint32_t *h_q_end) {
+    try {
+        return impl_hspz_get_seeds(engine, lo, hi, h_kmer, h_q_end);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_get_index(const hspz_engine *engine, uint32_t *h_end, uint32_t *h_pos,
+                            uint64_t *n_buckets, uint64_t *n_pos) {
+    try {
+        return impl_hspz_get_index(engine, h_end, h_pos, n_buckets, n_pos);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
+                            uint64_t cap, void *stream) {
+    try {
+        return impl_hspz_find_hits(engine, chunk, d_anchors, cap, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                             uint8_t *d_flags, void *stream) {
+    try {
+        return impl_hspz_score_gate(engine, d_anchors, n, d_flags, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
+                                 uint64_t cap, uint8_t *d_flags, void *stream) {
+    try {
+        return impl_hspz_find_hits_gate(engine, chunk, d_anchors, cap, d_flags, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n,
+                          uint32_t *d_ids, uint64_t cap, uint64_t *n_out, void *stream) {
+    try {
+        return impl_hspz_compact(engine, d_flags, n, d_ids, cap, n_out, stream);
+    } catch (...) {
+        if (n_out) *n_out = 0;
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors,
+                              const uint32_t *d_ids, uint64_t n_surv, hspz_segment_pair *d_hsp,
+                              uint8_t *d_status, void *stream) {
+    try {
+        return impl_hspz_materialize(engine, d_anchors, d_ids, n_surv, d_hsp, d_status, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_compact_hsps(hspz_engine *engine, const hspz_segment_pair *d_hsp,
+                               const uint8_t *d_status, uint64_t n, hspz_segment_pair *d_out,
+                               uint64_t cap, uint64_t *n_out, void *stream) {
+    try {
+        return impl_hspz_compact_hsps(engine, d_hsp, d_status, n, d_out, cap, n_out, stream);
+    } catch (...) {
+        if (n_out) *n_out = 0;
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi,
+                            int32_t time_gate, hspz_batch_stats *stats, void *stream) {
+    try {
+        return impl_hspz_run_batch(engine, seed_lo, seed_hi, time_gate, stats, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_get_batch_records(const hspz_engine *engine, hspz_segment_pair *h_out,
+                                    uint64_t cap, uint64_t *n) {
+    try {
+        return impl_hspz_get_batch_records(engine, h_out, cap, n);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_dedup_records(const hspz_segment_pair *h_in, uint64_t n,
+                                hspz_segment_pair *h_out, uint64_t cap, uint64_t *n_out) {
+    try {
+        return impl_hspz_dedup_records(h_in, n, h_out, cap, n_out);
+    } catch (...) {
+        if (n_out) *n_out = 0;
+        return api_exception(nullptr);
+    }
+}
+
+HSPZ_API int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                                   uint64_t *total_steps, void *stream) {
+    try {
+        return impl_hspz_debug_walk_steps(engine, d_anchors, n, total_steps, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2,
+                                      uint64_t *n_exact, void *stream) {
+    try {
+        return impl_hspz_debug_gate_deferred(engine, n_stage2, n_exact, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
 }
