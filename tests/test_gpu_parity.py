@@ -496,6 +496,34 @@ def test_run_batch_survivors_grow_mid_batch(mat):
                               acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 
 
+@pytest.mark.parametrize("gate_mode", [0, 1, 3, 4])
+def test_run_batch_shared_walks_on_tandem_repeats(gate_mode):
+    # the batch driver with shared walks (its survivors sorted by diagonal alone) behind
+    # every gate: windowed (0; 3 with a narrower first window), per-base (1) and bucketed
+    # (4); a tandem array gives long chains of merges in each of 17 chunks; counts and
+    # every accepted record against the oracle
+    rng = np.random.default_rng(53)
+    acgt = np.frombuffer(b"ACGT", np.uint8)
+    unit = acgt[rng.integers(0, 4, 61)]
+    arr = np.concatenate([unit] * 60).copy()
+    flip = rng.random(arr.size) < 0.04
+    arr[flip] = acgt[rng.integers(0, 4, int(flip.sum()))]
+    ref = np.concatenate([acgt[rng.integers(0, 4, 5_000)], arr, acgt[rng.integers(0, 4, 3_000)]])
+    qry = np.concatenate([acgt[rng.integers(0, 4, 2_000)], arr[300:], acgt[rng.integers(0, 4, 1_500)]])
+    p = params_of(SEED_PATTERN, max_hits=6_000)
+    eng = engine(p, gate_mode=gate_mode, ref_buckets=8 if gate_mode == 4 else 0,
+                 materialize_mode=2)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    o, _, _ = oracle_pass(ref, qry, p)
+    want, acc = _oracle_batch(o)
+    assert want["n_chunks"] > 2 and want["n_survivors"] > 2_000
+    st = eng.run_batch(0, eng.num_seeds())
+    assert {k: st[k] for k in want} == want
+    assert np.array_equal(eng.batch_records().view(np.uint8),
+                          acc.astype(oracle.HSP_DTYPE).view(np.uint8))
+
+
 def test_run_batch_errors():
     p = params_of(SEED_PATTERN)
     eng = engine(p)
