@@ -758,6 +758,47 @@ def test_shared_walks_at_the_lane_window_edges(identity):
         assert np.array_equal(gh[ok], oh[ok]), f"mode {mat}: records differ"
 
 
+@pytest.mark.parametrize("xdrop", [6, 8], ids=["one-wave-walks", "lane-stage"])
+@pytest.mark.parametrize("gap", [1, 3, 9, 30])
+def test_shared_walks_with_tied_scores(gap, xdrop):
+    # match +1, mismatch -1 and a small X: running scores tie their best all the time, so
+    # a walk may merge only at a strictly new best (a tie would move the earliest extent);
+    # X = 6 leaves eight-base blocks inexact (one wave per survivor), X = 8 runs the lane
+    # stage; records and status in both walk modes against the oracle
+    import torch
+    rng = np.random.default_rng(500 + gap)
+    ref, _ = random_pair(60 + gap, 2_000, 1)
+    qry = ref.copy()
+    acgt = np.frombuffer(b"ACGT", np.uint8)
+    flip = rng.random(qry.size) < 0.3
+    qry[flip] = acgt[rng.integers(0, 4, int(flip.sum()))]
+    sub = np.where(np.eye(4, dtype=bool), 1, -1).astype(np.int32)
+    p = params_of(SEED_PATTERN, sub=sub, xdrop=xdrop, K=10, n_score=-1)
+    pos = np.arange(50, 1_950, gap, dtype=np.uint64)[:500]
+    a = np.concatenate([pos | (pos << np.uint64(32)),
+                        (pos[::4] + np.uint64(1)) | (pos[::4] << np.uint64(32))])
+    T = oracle.keep_threshold(p["hsp_threshold"])
+    R = oracle.Reference(ref, p["seed_pattern"])
+    qc = oracle.strand_codes(qry, "+")
+    ids = np.arange(a.size, dtype=np.uint32)
+    oh, ost = oracle.materialize(a, ids, R.codes, qc, p["sub"], p["n_score"], p["xdrop"], T)
+    assert 0 < ost.sum() < a.size
+    for mat in (1, 2):
+        eng = engine(p, materialize_mode=mat)
+        eng.upload_reference(ref)
+        eng.upload_query(qry)
+        at = torch.from_numpy(a.view(np.int64)).cuda()
+        it = torch.from_numpy(ids.view(np.int32)).cuda()
+        hsp = torch.empty((a.size, 4), dtype=torch.int32, device="cuda")
+        st = torch.empty(a.size, dtype=torch.uint8, device="cuda")
+        eng.materialize(at, it, a.size, hsp, st)
+        gs = st.cpu().numpy()
+        gh = hsp.cpu().numpy().view(oracle.HSP_DTYPE).reshape(-1)
+        assert np.array_equal(gs, ost), f"mode {mat}: status differs"
+        ok = ost == 1
+        assert np.array_equal(gh[ok], oh[ok]), f"mode {mat}: records differ"
+
+
 def test_shared_walks_on_tandem_repeats_and_duplicates():
     # shared walks where they pay: a tandem array (thousands of survivors on a few
     # diagonals, long chains of merges), plus every survivor listed twice (equal anchors
