@@ -759,22 +759,23 @@ def test_shared_walks_at_the_lane_window_edges(identity):
 
 
 @pytest.mark.parametrize("xdrop", [6, 8], ids=["one-wave-walks", "lane-stage"])
-@pytest.mark.parametrize("gap", [1, 3, 9, 30])
+@pytest.mark.parametrize("gap", [1, 3, 9, 30, 150, 600])
 def test_shared_walks_with_tied_scores(gap, xdrop):
     # match +1, mismatch -1 and a small X: running scores tie their best all the time, so
     # a walk may merge only at a strictly new best (a tie would move the earliest extent);
     # X = 6 leaves eight-base blocks inexact (one wave per survivor), X = 8 runs the lane
-    # stage; records and status in both walk modes against the oracle
+    # stage, and gaps of 150 and 600 bases send the merges to the 512-base tile walks of
+    # the listed walks; records and status in both walk modes against the oracle
     import torch
     rng = np.random.default_rng(500 + gap)
-    ref, _ = random_pair(60 + gap, 2_000, 1)
+    ref, _ = random_pair(60 + gap, 2_000 if gap < 100 else 8_000, 1)
     qry = ref.copy()
     acgt = np.frombuffer(b"ACGT", np.uint8)
     flip = rng.random(qry.size) < 0.3
     qry[flip] = acgt[rng.integers(0, 4, int(flip.sum()))]
     sub = np.where(np.eye(4, dtype=bool), 1, -1).astype(np.int32)
     p = params_of(SEED_PATTERN, sub=sub, xdrop=xdrop, K=10, n_score=-1)
-    pos = np.arange(50, 1_950, gap, dtype=np.uint64)[:500]
+    pos = np.arange(50, ref.size - 50, gap, dtype=np.uint64)[:500]
     a = np.concatenate([pos | (pos << np.uint64(32)),
                         (pos[::4] + np.uint64(1)) | (pos[::4] << np.uint64(32))])
     T = oracle.keep_threshold(p["hsp_threshold"])
