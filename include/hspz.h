@@ -179,6 +179,19 @@ int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t 
 int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
                       int32_t strand, void *stream);
 
+/* Replace the current strand's seeds with the caller's ("C. Hit discovery", C.1: a seed
+ * is a packed k-mer and the query end of its window), in place of the device seeder's:
+ * h_kmer[i] < 4^w (w = the pattern's care positions) and h_q_end[i] in [span, query
+ * length], the window starting at h_q_end[i] - span.  The query ends must not decrease
+ * (the order hspz_upload_query produces, on which hspz_seed_range and the batch driver
+ * rely).  The k-mers need not match the query's bases; the uploaded strand stays, since
+ * the walks read it.  Host arrays, copied; invalidates a plan; synchronises stream.
+ * Errors: HSPZ_E_STATE (no query strand uploaded), HSPZ_E_INVALID (NULL arrays, a value
+ * out of range, decreasing query ends; the seeds are left as they were), HSPZ_E_NOMEM,
+ * HSPZ_E_HIP. */
+int hspz_upload_seeds(hspz_engine *engine, const uint32_t *h_kmer, const uint32_t *h_q_end,
+                      uint64_t n, void *stream);
+
 /* Number of seeds of the current query strand. */
 uint64_t hspz_num_seeds(const hspz_engine *engine);
 

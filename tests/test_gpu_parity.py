@@ -524,6 +524,73 @@ def test_run_batch_shared_walks_on_tandem_repeats(gate_mode):
                           acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 
 
+def test_upload_seeds_replaces_the_seeder():
+    # caller seeds in place of the device seeder's ("C. Hit discovery", C.1): every second
+    # seed of the strand, a tenth of them with another k-mer, and some seeds listed twice;
+    # the pass through the per-call ABI and through hspz_run_batch against the oracle's
+    # pass over the same seeds, and the batch ranges over their window starts
+    from ungapped_drop_hsp_amd.pipeline import PassBuffers, run_pass
+    ref, qry = random_pair(83, 40_000, 30_000, plant=40, plant_len=(80, 900), identity=0.9,
+                           n_frac=0.02)
+    p = params_of(SEED_PATTERN, max_hits=20_000)
+    span = len(SEED_PATTERN)
+    R = oracle.Reference(ref, p["seed_pattern"])
+    qc = oracle.strand_codes(qry, "+")
+    kmer, q_end, _ = oracle.query_seeds(qc, p["seed_pattern"])
+    rng = np.random.default_rng(83)
+    k, q = kmer[::2].copy(), q_end[::2].copy()
+    swap = rng.random(k.size) < 0.1
+    k[swap] = rng.integers(0, 4 ** SEED_PATTERN.count("1"), int(swap.sum()))
+    rep = np.sort(rng.choice(k.size, 50, replace=False))
+    k, q = np.insert(k, rep, k[rep]).astype(np.uint32), np.insert(q, rep, q[rep]).astype(np.uint32)
+    o = oracle.run_pass(R, qc, p, seeds=(k, q, q - span))
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    eng.upload_seeds(k, q)
+    assert eng.num_seeds() == k.size
+    g = run_pass(eng, 0, k.size, PassBuffers(), collect=True)
+    g["seeds"] = eng.get_seeds(0, k.size)
+    g["plan_arrays"] = eng.get_plan_arrays(k.size)
+    g["lo"] = 0
+    assert_pass_equal(g, o)
+    assert sum(c["ids"].size for c in o["chunks"]) > 0
+    want, acc = _oracle_batch(o)
+    st = eng.run_batch(0, k.size)
+    assert {kk: st[kk] for kk in want} == want
+    assert np.array_equal(eng.batch_records().view(np.uint8),
+                          acc.astype(oracle.HSP_DTYPE).view(np.uint8))
+    starts = (q - span).astype(np.int64)
+    for lo, hi in [(0, qry.size), (1_000, 20_000), (5, 6)]:
+        assert eng.seed_range(lo, hi) == (int(np.searchsorted(starts, lo)),
+                                          int(np.searchsorted(starts, hi)))
+
+
+def test_upload_seeds_errors():
+    import ungapped_drop_hsp_amd as h
+    ref, qry = random_pair(84, 5_000, 4_000)
+    p = params_of(SEED_PATTERN)
+    span = len(SEED_PATTERN)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    with pytest.raises(h.HspzError) as ei:
+        eng.upload_seeds([1], [span])  # no query strand yet
+    assert ei.value.code == -6
+    eng.upload_query(qry)
+    n = eng.num_seeds()
+    for k, q in (([4 ** SEED_PATTERN.count("1")], [span]),  # k-mer out of range
+                 ([1], [span - 1]), ([1], [qry.size + 1]),  # window outside the query
+                 ([1, 2], [span + 9, span + 8])):           # query ends decrease
+        with pytest.raises(h.HspzError) as ei:
+            eng.upload_seeds(k, q)
+        assert ei.value.code == -1
+        assert eng.num_seeds() == n  # left as they were
+    eng.upload_seeds([], [])
+    assert eng.num_seeds() == 0 and eng.plan(0, 0) == (0, 0)
+    eng.upload_seeds([5, 5], [qry.size, qry.size])  # the last window, twice
+    assert eng.num_seeds() == 2
+
+
 def test_run_batch_errors():
     p = params_of(SEED_PATTERN)
     eng = engine(p)

@@ -32,7 +32,7 @@ ABI_SYMBOLS = (
     "hspz_materialize", "hspz_compact_hsps", "hspz_get_seeds", "hspz_get_plan_arrays",
     "hspz_get_index", "hspz_debug_plan_counts", "hspz_debug_walk_steps",
     "hspz_debug_gate_deferred", "hspz_run_batch", "hspz_get_batch_records",
-    "hspz_find_hits_gate", "hspz_dedup_records",
+    "hspz_find_hits_gate", "hspz_dedup_records", "hspz_upload_seeds",
 )
 
 
@@ -77,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "hspz_last_error": (ctypes.c_char_p, [P]),
         "hspz_upload_reference": (ctypes.c_int, [P, P, U64, P]),
         "hspz_upload_query": (ctypes.c_int, [P, P, U64, I32, P]),
+        "hspz_upload_seeds": (ctypes.c_int, [P, P, P, U64, P]),
         "hspz_num_seeds": (U64, [P]),
         "hspz_seed_range": (ctypes.c_int, [P, U64, U64, PU64, PU64]),
         "hspz_plan": (ctypes.c_int, [P, U64, U64, P, PU64, PU32]),
@@ -222,6 +223,15 @@ class Engine:
     def upload_query(self, seq, strand: int = 0, stream=None):
         a = _host_bytes(seq)
         self._check(_lib.hspz_upload_query(self._h, a.ctypes.data, a.size, strand,
+                                           _stream(stream)))
+
+    def upload_seeds(self, kmer, q_end, stream=None):
+        """The caller's seeds (packed k-mers, query ends) in place of the seeder's."""
+        k = np.ascontiguousarray(kmer, dtype=np.uint32)
+        q = np.ascontiguousarray(q_end, dtype=np.uint32)
+        if k.shape != q.shape or k.ndim != 1:
+            raise ValueError("kmer and q_end must be 1-D arrays of one length")
+        self._check(_lib.hspz_upload_seeds(self._h, k.ctypes.data, q.ctypes.data, k.size,
                                            _stream(stream)))
 
     def num_seeds(self) -> int:

@@ -619,6 +619,50 @@ static int impl_hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, u
     return HSPZ_OK;
 }
 
+// Caller seeds in place of the device seeder's, for the current query strand.
+static int impl_hspz_upload_seeds(hspz_engine *engine, const uint32_t *h_kmer,
+                                  const uint32_t *h_q_end, uint64_t n, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_qry)
+        return fail(e, HSPZ_E_STATE, "upload the query strand first: the walks read it");
+    if (n && (!h_kmer || !h_q_end)) return fail(e, HSPZ_E_INVALID, "seed arrays are NULL");
+    if (n >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "at most 2^32 - 2 seeds");
+    const uint64_t nkeys = 1ull << (2 * e->weight);
+    const uint64_t span = (uint64_t)e->span;
+    for (uint64_t i = 0; i < n; i++) {
+        if (h_kmer[i] >= nkeys)
+            return fail(e, HSPZ_E_INVALID, "seed %llu: k-mer %u is not below 4^%d",
+                        (unsigned long long)i, h_kmer[i], e->weight);
+        if (h_q_end[i] < span || h_q_end[i] > e->n_qry)
+            return fail(e, HSPZ_E_INVALID, "seed %llu: query end %u is outside [%llu, %llu]",
+                        (unsigned long long)i, h_q_end[i], (unsigned long long)span,
+                        (unsigned long long)e->n_qry);
+        if (i && h_q_end[i] < h_q_end[i - 1])
+            return fail(e, HSPZ_E_INVALID, "seed %llu: query ends must not decrease",
+                        (unsigned long long)i);
+    }
+    int rc = set_device(e);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    e->free_plan();
+    std::vector<uint32_t> start(n);  // window starts, for hspz_seed_range
+    for (uint64_t i = 0; i < n; i++) start[i] = h_q_end[i] - (uint32_t)span;
+    e->n_seeds = 0;  // no seeds until the new ones have landed
+    e->h_seed_start.clear();
+    if ((rc = dalloc(e, e->d_kmer, n)) || (rc = dalloc(e, e->d_qend, n))) return rc;
+    if (n) {
+        HIP_TRY(e, hipMemcpyAsync(e->d_kmer, h_kmer, n * sizeof(uint32_t),
+                                  hipMemcpyHostToDevice, s));
+        HIP_TRY(e, hipMemcpyAsync(e->d_qend, h_q_end, n * sizeof(uint32_t),
+                                  hipMemcpyHostToDevice, s));
+    }
+    HIP_TRY(e, hipStreamSynchronize(s));
+    e->h_seed_start.swap(start);
+    e->n_seeds = n;
+    return HSPZ_OK;
+}
+
 HSPZ_API uint64_t hspz_num_seeds(const hspz_engine *engine) {
     const Engine *e = reinterpret_cast<const Engine *>(engine);
     return (e && e->has_qry) ? e->n_seeds : 0;
@@ -1638,5 +1682,14 @@ HSPZ_API int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2,
         return impl_hspz_debug_gate_deferred(engine, n_stage2, n_exact, stream);
     } catch (...) {
         return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_upload_seeds(hspz_engine *engine, const uint32_t *h_kmer,
+                               const uint32_t *h_q_end, uint64_t n, void *stream) {
+    try {
+        return impl_hspz_upload_seeds(engine, h_kmer, h_q_end, n, stream);
+    } catch (...) {
+        return api_exception(reinterpret_cast<Engine *>(engine));
     }
 }
