@@ -14,7 +14,9 @@
 //    from there the two walks are one (same later bases, same running best, same drop,
 //    and every base scored before lies below that best), so it keeps only its running
 //    score at the neighbour's start.  k_mm_lanes walks every side one lane each, for up
-//    to 128 bases in eight-base blocks, and lists the walks still open; k_mm_list walks
+//    to 128 bases in eight-base blocks (the first 32 in every lane, the rest only in the
+//    lanes of the walks still open, packed together), and lists the walks still open
+//    after that; k_mm_list walks
 //    those one wave each in 512-base tiles.  A side that merged takes the best of the
 //    first walk along its chain that ran to its drop, plus the summed scores at the starts
 //    in between, and that walk's extent plus the distance to it: one scan over both
@@ -42,9 +44,12 @@ constexpr int kPer = 8;  // bases per lane: 512-base tiles (16 measured slower o
 // Window of the shared walks' lane stage, in blocks of eight bases per side: about 0.3% of
 // the walks on dense tandem repeats run past 128 bases.  Per 1.04 M-survivor chunk, lane
 // stage + listed walks measured 183 + 51, 110 + 26, 84 + 17 and 93 + 15 us at 8, 12, 16
-// and 24 blocks.
+// and 24 blocks, with every lane held to its wave's longest walk.
 constexpr int kLaneBlocks = 16;
 constexpr int kLanePrefetch = 3;  // blocks each lane reads ahead
+// Blocks of the lane stage's first phase, after which the open walks are packed: the lane
+// stage measured 84 us per chunk unpacked and 67 us at 4; 2 to 6 are within noise.
+constexpr int kLaneFirst = 4;
 // Largest grid of the one-wave-per-survivor kernels (a launch holds fewer than 2^32
 // threads); beyond it each workgroup strides over several survivors.
 constexpr uint32_t kWaveGridMax = 1u << 22;
@@ -224,14 +229,23 @@ __device__ __forceinline__ void mm_store(const MatSide &m, uint32_t s, int32_t b
 // of their use (a ring of PF + 2 dwords), so that a block's loads have the blocks before
 // it to land.  Reads at most 8 * (NB + PF) + 16 nibbles from mr on either side, inside
 // the edge padding.
-template <int D, int NB, int PF>
+// The running state of a lane walk between blocks: score, best, earliest extent of the
+// best, and the score at walk index wm once the walk has passed it.
+struct LaneWalk {
+    int32_t s = 0, best = 0, ds = 0;
+    uint32_t ext = 0;
+};
+
+// Blocks K0 .. K1 - 1 of the walk, from the state w after block K0 - 1 (w is updated to
+// the state after the last block walked); a lane that is not active takes no part.
+template <int D, int K0, int K1, int PF>
 __device__ __forceinline__ bool lane_merge_walk(const int32_t *tab4,
                                                 const uint32_t *__restrict__ ref4,
                                                 const uint32_t *__restrict__ qry4, uint32_t mr,
                                                 uint32_t mq, int32_t xdrop, uint32_t wm,
-                                                int32_t &best, uint32_t &ext, bool &merged,
-                                                int32_t &ds) {
-    static_assert(8 * (NB + PF) + 16 <= kPad4, "the window must stay inside the edge padding");
+                                                bool active, LaneWalk &w, int32_t &best,
+                                                uint32_t &ext, bool &merged, int32_t &ds) {
+    static_assert(8 * (K1 + PF) + 16 <= kPad4, "the window must stay inside the edge padding");
     const uint32_t ar = D > 0 ? mr : mr - 8u, aq = D > 0 ? mq : mq - 8u;
     const uint32_t *__restrict__ pr = ref4 + (ar >> 3);
     const uint32_t *__restrict__ pq = qry4 + (aq >> 3);
@@ -243,23 +257,23 @@ __device__ __forceinline__ bool lane_merge_walk(const int32_t *tab4,
     uint32_t rr[PF + 2], qq[PF + 2];
 #pragma unroll
     for (int i = 0; i < PF + 2; i++) {
-        rr[i] = at(pr, i);
-        qq[i] = at(pq, i);
+        rr[i] = at(pr, K0 + i);
+        qq[i] = at(pq, K0 + i);
     }
     // The lanes run in step with no branch of their own: a lane that ends in a block keeps
     // its results from there and goes on scoring (its reads stay inside the window), and
     // the wave leaves once every lane has ended.  A branch per lane would make every value
     // of the ring cross a join, and copying a register that a load still writes waits for
     // the load; unrolled, the ring is register renaming.
-    int32_t s = 0, b_run = 0, ds_run = 0;
-    uint32_t e_run = 0;
-    bool done = false;
+    int32_t s = w.s, b_run = w.best, ds_run = w.ds;
+    uint32_t e_run = w.ext;
+    bool done = !active;
     best = 0;
     ext = 0;
     merged = false;
     ds = 0;
 #pragma unroll
-    for (int k = 0; k < NB; k++) {
+    for (int k = K0; k < K1; k++) {
         const uint32_t R = D > 0 ? __builtin_amdgcn_alignbit(rr[1], rr[0], shr)
                                  : __builtin_amdgcn_alignbit(rr[0], rr[1], shr);
         const uint32_t Q = D > 0 ? __builtin_amdgcn_alignbit(qq[1], qq[0], shq)
@@ -306,60 +320,105 @@ __device__ __forceinline__ bool lane_merge_walk(const int32_t *tab4,
             break;
         }
     }
+    w.s = s;
+    w.best = b_run;
+    w.ds = ds_run;
+    w.ext = e_run;
     return done;
 }
 
-// Lane stage of the diagonal-shared walks: one lane per sorted survivor walks both sides
-// with lane_merge_walk and stores what it finished; walks still running at the window's
-// end go to a list (right walks from list[0], left walks from list[n]; counts in lcnt),
-// each wave reserving its share of both with one atomic.
+// Lane stage of the diagonal-shared walks, per side in two phases.  Every lane walks its
+// survivor's first kLaneFirst blocks; the walks still running then go, with their state,
+// through LDS to as few waves as they fill (about one in eight on dense tandem repeats),
+// which walk them on to block NB.  A wave thus runs its first phase as long as its
+// longest short walk and its second only for the long ones, instead of every lane
+// waiting for the wave's longest walk.  Walks still running at block NB go to a list
+// (right walks from list[0], left walks from list[n]; counts in lcnt) that k_mm_list
+// walks in full, each wave reserving its share with one atomic.
 template <int NB>
 __global__ __launch_bounds__(256) void k_mm_lanes(
     const uint64_t *__restrict__ sa, const uint32_t *__restrict__ key_d, uint32_t n,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, ScoreParams sp,
     MatSide right, MatSide left, uint32_t *__restrict__ list, uint32_t *__restrict__ lcnt) {
+    static_assert(kLaneFirst < NB, "the second phase needs blocks");
     __shared__ int32_t tab4[kTab4];
+    // walks carried into the second phase: state, walk geometry and survivor index
+    __shared__ int32_t c_s[256], c_best[256], c_ds[256];
+    __shared__ uint32_t c_ext[256], c_wm[256], c_mr[256], c_mq[256], c_idx[256];
+    __shared__ uint32_t c_n[2];  // per side, so that no wave still reads the one cleared
+    if (threadIdx.x < 2) c_n[threadIdx.x] = 0;
     for (int i = threadIdx.x; i < kTab4; i += 256) {
         const int r = i >> 4, q = i & 15;
         tab4[i] = (r <= kCodeEdge && q <= kCodeEdge) ? sp.tab[(r << kRefShift) | q] : 0;
     }
-    __syncthreads();
     const uint32_t s = blockIdx.x * 256 + threadIdx.x;
     const bool live = s < n;
     MmAnchor A{};
     if (live) A = mm_anchor(sa, key_d, n, s, sp);
-    bool open[2] = {false, false};
+    const int w = threadIdx.x >> 6, lane = lane_id();
 #pragma unroll
     for (int side = 0; side < 2; side++) {
-        if (live) {
-            int32_t best, ds;
-            uint32_t ext;
-            bool merged, done;
-            if (side == 0)
-                done = lane_merge_walk<+1, NB, kLanePrefetch>(
-                    tab4, ref4, qry4, kPad4 + (A.bad ? sp.n_ref : A.r),
-                    kPad4 + (A.bad ? sp.n_qry : A.q), sp.xdrop, A.wr, best, ext, merged, ds);
-            else
-                done = lane_merge_walk<-1, NB, kLanePrefetch>(
-                    tab4, ref4, qry4, kPad4 + (A.bad ? 0u : A.r), kPad4 + (A.bad ? 0u : A.q),
-                    sp.xdrop, A.wl, best, ext, merged, ds);
-            if (done) mm_store(side == 0 ? right : left, s, best, ext, merged, ds);
-            open[side] = !done;
+        const MatSide &m = side == 0 ? right : left;
+        __syncthreads();  // orders the table and counters above, and the last side's reads
+        const uint32_t mr = kPad4 + (A.bad ? (side == 0 ? sp.n_ref : 0u) : A.r);
+        const uint32_t mq = kPad4 + (A.bad ? (side == 0 ? sp.n_qry : 0u) : A.q);
+        const uint32_t wm = side == 0 ? A.wr : A.wl;
+        LaneWalk st;
+        int32_t best, ds;
+        uint32_t ext;
+        bool merged, done;
+        if (side == 0)
+            done = lane_merge_walk<+1, 0, kLaneFirst, kLanePrefetch>(
+                tab4, ref4, qry4, mr, mq, sp.xdrop, wm, live, st, best, ext, merged, ds);
+        else
+            done = lane_merge_walk<-1, 0, kLaneFirst, kLanePrefetch>(
+                tab4, ref4, qry4, mr, mq, sp.xdrop, wm, live, st, best, ext, merged, ds);
+        if (live && done) mm_store(m, s, best, ext, merged, ds);
+        if (live && !done) {
+            const uint32_t c = atomicAdd(&c_n[side], 1u);
+            c_s[c] = st.s;
+            c_best[c] = st.best;
+            c_ds[c] = st.ds;
+            c_ext[c] = st.ext;
+            c_wm[c] = wm;
+            c_mr[c] = mr;
+            c_mq[c] = mq;
+            c_idx[c] = s;
         }
-    }
-    // one atomic per wave reserves both sides' list entries: lcnt as one little-endian
-    // u64, the right count in its low word (a count stays below 2^32, so no carry)
-    const uint64_t mr = __ballot(open[0]), ml = __ballot(open[1]);
-    if (mr | ml) {
-        unsigned long long at = 0;
-        if (lane_id() == 0)
-            at = atomicAdd(reinterpret_cast<unsigned long long *>(lcnt),
-                           ((unsigned long long)__popcll(ml) << 32) |
-                               (unsigned long long)__popcll(mr));
-        const uint32_t at_r = __shfl((uint32_t)at, 0, 64);
-        const uint32_t at_l = __shfl((uint32_t)(at >> 32), 0, 64);
-        if (open[0]) list[at_r + lane_rank(mr)] = s;
-        if (open[1]) list[(uint64_t)n + at_l + lane_rank(ml)] = s;
+        __syncthreads();
+        const uint32_t cn = c_n[side];  // uniform
+        if ((uint32_t)w * 64u < cn) {
+            const uint32_t c = (uint32_t)w * 64u + (uint32_t)lane;
+            const bool has = c < cn;
+            LaneWalk ct;
+            uint32_t cwm = UINT32_MAX, cmr = kPad4, cmq = kPad4, cidx = 0;
+            if (has) {
+                ct.s = c_s[c];
+                ct.best = c_best[c];
+                ct.ds = c_ds[c];
+                ct.ext = c_ext[c];
+                cwm = c_wm[c];
+                cmr = c_mr[c];
+                cmq = c_mq[c];
+                cidx = c_idx[c];
+            }
+            bool cdone;
+            if (side == 0)
+                cdone = lane_merge_walk<+1, kLaneFirst, NB, kLanePrefetch>(
+                    tab4, ref4, qry4, cmr, cmq, sp.xdrop, cwm, has, ct, best, ext, merged, ds);
+            else
+                cdone = lane_merge_walk<-1, kLaneFirst, NB, kLanePrefetch>(
+                    tab4, ref4, qry4, cmr, cmq, sp.xdrop, cwm, has, ct, best, ext, merged, ds);
+            if (has && cdone) mm_store(m, cidx, best, ext, merged, ds);
+            const bool open = has && !cdone;
+            const uint64_t om = __ballot(open);
+            if (om) {
+                uint32_t at = 0;
+                if (lane == 0) at = atomicAdd(&lcnt[side], (uint32_t)__popcll(om));
+                at = __shfl(at, 0, 64);
+                if (open) list[(uint64_t)side * n + at + lane_rank(om)] = cidx;
+            }
+        }
     }
 }
 
