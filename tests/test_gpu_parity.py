@@ -780,9 +780,11 @@ def test_materialize_every_anchor_near_the_ends(seed, mat):
 @pytest.mark.parametrize("identity", [1.0, 0.93], ids=["identical", "mutated"])
 def test_shared_walks_at_the_lane_window_edges(identity):
     # survivors on the main diagonal of a sequence and a copy of it, spaced so that a walk
-    # merges into its neighbour on the last bases of the lane stage's window, on the first
-    # bases past it (the walk goes to the one-wave list), and around the 64- and 512-base
-    # tile edges; on identical sequences every walk merges exactly at its neighbour's start
+    # merges into its neighbour on the last bases of the lane stage's first phase (32
+    # bases) or on the first bases after it (the walk moves to a packed wave), on the last
+    # bases of the lane stage's window, on the first bases past it (the walk goes to the
+    # one-wave list), and around the 64- and 512-base tile edges; on identical sequences
+    # every walk merges exactly at its neighbour's start
     import torch
     rng = np.random.default_rng(91)
     acgt = np.frombuffer(b"ACGT", np.uint8)
@@ -793,7 +795,8 @@ def test_shared_walks_at_the_lane_window_edges(identity):
         code[acgt] = np.arange(4)
         flip = rng.random(qry.size) > identity
         qry[flip] = acgt[(code[qry[flip]] + rng.integers(1, 4, int(flip.sum()))) % 4]
-    gaps = [1, 2, 7, 8, 9, 63, 64, 65, 127, 128, 129, 130, 136, 255, 256, 257, 511, 512, 513]
+    gaps = [1, 2, 7, 8, 9, 24, 25, 31, 32, 33, 40, 41, 63, 64, 65, 127, 128, 129, 130, 136,
+            255, 256, 257, 511, 512, 513]
     pos = 200 + np.cumsum(np.tile(gaps, 8))
     pos = pos[pos < ref.size - 200]
     # the main diagonal, plus every third position again on an unrelated diagonal
