@@ -65,8 +65,8 @@ def _load():
         "orc_gate_totals": (None, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _P, _P]),
         "orc_compact": (_I64, [_P, _I64, _P]),
         "orc_entropy_bits": (ctypes.c_double, [_P, _I64, _I64, _I64]),
-        "orc_materialize": (None, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32,
-                                   _I32, _I32, _P, _P]),
+        "orc_materialize": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _I32,
+                                           _I32, _I32, _I32, _I32, _P, _P]),
         "orc_compact_hsps": (_I64, [_P, _P, _I64, _P]),
     }
     for name, (res, args) in sig.items():
@@ -252,9 +252,12 @@ def materialize(anchors_, ids, rcodes, qcodes, sub, n_score, X, T, K=None, entro
     qc = _c(qcodes, np.uint8)
     hsp = np.zeros(max(ids.size, 1), HSP_DTYPE)
     status = np.zeros(max(ids.size, 1), np.uint8)
-    _load().orc_materialize(_ptr(a), _ptr(ids), ids.size, _ptr(rc), rc.size, _ptr(qc),
-                            qc.size, _ptr(_sub(sub)), n_score, X, T, T if K is None else K,
-                            entropy_mode, _ptr(hsp), _ptr(status))
+    rc_ = _load().orc_materialize(_ptr(a), _ptr(ids), ids.size, _ptr(rc), rc.size,
+                                  _ptr(qc), qc.size, _ptr(_sub(sub)), n_score, X, T,
+                                  T if K is None else K, entropy_mode, _ptr(hsp),
+                                  _ptr(status))
+    if rc_ != 0:
+        raise OverflowError("a record's score L* + R* does not fit in int32: refused")
     return hsp[: ids.size], status[: ids.size]
 
 

@@ -390,12 +390,16 @@ double orc_entropy_bits(const uint8_t *rc, int64_t nr, int64_t rs, int64_t len) 
  * also requires score * H >= 2 K with H the interval's entropy in bits (orc_entropy_bits;
  * an interval without A/C/G/T is rejected), i.e. the score scaled by H / 2 -- the
  * fraction of the 2-bit maximum -- must still reach K.  Status 1 = accepted, 0 =
- * rejected.  The record is written either way; only accepted slots are output. */
-void orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_surv,
-                     const uint8_t *rc, int64_t nr, const uint8_t *qc, int64_t nq,
-                     const int32_t *sub, int32_t n_score, int32_t xdrop, int32_t T,
-                     int32_t K, int32_t entropy_mode, orc_segment_pair *hsp,
-                     uint8_t *status) {
+ * rejected.  The record is written either way; only accepted slots are output.
+ * reading (score width; the pages name no width): a record's score is a 32-bit signed
+ * integer.  The walks sum in 64 bits here, and a call in which any record's L* + R* does
+ * not fit in int32 is refused: it returns -1 (the arrays are then unspecified) instead
+ * of storing a wrapped score.  Returns 0 otherwise. */
+int orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_surv,
+                    const uint8_t *rc, int64_t nr, const uint8_t *qc, int64_t nq,
+                    const int32_t *sub, int32_t n_score, int32_t xdrop, int32_t T,
+                    int32_t K, int32_t entropy_mode, orc_segment_pair *hsp,
+                    uint8_t *status) {
     for (int64_t i = 0; i < n_surv; i++) {
         uint64_t a = anchors[ids[i]];
         int64_t r = (int64_t)(a & 0xFFFFFFFFull);
@@ -403,6 +407,7 @@ void orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_sur
         int64_t R, k, L, m;
         orc_xdrop(rc, nr, qc, nq, r, q, +1, sub, n_score, xdrop, &R, &k);
         orc_xdrop(rc, nr, qc, nq, r, q, -1, sub, n_score, xdrop, &L, &m);
+        if (L + R > (int64_t)INT32_MAX || L + R < (int64_t)INT32_MIN) return -1;
         hsp[i].ref_start = (uint32_t)(r - m);
         hsp[i].query_start = (uint32_t)(q - m);
         hsp[i].len = (uint32_t)(m + k - 1);
@@ -414,6 +419,7 @@ void orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_sur
         }
         status[i] = ok ? 1 : 0;
     }
+    return 0;
 }
 
 /* "E. X-drop materialization", E.5: the accepted records in survivor order. */

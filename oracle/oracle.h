@@ -68,11 +68,11 @@ void orc_gate_totals(const uint64_t *anchors, int64_t n, const uint8_t *rc, int6
                      int32_t xdrop, int64_t *totals, int64_t *steps);
 int64_t orc_compact(const uint8_t *flags, int64_t n, uint32_t *ids);
 double orc_entropy_bits(const uint8_t *rc, int64_t nr, int64_t rs, int64_t len);
-void orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_surv,
-                     const uint8_t *rc, int64_t nr, const uint8_t *qc, int64_t nq,
-                     const int32_t *sub, int32_t n_score, int32_t xdrop, int32_t T,
-                     int32_t K, int32_t entropy_mode, orc_segment_pair *hsp,
-                     uint8_t *status);
+int orc_materialize(const uint64_t *anchors, const uint32_t *ids, int64_t n_surv,
+                    const uint8_t *rc, int64_t nr, const uint8_t *qc, int64_t nq,
+                    const int32_t *sub, int32_t n_score, int32_t xdrop, int32_t T,
+                    int32_t K, int32_t entropy_mode, orc_segment_pair *hsp,
+                    uint8_t *status);
 int64_t orc_compact_hsps(const orc_segment_pair *hsp, const uint8_t *status, int64_t n,
                          orc_segment_pair *out);
 

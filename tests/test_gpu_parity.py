@@ -165,6 +165,32 @@ def test_gate_on_arbitrary_anchors(gate_mode, seed):
         assert 0 < n2 < a.size and 0 < nx <= n2
 
 
+@pytest.mark.parametrize("gate_mode,mat", [(0, 0), (1, 1), (2, 0), (3, 0), (4, 2)])
+def test_keep_threshold_equal_to_exact_totals(gate_mode, mat):
+    # "D. Score gate", D.3: kept when the total is at least the threshold.  K is set to
+    # totals that anchors of the pass reach exactly (ties at the boundary), to one above
+    # and to one below; flags, ids, status and records must match the oracle's, which
+    # is pinned at the same boundary by hand-worked totals.
+    ref, qry = random_pair(31, 20_000, 20_000, n_frac=0.02, plant=25, plant_len=(40, 400),
+                           identity=0.85, gc=0.41)
+    p0 = params_of("1101011")
+    o, R, qc = oracle_pass(ref, qry, p0)
+    a = np.concatenate([c["anchors"] for c in o["chunks"]])
+    tot, _ = oracle.gate_totals(a, R.codes, qc, p0["sub"], p0["n_score"], p0["xdrop"])
+    vals, cnt = np.unique(tot[tot >= 200], return_counts=True)
+    picks = [int(vals[np.argmax(cnt)]), int(vals[-1]), int(vals[vals.size // 2])]
+    for K0 in picks:
+        assert (tot == K0).any()
+        for K in (K0, K0 + 1, K0 - 1):
+            p = params_of("1101011", K=K)
+            ok, _, _ = oracle_pass(ref, qry, p)
+            kept = sum(int(c["flags"].sum()) for c in ok["chunks"])
+            assert kept == int((tot >= K).sum())
+            eng = engine(p, gate_mode=gate_mode, materialize_mode=mat,
+                         ref_buckets=5 if gate_mode == 4 else 0)
+            assert_pass_equal(gpu_full_pass(eng, ref, qry), ok)
+
+
 @pytest.mark.parametrize("gate_mode", [2, 3, 4])
 def test_window_gate_defers_long_walks(gate_mode):
     # a sequence against itself: every anchor on the main diagonal walks to both ends

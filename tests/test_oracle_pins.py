@@ -482,3 +482,53 @@ def test_dedup_of_a_pass_removes_repeated_records_only():
     assert len(set(d.tolist())) == d.size and set(d.tolist()) == set(acc.tolist())
     first = [acc.tolist().index(r) for r in d.tolist()]
     assert first == sorted(first)
+
+
+# ------------------------------------------------------------------ keep boundary
+
+def test_keep_boundary_hand_worked():
+    # "D. Score gate", D.3: kept when the total is at least the threshold.  The totals
+    # are worked by hand in the golden file; a threshold equal to the total keeps the
+    # anchor and one above drops it, in the gate and in the materializer's decision.
+    g = _gold("keep_boundary_hand_worked.json")
+    for case in g["cases"]:
+        rc, qc = oracle.encode(case["ref"].encode()), oracle.encode(case["query"].encode())
+        r, q = case["r"], case["q"]
+        assert oracle.xdrop(rc, qc, r, q, +1, SUB, NS, g["xdrop"]) == \
+            (case["right_best"], case["right_extent"])
+        assert oracle.xdrop(rc, qc, r, q, -1, SUB, NS, g["xdrop"]) == \
+            (case["left_best"], case["left_extent"])
+        a = np.asarray([r | (q << 32)], np.uint64)
+        ids = np.zeros(1, np.uint32)
+        tot = case["total"]
+        for K, keep in ((tot, 1), (tot + 1, 0), (tot - 1, 1)):
+            T = oracle.keep_threshold(K)
+            assert T == K  # |K| <= 2^24: the single-precision threshold is K itself
+            assert oracle.gate(a, rc, qc, SUB, NS, g["xdrop"], T).tolist() == [keep]
+            hsp, st = oracle.materialize(a, ids, rc, qc, SUB, NS, g["xdrop"], T, K=K)
+            assert st.tolist() == [keep]
+            assert [int(hsp[0][f]) for f in ("ref_start", "query_start", "len", "score")] \
+                == case["record"]
+
+
+# ------------------------------------------------------------------ score width
+
+def test_score_width_refusal_at_the_int32_limit():
+    # identical all-C sequences: every pair scores HOXD70 C/C = 100, so neither walk ever
+    # drops and the total of an anchor is 100 times the sequence length.  21,474,836
+    # bases give 2,147,483,600 <= 2^31 - 1 and the record is stored; one base more gives
+    # 2,147,483,700, which does not fit in int32, and the oracle refuses the call.
+    for n, fits in ((21_474_836, True), (21_474_837, False)):
+        c = oracle.encode(b"C" * n)
+        a = np.asarray([(n // 2) | ((n // 2) << 32)], np.uint64)
+        ids = np.zeros(1, np.uint32)
+        tot, _ = oracle.gate_totals(a, c, c, SUB, NS, X)
+        assert tot.tolist() == [100 * n]
+        if fits:
+            hsp, st = oracle.materialize(a, ids, c, c, SUB, NS, X, 3000)
+            assert int(hsp[0]["score"]) == 100 * n == 2_147_483_600
+            assert (int(hsp[0]["ref_start"]), int(hsp[0]["len"])) == (0, n - 1)
+            assert st.tolist() == [1]
+        else:
+            with pytest.raises(OverflowError):
+                oracle.materialize(a, ids, c, c, SUB, NS, X, 3000)
