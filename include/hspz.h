@@ -235,6 +235,19 @@ int hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors, uin
 int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
                     uint8_t *d_flags, void *stream);
 
+/* hspz_score_gate for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments and the
+ * same d_flags bytes as hspz_score_gate, but the window gate's deferred-anchor lists and
+ * counters live in a static device array of the library (64 MiB + 64 B on every GPU the
+ * library runs on, held until the process ends), so the call allocates nothing and
+ * synchronises nothing.  n is at most 2^23 (8,388,608); split longer anchor arrays into
+ * several calls.  Every call on one GPU shares that array, from every engine: calls that
+ * overlap on one GPU (other streams, other host threads) race, so serialise them.
+ * Errors: as hspz_score_gate; HSPZ_E_CAPACITY when n exceeds 2^23, HSPZ_E_INVALID with
+ * the bucketed gate (gate_mode 4), whose sort needs scratch proportional to n. */
+int hspz_score_gate_noalloc(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
+                            uint8_t *d_flags, void *stream);
+
 /* hspz_find_hits and hspz_score_gate for chunk i in one call ("C. Hit discovery", C.5;
  * "D. Score gate", D.1-D.3): the gate's first window stage builds each anchor from the
  * chunk's seeds as it scores it, so the anchors are not written out and read back.

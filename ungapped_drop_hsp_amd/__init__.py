@@ -33,6 +33,7 @@ ABI_SYMBOLS = (
     "hspz_get_index", "hspz_debug_plan_counts", "hspz_debug_walk_steps",
     "hspz_debug_gate_deferred", "hspz_run_batch", "hspz_get_batch_records",
     "hspz_find_hits_gate", "hspz_dedup_records", "hspz_upload_seeds",
+    "hspz_score_gate_noalloc",
 )
 
 
@@ -84,6 +85,7 @@ def _load() -> ctypes.CDLL:
         "hspz_get_chunk": (ctypes.c_int, [P, U32, ctypes.POINTER(Chunk)]),
         "hspz_find_hits": (ctypes.c_int, [P, U32, P, U64, P]),
         "hspz_score_gate": (ctypes.c_int, [P, P, U64, P, P]),
+        "hspz_score_gate_noalloc": (ctypes.c_int, [P, P, U64, P, P]),
         "hspz_compact": (ctypes.c_int, [P, P, U64, P, U64, PU64, P]),
         "hspz_materialize": (ctypes.c_int, [P, P, P, U64, P, P, P]),
         "hspz_compact_hsps": (ctypes.c_int, [P, P, P, U64, P, U64, PU64, P]),
@@ -270,6 +272,10 @@ class Engine:
     def score_gate(self, anchors, n: int, flags, stream=None):
         self._check(_lib.hspz_score_gate(self._h, _ptr(anchors), n, _ptr(flags),
                                          _stream(stream)))
+
+    def score_gate_noalloc(self, anchors, n: int, flags, stream=None):
+        self._check(_lib.hspz_score_gate_noalloc(self._h, _ptr(anchors), n, _ptr(flags),
+                                                 _stream(stream)))
 
     def compact(self, flags, n: int, ids, cap: Optional[int] = None, stream=None) -> int:
         if cap is None:

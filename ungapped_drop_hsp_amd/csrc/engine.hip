@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <unordered_set>
 
@@ -383,6 +384,32 @@ void Engine::free_plan() {
 
 using namespace hspz;
 
+// Scratch of hspz_score_gate_noalloc, which allocates nothing: the two deferred-anchor
+// lists of the window gate (each able to hold every anchor of a call) and its two
+// counters, in one statically sized array that every GPU the library runs on holds until
+// the process ends.  Layout in u32 words: [0, 16) counters, then list 1, then list 2.
+constexpr uint64_t kNoAllocMaxAnchors = 1ull << 23;
+constexpr uint64_t kNoAllocWords = 16 + 2 * kNoAllocMaxAnchors;  // 64 MiB + 64 B
+static __device__ __align__(256) uint32_t scratch[kNoAllocWords];
+
+// scratch's device address on each device, resolved once per device with that device
+// current (the host-side name of the array is not a device address).
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint32_t *g_scratch_ptr[kMaxDevices] = {};
+
+static int resolve_scratch(Engine *e) {
+    if (e->device >= kMaxDevices)
+        return fail(e, HSPZ_E_INVALID, "device %d beyond the scratch table", e->device);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[e->device]) return HSPZ_OK;
+    void *ptr = nullptr;
+    HIP_TRY(e, hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(e, HSPZ_E_HIP, "hipGetSymbolAddress returned NULL for scratch");
+    g_scratch_ptr[e->device] = static_cast<uint32_t *>(ptr);
+    return HSPZ_OK;
+}
+
 static int impl_hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     if (!out) return fail(nullptr, HSPZ_E_INVALID, "out is NULL");
     *out = nullptr;
@@ -493,6 +520,11 @@ static int impl_hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         g_create_error = "pinned/device staging allocation failed";
         delete e;
         return HSPZ_E_NOMEM;
+    }
+    if ((rc = resolve_scratch(e))) {
+        g_create_error = e->err;
+        delete e;
+        return rc;
     }
     *out = reinterpret_cast<hspz_engine *>(e);
     return HSPZ_OK;
@@ -934,6 +966,41 @@ static int impl_hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, 
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
+    return HSPZ_OK;
+}
+
+// hspz_score_gate with the deferred lists and counters in the static scratch array: no
+// allocation of any kind.  The bucketed gate needs scratch proportional to n and is
+// refused.
+static int impl_hspz_score_gate_noalloc(hspz_engine *engine, const uint64_t *d_anchors,
+                                        uint64_t n, uint8_t *d_flags, void *stream) {
+    Engine *e = reinterpret_cast<Engine *>(engine);
+    if (!e) return HSPZ_E_INVALID;
+    if (!e->has_ref || !e->has_qry)
+        return fail(e, HSPZ_E_STATE, "score_gate_noalloc needs an uploaded reference and query");
+    if (n > kNoAllocMaxAnchors)
+        return fail(e, HSPZ_E_CAPACITY, "score_gate_noalloc takes at most %llu anchors, got %llu",
+                    (unsigned long long)kNoAllocMaxAnchors, (unsigned long long)n);
+    if (n && (!d_anchors || !d_flags)) return fail(e, HSPZ_E_INVALID, "NULL buffer");
+    if (e->params.gate_mode == 4)
+        return fail(e, HSPZ_E_INVALID, "the bucketed gate (gate_mode 4) allocates; use "
+                                       "hspz_score_gate");
+    int rc = set_device(e);
+    if (rc) return rc;
+    uint32_t *ptr = e->device < kMaxDevices ? g_scratch_ptr[e->device] : nullptr;
+    if (!ptr) return fail(e, HSPZ_E_STATE, "scratch not resolved on device %d", e->device);
+    hipStream_t s = as_stream(stream);
+    e->gate_deferred_valid = false;
+    if (!(e->window_ok && e->params.gate_mode != 1)) {
+        HIP_TRY(e, launch_gate(e->block_bases, d_anchors, (uint32_t)n, d_flags, e->d_ref + kPad,
+                               e->d_qry + kPad, e->sp, s));
+        return HSPZ_OK;
+    }
+    uint32_t *cnt = ptr, *list1 = ptr + 16, *list2 = ptr + 16 + kNoAllocMaxAnchors;
+    HIP_TRY(e, launch_gate_window(e->params.gate_mode == 3, d_anchors, (uint32_t)n, d_flags,
+                                  e->d_ref4, e->d_qry4, e->wp, list1, list2, cnt, s));
+    HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, cnt + 1, (uint32_t)n, d_flags,
+                                     e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     return HSPZ_OK;
 }
 
@@ -1594,6 +1661,15 @@ HSPZ_API int hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, uin
                              uint8_t *d_flags, void *stream) {
     try {
         return impl_hspz_score_gate(engine, d_anchors, n, d_flags, stream);
+    } catch (...) {
+        return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
+    }
+}
+
+HSPZ_API int hspz_score_gate_noalloc(hspz_engine *engine, const uint64_t *d_anchors,
+                                     uint64_t n, uint8_t *d_flags, void *stream) {
+    try {
+        return impl_hspz_score_gate_noalloc(engine, d_anchors, n, d_flags, stream);
     } catch (...) {
         return api_exception(const_cast<Engine *>(reinterpret_cast<const Engine *>(engine)));
     }
