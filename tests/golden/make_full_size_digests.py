@@ -50,7 +50,7 @@ G = {}
 
 
 def sha(a: np.ndarray) -> str:
-    return hashlib.sha256(memoryview(np.ascontiguousarray(a)).cast("B")).hexdigest()
+    return hashlib.sha256(np.ascontiguousarray(a).reshape(-1).view(np.uint8)).hexdigest()
 
 
 def _shared(n: int, dtype) -> np.ndarray:
