@@ -382,6 +382,22 @@ int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64
 int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2, uint64_t *n_exact,
                              void *stream);
 
+/* Test-only: the random-line probe, a ceiling for kernels whose traffic is one random
+ * 128-byte line per unit of work -- the score gate's reference windows ("D. Score gate",
+ * D.2: each anchor reads a window of the reference at an unpredictable address; D.5
+ * names the locality of those windows as the lever on their cost).  Each of the
+ * blocks * 256 lanes reads, iters times, in_flight windows of window_dwords (1 or 16)
+ * dwords, each at the start of a random 128-byte line of d_region (region_bytes long,
+ * 128-byte aligned, device memory), issuing all of them before it uses any.  Lines read
+ * = blocks * 256 * iters * in_flight; the caller times the launch on stream with its own
+ * events.  in_flight is 1, 2, 4 or 8.  d_sink (64 u32, device) is written only if the
+ * folded words equal key.  Asynchronous; no engine.  Errors: HSPZ_E_INVALID (bad sizes,
+ * alignment or counts), HSPZ_E_HIP (launch failure). */
+int hspz_debug_line_probe(const uint32_t *d_region, uint64_t region_bytes,
+                          uint32_t window_dwords, uint32_t in_flight, uint32_t blocks,
+                          uint32_t iters, uint32_t seed, uint32_t key, uint32_t *d_sink,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -932,3 +932,22 @@ def test_shared_walks_on_tandem_repeats_and_duplicates():
         assert np.array_equal(gs, ost), f"mode {mat}: status differs"
         ok = ost == 1
         assert np.array_equal(gh[ok], oh[ok]), f"mode {mat}: records differ"
+
+
+@pytest.mark.parametrize("pat", ["1", "11", "111111", "1101011"])
+def test_plan_counts_from_the_packed_table(pat):
+    # The plan reads hit counts and bucket starts from records of 28 keys (a start and a
+    # count byte per key); a record holding a count over 254 is read from the full table
+    # instead.  Tandem copies of ACGT give a few keys hundreds of hits (marked records)
+    # beside ordinary ones; every key of a record is queried, at every offset in it.
+    rng = np.random.default_rng(5)
+    bases = np.frombuffer(b"ACGT", np.uint8)
+    ref = np.concatenate([bases[rng.integers(0, 4, 120_000)],
+                          np.frombuffer(b"ACGT" * 400, np.uint8),
+                          bases[rng.integers(0, 4, 30_000)]])
+    qry = np.concatenate([bases[rng.integers(0, 4, 40_000)], ref[119_000:123_000]])
+    p = params_of(pat)
+    o, _, _ = oracle_pass(ref, qry, p)
+    assert int(o["count"].max()) > 254
+    eng = engine(p)
+    assert_pass_equal(gpu_full_pass(eng, ref, qry), o)

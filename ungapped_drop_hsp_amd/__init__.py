@@ -33,7 +33,7 @@ ABI_SYMBOLS = (
     "hspz_get_index", "hspz_debug_plan_counts", "hspz_debug_walk_steps",
     "hspz_debug_gate_deferred", "hspz_run_batch", "hspz_get_batch_records",
     "hspz_find_hits_gate", "hspz_dedup_records", "hspz_upload_seeds",
-    "hspz_score_gate_noalloc",
+    "hspz_score_gate_noalloc", "hspz_debug_line_probe",
 )
 
 
@@ -86,6 +86,9 @@ def _load() -> ctypes.CDLL:
         "hspz_find_hits": (ctypes.c_int, [P, U32, P, U64, P]),
         "hspz_score_gate": (ctypes.c_int, [P, P, U64, P, P]),
         "hspz_score_gate_noalloc": (ctypes.c_int, [P, P, U64, P, P]),
+        "hspz_debug_line_probe": (ctypes.c_int, [P, U64, ctypes.c_uint32, ctypes.c_uint32,
+                                                 ctypes.c_uint32, ctypes.c_uint32,
+                                                 ctypes.c_uint32, ctypes.c_uint32, P, P]),
         "hspz_compact": (ctypes.c_int, [P, P, U64, P, U64, PU64, P]),
         "hspz_materialize": (ctypes.c_int, [P, P, P, U64, P, P, P]),
         "hspz_compact_hsps": (ctypes.c_int, [P, P, P, U64, P, U64, PU64, P]),
@@ -165,6 +168,15 @@ def dedup_records(records: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise HspzError(rc, _lib.hspz_last_error(None).decode())
     return out[:n.value].copy()
+
+
+def debug_line_probe(region, region_bytes: int, window_dwords: int, in_flight: int,
+                     blocks: int, iters: int, seed: int, key: int, sink, stream=None):
+    """Launch the random-line probe (test-only; the caller times it on ``stream``)."""
+    rc = _lib.hspz_debug_line_probe(_ptr(region), region_bytes, window_dwords, in_flight,
+                                    blocks, iters, seed, key, _ptr(sink), _stream(stream))
+    if rc != 0:
+        raise HspzError(rc, "line probe rejected its arguments or failed to launch")
 
 
 class Engine:

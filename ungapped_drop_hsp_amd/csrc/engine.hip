@@ -100,7 +100,8 @@ int device_scan(Engine *e, uint32_t *counts, uint64_t n, uint32_t *prefix, hipSt
     DevBuf<uint32_t> bo;
     int rc;
     if ((rc = dalloc(e, bs.p, nblk)) || (rc = dalloc(e, bo.p, nblk))) return rc;
-    HIP_TRY(e, launch_count_scan(nullptr, counts, n, nullptr, counts, nullptr, prefix, bs.p, s));
+    HIP_TRY(e, launch_count_scan(nullptr, counts, n, nullptr, nullptr, counts, nullptr, prefix,
+                                 bs.p, s));
     HIP_TRY(e, launch_scan_blocks(bs.p, nblk, bo.p, &e->d_plan->info, s));
     HIP_TRY(e, launch_add_offsets(prefix, n, bo.p, s));
     HIP_TRY(e, hipStreamSynchronize(s));
@@ -309,6 +310,7 @@ int set_device(Engine *e) {
 Engine::~Engine() {
     (void)hipSetDevice(device);
     dfree(d_end);
+    dfree(d_ctab);
     dfree(d_pos);
     dfree(d_ref);
     dfree(d_qry);
@@ -583,6 +585,9 @@ static int impl_hspz_upload_reference(hspz_engine *engine, const uint8_t *h_asci
         HIP_TRY(e, launch_set_u32(e->d_end, 0u, s));
         HIP_TRY(e, hipMemcpyAsync(e->d_end + 1, ends.p, nb * sizeof(uint32_t),
                                   hipMemcpyDeviceToDevice, s));
+        // the packed form the plan's lookups read (two uint4 per record)
+        if ((rc = dalloc(e, e->d_ctab, 2ull * count_table_records(nb)))) return rc;
+        HIP_TRY(e, launch_count_table(e->d_end, nb, e->d_ctab, s));
         HIP_TRY(e, hipStreamSynchronize(s));
     }
     const uint32_t nblk = radix_blocks(nwin);
@@ -738,8 +743,8 @@ static int impl_hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_h
     if ((rc = ensure_batch(e, n))) return rc;
     e->batch_lo = seed_lo;
     e->batch_n = n;
-    HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_count,
-                                 e->d_first, e->d_prefix, e->d_blksum, s));
+    HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_ctab,
+                                 e->d_count, e->d_first, e->d_prefix, e->d_blksum, s));
     rc = finish_plan(e, n, s, total_hits, n_chunks);
     if (rc) {
         *total_hits = 0;
@@ -769,8 +774,8 @@ static int impl_hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_co
         // counts are staged through the prefix buffer, then scanned into place
         HIP_TRY(e, hipMemcpyAsync(e->d_count, h_counts, n * sizeof(uint32_t),
                                   hipMemcpyHostToDevice, s));
-        HIP_TRY(e, launch_count_scan(nullptr, e->d_count, n, nullptr, e->d_count, nullptr,
-                                     e->d_prefix, e->d_blksum, s));
+        HIP_TRY(e, launch_count_scan(nullptr, e->d_count, n, nullptr, nullptr, e->d_count,
+                                     nullptr, e->d_prefix, e->d_blksum, s));
     }
     rc = finish_plan(e, n, s, total_hits, n_chunks);
     if (rc) {
@@ -947,8 +952,8 @@ static int impl_hspz_score_gate(hspz_engine *engine, const uint64_t *d_anchors, 
         const uint64_t nh = (uint64_t)nb * bucket_blocks(n32);
         HIP_TRY(e, launch_bucket_hist(d_anchors, n32, e->slice_shift, nb, e->d_bhist, s));
         if (nh) {
-            HIP_TRY(e, launch_count_scan(nullptr, e->d_bhist, nh, nullptr, e->d_bhist, nullptr,
-                                         e->d_bincl, e->d_bsum, s));
+            HIP_TRY(e, launch_count_scan(nullptr, e->d_bhist, nh, nullptr, nullptr, e->d_bhist,
+                                         nullptr, e->d_bincl, e->d_bsum, s));
             HIP_TRY(e, launch_scan_blocks(e->d_bsum, (nh + kScanBlock - 1) / kScanBlock,
                                           e->d_boff, e->d_binfo, s));
             HIP_TRY(e, launch_add_offsets(e->d_bincl, nh, e->d_boff, s));
@@ -1141,7 +1146,7 @@ static MatSide mat_side(Engine *e, int side) {
 static int mat_scan(Engine *e, uint32_t *in, uint64_t n, uint32_t *out, hipStream_t s) {
     if (n == 0) return HSPZ_OK;
     MatScratch &m = *e->mat;
-    HIP_TRY(e, launch_count_scan(nullptr, in, n, nullptr, in, nullptr, out, m.sum, s));
+    HIP_TRY(e, launch_count_scan(nullptr, in, n, nullptr, nullptr, in, nullptr, out, m.sum, s));
     HIP_TRY(e, launch_scan_blocks(m.sum, (n + kScanBlock - 1) / kScanBlock, m.off, m.info, s));
     HIP_TRY(e, launch_add_offsets(out, n, m.off, s));
     return HSPZ_OK;

@@ -92,11 +92,20 @@ hipError_t launch_radix_scatter(const uint32_t *key_in, const uint32_t *val_in, 
                                 int shift, const uint32_t *incl, const uint32_t *hist,
                                 uint32_t *key_out, uint32_t *val_out, hipStream_t s);
 
+// Packed count table: 32-byte records (two uint4) of kCountTableKeys consecutive keys, the
+// first key's bucket start then one count byte per key; records with a count over 254 are
+// marked and their keys read from the full table.  count_table_records(nb) records cover
+// keys 0 .. nb - 1; launch_count_table builds them from the cumulative ends end_tbl[0..nb].
+constexpr uint32_t kCountTableKeys = 28;
+uint32_t count_table_records(uint64_t nb);
+hipError_t launch_count_table(const uint32_t *end_tbl, uint64_t nb, uint4 *ctab, hipStream_t s);
 // Per seed: hit count, bucket start (first, when kmer is given) and block-local
-// inclusive prefix; one 64-bit sum per kScanBlock seeds into blksum.
+// inclusive prefix; one 64-bit sum per kScanBlock seeds into blksum.  With kmer, counts
+// and starts come from ctab (the packed table) when it is given, else from end_tbl.
 hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, uint64_t n,
-                             const uint32_t *end_tbl, uint32_t *count, uint32_t *first,
-                             uint32_t *prefix, uint64_t *blksum, hipStream_t s);
+                             const uint32_t *end_tbl, const uint4 *ctab, uint32_t *count,
+                             uint32_t *first, uint32_t *prefix, uint64_t *blksum,
+                             hipStream_t s);
 hipError_t launch_add_offsets(uint32_t *prefix, uint64_t n, const uint32_t *blkoff,
                               hipStream_t s);
 

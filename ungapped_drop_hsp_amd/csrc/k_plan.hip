@@ -9,6 +9,14 @@
 // batch whose total is over 2^32 - 1) and k_add_offsets adds each block's exclusive
 // offset back, giving the inclusive prefix.
 //
+// The per-seed lookup reads a packed form of the cumulative bucket ends (k_count_table):
+// one 32-byte record per 28 consecutive keys, holding the bucket start of the first key
+// and the count of each key in a byte, eight times smaller than the 4^w-entry table.
+// Every lookup is one random line either way; random lines come faster from a smaller
+// region (an XCD's 4 MB L2 holds a larger share of it, and address translation reaches
+// it with fewer entries).  A record in which some key has 255 or more hits is marked,
+// and its keys are looked up in the full table.
+//
 // k_chunk_walk: the MAX_HITS cut ("C. Hit discovery", C.3) on the device, by one wave.
 // Each boundary is the first seed whose prefix reaches H + MAX_HITS, found by a 64-way
 // search: every round the lanes read the last prefix of 64 equal segments of the range
@@ -25,10 +33,55 @@ constexpr int kThreads = 256;
 constexpr int kPerThread = kScanBlock / kThreads;  // 4
 static_assert(kPerThread == 4, "uint4 stores assume four seeds per thread");
 
+constexpr uint32_t kCtMarked = 0xFFFFFFFFu;  // record with a count over 254
+
+// Record g of the packed count table from the cumulative ends end_tbl[0 .. nb].
+__global__ __launch_bounds__(kThreads) void k_count_table(const uint32_t *__restrict__ end_tbl,
+                                                          uint64_t nb, uint32_t n_rec,
+                                                          uint4 *__restrict__ ctab) {
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= n_rec) return;
+    const uint64_t k0 = (uint64_t)g * kCountTableKeys;
+    uint32_t w[8] = {end_tbl[min<uint64_t>(k0, nb)], 0, 0, 0, 0, 0, 0, 0};
+    bool marked = false;
+    for (uint32_t j = 0; j < kCountTableKeys; j++) {
+        const uint64_t k = k0 + j;
+        const uint32_t c = k < nb ? end_tbl[k + 1] - end_tbl[k] : 0u;
+        marked |= c > 254u;
+        w[1 + j / 4] |= min(c, 255u) << (8 * (j % 4));
+    }
+    if (marked) w[0] = kCtMarked;
+    ctab[2 * (uint64_t)g] = make_uint4(w[0], w[1], w[2], w[3]);
+    ctab[2 * (uint64_t)g + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// Bucket start and hit count of the key at offset i (0 .. 27) of an unmarked record
+// (dwords a.x .. b.w): the record's start plus the counts of the keys before it.
+__device__ __forceinline__ void count_record(const uint4 a, const uint4 b, uint32_t i,
+                                             uint32_t &start, uint32_t &cnt) {
+    const uint32_t w[7] = {a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t sum = 0, mine = 0;
+#pragma unroll
+    for (int d = 0; d < 7; d++) {
+        // bytes of word d that belong to keys before i
+        const int below = min(max((int)i - 4 * d, 0), 4);
+        const uint32_t mask = below == 4 ? 0xFFFFFFFFu : (1u << (8 * below)) - 1u;
+        sum = __builtin_amdgcn_sad_u8(w[d] & mask, 0u, sum);
+        mine = (int)(i >> 2) == d ? w[d] : mine;
+    }
+    start = a.x + sum;
+    cnt = (mine >> (8 * (i & 3u))) & 0xFFu;
+}
+
+// Mode: 0 = injected counts (counts_in), 1 = k-mers looked up in end_tbl, 2 = k-mers
+// looked up in the packed table.  The four seeds' loads are issued together, with no
+// branch between them, so that a thread keeps four lookups in flight.
+template <int Mode>
 __global__ __launch_bounds__(kThreads) void k_count_scan(
     const uint32_t *__restrict__ kmer, const uint32_t *counts_in, uint64_t n,
-    const uint32_t *__restrict__ end_tbl, uint32_t *count, uint32_t *__restrict__ first_out,
-    uint32_t *__restrict__ prefix, uint64_t *__restrict__ blksum) {
+    const uint32_t *__restrict__ end_tbl, const uint4 *__restrict__ ctab, uint32_t *count,
+    uint32_t *__restrict__ first_out, uint32_t *__restrict__ prefix,
+    uint64_t *__restrict__ blksum) {
     // counts_in may alias count (injected counts are scanned in place): each thread
     // reads its own four entries before writing them.
     __shared__ uint64_t wave_tot[kThreads / 64];
@@ -36,18 +89,53 @@ __global__ __launch_bounds__(kThreads) void k_count_scan(
     const uint64_t first = (uint64_t)blockIdx.x * kScanBlock + (uint64_t)t * kPerThread;
 
     uint32_t c[kPerThread], b[kPerThread];
+    bool in[kPerThread];
+    uint64_t sc[kPerThread];  // the seed, clamped into range (n > 0)
 #pragma unroll
     for (int i = 0; i < kPerThread; i++) {
-        const uint64_t s = first + i;
-        c[i] = 0;
-        b[i] = 0;
-        if (s < n) {
-            if (kmer) {
-                const uint32_t k = kmer[s];
-                b[i] = end_tbl[k];
-                c[i] = end_tbl[k + 1] - b[i];
-            } else {
-                c[i] = counts_in[s];
+        in[i] = first + i < n;
+        sc[i] = in[i] ? first + i : n - 1;
+    }
+    if (Mode == 0) {
+#pragma unroll
+        for (int i = 0; i < kPerThread; i++) {
+            const uint32_t v = counts_in[sc[i]];
+            c[i] = in[i] ? v : 0u;
+            b[i] = 0;
+        }
+    } else {
+        uint32_t k[kPerThread];
+#pragma unroll
+        for (int i = 0; i < kPerThread; i++) k[i] = kmer[sc[i]];
+        if (Mode == 1) {
+            uint32_t lo[kPerThread], hi[kPerThread];
+#pragma unroll
+            for (int i = 0; i < kPerThread; i++) {
+                lo[i] = end_tbl[k[i]];
+                hi[i] = end_tbl[k[i] + 1];
+            }
+#pragma unroll
+            for (int i = 0; i < kPerThread; i++) {
+                b[i] = in[i] ? lo[i] : 0u;
+                c[i] = in[i] ? hi[i] - lo[i] : 0u;
+            }
+        } else {
+            uint4 ra[kPerThread], rb[kPerThread];
+            uint32_t g[kPerThread];
+#pragma unroll
+            for (int i = 0; i < kPerThread; i++) {
+                g[i] = (uint32_t)(((uint64_t)(k[i] >> 2) * 613566757ull) >> 32);  // k / 28
+                ra[i] = ctab[2 * (uint64_t)g[i]];
+                rb[i] = ctab[2 * (uint64_t)g[i] + 1];
+            }
+#pragma unroll
+            for (int i = 0; i < kPerThread; i++) {
+                count_record(ra[i], rb[i], k[i] - g[i] * kCountTableKeys, b[i], c[i]);
+                if (ra[i].x == kCtMarked) {  // a key of this record has over 254 hits
+                    b[i] = end_tbl[k[i]];
+                    c[i] = end_tbl[k[i] + 1] - b[i];
+                }
+                if (!in[i]) b[i] = c[i] = 0;
             }
         }
     }
@@ -214,12 +302,32 @@ hipError_t launch_chunk_walk(const uint32_t *P, uint64_t n, uint64_t max_hits,
 }
 
 hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, uint64_t n,
-                             const uint32_t *end_tbl, uint32_t *count, uint32_t *first,
-                             uint32_t *prefix, uint64_t *blksum, hipStream_t s) {
+                             const uint32_t *end_tbl, const uint4 *ctab, uint32_t *count,
+                             uint32_t *first, uint32_t *prefix, uint64_t *blksum,
+                             hipStream_t s) {
     if (n == 0) return hipSuccess;
     const uint64_t blocks = (n + kScanBlock - 1) / kScanBlock;
-    hipLaunchKernelGGL(k_count_scan, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
-                       counts_in, n, end_tbl, count, first, prefix, blksum);
+    if (!kmer)
+        hipLaunchKernelGGL(k_count_scan<0>, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
+                           counts_in, n, end_tbl, ctab, count, first, prefix, blksum);
+    else if (!ctab)
+        hipLaunchKernelGGL(k_count_scan<1>, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
+                           counts_in, n, end_tbl, ctab, count, first, prefix, blksum);
+    else
+        hipLaunchKernelGGL(k_count_scan<2>, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
+                           counts_in, n, end_tbl, ctab, count, first, prefix, blksum);
+    return hipGetLastError();
+}
+
+uint32_t count_table_records(uint64_t nb) {
+    return (uint32_t)((nb + kCountTableKeys - 1) / kCountTableKeys);
+}
+
+hipError_t launch_count_table(const uint32_t *end_tbl, uint64_t nb, uint4 *ctab,
+                              hipStream_t s) {
+    const uint32_t n_rec = count_table_records(nb);
+    hipLaunchKernelGGL(k_count_table, dim3((n_rec + kThreads - 1) / kThreads), dim3(kThreads),
+                       0, s, end_tbl, nb, n_rec, ctab);
     return hipGetLastError();
 }
 
