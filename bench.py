@@ -65,26 +65,33 @@ def parse():
     return ap.parse_args()
 
 
-def gather_ceiling(torch) -> float:
-    """Random-line rate of the fabric: single 4-byte gathers from a 64 MiB table.
+def line_ceiling(torch, h, region_bytes: int, window_dwords: int):
+    """Random-line rate of the memory fabric, from the library's probe kernel.
 
-    Every gather touches its own 128-byte line, which misses L2 (4 MB per XCD); the rate
-    is the ceiling for kernels whose traffic is one random line per work unit.
+    The probe reads windows of ``window_dwords`` dwords at the start of random 128-byte
+    lines of a region of ``region_bytes`` (each window one line), with 1, 2 or 4 windows in
+    flight per lane; the best rate is the ceiling for a kernel whose traffic is one random
+    line per unit of work in a footprint of that size.  Returns (lines/s, per-variant).
     """
-    n = 48 << 20
-    tab = torch.zeros((1 << 24) + 1, dtype=torch.int32, device="cuda")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(7)
-    idx = torch.randint(0, 1 << 24, (n,), device="cuda", generator=gen)
-    out = torch.empty(n, dtype=torch.int32, device="cuda")
-    torch.index_select(tab, 0, idx, out=out)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        torch.index_select(tab, 0, idx, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    return n / (e0.elapsed_time(e1) / 10 / 1000.0)
+    nbytes = max(128, (region_bytes + 127) // 128 * 128)
+    region = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    blocks = 4096
+    rates = {}
+    for k in (1, 2, 4):
+        iters = max(1, (1 << 26) // (blocks * 256 * k))
+        args = (region, nbytes, window_dwords, k, blocks, iters, 12345, 0x5EED5EED, sink)
+        h.debug_line_probe(*args, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            h.debug_line_probe(*args, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates[k] = blocks * 256 * k * iters / (e0.elapsed_time(e1) / 3 / 1000.0)
+    del region
+    return max(rates.values()), {f"in_flight_{k}": v for k, v in rates.items()}
 
 
 # The sources the hspz_find_hits_gate call is compiled from; the committed counter summary
@@ -345,8 +352,14 @@ def main():
     gate_gsteps = steps_per_anchor * units_avg / (gate_ms_avg * 1e6)
 
     traffic = gate_traffic(w.name, args.gate_mode)
-    ceiling = gather_ceiling(torch)
+    # The gate's reference windows are 64-byte reads from the 4-bit reference copy and its
+    # line-split twin (about one byte per reference base in all); the plan's lookups read
+    # one 32-byte record of the packed count table per seed.
+    ceiling, ceiling_runs = line_ceiling(torch, h, int(w.ref.size), 16)
     gate_lines = None if traffic is None else traffic / 128.0 / (gate_ms_avg / 1000.0)
+    ct_bytes = 32 * -(-(4 ** len([c for c in p["seed_pattern"] if c == "1"])) // 28)
+    plan_ceiling, plan_runs = line_ceiling(torch, h, ct_bytes, 16)
+    plan_ms = stage_ms.get("plan", 0.0)  # every seed of the step planned once
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -381,7 +394,16 @@ def main():
         # the gate's measured fabric traffic in 128-byte lines/s against the random-line
         # rate of a plain gather kernel, measured in this run
         gate_lines=dict(achieved=gate_lines, ceiling=ceiling, unit="lines/s",
-                        frac=None if gate_lines is None else gate_lines / ceiling),
+                        frac=None if gate_lines is None else gate_lines / ceiling,
+                        ceiling_probe=dict(region_bytes=int(w.ref.size), window_bytes=64,
+                                           **ceiling_runs)),
+        # the plan's random lines: one count-table record per seed, over the plan stage's
+        # time (hit counts, block scan, offsets, chunk walk) in the instrumented pass
+        plan_lines=dict(achieved=seeds / (plan_ms / 1000.0) if plan_ms > 0 else None,
+                        ceiling=plan_ceiling, unit="lines/s",
+                        frac=seeds / (plan_ms / 1000.0) / plan_ceiling if plan_ms > 0 else None,
+                        ceiling_probe=dict(region_bytes=ct_bytes, window_bytes=64,
+                                           **plan_runs)),
         gate_stage2_fraction=None if deferred is None else deferred[0] / max(walked, 1),
         gate_exact_fraction=None if deferred is None else deferred[1] / max(walked, 1),
         setup_s=dict(generate=gen_s, upload=upload_s),

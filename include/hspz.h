@@ -85,7 +85,7 @@ typedef struct {
  *                A,C,G,T, row-major; each |entry| <= 10000.
  *  n_score       score of any pair involving N; |n_score| <= 10000.
  *  xdrop         X-drop, 0 <= xdrop <= 1000000 ("D. Score gate", D.2).
- *  hsp_threshold K >= 1; the keep threshold T is derived from it once per engine.
+ *  hsp_threshold K in 1 .. 2^30; the keep threshold T is derived from it once per engine.
  *  max_hits      MAX_HITS chunk cap, 0 = unlimited ("C. Hit discovery", C.3).
  *  expand_mode   0 = density rule (>= 16 hits per seed -> group per seed), 1 = always
  *                thread per seed, 2 = always group per seed ("C. Hit discovery", C.4).
@@ -276,8 +276,14 @@ int hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64_t n, uint32
  * (score >= T, and with entropy_mode 1 also score * H >= 2K, see hspz_params), else 0;
  * d_hsp[i] is written in either case and is meaningful only when accepted.  The
  * diagonal-shared walks (materialize_mode) allocate their scratch in the engine on first
- * use and keep it.  Errors: HSPZ_E_STATE (no reference or query uploaded), HSPZ_E_INVALID
- * (n_surv >= 2^32, NULL buffers), HSPZ_E_NOMEM (the shared walks' scratch), HSPZ_E_HIP. */
+ * use and keep it.  Scores are summed in 32-bit integers on the device: a record is exact
+ * while its two extents together stay below (2^31 - 1) / (largest pair score) - 1024
+ * bases (21,473,812 with HOXD70), which keeps the score and every running score of both
+ * walks, including the bases of their last 512-base tiles, inside int32.  Longer walks
+ * are outside the supported range and their records are unspecified (the CPU oracle
+ * refuses a record whose score does not fit int32).  Errors: HSPZ_E_STATE (no reference
+ * or query uploaded), HSPZ_E_INVALID (n_surv >= 2^32, NULL buffers), HSPZ_E_NOMEM (the
+ * shared walks' scratch), HSPZ_E_HIP. */
 int hspz_materialize(hspz_engine *engine, const uint64_t *d_anchors, const uint32_t *d_ids,
                      uint64_t n_surv, hspz_segment_pair *d_hsp, uint8_t *d_status,
                      void *stream);

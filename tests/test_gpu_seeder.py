@@ -5,7 +5,8 @@ per packed k-mer) against the oracle's sorted key list, and the bucket array of 
 end coordinates element by element (the order inside a bucket is ascending, so it is
 unique).  Seeds are compared whole too: packed k-mer, query end, and the window start
 behind hspz_seed_range.  Inputs mix case, N runs and bytes that are not bases; lengths
-sit around the seed span and across the radix sort's 4,096-pair blocks; seed weights
+sit around the seed span and across the radix sort's 2,048-pair blocks (one, two and
+three blocks); seed weights
 1, 4, 12 and 13 take one to four 8-bit radix passes.
 """
 import numpy as np
@@ -63,7 +64,8 @@ def _check_seeds(eng, qc, pat):
         assert eng.seed_range(lo, hi) == want
 
 
-LENGTHS = [0, 1, 18, 19, 20, 4095 + 18, 4096 + 18, 4097 + 18, 70_001, 1_000_003]
+LENGTHS = [0, 1, 18, 19, 20, 2047 + 18, 2048 + 18, 2049 + 18, 4095 + 18, 4096 + 18,
+           4097 + 18, 70_001, 1_000_003]
 
 
 @pytest.mark.parametrize("n", LENGTHS)
@@ -94,7 +96,7 @@ def test_index_seed_weights(pat):
 
 
 def test_single_bucket_keeps_position_order():
-    # every window has the same key: one bucket of 69,982 ends spanning 18 radix blocks,
+    # every window has the same key: one bucket of 69,982 ends spanning 35 radix blocks,
     # which must stay in ascending order through every stable pass
     ref = np.frombuffer(b"A" * 70_000, np.uint8)
     eng = engine(params_of(PAT12))

@@ -434,7 +434,10 @@ static int impl_hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "|n_score| must be <= 10000");
     if (p->xdrop < 0 || p->xdrop > 1000000)
         return fail(nullptr, HSPZ_E_INVALID, "xdrop must be in 0..1000000");
-    if (p->hsp_threshold < 1) return fail(nullptr, HSPZ_E_INVALID, "hsp_threshold must be >= 1");
+    // the device sums scores in 32 bits: a threshold up to 2^30 keeps R* + L* below 2^31
+    // while the gate still needs both (each walk stops once the flag is known)
+    if (p->hsp_threshold < 1 || p->hsp_threshold > (1 << 30))
+        return fail(nullptr, HSPZ_E_INVALID, "hsp_threshold must be in 1..2^30");
     if (p->expand_mode < 0 || p->expand_mode > 2)
         return fail(nullptr, HSPZ_E_INVALID, "expand_mode must be 0, 1 or 2");
     if (p->chunk_walk < 0 || p->chunk_walk > 1)

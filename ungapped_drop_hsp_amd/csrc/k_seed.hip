@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_key_hist(const uint32_t *__restric
 
 __global__ void k_set_u32(uint32_t *p, uint32_t v) { *p = v; }
 
-// Digit histogram of each 4,096-pair block, stored digit-major: hist[d * nblk + block].
+// Digit histogram of each 2,048-pair block, stored digit-major: hist[d * nblk + block].
 __global__ __launch_bounds__(kThreads) void k_rs_hist(const uint32_t *__restrict__ key,
                                                       uint32_t n, int shift, uint32_t nblk,
                                                       uint32_t *__restrict__ hist) {
