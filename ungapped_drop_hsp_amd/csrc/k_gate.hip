@@ -21,11 +21,13 @@
 //    and the left walk up to nine, all lanes in step, so every block's window word has a
 //    compile-time register index.  Pair scores come from a 16-bit LDS
 //    table indexed by (ref code << 4) | query code, formed for four bases at once with
-//    byte-wise bit selects.  A lane stops at its walk's first drop.  Later stages also
-//    stop it once R* (right) or R* + best so far (left) reaches T; the first stage, which
-//    sees every anchor, leaves that test out of its blocks, since only survivors (a few
-//    in 10^4 random anchors) would pass it, and their long walks go on to the later
-//    stages.  Walks still running at the window's end are appended to a deferred list:
+//    byte-wise bit selects.  A lane stops at its walk's first drop, or once R* (right)
+//    or R* + best so far (left) reaches T, when the flag is 1 whatever follows.  Where
+//    survivors are rare the reach test decides almost nothing in the first stage, which
+//    is bound by its random reference lines, so it costs no time there; where most
+//    anchors survive (tandem repeats) it decides them inside the first window instead of
+//    sending nearly all of them on to the later stages.  Walks still running at the
+//    window's end are appended to a deferred list:
 //    each wave collects them in LDS and the workgroup reserves its share of the global
 //    list with one atomic.
 //
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
         const uint64_t i = i0 + lane;
         const bool valid = i < n;
         const uint64_t a = valid ? anchors[i] : 0ull;
-        Win<RB, LB, false> win;
+        Win<RB, LB, true> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[i] = (uint8_t)res;
@@ -480,8 +482,14 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
 
 // Directory of the fused first stage: the seed that owns the first slot of each wave's
 // range, i.e. the first seed whose prefix - hit_lo exceeds that slot (a binary search).
-__global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n_waves) {
+// The first thread also clears the two deferred-list counters the stages append to.
+__global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n_waves,
+                                                       uint32_t *__restrict__ cnt) {
     const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
+    if (w == 0) {
+        cnt[0] = 0;
+        cnt[1] = 0;
+    }
     if (w >= n_waves) return;
     const uint32_t t = w * (64u * kSteps);
     uint32_t lo = 0, hi = cs.n_seeds;
@@ -560,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
         }
         uint64_t a = 0;
         if (valid) a = (uint64_t)cs.pos[bstart + (top - 1u - t)] | ((uint64_t)qend << 32);
-        Win<RB, LB, false> win;
+        Win<RB, LB, true> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[t] = (uint8_t)res;
@@ -608,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_bucketed(
             a = sa[j];
             raw = si[j];
         }
-        Win<RB, LB, false, false> win;
+        Win<RB, LB, true, false> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res == 1) flags[raw] = 1;
@@ -740,11 +748,13 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     const uint32_t *qry4, const WindowParams &wp,
                                     uint32_t *list1, uint32_t *list2, uint32_t *cnt,
                                     hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
-    if (n == 0) return hipGetLastError();
+    if (n == 0) {
+        hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+        return hipGetLastError();
+    }
     const uint32_t n_waves = (uint32_t)(((uint64_t)n + 64 * kSteps - 1) / (64 * kSteps));
     hipLaunchKernelGGL(k_slot_dir, dim3((n_waves + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                       s, cs, n_waves);
+                       s, cs, n_waves, cnt);
     const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
     if (narrow)
         hipLaunchKernelGGL((k_gate_window_fused<kNarrowRight, kNarrowLeft>), dim3(blocks),
