@@ -916,7 +916,7 @@ static int ensure_bucket(Engine *e, uint64_t n) {
 
 // The fused first stage's per-wave owner directory for a chunk of n anchors.
 static int ensure_dir(Engine *e, uint64_t n) {
-    const uint64_t n_waves = (n + gate_window_wave_slots() - 1) / gate_window_wave_slots();
+    const uint64_t n_waves = gate_window_waves(n);
     if (n_waves <= e->cap_dir && e->d_dir) return HSPZ_OK;
     const uint64_t want = std::max<uint64_t>({n_waves, 1024, e->cap_dir + e->cap_dir / 4});
     int rc = dalloc(e, e->d_dir, want);

@@ -159,13 +159,16 @@ struct ChunkSeeds {
     uint32_t n_seeds;
     uint32_t hit_lo;
 };
-// Slots per wave of the first window stage (and so entries of the directory per slot).
-uint32_t gate_window_wave_slots();
+// 64-slot steps per wave of the first window stage for a call of n anchors (fewer for
+// small calls, so that the grid still fills the GPU), and the number of waves that gives
+// (the entries of the fused stage's directory).
+uint32_t gate_window_steps(uint64_t n);
+uint64_t gate_window_waves(uint64_t n);
 // As launch_gate_window, but the first stage builds each anchor from the chunk's seeds
 // (occurrence j of seed s at slot prefix[s] - 1 - hit_lo - j, "C. Hit discovery", C.5)
 // instead of reading it: anchors[i] is written only where the first stage does not
 // decide flag 0 (the later stages and the materializer read exactly those).
-// cs.dir holds ceil(n / gate_window_wave_slots()) entries.
+// cs.dir holds gate_window_waves(n) entries.
 hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t n,
                                     uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
                                     const uint32_t *qry4, const WindowParams &wp,

@@ -224,7 +224,10 @@ __global__ __launch_bounds__(kThreads) void k_gate_list_wave(const uint64_t *__r
 
 // ------------------------------------------------------------------ window path
 
-constexpr int kSteps = 32;  // 64-anchor steps per wave (first window stage)
+// 64-anchor steps per wave of the first window stage: at most kSteps, and fewer for
+// calls too small to give every SIMD several waves that way (kFillWaves waves in all).
+constexpr int kSteps = 32;
+constexpr uint64_t kFillWaves = 8192;
 // Window sizes, in blocks of eight bases (right of the anchor, left of it).  The first
 // stage sees every anchor: (6, 9) decides about 98.4% of random anchors on the 50 Mb
 // workload; the narrower (4, 7) about 86%, with fewer block steps but more leftovers.
@@ -451,9 +454,10 @@ __device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_
 // First stage: every anchor, consecutive 64-anchor steps per wave.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window(
-    const uint64_t *__restrict__ anchors, uint32_t n, uint8_t *__restrict__ flags,
-    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
-    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    const uint64_t *__restrict__ anchors, uint32_t n, uint32_t steps,
+    uint8_t *__restrict__ flags, const uint32_t *__restrict__ ref4,
+    const uint32_t *__restrict__ qry4, WindowParams wp, uint32_t *__restrict__ defer,
+    uint32_t *__restrict__ defer_cnt) {
     __shared__ int16_t tab[kWinTab];
     __shared__ uint32_t seg[kWaves][kSeg];
     __shared__ uint32_t seg_n[kWaves];
@@ -464,8 +468,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     uint32_t nseg = 0;
-    const uint64_t first = ((uint64_t)blockIdx.x * kWaves + w) * (64 * kSteps);
-    for (int step = 0; step < kSteps; step++) {
+    const uint64_t first = ((uint64_t)blockIdx.x * kWaves + w) * (64ull * steps);
+    for (uint32_t step = 0; step < steps; step++) {
         const uint64_t i0 = first + (uint64_t)step * 64;
         if (i0 >= n) break;  // uniform
         const uint64_t i = i0 + lane;
@@ -484,6 +488,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
 // range, i.e. the first seed whose prefix - hit_lo exceeds that slot (a binary search).
 // The first thread also clears the two deferred-list counters the stages append to.
 __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n_waves,
+                                                       uint32_t steps,
                                                        uint32_t *__restrict__ cnt) {
     const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
     if (w == 0) {
@@ -491,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n
         cnt[1] = 0;
     }
     if (w >= n_waves) return;
-    const uint32_t t = w * (64u * kSteps);
+    const uint32_t t = w * (64u * steps);
     uint32_t lo = 0, hi = cs.n_seeds;
     while (lo < hi) {
         const uint32_t mid = lo + (hi - lo) / 2;
@@ -511,7 +516,8 @@ __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n
 // anchor is stored only when the slot is deferred or kept.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
-    ChunkSeeds cs, uint32_t n, uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
+    ChunkSeeds cs, uint32_t n, uint32_t steps, uint64_t *__restrict__ anchors,
+    uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
     __shared__ int16_t tab[kWinTab];
@@ -528,10 +534,10 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     const int w = threadIdx.x >> 6;
     uint32_t nseg = 0;
     const uint64_t wave = (uint64_t)blockIdx.x * kWaves + w;
-    const uint64_t first = wave * (64 * kSteps);
+    const uint64_t first = wave * (64ull * steps);
     uint32_t wb = first < n ? cs.dir[wave] : 0u;  // window: seeds wb .. wb + 63
     bool loaded = false;                          // uniform
-    for (int step = 0; step < kSteps; step++) {
+    for (uint32_t step = 0; step < steps; step++) {
         const uint64_t i0 = first + (uint64_t)step * 64;
         if (i0 >= n) break;  // uniform
         const uint32_t t = (uint32_t)(i0 + lane);
@@ -589,7 +595,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_bucketed(
     const uint64_t *__restrict__ sa, const uint32_t *__restrict__ si, uint32_t n,
-    uint32_t part, uint8_t *__restrict__ flags, const uint32_t *__restrict__ ref4,
+    uint32_t part, uint32_t steps, uint8_t *__restrict__ flags,
+    const uint32_t *__restrict__ ref4,
     const uint32_t *__restrict__ qry4, WindowParams wp, uint32_t *__restrict__ defer,
     uint32_t *__restrict__ defer_cnt) {
     __shared__ int16_t tab[kWinTab];
@@ -604,8 +611,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_bucketed(
     uint32_t nseg = 0;
     const uint64_t lo = (uint64_t)(blockIdx.x & 7u) * part;
     const uint64_t hi = std::min<uint64_t>(lo + part, n);
-    const uint64_t first = lo + ((uint64_t)(blockIdx.x >> 3) * kWaves + w) * (64 * kSteps);
-    for (int step = 0; step < kSteps; step++) {
+    const uint64_t first = lo + ((uint64_t)(blockIdx.x >> 3) * kWaves + w) * (64ull * steps);
+    for (uint32_t step = 0; step < steps; step++) {
         const uint64_t j0 = first + (uint64_t)step * 64;
         if (j0 >= hi) break;  // uniform
         const uint64_t j = j0 + lane;
@@ -729,19 +736,29 @@ hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, 
                               uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
     hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
     if (n == 0) return hipGetLastError();
-    const uint64_t per_block = (uint64_t)kWaves * 64 * kSteps;
+    const uint32_t steps = gate_window_steps(n);
+    const uint64_t per_block = (uint64_t)kWaves * 64 * steps;
     const uint32_t blocks = (uint32_t)(((uint64_t)n + per_block - 1) / per_block);
     if (narrow)
         hipLaunchKernelGGL((k_gate_window<kNarrowRight, kNarrowLeft>), dim3(blocks),
-                           dim3(kThreads), 0, s, anchors, n, flags, ref4, qry4, wp, list1, cnt);
+                           dim3(kThreads), 0, s, anchors, n, steps, flags, ref4, qry4, wp,
+                           list1, cnt);
     else
         hipLaunchKernelGGL((k_gate_window<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads),
-                           0, s, anchors, n, flags, ref4, qry4, wp, list1, cnt);
+                           0, s, anchors, n, steps, flags, ref4, qry4, wp, list1, cnt);
     launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
     return hipGetLastError();
 }
 
-uint32_t gate_window_wave_slots() { return 64u * kSteps; }
+uint32_t gate_window_steps(uint64_t n) {
+    const uint64_t want = (n + 64 * kFillWaves - 1) / (64 * kFillWaves);
+    return (uint32_t)std::min<uint64_t>(std::max<uint64_t>(want, 1), kSteps);
+}
+
+uint64_t gate_window_waves(uint64_t n) {
+    const uint64_t slots = 64ull * gate_window_steps(n);
+    return (n + slots - 1) / slots;
+}
 
 hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t n,
                                     uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
@@ -752,18 +769,19 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
         hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
     }
-    const uint32_t n_waves = (uint32_t)(((uint64_t)n + 64 * kSteps - 1) / (64 * kSteps));
+    const uint32_t steps = gate_window_steps(n);
+    const uint32_t n_waves = (uint32_t)gate_window_waves(n);
     hipLaunchKernelGGL(k_slot_dir, dim3((n_waves + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                       s, cs, n_waves, cnt);
+                       s, cs, n_waves, steps, cnt);
     const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
     if (narrow)
         hipLaunchKernelGGL((k_gate_window_fused<kNarrowRight, kNarrowLeft>), dim3(blocks),
-                           dim3(kThreads), 0, s, cs, n, anchors, flags, ref4, qry4, wp, list1,
-                           cnt);
+                           dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
+                           list1, cnt);
     else
         hipLaunchKernelGGL((k_gate_window_fused<kWideRight, kWideLeft>), dim3(blocks),
-                           dim3(kThreads), 0, s, cs, n, anchors, flags, ref4, qry4, wp, list1,
-                           cnt);
+                           dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
+                           list1, cnt);
     launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
     return hipGetLastError();
 }
@@ -778,10 +796,12 @@ hipError_t launch_gate_window_bucketed(const uint64_t *anchors, uint32_t n, cons
     hipError_t st = launch_zero_bytes(flags, n, s);
     if (st != hipSuccess) return st;
     const uint32_t part = (uint32_t)(((uint64_t)n + 7) / 8);
-    const uint64_t per_block = (uint64_t)kWaves * 64 * kSteps;
+    const uint32_t steps = gate_window_steps(n);
+    const uint64_t per_block = (uint64_t)kWaves * 64 * steps;
     const uint32_t blocks = 8u * (uint32_t)(((uint64_t)part + per_block - 1) / per_block);
     hipLaunchKernelGGL((k_gate_window_bucketed<kWideRight, kWideLeft>), dim3(blocks),
-                       dim3(kThreads), 0, s, sa, si, n, part, flags, ref4, qry4, wp, list1, cnt);
+                       dim3(kThreads), 0, s, sa, si, n, part, steps, flags, ref4, qry4, wp,
+                       list1, cnt);
     launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
     return hipGetLastError();
 }
