@@ -59,9 +59,9 @@ def parse():
                     help="CPU oracle sample budget in seconds (0 skips the CPU leg)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
-    ap.add_argument("--gate-mode", type=int, default=0, choices=[0, 1, 2, 3, 4],
+    ap.add_argument("--gate-mode", type=int, default=0, choices=[0, 1, 2, 3, 4, 5],
                     help="score gate variant (0 auto, 1 exact walk, 2 window, 3 narrow window, "
-                         "4 reference-bucketed window)")
+                         "4 reference-bucketed window, 5 key-grouped window)")
     return ap.parse_args()
 
 

@@ -99,9 +99,14 @@ typedef struct {
  *                D.5): the call's anchors are sorted stably by reference slice (2^22
  *                bases or more, at most 256 slices) with their raw indices, each XCD's
  *                waves score the windows of about one slice at a time, and results go
- *                back by raw index (2, 3 and 4 fail with HSPZ_E_INVALID if the window
- *                gate is not exact).  Every mode writes the same flags ("D. Score gate",
- *                D.2).
+ *                back by raw index; 5 = windowed, with hspz_find_hits_gate taking every
+ *                chunk in key-grouped order: the chunk's seeds of each k-mer times that
+ *                k-mer's bucket, so that same-k-mer seeds share the reads of the bucket's
+ *                reference windows (mode 0 does this for chunks holding at least half as
+ *                many seeds as the strand has distinct k-mers; the grouping is built by
+ *                hspz_upload_query and hspz_upload_seeds in modes 0 and 5).  2 to 5 fail
+ *                with HSPZ_E_INVALID if the window gate is not exact.  Every mode writes
+ *                the same flags ("D. Score gate", D.2).
  *  entropy_mode  the accept decision of hspz_materialize ("E. X-drop materialization",
  *                E.5, which names an entropy-adjusted decision without a formula):
  *                0 = accept iff score >= T; 1 = also require score * H >= 2 * K, where H

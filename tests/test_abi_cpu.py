@@ -51,7 +51,7 @@ def test_create_rejects_bad_parameters_without_gpu():
     for kw in (dict(seed_pattern="0111"), dict(seed_pattern="1" * 15),
                dict(seed_pattern="11x1"), dict(hsp_threshold=0), dict(hsp_threshold=2**30 + 1),
                dict(xdrop=-1),
-               dict(expand_mode=3), dict(chunk_walk=2), dict(gate_mode=5),
+               dict(expand_mode=3), dict(chunk_walk=2), dict(gate_mode=6),
                dict(gate_mode=-1), dict(entropy_mode=2), dict(ref_buckets=257),
                dict(ref_buckets=-1), dict(materialize_mode=3), dict(materialize_mode=-1),
                dict(gate_mode=2, xdrop=600)):  # 7 * max score > X: no exact window gate

@@ -109,9 +109,9 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
 @pytest.mark.parametrize("expand_mode,gate_mode,mat", [(0, 0, 0), (1, 1, 0), (2, 2, 0), (0, 3, 0),
-                                                        (0, 4, 0), (0, 0, 2)],
+                                                        (0, 4, 0), (0, 0, 2), (0, 5, 0)],
                          ids=["auto", "sparse-exact", "dense-window", "auto-window2",
-                              "bucketed", "shared-walks"])
+                              "bucketed", "shared-walks", "key-grouped"])
 def test_random_pass_parity(case, expand_mode, gate_mode, mat):
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
     ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
@@ -450,9 +450,10 @@ def _oracle_batch(o):
                 n_accepted=int(acc.size)), acc
 
 
+@pytest.mark.parametrize("gate_mode", [0, 5], ids=["auto", "key-grouped"])
 @pytest.mark.parametrize("mat", [0, 2], ids=["default-walks", "shared-walks"])
 @pytest.mark.parametrize("case", CASES[:4], ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
-def test_run_batch_matches_the_oracle(case, mat):
+def test_run_batch_matches_the_oracle(case, mat, gate_mode):
     # the native whole-batch driver against the oracle's pass: counts and every accepted
     # record, in chunk order, over the whole strand and over sub-batches (with shared
     # walks the driver sorts its own survivors by diagonal alone)
@@ -460,7 +461,7 @@ def test_run_batch_matches_the_oracle(case, mat):
     ref, qry = random_pair(seed, nr, nq, n_frac=nf, plant=plant, plant_len=(60, 600),
                            identity=ident, gc=gc, alphabet_noise=True)
     p = params_of(pat, max_hits=mx)
-    eng = engine(p, materialize_mode=mat)
+    eng = engine(p, materialize_mode=mat, gate_mode=gate_mode)
     eng.upload_reference(ref)
     eng.upload_query(qry)
     n = eng.num_seeds()
@@ -656,7 +657,7 @@ def _fused_vs_calls(eng, n_seeds):
     return tot, checked
 
 
-@pytest.mark.parametrize("gate_mode", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("gate_mode", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-{c[3]}-max{c[4]}")
 def test_find_hits_gate_matches_the_calls(case, gate_mode):
     seed, nr, nq, pat, mx, nf, plant, ident, gc = case
@@ -708,19 +709,20 @@ def test_find_hits_gate_huge_bucket_and_sparse_seeds():
                           bases[rng.integers(0, 4, 20_000)]])
     qry = np.concatenate([bases[rng.integers(0, 4, 9_000)], np.full(300, ord("A"), np.uint8),
                           bases[rng.integers(0, 4, 9_000)]])
-    for mx in (0, 50_000, 3_000):
-        eng = engine(params_of(SEED_PATTERN, max_hits=mx))
-        eng.upload_reference(ref)
-        eng.upload_query(qry)
+    for gm in (0, 5):  # 5: every chunk key-grouped, also chunks cut inside the bucket
+        for mx in (0, 50_000, 3_000):
+            eng = engine(params_of(SEED_PATTERN, max_hits=mx), gate_mode=gm)
+            eng.upload_reference(ref)
+            eng.upload_query(qry)
+            tot, checked = _fused_vs_calls(eng, eng.num_seeds())
+            assert checked == tot and tot > 100_000
+        ref2 = bases[rng.integers(0, 4, 60_000)]
+        qry2 = bases[rng.integers(0, 4, 60_000)]
+        eng = engine(params_of("11111111111", max_hits=7), gate_mode=gm)
+        eng.upload_reference(ref2)
+        eng.upload_query(qry2)
         tot, checked = _fused_vs_calls(eng, eng.num_seeds())
-        assert checked == tot and tot > 100_000
-    ref2 = bases[rng.integers(0, 4, 60_000)]
-    qry2 = bases[rng.integers(0, 4, 60_000)]
-    eng = engine(params_of("11111111111", max_hits=7))
-    eng.upload_reference(ref2)
-    eng.upload_query(qry2)
-    tot, checked = _fused_vs_calls(eng, eng.num_seeds())
-    assert checked == tot
+        assert checked == tot
 
 
 def test_dedup_records_matches_the_oracle():
@@ -951,3 +953,41 @@ def test_plan_counts_from_the_packed_table(pat):
     assert int(o["count"].max()) > 254
     eng = engine(p)
     assert_pass_equal(gpu_full_pass(eng, ref, qry), o)
+
+
+def test_key_grouped_stage_upload_orders_and_caller_seeds():
+    # the key-grouped first stage needs the grouped seeds and their buckets: the
+    # reference uploaded after the query, uploaded again, and caller seeds (some k-mers
+    # repeated, others absent from the reference) must each give the oracle's records
+    ref, qry = random_pair(41, 30_000, 25_000, n_frac=0.02, plant=20, plant_len=(80, 700),
+                           identity=0.9, gc=0.41)
+    p = params_of("1101011", max_hits=20_000)
+    o, R, qc = oracle_pass(ref, qry, p)
+    want, acc = _oracle_batch(o)
+    eng = engine(p, gate_mode=5)
+    eng.upload_query(qry)
+    eng.upload_reference(ref)  # after the query
+    st = eng.run_batch(0, eng.num_seeds())
+    assert {k: st[k] for k in want} == want
+    assert np.array_equal(eng.batch_records().view(np.uint8),
+                          acc.astype(oracle.HSP_DTYPE).view(np.uint8))
+    ref_b, _ = random_pair(42, 30_000, 1, gc=0.41)
+    eng.upload_reference(ref_b)  # a different reference: new buckets for the same runs
+    ob, _, _ = oracle_pass(ref_b, qry, p)
+    want_b, acc_b = _oracle_batch(ob)
+    st = eng.run_batch(0, eng.num_seeds())
+    assert {k: st[k] for k in want_b} == want_b
+    assert np.array_equal(eng.batch_records().view(np.uint8),
+                          acc_b.astype(oracle.HSP_DTYPE).view(np.uint8))
+    # caller seeds: every third seed, with a run of one repeated k-mer
+    kmer, q_end, _ = oracle.query_seeds(qc, p["seed_pattern"])
+    k2, q2 = kmer[::3].copy(), q_end[::3].copy()
+    k2[100:400] = k2[100]
+    eng.upload_reference(ref)
+    eng.upload_seeds(k2, q2)
+    oc = oracle.run_pass(R, qc, p, seeds=(k2, q2, q2 - 7))
+    want_c, acc_c = _oracle_batch(oc)
+    st = eng.run_batch(0, eng.num_seeds())
+    assert {k: st[k] for k in want_c} == want_c
+    assert np.array_equal(eng.batch_records().view(np.uint8),
+                          acc_c.astype(oracle.HSP_DTYPE).view(np.uint8))

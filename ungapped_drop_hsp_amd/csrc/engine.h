@@ -45,6 +45,21 @@ struct Engine {
     uint32_t *d_qend = nullptr;
     uint64_t n_seeds = 0;
     std::vector<uint32_t> h_seed_start;  // window start of every seed (ascending)
+    // the strand's seeds grouped by k-mer, for the key-grouped first gate stage
+    // (KeyGroups in hspz_internal.h): built with the seeds when that stage may run;
+    // kg_ready once the runs' buckets are known (a reference is there too)
+    bool kg_built = false, kg_ready = false;
+    uint32_t *d_kg_qk = nullptr, *d_kg_qs = nullptr, *d_kg_qe = nullptr;
+    uint32_t *d_kg_runs = nullptr, *d_kg_run_c = nullptr, *d_kg_run_first = nullptr;
+    uint2 *d_kg_run_seeds = nullptr;
+    uint32_t kg_n_runs = 0;
+    // its per-chunk scratch (KgScratch), for cap_kg runs and cap_kg_dir waves
+    uint32_t *d_kg_G = nullptr, *d_kg_a = nullptr, *d_kg_m = nullptr;
+    uint32_t *d_kg_dir = nullptr;
+    uint64_t *d_kg_blksum = nullptr;
+    uint32_t *d_kg_blkoff = nullptr;
+    PlanInfo *d_kg_info = nullptr;
+    uint64_t cap_kg = 0, cap_kg_dir = 0;
 
     // plan of one batch
     bool has_plan = false;

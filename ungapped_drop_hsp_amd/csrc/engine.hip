@@ -305,12 +305,121 @@ int set_device(Engine *e) {
     return HSPZ_OK;
 }
 
+// Whether the key-grouped first stage can serve this engine at all (gate_mode 0 or 5 with
+// the window gate's preconditions).
+bool kg_wanted(const Engine *e) {
+    return e->window_ok && (e->params.gate_mode == 0 || e->params.gate_mode == 5);
+}
+
+// Each run's bucket size and start, once both the grouping and a reference are there.
+int kg_run_info(Engine *e, hipStream_t s) {
+    e->kg_ready = false;
+    if (!e->kg_built || !e->has_ref) return HSPZ_OK;
+    int rc;
+    if ((rc = dalloc(e, e->d_kg_run_c, e->kg_n_runs)) ||
+        (rc = dalloc(e, e->d_kg_run_first, e->kg_n_runs)))
+        return rc;
+    HIP_TRY(e, launch_kg_run_info(e->d_kg_qk, e->d_kg_runs, e->kg_n_runs, e->d_end,
+                                  e->d_kg_run_c, e->d_kg_run_first, s));
+    HIP_TRY(e, hipStreamSynchronize(s));
+    e->kg_ready = true;
+    return HSPZ_OK;
+}
+
+// The strand's seeds grouped by k-mer (the key-grouped first stage): a stable radix sort
+// of (k-mer, seed) pairs, the query ends in that order, and the start of each k-mer's run.
+int kg_build(Engine *e, hipStream_t s) {
+    e->kg_built = e->kg_ready = false;
+    e->kg_n_runs = 0;
+    if (!kg_wanted(e) || e->n_seeds == 0) return HSPZ_OK;
+    const uint32_t n = (uint32_t)e->n_seeds;
+    int rc;
+    DevBuf<uint32_t> kb, vb;
+    if ((rc = dalloc(e, e->d_kg_qk, n)) || (rc = dalloc(e, e->d_kg_qs, n)) ||
+        (rc = dalloc(e, kb.p, n)) || (rc = dalloc(e, vb.p, n)))
+        return rc;
+    HIP_TRY(e, hipMemcpyAsync(e->d_kg_qk, e->d_kmer, (uint64_t)n * sizeof(uint32_t),
+                              hipMemcpyDeviceToDevice, s));
+    HIP_TRY(e, launch_iota(e->d_kg_qs, n, s));
+    {
+        const uint64_t nh = 256ull * radix_blocks(n);
+        DevBuf<uint32_t> hist, incl;
+        if ((rc = dalloc(e, hist.p, nh)) || (rc = dalloc(e, incl.p, nh))) return rc;
+        uint32_t *ka = e->d_kg_qk, *va = e->d_kg_qs, *kb2 = kb.p, *vb2 = vb.p;
+        for (int shift = 0; shift < 2 * e->weight; shift += 8) {
+            HIP_TRY(e, launch_radix_hist(ka, n, shift, hist.p, s));
+            if ((rc = device_scan(e, hist.p, nh, incl.p, s))) return rc;
+            HIP_TRY(e, launch_radix_scatter(ka, va, n, shift, incl.p, hist.p, kb2, vb2, s));
+            std::swap(ka, kb2);
+            std::swap(va, vb2);
+        }
+        if (ka != e->d_kg_qk) {  // an odd number of passes: the result is in kb / vb
+            HIP_TRY(e, hipMemcpyAsync(e->d_kg_qk, ka, (uint64_t)n * sizeof(uint32_t),
+                                      hipMemcpyDeviceToDevice, s));
+            HIP_TRY(e, hipMemcpyAsync(e->d_kg_qs, va, (uint64_t)n * sizeof(uint32_t),
+                                      hipMemcpyDeviceToDevice, s));
+        }
+    }
+    if ((rc = dalloc(e, e->d_kg_qe, n))) return rc;
+    HIP_TRY(e, launch_kg_gather(e->d_kg_qs, n, e->d_qend, e->d_kg_qe, s));
+    {
+        DevBuf<uint8_t> flag;
+        if ((rc = dalloc(e, flag.p, n)) || (rc = dalloc(e, e->d_kg_runs, n)) ||
+            (rc = ensure_compact(e, n)))
+            return rc;
+        HIP_TRY(e, launch_kg_run_flags(e->d_kg_qk, n, flag.p, s));
+        HIP_TRY(e, launch_compact(flag.p, n, e->d_cblk, e->d_ctotal, e->d_kg_runs, nullptr,
+                                  nullptr, n, s));
+        HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_ctotal, sizeof(uint32_t),
+                                  hipMemcpyDeviceToHost, s));
+        HIP_TRY(e, hipStreamSynchronize(s));
+    }
+    e->kg_n_runs = e->h_pinned[0];
+    if ((rc = dalloc(e, e->d_kg_run_seeds, e->kg_n_runs))) return rc;
+    HIP_TRY(e, launch_kg_run_seeds(e->d_kg_qs, n, e->d_kg_runs, e->kg_n_runs, e->d_kg_run_seeds,
+                                   s));
+    e->kg_built = true;
+    return kg_run_info(e, s);
+}
+
+// Per-chunk scratch of the key-grouped stage for the current runs and n_waves waves.
+int ensure_kg(Engine *e, uint64_t n_waves) {
+    int rc;
+    const uint64_t nr = std::max<uint64_t>(e->kg_n_runs, 1);
+    if (nr > e->cap_kg || !e->d_kg_G) {
+        const uint64_t nblk = (nr + kScanBlock - 1) / kScanBlock;
+        if ((rc = dalloc(e, e->d_kg_G, nr)) ||
+            (rc = dalloc(e, e->d_kg_a, nr)) || (rc = dalloc(e, e->d_kg_m, nr)) ||
+            (rc = dalloc(e, e->d_kg_blksum, nblk)) || (rc = dalloc(e, e->d_kg_blkoff, nblk)) ||
+            (rc = dalloc(e, e->d_kg_info, 1))) {
+            e->cap_kg = 0;
+            return rc;
+        }
+        e->cap_kg = nr;
+    }
+    if (n_waves > e->cap_kg_dir || !e->d_kg_dir) {
+        const uint64_t want = std::max<uint64_t>({n_waves, 1024, e->cap_kg_dir + e->cap_kg_dir / 4});
+        if ((rc = dalloc(e, e->d_kg_dir, want))) {
+            e->cap_kg_dir = 0;
+            return rc;
+        }
+        e->cap_kg_dir = want;
+    }
+    return HSPZ_OK;
+}
+
 }  // namespace
 
 Engine::~Engine() {
     (void)hipSetDevice(device);
     dfree(d_end);
     dfree(d_ctab);
+    for (uint32_t **q : {&d_kg_qk, &d_kg_qs, &d_kg_qe, &d_kg_runs, &d_kg_run_c, &d_kg_run_first,
+                         &d_kg_G, &d_kg_a, &d_kg_m, &d_kg_dir, &d_kg_blkoff})
+        dfree(*q);
+    dfree(d_kg_blksum);
+    dfree(d_kg_info);
+    dfree(d_kg_run_seeds);
     dfree(d_pos);
     dfree(d_ref);
     dfree(d_qry);
@@ -448,8 +557,8 @@ static int impl_hspz_engine_create(const hspz_params *p, hspz_engine **out) {
         return fail(nullptr, HSPZ_E_INVALID, "ref_buckets must be in 0..256");
     if (p->materialize_mode < 0 || p->materialize_mode > 2)
         return fail(nullptr, HSPZ_E_INVALID, "materialize_mode must be 0, 1 or 2");
-    if (p->gate_mode < 0 || p->gate_mode > 4)
-        return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2, 3 or 4");
+    if (p->gate_mode < 0 || p->gate_mode > 5)
+        return fail(nullptr, HSPZ_E_INVALID, "gate_mode must be 0, 1, 2, 3, 4 or 5");
 
     Engine *e = new (std::nothrow) Engine();
     if (!e) return fail(nullptr, HSPZ_E_NOMEM, "engine allocation failed");
@@ -502,7 +611,7 @@ static int impl_hspz_engine_create(const hspz_params *p, hspz_engine **out) {
     if (p->gate_mode >= 2 && !e->window_ok) {
         delete e;
         return fail(nullptr, HSPZ_E_INVALID,
-                    "gate_modes 2, 3 and 4 need 7 * max score <= xdrop and 16-bit pair scores");
+                    "gate_modes 2 to 5 need 7 * max score <= xdrop and 16-bit pair scores");
     }
     // the device last, so that every parameter error is reported as such on any machine
     int ndev = 0;
@@ -620,7 +729,7 @@ static int impl_hspz_upload_reference(hspz_engine *engine, const uint8_t *h_asci
     e->sp.n_ref = (uint32_t)len;
     e->wp.n_ref = (uint32_t)len;
     e->has_ref = true;
-    return HSPZ_OK;
+    return kg_run_info(e, s);  // the grouped seeds' buckets come from this reference
 }
 
 static int impl_hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
@@ -656,7 +765,7 @@ static int impl_hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, u
     e->n_seeds = ns;
     e->strand = strand;
     e->has_qry = true;
-    return HSPZ_OK;
+    return kg_build(e, s);
 }
 
 // Caller seeds in place of the device seeder's, for the current query strand.
@@ -700,7 +809,7 @@ static int impl_hspz_upload_seeds(hspz_engine *engine, const uint32_t *h_kmer,
     HIP_TRY(e, hipStreamSynchronize(s));
     e->h_seed_start.swap(start);
     e->n_seeds = n;
-    return HSPZ_OK;
+    return kg_build(e, s);
 }
 
 HSPZ_API uint64_t hspz_num_seeds(const hspz_engine *engine) {
@@ -1035,6 +1144,30 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     e->gate_deferred_valid = false;
     const uint64_t n = c.n_hits;
     if ((rc = ensure_defer(e, n))) return rc;
+    uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
+    // The key-grouped first stage pays a pass over every k-mer run of the strand per
+    // chunk; it is taken (gate_mode 0) when the chunk holds at least half as many seeds
+    // as there are runs, i.e. when same-k-mer seeds of the chunk share bucket windows.
+    const uint64_t chunk_seeds = c.seed_hi - c.seed_lo + 1;
+    const bool kg = e->kg_ready && n > 0 &&
+                    (e->params.gate_mode == 5 || 2 * chunk_seeds >= e->kg_n_runs);
+    if (kg) {
+        if ((rc = ensure_kg(e, gate_window_waves(n)))) return rc;
+        KeyGroups g{e->d_kg_qs,        e->d_kg_qe,        e->d_kg_runs,
+                    e->d_kg_run_c,     e->d_kg_run_first, e->d_kg_run_seeds,
+                    e->kg_n_runs,      (uint32_t)e->n_seeds};
+        KgScratch ks{e->d_kg_G, e->d_kg_a, e->d_kg_m, e->d_kg_dir, e->d_kg_blksum,
+                     e->d_kg_blkoff, e->d_kg_info};
+        HIP_TRY(e, launch_gate_window_kg(g, ks, e->d_prefix, (uint32_t)e->batch_lo,
+                                         (uint32_t)c.seed_lo, (uint32_t)c.seed_hi,
+                                         (uint32_t)c.hit_lo, (uint32_t)n, e->d_pos, d_anchors,
+                                         d_flags, e->d_ref4, e->d_qry4, e->wp, list1, list2,
+                                         e->d_defer_cnt, s));
+        HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n,
+                                         d_flags, e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
+        e->gate_deferred_valid = true;
+        return HSPZ_OK;
+    }
     if ((rc = ensure_dir(e, n))) return rc;
     const uint64_t local = c.seed_lo - e->batch_lo;
     ChunkSeeds cs;
@@ -1045,7 +1178,6 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     cs.dir = e->d_dir;
     cs.n_seeds = (uint32_t)(c.seed_hi - c.seed_lo + 1);
     cs.hit_lo = (uint32_t)c.hit_lo;
-    uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
     HIP_TRY(e, launch_gate_window_fused(e->params.gate_mode == 3, cs, (uint32_t)n, d_anchors,
                                         d_flags, e->d_ref4, e->d_qry4, e->wp, list1, list2,
                                         e->d_defer_cnt, s));

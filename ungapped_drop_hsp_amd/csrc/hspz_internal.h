@@ -174,6 +174,59 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     const uint32_t *qry4, const WindowParams &wp,
                                     uint32_t *list1, uint32_t *list2, uint32_t *cnt,
                                     hipStream_t s);
+// Key-grouped first stage (gate_mode 5, and gate_mode 0 for chunks holding a large share
+// of the strand's seeds).  The query strand's seeds are kept grouped by k-mer (built when
+// the query is uploaded): qs lists the seed indices ordered by k-mer and, within a k-mer,
+// ascending; qe their query ends; runs the start in qs of each k-mer's run; run_c and
+// run_first the k-mer's reference bucket (size and start), set once a reference is there.
+// A chunk's anchors are then enumerated run by run: the chunk's seeds of a k-mer (a
+// contiguous stretch of its run) times the k-mer's bucket, so the reference window of
+// each bucket entry and the query window of each seed are read once per group instead
+// of once per anchor.  Every anchor still gets its own flag at its raw slot.
+struct KeyGroups {
+    const uint32_t *qs;
+    const uint32_t *qe;
+    const uint32_t *runs;
+    const uint32_t *run_c;
+    const uint32_t *run_first;
+    const uint2 *run_seeds;  // the first and last seed of each run
+    uint32_t n_runs;
+    uint32_t n_qs;
+};
+// Per-chunk scratch of the key-grouped stage, n_runs entries each (dir: one per wave).
+struct KgScratch {
+    uint32_t *G;       // inclusive prefix of the runs' anchors in this chunk, within each
+                       // kScanBlock runs (plus blkoff[r / kScanBlock] for the chunk's)
+    uint32_t *a;       // index in qs of the run's first seed in the chunk
+    uint32_t *m;       // the run's seeds in the chunk
+    uint32_t *dir;     // per wave: the run owning the wave's first slot
+    uint64_t *blksum;  // per kScanBlock runs: their anchors
+    uint32_t *blkoff;  // and the exclusive prefix of those
+    PlanInfo *info;
+};
+// Upload side (k_seed.hip): identity values, run-start flags of a sorted key list, the
+// query ends in grouped order, and each run's bucket size and start from end_tbl.
+hipError_t launch_iota(uint32_t *v, uint32_t n, hipStream_t s);
+hipError_t launch_kg_run_flags(const uint32_t *qk, uint32_t n, uint8_t *flag, hipStream_t s);
+hipError_t launch_kg_gather(const uint32_t *qs, uint32_t n, const uint32_t *q_end, uint32_t *qe,
+                            hipStream_t s);
+hipError_t launch_kg_run_info(const uint32_t *qk, const uint32_t *runs, uint32_t n_runs,
+                              const uint32_t *end_tbl, uint32_t *run_c, uint32_t *run_first,
+                              hipStream_t s);
+hipError_t launch_kg_run_seeds(const uint32_t *qs, uint32_t n, const uint32_t *runs,
+                               uint32_t n_runs, uint2 *run_seeds, hipStream_t s);
+// The first window stage of one chunk (seeds seed_lo .. seed_hi, strand numbering; hit
+// base hit_lo; n anchors), key-grouped, then the second stage as launch_gate_window_fused:
+// flags receives the chunk's flags (zeroed first, then 1 for the anchors kept), anchors
+// the anchor of every slot whose flag is not decided 0, and list1/list2 the deferred
+// slots.  prefix is the batch's inclusive prefix (batch_lo = its first seed).
+hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
+                                 const uint32_t *prefix, uint32_t batch_lo, uint32_t seed_lo,
+                                 uint32_t seed_hi, uint32_t hit_lo, uint32_t n,
+                                 const uint32_t *pos, uint64_t *anchors, uint8_t *flags,
+                                 const uint32_t *ref4, const uint32_t *qry4,
+                                 const WindowParams &wp, uint32_t *list1, uint32_t *list2,
+                                 uint32_t *cnt, hipStream_t s);
 // Bucketed gate ("D. Score gate", D.5): stable sort of anchors by reference slice
 // (k_bucket.hip) and the first window stage over the sorted anchors (k_gate.hip).
 uint32_t bucket_blocks(uint32_t n);  // workgroups of the slice histogram and scatter

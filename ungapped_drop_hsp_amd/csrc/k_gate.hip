@@ -584,6 +584,208 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
 }
 
+// ------------------------------------------------------------------ key-grouped first stage
+//
+// The chunk's anchors in another order: run by run of the strand's seeds grouped by
+// k-mer, the chunk's seeds of the k-mer (m of them, a contiguous stretch of the run)
+// times the k-mer's bucket (c reference ends).  Within a run the anchors go bucket entry
+// by bucket entry, the m seeds of each entry next to each other, so the lanes of a wave
+// that share a bucket entry read the same reference window and the lanes that share a
+// seed the same query window: a run's c + m windows serve its c * m anchors.  Flags are
+// decided per anchor exactly as in the fused stage; a kept or deferred anchor's raw slot
+// (its seed's inclusive prefix - 1 - hit_lo - its occurrence) is formed only for it.
+
+// Index in the sorted stretch qs[lo, hi) of the first seed >= x (seeds ascend).  Short
+// stretches (most runs hold a few seeds) are counted with independent loads.
+__device__ __forceinline__ uint32_t kg_lower(const uint32_t *__restrict__ qs, uint32_t lo,
+                                             uint32_t hi, uint32_t x) {
+    if (hi - lo <= 8) {
+        if (hi == lo) return lo;
+        uint32_t below = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < 8; k++)
+            below += (lo + k < hi && qs[min(lo + k, hi - 1)] < x) ? 1u : 0u;
+        return lo + below;
+    }
+    while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (qs[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Per run: the chunk's seeds of its k-mer (index of the first in qs, and how many) and
+// the anchors they make with the k-mer's bucket; then the inclusive prefix of those
+// anchor counts within each workgroup's kScanBlock runs (one run per thread, so that
+// the runs' searches overlap), and each workgroup's total (the offsets of the
+// workgroups come from launch_scan_blocks; consumers add them).
+constexpr int kKgThreads = kScanBlock;
+__global__ __launch_bounds__(kKgThreads) void k_kg_groups(KeyGroups kg, uint32_t seed_lo,
+                                                          uint32_t seed_hi, KgScratch ks) {
+    __shared__ uint64_t wave_tot[kKgThreads / 64];
+    const int t = threadIdx.x;
+    const uint64_t r = (uint64_t)blockIdx.x * kKgThreads + t;
+    uint32_t cnt = 0;
+    if (r < kg.n_runs) {
+        const uint32_t c = kg.run_c[r];
+        const uint2 fl = kg.run_seeds[r];
+        uint32_t A = 0, B = 0, a = 0, b = 0;
+        if (c == 0 || fl.y < seed_lo || fl.x > seed_hi) {
+            // no anchors, or no seed of the chunk: nothing to search
+        } else if (fl.x >= seed_lo && fl.y <= seed_hi) {
+            a = kg.runs[r];  // the whole run lies in the chunk
+            b = r + 1 < kg.n_runs ? kg.runs[r + 1] : kg.n_qs;
+        } else if (((A = kg.runs[r]), (B = r + 1 < kg.n_runs ? kg.runs[r + 1] : kg.n_qs)),
+                   B - A <= 8) {
+            // both bounds from one round of loads (a run is never empty)
+            uint32_t v[8];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; k++) v[k] = kg.qs[min(A + k, B - 1)];
+            a = b = A;
+#pragma unroll
+            for (uint32_t k = 0; k < 8; k++) {
+                const bool in = A + k < B;
+                a += (in && v[k] < seed_lo) ? 1u : 0u;
+                b += (in && v[k] <= seed_hi) ? 1u : 0u;
+            }
+        } else {
+            a = kg_lower(kg.qs, A, B, seed_lo);
+            b = seed_hi + 1u == 0u ? B : kg_lower(kg.qs, a, B, seed_hi + 1u);
+        }
+        ks.a[r] = a;
+        ks.m[r] = b - a;
+        // at most the chunk's hits, which fit 32 bits
+        cnt = (uint32_t)((uint64_t)c * (b - a));
+    }
+    const uint64_t incl = wave_incl_sum_u64(cnt);
+    if (lane_id() == 63) wave_tot[t >> 6] = incl;
+    __syncthreads();
+    uint64_t run = incl;
+    for (int w = 0; w < (t >> 6); w++) run += wave_tot[w];
+    if (r < kg.n_runs) ks.G[r] = (uint32_t)run;
+    if (t == kKgThreads - 1) ks.blksum[blockIdx.x] = run;
+}
+
+// Inclusive prefix of run r's anchors over the chunk: its workgroup's offset plus the
+// workgroup-local prefix.
+__device__ __forceinline__ uint32_t kg_prefix(const KgScratch &ks, uint32_t r) {
+    return ks.G[r] + ks.blkoff[r / kScanBlock];
+}
+
+// Per wave of the key-grouped stage: the run owning its first slot (the first run whose
+// inclusive prefix exceeds it).  The first thread also clears the deferred-list counters.
+__global__ __launch_bounds__(kThreads) void k_kg_dir(KgScratch ks, uint32_t n_runs,
+                                                     uint32_t n_waves, uint32_t steps,
+                                                     uint32_t *__restrict__ cnt) {
+    const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
+    if (w == 0) {
+        cnt[0] = 0;
+        cnt[1] = 0;
+    }
+    if (w >= n_waves) return;
+    const uint32_t t = w * (64u * steps);
+    uint32_t lo = 0, hi = n_runs;
+    while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (kg_prefix(ks, mid) > t) hi = mid;
+        else lo = mid + 1;
+    }
+    ks.dir[w] = lo;
+}
+
+// The first window stage over the key-grouped order (see above).  As k_gate_window_fused,
+// a wave keeps a window of 64 runs in LDS (prefix end, bucket size and start, first seed
+// in qs, seeds) and its lanes binary-search it for the run owning their position.
+template <int RB, int LB>
+__global__ __launch_bounds__(kThreads) void k_gate_window_kg(
+    KeyGroups kg, KgScratch ks, const uint32_t *__restrict__ prefix, uint32_t batch_lo,
+    uint32_t hit_lo, uint32_t n, uint32_t steps, const uint32_t *__restrict__ pos,
+    uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
+    const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
+    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    __shared__ int16_t tab[kWinTab];
+    __shared__ uint32_t seg[kWaves][kSeg];
+    __shared__ uint32_t seg_n[kWaves];
+    __shared__ uint32_t blk_base;
+    __shared__ uint32_t rel[kWaves][64];  // inclusive prefix of the window's runs
+    __shared__ uint32_t rc_[kWaves][64];  // their bucket sizes
+    __shared__ uint32_t rf[kWaves][64];   // bucket starts
+    __shared__ uint32_t ra[kWaves][64];   // first seed in qs
+    __shared__ uint32_t rm[kWaves][64];   // seeds in the chunk
+    if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    __syncthreads();
+
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    uint32_t nseg = 0;
+    const uint64_t wave = (uint64_t)blockIdx.x * kWaves + w;
+    const uint64_t first = wave * (64ull * steps);
+    uint32_t wb = first < n ? ks.dir[wave] : 0u;  // window: runs wb .. wb + 63
+    bool loaded = false;                          // uniform
+    for (uint32_t step = 0; step < steps; step++) {
+        const uint64_t i0 = first + (uint64_t)step * 64;
+        if (i0 >= n) break;  // uniform
+        const uint32_t t = (uint32_t)(i0 + lane);
+        const bool valid = t < n;
+        uint32_t top = 0, c = 0, bfirst = 0, sa = 0, m = 1;  // of the position's run
+        bool found = !valid;
+        for (;;) {  // uniform: ends once every position has its run
+            if (!loaded) {
+                const uint32_t r = wb + lane;
+                const bool in = r < kg.n_runs;
+                rel[w][lane] = in ? kg_prefix(ks, r) : 0xFFFFFFFFu;
+                rc_[w][lane] = in ? kg.run_c[r] : 0u;
+                rf[w][lane] = in ? kg.run_first[r] : 0u;
+                ra[w][lane] = in ? ks.a[r] : 0u;
+                rm[w][lane] = in ? ks.m[r] : 1u;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                loaded = true;
+            }
+            if (!found && t < rel[w][63]) {
+                int L = 0;  // number of the window's runs whose prefix is <= t
+#pragma unroll
+                for (int k = 32; k >= 1; k >>= 1)
+                    if (rel[w][L + k - 1] <= t) L += k;
+                top = rel[w][L];
+                c = rc_[w][L];
+                bfirst = rf[w][L];
+                sa = ra[w][L];
+                m = rm[w][L];
+                found = true;
+            }
+            if (__ballot(!found) == 0) break;
+            // a position lies past the window: every lane is done reading it, slide it on
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            wb += 64;
+            loaded = false;
+        }
+        // position u of the run's c * m anchors: bucket entry u / m, seed u % m
+        uint32_t occ = 0, js = 0;
+        uint64_t a = 0;
+        if (valid) {
+            const uint32_t u = t - (top - c * m);
+            occ = u / m;
+            js = sa + (u - occ * m);
+            a = (uint64_t)pos[bfirst + occ] | ((uint64_t)kg.qe[js] << 32);
+        }
+        Win<RB, LB, true> win;
+        win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
+        const int res = win.decide(tab, wp);
+        uint32_t slot = 0;
+        if (valid && res != 0) {
+            const uint32_t seed = kg.qs[js];
+            slot = prefix[seed - batch_lo] - 1u - hit_lo - occ;
+            anchors[slot] = a;
+            if (res == 1) flags[slot] = 1;
+        }
+        defer_push(seg[w], nseg, valid && res == 2, slot, defer, defer_cnt);
+    }
+    defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
+}
+
 // First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
 // D.5).  The sorted array is cut into eight equal contiguous parts, one per XCD, and
 // workgroup b scores tile b / 8 of part b % 8: workgroups are dispatched in index order
@@ -783,6 +985,35 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
                            list1, cnt);
     launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
+                                 const uint32_t *prefix, uint32_t batch_lo, uint32_t seed_lo,
+                                 uint32_t seed_hi, uint32_t hit_lo, uint32_t n,
+                                 const uint32_t *pos, uint64_t *anchors, uint8_t *flags,
+                                 const uint32_t *ref4, const uint32_t *qry4,
+                                 const WindowParams &wp, uint32_t *list1, uint32_t *list2,
+                                 uint32_t *cnt, hipStream_t s) {
+    if (n == 0 || kg.n_runs == 0) {
+        hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+        return hipGetLastError();
+    }
+    const uint32_t nr = kg.n_runs;
+    const uint32_t nblk = (nr + kScanBlock - 1) / kScanBlock;
+    hipLaunchKernelGGL(k_kg_groups, dim3(nblk), dim3(kKgThreads), 0, s, kg, seed_lo, seed_hi, ks);
+    hipError_t st = launch_scan_blocks(ks.blksum, nblk, ks.blkoff, ks.info, s);
+    if (st != hipSuccess) return st;
+    const uint32_t steps = gate_window_steps(n);
+    const uint32_t n_waves = (uint32_t)gate_window_waves(n);
+    hipLaunchKernelGGL(k_kg_dir, dim3((n_waves + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                       ks, nr, n_waves, steps, cnt);
+    if ((st = launch_zero_bytes(flags, n, s)) != hipSuccess) return st;
+    const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL((k_gate_window_kg<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads), 0,
+                       s, kg, ks, prefix, batch_lo, hit_lo, n, steps, pos, anchors, flags, ref4,
+                       qry4, wp, list1, cnt);
+    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
     return hipGetLastError();
 }
 

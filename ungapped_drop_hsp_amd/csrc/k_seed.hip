@@ -112,6 +112,57 @@ __global__ __launch_bounds__(kThreads) void k_key_hist(const uint32_t *__restric
 
 __global__ void k_set_u32(uint32_t *p, uint32_t v) { *p = v; }
 
+// Grouping the query's seeds by k-mer (the key-grouped first gate stage): v[i] = i, the
+// seed indices that the stable sort by k-mer reorders.
+__global__ __launch_bounds__(kThreads) void k_iota(uint32_t *__restrict__ v, uint32_t n) {
+    const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) v[i] = (uint32_t)i;
+}
+
+// 1 where a run of equal keys starts in the sorted key list.
+__global__ __launch_bounds__(kThreads) void k_kg_run_flags(const uint32_t *__restrict__ qk,
+                                                           uint32_t n,
+                                                           uint8_t *__restrict__ flag) {
+    const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) flag[i] = (i == 0 || qk[i] != qk[i - 1]) ? 1 : 0;
+}
+
+// The query end of each seed in grouped order.
+__global__ __launch_bounds__(kThreads) void k_kg_gather(const uint32_t *__restrict__ qs,
+                                                        uint32_t n,
+                                                        const uint32_t *__restrict__ q_end,
+                                                        uint32_t *__restrict__ qe) {
+    const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) qe[i] = q_end[qs[i]];
+}
+
+// Each run's first and last seed.
+__global__ __launch_bounds__(kThreads) void k_kg_run_seeds(const uint32_t *__restrict__ qs,
+                                                           uint32_t n,
+                                                           const uint32_t *__restrict__ runs,
+                                                           uint32_t n_runs,
+                                                           uint2 *__restrict__ run_seeds) {
+    const uint64_t r = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (r >= n_runs) return;
+    const uint32_t end = r + 1 < n_runs ? runs[r + 1] : n;
+    run_seeds[r] = make_uint2(qs[runs[r]], qs[end - 1]);
+}
+
+// Each run's k-mer bucket: its size and start in the reference index.
+__global__ __launch_bounds__(kThreads) void k_kg_run_info(const uint32_t *__restrict__ qk,
+                                                          const uint32_t *__restrict__ runs,
+                                                          uint32_t n_runs,
+                                                          const uint32_t *__restrict__ end_tbl,
+                                                          uint32_t *__restrict__ run_c,
+                                                          uint32_t *__restrict__ run_first) {
+    const uint64_t r = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (r >= n_runs) return;
+    const uint32_t k = qk[runs[r]];
+    const uint32_t b = end_tbl[k];
+    run_first[r] = b;
+    run_c[r] = end_tbl[k + 1] - b;
+}
+
 // Digit histogram of each 2,048-pair block, stored digit-major: hist[d * nblk + block].
 __global__ __launch_bounds__(kThreads) void k_rs_hist(const uint32_t *__restrict__ key,
                                                       uint32_t n, int shift, uint32_t nblk,
@@ -229,6 +280,40 @@ hipError_t launch_set_u32(uint32_t *p, uint32_t v, hipStream_t s) {
 }
 
 uint32_t radix_blocks(uint32_t n) { return (uint32_t)(((uint64_t)n + kRsBlock - 1) / kRsBlock); }
+
+hipError_t launch_iota(uint32_t *v, uint32_t n, hipStream_t s) {
+    if (n) hipLaunchKernelGGL(k_iota, dim3(grid_of(n)), dim3(kThreads), 0, s, v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_kg_run_flags(const uint32_t *qk, uint32_t n, uint8_t *flag, hipStream_t s) {
+    if (n) hipLaunchKernelGGL(k_kg_run_flags, dim3(grid_of(n)), dim3(kThreads), 0, s, qk, n, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_kg_gather(const uint32_t *qs, uint32_t n, const uint32_t *q_end, uint32_t *qe,
+                            hipStream_t s) {
+    if (n)
+        hipLaunchKernelGGL(k_kg_gather, dim3(grid_of(n)), dim3(kThreads), 0, s, qs, n, q_end, qe);
+    return hipGetLastError();
+}
+
+hipError_t launch_kg_run_seeds(const uint32_t *qs, uint32_t n, const uint32_t *runs,
+                               uint32_t n_runs, uint2 *run_seeds, hipStream_t s) {
+    if (n_runs)
+        hipLaunchKernelGGL(k_kg_run_seeds, dim3(grid_of(n_runs)), dim3(kThreads), 0, s, qs, n,
+                           runs, n_runs, run_seeds);
+    return hipGetLastError();
+}
+
+hipError_t launch_kg_run_info(const uint32_t *qk, const uint32_t *runs, uint32_t n_runs,
+                              const uint32_t *end_tbl, uint32_t *run_c, uint32_t *run_first,
+                              hipStream_t s) {
+    if (n_runs)
+        hipLaunchKernelGGL(k_kg_run_info, dim3(grid_of(n_runs)), dim3(kThreads), 0, s, qk, runs,
+                           n_runs, end_tbl, run_c, run_first);
+    return hipGetLastError();
+}
 
 hipError_t launch_radix_hist(const uint32_t *key, uint32_t n, int shift, uint32_t *hist,
                              hipStream_t s) {
