@@ -94,9 +94,10 @@ def line_ceiling(torch, h, region_bytes: int, window_dwords: int):
     return max(rates.values()), {f"in_flight_{k}": v for k, v in rates.items()}
 
 
-# The sources the hspz_find_hits_gate call is compiled from; the committed counter summary
-# holds their combined SHA-256.
-GATE_SOURCES = ("k_gate.hip", "walk.h", "wave.h", "hspz_internal.h")
+# The sources the hspz_find_hits_gate call is compiled from (its kernels, and the block scan
+# and byte fill it launches); the committed counter summary holds their combined SHA-256.
+GATE_SOURCES = ("k_gate.hip", "walk.h", "wave.h", "hspz_internal.h", "k_plan.hip",
+                "k_bucket.hip")
 
 
 def gate_sources_sha() -> str:
@@ -383,7 +384,9 @@ def main():
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
                       traffic=traffic,
-                      kernel="find_hits_gate (expansion fused into the first window stage, second stage, exact list)",
+                      kernel="find_hits_gate (first window stage forming its own anchors, "
+                             "key-grouped when a chunk holds enough seeds; second stage; "
+                             "exact list)",
                       launches_per_step=gate_launches // args.steps,
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
                       base_steps_per_anchor=steps_per_anchor),

@@ -51,7 +51,7 @@ struct Engine {
     bool kg_built = false, kg_ready = false;
     uint32_t *d_kg_qk = nullptr, *d_kg_qs = nullptr, *d_kg_qe = nullptr;
     uint32_t *d_kg_runs = nullptr, *d_kg_run_c = nullptr, *d_kg_run_first = nullptr;
-    uint2 *d_kg_run_seeds = nullptr;
+    uint4 *d_kg_run_span = nullptr;
     uint32_t kg_n_runs = 0;
     // its per-chunk scratch (KgScratch), for cap_kg runs and cap_kg_dir waves
     uint32_t *d_kg_G = nullptr, *d_kg_a = nullptr, *d_kg_m = nullptr;

@@ -375,9 +375,9 @@ int kg_build(Engine *e, hipStream_t s) {
         HIP_TRY(e, hipStreamSynchronize(s));
     }
     e->kg_n_runs = e->h_pinned[0];
-    if ((rc = dalloc(e, e->d_kg_run_seeds, e->kg_n_runs))) return rc;
-    HIP_TRY(e, launch_kg_run_seeds(e->d_kg_qs, n, e->d_kg_runs, e->kg_n_runs, e->d_kg_run_seeds,
-                                   s));
+    if ((rc = dalloc(e, e->d_kg_run_span, e->kg_n_runs))) return rc;
+    HIP_TRY(e, launch_kg_run_span(e->d_kg_qs, n, e->d_kg_runs, e->kg_n_runs, e->d_kg_run_span,
+                                  s));
     e->kg_built = true;
     return kg_run_info(e, s);
 }
@@ -419,7 +419,7 @@ Engine::~Engine() {
         dfree(*q);
     dfree(d_kg_blksum);
     dfree(d_kg_info);
-    dfree(d_kg_run_seeds);
+    dfree(d_kg_run_span);
     dfree(d_pos);
     dfree(d_ref);
     dfree(d_qry);
@@ -1154,7 +1154,7 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     if (kg) {
         if ((rc = ensure_kg(e, gate_window_waves(n)))) return rc;
         KeyGroups g{e->d_kg_qs,        e->d_kg_qe,        e->d_kg_runs,
-                    e->d_kg_run_c,     e->d_kg_run_first, e->d_kg_run_seeds,
+                    e->d_kg_run_c,     e->d_kg_run_first, e->d_kg_run_span,
                     e->kg_n_runs,      (uint32_t)e->n_seeds};
         KgScratch ks{e->d_kg_G, e->d_kg_a, e->d_kg_m, e->d_kg_dir, e->d_kg_blksum,
                      e->d_kg_blkoff, e->d_kg_info};

@@ -189,7 +189,7 @@ struct KeyGroups {
     const uint32_t *runs;
     const uint32_t *run_c;
     const uint32_t *run_first;
-    const uint2 *run_seeds;  // the first and last seed of each run
+    const uint4 *run_span;  // each run: its qs range [x, y) and its first and last seed
     uint32_t n_runs;
     uint32_t n_qs;
 };
@@ -213,8 +213,8 @@ hipError_t launch_kg_gather(const uint32_t *qs, uint32_t n, const uint32_t *q_en
 hipError_t launch_kg_run_info(const uint32_t *qk, const uint32_t *runs, uint32_t n_runs,
                               const uint32_t *end_tbl, uint32_t *run_c, uint32_t *run_first,
                               hipStream_t s);
-hipError_t launch_kg_run_seeds(const uint32_t *qs, uint32_t n, const uint32_t *runs,
-                               uint32_t n_runs, uint2 *run_seeds, hipStream_t s);
+hipError_t launch_kg_run_span(const uint32_t *qs, uint32_t n, const uint32_t *runs,
+                              uint32_t n_runs, uint4 *run_span, hipStream_t s);
 // The first window stage of one chunk (seeds seed_lo .. seed_hi, strand numbering; hit
 // base hit_lo; n anchors), key-grouped, then the second stage as launch_gate_window_fused:
 // flags receives the chunk's flags (zeroed first, then 1 for the anchors kept), anchors

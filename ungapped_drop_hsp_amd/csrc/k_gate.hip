@@ -629,15 +629,15 @@ __global__ __launch_bounds__(kKgThreads) void k_kg_groups(KeyGroups kg, uint32_t
     uint32_t cnt = 0;
     if (r < kg.n_runs) {
         const uint32_t c = kg.run_c[r];
-        const uint2 fl = kg.run_seeds[r];
-        uint32_t A = 0, B = 0, a = 0, b = 0;
-        if (c == 0 || fl.y < seed_lo || fl.x > seed_hi) {
+        const uint4 sp = kg.run_span[r];  // issued with run_c: one round of loads
+        const uint32_t A = sp.x, B = sp.y;
+        uint32_t a = 0, b = 0;
+        if (c == 0 || sp.w < seed_lo || sp.z > seed_hi) {
             // no anchors, or no seed of the chunk: nothing to search
-        } else if (fl.x >= seed_lo && fl.y <= seed_hi) {
-            a = kg.runs[r];  // the whole run lies in the chunk
-            b = r + 1 < kg.n_runs ? kg.runs[r + 1] : kg.n_qs;
-        } else if (((A = kg.runs[r]), (B = r + 1 < kg.n_runs ? kg.runs[r + 1] : kg.n_qs)),
-                   B - A <= 8) {
+        } else if (sp.z >= seed_lo && sp.w <= seed_hi) {
+            a = A;  // the whole run lies in the chunk
+            b = B;
+        } else if (B - A <= 8) {
             // both bounds from one round of loads (a run is never empty)
             uint32_t v[8];
 #pragma unroll

@@ -136,16 +136,17 @@ __global__ __launch_bounds__(kThreads) void k_kg_gather(const uint32_t *__restri
     if (i < n) qe[i] = q_end[qs[i]];
 }
 
-// Each run's first and last seed.
-__global__ __launch_bounds__(kThreads) void k_kg_run_seeds(const uint32_t *__restrict__ qs,
-                                                           uint32_t n,
-                                                           const uint32_t *__restrict__ runs,
-                                                           uint32_t n_runs,
-                                                           uint2 *__restrict__ run_seeds) {
+// Each run's range in the grouped order and its first and last seed, in one record.
+__global__ __launch_bounds__(kThreads) void k_kg_run_span(const uint32_t *__restrict__ qs,
+                                                          uint32_t n,
+                                                          const uint32_t *__restrict__ runs,
+                                                          uint32_t n_runs,
+                                                          uint4 *__restrict__ run_span) {
     const uint64_t r = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
     if (r >= n_runs) return;
-    const uint32_t end = r + 1 < n_runs ? runs[r + 1] : n;
-    run_seeds[r] = make_uint2(qs[runs[r]], qs[end - 1]);
+    const uint32_t a = runs[r];
+    const uint32_t b = r + 1 < n_runs ? runs[r + 1] : n;
+    run_span[r] = make_uint4(a, b, qs[a], qs[b - 1]);
 }
 
 // Each run's k-mer bucket: its size and start in the reference index.
@@ -298,11 +299,11 @@ hipError_t launch_kg_gather(const uint32_t *qs, uint32_t n, const uint32_t *q_en
     return hipGetLastError();
 }
 
-hipError_t launch_kg_run_seeds(const uint32_t *qs, uint32_t n, const uint32_t *runs,
-                               uint32_t n_runs, uint2 *run_seeds, hipStream_t s) {
+hipError_t launch_kg_run_span(const uint32_t *qs, uint32_t n, const uint32_t *runs,
+                              uint32_t n_runs, uint4 *run_span, hipStream_t s) {
     if (n_runs)
-        hipLaunchKernelGGL(k_kg_run_seeds, dim3(grid_of(n_runs)), dim3(kThreads), 0, s, qs, n,
-                           runs, n_runs, run_seeds);
+        hipLaunchKernelGGL(k_kg_run_span, dim3(grid_of(n_runs)), dim3(kThreads), 0, s, qs, n,
+                           runs, n_runs, run_span);
     return hipGetLastError();
 }
 
