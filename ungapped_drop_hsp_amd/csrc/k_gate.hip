@@ -279,7 +279,7 @@ __device__ __forceinline__ void load_plain(const uint32_t *__restrict__ base, ui
 // indices (r << 4 | q) land in the bytes of ie, odd bases' in the bytes of io.
 template <bool Right>
 __device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t Q, int32_t &g,
-                                       int32_t &gmin, int32_t &s) {
+                                       int32_t &gmin, uint32_t &s) {
     const uint32_t hi = 0xF0F0F0F0u;
     uint32_t ie = ((R << 4) & hi) | (Q & ~hi);
     uint32_t io = (R & hi) | ((Q >> 4) & ~hi);
@@ -292,7 +292,7 @@ __device__ __forceinline__ void block8(const int16_t *tab, uint32_t R, uint32_t 
         const int32_t sg = tab[(w >> (8 * (i >> 1))) & 0xFFu];
         g = dd_step(g, sg);
         gmin = min(gmin, g);
-        s += sg;
+        s += (uint32_t)sg;
     }
 }
 
@@ -350,16 +350,19 @@ struct Win {
         const uint64_t live = __builtin_amdgcn_ballot_w64(inrange);
         uint64_t keep = 0;
         int32_t rstar = 0;
-        // right: bases r + 8k .. r + 8k + 7 are window dword LB + k onward
+        // right: bases r + 8k .. r + 8k + 7 are window dword LB + k onward.  s carries the
+        // running score plus kG0 (mod 2^32), so the best so far, score + drawdown, is
+        // s - g in one subtraction (it fits int32).
         uint64_t act = live;
-        int32_t g = kG0, gmin = kG0, s = 0;
+        int32_t g = kG0, gmin = kG0;
+        uint32_t s = (uint32_t)kG0;
         Unrolled<0, RB>::run([&](auto kc) {
             constexpr int k = decltype(kc)::value;
             if (act == 0) return false;
             const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB + k + 1], R[LB + k], shr);
             const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB + k + 1], Q[LB + k], shq);
             block8<true>(tab, Rb, Qb, g, gmin, s);
-            const int32_t best = s + (kG0 - g);
+            const int32_t best = (int32_t)(s - (uint32_t)g);
             const uint64_t drop = __builtin_amdgcn_ballot_w64(gmin < glim) & act;
             rstar = __builtin_amdgcn_inverse_ballot_w64(drop) ? best : rstar;
             act &= ~drop;
@@ -375,14 +378,15 @@ struct Win {
         act = live & ~keep & ~undecided;
         g = kG0;
         gmin = kG0;
-        s = 0;
+        s = (uint32_t)kG0;
+        const int32_t need = wp.T - rstar;  // the left best that makes the flag 1
         Unrolled<0, LB>::run([&](auto kc) {
             constexpr int k = decltype(kc)::value;
             if (act == 0) return false;
             const uint32_t Rb = __builtin_amdgcn_alignbit(R[LB - k], R[LB - 1 - k], shr);
             const uint32_t Qb = __builtin_amdgcn_alignbit(Q[LB - k], Q[LB - 1 - k], shq);
             block8<false>(tab, Rb, Qb, g, gmin, s);
-            const uint64_t reach = __builtin_amdgcn_ballot_w64(rstar + s + (kG0 - g) >= wp.T);
+            const uint64_t reach = __builtin_amdgcn_ballot_w64((int32_t)(s - (uint32_t)g) >= need);
             const uint64_t drop = __builtin_amdgcn_ballot_w64(gmin < glim) & act;
             const uint64_t done = EarlyKeep ? (drop | (reach & act)) : drop;
             keep |= done & reach;
@@ -546,11 +550,15 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
         bool found = !valid;
         for (;;) {  // uniform: ends once every slot has its owner
             if (!loaded) {
+                // the three reads are issued together (a seed past the end reads the
+                // last seed, of which there is at least one, and is then masked)
                 const uint32_t sj = wb + lane;
                 const bool in = sj < cs.n_seeds;
-                rel[w][lane] = in ? cs.prefix[sj] - cs.hit_lo : 0xFFFFFFFFu;
-                fst[w][lane] = in ? cs.first[sj] : 0u;
-                qen[w][lane] = in ? cs.q_end[sj] : 0u;
+                const uint32_t sr = in ? sj : cs.n_seeds - 1u;
+                const uint32_t pr = cs.prefix[sr], fs = cs.first[sr], qe = cs.q_end[sr];
+                rel[w][lane] = in ? pr - cs.hit_lo : 0xFFFFFFFFu;
+                fst[w][lane] = in ? fs : 0u;
+                qen[w][lane] = in ? qe : 0u;
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 loaded = true;
@@ -601,10 +609,12 @@ __device__ __forceinline__ uint32_t kg_lower(const uint32_t *__restrict__ qs, ui
                                              uint32_t hi, uint32_t x) {
     if (hi - lo <= 8) {
         if (hi == lo) return lo;
+        uint32_t v[8];  // all eight reads first, so none waits for another
+#pragma unroll
+        for (uint32_t k = 0; k < 8; k++) v[k] = qs[min(lo + k, hi - 1)];
         uint32_t below = 0;
 #pragma unroll
-        for (uint32_t k = 0; k < 8; k++)
-            below += (lo + k < hi && qs[min(lo + k, hi - 1)] < x) ? 1u : 0u;
+        for (uint32_t k = 0; k < 8; k++) below += (lo + k < hi && v[k] < x) ? 1u : 0u;
         return lo + below;
     }
     while (lo < hi) {
@@ -732,13 +742,19 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
         bool found = !valid;
         for (;;) {  // uniform: ends once every position has its run
             if (!loaded) {
+                // the six reads are issued together (a run past the end reads the last
+                // run, of which there is at least one, and is then masked)
                 const uint32_t r = wb + lane;
                 const bool in = r < kg.n_runs;
-                rel[w][lane] = in ? kg_prefix(ks, r) : 0xFFFFFFFFu;
-                rc_[w][lane] = in ? kg.run_c[r] : 0u;
-                rf[w][lane] = in ? kg.run_first[r] : 0u;
-                ra[w][lane] = in ? ks.a[r] : 0u;
-                rm[w][lane] = in ? ks.m[r] : 1u;
+                const uint32_t rr = in ? r : kg.n_runs - 1u;
+                const uint32_t g = ks.G[rr], off = ks.blkoff[rr / kScanBlock];
+                const uint32_t c = kg.run_c[rr], f = kg.run_first[rr];
+                const uint32_t sa0 = ks.a[rr], m0 = ks.m[rr];
+                rel[w][lane] = in ? g + off : 0xFFFFFFFFu;
+                rc_[w][lane] = in ? c : 0u;
+                rf[w][lane] = in ? f : 0u;
+                ra[w][lane] = in ? sa0 : 0u;
+                rm[w][lane] = in ? m0 : 1u;
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 loaded = true;
@@ -763,20 +779,20 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
             loaded = false;
         }
         // position u of the run's c * m anchors: bucket entry u / m, seed u % m
-        uint32_t occ = 0, js = 0;
+        uint32_t occ = 0, seed = 0;
         uint64_t a = 0;
         if (valid) {
             const uint32_t u = t - (top - c * m);
             occ = u / m;
-            js = sa + (u - occ * m);
+            const uint32_t js = sa + (u - occ * m);
             a = (uint64_t)pos[bfirst + occ] | ((uint64_t)kg.qe[js] << 32);
+            seed = kg.qs[js];  // read with the anchor: a kept or deferred slot needs it
         }
         Win<RB, LB, true> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         uint32_t slot = 0;
         if (valid && res != 0) {
-            const uint32_t seed = kg.qs[js];
             slot = prefix[seed - batch_lo] - 1u - hit_lo - occ;
             anchors[slot] = a;
             if (res == 1) flags[slot] = 1;
