@@ -179,8 +179,12 @@ int hspz_upload_reference(hspz_engine *engine, const uint8_t *h_ascii, uint64_t 
  * care positions are all A/C/G/T, in ascending window position, each with its packed
  * k-mer and its query end coordinate (window start + span).  strand 0 = the sequence
  * as given, 1 = its reverse complement, in the reverse complement's own coordinates.
- * Replaces the previous query and invalidates a plan.  Synchronises stream.  Errors as
- * above. */
+ * In gate_mode 0 and 5, when the window gate is exact, the call also groups the seeds by
+ * k-mer for the key-grouped first gate stage (a stable radix sort of (k-mer, seed)
+ * pairs, then the runs of equal k-mers); the engine then holds 16 more bytes per seed
+ * and 36 per distinct k-mer, and each run's bucket is looked up again whenever a
+ * reference is uploaded.  Replaces the previous query and invalidates a plan.
+ * Synchronises stream.  Errors as above. */
 int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
                       int32_t strand, void *stream);
 
@@ -190,7 +194,8 @@ int hspz_upload_query(hspz_engine *engine, const uint8_t *h_ascii, uint64_t len,
  * length], the window starting at h_q_end[i] - span.  The query ends must not decrease
  * (the order hspz_upload_query produces, on which hspz_seed_range and the batch driver
  * rely).  The k-mers need not match the query's bases; the uploaded strand stays, since
- * the walks read it.  Host arrays, copied; invalidates a plan; synchronises stream.
+ * the walks read it.  The key grouping of hspz_upload_query is rebuilt for these seeds.
+ * Host arrays, copied; invalidates a plan; synchronises stream.
  * Errors: HSPZ_E_STATE (no query strand uploaded), HSPZ_E_INVALID (NULL arrays, a value
  * out of range, decreasing query ends; the seeds are left as they were), HSPZ_E_NOMEM,
  * HSPZ_E_HIP. */

@@ -75,6 +75,8 @@ struct Engine {
     // gate scratch: anchor indices left by each window stage, and their two counts
     uint32_t *d_defer = nullptr;  // 2 * cap_defer entries: stage-1 list, then stage-2 list
     uint64_t cap_defer = 0;
+    uint64_t *d_defer_a = nullptr;  // the key-grouped stage's anchors of the stage-1 list
+    uint64_t cap_defer_a = 0;
     uint32_t *d_defer_cnt = nullptr;
     bool gate_deferred_valid = false;
 

@@ -426,6 +426,7 @@ Engine::~Engine() {
     dfree(d_ref4);
     dfree(d_qry4);
     dfree(d_defer);
+    dfree(d_defer_a);
     dfree(d_defer_cnt);
     dfree(d_kmer);
     dfree(d_qend);
@@ -1153,6 +1154,13 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
                     (e->params.gate_mode == 5 || 2 * chunk_seeds >= e->kg_n_runs);
     if (kg) {
         if ((rc = ensure_kg(e, gate_window_waves(n)))) return rc;
+        if (e->cap_defer_a < e->cap_defer || !e->d_defer_a) {
+            if ((rc = dalloc(e, e->d_defer_a, e->cap_defer))) {
+                e->cap_defer_a = 0;
+                return rc;
+            }
+            e->cap_defer_a = e->cap_defer;
+        }
         KeyGroups g{e->d_kg_qs,        e->d_kg_qe,        e->d_kg_runs,
                     e->d_kg_run_c,     e->d_kg_run_first, e->d_kg_run_span,
                     e->kg_n_runs,      (uint32_t)e->n_seeds};
@@ -1161,8 +1169,8 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
         HIP_TRY(e, launch_gate_window_kg(g, ks, e->d_prefix, (uint32_t)e->batch_lo,
                                          (uint32_t)c.seed_lo, (uint32_t)c.seed_hi,
                                          (uint32_t)c.hit_lo, (uint32_t)n, e->d_pos, d_anchors,
-                                         d_flags, e->d_ref4, e->d_qry4, e->wp, list1, list2,
-                                         e->d_defer_cnt, s));
+                                         d_flags, e->d_ref4, e->d_qry4, e->wp, list1,
+                                         e->d_defer_a, list2, e->d_defer_cnt, s));
         HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n,
                                          d_flags, e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
         e->gate_deferred_valid = true;

@@ -217,16 +217,19 @@ hipError_t launch_kg_run_span(const uint32_t *qs, uint32_t n, const uint32_t *ru
                               uint32_t n_runs, uint4 *run_span, hipStream_t s);
 // The first window stage of one chunk (seeds seed_lo .. seed_hi, strand numbering; hit
 // base hit_lo; n anchors), key-grouped, then the second stage as launch_gate_window_fused:
-// flags receives the chunk's flags (zeroed first, then 1 for the anchors kept), anchors
-// the anchor of every slot whose flag is not decided 0, and list1/list2 the deferred
-// slots.  prefix is the batch's inclusive prefix (batch_lo = its first seed).
+// flags receives the chunk's flags (zeroed first, then 1 for the anchors kept), list1/list2
+// the deferred slots, and list1_a (list1's capacity) the anchors of list1's slots, which
+// the second stage reads there instead of at their scattered slots.  anchors receives the
+// anchor of every slot whose flag is 1 and of every slot listed in list2 (what the exact
+// list and the materializer read).  prefix is the batch's inclusive prefix (batch_lo = its
+// first seed).
 hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const uint32_t *prefix, uint32_t batch_lo, uint32_t seed_lo,
                                  uint32_t seed_hi, uint32_t hit_lo, uint32_t n,
                                  const uint32_t *pos, uint64_t *anchors, uint8_t *flags,
                                  const uint32_t *ref4, const uint32_t *qry4,
-                                 const WindowParams &wp, uint32_t *list1, uint32_t *list2,
-                                 uint32_t *cnt, hipStream_t s);
+                                 const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
+                                 uint32_t *list2, uint32_t *cnt, hipStream_t s);
 // Bucketed gate ("D. Score gate", D.5): stable sort of anchors by reference slice
 // (k_bucket.hip) and the first window stage over the sorted anchors (k_gate.hip).
 uint32_t bucket_blocks(uint32_t n);  // workgroups of the slice histogram and scatter

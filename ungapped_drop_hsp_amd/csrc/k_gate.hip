@@ -237,6 +237,7 @@ constexpr int kWideRight = 6, kWideLeft = 9;
 constexpr int kNarrowRight = 4, kNarrowLeft = 7;
 constexpr int kStage2Right = 8, kStage2Left = 12;
 constexpr int kSeg = 512;   // LDS slots per wave for deferred anchor indices
+constexpr int kSegKg = 256;  // the same with anchors, in the key-grouped stage
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -405,41 +406,48 @@ __device__ __forceinline__ bool in_range(bool valid, uint64_t a, const WindowPar
     return valid && (uint32_t)a <= wp.n_ref && (uint32_t)(a >> 32) <= wp.n_qry;
 }
 
-// Deferred indices are gathered per wave in LDS and reserved in the global list once per
-// workgroup (a full wave segment is flushed on its own).
-struct DeferSeg {
-    uint32_t (*seg)[kSeg];
-    uint32_t *seg_n;
-    uint32_t *blk_base;
-};
-
-__device__ __forceinline__ void defer_push(uint32_t *seg, uint32_t &nseg, bool dfr, uint32_t i,
-                                           uint32_t *__restrict__ defer,
-                                           uint32_t *__restrict__ defer_cnt) {
+// Deferred indices are gathered per wave in LDS (S slots) and reserved in the global list
+// once per workgroup (a full wave segment is flushed on its own).  With P each index
+// carries its anchor into a parallel list (sega in LDS, defer_a in the global list).
+template <int S, bool P>
+__device__ __forceinline__ void defer_push_g(uint32_t *seg, uint64_t *sega, uint32_t &nseg,
+                                             bool dfr, uint32_t i, uint64_t a,
+                                             uint32_t *__restrict__ defer,
+                                             uint64_t *__restrict__ defer_a,
+                                             uint32_t *__restrict__ defer_cnt) {
     const int lane = lane_id();
     const uint64_t m = __ballot(dfr);
     if (!m) return;
     const uint32_t c = (uint32_t)__popcll(m);
-    if (nseg + c > (uint32_t)kSeg) {
+    if (nseg + c > (uint32_t)S) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(defer_cnt, nseg);
         base = __shfl(base, 0, 64);
-        for (uint32_t j = lane; j < nseg; j += 64) defer[base + j] = seg[j];
+        for (uint32_t j = lane; j < nseg; j += 64) {
+            defer[base + j] = seg[j];
+            if (P) defer_a[base + j] = sega[j];
+        }
         nseg = 0;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
-    if (dfr) seg[nseg + lane_rank(m)] = i;
+    if (dfr) {
+        const uint32_t k = nseg + lane_rank(m);
+        seg[k] = i;
+        if (P) sega[k] = a;
+    }
     nseg += c;
 }
 
 // All waves of the block call this once at the end.
-__device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_t *seg_n,
-                                                  uint32_t *blk_base, uint32_t nseg,
-                                                  uint32_t *__restrict__ defer,
-                                                  uint32_t *__restrict__ defer_cnt) {
+template <int S, bool P>
+__device__ __forceinline__ void defer_flush_block_g(uint32_t (*seg)[S], uint64_t (*sega)[S],
+                                                    uint32_t *seg_n, uint32_t *blk_base,
+                                                    uint32_t nseg, uint32_t *__restrict__ defer,
+                                                    uint64_t *__restrict__ defer_a,
+                                                    uint32_t *__restrict__ defer_cnt) {
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     if (lane == 0) seg_n[w] = nseg;
@@ -452,7 +460,24 @@ __device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_
     __syncthreads();
     uint32_t base = *blk_base;
     for (int v = 0; v < w; v++) base += seg_n[v];
-    for (uint32_t j = lane; j < nseg; j += 64) defer[base + j] = seg[w][j];
+    for (uint32_t j = lane; j < nseg; j += 64) {
+        defer[base + j] = seg[w][j];
+        if (P) defer_a[base + j] = sega[w][j];
+    }
+}
+
+__device__ __forceinline__ void defer_push(uint32_t *seg, uint32_t &nseg, bool dfr, uint32_t i,
+                                           uint32_t *__restrict__ defer,
+                                           uint32_t *__restrict__ defer_cnt) {
+    defer_push_g<kSeg, false>(seg, nullptr, nseg, dfr, i, 0, defer, nullptr, defer_cnt);
+}
+
+__device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_t *seg_n,
+                                                  uint32_t *blk_base, uint32_t nseg,
+                                                  uint32_t *__restrict__ defer,
+                                                  uint32_t *__restrict__ defer_cnt) {
+    defer_flush_block_g<kSeg, false>(seg, nullptr, seg_n, blk_base, nseg, defer, nullptr,
+                                     defer_cnt);
 }
 
 // First stage: every anchor, consecutive 64-anchor steps per wave.
@@ -713,9 +738,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     uint32_t hit_lo, uint32_t n, uint32_t steps, const uint32_t *__restrict__ pos,
     uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
-    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    uint32_t *__restrict__ defer, uint64_t *__restrict__ defer_a,
+    uint32_t *__restrict__ defer_cnt) {
     __shared__ int16_t tab[kWinTab];
-    __shared__ uint32_t seg[kWaves][kSeg];
+    __shared__ uint32_t seg[kWaves][kSegKg];
+    __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
     __shared__ uint32_t blk_base;
     __shared__ uint32_t rel[kWaves][64];  // inclusive prefix of the window's runs
@@ -794,12 +821,17 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
         uint32_t slot = 0;
         if (valid && res != 0) {
             slot = prefix[seed - batch_lo] - 1u - hit_lo - occ;
-            anchors[slot] = a;
-            if (res == 1) flags[slot] = 1;
+            if (res == 1) {
+                anchors[slot] = a;
+                flags[slot] = 1;
+            }
         }
-        defer_push(seg[w], nseg, valid && res == 2, slot, defer, defer_cnt);
+        // a deferred slot's anchor travels in the list; the next stage stores it if kept
+        defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, slot, a, defer,
+                                   defer_a, defer_cnt);
     }
-    defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
+    defer_flush_block_g<kSegKg, true>(seg, sega, seg_n, &blk_base, nseg, defer, defer_a,
+                                      defer_cnt);
 }
 
 // First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
@@ -853,7 +885,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_bucketed(
 // Later stage: the anchors listed by the previous stage (*count of them), wider windows.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_list(
-    const uint64_t *__restrict__ anchors, const uint32_t *__restrict__ list,
+    const uint64_t *anchors, const uint32_t *__restrict__ list,
+    const uint64_t *__restrict__ list_a, uint64_t *anchors_out,
     const uint32_t *__restrict__ count, uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
@@ -873,9 +906,10 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
         const uint64_t t = t0 + lane;
         const bool valid = t < total;
         uint32_t i = 0, r = 0, q = 0;
+        uint64_t a = 0;
         if (valid) {
             i = list[t];
-            const uint64_t a = anchors[i];
+            a = list_a ? list_a[t] : anchors[i];  // uniform choice
             r = (uint32_t)a;
             q = (uint32_t)(a >> 32);
         }
@@ -883,6 +917,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
         win.load(valid && r <= wp.n_ref && q <= wp.n_qry, r, q, ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[i] = (uint8_t)res;
+        // anchors that came in the list are stored where they are kept or go on
+        if (list_a && valid && res != 0) anchors_out[i] = a;
         defer_push(seg[w], nseg, valid && res == 2, i, defer, defer_cnt);
     }
     defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
@@ -938,15 +974,18 @@ hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
 }
 
 // The second stage strides over whatever the first left, up to all n anchors.
+// list1_a: the anchors of list1's entries, or NULL when they are read from anchors[];
+// with list1_a, the anchors the stage keeps or defers are stored into anchors_out.
 static void launch_stage2(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
                           const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
-                          uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
+                          uint32_t *list1, const uint64_t *list1_a, uint64_t *anchors_out,
+                          uint32_t *list2, uint32_t *cnt, hipStream_t s) {
     const uint32_t cap2 = narrow ? n : n / 8 + 1;
     const uint32_t blocks2 =
         (uint32_t)std::min<uint64_t>(((uint64_t)cap2 + kWaves * 64 - 1) / (kWaves * 64), 4096);
     hipLaunchKernelGGL((k_gate_window_list<kStage2Right, kStage2Left>), dim3(blocks2),
-                       dim3(kThreads), 0, s, anchors, list1, cnt, flags, ref4, qry4, wp, list2,
-                       cnt + 1);
+                       dim3(kThreads), 0, s, anchors, list1, list1_a, anchors_out, cnt, flags, ref4,
+                       qry4, wp, list2, cnt + 1);
 }
 
 hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
@@ -964,7 +1003,8 @@ hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, 
     else
         hipLaunchKernelGGL((k_gate_window<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads),
                            0, s, anchors, n, steps, flags, ref4, qry4, wp, list1, cnt);
-    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
+    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr, list2, cnt,
+                  s);
     return hipGetLastError();
 }
 
@@ -1000,7 +1040,8 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
         hipLaunchKernelGGL((k_gate_window_fused<kWideRight, kWideLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
                            list1, cnt);
-    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
+    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr, list2, cnt,
+                  s);
     return hipGetLastError();
 }
 
@@ -1009,8 +1050,8 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  uint32_t seed_hi, uint32_t hit_lo, uint32_t n,
                                  const uint32_t *pos, uint64_t *anchors, uint8_t *flags,
                                  const uint32_t *ref4, const uint32_t *qry4,
-                                 const WindowParams &wp, uint32_t *list1, uint32_t *list2,
-                                 uint32_t *cnt, hipStream_t s) {
+                                 const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
+                                 uint32_t *list2, uint32_t *cnt, hipStream_t s) {
     if (n == 0 || kg.n_runs == 0) {
         hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
@@ -1028,8 +1069,9 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
     const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
     hipLaunchKernelGGL((k_gate_window_kg<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads), 0,
                        s, kg, ks, prefix, batch_lo, hit_lo, n, steps, pos, anchors, flags, ref4,
-                       qry4, wp, list1, cnt);
-    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
+                       qry4, wp, list1, list1_a, cnt);
+    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors, list2, cnt,
+                  s);
     return hipGetLastError();
 }
 
@@ -1049,7 +1091,8 @@ hipError_t launch_gate_window_bucketed(const uint64_t *anchors, uint32_t n, cons
     hipLaunchKernelGGL((k_gate_window_bucketed<kWideRight, kWideLeft>), dim3(blocks),
                        dim3(kThreads), 0, s, sa, si, n, part, steps, flags, ref4, qry4, wp,
                        list1, cnt);
-    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, list2, cnt, s);
+    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr, list2, cnt,
+                  s);
     return hipGetLastError();
 }
 
