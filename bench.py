@@ -109,12 +109,12 @@ def gate_sources_sha() -> str:
     return h.hexdigest()
 
 
-def gate_traffic(workload: str, gate_mode: int):
-    """Measured fabric bytes per hspz_find_hits_gate call from the committed counter summary.
+def gate_traffic(workload: str, gate_mode: int, anchors_per_call: float):
+    """Measured fabric bytes per timed gate call from the committed counter summary.
 
     The summary was taken with rocprofv3 FETCH_SIZE / WRITE_SIZE runs and calibrated
-    against a plain device copy.  It applies only to the sources it was measured on and to
-    the same workload and gate mode; otherwise None.
+    against a plain device copy.  It applies only to the sources it was measured on, to
+    the same workload and gate mode, and to calls of the same size; otherwise None.
     """
     path = os.path.join(ROOT, "profiles", "find_hits_gate_traffic_c3_50Mb.json")
     try:
@@ -123,7 +123,8 @@ def gate_traffic(workload: str, gate_mode: int):
     except OSError:
         return None
     if (rec.get("gate_sources_sha256") != sha or not rec["workload"].startswith(workload)
-            or rec.get("gate_mode", 0) != gate_mode):
+            or rec.get("gate_mode", 0) != gate_mode
+            or abs(rec.get("anchors_per_call", 0) - anchors_per_call) > 1e-3 * anchors_per_call):
         return None
     return rec["hbm_bytes_per_call"]
 
@@ -280,7 +281,7 @@ def main():
     stages = StageTimer()
     wall = 0.0
     gate_ms_sum = 0.0
-    gate_calls = gate_anchors = 0
+    gate_calls = gate_anchors = whole_batches = 0
     anchors = surv = acc = chunks = seeds = 0
     chunk_list = []  # (strand, lo, hi) batches of the last step, for the walk statistics
     # Python's cyclic collector stays off over the passes: a collection inside the timed
@@ -308,6 +309,7 @@ def main():
                 gate_ms_sum += r["gate_ms"]
                 gate_calls += r["gate_calls"]
                 gate_anchors += r["n_anchors"]
+                whole_batches += r["whole_batch_gate"]
         torch.cuda.synchronize()
         wall += time.perf_counter() - t0
         for lo, hi in bs:
@@ -352,7 +354,7 @@ def main():
     steps_per_anchor = steps_total / max(walked, 1)
     gate_gsteps = steps_per_anchor * units_avg / (gate_ms_avg * 1e6)
 
-    traffic = gate_traffic(w.name, args.gate_mode)
+    traffic = gate_traffic(w.name, args.gate_mode, units_avg)
     # The gate's reference windows are 64-byte reads from the 4-bit reference copy and its
     # line-split twin (about one byte per reference base in all); the plan's lookups read
     # one 32-byte record of the packed count table per seed.
@@ -384,9 +386,12 @@ def main():
         roofline=dict(bound="alu", achieved=gate_gsteps, peak=ALU_PEAK_GSTEPS,
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
                       traffic=traffic,
-                      kernel="find_hits_gate (first window stage forming its own anchors, "
-                             "key-grouped when a chunk holds enough seeds; second stage; "
-                             "exact list)",
+                      kernel=("the gate over the whole batch at once (key-grouped first "
+                              "window stage forming its own anchors; second stage; exact list)"
+                              if whole_batches else
+                              "find_hits_gate per chunk (first window stage forming its own "
+                              "anchors, key-grouped when a chunk holds enough seeds; second "
+                              "stage; exact list)"),
                       launches_per_step=gate_launches // args.steps,
                       avg_launch_ms=gate_ms_avg, anchors_per_launch=units_avg,
                       base_steps_per_anchor=steps_per_anchor),

@@ -315,6 +315,7 @@ typedef struct {
     uint64_t n_accepted;   /* accepted records                                          */
     uint64_t gate_calls;   /* expansion-and-gate calls timed (time_gate != 0), else 0  */
     double gate_ms;        /* their summed durations from HIP events on the stream      */
+    uint64_t whole_batch_gate; /* 1: one gate call covered every chunk, else 0          */
 } hspz_batch_stats;
 
 /* The whole pass for query seeds [seed_lo, seed_hi) of the current strand, in one call:
@@ -326,11 +327,17 @@ typedef struct {
  * hspz_get_batch_records reads them.  Those copies run on a second stream that the
  * engine creates (default priority), ordered behind each chunk's records by events, so
  * that they overlap the next chunks' kernels; the call returns once every copy has
- * landed, also on error.  With time_gate != 0 each expansion-and-gate call
- * (hspz_find_hits_gate) is bracketed by HIP events on stream and *stats reports their
- * summed duration.  The plan stays current afterwards.  Synchronises stream.  Errors: as
- * hspz_plan, hspz_find_hits and the calls above; HSPZ_E_INVALID for a NULL stats
- * pointer. */
+ * landed, also on error.  Where the key-grouped first gate stage serves the whole batch
+ * (gate_mode 0 or 5, see hspz_params) and the batch has more than one chunk, at most
+ * 2^30 anchors and at least 2^22 per chunk on average, the gate runs once over every
+ * chunk's slots (the batch's flags and kept
+ * anchors in engine buffers of 9 bytes per anchor, its deferred lists sized for the
+ * batch) and the chunks are then compacted, materialized and copied one by one from their
+ * slices; the records are the same (stats->whole_batch_gate = 1).  The chunk cut still
+ * bounds every other buffer.  With time_gate != 0 each expansion-and-gate call is
+ * bracketed by HIP events on stream and *stats reports their number and summed duration.
+ * The plan stays current afterwards.  Synchronises stream.  Errors: as hspz_plan,
+ * hspz_find_hits and the calls above; HSPZ_E_INVALID for a NULL stats pointer. */
 int hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, int32_t time_gate,
                    hspz_batch_stats *stats, void *stream);
 

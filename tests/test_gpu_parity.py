@@ -470,10 +470,53 @@ def test_run_batch_matches_the_oracle(case, mat, gate_mode):
         want, acc = _oracle_batch(o)
         st = eng.run_batch(lo, hi, time_gate=True)
         assert {k: st[k] for k in want} == want
-        assert st["gate_calls"] == st["n_chunks"]
+        # one gate call over every chunk where the key-grouped stage serves a batch of
+        # large chunks, else one per chunk (these chunks are small)
+        assert st["whole_batch_gate"] == 0
+        assert st["gate_calls"] == (1 if st["whole_batch_gate"] else st["n_chunks"])
         assert (st["gate_ms"] > 0) == (st["n_chunks"] > 0)
         got = eng.batch_records()
         assert np.array_equal(got.view(np.uint8), acc.astype(oracle.HSP_DTYPE).view(np.uint8))
+
+
+@pytest.mark.timeout(600)
+def test_whole_batch_gate_matches_the_oracle():
+    # hspz_run_batch gates a batch of large chunks (2^22 anchors or more on average) in one
+    # key-grouped call over every chunk's slots, then compacts and materializes each chunk
+    # from its slice.  A 1 Mb x 1 Mb pair with an 8-of-11 seed (about 1.5e7 anchors) cut
+    # into two and into three chunks, in gate modes 0 and 5, and a sub-batch of small
+    # chunks (one call per chunk), against the oracle's pass.
+    ref, qry = random_pair(23, 1_000_000, 1_000_000, n_frac=0.01, plant=60,
+                           plant_len=(200, 3000), identity=0.9, gc=0.45)
+    pat = "11011011011"
+    for mx in (1 << 23, 6_000_000):
+        p = params_of(pat, max_hits=mx)
+        o, _, _ = oracle_pass(ref, qry, p)
+        want, acc = _oracle_batch(o)
+        assert want["n_chunks"] in (2, 3) and want["n_anchors"] >= (1 << 22) * want["n_chunks"]
+        for gm in (0, 5):
+            eng = engine(p, gate_mode=gm)
+            eng.upload_reference(ref)
+            eng.upload_query(qry)
+            st = eng.run_batch(0, eng.num_seeds(), time_gate=True)
+            assert {k: st[k] for k in want} == want, (mx, gm)
+            assert st["whole_batch_gate"] == 1 and st["gate_calls"] == 1
+            assert np.array_equal(eng.batch_records().view(np.uint8),
+                                  acc.astype(oracle.HSP_DTYPE).view(np.uint8)), (mx, gm)
+            print(f"max_hits {mx} gate_mode {gm}: {want}", flush=True)
+    # a sub-batch whose chunks average under 2^22 anchors: one gate call per chunk
+    p = params_of(pat, max_hits=1 << 21)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry)
+    lo, hi = 0, eng.num_seeds() // 4
+    o, _, _ = oracle_pass(ref, qry, p, seed_range=(lo, hi))
+    want, acc = _oracle_batch(o)
+    st = eng.run_batch(lo, hi, time_gate=True)
+    assert {k: st[k] for k in want} == want and want["n_chunks"] > 1
+    assert st["whole_batch_gate"] == 0 and st["gate_calls"] == st["n_chunks"]
+    assert np.array_equal(eng.batch_records().view(np.uint8),
+                          acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 
 
 @pytest.mark.parametrize("mat", [0, 2], ids=["default-walks", "shared-walks"])
@@ -518,7 +561,7 @@ def test_run_batch_survivors_grow_mid_batch(mat):
     for _ in range(2):
         st = eng.run_batch(0, eng.num_seeds(), time_gate=True)
         assert {k: st[k] for k in want} == want
-        assert st["gate_calls"] == st["n_chunks"]
+        assert st["gate_calls"] == (1 if st["whole_batch_gate"] else st["n_chunks"])
         assert np.array_equal(eng.batch_records().view(np.uint8),
                               acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 

@@ -62,7 +62,8 @@ class Chunk(ctypes.Structure):
 class BatchStats(ctypes.Structure):
     _fields_ = [("n_anchors", ctypes.c_uint64), ("n_chunks", ctypes.c_uint64),
                 ("n_survivors", ctypes.c_uint64), ("n_accepted", ctypes.c_uint64),
-                ("gate_calls", ctypes.c_uint64), ("gate_ms", ctypes.c_double)]
+                ("gate_calls", ctypes.c_uint64), ("gate_ms", ctypes.c_double),
+                ("whole_batch_gate", ctypes.c_uint64)]
 
 
 def _load() -> ctypes.CDLL:

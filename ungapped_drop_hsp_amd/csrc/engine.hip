@@ -427,6 +427,8 @@ Engine::~Engine() {
     dfree(d_qry4);
     dfree(d_defer);
     dfree(d_defer_a);
+    dfree(bb_flags);
+    dfree(bb_anchors);
     dfree(d_defer_cnt);
     dfree(d_kmer);
     dfree(d_qend);
@@ -1122,6 +1124,54 @@ static int impl_hspz_score_gate_noalloc(hspz_engine *engine, const uint64_t *d_a
     return HSPZ_OK;
 }
 
+// The deferred-anchor list beside the first stage's list of deferred slots (both first
+// stages of hspz_find_hits_gate pass their deferred anchors to the second stage in it).
+static int ensure_defer_anchors(Engine *e) {
+    if (e->cap_defer_a >= e->cap_defer && e->d_defer_a) return HSPZ_OK;
+    int rc = dalloc(e, e->d_defer_a, e->cap_defer);
+    if (rc) {
+        e->cap_defer_a = 0;
+        return rc;
+    }
+    e->cap_defer_a = e->cap_defer;
+    return HSPZ_OK;
+}
+
+// Whether the key-grouped first stage serves a range of n_seeds seeds of the batch: it
+// pays a pass over every k-mer run of the strand, so gate_mode 0 takes it when the range
+// holds at least half as many seeds as there are runs, i.e. when same-k-mer seeds of the
+// range share bucket windows; gate_mode 5 always (with the window gate's preconditions).
+static bool key_grouped_suits(const Engine *e, uint64_t n_seeds) {
+    return e->kg_ready && (e->params.gate_mode == 5 || 2 * n_seeds >= e->kg_n_runs);
+}
+
+// The window gate over seeds seed_lo .. seed_hi of the planned batch, whose n anchors are
+// the batch's slots hit_lo .. hit_lo + n - 1, with the key-grouped first stage: flags
+// receives their n flags, anchors (indexed from hit_lo) the anchor of every slot whose
+// flag is 1.  A chunk of the plan, or the whole batch (hspz_run_batch).
+static int gate_key_grouped(Engine *e, uint64_t seed_lo, uint64_t seed_hi, uint64_t hit_lo,
+                            uint64_t n, uint64_t *d_anchors, uint8_t *d_flags, hipStream_t s) {
+    int rc;
+    if ((rc = ensure_defer(e, n)) || (rc = ensure_defer_anchors(e)) ||
+        (rc = ensure_kg(e, gate_window_waves(n))))
+        return rc;
+    uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
+    KeyGroups g{e->d_kg_qs,        e->d_kg_qe,        e->d_kg_runs,
+                e->d_kg_run_c,     e->d_kg_run_first, e->d_kg_run_span,
+                e->kg_n_runs,      (uint32_t)e->n_seeds};
+    KgScratch ks{e->d_kg_G, e->d_kg_a, e->d_kg_m, e->d_kg_dir, e->d_kg_blksum,
+                 e->d_kg_blkoff, e->d_kg_info};
+    HIP_TRY(e, launch_gate_window_kg(g, ks, e->d_prefix, (uint32_t)e->batch_lo,
+                                     (uint32_t)seed_lo, (uint32_t)seed_hi, (uint32_t)hit_lo,
+                                     (uint32_t)n, e->d_pos, d_anchors, d_flags, e->d_ref4,
+                                     e->d_qry4, e->wp, list1, e->d_defer_a, list2,
+                                     e->d_defer_cnt, s));
+    HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
+                                     e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
+    e->gate_deferred_valid = true;
+    return HSPZ_OK;
+}
+
 static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_t *d_anchors,
                                     uint64_t cap, uint8_t *d_flags, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
@@ -1144,38 +1194,10 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     hipStream_t s = as_stream(stream);
     e->gate_deferred_valid = false;
     const uint64_t n = c.n_hits;
-    if ((rc = ensure_defer(e, n))) return rc;
+    if (n > 0 && key_grouped_suits(e, c.seed_hi - c.seed_lo + 1))
+        return gate_key_grouped(e, c.seed_lo, c.seed_hi, c.hit_lo, n, d_anchors, d_flags, s);
+    if ((rc = ensure_defer(e, n)) || (rc = ensure_defer_anchors(e))) return rc;
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
-    // The key-grouped first stage pays a pass over every k-mer run of the strand per
-    // chunk; it is taken (gate_mode 0) when the chunk holds at least half as many seeds
-    // as there are runs, i.e. when same-k-mer seeds of the chunk share bucket windows.
-    const uint64_t chunk_seeds = c.seed_hi - c.seed_lo + 1;
-    const bool kg = e->kg_ready && n > 0 &&
-                    (e->params.gate_mode == 5 || 2 * chunk_seeds >= e->kg_n_runs);
-    if (kg) {
-        if ((rc = ensure_kg(e, gate_window_waves(n)))) return rc;
-        if (e->cap_defer_a < e->cap_defer || !e->d_defer_a) {
-            if ((rc = dalloc(e, e->d_defer_a, e->cap_defer))) {
-                e->cap_defer_a = 0;
-                return rc;
-            }
-            e->cap_defer_a = e->cap_defer;
-        }
-        KeyGroups g{e->d_kg_qs,        e->d_kg_qe,        e->d_kg_runs,
-                    e->d_kg_run_c,     e->d_kg_run_first, e->d_kg_run_span,
-                    e->kg_n_runs,      (uint32_t)e->n_seeds};
-        KgScratch ks{e->d_kg_G, e->d_kg_a, e->d_kg_m, e->d_kg_dir, e->d_kg_blksum,
-                     e->d_kg_blkoff, e->d_kg_info};
-        HIP_TRY(e, launch_gate_window_kg(g, ks, e->d_prefix, (uint32_t)e->batch_lo,
-                                         (uint32_t)c.seed_lo, (uint32_t)c.seed_hi,
-                                         (uint32_t)c.hit_lo, (uint32_t)n, e->d_pos, d_anchors,
-                                         d_flags, e->d_ref4, e->d_qry4, e->wp, list1,
-                                         e->d_defer_a, list2, e->d_defer_cnt, s));
-        HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n,
-                                         d_flags, e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
-        e->gate_deferred_valid = true;
-        return HSPZ_OK;
-    }
     if ((rc = ensure_dir(e, n))) return rc;
     const uint64_t local = c.seed_lo - e->batch_lo;
     ChunkSeeds cs;
@@ -1187,8 +1209,8 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     cs.n_seeds = (uint32_t)(c.seed_hi - c.seed_lo + 1);
     cs.hit_lo = (uint32_t)c.hit_lo;
     HIP_TRY(e, launch_gate_window_fused(e->params.gate_mode == 3, cs, (uint32_t)n, d_anchors,
-                                        d_flags, e->d_ref4, e->d_qry4, e->wp, list1, list2,
-                                        e->d_defer_cnt, s));
+                                        d_flags, e->d_ref4, e->d_qry4, e->wp, list1,
+                                        e->d_defer_a, list2, e->d_defer_cnt, s));
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
@@ -1416,6 +1438,18 @@ static int ensure_run_buffers(Engine *e, uint64_t n, uint64_t ns) {
     return HSPZ_OK;
 }
 
+// The whole-batch gate's buffers for n anchors.
+static int ensure_batch_buffers(Engine *e, uint64_t n) {
+    if (n <= e->bb_cap && e->bb_flags) return HSPZ_OK;
+    int rc;
+    if ((rc = dalloc(e, e->bb_flags, n + 16)) || (rc = dalloc(e, e->bb_anchors, n))) {
+        e->bb_cap = 0;
+        return rc;
+    }
+    e->bb_cap = n;
+    return HSPZ_OK;
+}
+
 // Room for n records in the pinned staging; the first keep records are carried over.
 static int ensure_record_staging(Engine *e, uint64_t n, uint64_t keep, hipStream_t s) {
     if (n <= e->h_rec_cap && e->h_rec) return HSPZ_OK;
@@ -1464,6 +1498,9 @@ static int count_wait(Engine *e, int slot, uint64_t cap, uint64_t *n_out) {
     return HSPZ_OK;
 }
 
+constexpr uint64_t kWholeBatchMax = 1ull << 30;  // anchors of a whole-batch gate call
+constexpr uint64_t kWholeChunkMin = 1ull << 22;  // and the least anchors per chunk
+
 static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi,
                                int32_t time_gate, hspz_batch_stats *stats, void *stream) {
     Engine *e = reinterpret_cast<Engine *>(engine);
@@ -1502,6 +1539,27 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
         for (hipEvent_t &ev : e->gate_ev)
             if (!ev) HIP_TRY(e, hipEventCreate(&ev));
 
+    // The whole-batch gate: where the key-grouped stage serves the batch, one gate call
+    // covers the slots of every chunk at once (the batch's flags and kept anchors in one
+    // buffer each; the chunk cut bounds memory on small GPUs, and up to 2^30 anchors fit
+    // here), so a k-mer's seeds in every chunk share their reference windows and the
+    // stage runs once.  Compaction, materialization and the records then go chunk by
+    // chunk, from each chunk's slice, exactly as below.  Batches of small chunks (under
+    // 2^22 anchors on average) keep one gate call per chunk: there each chunk's gate,
+    // queued ahead, covers the host's wait for the previous chunk's counts.
+    const bool whole = nch > 1 && total <= kWholeBatchMax && total / nch >= kWholeChunkMin &&
+                       key_grouped_suits(e, e->batch_n);
+    stats->whole_batch_gate = whole ? 1 : 0;
+    if (whole) {
+        if ((rc = ensure_batch_buffers(e, total))) return rc;
+        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
+        if ((rc = set_device(e)) ||
+            (rc = gate_key_grouped(e, e->batch_lo, e->batch_lo + e->batch_n - 1, 0, total,
+                                   e->bb_anchors, e->bb_flags, s)))
+            return rc;
+        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[1], s));
+    }
+
     // One stream, queued one chunk ahead: chunk c + 1's expansion+gate and survivor
     // compaction are queued before the host waits on chunk c's counts, so the GPU has work
     // while the host reads them.  Chunk c uses buffer set c & 1; stream order keeps every
@@ -1509,6 +1567,7 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
     // host on copy_s, behind its record count, while the next chunks run; the compaction
     // of chunk c + 2 into the same record buffer waits for that copy.
     auto gate = [&](uint32_t c) -> int {
+        if (whole) return HSPZ_OK;
         const int b = c & 1;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[2 * b], s));
         int r = hspz_find_hits_gate(engine, c, e->rb_anchors[b], e->rb_cap_a, e->rb_flags[b],
@@ -1519,8 +1578,17 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
     };
     auto survivors = [&](uint32_t c) -> int {
         const int b = c & 1;
-        return count_queue(e, e->rb_flags[b], e->chunks[c].n_hits, e->rb_ids[b], nullptr,
-                           nullptr, e->rb_cap_a, 0, s);
+        const uint8_t *f = e->rb_flags[b];
+        if (whole) {  // the chunk's slice; compaction reads 16-byte aligned flags fastest
+            f = e->bb_flags + e->chunks[c].hit_lo;
+            if (reinterpret_cast<uintptr_t>(f) & 15) {
+                HIP_TRY(e, hipMemcpyAsync(e->rb_flags[b], f, e->chunks[c].n_hits,
+                                          hipMemcpyDeviceToDevice, s));
+                f = e->rb_flags[b];
+            }
+        }
+        return count_queue(e, f, e->chunks[c].n_hits, e->rb_ids[b], nullptr, nullptr,
+                           e->rb_cap_a, 0, s);
     };
     if (nch && ((rc = gate(0)) || (rc = survivors(0)))) return rc;
     uint64_t acc = 0;
@@ -1529,9 +1597,10 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
         if (c + 1 < nch && (rc = gate(c + 1))) return rc;
         uint64_t ns = 0, na = 0;
         if ((rc = count_wait(e, 0, e->rb_cap_a, &ns))) return rc;
-        if (time_gate) {  // the survivor count lands after the chunk's gate events
+        if (time_gate && (!whole || c == 0)) {  // the count lands after the gate events
             float ms = 0.f;
-            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[2 * b], e->gate_ev[2 * b + 1]));
+            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[whole ? 0 : 2 * b],
+                                           e->gate_ev[whole ? 1 : 2 * b + 1]));
             stats->gate_ms += ms;
             stats->gate_calls++;
         }
@@ -1542,8 +1611,9 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
             if ((rc = ensure_run_buffers(e, maxn, ns))) return rc;
         }
         // the chunk's own survivors, in slot order: query ends never decrease
-        if ((rc = materialize(e, e->rb_anchors[b], e->rb_ids[b], ns, e->rb_hsp, e->rb_status,
-                              true, stream)))
+        const uint64_t *anch = whole ? e->bb_anchors + e->chunks[c].hit_lo : e->rb_anchors[b];
+        if ((rc = materialize(e, anch, e->rb_ids[b], ns, e->rb_hsp, e->rb_status, true,
+                              stream)))
             return rc;
         if (e->copy_pending[b]) {  // chunk c - 2's records are still being read out of it
             HIP_TRY(e, hipStreamWaitEvent(s, e->copied_ev[b], 0));

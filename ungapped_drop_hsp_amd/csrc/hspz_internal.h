@@ -166,14 +166,15 @@ uint32_t gate_window_steps(uint64_t n);
 uint64_t gate_window_waves(uint64_t n);
 // As launch_gate_window, but the first stage builds each anchor from the chunk's seeds
 // (occurrence j of seed s at slot prefix[s] - 1 - hit_lo - j, "C. Hit discovery", C.5)
-// instead of reading it: anchors[i] is written only where the first stage does not
-// decide flag 0 (the later stages and the materializer read exactly those).
-// cs.dir holds gate_window_waves(n) entries.
+// instead of reading it.  A deferred slot's anchor goes into list1_a (list1's capacity)
+// beside its index in list1, and the second stage reads it there; anchors[i] receives the
+// anchor of every slot whose flag is 1 and of every slot listed in list2 (what the exact
+// list and the materializer read).  cs.dir holds gate_window_waves(n) entries.
 hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t n,
                                     uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
                                     const uint32_t *qry4, const WindowParams &wp,
-                                    uint32_t *list1, uint32_t *list2, uint32_t *cnt,
-                                    hipStream_t s);
+                                    uint32_t *list1, uint64_t *list1_a, uint32_t *list2,
+                                    uint32_t *cnt, hipStream_t s);
 // Key-grouped first stage (gate_mode 5, and gate_mode 0 for chunks holding a large share
 // of the strand's seeds).  The query strand's seeds are kept grouped by k-mer (built when
 // the query is uploaded): qs lists the seed indices ordered by k-mer and, within a k-mer,

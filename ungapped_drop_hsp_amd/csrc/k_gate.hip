@@ -548,9 +548,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     ChunkSeeds cs, uint32_t n, uint32_t steps, uint64_t *__restrict__ anchors,
     uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
-    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    uint32_t *__restrict__ defer, uint64_t *__restrict__ defer_a,
+    uint32_t *__restrict__ defer_cnt) {
     __shared__ int16_t tab[kWinTab];
-    __shared__ uint32_t seg[kWaves][kSeg];
+    __shared__ uint32_t seg[kWaves][kSegKg];
+    __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
     __shared__ uint32_t blk_base;
     __shared__ uint32_t rel[kWaves][64];  // prefix - hit_lo of the window's seeds
@@ -611,10 +613,13 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 2) flags[t] = (uint8_t)res;
-        if (valid && res != 0) anchors[t] = a;
-        defer_push(seg[w], nseg, valid && res == 2, t, defer, defer_cnt);
+        if (valid && res == 1) anchors[t] = a;
+        // a deferred slot's anchor travels in the list; the next stage stores it if kept
+        defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, t, a, defer,
+                                   defer_a, defer_cnt);
     }
-    defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
+    defer_flush_block_g<kSegKg, true>(seg, sega, seg_n, &blk_base, nseg, defer, defer_a,
+                                      defer_cnt);
 }
 
 // ------------------------------------------------------------------ key-grouped first stage
@@ -1021,8 +1026,8 @@ uint64_t gate_window_waves(uint64_t n) {
 hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t n,
                                     uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
                                     const uint32_t *qry4, const WindowParams &wp,
-                                    uint32_t *list1, uint32_t *list2, uint32_t *cnt,
-                                    hipStream_t s) {
+                                    uint32_t *list1, uint64_t *list1_a, uint32_t *list2,
+                                    uint32_t *cnt, hipStream_t s) {
     if (n == 0) {
         hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
@@ -1035,12 +1040,12 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
     if (narrow)
         hipLaunchKernelGGL((k_gate_window_fused<kNarrowRight, kNarrowLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, cnt);
+                           list1, list1_a, cnt);
     else
         hipLaunchKernelGGL((k_gate_window_fused<kWideRight, kWideLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, cnt);
-    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr, list2, cnt,
+                           list1, list1_a, cnt);
+    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors, list2, cnt,
                   s);
     return hipGetLastError();
 }
