@@ -180,10 +180,11 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
 // the query is uploaded): qs lists the seed indices ordered by k-mer and, within a k-mer,
 // ascending; qe their query ends; runs the start in qs of each k-mer's run; run_c and
 // run_first the k-mer's reference bucket (size and start), set once a reference is there.
-// A chunk's anchors are then enumerated run by run: the chunk's seeds of a k-mer (a
-// contiguous stretch of its run) times the k-mer's bucket, so the reference window of
-// each bucket entry and the query window of each seed are read once per group instead
-// of once per anchor.  Every anchor still gets its own flag at its raw slot.
+// A range's anchors (a chunk, or a whole batch) are then enumerated run by run: the
+// range's seeds of a k-mer (a contiguous stretch of its run) times the k-mer's bucket, so
+// the reference window of each bucket entry and the query window of each seed are read
+// once per group instead of once per anchor.  Every anchor still gets its own flag at its
+// raw slot.
 struct KeyGroups {
     const uint32_t *qs;
     const uint32_t *qe;
@@ -194,12 +195,12 @@ struct KeyGroups {
     uint32_t n_runs;
     uint32_t n_qs;
 };
-// Per-chunk scratch of the key-grouped stage, n_runs entries each (dir: one per wave).
+// Per-call scratch of the key-grouped stage, n_runs entries each (dir: one per wave).
 struct KgScratch {
-    uint32_t *G;       // inclusive prefix of the runs' anchors in this chunk, within each
-                       // kScanBlock runs (plus blkoff[r / kScanBlock] for the chunk's)
-    uint32_t *a;       // index in qs of the run's first seed in the chunk
-    uint32_t *m;       // the run's seeds in the chunk
+    uint32_t *G;       // inclusive prefix of the runs' anchors in the range, within each
+                       // kScanBlock runs (plus blkoff[r / kScanBlock] for the range's)
+    uint32_t *a;       // index in qs of the run's first seed in the range
+    uint32_t *m;       // the run's seeds in the range
     uint32_t *dir;     // per wave: the run owning the wave's first slot
     uint64_t *blksum;  // per kScanBlock runs: their anchors
     uint32_t *blkoff;  // and the exclusive prefix of those
@@ -216,9 +217,10 @@ hipError_t launch_kg_run_info(const uint32_t *qk, const uint32_t *runs, uint32_t
                               hipStream_t s);
 hipError_t launch_kg_run_span(const uint32_t *qs, uint32_t n, const uint32_t *runs,
                               uint32_t n_runs, uint4 *run_span, hipStream_t s);
-// The first window stage of one chunk (seeds seed_lo .. seed_hi, strand numbering; hit
-// base hit_lo; n anchors), key-grouped, then the second stage as launch_gate_window_fused:
-// flags receives the chunk's flags (zeroed first, then 1 for the anchors kept), list1/list2
+// The first window stage of a range of the batch's seeds (seed_lo .. seed_hi, strand
+// numbering; its first slot hit_lo; n anchors: a chunk, or the whole batch with hit_lo
+// 0), key-grouped, then the second stage as launch_gate_window_fused: flags receives the
+// range's flags (zeroed first, then 1 for the anchors kept), list1/list2
 // the deferred slots, and list1_a (list1's capacity) the anchors of list1's slots, which
 // the second stage reads there instead of at their scattered slots.  anchors receives the
 // anchor of every slot whose flag is 1 and of every slot listed in list2 (what the exact

@@ -5,7 +5,9 @@
 // drawdown is held as its complement g = INT32_MAX - d: then d' = max(d - sigma, 0) is
 // the signed saturating add g' = sat(g + sigma) (the clamp at INT32_MAX is the clamp of
 // d at 0), one instruction per base, and the running maximum of d is the running
-// minimum of g.  d never exceeds xdrop + B * (xdrop + 1), far from the lower limit.  A drop
+// minimum of g.  The score is carried plus INT32_MAX (mod 2^32), so the best so far,
+// score + d, is one subtraction of g.  d never exceeds xdrop + B * (xdrop + 1), far from
+// the lower limit.  A drop
 // inside a block shows as max(d) > xdrop at the block's end.  B satisfies
 // (B - 1) * max(sigma) <= xdrop, so after a drop the score cannot climb back above the
 // best inside the same block: best = score + d at the block's end is exactly the
@@ -14,8 +16,9 @@
 //
 // Two paths decide the same flag:
 //
-//  window (k_gate_window): one lane per anchor, 64 anchors of consecutive raw ids per
-//    wave step.  Each lane loads a window of both sequences around its anchor once
+//  window (k_gate_window): one lane per anchor, 64 anchors per wave step (consecutive
+//    raw ids; in the key-grouped stage, consecutive positions of k-mer runs).  Each lane
+//    loads a window of both sequences around its anchor once
 //    (4-bit codes, 16-byte loads, kept in registers): by default 72 bases before the
 //    anchor and 48 from it.  The right walk then scores up to six blocks of eight bases
 //    and the left walk up to nine, all lanes in step, so every block's window word has a
@@ -23,13 +26,13 @@
 //    table indexed by (ref code << 4) | query code, formed for four bases at once with
 //    byte-wise bit selects.  A lane stops at its walk's first drop, or once R* (right)
 //    or R* + best so far (left) reaches T, when the flag is 1 whatever follows.  Where
-//    survivors are rare the reach test decides almost nothing in the first stage, which
-//    is bound by its random reference lines, so it costs no time there; where most
-//    anchors survive (tandem repeats) it decides them inside the first window instead of
+//    survivors are rare the reach test decides almost nothing; where most anchors
+//    survive (tandem repeats) it decides them inside the first window instead of
 //    sending nearly all of them on to the later stages.  Walks still running at the
-//    window's end are appended to a deferred list:
-//    each wave collects them in LDS and the workgroup reserves its share of the global
-//    list with one atomic.
+//    window's end are appended to a deferred list: each wave collects them in LDS and
+//    the workgroup reserves its share of the global list with one atomic.  The stages
+//    that form their own anchors put each deferred anchor in a second list beside its
+//    slot, which the next stage reads in order.
 //
 //  exact, all anchors (k_gate): one lane per anchor walking base blocks straight from
 //    the byte-per-base sequences, refilling finished lanes from the wave's tile of
@@ -624,9 +627,9 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
 
 // ------------------------------------------------------------------ key-grouped first stage
 //
-// The chunk's anchors in another order: run by run of the strand's seeds grouped by
-// k-mer, the chunk's seeds of the k-mer (m of them, a contiguous stretch of the run)
-// times the k-mer's bucket (c reference ends).  Within a run the anchors go bucket entry
+// A range of seeds' anchors (one chunk, or a whole batch of chunks) in another order: run
+// by run of the strand's seeds grouped by k-mer, the range's seeds of the k-mer (m of
+// them, a contiguous stretch of the run) times the k-mer's bucket (c reference ends).  Within a run the anchors go bucket entry
 // by bucket entry, the m seeds of each entry next to each other, so the lanes of a wave
 // that share a bucket entry read the same reference window and the lanes that share a
 // seed the same query window: a run's c + m windows serve its c * m anchors.  Flags are
@@ -655,7 +658,7 @@ __device__ __forceinline__ uint32_t kg_lower(const uint32_t *__restrict__ qs, ui
     return lo;
 }
 
-// Per run: the chunk's seeds of its k-mer (index of the first in qs, and how many) and
+// Per run: the range's seeds of its k-mer (index of the first in qs, and how many) and
 // the anchors they make with the k-mer's bucket; then the inclusive prefix of those
 // anchor counts within each workgroup's kScanBlock runs (one run per thread, so that
 // the runs' searches overlap), and each workgroup's total (the offsets of the
@@ -673,9 +676,9 @@ __global__ __launch_bounds__(kKgThreads) void k_kg_groups(KeyGroups kg, uint32_t
         const uint32_t A = sp.x, B = sp.y;
         uint32_t a = 0, b = 0;
         if (c == 0 || sp.w < seed_lo || sp.z > seed_hi) {
-            // no anchors, or no seed of the chunk: nothing to search
+            // no anchors, or no seed in the range: nothing to search
         } else if (sp.z >= seed_lo && sp.w <= seed_hi) {
-            a = A;  // the whole run lies in the chunk
+            a = A;  // the whole run lies in the range
             b = B;
         } else if (B - A <= 8) {
             // both bounds from one round of loads (a run is never empty)
@@ -695,7 +698,7 @@ __global__ __launch_bounds__(kKgThreads) void k_kg_groups(KeyGroups kg, uint32_t
         }
         ks.a[r] = a;
         ks.m[r] = b - a;
-        // at most the chunk's hits, which fit 32 bits
+        // at most the range's hits, which fit 32 bits
         cnt = (uint32_t)((uint64_t)c * (b - a));
     }
     const uint64_t incl = wave_incl_sum_u64(cnt);
@@ -707,7 +710,7 @@ __global__ __launch_bounds__(kKgThreads) void k_kg_groups(KeyGroups kg, uint32_t
     if (t == kKgThreads - 1) ks.blksum[blockIdx.x] = run;
 }
 
-// Inclusive prefix of run r's anchors over the chunk: its workgroup's offset plus the
+// Inclusive prefix of run r's anchors over the range: its workgroup's offset plus the
 // workgroup-local prefix.
 __device__ __forceinline__ uint32_t kg_prefix(const KgScratch &ks, uint32_t r) {
     return ks.G[r] + ks.blkoff[r / kScanBlock];
@@ -754,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     __shared__ uint32_t rs_[kWaves][64];  // exclusive prefix (rel minus c * m)
     __shared__ uint32_t rf[kWaves][64];   // bucket starts
     __shared__ uint32_t ra[kWaves][64];   // first seed in qs
-    __shared__ uint32_t rm[kWaves][64];   // seeds in the chunk
+    __shared__ uint32_t rm[kWaves][64];   // seeds in the range
     __shared__ float rq[kWaves][64];      // 1 / m (hardware reciprocal)
     if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
     __syncthreads();
