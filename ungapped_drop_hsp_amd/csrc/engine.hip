@@ -1547,11 +1547,27 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
     // chunk, from each chunk's slice, exactly as below.  Batches of small chunks (under
     // 2^22 anchors on average) keep one gate call per chunk: there each chunk's gate,
     // queued ahead, covers the host's wait for the previous chunk's counts.
-    const bool whole = nch > 1 && total <= kWholeBatchMax && total / nch >= kWholeChunkMin &&
-                       key_grouped_suits(e, e->batch_n);
+    bool whole = nch > 1 && total <= kWholeBatchMax && total / nch >= kWholeChunkMin &&
+                 key_grouped_suits(e, e->batch_n);
+    if (whole) {
+        // its buffers (flags, kept anchors, both deferred lists) are sized for the batch;
+        // where the device cannot hold them the batch is gated chunk by chunk after all
+        if ((rc = ensure_batch_buffers(e, total)) || (rc = ensure_defer(e, total)) ||
+            (rc = ensure_defer_anchors(e)) || (rc = ensure_kg(e, gate_window_waves(total)))) {
+            if (rc != HSPZ_E_NOMEM) return rc;
+            (void)hipGetLastError();  // the failed allocation's error is not the next call's
+            e->err.clear();
+            dfree(e->bb_flags);
+            dfree(e->bb_anchors);
+            dfree(e->d_defer);
+            dfree(e->d_defer_a);
+            e->bb_cap = e->cap_defer = e->cap_defer_a = 0;
+            if ((rc = ensure_defer(e, maxn)) || (rc = ensure_defer_anchors(e))) return rc;
+            whole = false;
+        }
+    }
     stats->whole_batch_gate = whole ? 1 : 0;
     if (whole) {
-        if ((rc = ensure_batch_buffers(e, total))) return rc;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
         if ((rc = set_device(e)) ||
             (rc = gate_key_grouped(e, e->batch_lo, e->batch_lo + e->batch_n - 1, 0, total,
