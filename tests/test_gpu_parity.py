@@ -483,9 +483,9 @@ def test_run_batch_matches_the_oracle(case, mat, gate_mode):
 def test_whole_batch_gate_matches_the_oracle():
     # hspz_run_batch gates a batch of large chunks (2^22 anchors or more on average) in one
     # key-grouped call over every chunk's slots, then compacts and materializes each chunk
-    # from its slice.  A 1 Mb x 1 Mb pair with an 8-of-11 seed (about 1.5e7 anchors) cut
-    # into two and into three chunks, in gate modes 0 and 5, and a sub-batch of small
-    # chunks (one call per chunk), against the oracle's pass.
+    # from its slice.  A 1 Mb x 1 Mb pair with an 8-of-11 seed (about 1.6e7 anchors) cut
+    # into two and into three chunks, in gate modes 0 and 5 and with the shared walks, and
+    # a sub-batch of small chunks (one call per chunk), against the oracle's pass.
     ref, qry = random_pair(23, 1_000_000, 1_000_000, n_frac=0.01, plant=60,
                            plant_len=(200, 3000), identity=0.9, gc=0.45)
     pat = "11011011011"
@@ -494,16 +494,16 @@ def test_whole_batch_gate_matches_the_oracle():
         o, _, _ = oracle_pass(ref, qry, p)
         want, acc = _oracle_batch(o)
         assert want["n_chunks"] in (2, 3) and want["n_anchors"] >= (1 << 22) * want["n_chunks"]
-        for gm in (0, 5):
-            eng = engine(p, gate_mode=gm)
+        for gm, mat in ((0, 0), (5, 0), (0, 2)):
+            eng = engine(p, gate_mode=gm, materialize_mode=mat)
             eng.upload_reference(ref)
             eng.upload_query(qry)
             st = eng.run_batch(0, eng.num_seeds(), time_gate=True)
-            assert {k: st[k] for k in want} == want, (mx, gm)
+            assert {k: st[k] for k in want} == want, (mx, gm, mat)
             assert st["whole_batch_gate"] == 1 and st["gate_calls"] == 1
             assert np.array_equal(eng.batch_records().view(np.uint8),
-                                  acc.astype(oracle.HSP_DTYPE).view(np.uint8)), (mx, gm)
-            print(f"max_hits {mx} gate_mode {gm}: {want}", flush=True)
+                                  acc.astype(oracle.HSP_DTYPE).view(np.uint8)), (mx, gm, mat)
+            print(f"max_hits {mx} gate_mode {gm} materialize_mode {mat}: {want}", flush=True)
     # a sub-batch whose chunks average under 2^22 anchors: one gate call per chunk
     p = params_of(pat, max_hits=1 << 21)
     eng = engine(p)
