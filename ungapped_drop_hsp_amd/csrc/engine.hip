@@ -1156,9 +1156,8 @@ static int gate_key_grouped(Engine *e, uint64_t seed_lo, uint64_t seed_hi, uint6
         (rc = ensure_kg(e, gate_window_waves(n))))
         return rc;
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
-    KeyGroups g{e->d_kg_qs,        e->d_kg_qe,        e->d_kg_runs,
-                e->d_kg_run_c,     e->d_kg_run_first, e->d_kg_run_span,
-                e->kg_n_runs,      (uint32_t)e->n_seeds};
+    KeyGroups g{e->d_kg_qs,          e->d_kg_qe,       e->d_kg_run_c,
+                e->d_kg_run_first,   e->d_kg_run_span, e->kg_n_runs};
     KgScratch ks{e->d_kg_G, e->d_kg_a, e->d_kg_m, e->d_kg_dir, e->d_kg_blksum,
                  e->d_kg_blkoff, e->d_kg_info};
     HIP_TRY(e, launch_gate_window_kg(g, ks, e->d_prefix, (uint32_t)e->batch_lo,

@@ -175,11 +175,12 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     const uint32_t *qry4, const WindowParams &wp,
                                     uint32_t *list1, uint64_t *list1_a, uint32_t *list2,
                                     uint32_t *cnt, hipStream_t s);
-// Key-grouped first stage (gate_mode 5, and gate_mode 0 for chunks holding a large share
-// of the strand's seeds).  The query strand's seeds are kept grouped by k-mer (built when
+// Key-grouped first stage (gate_mode 5, and gate_mode 0 for ranges of seeds holding a
+// large share of the strand's seeds).  The query strand's seeds are kept grouped by k-mer (built when
 // the query is uploaded): qs lists the seed indices ordered by k-mer and, within a k-mer,
-// ascending; qe their query ends; runs the start in qs of each k-mer's run; run_c and
-// run_first the k-mer's reference bucket (size and start), set once a reference is there.
+// ascending; qe their query ends; run_span each k-mer run's range in qs and its first and
+// last seed; run_c and run_first the k-mer's reference bucket (size and start), set once
+// a reference is there.
 // A range's anchors (a chunk, or a whole batch) are then enumerated run by run: the
 // range's seeds of a k-mer (a contiguous stretch of its run) times the k-mer's bucket, so
 // the reference window of each bucket entry and the query window of each seed are read
@@ -188,12 +189,10 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
 struct KeyGroups {
     const uint32_t *qs;
     const uint32_t *qe;
-    const uint32_t *runs;
     const uint32_t *run_c;
     const uint32_t *run_first;
     const uint4 *run_span;  // each run: its qs range [x, y) and its first and last seed
     uint32_t n_runs;
-    uint32_t n_qs;
 };
 // Per-call scratch of the key-grouped stage, n_runs entries each (dir: one per wave).
 struct KgScratch {
