@@ -329,12 +329,14 @@ typedef struct {
  * that they overlap the next chunks' kernels; the call returns once every copy has
  * landed, also on error.  Where the key-grouped first gate stage serves the whole batch
  * (gate_mode 0 or 5, see hspz_params) and the batch has more than one chunk, at most
- * 2^30 anchors and at least 2^22 per chunk on average, the gate runs once over every
- * chunk's slots (the batch's flags and kept
- * anchors in engine buffers of 9 bytes per anchor, its deferred lists sized for the
- * batch) and the chunks are then compacted, materialized and copied one by one from their
- * slices; the records are the same (stats->whole_batch_gate = 1).  The chunk cut still
- * bounds every other buffer.  With time_gate != 0 each expansion-and-gate call is
+ * 2^30 anchors and at least 2^22 per chunk on average, the whole batch goes at once:
+ * one gate call over every chunk's slots, one compaction of the batch's flags (survivor
+ * ids are batch slots, so the chunks' survivors come one chunk after another), one
+ * materialization of them all (their anchors are in query order) and one copy of the
+ * accepted records.  The records are the chunks' records in chunk order, as chunk by
+ * chunk (stats->whole_batch_gate = 1).  Its engine buffers take 13 bytes per anchor
+ * (flags, kept anchors, survivor ids) and the gate's deferred lists 20 more; where the
+ * device cannot hold them the batch goes chunk by chunk.  With time_gate != 0 each expansion-and-gate call is
  * bracketed by HIP events on stream and *stats reports their number and summed duration.
  * The plan stays current afterwards.  Synchronises stream.  Errors: as hspz_plan,
  * hspz_find_hits and the calls above; HSPZ_E_INVALID for a NULL stats pointer. */

@@ -117,9 +117,11 @@ struct Engine {
     hspz_segment_pair *rb_out[2] = {nullptr, nullptr};  // accepted records, by chunk parity
     uint8_t *rb_status = nullptr;
     uint64_t rb_cap_s = 0;
-    // the whole-batch gate of hspz_run_batch: the batch's flags and kept anchors
+    // the whole-batch gate of hspz_run_batch: the batch's flags, kept anchors and
+    // survivor ids
     uint8_t *bb_flags = nullptr;
     uint64_t *bb_anchors = nullptr;
+    uint32_t *bb_ids = nullptr;
     uint64_t bb_cap = 0;
     hspz_segment_pair *h_rec = nullptr;  // pinned: accepted records of the last batch
     uint64_t h_rec_cap = 0, h_rec_n = 0;

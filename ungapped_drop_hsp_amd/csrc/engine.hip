@@ -429,6 +429,7 @@ Engine::~Engine() {
     dfree(d_defer_a);
     dfree(bb_flags);
     dfree(bb_anchors);
+    dfree(bb_ids);
     dfree(d_defer_cnt);
     dfree(d_kmer);
     dfree(d_qend);
@@ -1441,7 +1442,8 @@ static int ensure_run_buffers(Engine *e, uint64_t n, uint64_t ns) {
 static int ensure_batch_buffers(Engine *e, uint64_t n) {
     if (n <= e->bb_cap && e->bb_flags) return HSPZ_OK;
     int rc;
-    if ((rc = dalloc(e, e->bb_flags, n + 16)) || (rc = dalloc(e, e->bb_anchors, n))) {
+    if ((rc = dalloc(e, e->bb_flags, n + 16)) || (rc = dalloc(e, e->bb_anchors, n)) ||
+        (rc = dalloc(e, e->bb_ids, n))) {
         e->bb_cap = 0;
         return rc;
     }
@@ -1516,10 +1518,40 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
     stats->n_chunks = nch;
     uint64_t maxn = 0;
     for (const hspz_chunk &c : e->chunks) maxn = std::max<uint64_t>(maxn, c.n_hits);
+    // The whole batch at once: where the key-grouped stage serves the batch, one gate call
+    // covers the slots of every chunk (the batch's flags, kept anchors and survivor ids in
+    // one buffer each; the chunk cut bounds memory on small GPUs, and up to 2^30 anchors
+    // fit here), so a k-mer's seeds in every chunk share their reference windows and the
+    // stage runs once; the survivors are then compacted and materialized in one call
+    // each (below).  Batches of small chunks (under 2^22 anchors on average) go chunk by
+    // chunk: there each chunk's gate, queued ahead, covers the host's wait for the
+    // previous chunk's counts.
+    bool whole = nch > 1 && total <= kWholeBatchMax && total / nch >= kWholeChunkMin &&
+                 key_grouped_suits(e, e->batch_n);
+    if (whole) {
+        // its buffers (flags, kept anchors, survivor ids, both deferred lists, compaction
+        // blocks) are sized for the batch; where the device cannot hold them the batch
+        // goes chunk by chunk after all
+        if ((rc = ensure_batch_buffers(e, total)) || (rc = ensure_defer(e, total)) ||
+            (rc = ensure_defer_anchors(e)) || (rc = ensure_kg(e, gate_window_waves(total))) ||
+            (rc = ensure_compact(e, total))) {
+            if (rc != HSPZ_E_NOMEM) return rc;
+            (void)hipGetLastError();  // the failed allocation's error is not the next call's
+            e->err.clear();
+            dfree(e->bb_flags);
+            dfree(e->bb_anchors);
+            dfree(e->bb_ids);
+            dfree(e->d_defer);
+            dfree(e->d_defer_a);
+            e->bb_cap = e->cap_defer = e->cap_defer_a = 0;
+            whole = false;
+        }
+    }
     // Scratch that queued work may still be using is never regrown inside the loop: size
     // the gate's lists and directory and the compaction blocks for the largest chunk now.
-    if ((rc = ensure_run_buffers(e, maxn, 0)) || (rc = ensure_defer(e, maxn)) ||
-        (rc = ensure_dir(e, maxn)) || (rc = ensure_compact(e, maxn)))
+    if (!whole && ((rc = ensure_run_buffers(e, maxn, 0)) || (rc = ensure_defer(e, maxn)) ||
+                   (rc = ensure_defer_anchors(e)) || (rc = ensure_dir(e, maxn)) ||
+                   (rc = ensure_compact(e, maxn))))
         return rc;
     for (hipEvent_t &ev : e->count_ev)
         if (!ev) HIP_TRY(e, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
@@ -1538,33 +1570,6 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
         for (hipEvent_t &ev : e->gate_ev)
             if (!ev) HIP_TRY(e, hipEventCreate(&ev));
 
-    // The whole-batch gate: where the key-grouped stage serves the batch, one gate call
-    // covers the slots of every chunk at once (the batch's flags and kept anchors in one
-    // buffer each; the chunk cut bounds memory on small GPUs, and up to 2^30 anchors fit
-    // here), so a k-mer's seeds in every chunk share their reference windows and the
-    // stage runs once.  Compaction, materialization and the records then go chunk by
-    // chunk, from each chunk's slice, exactly as below.  Batches of small chunks (under
-    // 2^22 anchors on average) keep one gate call per chunk: there each chunk's gate,
-    // queued ahead, covers the host's wait for the previous chunk's counts.
-    bool whole = nch > 1 && total <= kWholeBatchMax && total / nch >= kWholeChunkMin &&
-                 key_grouped_suits(e, e->batch_n);
-    if (whole) {
-        // its buffers (flags, kept anchors, both deferred lists) are sized for the batch;
-        // where the device cannot hold them the batch is gated chunk by chunk after all
-        if ((rc = ensure_batch_buffers(e, total)) || (rc = ensure_defer(e, total)) ||
-            (rc = ensure_defer_anchors(e)) || (rc = ensure_kg(e, gate_window_waves(total)))) {
-            if (rc != HSPZ_E_NOMEM) return rc;
-            (void)hipGetLastError();  // the failed allocation's error is not the next call's
-            e->err.clear();
-            dfree(e->bb_flags);
-            dfree(e->bb_anchors);
-            dfree(e->d_defer);
-            dfree(e->d_defer_a);
-            e->bb_cap = e->cap_defer = e->cap_defer_a = 0;
-            if ((rc = ensure_defer(e, maxn)) || (rc = ensure_defer_anchors(e))) return rc;
-            whole = false;
-        }
-    }
     stats->whole_batch_gate = whole ? 1 : 0;
     if (whole) {
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
@@ -1573,6 +1578,38 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
                                    e->bb_anchors, e->bb_flags, s)))
             return rc;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[1], s));
+        // The survivors of every chunk at once: their ids are batch slots, ascending, so
+        // chunk by chunk in chunk order and within a chunk in slot order; their anchors
+        // are in query order, so they are materialized in one call and the accepted
+        // records leave in one copy -- the records of the chunks one after another.
+        uint64_t ns = 0, na = 0;
+        if ((rc = count_queue(e, e->bb_flags, total, e->bb_ids, nullptr, nullptr, e->bb_cap, 0,
+                              s)) ||
+            (rc = count_wait(e, 0, e->bb_cap, &ns)))
+            return rc;
+        if (time_gate) {
+            float ms = 0.f;
+            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[0], e->gate_ev[1]));
+            stats->gate_ms = ms;
+            stats->gate_calls = 1;
+        }
+        if ((rc = ensure_run_buffers(e, 0, ns)) ||
+            (rc = materialize(e, e->bb_anchors, e->bb_ids, ns, e->rb_hsp, e->rb_status, true,
+                              stream)) ||
+            (rc = count_queue(e, e->rb_status, ns, nullptr, e->rb_hsp, e->rb_out[0],
+                              e->rb_cap_s, 1, s)) ||
+            (rc = count_wait(e, 1, e->rb_cap_s, &na)))
+            return rc;
+        if (na) {
+            if ((rc = ensure_record_staging(e, na, 0, s))) return rc;
+            HIP_TRY(e, hipMemcpyAsync(e->h_rec, e->rb_out[0], na * sizeof(hspz_segment_pair),
+                                      hipMemcpyDeviceToHost, s));
+        }
+        HIP_TRY(e, hipStreamSynchronize(s));
+        stats->n_survivors = ns;
+        stats->n_accepted = na;
+        e->h_rec_n = na;
+        return HSPZ_OK;
     }
 
     // One stream, queued one chunk ahead: chunk c + 1's expansion+gate and survivor
@@ -1582,7 +1619,6 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
     // host on copy_s, behind its record count, while the next chunks run; the compaction
     // of chunk c + 2 into the same record buffer waits for that copy.
     auto gate = [&](uint32_t c) -> int {
-        if (whole) return HSPZ_OK;
         const int b = c & 1;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[2 * b], s));
         int r = hspz_find_hits_gate(engine, c, e->rb_anchors[b], e->rb_cap_a, e->rb_flags[b],
@@ -1593,17 +1629,8 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
     };
     auto survivors = [&](uint32_t c) -> int {
         const int b = c & 1;
-        const uint8_t *f = e->rb_flags[b];
-        if (whole) {  // the chunk's slice; compaction reads 16-byte aligned flags fastest
-            f = e->bb_flags + e->chunks[c].hit_lo;
-            if (reinterpret_cast<uintptr_t>(f) & 15) {
-                HIP_TRY(e, hipMemcpyAsync(e->rb_flags[b], f, e->chunks[c].n_hits,
-                                          hipMemcpyDeviceToDevice, s));
-                f = e->rb_flags[b];
-            }
-        }
-        return count_queue(e, f, e->chunks[c].n_hits, e->rb_ids[b], nullptr, nullptr,
-                           e->rb_cap_a, 0, s);
+        return count_queue(e, e->rb_flags[b], e->chunks[c].n_hits, e->rb_ids[b], nullptr,
+                           nullptr, e->rb_cap_a, 0, s);
     };
     if (nch && ((rc = gate(0)) || (rc = survivors(0)))) return rc;
     uint64_t acc = 0;
@@ -1612,10 +1639,9 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
         if (c + 1 < nch && (rc = gate(c + 1))) return rc;
         uint64_t ns = 0, na = 0;
         if ((rc = count_wait(e, 0, e->rb_cap_a, &ns))) return rc;
-        if (time_gate && (!whole || c == 0)) {  // the count lands after the gate events
+        if (time_gate) {  // the survivor count lands after the chunk's gate events
             float ms = 0.f;
-            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[whole ? 0 : 2 * b],
-                                           e->gate_ev[whole ? 1 : 2 * b + 1]));
+            HIP_TRY(e, hipEventElapsedTime(&ms, e->gate_ev[2 * b], e->gate_ev[2 * b + 1]));
             stats->gate_ms += ms;
             stats->gate_calls++;
         }
@@ -1626,9 +1652,8 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
             if ((rc = ensure_run_buffers(e, maxn, ns))) return rc;
         }
         // the chunk's own survivors, in slot order: query ends never decrease
-        const uint64_t *anch = whole ? e->bb_anchors + e->chunks[c].hit_lo : e->rb_anchors[b];
-        if ((rc = materialize(e, anch, e->rb_ids[b], ns, e->rb_hsp, e->rb_status, true,
-                              stream)))
+        if ((rc = materialize(e, e->rb_anchors[b], e->rb_ids[b], ns, e->rb_hsp, e->rb_status,
+                              true, stream)))
             return rc;
         if (e->copy_pending[b]) {  // chunk c - 2's records are still being read out of it
             HIP_TRY(e, hipStreamWaitEvent(s, e->copied_ev[b], 0));
