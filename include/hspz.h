@@ -126,7 +126,7 @@ typedef struct {
  *                strictly new best at or past its neighbour's start takes the rest from
  *                the neighbour (the walks coincide from there), so a stretch of a
  *                diagonal shared by many survivors is walked about once; 0 = 2 for calls
- *                of at least 65,536 survivors, else 1.  Mode 2 needs
+ *                of at least 131,072 survivors, else 1.  Mode 2 needs
  *                n_ref + n_qry + 2 < 2^32 (32-bit diagonal keys) and takes mode 1
  *                otherwise.  Every mode writes the same records and status.
  */

@@ -1253,8 +1253,10 @@ static int impl_hspz_compact(hspz_engine *engine, const uint8_t *d_flags, uint64
 }
 
 // Diagonal-shared materialization: calls of at least this many survivors take it in
-// materialize_mode 0 (below it the sort's fixed launches cost more than the walks save).
-constexpr uint64_t kMatSharedMin = 65536;
+// materialize_mode 0.  Below it the sort's and scans' fixed launches (about 0.3 ms in
+// all) cost more than the walks save: 66,579 survivors of the 50 Mb workload take
+// 0.11 ms walked one by one.
+constexpr uint64_t kMatSharedMin = 131072;
 
 // Scratch of the diagonal-shared materialization for n survivors.  The per-side arrays
 // (best, ext, term, ds, cnt, sum, pos: seven u32 each) are carved out
