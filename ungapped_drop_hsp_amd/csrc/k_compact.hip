@@ -73,24 +73,51 @@ __global__ __launch_bounds__(kThreads) void k_count(const uint8_t *__restrict__ 
     if (threadIdx.x == 0) blk[blockIdx.x] = total;
 }
 
-// In place: blk[0..nblk) counts -> exclusive offsets, blk[nblk] = *total = sum.
+// In place: blk[0..nblk) counts -> exclusive offsets, blk[nblk] = *total = sum.  Tiles of
+// kScanThreads * kScanTile counts are read coalesced into LDS (a thread's reads in flight
+// together), scanned there kScanTile consecutive counts per thread, and written back.
+constexpr int kScanTile = 8;
 __global__ __launch_bounds__(kScanThreads) void k_scan(uint32_t *__restrict__ blk, uint32_t nblk,
                                                        uint32_t *__restrict__ total_out) {
+    __shared__ uint32_t tile[kScanThreads * kScanTile];
     __shared__ uint32_t sh[kScanThreads / 64];
-    const uint32_t per = (nblk + kScanThreads - 1) / kScanThreads;
-    const uint32_t lo = min(nblk, threadIdx.x * per), hi = min(nblk, lo + per);
-    uint32_t sum = 0;
-    for (uint32_t i = lo; i < hi; i++) sum += blk[i];
-    uint32_t total;
-    uint32_t run = block_excl_scan(sum, sh, total);
-    for (uint32_t i = lo; i < hi; i++) {
-        const uint32_t c = blk[i];
-        blk[i] = run;
-        run += c;
+    const int t = threadIdx.x;
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < nblk; base += kScanThreads * kScanTile) {
+        uint32_t v[kScanTile];
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) {
+            const uint32_t i = base + k * kScanThreads + t;
+            v[k] = i < nblk ? blk[i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) tile[k * kScanThreads + t] = v[k];
+        __syncthreads();
+        uint32_t loc[kScanTile], sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) {
+            loc[k] = tile[t * kScanTile + k];
+            sum += loc[k];
+        }
+        uint32_t tile_total;
+        uint32_t acc = carry + block_excl_scan(sum, sh, tile_total);
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) {
+            tile[t * kScanTile + k] = acc;
+            acc += loc[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) {
+            const uint32_t i = base + k * kScanThreads + t;
+            if (i < nblk) blk[i] = tile[k * kScanThreads + t];
+        }
+        carry += tile_total;
+        __syncthreads();  // the next tile reuses tile and sh
     }
-    if (threadIdx.x == 0) {
-        blk[nblk] = total;
-        *total_out = total;
+    if (t == 0) {
+        blk[nblk] = carry;
+        *total_out = carry;
     }
 }
 

@@ -197,47 +197,57 @@ __global__ __launch_bounds__(kThreads) void k_add_offsets(uint32_t *__restrict__
 
 constexpr int kScanThreads = 1024;
 
+// One workgroup: tiles of kScanThreads * kScanTile block sums are read coalesced (all of
+// a thread's reads in flight together) into LDS, where each thread scans kScanTile
+// consecutive sums, and the offsets go back out coalesced; the tile totals carry on.
+constexpr int kScanTile = 8;
 __global__ __launch_bounds__(kScanThreads) void k_scan_blocks(const uint64_t *__restrict__ blksum,
                                                              uint64_t nblk,
                                                              uint32_t *__restrict__ blkoff,
                                                              PlanInfo *__restrict__ info) {
+    __shared__ uint64_t tile[kScanThreads * kScanTile];
     __shared__ uint64_t wave_tot[kScanThreads / 64];
     const int t = threadIdx.x;
-    const uint64_t per = (nblk + kScanThreads - 1) / kScanThreads;
-    const uint64_t lo = min((uint64_t)t * per, nblk), hi = min(lo + per, nblk);
-    // each thread's segment is read eight sums at a time, so the loads overlap
-    constexpr int kBatch = 8;
-    uint64_t sum = 0;
-    uint64_t b = lo;
-    for (; b + kBatch <= hi; b += kBatch) {
-        uint64_t v[kBatch];
+    uint64_t carry = 0;
+    for (uint64_t base = 0; base < nblk; base += kScanThreads * kScanTile) {
+        uint64_t v[kScanTile];
 #pragma unroll
-        for (int k = 0; k < kBatch; k++) v[k] = blksum[b + k];
-#pragma unroll
-        for (int k = 0; k < kBatch; k++) sum += v[k];
-    }
-    for (; b < hi; b++) sum += blksum[b];
-    const uint64_t incl = wave_incl_sum_u64(sum);
-    if (lane_id() == 63) wave_tot[t >> 6] = incl;
-    __syncthreads();
-    uint64_t acc = incl - sum;
-    for (int w = 0; w < (t >> 6); w++) acc += wave_tot[w];
-    b = lo;
-    for (; b + kBatch <= hi; b += kBatch) {
-        uint64_t v[kBatch];
-#pragma unroll
-        for (int k = 0; k < kBatch; k++) v[k] = blksum[b + k];
-#pragma unroll
-        for (int k = 0; k < kBatch; k++) {
-            blkoff[b + k] = (uint32_t)acc;
-            acc += v[k];
+        for (int k = 0; k < kScanTile; k++) {
+            const uint64_t i = base + (uint64_t)k * kScanThreads + t;
+            v[k] = i < nblk ? blksum[i] : 0;
         }
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) tile[k * kScanThreads + t] = v[k];
+        __syncthreads();
+        uint64_t loc[kScanTile], sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) {
+            loc[k] = tile[t * kScanTile + k];
+            sum += loc[k];
+        }
+        const uint64_t incl = wave_incl_sum_u64(sum);
+        if (lane_id() == 63) wave_tot[t >> 6] = incl;
+        __syncthreads();
+        uint64_t acc = carry + incl - sum, tile_total = 0;
+        for (int w = 0; w < kScanThreads / 64; w++) {
+            if (w < (t >> 6)) acc += wave_tot[w];
+            tile_total += wave_tot[w];
+        }
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) {
+            tile[t * kScanTile + k] = acc;
+            acc += loc[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kScanTile; k++) {
+            const uint64_t i = base + (uint64_t)k * kScanThreads + t;
+            if (i < nblk) blkoff[i] = (uint32_t)tile[k * kScanThreads + t];
+        }
+        carry += tile_total;
+        __syncthreads();  // the next tile reuses tile and wave_tot
     }
-    for (; b < hi; b++) {
-        blkoff[b] = (uint32_t)acc;
-        acc += blksum[b];
-    }
-    if (t == kScanThreads - 1) info->total = acc;
+    if (t == 0) info->total = carry;
 }
 
 __global__ __launch_bounds__(64) void k_chunk_walk(const uint32_t *__restrict__ P, uint64_t n,
