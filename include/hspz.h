@@ -399,11 +399,12 @@ int hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64
 int hspz_debug_walk_steps(hspz_engine *engine, const uint64_t *d_anchors, uint64_t n,
                           uint64_t *total_steps, void *stream);
 
-/* How the last hspz_score_gate call split its anchors when it took the window path:
- * *n_stage2 walked past the first window (48 bases right of the anchor and 72 left, or
- * 32 and 56 with gate_mode 3) and went to the second (64 and 96); *n_exact walked past
- * that too and were decided by the exact per-base walk.  Synchronises stream.
- * Errors: HSPZ_E_STATE if that call did not take the window path. */
+/* How the last hspz_score_gate or hspz_find_hits_gate call split its anchors when it
+ * took the window path: *n_stage2 walked past the first window (48 bases right of the
+ * anchor and 72 left, or 32 and 56 with gate_mode 3) and went to the second (64 and 96);
+ * *n_exact walked past that too and were decided by the exact per-base walk.
+ * Synchronises stream.  Errors: HSPZ_E_STATE if that call did not take the window
+ * path. */
 int hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2, uint64_t *n_exact,
                              void *stream);
 

@@ -742,6 +742,63 @@ def test_bucketed_gate_slice_counts(slices):
         assert np.array_equal(f[:n].cpu().numpy(), want[:n]), f"n={n}"
 
 
+def _copies_with_spacers(seed, unit_len, copies, spacer):
+    """Copies of one random unit separated by random spacers: anchors between copies walk
+    to the end of their copy, then drop within the spacer."""
+    rng = np.random.default_rng(seed)
+    bases = np.frombuffer(b"ACGT", np.uint8)
+    unit = bases[rng.integers(0, 4, unit_len)]
+    parts = []
+    for _ in range(copies):
+        parts += [unit, bases[rng.integers(0, 4, spacer)]]
+    return np.concatenate(parts)
+
+
+@pytest.mark.parametrize("gate_mode", [0, 2, 3, 5])
+def test_find_hits_gate_defers_most_anchors(gate_mode):
+    # "D. Score gate", D.2: the first window stage defers every walk that outlives its
+    # window; here most anchors do, more than a wave's LDS segment holds, so deferred
+    # anchors reach the second stage both through the global list (segments flushed on
+    # the way) and through the second stage the first stage's workgroups run themselves.
+    # K is set below and at the median total, so the second stage decides both flags, and
+    # out of reach, so that no walk stops early at the threshold and deferrals peak.
+    # Flags and kept anchors against the oracle's, chunk by chunk.
+    import torch
+    seq = _copies_with_spacers(21, 90, 48, 70)
+    p0 = params_of("1101011")
+    o0, R, qc = oracle_pass(seq, seq, p0)
+    a = np.concatenate([c["anchors"] for c in o0["chunks"]])
+    tot, _ = oracle.gate_totals(a, R.codes, qc, p0["sub"], p0["n_score"], p0["xdrop"])
+    for K in (3000, int(np.median(tot)), 10**6):
+        p = params_of("1101011", K=K, max_hits=70_000)
+        o, _, _ = oracle_pass(seq, seq, p)
+        eng = engine(p, gate_mode=gate_mode)
+        eng.upload_reference(seq)
+        eng.upload_query(seq)
+        total, nch = eng.plan(0, eng.num_seeds())
+        assert nch == len(o["chunks"]) > 2 and total == o["total"] > 200_000
+        kept = n2_all = 0
+        for c in range(nch):
+            n = eng.get_chunk(c)["n_hits"]
+            at = torch.full((max(n, 1),), -1, dtype=torch.int64, device="cuda")
+            f = torch.full((max(n, 1) + 16,), 7, dtype=torch.uint8, device="cuda")
+            eng.find_hits_gate(c, at, f)
+            want = o["chunks"][c]["flags"]
+            got = f[:n].cpu().numpy()
+            assert np.array_equal(got, want), f"K={K} chunk {c}: flags differ"
+            keep = np.flatnonzero(want)
+            got_a = at[:n].cpu().numpy().view(np.uint64)
+            assert np.array_equal(got_a[keep], o["chunks"][c]["anchors"][keep])
+            n2, nx = eng.debug_gate_deferred()
+            assert nx <= n2 <= n
+            n2_all += n2
+            kept += keep.size
+        if K < 10**6:
+            assert 0 < kept < total
+        else:
+            assert kept == 0 and n2_all > total // 4
+
+
 def test_find_hits_gate_huge_bucket_and_sparse_seeds():
     # one k-mer owning thousands of slots (a poly-A block on both sides), chunked so that
     # chunks start and end inside its bucket's seeds; and a reference sharing almost no

@@ -1800,10 +1800,11 @@ static int impl_hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2
     int rc = set_device(e);
     if (rc) return rc;
     hipStream_t s = as_stream(stream);
-    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_defer_cnt, 2 * sizeof(uint32_t),
+    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_defer_cnt, 3 * sizeof(uint32_t),
                               hipMemcpyDeviceToHost, s));
     HIP_TRY(e, hipStreamSynchronize(s));
-    *n_stage2 = e->h_pinned[0];
+    // the listed second stage plus the one the first stage's workgroups ran themselves
+    *n_stage2 = (uint64_t)e->h_pinned[0] + e->h_pinned[2];
     *n_exact = e->h_pinned[1];
     return HSPZ_OK;
 }

@@ -483,6 +483,70 @@ __device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_
                                      defer_cnt);
 }
 
+// The second window stage run by the workgroup of a first stage that forms its own
+// anchors, once all four waves are done with their steps: the deferred (slot, anchor)
+// pairs still in the waves' LDS segments are taken 64 at a time, each wave a step in turn,
+// with the wider windows.  The lines of a step's windows are read while the other waves
+// on the SIMD score their blocks, instead of in a separate launch whose one step per wave
+// waits on them.  A deferred slot's anchor is stored unless its flag is 0 (the exact list
+// reads it there); flags already hold 0 when ZeroSet.  Anchors the wider windows leave
+// undecided go to the exact list.  Segments a wave flushed to the global list on the way
+// are left to the separate second stage.  cnt[1] counts the exact list, cnt[2] the
+// anchors pooled here.
+template <int S, bool ZeroSet>
+__device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint64_t (*sega)[S],
+                                            uint32_t *seg_n, uint32_t nseg, const int16_t *tab,
+                                            uint64_t *__restrict__ anchors,
+                                            uint8_t *__restrict__ flags,
+                                            const uint32_t *__restrict__ ref4,
+                                            const uint32_t *__restrict__ qry4,
+                                            const WindowParams &wp, uint32_t *__restrict__ list2,
+                                            uint32_t *__restrict__ cnt) {
+    static_assert(kWaves == 4, "four wave segments");
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    if (lane == 0) seg_n[w] = nseg;
+    __syncthreads();
+    const uint32_t n0 = seg_n[0], n1 = seg_n[1], n2 = seg_n[2];
+    const uint32_t total = n0 + n1 + n2 + seg_n[3];
+    if (threadIdx.x == 0 && total) atomicAdd(cnt + 2, total);  // the pooled count
+    for (uint32_t e0 = (uint32_t)w * 64; e0 < total; e0 += kWaves * 64) {  // uniform
+        const uint32_t e = e0 + lane;
+        const bool valid = e < total;
+        uint32_t slot = 0;
+        uint64_t a = 0;
+        if (valid) {
+            uint32_t v = 0, j = e;
+            if (j >= n0) {
+                j -= n0;
+                v = 1;
+                if (j >= n1) {
+                    j -= n1;
+                    v = 2;
+                    if (j >= n2) {
+                        j -= n2;
+                        v = 3;
+                    }
+                }
+            }
+            slot = seg[v][j];
+            a = sega[v][j];
+        }
+        Win<kStage2Right, kStage2Left, true> win;
+        win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
+        const int res = win.decide(tab, wp);
+        if (valid && res != 0) anchors[slot] = a;
+        if (valid && (ZeroSet ? res == 1 : res != 2)) flags[slot] = (uint8_t)res;
+        const uint64_t m = __ballot(valid && res == 2);
+        if (m) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(cnt + 1, (uint32_t)__popcll(m));
+            base = __shfl(base, 0, 64);
+            if (valid && res == 2) list2[base + lane_rank(m)] = slot;
+        }
+    }
+}
+
 // First stage: every anchor, consecutive 64-anchor steps per wave.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window(
@@ -518,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
 
 // Directory of the fused first stage: the seed that owns the first slot of each wave's
 // range, i.e. the first seed whose prefix - hit_lo exceeds that slot (a binary search).
-// The first thread also clears the two deferred-list counters the stages append to.
+// The first thread also clears the three deferred-list counters the stages append to.
 __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n_waves,
                                                        uint32_t steps,
                                                        uint32_t *__restrict__ cnt) {
@@ -526,6 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n
     if (w == 0) {
         cnt[0] = 0;
         cnt[1] = 0;
+        cnt[2] = 0;
     }
     if (w >= n_waves) return;
     const uint32_t t = w * (64u * steps);
@@ -552,12 +617,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint64_t *__restrict__ defer_a,
-    uint32_t *__restrict__ defer_cnt) {
+    uint32_t *__restrict__ defer_cnt, uint32_t *__restrict__ list2) {
     __shared__ int16_t tab[kWinTab];
     __shared__ uint32_t seg[kWaves][kSegKg];
     __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
-    __shared__ uint32_t blk_base;
     __shared__ uint32_t rel[kWaves][64];  // prefix - hit_lo of the window's seeds
     __shared__ uint32_t fst[kWaves][64];  // their bucket starts
     __shared__ uint32_t qen[kWaves][64];  // their query ends
@@ -621,8 +685,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
         defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, t, a, defer,
                                    defer_a, defer_cnt);
     }
-    defer_flush_block_g<kSegKg, true>(seg, sega, seg_n, &blk_base, nseg, defer, defer_a,
-                                      defer_cnt);
+    stage2_pool<kSegKg, false>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
+                               list2, defer_cnt);
 }
 
 // ------------------------------------------------------------------ key-grouped first stage
@@ -725,6 +789,7 @@ __global__ __launch_bounds__(kThreads) void k_kg_dir(KgScratch ks, uint32_t n_ru
     if (w == 0) {
         cnt[0] = 0;
         cnt[1] = 0;
+        cnt[2] = 0;
     }
     if (w >= n_waves) return;
     const uint32_t t = w * (64u * steps);
@@ -747,12 +812,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint64_t *__restrict__ defer_a,
-    uint32_t *__restrict__ defer_cnt) {
+    uint32_t *__restrict__ defer_cnt, uint32_t *__restrict__ list2) {
     __shared__ int16_t tab[kWinTab];
     __shared__ uint32_t seg[kWaves][kSegKg];
     __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
-    __shared__ uint32_t blk_base;
     __shared__ uint32_t rel[kWaves][64];  // inclusive prefix of the window's runs
     __shared__ uint32_t rs_[kWaves][64];  // exclusive prefix (rel minus c * m)
     __shared__ uint32_t rf[kWaves][64];   // bucket starts
@@ -865,8 +929,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
         defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, slot, a, defer,
                                    defer_a, defer_cnt);
     }
-    defer_flush_block_g<kSegKg, true>(seg, sega, seg_n, &blk_base, nseg, defer, defer_a,
-                                      defer_cnt);
+    stage2_pool<kSegKg, true>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
+                              list2, defer_cnt);
 }
 
 // First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
@@ -959,9 +1023,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
     defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
 }
 
-__global__ void k_zero_u32x2(uint32_t *p) {
+// Clears the deferred-list counters: second stage, exact list, pooled second stage.
+__global__ void k_zero_counts(uint32_t *p) {
     p[0] = 0;
     p[1] = 0;
+    p[2] = 0;
 }
 
 
@@ -1011,15 +1077,18 @@ hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
 // The second stage strides over whatever the first left, up to all n anchors.
 // list1_a: the anchors of list1's entries, or NULL when they are read from anchors[];
 // with list1_a, the anchors the stage keeps or defers are stored into anchors_out.
-static void launch_stage2(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
-                          const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
-                          uint32_t *list1, const uint64_t *list1_a, uint64_t *anchors_out,
-                          uint32_t *list2, uint32_t *cnt, hipStream_t s) {
+static void launch_stage2(bool narrow, bool pooled, const uint64_t *anchors, uint32_t n,
+                          uint8_t *flags, const uint32_t *ref4, const uint32_t *qry4,
+                          const WindowParams &wp, uint32_t *list1, const uint64_t *list1_a,
+                          uint64_t *anchors_out, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
     // enough waves for one 64-anchor step each when an eighth of the anchors is listed
-    // (about one step per wave on the 50 Mb workload: 7% faster than three)
+    // (about one step per wave on the 50 Mb workload: 7% faster than three).  After a
+    // first stage that runs the second stage on its own deferred anchors, the list holds
+    // only the segments its waves flushed on the way (none on random sequence), and a
+    // smaller grid strides over them.
     const uint32_t cap2 = narrow ? n : n / 8 + 1;
-    const uint32_t blocks2 =
-        (uint32_t)std::min<uint64_t>(((uint64_t)cap2 + kWaves * 64 - 1) / (kWaves * 64), 16384);
+    const uint32_t blocks2 = (uint32_t)std::min<uint64_t>(
+        ((uint64_t)cap2 + kWaves * 64 - 1) / (kWaves * 64), pooled ? 2048 : 16384);
     hipLaunchKernelGGL((k_gate_window_list<kStage2Right, kStage2Left>), dim3(blocks2),
                        dim3(kThreads), 0, s, anchors, list1, list1_a, anchors_out, cnt, flags, ref4,
                        qry4, wp, list2, cnt + 1);
@@ -1028,7 +1097,7 @@ static void launch_stage2(bool narrow, const uint64_t *anchors, uint32_t n, uint
 hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
                               const uint32_t *ref4, const uint32_t *qry4, const WindowParams &wp,
                               uint32_t *list1, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
     if (n == 0) return hipGetLastError();
     const uint32_t steps = gate_window_steps(n);
     const uint64_t per_block = (uint64_t)kWaves * 64 * steps;
@@ -1040,8 +1109,8 @@ hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, 
     else
         hipLaunchKernelGGL((k_gate_window<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads),
                            0, s, anchors, n, steps, flags, ref4, qry4, wp, list1, cnt);
-    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr, list2, cnt,
-                  s);
+    launch_stage2(narrow, false, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr,
+                  list2, cnt, s);
     return hipGetLastError();
 }
 
@@ -1061,7 +1130,7 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     uint32_t *list1, uint64_t *list1_a, uint32_t *list2,
                                     uint32_t *cnt, hipStream_t s) {
     if (n == 0) {
-        hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+        hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
     }
     const uint32_t steps = gate_window_steps(n);
@@ -1072,13 +1141,13 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
     if (narrow)
         hipLaunchKernelGGL((k_gate_window_fused<kNarrowRight, kNarrowLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, list1_a, cnt);
+                           list1, list1_a, cnt, list2);
     else
         hipLaunchKernelGGL((k_gate_window_fused<kWideRight, kWideLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, list1_a, cnt);
-    launch_stage2(narrow, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors, list2, cnt,
-                  s);
+                           list1, list1_a, cnt, list2);
+    launch_stage2(narrow, true, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors,
+                  list2, cnt, s);
     return hipGetLastError();
 }
 
@@ -1090,7 +1159,7 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
                                  uint32_t *list2, uint32_t *cnt, hipStream_t s) {
     if (n == 0 || kg.n_runs == 0) {
-        hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+        hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
     }
     const uint32_t nr = kg.n_runs;
@@ -1106,9 +1175,9 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
     const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
     hipLaunchKernelGGL((k_gate_window_kg<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads), 0,
                        s, kg, ks, prefix, batch_lo, hit_lo, n, steps, pos, anchors, flags, ref4,
-                       qry4, wp, list1, list1_a, cnt);
-    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors, list2, cnt,
-                  s);
+                       qry4, wp, list1, list1_a, cnt, list2);
+    launch_stage2(false, true, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors,
+                  list2, cnt, s);
     return hipGetLastError();
 }
 
@@ -1117,7 +1186,7 @@ hipError_t launch_gate_window_bucketed(const uint64_t *anchors, uint32_t n, cons
                                        const uint32_t *qry4, const WindowParams &wp,
                                        uint32_t *list1, uint32_t *list2, uint32_t *cnt,
                                        hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, cnt);
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
     if (n == 0) return hipGetLastError();
     hipError_t st = launch_zero_bytes(flags, n, s);
     if (st != hipSuccess) return st;
@@ -1128,8 +1197,8 @@ hipError_t launch_gate_window_bucketed(const uint64_t *anchors, uint32_t n, cons
     hipLaunchKernelGGL((k_gate_window_bucketed<kWideRight, kWideLeft>), dim3(blocks),
                        dim3(kThreads), 0, s, sa, si, n, part, steps, flags, ref4, qry4, wp,
                        list1, cnt);
-    launch_stage2(false, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr, list2, cnt,
-                  s);
+    launch_stage2(false, false, anchors, n, flags, ref4, qry4, wp, list1, nullptr, nullptr,
+                  list2, cnt, s);
     return hipGetLastError();
 }
 
