@@ -802,9 +802,18 @@ __global__ __launch_bounds__(kThreads) void k_kg_dir(KgScratch ks, uint32_t n_ru
     ks.dir[w] = lo;
 }
 
+// A run as the key-grouped stage's window holds it: inclusive and exclusive prefix of its
+// anchors in the call (rs above rel for an entry past the last run), bucket start, first
+// seed in qs, seeds in the range and the hardware reciprocal of that count.
+struct KgRun {
+    uint32_t rel, rs, f, a, m;
+    float q;
+};
+
 // The first window stage over the key-grouped order (see above).  As k_gate_window_fused,
 // a wave keeps a window of 64 runs in LDS (prefix end, bucket size and start, first seed
-// in qs, seeds) and its lanes binary-search it for the run owning their position.
+// in qs, seeds); each step's lanes find the run owning their position from the marks the
+// runs leave at their first positions in the step, by a max-scan across the wave.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     KeyGroups kg, KgScratch ks, const uint32_t *__restrict__ prefix, uint32_t batch_lo,
@@ -817,12 +826,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     __shared__ uint32_t seg[kWaves][kSegKg];
     __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
-    __shared__ uint32_t rel[kWaves][64];  // inclusive prefix of the window's runs
-    __shared__ uint32_t rs_[kWaves][64];  // exclusive prefix (rel minus c * m)
-    __shared__ uint32_t rf[kWaves][64];   // bucket starts
-    __shared__ uint32_t ra[kWaves][64];   // first seed in qs
-    __shared__ uint32_t rm[kWaves][64];   // seeds in the range
-    __shared__ float rq[kWaves][64];      // 1 / m (hardware reciprocal)
+    __shared__ KgRun run[kWaves][64];    // the wave's window of runs
+    __shared__ uint32_t mk[kWaves][64];  // marks of the step's positions (run index)
     if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
     __syncthreads();
 
@@ -854,29 +859,47 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
                 const uint32_t c = kg.run_c[rr], f = kg.run_first[rr];
                 const uint32_t sa0 = ks.a[rr], m0 = ks.m[rr];
                 const uint32_t cm = c * m0;  // the run's anchors in this call
-                rel[w][lane] = in ? g + off : 0xFFFFFFFFu;
-                rs_[w][lane] = in ? g + off - cm : 0u;
-                rf[w][lane] = in ? f : 0u;
-                ra[w][lane] = in ? sa0 : 0u;
-                rm[w][lane] = in ? m0 : 1u;
-                rq[w][lane] = __builtin_amdgcn_rcpf((float)(in ? m0 : 1u));
+                KgRun &q = run[w][lane];
+                q.rel = in ? g + off : 0xFFFFFFFFu;
+                q.rs = in ? g + off - cm : 0xFFFFFFFFu;  // above rel: holds no position
+                q.f = in ? f : 0u;
+                q.a = in ? sa0 : 0u;
+                q.m = in ? m0 : 1u;
+                q.q = __builtin_amdgcn_rcpf((float)(in ? m0 : 1u));
                 small = __ballot(in && cm >= (1u << 22)) == 0;
                 step_small = step_small && small;
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 loaded = true;
             }
-            if (!found && t < rel[w][63]) {
-                int L = 0;  // number of the window's runs whose prefix is <= t
-#pragma unroll
-                for (int k = 32; k >= 1; k >>= 1)
-                    if (rel[w][L + k - 1] <= t) L += k;
-                start = rs_[w][L];
-                bfirst = rf[w][L];
-                sa = ra[w][L];
-                m = rm[w][L];
-                rcp = rq[w][L];
-                found = true;
+            // positions past the window's last run wait for the next window
+            const uint32_t lim = run[w][63].rel;
+            const bool look = !found && t < lim;
+            if (__ballot(look)) {  // uniform
+                // Each run of the window holding positions of this step marks the first of
+                // them (its start, or the step's first position) with its index.  Runs
+                // start in order, so a position holds one mark at most, and the largest
+                // mark at or below a position, an inclusive max-scan over the lanes, is
+                // the run that holds it (-1: no mark).
+                mk[w][lane] = 0xFFFFFFFFu;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                const uint32_t t0 = (uint32_t)i0;
+                const uint32_t re = run[w][lane].rel, rb = run[w][lane].rs;
+                const uint32_t pm = rb > t0 ? rb - t0 : 0u;
+                if (re > rb && re > t0 && pm < 64u) mk[w][pm] = (uint32_t)lane;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                const int32_t o = wave_incl_max((int32_t)mk[w][lane]);
+                if (look) {  // o >= 0: the run holding t is in the window and marks <= t
+                    const KgRun q = run[w][(uint32_t)o & 63u];
+                    start = q.rs;
+                    bfirst = q.f;
+                    sa = q.a;
+                    m = q.m;
+                    rcp = q.q;
+                    found = true;
+                }
             }
             if (__ballot(!found) == 0) break;
             // a position lies past the window: every lane is done reading it, slide it on
