@@ -1165,7 +1165,8 @@ static int gate_key_grouped(Engine *e, uint64_t seed_lo, uint64_t seed_hi, uint6
                                      (uint32_t)seed_lo, (uint32_t)seed_hi, (uint32_t)hit_lo,
                                      (uint32_t)n, e->d_pos, d_anchors, d_flags, e->d_ref4,
                                      e->d_qry4, e->wp, list1, e->d_defer_a, list2,
-                                     e->d_defer_cnt, s));
+                                     e->d_defer_cnt, e->sp, e->d_ref + kPad, e->d_qry + kPad,
+                                     s));
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
@@ -1210,7 +1211,8 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     cs.hit_lo = (uint32_t)c.hit_lo;
     HIP_TRY(e, launch_gate_window_fused(e->params.gate_mode == 3, cs, (uint32_t)n, d_anchors,
                                         d_flags, e->d_ref4, e->d_qry4, e->wp, list1,
-                                        e->d_defer_a, list2, e->d_defer_cnt, s));
+                                        e->d_defer_a, list2, e->d_defer_cnt, e->sp,
+                                        e->d_ref + kPad, e->d_qry + kPad, s));
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
@@ -1800,12 +1802,12 @@ static int impl_hspz_debug_gate_deferred(hspz_engine *engine, uint64_t *n_stage2
     int rc = set_device(e);
     if (rc) return rc;
     hipStream_t s = as_stream(stream);
-    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_defer_cnt, 3 * sizeof(uint32_t),
+    HIP_TRY(e, hipMemcpyAsync(e->h_pinned, e->d_defer_cnt, 4 * sizeof(uint32_t),
                               hipMemcpyDeviceToHost, s));
     HIP_TRY(e, hipStreamSynchronize(s));
-    // the listed second stage plus the one the first stage's workgroups ran themselves
+    // the listed stages plus the ones the first stage's workgroups ran themselves
     *n_stage2 = (uint64_t)e->h_pinned[0] + e->h_pinned[2];
-    *n_exact = e->h_pinned[1];
+    *n_exact = (uint64_t)e->h_pinned[1] + e->h_pinned[3];
     return HSPZ_OK;
 }
 

@@ -189,6 +189,22 @@ __global__ __launch_bounds__(kThreads) void k_gate(const uint64_t *__restrict__ 
     }
 }
 
+// The exact flag of anchor a, decided by the whole wave: the right walk, then the left one
+// unless R* alone reaches T; each stops as soon as the flag is known.  An anchor outside
+// the sequences scores 0 on both sides.
+__device__ __forceinline__ bool exact_flag(const int32_t *tab, const uint8_t *__restrict__ ref,
+                                           const uint8_t *__restrict__ qry, uint64_t a,
+                                           const ScoreParams &sp) {
+    const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
+    if (r > sp.n_ref || q > sp.n_qry) return false;
+    int32_t R, L;
+    uint32_t ext;
+    exact_walk<+1, false, false>(tab, ref + r, qry + q, sp.xdrop, sp.T, R, ext);
+    if (R >= sp.T) return true;
+    exact_walk<-1, false, false>(tab, ref + r, qry + q, sp.xdrop, sp.T - R, L, ext);
+    return (int64_t)R + L >= (int64_t)sp.T;
+}
+
 // The exact decision for the anchors the window stages could not finish (*count of them,
 // listed by index, read on the device).  Their walks are long (homologous stretches), so
 // each gets one wave that walks 64-base tiles (exact_walk) and stops as soon as the flag
@@ -207,20 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_list_wave(const uint64_t *__r
     const uint64_t nw = (uint64_t)gridDim.x * kWaves;
     for (uint64_t t = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); t < total; t += nw) {
         const uint32_t i = list[t];
-        const uint64_t a = anchors[i];
-        const uint32_t r = (uint32_t)a, q = (uint32_t)(a >> 32);
-        bool keep = false;  // an anchor outside the sequences scores 0 on both sides
-        if (r <= sp.n_ref && q <= sp.n_qry) {
-            int32_t R, L;
-            uint32_t ext;
-            exact_walk<+1, false, false>(tab, ref + r, qry + q, sp.xdrop, sp.T, R, ext);
-            if (R >= sp.T) {
-                keep = true;
-            } else {
-                exact_walk<-1, false, false>(tab, ref + r, qry + q, sp.xdrop, sp.T - R, L, ext);
-                keep = (int64_t)R + L >= (int64_t)sp.T;
-            }
-        }
+        const bool keep = exact_flag(tab, ref, qry, anchors[i], sp);
         if (lane_id() == 0) flags[i] = keep ? 1 : 0;
     }
 }
@@ -241,6 +244,7 @@ constexpr int kNarrowRight = 4, kNarrowLeft = 7;
 constexpr int kStage2Right = 8, kStage2Left = 12;
 constexpr int kSeg = 512;   // LDS slots per wave for deferred anchor indices
 constexpr int kSegKg = 256;  // the same with anchors, in the key-grouped stage
+constexpr int kXPool = 128;  // anchors per workgroup for its own exact walks
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -491,8 +495,16 @@ __device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_
 // waits on them.  A deferred slot's anchor is stored unless its flag is 0 (the exact list
 // reads it there); flags already hold 0 when ZeroSet.  Anchors the wider windows leave
 // undecided go to the exact list.  Segments a wave flushed to the global list on the way
-// are left to the separate second stage.  cnt[1] counts the exact list, cnt[2] the
-// anchors pooled here.
+// are left to the separate second stage.  The anchors the wider windows leave go on, up
+// to kXPool of them, to the exact walk the workgroup then runs itself (one wave per
+// anchor, as the exact list does), the rest to the exact list.  cnt[1] counts the exact
+// list, cnt[2] the anchors pooled here, cnt[3] the exact walks pooled here.
+struct ExactPool {
+    uint32_t slot[kXPool];
+    uint64_t a[kXPool];
+    uint32_t n;  // reserved entries (may exceed kXPool: those went to the exact list)
+};
+
 template <int S, bool ZeroSet>
 __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint64_t (*sega)[S],
                                             uint32_t *seg_n, uint32_t nseg, const int16_t *tab,
@@ -501,7 +513,10 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
                                             const uint32_t *__restrict__ ref4,
                                             const uint32_t *__restrict__ qry4,
                                             const WindowParams &wp, uint32_t *__restrict__ list2,
-                                            uint32_t *__restrict__ cnt) {
+                                            uint32_t *__restrict__ cnt, ExactPool &xp,
+                                            const int32_t *tab32, const uint8_t *__restrict__ ref8,
+                                            const uint8_t *__restrict__ qry8,
+                                            const ScoreParams &sp) {
     static_assert(kWaves == 4, "four wave segments");
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
@@ -540,10 +555,29 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
         const uint64_t m = __ballot(valid && res == 2);
         if (m) {
             uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(cnt + 1, (uint32_t)__popcll(m));
+            if (lane == 0) base = atomicAdd(&xp.n, (uint32_t)__popcll(m));
             base = __shfl(base, 0, 64);
-            if (valid && res == 2) list2[base + lane_rank(m)] = slot;
+            const uint32_t k = base + (uint32_t)lane_rank(m);
+            const bool pooled = k < (uint32_t)kXPool;
+            if (valid && res == 2 && pooled) {
+                xp.slot[k] = slot;
+                xp.a[k] = a;
+            }
+            const uint64_t m2 = __ballot(valid && res == 2 && !pooled);
+            if (m2) {
+                uint32_t b2 = 0;
+                if (lane == 0) b2 = atomicAdd(cnt + 1, (uint32_t)__popcll(m2));
+                b2 = __shfl(b2, 0, 64);
+                if (valid && res == 2 && !pooled) list2[b2 + lane_rank(m2)] = slot;
+            }
         }
+    }
+    __syncthreads();
+    const uint32_t nx = min(xp.n, (uint32_t)kXPool);
+    if (threadIdx.x == 0 && nx) atomicAdd(cnt + 3, nx);  // the pooled exact walks
+    for (uint32_t e = (uint32_t)w; e < nx; e += kWaves) {  // uniform
+        const bool keep = exact_flag(tab32, ref8, qry8, xp.a[e], sp);
+        if (lane == 0 && (keep || !ZeroSet)) flags[xp.slot[e]] = keep ? 1 : 0;
     }
 }
 
@@ -582,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
 
 // Directory of the fused first stage: the seed that owns the first slot of each wave's
 // range, i.e. the first seed whose prefix - hit_lo exceeds that slot (a binary search).
-// The first thread also clears the three deferred-list counters the stages append to.
+// The first thread also clears the four deferred-list counters the stages append to.
 __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n_waves,
                                                        uint32_t steps,
                                                        uint32_t *__restrict__ cnt) {
@@ -591,6 +625,7 @@ __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n
         cnt[0] = 0;
         cnt[1] = 0;
         cnt[2] = 0;
+        cnt[3] = 0;
     }
     if (w >= n_waves) return;
     const uint32_t t = w * (64u * steps);
@@ -617,8 +652,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint64_t *__restrict__ defer_a,
-    uint32_t *__restrict__ defer_cnt, uint32_t *__restrict__ list2) {
+    uint32_t *__restrict__ defer_cnt, uint32_t *__restrict__ list2, ScoreParams sp,
+    const uint8_t *__restrict__ ref8, const uint8_t *__restrict__ qry8) {
     __shared__ int16_t tab[kWinTab];
+    __shared__ int32_t tab32[kTabSize];  // the exact walks' table
+    __shared__ ExactPool xp;
     __shared__ uint32_t seg[kWaves][kSegKg];
     __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
@@ -626,6 +664,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     __shared__ uint32_t fst[kWaves][64];  // their bucket starts
     __shared__ uint32_t qen[kWaves][64];  // their query ends
     if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    if (threadIdx.x < kTabSize) tab32[threadIdx.x] = sp.tab[threadIdx.x];
+    if (threadIdx.x == 0) xp.n = 0;
     __syncthreads();
 
     const int lane = lane_id();
@@ -686,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
                                    defer_a, defer_cnt);
     }
     stage2_pool<kSegKg, false>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
-                               list2, defer_cnt);
+                               list2, defer_cnt, xp, tab32, ref8, qry8, sp);
 }
 
 // ------------------------------------------------------------------ key-grouped first stage
@@ -790,6 +830,7 @@ __global__ __launch_bounds__(kThreads) void k_kg_dir(KgScratch ks, uint32_t n_ru
         cnt[0] = 0;
         cnt[1] = 0;
         cnt[2] = 0;
+        cnt[3] = 0;
     }
     if (w >= n_waves) return;
     const uint32_t t = w * (64u * steps);
@@ -821,14 +862,19 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint64_t *__restrict__ defer_a,
-    uint32_t *__restrict__ defer_cnt, uint32_t *__restrict__ list2) {
+    uint32_t *__restrict__ defer_cnt, uint32_t *__restrict__ list2, ScoreParams sp,
+    const uint8_t *__restrict__ ref8, const uint8_t *__restrict__ qry8) {
     __shared__ int16_t tab[kWinTab];
+    __shared__ int32_t tab32[kTabSize];  // the exact walks' table
+    __shared__ ExactPool xp;
     __shared__ uint32_t seg[kWaves][kSegKg];
     __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
     __shared__ KgRun run[kWaves][64];    // the wave's window of runs
     __shared__ uint32_t mk[kWaves][64];  // marks of the step's positions (run index)
     if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
+    if (threadIdx.x < kTabSize) tab32[threadIdx.x] = sp.tab[threadIdx.x];
+    if (threadIdx.x == 0) xp.n = 0;
     __syncthreads();
 
     const int lane = lane_id();
@@ -953,7 +999,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
                                    defer_a, defer_cnt);
     }
     stage2_pool<kSegKg, true>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
-                              list2, defer_cnt);
+                              list2, defer_cnt, xp, tab32, ref8, qry8, sp);
 }
 
 // First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
@@ -1046,11 +1092,13 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
     defer_flush_block(seg, seg_n, &blk_base, nseg, defer, defer_cnt);
 }
 
-// Clears the deferred-list counters: second stage, exact list, pooled second stage.
+// Clears the deferred-list counters: second stage, exact list, pooled second stage,
+// pooled exact walks.
 __global__ void k_zero_counts(uint32_t *p) {
     p[0] = 0;
     p[1] = 0;
     p[2] = 0;
+    p[3] = 0;
 }
 
 
@@ -1151,7 +1199,8 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
                                     const uint32_t *qry4, const WindowParams &wp,
                                     uint32_t *list1, uint64_t *list1_a, uint32_t *list2,
-                                    uint32_t *cnt, hipStream_t s) {
+                                    uint32_t *cnt, const ScoreParams &sp, const uint8_t *ref8,
+                                    const uint8_t *qry8, hipStream_t s) {
     if (n == 0) {
         hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
@@ -1164,11 +1213,11 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
     if (narrow)
         hipLaunchKernelGGL((k_gate_window_fused<kNarrowRight, kNarrowLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, list1_a, cnt, list2);
+                           list1, list1_a, cnt, list2, sp, ref8, qry8);
     else
         hipLaunchKernelGGL((k_gate_window_fused<kWideRight, kWideLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, list1_a, cnt, list2);
+                           list1, list1_a, cnt, list2, sp, ref8, qry8);
     launch_stage2(narrow, true, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors,
                   list2, cnt, s);
     return hipGetLastError();
@@ -1180,7 +1229,8 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const uint32_t *pos, uint64_t *anchors, uint8_t *flags,
                                  const uint32_t *ref4, const uint32_t *qry4,
                                  const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
-                                 uint32_t *list2, uint32_t *cnt, hipStream_t s) {
+                                 uint32_t *list2, uint32_t *cnt, const ScoreParams &sp,
+                                 const uint8_t *ref8, const uint8_t *qry8, hipStream_t s) {
     if (n == 0 || kg.n_runs == 0) {
         hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
@@ -1198,7 +1248,7 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
     const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
     hipLaunchKernelGGL((k_gate_window_kg<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads), 0,
                        s, kg, ks, prefix, batch_lo, hit_lo, n, steps, pos, anchors, flags, ref4,
-                       qry4, wp, list1, list1_a, cnt, list2);
+                       qry4, wp, list1, list1_a, cnt, list2, sp, ref8, qry8);
     launch_stage2(false, true, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors,
                   list2, cnt, s);
     return hipGetLastError();
