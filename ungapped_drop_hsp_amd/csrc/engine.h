@@ -127,6 +127,7 @@ struct Engine {
     uint64_t h_rec_cap = 0, h_rec_n = 0;
     hipEvent_t gate_ev[4] = {nullptr, nullptr, nullptr, nullptr};
     hipEvent_t count_ev[2] = {nullptr, nullptr};  // survivor and record counts landed
+    hipEvent_t plan_ev = nullptr;                  // the plan's copy to the host landed
     // the records' copies to the host run on their own stream (default priority) and
     // overlap the next chunks; copied_ev[b] marks the copy out of rb_out[b]
     hipStream_t copy_s = nullptr;

@@ -1,6 +1,7 @@
 // Host side of libhspz: parameter validation, the keep threshold, reference index and
 // query seed construction, the plan (prefix and MAX_HITS chunk walk) and the C ABI.
 #include <algorithm>
+#include <functional>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -212,7 +213,10 @@ int host_walk(Engine *e, uint64_t n, uint64_t total, const std::vector<uint64_t>
 // chunk walk run on the device, and one copy brings back the total and the chunk list.
 // chunk_walk = 1: the host scans the block sums and walks the whole prefix.  A total
 // over 2^32 - 1 is refused either way.
-int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint32_t *n_chunks) {
+// queued is called, when not null, once the plan's copy to the host is queued and before
+// the host waits for it: work it queues runs while the host waits.
+int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint32_t *n_chunks,
+                const std::function<int()> &queued) {
     const uint64_t nblk = (n + kScanBlock - 1) / kScanBlock;
     e->chunks.clear();
     std::vector<uint64_t> incl;  // inclusive block sums, for the host walk
@@ -244,7 +248,10 @@ int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint
                                      e->d_plan, s));
         HIP_TRY(e, hipMemcpyAsync(e->h_plan, e->d_plan, sizeof(PlanBuf), hipMemcpyDeviceToHost,
                                   s));
-        HIP_TRY(e, hipStreamSynchronize(s));
+        if (!e->plan_ev) HIP_TRY(e, hipEventCreateWithFlags(&e->plan_ev, hipEventDisableTiming));
+        HIP_TRY(e, hipEventRecord(e->plan_ev, s));
+        if (queued && (rc = queued())) return rc;
+        HIP_TRY(e, hipEventSynchronize(e->plan_ev));
         total = e->h_plan->info.total;
         if (total > 0xFFFFFFFFull) return refuse(total);
         const uint32_t nc = e->h_plan->info.n_chunks;
@@ -267,6 +274,7 @@ int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint
         }
     }
     if (!walked && (rc = host_walk(e, n, total, incl, s))) return rc;
+    if (e->params.chunk_walk != 0 && queued && (rc = queued())) return rc;
     e->total = total;
     e->has_plan = true;
     *total_hits = total;
@@ -482,6 +490,7 @@ Engine::~Engine() {
         if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : copied_ev)
         if (ev) (void)hipEventDestroy(ev);
+    if (plan_ev) (void)hipEventDestroy(plan_ev);
     if (copy_s) (void)hipStreamDestroy(copy_s);
     if (h_pinned) (void)hipHostFree(h_pinned);
     if (h_plan) (void)hipHostFree(h_plan);
@@ -838,8 +847,10 @@ static int impl_hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint
     return HSPZ_OK;
 }
 
-static int impl_hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
-                          uint64_t *total_hits, uint32_t *n_chunks) {
+// hspz_plan, with finish_plan's queued hook (hspz_run_batch queues work there).
+static int plan_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
+                      uint64_t *total_hits, uint32_t *n_chunks,
+                      const std::function<int()> &queued) {
     Engine *e = reinterpret_cast<Engine *>(engine);
     if (!e) return HSPZ_E_INVALID;
     if (!total_hits || !n_chunks) return fail(e, HSPZ_E_INVALID, "NULL output");
@@ -861,7 +872,7 @@ static int impl_hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_h
     e->batch_n = n;
     HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_ctab,
                                  e->d_count, e->d_first, e->d_prefix, e->d_blksum, s));
-    rc = finish_plan(e, n, s, total_hits, n_chunks);
+    rc = finish_plan(e, n, s, total_hits, n_chunks, queued);
     if (rc) {
         *total_hits = 0;
         *n_chunks = 0;
@@ -869,6 +880,11 @@ static int impl_hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_h
     }
     e->plan_expandable = true;
     return HSPZ_OK;
+}
+
+static int impl_hspz_plan(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
+                          uint64_t *total_hits, uint32_t *n_chunks) {
+    return plan_batch(engine, seed_lo, seed_hi, stream, total_hits, n_chunks, nullptr);
 }
 
 static int impl_hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_counts, uint64_t n,
@@ -893,7 +909,7 @@ static int impl_hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_co
         HIP_TRY(e, launch_count_scan(nullptr, e->d_count, n, nullptr, nullptr, e->d_count,
                                      nullptr, e->d_prefix, e->d_blksum, s));
     }
-    rc = finish_plan(e, n, s, total_hits, n_chunks);
+    rc = finish_plan(e, n, s, total_hits, n_chunks, nullptr);
     if (rc) {
         *total_hits = 0;
         *n_chunks = 0;
@@ -1150,23 +1166,34 @@ static bool key_grouped_suits(const Engine *e, uint64_t n_seeds) {
 // the batch's slots hit_lo .. hit_lo + n - 1, with the key-grouped first stage: flags
 // receives their n flags, anchors (indexed from hit_lo) the anchor of every slot whose
 // flag is 1.  A chunk of the plan, or the whole batch (hspz_run_batch).
+static KeyGroups key_groups(const Engine *e) {
+    return KeyGroups{e->d_kg_qs,        e->d_kg_qe,       e->d_kg_run_c,
+                     e->d_kg_run_first, e->d_kg_run_span, e->kg_n_runs};
+}
+
+static KgScratch kg_scratch(const Engine *e) {
+    return KgScratch{e->d_kg_G,      e->d_kg_a,      e->d_kg_m,   e->d_kg_dir,
+                     e->d_kg_blksum, e->d_kg_blkoff, e->d_kg_info};
+}
+
+// groups_ready: the grouping pass for this seed range is already queued (hspz_run_batch
+// queues it while the host waits for the plan).
 static int gate_key_grouped(Engine *e, uint64_t seed_lo, uint64_t seed_hi, uint64_t hit_lo,
-                            uint64_t n, uint64_t *d_anchors, uint8_t *d_flags, hipStream_t s) {
+                            uint64_t n, uint64_t *d_anchors, uint8_t *d_flags, hipStream_t s,
+                            bool groups_ready = false) {
     int rc;
     if ((rc = ensure_defer(e, n)) || (rc = ensure_defer_anchors(e)) ||
         (rc = ensure_kg(e, gate_window_waves(n))))
         return rc;
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
-    KeyGroups g{e->d_kg_qs,          e->d_kg_qe,       e->d_kg_run_c,
-                e->d_kg_run_first,   e->d_kg_run_span, e->kg_n_runs};
-    KgScratch ks{e->d_kg_G, e->d_kg_a, e->d_kg_m, e->d_kg_dir, e->d_kg_blksum,
-                 e->d_kg_blkoff, e->d_kg_info};
+    const KeyGroups g = key_groups(e);
+    const KgScratch ks = kg_scratch(e);
     HIP_TRY(e, launch_gate_window_kg(g, ks, e->d_prefix, (uint32_t)e->batch_lo,
                                      (uint32_t)seed_lo, (uint32_t)seed_hi, (uint32_t)hit_lo,
                                      (uint32_t)n, e->d_pos, d_anchors, d_flags, e->d_ref4,
                                      e->d_qry4, e->wp, list1, e->d_defer_a, list2,
                                      e->d_defer_cnt, e->sp, e->d_ref + kPad, e->d_qry + kPad,
-                                     s));
+                                     groups_ready, s));
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;
@@ -1516,7 +1543,29 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
     hipStream_t s = as_stream(stream);
     uint64_t total = 0;
     uint32_t nch = 0;
-    int rc = hspz_plan(engine, seed_lo, seed_hi, stream, &total, &nch);
+    if (time_gate)
+        for (hipEvent_t &ev : e->gate_ev)
+            if (!ev) HIP_TRY(e, hipEventCreate(&ev));
+    // A batch of large MAX_HITS chunks (below) is gated at once with the key-grouped
+    // stage, whose first pass depends on the seed range alone: it is queued behind the
+    // plan's copy to the host, so that it runs while the host waits for the plan.
+    bool spec = false;
+    auto queued = [&]() -> int {
+        if (!(key_grouped_suits(e, seed_hi - seed_lo) && seed_hi > seed_lo &&
+              (e->params.max_hits == 0 || e->params.max_hits >= kWholeChunkMin)))
+            return HSPZ_OK;
+        if (ensure_kg(e, 0) != HSPZ_OK) {  // not enough memory now: no head start
+            (void)hipGetLastError();
+            e->err.clear();
+            return HSPZ_OK;
+        }
+        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
+        HIP_TRY(e, launch_kg_groups(key_groups(e), kg_scratch(e), (uint32_t)seed_lo,
+                                    (uint32_t)(seed_hi - 1), s));
+        spec = true;
+        return HSPZ_OK;
+    };
+    int rc = plan_batch(engine, seed_lo, seed_hi, stream, &total, &nch, queued);
     if (rc) return rc;
     stats->n_anchors = total;
     stats->n_chunks = nch;
@@ -1570,16 +1619,13 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
             e->copy_pending[0] = e->copy_pending[1] = false;
         }
     } drain{e};
-    if (time_gate)
-        for (hipEvent_t &ev : e->gate_ev)
-            if (!ev) HIP_TRY(e, hipEventCreate(&ev));
 
     stats->whole_batch_gate = whole ? 1 : 0;
     if (whole) {
-        if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
+        if (time_gate && !spec) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
         if ((rc = set_device(e)) ||
             (rc = gate_key_grouped(e, e->batch_lo, e->batch_lo + e->batch_n - 1, 0, total,
-                                   e->bb_anchors, e->bb_flags, s)))
+                                   e->bb_anchors, e->bb_flags, s, spec)))
             return rc;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[1], s));
         // The survivors of every chunk at once: their ids are batch slots, ascending, so
@@ -1597,19 +1643,18 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
             stats->gate_ms = ms;
             stats->gate_calls = 1;
         }
-        if ((rc = ensure_run_buffers(e, 0, ns)) ||
-            (rc = materialize(e, e->bb_anchors, e->bb_ids, ns, e->rb_hsp, e->rb_status, true,
-                              stream)) ||
-            (rc = count_queue(e, e->rb_status, ns, nullptr, e->rb_hsp, e->rb_out[0],
-                              e->rb_cap_s, 1, s)) ||
-            (rc = count_wait(e, 1, e->rb_cap_s, &na)))
+        // the accepted records are compacted straight into the pinned host staging (sized
+        // for every survivor), so the host's one wait, for their count, ends the batch
+        if ((rc = ensure_run_buffers(e, 0, ns)) || (rc = ensure_record_staging(e, ns, 0, s)))
             return rc;
-        if (na) {
-            if ((rc = ensure_record_staging(e, na, 0, s))) return rc;
-            HIP_TRY(e, hipMemcpyAsync(e->h_rec, e->rb_out[0], na * sizeof(hspz_segment_pair),
-                                      hipMemcpyDeviceToHost, s));
-        }
-        HIP_TRY(e, hipStreamSynchronize(s));
+        hspz_segment_pair *d_rec = nullptr;
+        HIP_TRY(e, hipHostGetDevicePointer(reinterpret_cast<void **>(&d_rec), e->h_rec, 0));
+        if ((rc = materialize(e, e->bb_anchors, e->bb_ids, ns, e->rb_hsp, e->rb_status, true,
+                              stream)) ||
+            (rc = count_queue(e, e->rb_status, ns, nullptr, e->rb_hsp, d_rec, e->h_rec_cap, 1,
+                              s)) ||
+            (rc = count_wait(e, 1, e->h_rec_cap, &na)))
+            return rc;
         stats->n_survivors = ns;
         stats->n_accepted = na;
         e->h_rec_n = na;

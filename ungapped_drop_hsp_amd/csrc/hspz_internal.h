@@ -233,7 +233,13 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const uint32_t *ref4, const uint32_t *qry4,
                                  const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
                                  uint32_t *list2, uint32_t *cnt, const ScoreParams &sp,
-                                 const uint8_t *ref8, const uint8_t *qry8, hipStream_t s);
+                                 const uint8_t *ref8, const uint8_t *qry8, bool groups_ready,
+                                 hipStream_t s);
+// The grouping pass of launch_gate_window_kg alone (k_kg_groups and the scan of its block
+// sums), for seeds seed_lo .. seed_hi; launch_gate_window_kg with groups_ready set then
+// starts after it.
+hipError_t launch_kg_groups(const KeyGroups &kg, const KgScratch &ks, uint32_t seed_lo,
+                            uint32_t seed_hi, hipStream_t s);
 // Bucketed gate ("D. Score gate", D.5): stable sort of anchors by reference slice
 // (k_bucket.hip) and the first window stage over the sorted anchors (k_gate.hip).
 uint32_t bucket_blocks(uint32_t n);  // workgroups of the slice histogram and scatter

@@ -1223,6 +1223,14 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
     return hipGetLastError();
 }
 
+hipError_t launch_kg_groups(const KeyGroups &kg, const KgScratch &ks, uint32_t seed_lo,
+                            uint32_t seed_hi, hipStream_t s) {
+    if (kg.n_runs == 0) return hipSuccess;
+    const uint32_t nblk = (kg.n_runs + kScanBlock - 1) / kScanBlock;
+    hipLaunchKernelGGL(k_kg_groups, dim3(nblk), dim3(kKgThreads), 0, s, kg, seed_lo, seed_hi, ks);
+    return launch_scan_blocks(ks.blksum, nblk, ks.blkoff, ks.info, s);
+}
+
 hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const uint32_t *prefix, uint32_t batch_lo, uint32_t seed_lo,
                                  uint32_t seed_hi, uint32_t hit_lo, uint32_t n,
@@ -1230,16 +1238,16 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const uint32_t *ref4, const uint32_t *qry4,
                                  const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
                                  uint32_t *list2, uint32_t *cnt, const ScoreParams &sp,
-                                 const uint8_t *ref8, const uint8_t *qry8, hipStream_t s) {
+                                 const uint8_t *ref8, const uint8_t *qry8, bool groups_ready,
+                                 hipStream_t s) {
     if (n == 0 || kg.n_runs == 0) {
         hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
     }
     const uint32_t nr = kg.n_runs;
-    const uint32_t nblk = (nr + kScanBlock - 1) / kScanBlock;
-    hipLaunchKernelGGL(k_kg_groups, dim3(nblk), dim3(kKgThreads), 0, s, kg, seed_lo, seed_hi, ks);
-    hipError_t st = launch_scan_blocks(ks.blksum, nblk, ks.blkoff, ks.info, s);
-    if (st != hipSuccess) return st;
+    hipError_t st;
+    if (!groups_ready && (st = launch_kg_groups(kg, ks, seed_lo, seed_hi, s)) != hipSuccess)
+        return st;
     const uint32_t steps = gate_window_steps(n);
     const uint32_t n_waves = (uint32_t)gate_window_waves(n);
     hipLaunchKernelGGL(k_kg_dir, dim3((n_waves + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
