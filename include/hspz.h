@@ -212,9 +212,10 @@ int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
 
 /* Plan one batch, seeds [seed_lo, seed_hi) ("C. Hit discovery", C.1-C.3): count each
  * seed's hits, scan blocks of counts on the device, exclusive-scan the block sums in
- * 64 bits on the device, add the offsets back to form the global inclusive prefix, and
- * cut MAX_HITS chunks with the lower-bound walk (a seed is never split), also on the
- * device; one copy brings back the total and the chunk list.  A batch whose total
+ * 64 bits on the device (the global inclusive prefix is a block's local prefix plus its
+ * offset; the library adds the offset wherever it reads a prefix), and cut MAX_HITS
+ * chunks with the lower-bound walk (a seed is never split), also on the device; one copy
+ * brings back the total and the chunk list.  A batch whose total
  * exceeds 2^32 - 1 is refused with HSPZ_E_OVERFLOW and leaves no plan.
  * *total_hits and *n_chunks receive the totals (0 chunks when the total is 0).
  * Synchronises stream.  Errors: HSPZ_E_STATE (no reference/query), HSPZ_E_INVALID,

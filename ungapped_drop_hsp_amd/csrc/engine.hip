@@ -158,8 +158,9 @@ int seed_windows(Engine *e, const uint8_t *h_ascii, uint64_t len, int strand, in
 
 // Host half of the MAX_HITS walk ("C. Hit discovery", C.3), for chunk_walk = 1 and for
 // plans with more than kChunkCap chunks.  incl holds the inclusive block sums; the
-// prefix on the device is final.  With chunk_walk = 1 the whole prefix is copied back;
-// otherwise one 1,024-entry prefix block is copied per boundary.
+// device holds block-local prefixes, to which the host adds the block offsets.  With
+// chunk_walk = 1 the whole prefix is copied back; otherwise one 1,024-entry prefix block is
+// copied per boundary.
 int host_walk(Engine *e, uint64_t n, uint64_t total, const std::vector<uint64_t> &incl,
               hipStream_t s) {
     const uint64_t MAX = e->params.max_hits;
@@ -170,6 +171,10 @@ int host_walk(Engine *e, uint64_t n, uint64_t total, const std::vector<uint64_t>
                                   hipMemcpyDeviceToHost, s));
     }
     HIP_TRY(e, hipStreamSynchronize(s));
+    for (uint64_t i = 0; i < full.size(); i++) {
+        const uint64_t b = i / kScanBlock;
+        full[i] += (uint32_t)(b ? incl[b - 1] : 0);
+    }
     std::vector<uint32_t> blkvals(kScanBlock);
     uint64_t s0 = 0, H = 0;
     while (total > 0 && s0 < n) {
@@ -193,6 +198,7 @@ int host_walk(Engine *e, uint64_t n, uint64_t total, const std::vector<uint64_t>
             const uint64_t lo = b * kScanBlock, cnt = std::min<uint64_t>(kScanBlock, n - lo);
             HIP_TRY(e, hipMemcpy(blkvals.data(), e->d_prefix + lo, cnt * sizeof(uint32_t),
                                  hipMemcpyDeviceToHost));
+            for (uint64_t j = 0; j < cnt; j++) blkvals[j] += (uint32_t)(b ? incl[b - 1] : 0);
             eidx = lo + (uint64_t)(std::lower_bound(blkvals.begin(), blkvals.begin() + cnt,
                                                     target) - blkvals.begin());
         }
@@ -243,9 +249,8 @@ int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint
     int rc;
     if (e->params.chunk_walk == 0) {
         HIP_TRY(e, launch_scan_blocks(e->d_blksum, nblk, e->d_blkoff, &e->d_plan->info, s));
-        HIP_TRY(e, launch_add_offsets(e->d_prefix, n, e->d_blkoff, s));
-        HIP_TRY(e, launch_chunk_walk(e->d_prefix, n, e->params.max_hits, e->batch_lo,
-                                     e->d_plan, s));
+        HIP_TRY(e, launch_chunk_walk(PrefixView{e->d_prefix, e->d_blkoff, 0}, n,
+                                     e->params.max_hits, e->batch_lo, e->d_plan, s));
         HIP_TRY(e, hipMemcpyAsync(e->h_plan, e->d_plan, sizeof(PlanBuf), hipMemcpyDeviceToHost,
                                   s));
         if (!e->plan_ev) HIP_TRY(e, hipEventCreateWithFlags(&e->plan_ev, hipEventDisableTiming));
@@ -270,7 +275,6 @@ int finish_plan(Engine *e, uint64_t n, hipStream_t s, uint64_t *total_hits, uint
         if (nblk) {
             HIP_TRY(e, hipMemcpyAsync(e->d_blkoff, off.data(), nblk * sizeof(uint32_t),
                                       hipMemcpyHostToDevice, s));
-            HIP_TRY(e, launch_add_offsets(e->d_prefix, n, e->d_blkoff, s));
         }
     }
     if (!walked && (rc = host_walk(e, n, total, incl, s))) return rc;
@@ -938,9 +942,16 @@ static int impl_hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_coun
         if (h_counts)
             HIP_TRY(e, hipMemcpy(h_counts, e->d_count, e->batch_n * sizeof(uint32_t),
                                  hipMemcpyDeviceToHost));
-        if (h_prefix)
+        if (h_prefix) {
+            // the device keeps block-local prefixes and the blocks' offsets
+            const uint64_t nblk = (e->batch_n + kScanBlock - 1) / kScanBlock;
+            std::vector<uint32_t> off(nblk);
             HIP_TRY(e, hipMemcpy(h_prefix, e->d_prefix, e->batch_n * sizeof(uint32_t),
                                  hipMemcpyDeviceToHost));
+            HIP_TRY(e, hipMemcpy(off.data(), e->d_blkoff, nblk * sizeof(uint32_t),
+                                 hipMemcpyDeviceToHost));
+            for (uint64_t i = 0; i < e->batch_n; i++) h_prefix[i] += off[i / kScanBlock];
+        }
     }
     return HSPZ_OK;
 }
@@ -1004,8 +1015,9 @@ static int impl_hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_
     else dense = c.n_hits >= 16 * ns;  // "C. Hit discovery", C.4 density rule
     const uint64_t local = c.seed_lo - e->batch_lo;
     HIP_TRY(e, launch_expand(dense, e->d_count + local, e->d_first + local,
-                             e->d_qend + c.seed_lo, e->d_prefix + local, ns, e->d_pos,
-                             (uint32_t)c.hit_lo, d_anchors, as_stream(stream)));
+                             e->d_qend + c.seed_lo,
+                             PrefixView{e->d_prefix + local, e->d_blkoff, (uint32_t)local}, ns,
+                             e->d_pos, (uint32_t)c.hit_lo, d_anchors, as_stream(stream)));
     return HSPZ_OK;
 }
 
@@ -1188,7 +1200,8 @@ static int gate_key_grouped(Engine *e, uint64_t seed_lo, uint64_t seed_hi, uint6
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
     const KeyGroups g = key_groups(e);
     const KgScratch ks = kg_scratch(e);
-    HIP_TRY(e, launch_gate_window_kg(g, ks, e->d_prefix, (uint32_t)e->batch_lo,
+    HIP_TRY(e, launch_gate_window_kg(g, ks, PrefixView{e->d_prefix, e->d_blkoff, 0},
+                                     (uint32_t)e->batch_lo,
                                      (uint32_t)seed_lo, (uint32_t)seed_hi, (uint32_t)hit_lo,
                                      (uint32_t)n, e->d_pos, d_anchors, d_flags, e->d_ref4,
                                      e->d_qry4, e->wp, list1, e->d_defer_a, list2,
@@ -1229,7 +1242,7 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     if ((rc = ensure_dir(e, n))) return rc;
     const uint64_t local = c.seed_lo - e->batch_lo;
     ChunkSeeds cs;
-    cs.prefix = e->d_prefix + local;
+    cs.prefix = PrefixView{e->d_prefix + local, e->d_blkoff, (uint32_t)local};
     cs.first = e->d_first + local;
     cs.q_end = e->d_qend + c.seed_lo;
     cs.pos = e->d_pos;

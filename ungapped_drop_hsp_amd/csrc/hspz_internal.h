@@ -125,14 +125,27 @@ struct PlanBuf {
 // offset to add to block b) and info->total.
 hipError_t launch_scan_blocks(const uint64_t *blksum, uint64_t nblk, uint32_t *blkoff,
                               PlanInfo *info, hipStream_t s);
-// Greedy MAX_HITS walk over the final inclusive prefix P[0..n) ("C. Hit discovery", C.3)
-// by one wave; chunk seed indices are offset by batch_lo.  Reads info->total and
-// writes buf->info.n_chunks and up to kChunkCap chunks.
-hipError_t launch_chunk_walk(const uint32_t *P, uint64_t n, uint64_t max_hits,
-                             uint64_t batch_lo, PlanBuf *buf, hipStream_t s);
+// The batch's inclusive prefix as the plan leaves it: block-local inclusive prefixes of
+// kScanBlock seeds (count_scan) and each block's exclusive offset (launch_scan_blocks),
+// added where a prefix is read instead of in a pass over the whole prefix.  at(i) is the
+// global inclusive prefix of seed base + i of the batch, for p = the local prefixes from
+// seed base on.
+struct PrefixView {
+    const uint32_t *p;
+    const uint32_t *blkoff;
+    uint32_t base;
+    __device__ __forceinline__ uint32_t at(uint64_t i) const {
+        return p[i] + blkoff[((uint64_t)base + i) / kScanBlock];
+    }
+};
+// Greedy MAX_HITS walk over the inclusive prefix P[0..n) ("C. Hit discovery", C.3) by one
+// wave; chunk seed indices are offset by batch_lo.  Reads info->total and writes
+// buf->info.n_chunks and up to kChunkCap chunks.
+hipError_t launch_chunk_walk(PrefixView P, uint64_t n, uint64_t max_hits, uint64_t batch_lo,
+                             PlanBuf *buf, hipStream_t s);
 // Expand the seeds of one chunk (count, first, prefix and q_end of its seeds).
 hipError_t launch_expand(bool dense, const uint32_t *count, const uint32_t *first,
-                         const uint32_t *q_end, const uint32_t *prefix, uint64_t n_seeds,
+                         const uint32_t *q_end, PrefixView prefix, uint64_t n_seeds,
                          const uint32_t *pos, uint32_t hit_lo, uint64_t *anchors,
                          hipStream_t s);
 hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uint8_t *flags,
@@ -151,7 +164,7 @@ hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, 
 // bucket starts and query ends, the index bucket array, and the directory of the seed
 // that owns the first slot of each wave's range (filled by the launcher).
 struct ChunkSeeds {
-    const uint32_t *prefix;
+    PrefixView prefix;
     const uint32_t *first;
     const uint32_t *q_end;
     const uint32_t *pos;
@@ -227,7 +240,7 @@ hipError_t launch_kg_run_span(const uint32_t *qs, uint32_t n, const uint32_t *ru
 // list and the materializer read).  prefix is the batch's inclusive prefix (batch_lo = its
 // first seed).
 hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
-                                 const uint32_t *prefix, uint32_t batch_lo, uint32_t seed_lo,
+                                 PrefixView prefix, uint32_t batch_lo, uint32_t seed_lo,
                                  uint32_t seed_hi, uint32_t hit_lo, uint32_t n,
                                  const uint32_t *pos, uint64_t *anchors, uint8_t *flags,
                                  const uint32_t *ref4, const uint32_t *qry4,

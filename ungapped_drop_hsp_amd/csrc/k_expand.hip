@@ -26,7 +26,7 @@ constexpr int kGroup = 16;
 
 __global__ __launch_bounds__(kThreads) void k_expand_sparse(
     const uint32_t *__restrict__ count, const uint32_t *__restrict__ first,
-    const uint32_t *__restrict__ q_end, const uint32_t *__restrict__ prefix, uint64_t n_seeds,
+    const uint32_t *__restrict__ q_end, PrefixView prefix, uint64_t n_seeds,
     const uint32_t *__restrict__ pos, uint32_t hit_lo, uint64_t *__restrict__ anchors) {
     __shared__ uint32_t s_incl[kWaves][64];  // inclusive hit count over the wave's seeds
     __shared__ uint32_t s_b[kWaves][64];     // bucket start
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void k_expand_sparse(
     if (s < n_seeds) {
         cnt = count[s];
         b = first[s];
-        top = prefix[s] - 1u - hit_lo;
+        top = prefix.at(s) - 1u - hit_lo;
         qe = q_end[s];
     }
     const uint32_t incl = wave_incl_sum_u32(cnt);
@@ -68,14 +68,14 @@ __global__ __launch_bounds__(kThreads) void k_expand_sparse(
 
 __global__ __launch_bounds__(kThreads) void k_expand_dense(
     const uint32_t *__restrict__ count, const uint32_t *__restrict__ first,
-    const uint32_t *__restrict__ q_end, const uint32_t *__restrict__ prefix, uint64_t n_seeds,
+    const uint32_t *__restrict__ q_end, PrefixView prefix, uint64_t n_seeds,
     const uint32_t *__restrict__ pos, uint32_t hit_lo, uint64_t *__restrict__ anchors) {
     const uint64_t s = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) / kGroup;
     const uint32_t g = threadIdx.x % kGroup;
     if (s >= n_seeds) return;
     const uint32_t cnt = count[s];
     const uint32_t b = first[s];
-    const uint32_t slot0 = prefix[s] - 1u - hit_lo;
+    const uint32_t slot0 = prefix.at(s) - 1u - hit_lo;
     const uint64_t hi = (uint64_t)q_end[s] << 32;
     for (uint32_t j = g; j < cnt; j += kGroup) anchors[slot0 - j] = (uint64_t)pos[b + j] | hi;
 }
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void k_expand_dense(
 }  // namespace
 
 hipError_t launch_expand(bool dense, const uint32_t *count, const uint32_t *first,
-                         const uint32_t *q_end, const uint32_t *prefix, uint64_t n_seeds,
+                         const uint32_t *q_end, PrefixView prefix, uint64_t n_seeds,
                          const uint32_t *pos, uint32_t hit_lo, uint64_t *anchors,
                          hipStream_t s) {
     if (n_seeds == 0) return hipSuccess;

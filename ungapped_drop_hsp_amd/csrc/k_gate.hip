@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n
     uint32_t lo = 0, hi = cs.n_seeds;
     while (lo < hi) {
         const uint32_t mid = lo + (hi - lo) / 2;
-        if (cs.prefix[mid] - cs.hit_lo > t) hi = mid;
+        if (cs.prefix.at(mid) - cs.hit_lo > t) hi = mid;
         else lo = mid + 1;
     }
     cs.dir[w] = lo;
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
                 const uint32_t sj = wb + lane;
                 const bool in = sj < cs.n_seeds;
                 const uint32_t sr = in ? sj : cs.n_seeds - 1u;
-                const uint32_t pr = cs.prefix[sr], fs = cs.first[sr], qe = cs.q_end[sr];
+                const uint32_t pr = cs.prefix.at(sr), fs = cs.first[sr], qe = cs.q_end[sr];
                 rel[w][lane] = in ? pr - cs.hit_lo : 0xFFFFFFFFu;
                 fst[w][lane] = in ? fs : 0u;
                 qen[w][lane] = in ? qe : 0u;
@@ -857,7 +857,7 @@ struct KgRun {
 // runs leave at their first positions in the step, by a max-scan across the wave.
 template <int RB, int LB>
 __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
-    KeyGroups kg, KgScratch ks, const uint32_t *__restrict__ prefix, uint32_t batch_lo,
+    KeyGroups kg, KgScratch ks, PrefixView prefix, uint32_t batch_lo,
     uint32_t hit_lo, uint32_t n, uint32_t steps, const uint32_t *__restrict__ pos,
     uint64_t *__restrict__ anchors, uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
         const int res = win.decide(tab, wp);
         uint32_t slot = 0;
         if (valid && res != 0) {
-            slot = prefix[seed - batch_lo] - 1u - hit_lo - occ;
+            slot = prefix.at(seed - batch_lo) - 1u - hit_lo - occ;
             if (res == 1) {
                 anchors[slot] = a;
                 flags[slot] = 1;
@@ -1232,7 +1232,7 @@ hipError_t launch_kg_groups(const KeyGroups &kg, const KgScratch &ks, uint32_t s
 }
 
 hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
-                                 const uint32_t *prefix, uint32_t batch_lo, uint32_t seed_lo,
+                                 PrefixView prefix, uint32_t batch_lo, uint32_t seed_lo,
                                  uint32_t seed_hi, uint32_t hit_lo, uint32_t n,
                                  const uint32_t *pos, uint64_t *anchors, uint8_t *flags,
                                  const uint32_t *ref4, const uint32_t *qry4,

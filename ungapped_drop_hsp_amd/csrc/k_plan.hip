@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_blocks(const uint64_t *__
     if (t == 0) info->total = carry;
 }
 
-__global__ __launch_bounds__(64) void k_chunk_walk(const uint32_t *__restrict__ P, uint64_t n,
+__global__ __launch_bounds__(64) void k_chunk_walk(PrefixView P, uint64_t n,
                                                    uint64_t max_hits, uint64_t batch_lo,
                                                    PlanBuf *__restrict__ buf) {
     const int lane = lane_id();
@@ -270,16 +270,16 @@ __global__ __launch_bounds__(64) void k_chunk_walk(const uint32_t *__restrict__ 
                     const uint64_t step = (hi - lo + 64) / 64;  // ceil(span / 64)
                     const uint64_t idx = min(lo + (uint64_t)(lane + 1) * step - 1, hi);
                     // lane 63 reads P[hi] >= target, so the mask is never empty
-                    const uint64_t m = __ballot(P[idx] >= target);
+                    const uint64_t m = __ballot(P.at(idx) >= target);
                     const uint64_t f = (uint64_t)__builtin_ctzll(m);
                     hi = min(lo + (f + 1) * step - 1, hi);
                     lo = lo + f * step;
                 }
                 const uint64_t idx = lo + (uint64_t)lane;
-                const uint64_t m = __ballot(idx <= hi && P[min(idx, hi)] >= target);
+                const uint64_t m = __ballot(idx <= hi && P.at(min(idx, hi)) >= target);
                 e = lo + (uint64_t)__builtin_ctzll(m);
             }
-            const uint32_t Pe = P[e];
+            const uint32_t Pe = P.at(e);
             if (lane == 0 && c < kChunkCap) {
                 hspz_chunk ch;
                 ch.seed_lo = batch_lo + s0;
@@ -305,8 +305,8 @@ hipError_t launch_scan_blocks(const uint64_t *blksum, uint64_t nblk, uint32_t *b
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_walk(const uint32_t *P, uint64_t n, uint64_t max_hits,
-                             uint64_t batch_lo, PlanBuf *buf, hipStream_t s) {
+hipError_t launch_chunk_walk(PrefixView P, uint64_t n, uint64_t max_hits, uint64_t batch_lo,
+                             PlanBuf *buf, hipStream_t s) {
     hipLaunchKernelGGL(k_chunk_walk, dim3(1), dim3(64), 0, s, P, n, max_hits, batch_lo, buf);
     return hipGetLastError();
 }
