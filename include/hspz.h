@@ -335,9 +335,11 @@ typedef struct {
  * ids are batch slots, so the chunks' survivors come one chunk after another), one
  * materialization of them all (their anchors are in query order) and one copy of the
  * accepted records.  The records are the chunks' records in chunk order, as chunk by
- * chunk (stats->whole_batch_gate = 1).  Its engine buffers take 13 bytes per anchor
- * (flags, kept anchors, survivor ids) and the gate's deferred lists 20 more; where the
- * device cannot hold them the batch goes chunk by chunk.  With time_gate != 0 each expansion-and-gate call is
+ * chunk (stats->whole_batch_gate = 1).  Its engine buffers take about 12 bytes per
+ * anchor (a flag bit, kept anchors, survivor ids) and the gate's deferred lists 20 more;
+ * where the device cannot hold them the batch goes chunk by chunk.  The accepted records
+ * are compacted straight into the pinned host staging that hspz_get_batch_records reads.
+ * With time_gate != 0 each expansion-and-gate call is
  * bracketed by HIP events on stream and *stats reports their number and summed duration.
  * The plan stays current afterwards.  Synchronises stream.  Errors: as hspz_plan,
  * hspz_find_hits and the calls above; HSPZ_E_INVALID for a NULL stats pointer. */

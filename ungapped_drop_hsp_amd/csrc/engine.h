@@ -117,8 +117,8 @@ struct Engine {
     hspz_segment_pair *rb_out[2] = {nullptr, nullptr};  // accepted records, by chunk parity
     uint8_t *rb_status = nullptr;
     uint64_t rb_cap_s = 0;
-    // the whole-batch gate of hspz_run_batch: the batch's flags, kept anchors and
-    // survivor ids
+    // the whole-batch gate of hspz_run_batch: the batch's flags (a bit per anchor, 32-bit
+    // words), kept anchors and survivor ids
     uint8_t *bb_flags = nullptr;
     uint64_t *bb_anchors = nullptr;
     uint32_t *bb_ids = nullptr;

@@ -1189,10 +1189,11 @@ static KgScratch kg_scratch(const Engine *e) {
 }
 
 // groups_ready: the grouping pass for this seed range is already queued (hspz_run_batch
-// queues it while the host waits for the plan).
+// queues it while the host waits for the plan).  bits: d_flags holds a bit per anchor
+// (bit i % 32 of 32-bit word i / 32), for hspz_run_batch's own compaction.
 static int gate_key_grouped(Engine *e, uint64_t seed_lo, uint64_t seed_hi, uint64_t hit_lo,
                             uint64_t n, uint64_t *d_anchors, uint8_t *d_flags, hipStream_t s,
-                            bool groups_ready = false) {
+                            bool groups_ready = false, bool bits = false) {
     int rc;
     if ((rc = ensure_defer(e, n)) || (rc = ensure_defer_anchors(e)) ||
         (rc = ensure_kg(e, gate_window_waves(n))))
@@ -1206,9 +1207,9 @@ static int gate_key_grouped(Engine *e, uint64_t seed_lo, uint64_t seed_hi, uint6
                                      (uint32_t)n, e->d_pos, d_anchors, d_flags, e->d_ref4,
                                      e->d_qry4, e->wp, list1, e->d_defer_a, list2,
                                      e->d_defer_cnt, e->sp, e->d_ref + kPad, e->d_qry + kPad,
-                                     groups_ready, s));
+                                     groups_ready, bits, s));
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
-                                     e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
+                                     e->d_ref + kPad, e->d_qry + kPad, e->sp, s, bits));
     e->gate_deferred_valid = true;
     return HSPZ_OK;
 }
@@ -1486,7 +1487,8 @@ static int ensure_run_buffers(Engine *e, uint64_t n, uint64_t ns) {
 static int ensure_batch_buffers(Engine *e, uint64_t n) {
     if (n <= e->bb_cap && e->bb_flags) return HSPZ_OK;
     int rc;
-    if ((rc = dalloc(e, e->bb_flags, n + 16)) || (rc = dalloc(e, e->bb_anchors, n)) ||
+    // flags one bit per anchor (32-bit words)
+    if ((rc = dalloc(e, e->bb_flags, (n + 31) / 32 * 4 + 16)) || (rc = dalloc(e, e->bb_anchors, n)) ||
         (rc = dalloc(e, e->bb_ids, n))) {
         e->bb_cap = 0;
         return rc;
@@ -1519,7 +1521,7 @@ static int ensure_record_staging(Engine *e, uint64_t n, uint64_t keep, hipStream
 // with count_ev[slot] recorded behind the copy; count_wait() reads it back.
 static int count_queue(Engine *e, const uint8_t *flags, uint64_t n, uint32_t *ids,
                        const hspz_segment_pair *rin, hspz_segment_pair *rout, uint64_t cap,
-                       int slot, hipStream_t s) {
+                       int slot, hipStream_t s, bool bits = false) {
     if (n >= 0xFFFFFFFFull) return fail(e, HSPZ_E_INVALID, "n must be < 2^32");
     if ((n + kCompactBlock - 1) / kCompactBlock + 1 > e->cap_cblk)
         return fail(e, HSPZ_E_INVALID, "compaction scratch not sized for %llu",
@@ -1527,7 +1529,12 @@ static int count_queue(Engine *e, const uint8_t *flags, uint64_t n, uint32_t *id
     uint32_t *d_total = e->d_ctotal + 4 * (slot + 1);
     uint32_t *h_total = e->h_pinned + 16 + 4 * slot;
     const uint32_t c32 = (uint32_t)std::min<uint64_t>(cap, 0xFFFFFFFFull);
-    HIP_TRY(e, launch_compact(flags, (uint32_t)n, e->d_cblk, d_total, ids, rin, rout, c32, s));
+    if (bits)  // ids of the set bits (flags as 32-bit words)
+        HIP_TRY(e, launch_compact_bits(reinterpret_cast<const uint32_t *>(flags), (uint32_t)n,
+                                       e->d_cblk, d_total, ids, c32, s));
+    else
+        HIP_TRY(e, launch_compact(flags, (uint32_t)n, e->d_cblk, d_total, ids, rin, rout, c32,
+                                  s));
     HIP_TRY(e, hipMemcpyAsync(h_total, d_total, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
     HIP_TRY(e, hipEventRecord(e->count_ev[slot], s));
     return HSPZ_OK;
@@ -1638,7 +1645,7 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
         if (time_gate && !spec) HIP_TRY(e, hipEventRecord(e->gate_ev[0], s));
         if ((rc = set_device(e)) ||
             (rc = gate_key_grouped(e, e->batch_lo, e->batch_lo + e->batch_n - 1, 0, total,
-                                   e->bb_anchors, e->bb_flags, s, spec)))
+                                   e->bb_anchors, e->bb_flags, s, spec, true)))
             return rc;
         if (time_gate) HIP_TRY(e, hipEventRecord(e->gate_ev[1], s));
         // The survivors of every chunk at once: their ids are batch slots, ascending, so
@@ -1647,7 +1654,7 @@ static int impl_hspz_run_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t s
         // records leave in one copy -- the records of the chunks one after another.
         uint64_t ns = 0, na = 0;
         if ((rc = count_queue(e, e->bb_flags, total, e->bb_ids, nullptr, nullptr, e->bb_cap, 0,
-                              s)) ||
+                              s, true)) ||
             (rc = count_wait(e, 0, e->bb_cap, &ns)))
             return rc;
         if (time_gate) {

@@ -247,7 +247,7 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
                                  uint32_t *list2, uint32_t *cnt, const ScoreParams &sp,
                                  const uint8_t *ref8, const uint8_t *qry8, bool groups_ready,
-                                 hipStream_t s);
+                                 bool bits, hipStream_t s);
 // The grouping pass of launch_gate_window_kg alone (k_kg_groups and the scan of its block
 // sums), for seeds seed_lo .. seed_hi; launch_gate_window_kg with groups_ready set then
 // starts after it.
@@ -270,7 +270,7 @@ hipError_t launch_gate_window_bucketed(const uint64_t *anchors, uint32_t n, cons
 hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
                                  const uint32_t *count, uint32_t max_count, uint8_t *flags,
                                  const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
-                                 hipStream_t s);
+                                 hipStream_t s, bool bits = false);
 // ref: the padded byte reference past its padding (base 0), for the entropy decision;
 // ref4, qry4: the 4-bit copies (base b at padded nibble kPad4 + b), for the walks.
 hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint32_t n_surv,
@@ -280,6 +280,10 @@ hipError_t launch_materialize(const uint64_t *anchors, const uint32_t *ids, uint
 // Stable compaction: count non-zero bytes per block, scan block counts on the device
 // (total -> *d_total), then emit either the indices (ids != nullptr) or the selected
 // 16-byte records (rec_in/rec_out).
+// launch_compact for flags held one bit per element (bit i % 32 of word i / 32; bits past
+// n clear), listing the set ones' indices in ids.
+hipError_t launch_compact_bits(const uint32_t *bits, uint32_t n, uint32_t *blk,
+                               uint32_t *d_total, uint32_t *ids, uint32_t cap, hipStream_t s);
 hipError_t launch_compact(const uint8_t *flags, uint32_t n, uint32_t *blk, uint32_t *d_total,
                           uint32_t *ids, const hspz_segment_pair *rec_in,
                           hspz_segment_pair *rec_out, uint32_t cap, hipStream_t s);

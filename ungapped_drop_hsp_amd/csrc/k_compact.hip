@@ -153,7 +153,54 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint8_t *__restrict__ f
     }
 }
 
+// The same for flags held one bit per element: a workgroup's kCompactBlock flags are its
+// threads' 32-bit words, one each.
+__global__ __launch_bounds__(kThreads) void k_count_bits(const uint32_t *__restrict__ bits,
+                                                         uint32_t words,
+                                                         uint32_t *__restrict__ blk) {
+    __shared__ uint32_t sh[kThreads / 64];
+    const uint64_t w = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t c = w < words ? (uint32_t)__popc(bits[w]) : 0u;
+    uint32_t total;
+    block_excl_scan(c, sh, total);
+    if (threadIdx.x == 0) blk[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kThreads) void k_emit_bits(const uint32_t *__restrict__ bits,
+                                                        uint32_t words,
+                                                        const uint32_t *__restrict__ off,
+                                                        uint32_t *__restrict__ ids,
+                                                        uint32_t cap) {
+    __shared__ uint32_t sh[kThreads / 64];
+    const uint32_t b0 = off[blockIdx.x];
+    if (off[blockIdx.x + 1] == b0) return;  // no set flag in this block (uniform)
+    const uint64_t w = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint32_t v = w < words ? bits[w] : 0u;
+    uint32_t total;
+    uint32_t o = b0 + block_excl_scan((uint32_t)__popc(v), sh, total);
+    while (v) {
+        const uint32_t j = (uint32_t)__builtin_ctz(v);
+        if (o < cap) ids[o] = (uint32_t)(w * 32u + j);
+        o++;
+        v &= v - 1u;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_compact_bits(const uint32_t *bits, uint32_t n, uint32_t *blk,
+                               uint32_t *d_total, uint32_t *ids, uint32_t cap, hipStream_t s) {
+    const uint32_t nblk = (uint32_t)(((uint64_t)n + kCompactBlock - 1) / kCompactBlock);
+    const uint32_t words = (uint32_t)(((uint64_t)n + 31) / 32);
+    static_assert(kCompactBlock == 32 * kThreads, "one flag word per thread");
+    if (nblk > 0)
+        hipLaunchKernelGGL(k_count_bits, dim3(nblk), dim3(kThreads), 0, s, bits, words, blk);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, blk, nblk, d_total);
+    if (nblk > 0)
+        hipLaunchKernelGGL(k_emit_bits, dim3(nblk), dim3(kThreads), 0, s, bits, words, blk, ids,
+                           cap);
+    return hipGetLastError();
+}
 
 hipError_t launch_compact(const uint8_t *flags, uint32_t n, uint32_t *blk, uint32_t *d_total,
                           uint32_t *ids, const hspz_segment_pair *rec_in,

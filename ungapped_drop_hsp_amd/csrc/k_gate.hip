@@ -72,6 +72,17 @@ __device__ __forceinline__ void load8(const uint8_t *p, uint32_t &lo, uint32_t &
 
 constexpr int32_t kG0 = INT32_MAX;  // g of a zero drawdown
 
+// Sets an anchor's flag to 1 where the flags were cleared beforehand: a byte per anchor,
+// or with Bits a bit per anchor (bit slot % 32 of 32-bit word slot / 32), set atomically
+// since the words are shared.
+template <bool Bits>
+__device__ __forceinline__ void set_flag(uint8_t *__restrict__ flags, uint32_t slot) {
+    if (Bits)
+        atomicOr(reinterpret_cast<uint32_t *>(flags) + (slot >> 5), 1u << (slot & 31u));
+    else
+        flags[slot] = 1;
+}
+
 // One base: g = INT32_MAX - d becomes INT32_MAX - max(d - sg, 0).
 __device__ __forceinline__ int32_t dd_step(int32_t g, int32_t sg) {
     return __builtin_elementwise_add_sat(g, sg);
@@ -215,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_list_wave(const uint64_t *__r
                                                              uint8_t *__restrict__ flags,
                                                              const uint8_t *__restrict__ ref,
                                                              const uint8_t *__restrict__ qry,
-                                                             ScoreParams sp) {
+                                                             ScoreParams sp, int bits) {
     __shared__ int32_t tab[kTabSize];
     if (threadIdx.x < kTabSize) tab[threadIdx.x] = sp.tab[threadIdx.x];
     __syncthreads();
@@ -224,7 +235,13 @@ __global__ __launch_bounds__(kThreads) void k_gate_list_wave(const uint64_t *__r
     for (uint64_t t = (uint64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); t < total; t += nw) {
         const uint32_t i = list[t];
         const bool keep = exact_flag(tab, ref, qry, anchors[i], sp);
-        if (lane_id() == 0) flags[i] = keep ? 1 : 0;
+        if (lane_id() == 0) {
+            if (bits) {
+                if (keep) set_flag<true>(flags, i);
+            } else {
+                flags[i] = keep ? 1 : 0;
+            }
+        }
     }
 }
 
@@ -505,7 +522,7 @@ struct ExactPool {
     uint32_t n;  // reserved entries (may exceed kXPool: those went to the exact list)
 };
 
-template <int S, bool ZeroSet>
+template <int S, bool ZeroSet, bool Bits = false>
 __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint64_t (*sega)[S],
                                             uint32_t *seg_n, uint32_t nseg, const int16_t *tab,
                                             uint64_t *__restrict__ anchors,
@@ -518,6 +535,7 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
                                             const uint8_t *__restrict__ qry8,
                                             const ScoreParams &sp) {
     static_assert(kWaves == 4, "four wave segments");
+    static_assert(ZeroSet || !Bits, "bit flags are cleared beforehand");
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     if (lane == 0) seg_n[w] = nseg;
@@ -551,7 +569,11 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 0) anchors[slot] = a;
-        if (valid && (ZeroSet ? res == 1 : res != 2)) flags[slot] = (uint8_t)res;
+        if (Bits) {
+            if (valid && res == 1) set_flag<true>(flags, slot);
+        } else if (valid && (ZeroSet ? res == 1 : res != 2)) {
+            flags[slot] = (uint8_t)res;
+        }
         const uint64_t m = __ballot(valid && res == 2);
         if (m) {
             uint32_t base = 0;
@@ -577,7 +599,10 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
     if (threadIdx.x == 0 && nx) atomicAdd(cnt + 3, nx);  // the pooled exact walks
     for (uint32_t e = (uint32_t)w; e < nx; e += kWaves) {  // uniform
         const bool keep = exact_flag(tab32, ref8, qry8, xp.a[e], sp);
-        if (lane == 0 && (keep || !ZeroSet)) flags[xp.slot[e]] = keep ? 1 : 0;
+        if (lane == 0 && (keep || !ZeroSet)) {
+            if (Bits) set_flag<true>(flags, xp.slot[e]);
+            else flags[xp.slot[e]] = keep ? 1 : 0;
+        }
     }
 }
 
@@ -855,7 +880,7 @@ struct KgRun {
 // a wave keeps a window of 64 runs in LDS (prefix end, bucket size and start, first seed
 // in qs, seeds); each step's lanes find the run owning their position from the marks the
 // runs leave at their first positions in the step, by a max-scan across the wave.
-template <int RB, int LB>
+template <int RB, int LB, bool Bits>
 __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     KeyGroups kg, KgScratch ks, PrefixView prefix, uint32_t batch_lo,
     uint32_t hit_lo, uint32_t n, uint32_t steps, const uint32_t *__restrict__ pos,
@@ -991,15 +1016,15 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
             slot = prefix.at(seed - batch_lo) - 1u - hit_lo - occ;
             if (res == 1) {
                 anchors[slot] = a;
-                flags[slot] = 1;
+                set_flag<Bits>(flags, slot);
             }
         }
         // a deferred slot's anchor travels in the list; the next stage stores it if kept
         defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, slot, a, defer,
                                    defer_a, defer_cnt);
     }
-    stage2_pool<kSegKg, true>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
-                              list2, defer_cnt, xp, tab32, ref8, qry8, sp);
+    stage2_pool<kSegKg, true, Bits>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
+                                    list2, defer_cnt, xp, tab32, ref8, qry8, sp);
 }
 
 // First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
@@ -1057,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
     const uint64_t *__restrict__ list_a, uint64_t *anchors_out,
     const uint32_t *__restrict__ count, uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
-    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt) {
+    uint32_t *__restrict__ defer, uint32_t *__restrict__ defer_cnt, int bits) {
     __shared__ int16_t tab[kWinTab];
     __shared__ uint32_t seg[kWaves][kSeg];
     __shared__ uint32_t seg_n[kWaves];
@@ -1084,7 +1109,11 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_list(
         Win<RB, LB, true> win;
         win.load(valid && r <= wp.n_ref && q <= wp.n_qry, r, q, ref4, qry4, wp);
         const int res = win.decide(tab, wp);
-        if (valid && res != 2) flags[i] = (uint8_t)res;
+        if (bits) {  // cleared beforehand: only 1s are written
+            if (valid && res == 1) set_flag<true>(flags, i);
+        } else if (valid && res != 2) {
+            flags[i] = (uint8_t)res;
+        }
         // anchors that came in the list are stored where they are kept or go on
         if (list_a && valid && res != 0) anchors_out[i] = a;
         defer_push(seg[w], nseg, valid && res == 2, i, defer, defer_cnt);
@@ -1136,12 +1165,12 @@ hipError_t launch_gate(int block_bases, const uint64_t *anchors, uint32_t n, uin
 hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
                                  const uint32_t *count, uint32_t max_count, uint8_t *flags,
                                  const uint8_t *ref, const uint8_t *qry, const ScoreParams &sp,
-                                 hipStream_t s) {
+                                 hipStream_t s, bool bits) {
     if (max_count == 0) return hipSuccess;
     const uint32_t blocks =
         (uint32_t)std::min<uint64_t>(((uint64_t)max_count + kWaves - 1) / kWaves, 4096);
     hipLaunchKernelGGL(k_gate_list_wave, dim3(blocks), dim3(kThreads), 0, s, anchors, list, count,
-                       flags, ref, qry, sp);
+                       flags, ref, qry, sp, bits ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1151,7 +1180,8 @@ hipError_t launch_gate_list_wave(const uint64_t *anchors, const uint32_t *list,
 static void launch_stage2(bool narrow, bool pooled, const uint64_t *anchors, uint32_t n,
                           uint8_t *flags, const uint32_t *ref4, const uint32_t *qry4,
                           const WindowParams &wp, uint32_t *list1, const uint64_t *list1_a,
-                          uint64_t *anchors_out, uint32_t *list2, uint32_t *cnt, hipStream_t s) {
+                          uint64_t *anchors_out, uint32_t *list2, uint32_t *cnt, hipStream_t s,
+                          bool bits = false) {
     // enough waves for one 64-anchor step each when an eighth of the anchors is listed
     // (about one step per wave on the 50 Mb workload: 7% faster than three).  After a
     // first stage that runs the second stage on its own deferred anchors, the list holds
@@ -1162,7 +1192,7 @@ static void launch_stage2(bool narrow, bool pooled, const uint64_t *anchors, uin
         ((uint64_t)cap2 + kWaves * 64 - 1) / (kWaves * 64), pooled ? 2048 : 16384);
     hipLaunchKernelGGL((k_gate_window_list<kStage2Right, kStage2Left>), dim3(blocks2),
                        dim3(kThreads), 0, s, anchors, list1, list1_a, anchors_out, cnt, flags, ref4,
-                       qry4, wp, list2, cnt + 1);
+                       qry4, wp, list2, cnt + 1, bits ? 1 : 0);
 }
 
 hipError_t launch_gate_window(bool narrow, const uint64_t *anchors, uint32_t n, uint8_t *flags,
@@ -1239,7 +1269,7 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
                                  const WindowParams &wp, uint32_t *list1, uint64_t *list1_a,
                                  uint32_t *list2, uint32_t *cnt, const ScoreParams &sp,
                                  const uint8_t *ref8, const uint8_t *qry8, bool groups_ready,
-                                 hipStream_t s) {
+                                 bool bits, hipStream_t s) {
     if (n == 0 || kg.n_runs == 0) {
         hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
@@ -1252,13 +1282,21 @@ hipError_t launch_gate_window_kg(const KeyGroups &kg, const KgScratch &ks,
     const uint32_t n_waves = (uint32_t)gate_window_waves(n);
     hipLaunchKernelGGL(k_kg_dir, dim3((n_waves + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
                        ks, nr, n_waves, steps, cnt);
-    if ((st = launch_zero_bytes(flags, n, s)) != hipSuccess) return st;
+    const uint64_t flag_bytes = bits ? ((uint64_t)n + 31) / 32 * 4 : (uint64_t)n;
+    if ((st = launch_zero_bytes(flags, flag_bytes, s)) != hipSuccess) return st;
     const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((k_gate_window_kg<kWideRight, kWideLeft>), dim3(blocks), dim3(kThreads), 0,
-                       s, kg, ks, prefix, batch_lo, hit_lo, n, steps, pos, anchors, flags, ref4,
-                       qry4, wp, list1, list1_a, cnt, list2, sp, ref8, qry8);
+    if (bits)
+        hipLaunchKernelGGL((k_gate_window_kg<kWideRight, kWideLeft, true>), dim3(blocks),
+                           dim3(kThreads), 0, s, kg, ks, prefix, batch_lo, hit_lo, n, steps, pos,
+                           anchors, flags, ref4, qry4, wp, list1, list1_a, cnt, list2, sp, ref8,
+                           qry8);
+    else
+        hipLaunchKernelGGL((k_gate_window_kg<kWideRight, kWideLeft, false>), dim3(blocks),
+                           dim3(kThreads), 0, s, kg, ks, prefix, batch_lo, hit_lo, n, steps, pos,
+                           anchors, flags, ref4, qry4, wp, list1, list1_a, cnt, list2, sp, ref8,
+                           qry8);
     launch_stage2(false, true, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors,
-                  list2, cnt, s);
+                  list2, cnt, s, bits);
     return hipGetLastError();
 }
 
