@@ -1252,8 +1252,7 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
     cs.hit_lo = (uint32_t)c.hit_lo;
     HIP_TRY(e, launch_gate_window_fused(e->params.gate_mode == 3, cs, (uint32_t)n, d_anchors,
                                         d_flags, e->d_ref4, e->d_qry4, e->wp, list1,
-                                        e->d_defer_a, list2, e->d_defer_cnt, e->sp,
-                                        e->d_ref + kPad, e->d_qry + kPad, s));
+                                        e->d_defer_a, list2, e->d_defer_cnt, s));
     HIP_TRY(e, launch_gate_list_wave(d_anchors, list2, e->d_defer_cnt + 1, (uint32_t)n, d_flags,
                                      e->d_ref + kPad, e->d_qry + kPad, e->sp, s));
     e->gate_deferred_valid = true;

@@ -187,8 +187,7 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
                                     const uint32_t *qry4, const WindowParams &wp,
                                     uint32_t *list1, uint64_t *list1_a, uint32_t *list2,
-                                    uint32_t *cnt, const ScoreParams &sp, const uint8_t *ref8,
-                                    const uint8_t *qry8, hipStream_t s);
+                                    uint32_t *cnt, hipStream_t s);
 // Key-grouped first stage (gate_mode 5, and gate_mode 0 for ranges of seeds holding a
 // large share of the strand's seeds).  The query strand's seeds are kept grouped by k-mer (built when
 // the query is uploaded): qs lists the seed indices ordered by k-mer and, within a k-mer,

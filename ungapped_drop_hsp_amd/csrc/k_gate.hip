@@ -504,25 +504,27 @@ __device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_
                                      defer_cnt);
 }
 
-// The second window stage run by the workgroup of a first stage that forms its own
-// anchors, once all four waves are done with their steps: the deferred (slot, anchor)
-// pairs still in the waves' LDS segments are taken 64 at a time, each wave a step in turn,
-// with the wider windows.  The lines of a step's windows are read while the other waves
-// on the SIMD score their blocks, instead of in a separate launch whose one step per wave
-// waits on them.  A deferred slot's anchor is stored unless its flag is 0 (the exact list
-// reads it there); flags already hold 0 when ZeroSet.  Anchors the wider windows leave
-// undecided go to the exact list.  Segments a wave flushed to the global list on the way
-// are left to the separate second stage.  The anchors the wider windows leave go on, up
-// to kXPool of them, to the exact walk the workgroup then runs itself (one wave per
-// anchor, as the exact list does), the rest to the exact list.  cnt[1] counts the exact
-// list, cnt[2] the anchors pooled here, cnt[3] the exact walks pooled here.
+// The second window stage run by the workgroup of the key-grouped first stage, once all
+// four waves are done with their steps: the deferred (slot, anchor) pairs still in the
+// waves' LDS segments are taken 64 at a time, each wave a step in turn, with the wider
+// windows.  The lines of a step's windows are read while the other waves on the SIMD
+// score their blocks, instead of in a separate launch whose one step per wave waits on
+// them.  A deferred slot's anchor is stored unless its flag is 0 (the exact walk reads it
+// there); the flags were cleared, so only 1s are written (Bits: set_flag).  Segments a
+// wave flushed to the global list on the way are left to the separate second stage.  The
+// anchors the wider windows leave go on, up to kXPool of them, to the exact walk the
+// workgroup then runs itself (one wave per anchor, as the exact list does), the rest to
+// the exact list.  cnt[1] counts the exact list, cnt[2] the anchors pooled here, cnt[3]
+// the exact walks pooled here.  (The raw-order first stage, whose calls are often small,
+// leaves both stages to their own launches: run inside its few workgroups, they slowed
+// the 5 Mb dense-repeat workload's chunks from 0.080 to 0.10-0.15 ms.)
 struct ExactPool {
     uint32_t slot[kXPool];
     uint64_t a[kXPool];
     uint32_t n;  // reserved entries (may exceed kXPool: those went to the exact list)
 };
 
-template <int S, bool ZeroSet, bool Bits = false>
+template <int S, bool Bits>
 __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint64_t (*sega)[S],
                                             uint32_t *seg_n, uint32_t nseg, const int16_t *tab,
                                             uint64_t *__restrict__ anchors,
@@ -535,7 +537,6 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
                                             const uint8_t *__restrict__ qry8,
                                             const ScoreParams &sp) {
     static_assert(kWaves == 4, "four wave segments");
-    static_assert(ZeroSet || !Bits, "bit flags are cleared beforehand");
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     if (lane == 0) seg_n[w] = nseg;
@@ -569,11 +570,7 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
         if (valid && res != 0) anchors[slot] = a;
-        if (Bits) {
-            if (valid && res == 1) set_flag<true>(flags, slot);
-        } else if (valid && (ZeroSet ? res == 1 : res != 2)) {
-            flags[slot] = (uint8_t)res;
-        }
+        if (valid && res == 1) set_flag<Bits>(flags, slot);
         const uint64_t m = __ballot(valid && res == 2);
         if (m) {
             uint32_t base = 0;
@@ -599,10 +596,7 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
     if (threadIdx.x == 0 && nx) atomicAdd(cnt + 3, nx);  // the pooled exact walks
     for (uint32_t e = (uint32_t)w; e < nx; e += kWaves) {  // uniform
         const bool keep = exact_flag(tab32, ref8, qry8, xp.a[e], sp);
-        if (lane == 0 && (keep || !ZeroSet)) {
-            if (Bits) set_flag<true>(flags, xp.slot[e]);
-            else flags[xp.slot[e]] = keep ? 1 : 0;
-        }
+        if (lane == 0 && keep) set_flag<Bits>(flags, xp.slot[e]);
     }
 }
 
@@ -677,20 +671,16 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
     uint8_t *__restrict__ flags,
     const uint32_t *__restrict__ ref4, const uint32_t *__restrict__ qry4, WindowParams wp,
     uint32_t *__restrict__ defer, uint64_t *__restrict__ defer_a,
-    uint32_t *__restrict__ defer_cnt, uint32_t *__restrict__ list2, ScoreParams sp,
-    const uint8_t *__restrict__ ref8, const uint8_t *__restrict__ qry8) {
+    uint32_t *__restrict__ defer_cnt) {
     __shared__ int16_t tab[kWinTab];
-    __shared__ int32_t tab32[kTabSize];  // the exact walks' table
-    __shared__ ExactPool xp;
     __shared__ uint32_t seg[kWaves][kSegKg];
     __shared__ uint64_t sega[kWaves][kSegKg];
     __shared__ uint32_t seg_n[kWaves];
+    __shared__ uint32_t blk_base;
     __shared__ uint32_t rel[kWaves][64];  // prefix - hit_lo of the window's seeds
     __shared__ uint32_t fst[kWaves][64];  // their bucket starts
     __shared__ uint32_t qen[kWaves][64];  // their query ends
     if (threadIdx.x < kWinTab) tab[threadIdx.x] = wp.tab[threadIdx.x];
-    if (threadIdx.x < kTabSize) tab32[threadIdx.x] = sp.tab[threadIdx.x];
-    if (threadIdx.x == 0) xp.n = 0;
     __syncthreads();
 
     const int lane = lane_id();
@@ -750,8 +740,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_fused(
         defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, t, a, defer,
                                    defer_a, defer_cnt);
     }
-    stage2_pool<kSegKg, false>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
-                               list2, defer_cnt, xp, tab32, ref8, qry8, sp);
+    defer_flush_block_g<kSegKg, true>(seg, sega, seg_n, &blk_base, nseg, defer, defer_a,
+                                      defer_cnt);
 }
 
 // ------------------------------------------------------------------ key-grouped first stage
@@ -1023,8 +1013,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
         defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, slot, a, defer,
                                    defer_a, defer_cnt);
     }
-    stage2_pool<kSegKg, true, Bits>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp,
-                                    list2, defer_cnt, xp, tab32, ref8, qry8, sp);
+    stage2_pool<kSegKg, Bits>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp, list2,
+                              defer_cnt, xp, tab32, ref8, qry8, sp);
 }
 
 // First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
@@ -1229,8 +1219,7 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
                                     uint64_t *anchors, uint8_t *flags, const uint32_t *ref4,
                                     const uint32_t *qry4, const WindowParams &wp,
                                     uint32_t *list1, uint64_t *list1_a, uint32_t *list2,
-                                    uint32_t *cnt, const ScoreParams &sp, const uint8_t *ref8,
-                                    const uint8_t *qry8, hipStream_t s) {
+                                    uint32_t *cnt, hipStream_t s) {
     if (n == 0) {
         hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(1), 0, s, cnt);
         return hipGetLastError();
@@ -1243,12 +1232,14 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
     if (narrow)
         hipLaunchKernelGGL((k_gate_window_fused<kNarrowRight, kNarrowLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, list1_a, cnt, list2, sp, ref8, qry8);
+                           list1, list1_a, cnt);
     else
         hipLaunchKernelGGL((k_gate_window_fused<kWideRight, kWideLeft>), dim3(blocks),
                            dim3(kThreads), 0, s, cs, n, steps, anchors, flags, ref4, qry4, wp,
-                           list1, list1_a, cnt, list2, sp, ref8, qry8);
-    launch_stage2(narrow, true, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors,
+                           list1, list1_a, cnt);
+    // its second stage is a launch of its own: small calls (many chunks of about 2^20
+    // anchors, often with long walks) leave the first stage too few waves to run it in
+    launch_stage2(narrow, false, anchors, n, flags, ref4, qry4, wp, list1, list1_a, anchors,
                   list2, cnt, s);
     return hipGetLastError();
 }
