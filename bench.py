@@ -387,7 +387,9 @@ def main():
                       unit="G base-steps/s", frac=gate_gsteps / ALU_PEAK_GSTEPS,
                       traffic=traffic,
                       kernel=("the gate over the whole batch at once (key-grouped first "
-                              "window stage forming its own anchors; second stage; exact list)"
+                              "window stage forming its own anchors, its workgroups then "
+                              "running the second stage and exact walks of their deferred "
+                              "anchors)"
                               if whole_batches else
                               "find_hits_gate per chunk (first window stage forming its own "
                               "anchors, key-grouped when a chunk holds enough seeds; second "
