@@ -32,15 +32,19 @@
 //    window's end are appended to a deferred list: each wave collects them in LDS and
 //    the workgroup reserves its share of the global list with one atomic.  The stages
 //    that form their own anchors put each deferred anchor in a second list beside its
-//    slot, which the next stage reads in order.
+//    slot, which the next stage reads in order.  The key-grouped stage instead keeps its
+//    deferred anchors in LDS and its workgroups run the wider second window and then the
+//    exact walk on them at their end (stage2_pool); only what overflows LDS goes to the
+//    lists.
 //
 //  exact, all anchors (k_gate): one lane per anchor walking base blocks straight from
 //    the byte-per-base sequences, refilling finished lanes from the wave's tile of
 //    anchors (ranks from a ballot).  Used when the window path's preconditions do not
 //    hold.
 //
-//  exact, listed anchors (k_gate_list_wave): one wave per anchor the window stages left,
-//    walking 64-base tiles with wave scans (walk.h), since those walks are long.
+//  exact, listed anchors (k_gate_list_wave, and exact_flag inside stage2_pool): one wave
+//    per anchor the window stages left, walking 64-base tiles with wave scans (walk.h),
+//    since those walks are long.
 #include <algorithm>
 #include <type_traits>
 
@@ -260,7 +264,10 @@ constexpr int kWideRight = 6, kWideLeft = 9;
 constexpr int kNarrowRight = 4, kNarrowLeft = 7;
 constexpr int kStage2Right = 8, kStage2Left = 12;
 constexpr int kSeg = 512;   // LDS slots per wave for deferred anchor indices
-constexpr int kSegKg = 256;  // the same with anchors, in the key-grouped stage
+constexpr int kSegKg = 256;  // the same with anchors, in the raw-order fused stage
+// LDS entries per wave for the key-grouped stage's deferred anchors (seed, occurrence and
+// anchor, 16 bytes), sized so that seven of its workgroups still fit a CU's LDS
+constexpr int kSegPool = 208;
 constexpr int kXPool = 128;  // anchors per workgroup for its own exact walks
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
@@ -465,6 +472,44 @@ __device__ __forceinline__ void defer_push_g(uint32_t *seg, uint64_t *sega, uint
     nseg += c;
 }
 
+// The key-grouped stage's deferral.  A deferred anchor's slot needs its seed's prefix, a
+// random read that would hold the whole wave for one lane, so each entry keeps the seed
+// (relative to the batch), the occurrence and the anchor, and the slot is formed where the
+// entries are consumed: for a segment that fills, here with up to 64 reads in flight.
+template <int S>
+__device__ __forceinline__ void defer_push_kg(uint32_t *segs, uint32_t *sego, uint64_t *sega,
+                                              uint32_t &nseg, bool dfr, uint32_t sr,
+                                              uint32_t occ, uint64_t a, const PrefixView &prefix,
+                                              uint32_t hit_lo, uint32_t *__restrict__ defer,
+                                              uint64_t *__restrict__ defer_a,
+                                              uint32_t *__restrict__ defer_cnt) {
+    const int lane = lane_id();
+    const uint64_t m = __ballot(dfr);
+    if (!m) return;
+    const uint32_t c = (uint32_t)__popcll(m);
+    if (nseg + c > (uint32_t)S) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(defer_cnt, nseg);
+        base = __shfl(base, 0, 64);
+        for (uint32_t j = lane; j < nseg; j += 64) {
+            defer[base + j] = prefix.at(segs[j]) - 1u - hit_lo - sego[j];
+            defer_a[base + j] = sega[j];
+        }
+        nseg = 0;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (dfr) {
+        const uint32_t k = nseg + lane_rank(m);
+        segs[k] = sr;
+        sego[k] = occ;
+        sega[k] = a;
+    }
+    nseg += c;
+}
+
 // All waves of the block call this once at the end.
 template <int S, bool P>
 __device__ __forceinline__ void defer_flush_block_g(uint32_t (*seg)[S], uint64_t (*sega)[S],
@@ -505,11 +550,13 @@ __device__ __forceinline__ void defer_flush_block(uint32_t (*seg)[kSeg], uint32_
 }
 
 // The second window stage run by the workgroup of the key-grouped first stage, once all
-// four waves are done with their steps: the deferred (slot, anchor) pairs still in the
-// waves' LDS segments are taken 64 at a time, each wave a step in turn, with the wider
-// windows.  The lines of a step's windows are read while the other waves on the SIMD
-// score their blocks, instead of in a separate launch whose one step per wave waits on
-// them.  A deferred slot's anchor is stored unless its flag is 0 (the exact walk reads it
+// four waves are done with their steps: the deferred entries still in the waves' LDS
+// segments are taken 64 at a time, each wave a step in turn, with the wider windows.  The
+// lines of a step's windows are read while the other waves on the SIMD score their
+// blocks, instead of in a separate launch whose one step per wave waits on them.  An
+// entry's slot (its seed's prefix, less hit_lo and the occurrence, the slot rule of
+// "C. Hit discovery", C.5) is read only once the wider window leaves its flag open or 1.
+// A deferred slot's anchor is stored unless its flag is 0 (the exact walk reads it
 // there); the flags were cleared, so only 1s are written (Bits: set_flag).  Segments a
 // wave flushed to the global list on the way are left to the separate second stage.  The
 // anchors the wider windows leave go on, up to kXPool of them, to the exact walk the
@@ -525,8 +572,10 @@ struct ExactPool {
 };
 
 template <int S, bool Bits>
-__device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint64_t (*sega)[S],
-                                            uint32_t *seg_n, uint32_t nseg, const int16_t *tab,
+__device__ __forceinline__ void stage2_pool(const uint32_t (*segs)[S], const uint32_t (*sego)[S],
+                                            const uint64_t (*sega)[S], const PrefixView &prefix,
+                                            uint32_t hit_lo, uint32_t *seg_n, uint32_t nseg,
+                                            const int16_t *tab,
                                             uint64_t *__restrict__ anchors,
                                             uint8_t *__restrict__ flags,
                                             const uint32_t *__restrict__ ref4,
@@ -547,7 +596,7 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
     for (uint32_t e0 = (uint32_t)w * 64; e0 < total; e0 += kWaves * 64) {  // uniform
         const uint32_t e = e0 + lane;
         const bool valid = e < total;
-        uint32_t slot = 0;
+        uint32_t sr = 0, occ = 0;
         uint64_t a = 0;
         if (valid) {
             uint32_t v = 0, j = e;
@@ -563,13 +612,18 @@ __device__ __forceinline__ void stage2_pool(const uint32_t (*seg)[S], const uint
                     }
                 }
             }
-            slot = seg[v][j];
+            sr = segs[v][j];
+            occ = sego[v][j];
             a = sega[v][j];
         }
         Win<kStage2Right, kStage2Left, true> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
-        if (valid && res != 0) anchors[slot] = a;
+        uint32_t slot = 0;
+        if (valid && res != 0) {
+            slot = prefix.at(sr) - 1u - hit_lo - occ;
+            anchors[slot] = a;
+        }
         if (valid && res == 1) set_flag<Bits>(flags, slot);
         const uint64_t m = __ballot(valid && res == 2);
         if (m) {
@@ -882,8 +936,9 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
     __shared__ int16_t tab[kWinTab];
     __shared__ int32_t tab32[kTabSize];  // the exact walks' table
     __shared__ ExactPool xp;
-    __shared__ uint32_t seg[kWaves][kSegKg];
-    __shared__ uint64_t sega[kWaves][kSegKg];
+    __shared__ uint32_t segs[kWaves][kSegPool];  // deferred: seed - batch_lo
+    __shared__ uint32_t sego[kWaves][kSegPool];  // occurrence
+    __shared__ uint64_t sega[kWaves][kSegPool];  // anchor
     __shared__ uint32_t seg_n[kWaves];
     __shared__ KgRun run[kWaves][64];    // the wave's window of runs
     __shared__ uint32_t mk[kWaves][64];  // marks of the step's positions (run index)
@@ -1001,20 +1056,20 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
         Win<RB, LB, true> win;
         win.load(in_range(valid, a, wp), (uint32_t)a, (uint32_t)(a >> 32), ref4, qry4, wp);
         const int res = win.decide(tab, wp);
-        uint32_t slot = 0;
-        if (valid && res != 0) {
-            slot = prefix.at(seed - batch_lo) - 1u - hit_lo - occ;
-            if (res == 1) {
-                anchors[slot] = a;
-                set_flag<Bits>(flags, slot);
-            }
+        if (valid && res == 1) {
+            const uint32_t slot = prefix.at(seed - batch_lo) - 1u - hit_lo - occ;
+            anchors[slot] = a;
+            set_flag<Bits>(flags, slot);
         }
-        // a deferred slot's anchor travels in the list; the next stage stores it if kept
-        defer_push_g<kSegKg, true>(seg[w], sega[w], nseg, valid && res == 2, slot, a, defer,
-                                   defer_a, defer_cnt);
+        // a deferred anchor travels with its seed and occurrence (its slot is formed where
+        // it is consumed); the next stage stores it if kept
+        defer_push_kg<kSegPool>(segs[w], sego[w], sega[w], nseg, valid && res == 2,
+                                seed - batch_lo, occ, a, prefix, hit_lo, defer, defer_a,
+                                defer_cnt);
     }
-    stage2_pool<kSegKg, Bits>(seg, sega, seg_n, nseg, tab, anchors, flags, ref4, qry4, wp, list2,
-                              defer_cnt, xp, tab32, ref8, qry8, sp);
+    stage2_pool<kSegPool, Bits>(segs, sego, sega, prefix, hit_lo, seg_n, nseg, tab, anchors,
+                                flags, ref4, qry4, wp, list2, defer_cnt, xp, tab32, ref8, qry8,
+                                sp);
 }
 
 // First stage over anchors sorted by reference slice (bucketed gate, "D. Score gate",
