@@ -914,7 +914,8 @@ __global__ __launch_bounds__(kThreads) void k_kg_dir(KgScratch ks, uint32_t n_ru
 
 // A run as the key-grouped stage's window holds it: inclusive and exclusive prefix of its
 // anchors in the call (rs above rel for an entry past the last run), bucket start, first
-// seed in qs, seeds in the range and the hardware reciprocal of that count.
+// seed in qs, the smaller of its bucket entries and its seeds in the range (bit 31 set
+// when that is the bucket entries) and the hardware reciprocal of that count.
 struct KgRun {
     uint32_t rel, rs, f, a, m;
     float q;
@@ -980,8 +981,10 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
                 q.rs = in ? g + off - cm : 0xFFFFFFFFu;  // above rel: holds no position
                 q.f = in ? f : 0u;
                 q.a = in ? sa0 : 0u;
-                q.m = in ? m0 : 1u;
-                q.q = __builtin_amdgcn_rcpf((float)(in ? m0 : 1u));
+                // the smaller of c and m runs fastest (bit 31: c, the bucket entries)
+                const uint32_t x = !in ? 1u : (c < m0 ? c : m0);
+                q.m = x | (in && c < m0 ? 0x80000000u : 0u);
+                q.q = __builtin_amdgcn_rcpf((float)x);
                 small = __ballot(in && cm >= (1u << 22)) == 0;
                 step_small = step_small && small;
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -1024,32 +1027,38 @@ __global__ __launch_bounds__(kThreads) void k_gate_window_kg(
             wb += 64;
             loaded = false;
         }
-        // position u of the run's c * m anchors: bucket entry u / m, seed u % m.  When
-        // every run the step reads has under 2^22 anchors, the quotient comes from the
-        // float reciprocal: u and m are exact in float, the hardware reciprocal is within
-        // one unit in the last place and the product rounds once, so the estimate is
-        // within one of u / m (exact for m = 1) and the remainder's sign corrects it;
-        // 24-bit multiplies suffice, since u, m and the quotient stay under 2^22.
+        // position u of the run's c * m anchors: with x the smaller of c and m, the one
+        // that runs fastest (a run cut by a step boundary then has its x windows read in
+        // both steps, not its m query windows), u / x indexes the other and u % x this
+        // one.  When every run the step reads has under 2^22 anchors, the quotient comes
+        // from the float reciprocal: u and x are exact in float, the hardware reciprocal
+        // is within one unit in the last place and the product rounds once, so the
+        // estimate is within one of u / x (exact for x = 1) and the remainder's sign
+        // corrects it; 24-bit multiplies suffice, since u, x and the quotient stay under
+        // 2^22.
         uint32_t occ = 0, seed = 0;
         uint64_t a = 0;
         if (valid) {
             const uint32_t u = t - start;
-            uint32_t r;
+            const bool sw = (m >> 31) != 0u;
+            const uint32_t x = m & 0x7FFFFFFFu;
+            uint32_t qq, r;
             if (step_small) {
-                occ = (uint32_t)((float)u * rcp);
-                r = u - __umul24(occ, m);
+                qq = (uint32_t)((float)u * rcp);
+                r = u - __umul24(qq, x);
                 if ((int32_t)r < 0) {
-                    occ -= 1u;
-                    r += m;
-                } else if (r >= m) {
-                    occ += 1u;
-                    r -= m;
+                    qq -= 1u;
+                    r += x;
+                } else if (r >= x) {
+                    qq += 1u;
+                    r -= x;
                 }
             } else {
-                occ = u / m;
-                r = u - occ * m;
+                qq = u / x;
+                r = u - qq * x;
             }
-            const uint32_t js = sa + r;
+            occ = sw ? r : qq;
+            const uint32_t js = sa + (sw ? qq : r);
             a = (uint64_t)pos[bfirst + occ] | ((uint64_t)kg.qe[js] << 32);
             seed = kg.qs[js];  // read with the anchor: a kept or deferred slot needs it
         }
