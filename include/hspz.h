@@ -215,8 +215,11 @@ int hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint64_t pos_hi,
  * 64 bits on the device (the global inclusive prefix is a block's local prefix plus its
  * offset; the library adds the offset wherever it reads a prefix), and cut MAX_HITS
  * chunks with the lower-bound walk (a seed is never split), also on the device; one copy
- * brings back the total and the chunk list.  A batch whose total
- * exceeds 2^32 - 1 is refused with HSPZ_E_OVERFLOW and leaves no plan.
+ * brings back the total and the chunk list.  Only the prefix stays on the device: the
+ * per-seed counts and bucket starts are looked up again, once per plan, by the first call
+ * that reads them (hspz_find_hits, a raw-order hspz_find_hits_gate, hspz_get_plan_arrays).
+ * A batch whose total exceeds 2^32 - 1 is refused with HSPZ_E_OVERFLOW and leaves no
+ * plan.
  * *total_hits and *n_chunks receive the totals (0 chunks when the total is 0).
  * Synchronises stream.  Errors: HSPZ_E_STATE (no reference/query), HSPZ_E_INVALID,
  * HSPZ_E_OVERFLOW, HSPZ_E_NOMEM, HSPZ_E_HIP. */

@@ -67,6 +67,9 @@ struct Engine {
     uint64_t batch_lo = 0, batch_n = 0, total = 0;
     uint32_t *d_count = nullptr, *d_prefix = nullptr;
     uint32_t *d_first = nullptr;  // bucket start of every seed of the batch
+    // d_count and d_first hold this plan's values (the plan writes only the prefix; they
+    // are filled on first use, ensure_plan_aux)
+    bool plan_aux = false;
     uint64_t *d_blksum = nullptr;
     uint32_t *d_blkoff = nullptr;
     uint64_t cap_batch = 0;

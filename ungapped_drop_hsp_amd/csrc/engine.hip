@@ -504,6 +504,7 @@ Engine::~Engine() {
 void Engine::free_plan() {
     has_plan = false;
     plan_expandable = false;
+    plan_aux = false;
     chunks.clear();
     total = 0;
 }
@@ -852,6 +853,19 @@ static int impl_hspz_seed_range(const hspz_engine *engine, uint64_t pos_lo, uint
 }
 
 // hspz_plan, with finish_plan's queued hook (hspz_run_batch queues work there).
+// The per-seed counts and bucket starts of the planned batch ("C. Hit discovery", C.1),
+// which the plan leaves out: the same lookups again, writing those two arrays and no
+// prefix.  Queued on s once per plan, by the first caller that reads them (the raw-order
+// expansion and fused gate stage, hspz_get_plan_arrays).
+static int ensure_plan_aux(Engine *e, hipStream_t s) {
+    if (e->plan_aux) return HSPZ_OK;
+    if (e->batch_n)
+        HIP_TRY(e, launch_count_scan(e->d_kmer + e->batch_lo, nullptr, e->batch_n, e->d_end,
+                                     e->d_ctab, e->d_count, e->d_first, nullptr, nullptr, s));
+    e->plan_aux = true;
+    return HSPZ_OK;
+}
+
 static int plan_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, void *stream,
                       uint64_t *total_hits, uint32_t *n_chunks,
                       const std::function<int()> &queued) {
@@ -874,8 +888,10 @@ static int plan_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, v
     if ((rc = ensure_batch(e, n))) return rc;
     e->batch_lo = seed_lo;
     e->batch_n = n;
-    HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_ctab,
-                                 e->d_count, e->d_first, e->d_prefix, e->d_blksum, s));
+    // the prefix alone: the per-seed counts and bucket starts only where a caller needs
+    // them (ensure_plan_aux)
+    HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_ctab, nullptr,
+                                 nullptr, e->d_prefix, e->d_blksum, s));
     rc = finish_plan(e, n, s, total_hits, n_chunks, queued);
     if (rc) {
         *total_hits = 0;
@@ -914,6 +930,7 @@ static int impl_hspz_debug_plan_counts(hspz_engine *engine, const uint32_t *h_co
                                      nullptr, e->d_prefix, e->d_blksum, s));
     }
     rc = finish_plan(e, n, s, total_hits, n_chunks, nullptr);
+    e->plan_aux = rc == HSPZ_OK;  // the counts are in place (this plan has no bucket starts)
     if (rc) {
         *total_hits = 0;
         *n_chunks = 0;
@@ -939,9 +956,13 @@ static int impl_hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_coun
     int rc = set_device(e);
     if (rc) return rc;
     if (e->batch_n) {
-        if (h_counts)
+        if (h_counts) {
+            // the counts' pass reads only the uploaded k-mers and table; the copy on the
+            // same (null) stream waits for it
+            if ((rc = ensure_plan_aux(e, nullptr))) return rc;
             HIP_TRY(e, hipMemcpy(h_counts, e->d_count, e->batch_n * sizeof(uint32_t),
                                  hipMemcpyDeviceToHost));
+        }
         if (h_prefix) {
             // the device keeps block-local prefixes and the blocks' offsets
             const uint64_t nblk = (e->batch_n + kScanBlock - 1) / kScanBlock;
@@ -1014,6 +1035,7 @@ static int impl_hspz_find_hits(hspz_engine *engine, uint32_t chunk, uint64_t *d_
     else if (e->params.expand_mode == 2) dense = true;
     else dense = c.n_hits >= 16 * ns;  // "C. Hit discovery", C.4 density rule
     const uint64_t local = c.seed_lo - e->batch_lo;
+    if ((rc = ensure_plan_aux(e, as_stream(stream)))) return rc;
     HIP_TRY(e, launch_expand(dense, e->d_count + local, e->d_first + local,
                              e->d_qend + c.seed_lo,
                              PrefixView{e->d_prefix + local, e->d_blkoff, (uint32_t)local}, ns,
@@ -1240,7 +1262,7 @@ static int impl_hspz_find_hits_gate(hspz_engine *engine, uint32_t chunk, uint64_
         return gate_key_grouped(e, c.seed_lo, c.seed_hi, c.hit_lo, n, d_anchors, d_flags, s);
     if ((rc = ensure_defer(e, n)) || (rc = ensure_defer_anchors(e))) return rc;
     uint32_t *list1 = e->d_defer, *list2 = e->d_defer + e->cap_defer;
-    if ((rc = ensure_dir(e, n))) return rc;
+    if ((rc = ensure_dir(e, n)) || (rc = ensure_plan_aux(e, s))) return rc;
     const uint64_t local = c.seed_lo - e->batch_lo;
     ChunkSeeds cs;
     cs.prefix = PrefixView{e->d_prefix + local, e->d_blkoff, (uint32_t)local};

@@ -102,6 +102,7 @@ hipError_t launch_count_table(const uint32_t *end_tbl, uint64_t nb, uint4 *ctab,
 // Per seed: hit count, bucket start (first, when kmer is given) and block-local
 // inclusive prefix; one 64-bit sum per kScanBlock seeds into blksum.  With kmer, counts
 // and starts come from ctab (the packed table) when it is given, else from end_tbl.
+// count, first, prefix and blksum may each be null: that output is not written.
 hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, uint64_t n,
                              const uint32_t *end_tbl, const uint4 *ctab, uint32_t *count,
                              uint32_t *first, uint32_t *prefix, uint64_t *blksum,
