@@ -357,11 +357,11 @@ def main():
     traffic = gate_traffic(w.name, args.gate_mode, units_avg)
     # The gate's reference windows are 64-byte reads from the 4-bit reference copy and its
     # line-split twin (about one byte per reference base in all); the plan's lookups read
-    # one 32-byte record of the packed count table per seed.
+    # one dword of the 4-bit count table (eight keys' counts) per seed.
     ceiling, ceiling_runs = line_ceiling(torch, h, int(w.ref.size), 16)
     gate_lines = None if traffic is None else traffic / 128.0 / (gate_ms_avg / 1000.0)
-    ct_bytes = 32 * -(-(4 ** len([c for c in p["seed_pattern"] if c == "1"])) // 28)
-    plan_ceiling, plan_runs = line_ceiling(torch, h, ct_bytes, 16)
+    ct_bytes = 4 * -(-(4 ** len([c for c in p["seed_pattern"] if c == "1"])) // 8)
+    plan_ceiling, plan_runs = line_ceiling(torch, h, ct_bytes, 1)
     plan_ms = stage_ms.get("plan", 0.0)  # every seed of the step planned once
 
     if args.copy_probe_mib:
@@ -407,12 +407,12 @@ def main():
                         frac=None if gate_lines is None else gate_lines / ceiling,
                         ceiling_probe=dict(region_bytes=int(w.ref.size), window_bytes=64,
                                            **ceiling_runs)),
-        # the plan's random lines: one count-table record per seed, over the plan stage's
+        # the plan's random lines: one count-table dword per seed, over the plan stage's
         # time (hit counts, block scan, offsets, chunk walk) in the instrumented pass
         plan_lines=dict(achieved=seeds / (plan_ms / 1000.0) if plan_ms > 0 else None,
                         ceiling=plan_ceiling, unit="lines/s",
                         frac=seeds / (plan_ms / 1000.0) / plan_ceiling if plan_ms > 0 else None,
-                        ceiling_probe=dict(region_bytes=ct_bytes, window_bytes=64,
+                        ceiling_probe=dict(region_bytes=ct_bytes, window_bytes=4,
                                            **plan_runs)),
         gate_stage2_fraction=None if deferred is None else deferred[0] / max(walked, 1),
         gate_exact_fraction=None if deferred is None else deferred[1] / max(walked, 1),

@@ -29,6 +29,7 @@ struct Engine {
     uint64_t n_ref = 0;
     uint32_t *d_end = nullptr;   // 4^w + 1 cumulative bucket ends, leading 0
     uint4 *d_ctab = nullptr;     // the same in packed records (launch_count_table)
+    uint32_t *d_cnib = nullptr;  // each key's count in 4 bits (launch_count_nibbles)
     uint32_t *d_pos = nullptr;   // reference end coordinate of every valid window
     uint64_t n_index = 0;        // entries of d_pos
     uint8_t *d_ref = nullptr;    // padded encoded reference (kPad edge bytes each side)

@@ -426,6 +426,7 @@ Engine::~Engine() {
     (void)hipSetDevice(device);
     dfree(d_end);
     dfree(d_ctab);
+    dfree(d_cnib);
     for (uint32_t **q : {&d_kg_qk, &d_kg_qs, &d_kg_qe, &d_kg_runs, &d_kg_run_c, &d_kg_run_first,
                          &d_kg_G, &d_kg_a, &d_kg_m, &d_kg_dir, &d_kg_blkoff})
         dfree(*q);
@@ -718,6 +719,9 @@ static int impl_hspz_upload_reference(hspz_engine *engine, const uint8_t *h_asci
         // the packed form the plan's lookups read (two uint4 per record)
         if ((rc = dalloc(e, e->d_ctab, 2ull * count_table_records(nb)))) return rc;
         HIP_TRY(e, launch_count_table(e->d_end, nb, e->d_ctab, s));
+        // and the 4-bit counts the plan reads
+        if ((rc = dalloc(e, e->d_cnib, count_nibble_words(nb)))) return rc;
+        HIP_TRY(e, launch_count_nibbles(e->d_end, nb, e->d_cnib, s));
         HIP_TRY(e, hipStreamSynchronize(s));
     }
     const uint32_t nblk = radix_blocks(nwin);
@@ -890,8 +894,8 @@ static int plan_batch(hspz_engine *engine, uint64_t seed_lo, uint64_t seed_hi, v
     e->batch_n = n;
     // the prefix alone: the per-seed counts and bucket starts only where a caller needs
     // them (ensure_plan_aux)
-    HIP_TRY(e, launch_count_scan(e->d_kmer + seed_lo, nullptr, n, e->d_end, e->d_ctab, nullptr,
-                                 nullptr, e->d_prefix, e->d_blksum, s));
+    HIP_TRY(e, launch_count_prefix(e->d_kmer + seed_lo, n, e->d_end, e->d_cnib, e->d_prefix,
+                                   e->d_blksum, s));
     rc = finish_plan(e, n, s, total_hits, n_chunks, queued);
     if (rc) {
         *total_hits = 0;

@@ -99,6 +99,11 @@ hipError_t launch_radix_scatter(const uint32_t *key_in, const uint32_t *val_in, 
 constexpr uint32_t kCountTableKeys = 28;
 uint32_t count_table_records(uint64_t nb);
 hipError_t launch_count_table(const uint32_t *end_tbl, uint64_t nb, uint4 *ctab, hipStream_t s);
+// 4-bit count table: count_nibble_words(nb) dwords, key k's count (capped at 15) in bits
+// 4 (k % 8) .. of dword k / 8; launch_count_nibbles builds it from end_tbl[0..nb].
+uint64_t count_nibble_words(uint64_t nb);
+hipError_t launch_count_nibbles(const uint32_t *end_tbl, uint64_t nb, uint32_t *cnib,
+                                hipStream_t s);
 // Per seed: hit count, bucket start (first, when kmer is given) and block-local
 // inclusive prefix; one 64-bit sum per kScanBlock seeds into blksum.  With kmer, counts
 // and starts come from ctab (the packed table) when it is given, else from end_tbl.
@@ -107,6 +112,11 @@ hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, ui
                              const uint32_t *end_tbl, const uint4 *ctab, uint32_t *count,
                              uint32_t *first, uint32_t *prefix, uint64_t *blksum,
                              hipStream_t s);
+// The plan's form of it: block-local inclusive prefix and block sums only, each seed's
+// count read from the 4-bit table (end_tbl for counts of 15 or more).
+hipError_t launch_count_prefix(const uint32_t *kmer, uint64_t n, const uint32_t *end_tbl,
+                               const uint32_t *cnib, uint32_t *prefix, uint64_t *blksum,
+                               hipStream_t s);
 hipError_t launch_add_offsets(uint32_t *prefix, uint64_t n, const uint32_t *blkoff,
                               hipStream_t s);
 

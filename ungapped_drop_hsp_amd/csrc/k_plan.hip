@@ -20,6 +20,11 @@
 // it with fewer entries).  A record in which some key has 255 or more hits is marked,
 // and its keys are looked up in the full table.
 //
+// The plan itself needs counts only, so it reads a smaller table still (k_count_nibbles):
+// each key's count in four bits, eight keys to a dword, 15 meaning "15 or more: look it
+// up in the full table".  For 12-mers that is 8.4 MB against the records' 19 MB, and an
+// XCD's 4 MB L2 holds about half of it instead of a fifth.
+//
 // k_chunk_walk: the MAX_HITS cut ("C. Hit discovery", C.3) on the device, by one wave.
 // Each boundary is the first seed whose prefix reaches H + MAX_HITS, found by a 64-way
 // search: every round the lanes read the last prefix of 64 equal segments of the range
@@ -58,6 +63,21 @@ __global__ __launch_bounds__(kThreads) void k_count_table(const uint32_t *__rest
     ctab[2 * (uint64_t)g + 1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+// Dword g of the 4-bit count table: key 8g + j's count, capped at 15, in bits 4j .. 4j+3.
+__global__ __launch_bounds__(kThreads) void k_count_nibbles(const uint32_t *__restrict__ end_tbl,
+                                                            uint64_t nb, uint32_t n_words,
+                                                            uint32_t *__restrict__ cnib) {
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= n_words) return;
+    uint32_t w = 0;
+    for (uint32_t j = 0; j < 8; j++) {
+        const uint64_t k = (uint64_t)g * 8 + j;
+        const uint32_t c = k < nb ? end_tbl[k + 1] - end_tbl[k] : 0u;
+        w |= min(c, 15u) << (4 * j);
+    }
+    cnib[g] = w;
+}
+
 // Bucket start and hit count of the key at offset i (0 .. 27) of an unmarked record
 // (dwords a.x .. b.w): the record's start plus the counts of the keys before it.
 __device__ __forceinline__ void count_record(const uint4 a, const uint4 b, uint32_t i,
@@ -77,14 +97,15 @@ __device__ __forceinline__ void count_record(const uint4 a, const uint4 b, uint3
 }
 
 // Mode: 0 = injected counts (counts_in), 1 = k-mers looked up in end_tbl, 2 = k-mers
-// looked up in the packed table.  The four seeds' loads are issued together, with no
-// branch between them, so that a thread keeps four lookups in flight.
+// looked up in the packed table, 3 = counts alone from the 4-bit table (cnib; no bucket
+// starts).  The four seeds' loads are issued together, with no branch between them, so
+// that a thread keeps four lookups in flight.
 template <int Mode>
 __global__ __launch_bounds__(kThreads) void k_count_scan(
     const uint32_t *__restrict__ kmer, const uint32_t *counts_in, uint64_t n,
-    const uint32_t *__restrict__ end_tbl, const uint4 *__restrict__ ctab, uint32_t *count,
-    uint32_t *__restrict__ first_out, uint32_t *__restrict__ prefix,
-    uint64_t *__restrict__ blksum) {
+    const uint32_t *__restrict__ end_tbl, const uint4 *__restrict__ ctab,
+    const uint32_t *__restrict__ cnib, uint32_t *count, uint32_t *__restrict__ first_out,
+    uint32_t *__restrict__ prefix, uint64_t *__restrict__ blksum) {
     // counts_in may alias count (injected counts are scanned in place): each thread
     // reads its own four entries before writing them.
     __shared__ uint64_t wave_tot[kThreads / 64];
@@ -110,7 +131,18 @@ __global__ __launch_bounds__(kThreads) void k_count_scan(
         uint32_t k[kPerThread];
 #pragma unroll
         for (int i = 0; i < kPerThread; i++) k[i] = kmer[sc[i]];
-        if (Mode == 1) {
+        if (Mode == 3) {
+            uint32_t wv[kPerThread];
+#pragma unroll
+            for (int i = 0; i < kPerThread; i++) wv[i] = cnib[k[i] >> 3];
+#pragma unroll
+            for (int i = 0; i < kPerThread; i++) {
+                c[i] = (wv[i] >> (4 * (k[i] & 7u))) & 15u;
+                if (c[i] == 15u) c[i] = end_tbl[k[i] + 1] - end_tbl[k[i]];  // 15 or more
+                if (!in[i]) c[i] = 0;
+                b[i] = 0;
+            }
+        } else if (Mode == 1) {
             uint32_t lo[kPerThread], hi[kPerThread];
 #pragma unroll
             for (int i = 0; i < kPerThread; i++) {
@@ -323,13 +355,23 @@ hipError_t launch_count_scan(const uint32_t *kmer, const uint32_t *counts_in, ui
     const uint64_t blocks = (n + kScanBlock - 1) / kScanBlock;
     if (!kmer)
         hipLaunchKernelGGL(k_count_scan<0>, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
-                           counts_in, n, end_tbl, ctab, count, first, prefix, blksum);
+                           counts_in, n, end_tbl, ctab, nullptr, count, first, prefix, blksum);
     else if (!ctab)
         hipLaunchKernelGGL(k_count_scan<1>, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
-                           counts_in, n, end_tbl, ctab, count, first, prefix, blksum);
+                           counts_in, n, end_tbl, ctab, nullptr, count, first, prefix, blksum);
     else
         hipLaunchKernelGGL(k_count_scan<2>, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
-                           counts_in, n, end_tbl, ctab, count, first, prefix, blksum);
+                           counts_in, n, end_tbl, ctab, nullptr, count, first, prefix, blksum);
+    return hipGetLastError();
+}
+
+hipError_t launch_count_prefix(const uint32_t *kmer, uint64_t n, const uint32_t *end_tbl,
+                               const uint32_t *cnib, uint32_t *prefix, uint64_t *blksum,
+                               hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const uint64_t blocks = (n + kScanBlock - 1) / kScanBlock;
+    hipLaunchKernelGGL(k_count_scan<3>, dim3((uint32_t)blocks), dim3(kThreads), 0, s, kmer,
+                       nullptr, n, end_tbl, nullptr, cnib, nullptr, nullptr, prefix, blksum);
     return hipGetLastError();
 }
 
@@ -342,6 +384,16 @@ hipError_t launch_count_table(const uint32_t *end_tbl, uint64_t nb, uint4 *ctab,
     const uint32_t n_rec = count_table_records(nb);
     hipLaunchKernelGGL(k_count_table, dim3((n_rec + kThreads - 1) / kThreads), dim3(kThreads),
                        0, s, end_tbl, nb, n_rec, ctab);
+    return hipGetLastError();
+}
+
+uint64_t count_nibble_words(uint64_t nb) { return (nb + 7) / 8; }
+
+hipError_t launch_count_nibbles(const uint32_t *end_tbl, uint64_t nb, uint32_t *cnib,
+                                hipStream_t s) {
+    const uint64_t nw = count_nibble_words(nb);
+    hipLaunchKernelGGL(k_count_nibbles, dim3((uint32_t)((nw + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, end_tbl, nb, (uint32_t)nw, cnib);
     return hipGetLastError();
 }
 
