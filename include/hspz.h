@@ -387,7 +387,9 @@ int hspz_get_index(const hspz_engine *engine, uint32_t *h_end, uint32_t *h_pos,
                    uint64_t *n_buckets, uint64_t *n_pos);
 
 /* Copy the planned batch's per-seed hit counts and global inclusive prefix (u32 each,
- * one per seed of the batch) to the host (either pointer may be NULL).  Synchronous. */
+ * one per seed of the batch) to the host (either pointer may be NULL).  The counts are
+ * looked up first (on the null stream, from the uploaded k-mers and index alone) if no
+ * call has needed them since the plan.  Synchronous. */
 int hspz_get_plan_arrays(const hspz_engine *engine, uint32_t *h_counts, uint32_t *h_prefix);
 
 /* Run the prefix and chunk steps ("C. Hit discovery", C.2-C.3) on n injected per-seed
