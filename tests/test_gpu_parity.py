@@ -44,6 +44,34 @@ def test_worked_example_through_the_abi():
     assert_pass_equal(r, o)
 
 
+def test_plan_counts_follow_each_plan():
+    # The plan keeps only the prefix ("C. Hit discovery", C.1-C.2); the per-seed counts are
+    # looked up again on first use.  Each new plan, a real one or injected counts, must
+    # replace them, also when no expansion ran in between.
+    ref, qry = random_pair(31, 20_000, 20_000, plant=10, plant_len=(50, 300), identity=0.9,
+                           n_frac=0.01)
+    p = params_of(SEED_PATTERN)
+    eng = engine(p)
+    eng.upload_reference(ref)
+    eng.upload_query(qry, strand=0)
+    o, _, _ = oracle_pass(ref, qry, p)
+    n = eng.num_seeds()
+    assert n == o["count"].size and n > 100
+    for lo, hi in [(0, n // 2), (n // 2, n), (n // 3, n // 3 + 77), (0, n)]:
+        eng.plan(lo, hi)
+        cnt, pre = eng.get_plan_arrays(hi - lo)
+        want = np.asarray(o["count"][lo:hi], np.uint64)
+        assert np.array_equal(cnt.astype(np.uint64), want), (lo, hi)
+        assert np.array_equal(pre.astype(np.uint64), np.cumsum(want)), (lo, hi)
+    inj = np.arange(7, dtype=np.uint32)
+    eng.debug_plan_counts(inj)
+    cnt, pre = eng.get_plan_arrays(inj.size)
+    assert cnt.tolist() == inj.tolist() and pre.tolist() == np.cumsum(inj).tolist()
+    eng.plan(0, n)
+    cnt, _ = eng.get_plan_arrays(n)
+    assert np.array_equal(cnt.astype(np.uint64), np.asarray(o["count"], np.uint64))
+
+
 @pytest.mark.parametrize("walk", [0, 1])
 def test_chunk_cuts_from_injected_counts(walk):
     gold = json.load(open(os.path.join(GOLD, "chunk_cuts_worked_example.json")))
