@@ -853,6 +853,31 @@ def test_find_hits_gate_huge_bucket_and_sparse_seeds():
         assert checked == tot
 
 
+@pytest.mark.parametrize("max_hits", [0, 9_000])
+def test_key_grouped_runs_of_both_shapes(max_hits):
+    # The key-grouped stage enumerates each run of c bucket entries and m seeds with the
+    # smaller of the two varying fastest.  One unit is in the reference 3 times and in the
+    # query 120 times (c < m), another the other way round (c > m); their runs of 360
+    # anchors span several 64-anchor steps and steps start inside them, and the copies are
+    # homologous, so walks run long and many anchors are kept.  Everything against the
+    # oracle, gated key-grouped (gate_mode 5) and chosen automatically (0).
+    rng = np.random.default_rng(41)
+    bases = np.frombuffer(b"ACGT", np.uint8)
+    a3 = _copies_with_spacers(51, 45, 3, 30)
+    a120 = _copies_with_spacers(51, 45, 120, 30)
+    b120 = _copies_with_spacers(52, 45, 120, 30)
+    b3 = _copies_with_spacers(52, 45, 3, 30)
+    ref = np.concatenate([bases[rng.integers(0, 4, 4_000)], a3, bases[rng.integers(0, 4, 3_000)],
+                          b120, bases[rng.integers(0, 4, 4_000)]])
+    qry = np.concatenate([bases[rng.integers(0, 4, 3_000)], a120, bases[rng.integers(0, 4, 4_000)],
+                          b3, bases[rng.integers(0, 4, 3_000)]])
+    p = params_of(SEED_PATTERN, max_hits=max_hits)
+    o, _, _ = oracle_pass(ref, qry, p)
+    assert o["total"] > 20_000
+    for gm in (5, 0):
+        assert_pass_equal(gpu_full_pass(engine(p, gate_mode=gm), ref, qry), o)
+
+
 def test_dedup_records_matches_the_oracle():
     # the library's host dedup against the oracle's: random record arrays with heavy
     # repetition, in place through the C ABI, the capacity error, and an empty array
