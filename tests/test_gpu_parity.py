@@ -547,6 +547,45 @@ def test_whole_batch_gate_matches_the_oracle():
                           acc.astype(oracle.HSP_DTYPE).view(np.uint8))
 
 
+def _unit_copies(unit_seed, spacer_seed, unit_len, copies, spacer):
+    """Copies of one random unit, each followed by its own random spacer."""
+    bases = np.frombuffer(b"ACGT", np.uint8)
+    unit = bases[np.random.default_rng(unit_seed).integers(0, 4, unit_len)]
+    rs = np.random.default_rng(spacer_seed)
+    parts = []
+    for _ in range(copies):
+        parts += [unit, bases[rs.integers(0, 4, spacer)]]
+    return np.concatenate(parts)
+
+
+def test_whole_batch_with_most_anchors_deferred():
+    # The whole-batch gate (flag bits) when most walks outlive the first window: copies of
+    # a 90-base unit (150 in each sequence, totals near 8,600: kept at K = 7,000) and of a
+    # 60-base unit (420 in each, totals near 5,700: dropped), different spacers on the two
+    # sides, about 9e6 anchors in two chunks.  The waves' LDS segments fill, so deferred
+    # anchors also go through the global list with their slots formed from the prefix, and
+    # the exact walks overflow the workgroups' pools into the exact list.
+    ref = np.concatenate([_unit_copies(61, 1, 90, 150, 70), _unit_copies(62, 2, 60, 420, 70)])
+    qry = np.concatenate([_unit_copies(61, 3, 90, 150, 70), _unit_copies(62, 4, 60, 420, 70)])
+    p = params_of(SEED_PATTERN, max_hits=5_000_000, K=7000)
+    o, _, _ = oracle_pass(ref, qry, p)
+    want, acc = _oracle_batch(o)
+    assert want["n_chunks"] == 2 and want["n_anchors"] >= (1 << 22) * 2
+    assert 0 < want["n_accepted"] < want["n_anchors"] // 2
+    for gm in (0, 5):
+        eng = engine(p, gate_mode=gm)
+        eng.upload_reference(ref)
+        eng.upload_query(qry)
+        st = eng.run_batch(0, eng.num_seeds(), time_gate=True)
+        assert {k: st[k] for k in want} == want, gm
+        assert st["whole_batch_gate"] == 1
+        n2, nx = eng.debug_gate_deferred()
+        print(f"gate_mode {gm}: {want}, second stage {n2}, exact {nx}", flush=True)
+        assert n2 > want["n_anchors"] // 10 and nx > 0
+        assert np.array_equal(eng.batch_records().view(np.uint8),
+                              acc.astype(oracle.HSP_DTYPE).view(np.uint8)), gm
+
+
 @pytest.mark.parametrize("mat", [0, 2], ids=["default-walks", "shared-walks"])
 def test_run_batch_reverse_strand_and_entropy(mat):
     ref, qry = random_pair(11, 30_000, 25_000, n_frac=0.02, plant=25, plant_len=(80, 900),
