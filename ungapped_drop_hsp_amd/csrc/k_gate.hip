@@ -693,27 +693,34 @@ __global__ __launch_bounds__(kThreads) void k_gate_window(
 }
 
 // Directory of the fused first stage: the seed that owns the first slot of each wave's
-// range, i.e. the first seed whose prefix - hit_lo exceeds that slot (a binary search).
-// The first thread also clears the four deferred-list counters the stages append to.
+// range, i.e. the first seed whose prefix - hit_lo exceeds that slot.  One wave per entry
+// searches 64 ways: each round its lanes read the last prefix of 64 equal segments of the
+// range and a ballot picks the first segment past the slot, so a search costs about
+// log64(seeds) dependent reads where a per-thread binary search costs log2(seeds) (a
+// chunk's prefixes are few enough to stay in L2, so the extra reads are cheap).  The
+// first wave also clears the four deferred-list counters the stages append to.
 __global__ __launch_bounds__(kThreads) void k_slot_dir(ChunkSeeds cs, uint32_t n_waves,
                                                        uint32_t steps,
                                                        uint32_t *__restrict__ cnt) {
-    const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
-    if (w == 0) {
-        cnt[0] = 0;
-        cnt[1] = 0;
-        cnt[2] = 0;
-        cnt[3] = 0;
-    }
-    if (w >= n_waves) return;
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t w = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (w == 0 && lane < 4) cnt[lane] = 0;
+    if (w >= n_waves) return;  // uniform
     const uint32_t t = w * (64u * steps);
-    uint32_t lo = 0, hi = cs.n_seeds;
-    while (lo < hi) {
-        const uint32_t mid = lo + (hi - lo) / 2;
-        if (cs.prefix.at(mid) - cs.hit_lo > t) hi = mid;
-        else lo = mid + 1;
+    // the answer lies in [lo, hi], and the chunk's last seed is past every wave's first slot
+    // (t < n), so the ballot over the probes always holds lane 63's bit
+    uint32_t lo = 0, hi = cs.n_seeds - 1;
+    while (hi - lo >= 64) {  // uniform
+        const uint64_t step = ((uint64_t)hi - lo + 64) / 64;
+        const uint32_t idx = (uint32_t)min((uint64_t)lo + (lane + 1) * step - 1, (uint64_t)hi);
+        const uint64_t m = __ballot(cs.prefix.at(idx) - cs.hit_lo > t);
+        const uint32_t f = (uint32_t)__builtin_ctzll(m);
+        hi = (uint32_t)min((uint64_t)lo + (f + 1) * step - 1, (uint64_t)hi);
+        lo = (uint32_t)(lo + f * step);
     }
-    cs.dir[w] = lo;
+    const uint32_t idx = min(lo + lane, hi);
+    const uint64_t m = __ballot(lo + lane <= hi && cs.prefix.at(idx) - cs.hit_lo > t);
+    if (lane == 0) cs.dir[w] = lo + (uint32_t)__builtin_ctzll(m);
 }
 
 // First stage fused with the backward expansion ("C. Hit discovery", C.5): a wave walks
@@ -1295,7 +1302,7 @@ hipError_t launch_gate_window_fused(bool narrow, const ChunkSeeds &cs, uint32_t 
     }
     const uint32_t steps = gate_window_steps(n);
     const uint32_t n_waves = (uint32_t)gate_window_waves(n);
-    hipLaunchKernelGGL(k_slot_dir, dim3((n_waves + kThreads - 1) / kThreads), dim3(kThreads), 0,
+    hipLaunchKernelGGL(k_slot_dir, dim3((n_waves + kWaves - 1) / kWaves), dim3(kThreads), 0,
                        s, cs, n_waves, steps, cnt);
     const uint32_t blocks = (n_waves + kWaves - 1) / kWaves;
     if (narrow)
